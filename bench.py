@@ -1,0 +1,190 @@
+"""Benchmark of the KDA hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one chunked-prefill launch over the whole workload (default: B=4, H=16,
+T=4096, dk=dv=128, bf16 inputs, fp32 state).  Inputs are generated once on the GPU and are
+resident in HBM before timing; the 256 MB last-level cache is flushed between timed steps
+so no step reuses the previous step's inputs from cache.  Each step is timed with HIP
+events on the stream the kernel runs on.  Prints one JSON line.
+
+The decode step (256 sequences x 32 heads, 128x128 fp32 states, 1000 consecutive steps)
+is measured in the same run and reported under "decode".
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # dense bf16 (256 CU x 4096 flop/clk x 2.4 GHz)
+
+
+def prefill_algorithmic(lengths, H, dk, dv, es, has_s0, chunk=16):
+    """Bytes and flops a prefill launch must move/do at minimum.
+
+    Per token-head: read q, k, log_alpha (dk each), v, gate (dv each), beta; write o (dv).
+    Per (sequence, head): read S0 (if given) and write S_T, fp32 dk x dv each.
+    Flops per token-head: 6 dk dv (W S, Qh S, Kb^T U) + 6 C dk (Gram pair, W) +
+    4 C dv (T V, P U)."""
+    tokens = sum(lengths)
+    th = tokens * H
+    bytes_ = th * (es * (3 * dk + 2 * dv) + es + es * dv)
+    bytes_ += len(lengths) * H * 4 * dk * dv * (2 if has_s0 else 1)
+    flops = th * (6 * dk * dv + 6 * chunk * dk + 4 * chunk * dv)
+    return bytes_, flops
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill_b4_h16_t4096")
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flush", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
+              "the operator shards over (sequence, head) with no communication, so the "
+              "N-GPU figure is N independent copies of this one.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import kda_inputs as ki
+    import linear_attention_sequence_chunked_amd as kda
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    w = ki.WORKLOADS[args.workload]
+    x = ki.make_workload_inputs(w, seed=1, device="cuda")
+    es = 2 if w.dtype == "bf16" else 4
+    T_total = x.total_tokens
+    out = torch.empty((T_total, w.H, w.dv), dtype=x.q.dtype, device="cuda")
+    Sf = torch.empty((len(w.lengths), w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    flush = None if args.no_flush else torch.empty(256 << 20, dtype=torch.float32,
+                                                   device="cuda")  # 1 GiB
+
+    def step():
+        kda.chunk_prefill(x.q, x.k, x.v, x.log_alpha, x.beta, x.gate, cu_seqlens=x.cu_seqlens,
+                          cu_seqlens_host=x.cu_seqlens_host, initial_state=x.initial_state,
+                          out=out, final_state=Sf)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        if flush is not None:
+            flush.zero_()
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    times_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    ms = float(np.mean(times_ms))
+    tokens_per_s = T_total / (ms * 1e-3)
+    alg_bytes, alg_flops = prefill_algorithmic(w.lengths, w.H, w.dk, w.dv, es,
+                                               x.initial_state is not None)
+    gbps = alg_bytes / (ms * 1e-3) / 1e9
+    tflops = alg_flops / (ms * 1e-3) / 1e12
+
+    result = {
+        "metric": "KDA prefill tokens/s (%MFMA peak); decode state GB/s (%HBM peak), 1 MI355X",
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "ms_per_step_median": float(np.median(times_ms)),
+        "wall_s_timed_region_incl_cache_flush": wall,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded; q,k L2-normalised N(0,1); v N(0,1); beta, gate "
+                "sigmoid(N(0,1)); log_alpha max(-softplus(N(0,1)),-0.3))",
+        "config": {"workload": w.name, "batch": len(w.lengths), "seq_len": max(w.lengths),
+                   "tokens": T_total, "heads": w.H, "dk": w.dk, "dv": w.dv, "chunk": 16,
+                   "state": "fp32", "initial_state": x.initial_state is not None},
+        "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "prefill_kernel", "algorithmic_bytes_per_launch": alg_bytes},
+        "mfma": {"achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                 "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+                 "algorithmic_flops_per_launch": alg_flops},
+    }
+
+    # ---------------------------------------------------------------- decode step
+    if not args.no_decode and args.decode_steps > 0:
+        d = ki.WORKLOADS["decode_n256_h32"]
+        N = len(d.lengths)
+        nsteps = args.decode_steps
+        inp = ki.make_decode_inputs(nsteps, N, d.H, d.dk, d.dv, d.dtype, seed=3, device="cuda")
+        state = ki.make_state(N, d.H, d.dk, d.dv, d.s0_std, seed=3, device="cuda")
+        dout = torch.empty((N, d.H, d.dv), dtype=torch.bfloat16, device="cuda")
+
+        def dstep(s):
+            kda.decode_step(inp["q"][s], inp["k"][s], inp["v"][s], inp["log_alpha"][s],
+                            inp["beta"][s], inp["gate"][s], state, out=dout)
+
+        for s in range(min(5, nsteps)):
+            dstep(s)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for s in range(nsteps):
+            dstep(s)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dms = e0.elapsed_time(e1) / nsteps
+        state_bytes = N * d.H * d.dk * d.dv * 4
+        io_bytes = N * d.H * (2 * (3 * d.dk + 3 * d.dv) + 2)
+        result["decode"] = {
+            "workload": d.name, "steps": nsteps, "us_per_step": dms * 1e3,
+            "state_GBps": 2 * state_bytes / (dms * 1e-3) / 1e9,
+            "frac_hbm": 2 * state_bytes / (dms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "total_GBps_incl_token_io": (2 * state_bytes + io_bytes) / (dms * 1e-3) / 1e9,
+            "state_bytes": state_bytes,
+        }
+        del inp, state
+        torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------------- CPU oracle
+    if not args.no_cpu_baseline:
+        import oracle
+        f = lambda t: None if t is None else t.detach().float().cpu().numpy()
+        hq, hk, hv, hla, hb, hg, hs = (f(t) for t in (x.q, x.k, x.v, x.log_alpha, x.beta,
+                                                      x.gate, x.initial_state))
+        oracle.ensure_built()
+        t0 = time.perf_counter()
+        _, _, used = oracle.run(hq, hk, hv, hla, hb, hg, x.cu_seqlens_host, hs,
+                                want_out=True)
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {
+            "value": T_total / dt, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"the whole workload: all {len(w.lengths) * w.H} (sequence, head) "
+                      f"pairs, {T_total} tokens, fp64 token loop ({dt:.1f} s)"}
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,129 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention (KDA) operator library.
+ *
+ * The operator is a gated delta-rule recurrence with a fixed-size state per head,
+ * S in R^{dk x dv} (rows = key channels).  For every token of a sequence:
+ *     a   = exp(max(log_alpha_t, log_alpha_floor))       per key channel
+ *     S  <- Diag(a) S                                     per-row (per-channel) decay
+ *     S  <- S + beta_t k_t (v_t - S^T k_t)^T              delta-rule erase/write along k
+ *     o_t = gate_t (elementwise) (S^T (scale q_t))         gated readout of the new state
+ * Sources (page title, section/figure):
+ *   "Kimi-K3 为什么这么强？" §① KDA part ② and the "一次 KDA 更新" figure caption
+ *     (per-row forgetting -> weaken the key's row by beta -> write; in-place table);
+ *   "Kimi K3 深度拆解" 突破一 (per-channel diagonal decay, DPLR transition);
+ *   digest of "Kimi K3: Open Frontier Intelligence", section
+ *     "KDA：百万上下文先要过「数值 算子」这一关" and Fig. 3 (lower-bounded per-step
+ *     log-decay, 16-token chunks whose causal block runs on dense matrix units; output
+ *     gate as a channel-wise switch on the recurrence output); same page, section
+ *     "基础设施" (intra-chunk work overlapped with inter-chunk state propagation; state
+ *     updated in place when decoding; state snapshots for resuming a prefix).
+ *
+ * Conventions for every entry point
+ *   - Pointers without a _host suffix are DEVICE pointers (HIP global memory) that the
+ *     caller allocated and owns; the library allocates no device memory and keeps no
+ *     per-call state.  Every tensor is dense, row-major and 16-byte aligned.
+ *   - Element type of q, k, v, log_alpha, beta, gate and out is params->dtype (bf16 or
+ *     fp32).  States are always fp32.
+ *   - Calls only enqueue work on `stream` (a hipStream_t; NULL = the null stream) and
+ *     return without synchronising.  Results are visible after the stream completes.
+ *   - Every argument is validated on the host BEFORE any HIP call; a rejected call
+ *     returns KDA_ERR_INVALID_ARGUMENT or KDA_ERR_UNSUPPORTED and enqueues nothing.
+ *     A failed launch returns KDA_ERR_HIP.  kda_last_error() gives the detail (per
+ *     thread).  Faults inside a kernel surface at the caller's next synchronisation.
+ *   - Calls on one stream are ordered; calls that write the same buffers from
+ *     different streams race.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad size, aliasing, ... */
+    KDA_ERR_UNSUPPORTED = 2,      /* valid request this build does not implement      */
+    KDA_ERR_HIP = 3               /* the HIP runtime reported an error on launch        */
+} kda_status;
+
+typedef enum { KDA_DTYPE_BF16 = 0, KDA_DTYPE_F32 = 1 } kda_dtype;
+
+typedef struct {
+    int32_t dtype;           /* kda_dtype of q, k, v, log_alpha, beta, gate, out       */
+    int32_t num_heads;       /* H >= 1                                                  */
+    int32_t dk;              /* key channels per head: 64 or 128                        */
+    int32_t dv;              /* value channels per head: 64 or 128                      */
+    int32_t chunk;           /* tokens per chunk of the prefill; must be 16             */
+    float log_alpha_floor;   /* lower bound on the per-step log-decay, in [-5, 0]
+                                (the pages' bound keeps 16-token cumulative decay
+                                representable; the constant itself is not given there,
+                                the workloads use -0.3)                                */
+    float scale;             /* multiplies q before the readout (finite; usually 1)    */
+} kda_params;
+
+/*
+ * kda_chunk_prefill -- run the recurrence over packed variable-length sequences.
+ *
+ * Sequence n (0 <= n < num_seqs) owns packed token rows cu_seqlens[n] ..
+ * cu_seqlens[n+1]-1; each sequence starts from its own initial state and its 16-token
+ * chunks are aligned at the sequence start (the last chunk may be partial).  A
+ * fixed-length batch of B sequences of length T is cu_seqlens = {0, T, 2T, ..., BT}.
+ *
+ *   q, k, log_alpha : [T_total, H, dk]     (T_total = cu_seqlens[num_seqs])
+ *   v, gate         : [T_total, H, dv]     gate holds the gate VALUES (e.g. sigmoid
+ *                                          outputs); the op multiplies them in
+ *   beta            : [T_total, H]
+ *   cu_seqlens      : int32 [num_seqs+1], device copy
+ *   cu_seqlens_host : int32 [num_seqs+1], host copy of the same values (used for
+ *                     validation and scheduling; must start at 0 and not decrease)
+ *   initial_state   : fp32 [num_seqs, H, dk, dv] or NULL (zeros)
+ *   final_state     : fp32 [num_seqs, H, dk, dv] or NULL (not written).  May be the
+ *                     same pointer as initial_state (updated in place); any other
+ *                     overlap with an input is rejected.
+ *   out             : [T_total, H, dv], params->dtype; must not overlap any input.
+ *
+ * A zero-length sequence writes no output rows and copies its initial state (or
+ * zeros) to final_state.  T_total == 0 is allowed and only writes final_state.
+ */
+kda_status kda_chunk_prefill(const kda_params* params, const void* q, const void* k,
+                             const void* v, const void* log_alpha, const void* beta,
+                             const void* gate, const int32_t* cu_seqlens,
+                             const int32_t* cu_seqlens_host, int32_t num_seqs,
+                             const float* initial_state, float* final_state, void* out,
+                             void* stream);
+
+/*
+ * kda_decode_step -- one token per sequence, state updated in place.
+ *
+ *   q, k, log_alpha : [num_seqs, H, dk];  v, gate, out : [num_seqs, H, dv];
+ *   beta            : [num_seqs, H];
+ *   state           : fp32 [num_seqs, H, dk, dv], read and written in place (one read
+ *                     and one write of every element).
+ *   out must not overlap any input or the state.
+ * Equivalent to kda_chunk_prefill with one token per sequence and
+ * final_state == initial_state == state.
+ */
+kda_status kda_decode_step(const kda_params* params, const void* q, const void* k,
+                           const void* v, const void* log_alpha, const void* beta,
+                           const void* gate, int32_t num_seqs, float* state, void* out,
+                           void* stream);
+
+/* Static English text for a status code (never NULL). */
+const char* kda_status_string(kda_status status);
+
+/* Detail of the last failed call made by the calling thread ("" if none). */
+const char* kda_last_error(void);
+
+/* KDA_ABI_VERSION of the loaded library. */
+int32_t kda_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

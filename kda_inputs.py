@@ -119,20 +119,32 @@ def _l2norm(x: torch.Tensor) -> torch.Tensor:
 def make_prefill_inputs(lengths: Sequence[int], H: int, dk: int, dv: int, dtype: str,
                         s0_std: float, seed: int, device="cpu",
                         log_alpha_min: float = -0.3) -> KdaInputs:
-    """Draw one packed varlen batch.  `seed` identifies the workload; each tensor uses
-    its own stream (seed, tensor_id)."""
+    """Draw one packed varlen batch.  Every (sequence, tensor) pair has its own seeded
+    stream (seed, tensor_id, sequence), so a sequence's values do not depend on the
+    other lengths in the batch and temporaries stay one sequence in size."""
     dt = _torch_dtype(dtype)
     T = int(sum(lengths))
     cu = [0]
     for L in lengths:
         cu.append(cu[-1] + int(L))
-    q = _l2norm(_randn((T, H, dk), (seed, 0), device)).to(dt)
-    k = _l2norm(_randn((T, H, dk), (seed, 1), device)).to(dt)
-    v = _randn((T, H, dv), (seed, 2), device).to(dt)
-    la = torch.clamp(-torch.nn.functional.softplus(_randn((T, H, dk), (seed, 3), device)),
-                     min=log_alpha_min).to(dt)
-    beta = torch.sigmoid(_randn((T, H), (seed, 4), device)).to(dt)
-    gate = torch.sigmoid(_randn((T, H, dv), (seed, 5), device)).to(dt)
+    q = torch.empty((T, H, dk), dtype=dt, device=device)
+    k = torch.empty((T, H, dk), dtype=dt, device=device)
+    v = torch.empty((T, H, dv), dtype=dt, device=device)
+    la = torch.empty((T, H, dk), dtype=dt, device=device)
+    beta = torch.empty((T, H), dtype=dt, device=device)
+    gate = torch.empty((T, H, dv), dtype=dt, device=device)
+    sp = torch.nn.functional.softplus
+    for n, L in enumerate(lengths):
+        a, e = cu[n], cu[n + 1]
+        if L == 0:
+            continue
+        q[a:e] = _l2norm(_randn((L, H, dk), (seed, 0, n), device)).to(dt)
+        k[a:e] = _l2norm(_randn((L, H, dk), (seed, 1, n), device)).to(dt)
+        v[a:e] = _randn((L, H, dv), (seed, 2, n), device).to(dt)
+        la[a:e] = torch.clamp(-sp(_randn((L, H, dk), (seed, 3, n), device)),
+                              min=log_alpha_min).to(dt)
+        beta[a:e] = torch.sigmoid(_randn((L, H), (seed, 4, n), device)).to(dt)
+        gate[a:e] = torch.sigmoid(_randn((L, H, dv), (seed, 5, n), device)).to(dt)
     S0 = None
     if s0_std > 0:
         S0 = (_randn((len(lengths), H, dk, dv), (seed, 6), device) * s0_std).contiguous()
@@ -146,12 +158,23 @@ def make_workload_inputs(w: Workload, seed: int, device="cpu",
                                w.dv, w.dtype, w.s0_std, seed, device)
 
 
-def make_decode_inputs(N: int, H: int, dk: int, dv: int, dtype: str, seed: int, step: int,
-                       device="cpu", log_alpha_min: float = -0.3) -> KdaInputs:
-    """One fresh token per sequence for decode step `step` (tensors [N, H, d])."""
-    x = make_prefill_inputs((1,) * N, H, dk, dv, dtype, 0.0, seed * 1_000_003 + step,
-                            device, log_alpha_min)
-    return x
+def make_decode_inputs(steps: int, N: int, H: int, dk: int, dv: int, dtype: str, seed: int,
+                       device="cpu", log_alpha_min: float = -0.3) -> dict:
+    """Fresh tokens for `steps` consecutive decode steps, one per sequence per step.
+
+    Returns a dict of tensors shaped [steps, N, H, d] ([steps, N, H] for beta); step s
+    feeds row s.  Same distributions as the prefill inputs."""
+    dt = _torch_dtype(dtype)
+    sp = torch.nn.functional.softplus
+    return dict(
+        q=_l2norm(_randn((steps, N, H, dk), (seed, 10), device)).to(dt),
+        k=_l2norm(_randn((steps, N, H, dk), (seed, 11), device)).to(dt),
+        v=_randn((steps, N, H, dv), (seed, 12), device).to(dt),
+        log_alpha=torch.clamp(-sp(_randn((steps, N, H, dk), (seed, 13), device)),
+                              min=log_alpha_min).to(dt),
+        beta=torch.sigmoid(_randn((steps, N, H), (seed, 14), device)).to(dt),
+        gate=torch.sigmoid(_randn((steps, N, H, dv), (seed, 15), device)).to(dt),
+    )
 
 
 def make_state(N: int, H: int, dk: int, dv: int, std: float, seed: int,

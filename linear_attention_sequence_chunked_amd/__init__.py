@@ -1,0 +1,9 @@
+"""MI355X (gfx950) Kimi Delta Attention: chunked prefill and decode step.
+
+The compute runs in libkda.so (hand-written HIP kernels behind the C ABI of
+include/kda.h); this package only marshals torch tensors and the current stream.
+"""
+from ._lib import KdaError, LIB_PATH, load as load_library  # noqa: F401
+from .ops import chunk_prefill, decode_step  # noqa: F401
+
+__all__ = ["chunk_prefill", "decode_step", "KdaError", "load_library", "LIB_PATH"]

@@ -1,0 +1,233 @@
+// kda_api.cpp -- C ABI of the KDA library: argument validation, scheduling, launch.
+//
+// Every check runs on the host before any HIP call, so a rejected call enqueues
+// nothing and the validation paths can be exercised on a machine without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <numeric>
+#include <string>
+#include <vector>
+
+#include "../../include/kda.h"
+#include "kda_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kda_status fail(kda_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+kda_status ok() {
+    g_last_error.clear();
+    return KDA_OK;
+}
+
+struct Range {
+    const char* name;
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlaps(const Range& a, const Range& b) {
+    return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+Range range(const char* name, const void* p, uint64_t bytes) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{name, lo, p ? lo + bytes : lo};
+}
+
+kda_status check_params(const kda_params* p) {
+    if (!p) return fail(KDA_ERR_INVALID_ARGUMENT, "params is NULL");
+    if (p->dtype != KDA_DTYPE_BF16 && p->dtype != KDA_DTYPE_F32)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "dtype %d is not KDA_DTYPE_BF16 or KDA_DTYPE_F32",
+                    p->dtype);
+    if (p->num_heads < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "num_heads %d < 1", p->num_heads);
+    if (p->chunk != 16) return fail(KDA_ERR_UNSUPPORTED, "chunk %d: only 16 is supported", p->chunk);
+    if ((p->dk != 64 && p->dk != 128) || (p->dv != 64 && p->dv != 128))
+        return fail(KDA_ERR_UNSUPPORTED, "dk=%d dv=%d: each must be 64 or 128", p->dk, p->dv);
+    if (!std::isfinite(p->log_alpha_floor) || p->log_alpha_floor > 0.f ||
+        p->log_alpha_floor < -5.f)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "log_alpha_floor %g outside [-5, 0]",
+                    (double)p->log_alpha_floor);
+    if (!std::isfinite(p->scale)) return fail(KDA_ERR_INVALID_ARGUMENT, "scale is not finite");
+    return KDA_OK;
+}
+
+kda_status check_ptr(const char* name, const void* ptr, size_t align) {
+    if (!ptr) return fail(KDA_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+    if (reinterpret_cast<uintptr_t>(ptr) % align)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "%s is not %zu-byte aligned", name, align);
+    return KDA_OK;
+}
+
+int device_cu_count() {
+    static int cached = 0;
+    if (cached) return cached;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        cus > 0)
+        cached = cus;
+    else
+        cached = 256;
+    return cached;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_string(kda_status s) {
+    switch (s) {
+        case KDA_OK: return "ok";
+        case KDA_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case KDA_ERR_UNSUPPORTED: return "unsupported";
+        case KDA_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* kda_last_error(void) { return g_last_error.c_str(); }
+
+int32_t kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+kda_status kda_chunk_prefill(const kda_params* params, const void* q, const void* k,
+                             const void* v, const void* log_alpha, const void* beta,
+                             const void* gate, const int32_t* cu_seqlens,
+                             const int32_t* cu_seqlens_host, int32_t num_seqs,
+                             const float* initial_state, float* final_state, void* out,
+                             void* stream) {
+    kda_status st = check_params(params);
+    if (st != KDA_OK) return st;
+    const kda_params& p = *params;
+    if (num_seqs < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "num_seqs %d < 1", num_seqs);
+    if (!cu_seqlens_host) return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens_host is NULL");
+    if ((st = check_ptr("cu_seqlens", cu_seqlens, 4)) != KDA_OK) return st;
+    if (cu_seqlens_host[0] != 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens_host[0] = %d, must be 0",
+                    cu_seqlens_host[0]);
+    int64_t longest = 0;
+    for (int32_t n = 0; n < num_seqs; ++n) {
+        const int64_t len = (int64_t)cu_seqlens_host[n + 1] - cu_seqlens_host[n];
+        if (len < 0)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens_host decreases at index %d", n + 1);
+        longest = std::max(longest, len);
+    }
+    const int64_t T = cu_seqlens_host[num_seqs];
+    const int64_t H = p.num_heads;
+    const size_t es = p.dtype == KDA_DTYPE_BF16 ? 2 : 4;
+
+    const void* tens[] = {q, k, v, log_alpha, gate, out};
+    const char* names[] = {"q", "k", "v", "log_alpha", "gate", "out"};
+    if (T > 0) {
+        for (int i = 0; i < 6; ++i)
+            if ((st = check_ptr(names[i], tens[i], 16)) != KDA_OK) return st;
+        if ((st = check_ptr("beta", beta, es)) != KDA_OK) return st;
+    }
+    if (initial_state && (st = check_ptr("initial_state", initial_state, 16)) != KDA_OK) return st;
+    if (final_state && (st = check_ptr("final_state", final_state, 16)) != KDA_OK) return st;
+
+    const uint64_t nk = (uint64_t)T * H * p.dk * es, nv = (uint64_t)T * H * p.dv * es;
+    const uint64_t ns = (uint64_t)num_seqs * H * p.dk * p.dv * 4;
+    const Range inputs[] = {range("q", q, nk),         range("k", k, nk),
+                            range("v", v, nv),         range("log_alpha", log_alpha, nk),
+                            range("beta", beta, (uint64_t)T * H * es),
+                            range("gate", gate, nv),   range("initial_state", initial_state, ns)};
+    const Range ro = range("out", out, nv);
+    for (const Range& in : inputs)
+        if (overlaps(ro, in)) return fail(KDA_ERR_INVALID_ARGUMENT, "out overlaps %s", in.name);
+    if (final_state) {
+        const Range rf = range("final_state", final_state, ns);
+        if (overlaps(rf, ro)) return fail(KDA_ERR_INVALID_ARGUMENT, "final_state overlaps out");
+        for (const Range& in : inputs) {
+            if (!overlaps(rf, in)) continue;
+            if (in.lo == rf.lo && std::string(in.name) == "initial_state") continue;
+            return fail(KDA_ERR_INVALID_ARGUMENT, "final_state overlaps %s", in.name);
+        }
+    }
+
+    kda::PrefillArgs a;
+    a.dtype = p.dtype; a.H = p.num_heads; a.dk = p.dk; a.dv = p.dv;
+    a.floor_ = p.log_alpha_floor; a.scale = p.scale; a.num_seqs = num_seqs;
+    a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta; a.gate = gate;
+    a.cu_seqlens = cu_seqlens; a.initial_state = initial_state; a.final_state = final_state;
+    a.out = out;
+    a.num_ordered = 0;
+    if (num_seqs > 1 && num_seqs <= kda::kMaxOrdered) {
+        // longest sequences first: they bound the launch's critical path
+        std::vector<int32_t> idx(num_seqs);
+        std::iota(idx.begin(), idx.end(), 0);
+        std::stable_sort(idx.begin(), idx.end(), [&](int32_t x, int32_t y) {
+            return cu_seqlens_host[x + 1] - cu_seqlens_host[x] >
+                   cu_seqlens_host[y + 1] - cu_seqlens_host[y];
+        });
+        a.num_ordered = num_seqs;
+        for (int32_t i = 0; i < num_seqs; ++i) a.order[i] = idx[i];
+    }
+    const char* env = std::getenv("KDA_PREFILL_NV");
+    const int forced = env ? std::atoi(env) : 0;
+    if (forced == 16 || forced == 32 || forced == 64 || forced == 128) {
+        a.nv = std::min(forced, p.dv);
+    } else {
+        a.nv = kda::prefill_pick_nv(p.dv, (int64_t)num_seqs * H, (longest + 15) / 16,
+                                    device_cu_count());
+    }
+    const hipError_t e = kda::launch_prefill(a, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(KDA_ERR_HIP, "kda_chunk_prefill launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+kda_status kda_decode_step(const kda_params* params, const void* q, const void* k,
+                           const void* v, const void* log_alpha, const void* beta,
+                           const void* gate, int32_t num_seqs, float* state, void* out,
+                           void* stream) {
+    kda_status st = check_params(params);
+    if (st != KDA_OK) return st;
+    const kda_params& p = *params;
+    if (num_seqs < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "num_seqs %d < 0", num_seqs);
+    if (num_seqs == 0) return ok();
+    const size_t es = p.dtype == KDA_DTYPE_BF16 ? 2 : 4;
+    const void* tens[] = {q, k, v, log_alpha, gate, out};
+    const char* names[] = {"q", "k", "v", "log_alpha", "gate", "out"};
+    for (int i = 0; i < 6; ++i)
+        if ((st = check_ptr(names[i], tens[i], 16)) != KDA_OK) return st;
+    if ((st = check_ptr("beta", beta, es)) != KDA_OK) return st;
+    if ((st = check_ptr("state", state, 16)) != KDA_OK) return st;
+    const int64_t NH = (int64_t)num_seqs * p.num_heads;
+    const uint64_t nk = NH * p.dk * es, nv = NH * p.dv * es;
+    const Range inputs[] = {range("q", q, nk),        range("k", k, nk),
+                            range("v", v, nv),        range("log_alpha", log_alpha, nk),
+                            range("beta", beta, NH * es), range("gate", gate, nv)};
+    const Range ro = range("out", out, nv);
+    const Range rs = range("state", state, (uint64_t)NH * p.dk * p.dv * 4);
+    if (overlaps(ro, rs)) return fail(KDA_ERR_INVALID_ARGUMENT, "out overlaps state");
+    for (const Range& in : inputs) {
+        if (overlaps(ro, in)) return fail(KDA_ERR_INVALID_ARGUMENT, "out overlaps %s", in.name);
+        if (overlaps(rs, in)) return fail(KDA_ERR_INVALID_ARGUMENT, "state overlaps %s", in.name);
+    }
+    kda::DecodeArgs a;
+    a.dtype = p.dtype; a.H = p.num_heads; a.dk = p.dk; a.dv = p.dv;
+    a.floor_ = p.log_alpha_floor; a.scale = p.scale; a.num_seqs = num_seqs;
+    a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta; a.gate = gate;
+    a.state = state; a.out = out;
+    const hipError_t e = kda::launch_decode(a, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(KDA_ERR_HIP, "kda_decode_step launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

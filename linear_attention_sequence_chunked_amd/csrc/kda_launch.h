@@ -1,0 +1,44 @@
+// kda_launch.h -- host-side launch descriptors shared by the C ABI and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+enum { DTYPE_BF16 = 0, DTYPE_F32 = 1 };
+
+struct DecodeArgs {
+    int dtype, H, dk, dv;
+    float floor_, scale;
+    int64_t num_seqs;
+    const void *q, *k, *v, *log_alpha, *beta, *gate;
+    float* state;
+    void* out;
+};
+
+// Maximum number of sequences whose launch order is passed in the kernel arguments
+// (longest first); larger batches run in their natural order.
+constexpr int kMaxOrdered = 256;
+
+struct PrefillArgs {
+    int dtype, H, dk, dv;
+    float floor_, scale;
+    int num_seqs;
+    const void *q, *k, *v, *log_alpha, *beta, *gate;
+    const int32_t* cu_seqlens;   // device
+    const float* initial_state;  // may be null
+    float* final_state;          // may be null
+    void* out;
+    int nv;                      // value columns per workgroup (dv-slice width)
+    int num_ordered;             // entries of order[] in use (0 = natural order)
+    int32_t order[kMaxOrdered];  // sequence ids, longest first
+};
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+// value-slice width the prefill would pick for this problem (exposed for tests)
+int prefill_pick_nv(int dv, int64_t num_pairs, int64_t longest_chunks, int cu_count);
+
+}  // namespace kda

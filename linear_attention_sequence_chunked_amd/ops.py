@@ -1,0 +1,129 @@
+"""torch-facing wrappers over the C ABI: shape checks, output allocation, the current
+stream.  Every step of the operator runs in the HIP kernels of libkda.so; there is no
+CPU or PyTorch fallback."""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence, Union
+
+import torch
+
+from . import _lib
+
+_DT = {torch.bfloat16: _lib.KDA_DTYPE_BF16, torch.float32: _lib.KDA_DTYPE_F32}
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _check_dev(name, t, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def chunk_prefill(q, k, v, log_alpha, beta, gate, cu_seqlens=None, initial_state=None,
+                  output_final_state: bool = True, log_alpha_floor: float = -0.3,
+                  scale: float = 1.0, cu_seqlens_host: Optional[Sequence[int]] = None,
+                  out: Optional[torch.Tensor] = None,
+                  final_state: Optional[torch.Tensor] = None):
+    """KDA chunked prefill.
+
+    Fixed length: q/k/log_alpha [B, T, H, dk], v/gate [B, T, H, dv], beta [B, T, H].
+    Varlen: the same tensors packed as [T_total, H, .] with cu_seqlens (int32 tensor
+    or list, N+1 entries).  initial_state: fp32 [N, H, dk, dv] or None.
+    Returns (o, final_state or None); o has v's shape and dtype.
+    """
+    dt = q.dtype
+    if dt not in _DT:
+        raise ValueError(f"unsupported dtype {dt}")
+    if q.dim() == 4:
+        B, T, H, dk = q.shape
+        if cu_seqlens is not None:
+            raise ValueError("cu_seqlens is for packed [T_total, H, d] inputs")
+        cu_host = [i * T for i in range(B + 1)]
+        flat = lambda x: x.reshape(B * T, *x.shape[2:])
+        qf, kf, vf, laf, bf, gf = (flat(x) for x in (q, k, v, log_alpha, beta, gate))
+    elif q.dim() == 3:
+        if cu_seqlens is None:
+            raise ValueError("packed [T_total, H, d] inputs need cu_seqlens")
+        qf, kf, vf, laf, bf, gf = q, k, v, log_alpha, beta, gate
+        if cu_seqlens_host is not None:
+            cu_host = [int(x) for x in cu_seqlens_host]
+        elif isinstance(cu_seqlens, torch.Tensor):
+            cu_host = [int(x) for x in cu_seqlens.tolist()]
+        else:
+            cu_host = [int(x) for x in cu_seqlens]
+    else:
+        raise ValueError("q must be [B, T, H, dk] or [T_total, H, dk]")
+    Ttot, H, dk = qf.shape
+    dv = vf.shape[-1]
+    N = len(cu_host) - 1
+    for name, t, shp in (("q", qf, (Ttot, H, dk)), ("k", kf, (Ttot, H, dk)),
+                         ("v", vf, (Ttot, H, dv)), ("log_alpha", laf, (Ttot, H, dk)),
+                         ("beta", bf, (Ttot, H)), ("gate", gf, (Ttot, H, dv))):
+        _check_dev(name, t, dt)
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shp}")
+    dev = qf.device
+    if isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.is_cuda:
+        cu_dev = cu_seqlens.to(torch.int32).contiguous()
+    else:
+        cu_dev = torch.tensor(cu_host, dtype=torch.int32, device=dev)
+    cu_h = (ctypes.c_int32 * len(cu_host))(*cu_host)
+    if initial_state is not None:
+        _check_dev("initial_state", initial_state, torch.float32)
+        if tuple(initial_state.shape) != (N, H, dk, dv):
+            raise ValueError("initial_state must be [N, H, dk, dv]")
+    if out is None:
+        out = torch.empty((Ttot, H, dv), dtype=dt, device=dev)
+    else:
+        _check_dev("out", out, dt)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    elif final_state is not None:
+        _check_dev("final_state", final_state, torch.float32)
+    p = _lib.params(_DT[dt], H, dk, dv, log_alpha_floor, scale)
+    lib = _lib.load()
+    st = lib.kda_chunk_prefill(ctypes.byref(p), _ptr(qf), _ptr(kf), _ptr(vf), _ptr(laf),
+                               _ptr(bf), _ptr(gf), _ptr(cu_dev), cu_h, N,
+                               _ptr(initial_state), _ptr(final_state), _ptr(out), _stream())
+    _lib.check(st)
+    o = out.reshape(v.shape) if q.dim() == 4 else out
+    return o, final_state
+
+
+def decode_step(q, k, v, log_alpha, beta, gate, state, log_alpha_floor: float = -0.3,
+                scale: float = 1.0, out: Optional[torch.Tensor] = None):
+    """One token per sequence; `state` (fp32 [N, H, dk, dv]) is updated in place.
+    q/k/log_alpha [N, H, dk], v/gate [N, H, dv], beta [N, H].  Returns o [N, H, dv]."""
+    dt = q.dtype
+    if dt not in _DT:
+        raise ValueError(f"unsupported dtype {dt}")
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    for name, t, shp in (("q", q, (N, H, dk)), ("k", k, (N, H, dk)), ("v", v, (N, H, dv)),
+                         ("log_alpha", log_alpha, (N, H, dk)), ("beta", beta, (N, H)),
+                         ("gate", gate, (N, H, dv))):
+        _check_dev(name, t, dt)
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shp}")
+    _check_dev("state", state, torch.float32)
+    if tuple(state.shape) != (N, H, dk, dv):
+        raise ValueError("state must be [N, H, dk, dv]")
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=dt, device=q.device)
+    p = _lib.params(_DT[dt], H, dk, dv, log_alpha_floor, scale)
+    st = _lib.load().kda_decode_step(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
+                                     _ptr(log_alpha), _ptr(beta), _ptr(gate), N,
+                                     _ptr(state), _ptr(out), _stream())
+    _lib.check(st)
+    return out

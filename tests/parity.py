@@ -1,0 +1,80 @@
+"""Shared helpers for GPU-vs-oracle parity tests.
+
+Tolerances (per tensor, o and final state checked separately):
+  bf16 inputs : max|x_gpu - x_ref| <= 2e-2 * RMS(x_ref)
+  fp32 inputs : max|x_gpu - x_ref| <= 1e-4 * RMS(x_ref)
+The oracle runs in fp64 on the exact (bf16-rounded) inputs the GPU saw.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+
+TOL = {torch.bfloat16: 2e-2, torch.float32: 1e-4}
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def rel_max_err(got, ref) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), "non-finite values in GPU output"
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    if rms == 0.0:
+        return float(np.max(np.abs(got)))
+    return float(np.max(np.abs(got - ref)) / rms)
+
+
+def assert_close(name, got, ref, dtype):
+    e = rel_max_err(got, ref)
+    log(f"  {name}: max|err|/RMS = {e:.3e} (tol {TOL[dtype]:.0e})")
+    assert e <= TOL[dtype], f"{name}: max|err|/RMS = {e:.3e} > {TOL[dtype]}"
+
+
+def host(x):
+    return None if x is None else x.detach().to("cpu", torch.float32).numpy()
+
+
+def oracle_full(x, floor=-0.3, scale=1.0, initial_state=None):
+    """Oracle on every (sequence, head) of a KdaInputs batch."""
+    S0 = x.initial_state if initial_state is None else initial_state
+    out, Sf, _ = oracle.run(host(x.q), host(x.k), host(x.v), host(x.log_alpha),
+                            host(x.beta), host(x.gate), x.cu_seqlens_host, host(S0), floor,
+                            scale)
+    return out, Sf
+
+
+def oracle_pairs(x, pairs, floor=-0.3, scale=1.0):
+    """Oracle on selected (sequence n, head h) pairs, downloading only their rows.
+
+    Returns {(n, h): (o [T_n, dv], S_T [dk, dv])}."""
+    H = x.q.shape[1]
+    qs, ks, vs, las, bs, gs, s0s, cu = [], [], [], [], [], [], [], [0]
+    for n, h in pairs:
+        a, e = x.cu_seqlens_host[n], x.cu_seqlens_host[n + 1]
+        qs.append(host(x.q[a:e, h:h + 1]))
+        ks.append(host(x.k[a:e, h:h + 1]))
+        vs.append(host(x.v[a:e, h:h + 1]))
+        las.append(host(x.log_alpha[a:e, h:h + 1]))
+        bs.append(host(x.beta[a:e, h:h + 1]))
+        gs.append(host(x.gate[a:e, h:h + 1]))
+        if x.initial_state is not None:
+            s0s.append(host(x.initial_state[n, h:h + 1]))
+        cu.append(cu[-1] + (e - a))
+    cat = lambda xs: np.concatenate(xs, axis=0)
+    S0 = None if x.initial_state is None else np.stack(s0s)  # [P, 1, dk, dv]
+    out, Sf, _ = oracle.run(cat(qs), cat(ks), cat(vs), cat(las), cat(bs), cat(gs), cu, S0,
+                            floor, scale)
+    res = {}
+    for i, (n, h) in enumerate(pairs):
+        res[(n, h)] = (out[cu[i]:cu[i + 1], 0], Sf[i, 0])
+    del H
+    return res

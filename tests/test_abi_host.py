@@ -1,0 +1,131 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared symbol, and
+rejects bad arguments before any HIP call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_attention_sequence_chunked_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+A = 1 << 20  # a fake, 16-byte aligned "device" address; never dereferenced by these calls
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_documented_entry_points():
+    assert declared_functions() == sorted(_lib.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.kda_abi_version() == 1
+
+
+def test_status_strings():
+    lib = _lib.load()
+    for s in range(4):
+        assert lib.kda_status_string(s)
+    assert lib.kda_status_string(99) == b"unknown status"
+
+
+def cu(*vals):
+    return (ctypes.c_int32 * len(vals))(*vals)
+
+
+def prefill(p=None, q=A, k=A + 0x10000, v=A + 0x20000, la=A + 0x30000, beta=A + 0x40000,
+            gate=A + 0x50000, cu_dev=A + 0x60000, cu_host=None, n=2, s0=None, sf=None,
+            out=A + 0x70000):
+    lib = _lib.load()
+    if p is None:
+        p = _lib.params(_lib.KDA_DTYPE_BF16, 2, 64, 64)
+    if cu_host is None:
+        cu_host = cu(0, 3, 5)
+    pp = ctypes.byref(p) if p is not False else None
+    st = lib.kda_chunk_prefill(pp, q, k, v, la, beta, gate, cu_dev, cu_host, n, s0, sf, out,
+                               None)
+    return st, lib.kda_last_error().decode()
+
+
+def decode(p=None, q=A, k=A + 0x10000, v=A + 0x20000, la=A + 0x30000, beta=A + 0x40000,
+           gate=A + 0x50000, n=2, state=A + 0x100000, out=A + 0x70000):
+    lib = _lib.load()
+    if p is None:
+        p = _lib.params(_lib.KDA_DTYPE_BF16, 2, 64, 64)
+    st = lib.kda_decode_step(ctypes.byref(p), q, k, v, la, beta, gate, n, state, out, None)
+    return st, lib.kda_last_error().decode()
+
+
+INV, UNS = _lib.KDA_ERR_INVALID_ARGUMENT, _lib.KDA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(p=False), INV, "params is NULL"),
+    (dict(p=_lib.params(7, 2, 64, 64)), INV, "dtype"),
+    (dict(p=_lib.params(0, 0, 64, 64)), INV, "num_heads"),
+    (dict(p=_lib.params(0, 2, 64, 64, chunk=32)), UNS, "chunk"),
+    (dict(p=_lib.params(0, 2, 96, 64)), UNS, "dk=96"),
+    (dict(p=_lib.params(0, 2, 64, 256)), UNS, "dv=256"),
+    (dict(p=_lib.params(0, 2, 64, 64, floor=0.5)), INV, "log_alpha_floor"),
+    (dict(p=_lib.params(0, 2, 64, 64, floor=-6.0)), INV, "log_alpha_floor"),
+    (dict(p=_lib.params(0, 2, 64, 64, floor=float("nan"))), INV, "log_alpha_floor"),
+    (dict(p=_lib.params(0, 2, 64, 64, scale=float("inf"))), INV, "scale"),
+    (dict(n=0), INV, "num_seqs"),
+    (dict(cu_host=False), INV, "cu_seqlens_host is NULL"),
+    (dict(cu_dev=None), INV, "cu_seqlens is NULL"),
+    (dict(cu_host=cu(1, 3, 5)), INV, "must be 0"),
+    (dict(cu_host=cu(0, 5, 3)), INV, "decreases"),
+    (dict(q=None), INV, "q is NULL"),
+    (dict(k=A + 8), INV, "k is not 16-byte aligned"),
+    (dict(gate=None), INV, "gate is NULL"),
+    (dict(beta=A + 1), INV, "beta is not 2-byte aligned"),
+    (dict(out=None), INV, "out is NULL"),
+    (dict(out=A + 0x10000), INV, "out overlaps k"),
+    (dict(s0=A + 4), INV, "initial_state is not 16-byte aligned"),
+    (dict(s0=A + 0x100000, sf=A + 0x100000 + 256), INV, "final_state overlaps initial_state"),
+    (dict(sf=A + 0x70000), INV, "final_state overlaps out"),
+    (dict(sf=A + 0x20000), INV, "final_state overlaps v"),
+])
+def test_prefill_rejects(kw, status, msg):
+    if kw.get("cu_host") is False:
+        kw["cu_host"] = None
+        lib = _lib.load()
+        p = _lib.params(_lib.KDA_DTYPE_BF16, 2, 64, 64)
+        st = lib.kda_chunk_prefill(ctypes.byref(p), A, A, A, A, A, A, A, None, 2, None, None,
+                                   A, None)
+        assert st == status
+        assert msg in lib.kda_last_error().decode()
+        return
+    st, err = prefill(**kw)
+    assert st == status, err
+    assert msg in err, err
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(p=_lib.params(0, 2, 64, 64, chunk=8)), UNS, "chunk"),
+    (dict(n=-1), INV, "num_seqs"),
+    (dict(state=None), INV, "state is NULL"),
+    (dict(state=A + 0x100008), INV, "state is not 16-byte aligned"),
+    (dict(out=A), INV, "out overlaps q"),
+    (dict(out=A + 0x100000), INV, "out overlaps state"),
+    (dict(state=A + 0x40000), INV, "state overlaps beta"),
+    (dict(v=None), INV, "v is NULL"),
+])
+def test_decode_rejects(kw, status, msg):
+    st, err = decode(**kw)
+    assert st == status, err
+    assert msg in err, err
+
+
+def test_decode_zero_sequences_is_a_no_op():
+    st, err = decode(n=0, q=None, state=None)
+    assert st == _lib.KDA_OK and err == ""

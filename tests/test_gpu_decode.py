@@ -1,0 +1,118 @@
+"""GPU parity of kda_decode_step against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import kda_inputs as ki
+import linear_attention_sequence_chunked_amd as kda
+import oracle
+from parity import assert_close, host, log
+
+pytestmark = pytest.mark.gpu
+DT = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def decode_oracle(steps_in, S0, pairs, floor=-0.3, scale=1.0):
+    """Run the oracle over the decode steps of selected (n, h) pairs as one sequence each.
+    steps_in tensors are [steps, N, H, d]; returns out [steps, P, dv], S [P, dk, dv]."""
+    steps = steps_in["q"].shape[0]
+    sel = lambda t: np.stack([host(t[:, n, h]) for n, h in pairs], axis=0)  # [P, steps, ...]
+    q, k, v, la, g = (sel(steps_in[x]) for x in ("q", "k", "v", "log_alpha", "gate"))
+    b = sel(steps_in["beta"])
+    P = len(pairs)
+    flat = lambda a: a.reshape(P * steps, 1, *a.shape[2:]) if a.ndim > 2 else a.reshape(
+        P * steps, 1)
+    S0p = np.stack([host(S0[n, h]) for n, h in pairs])[:, None]
+    out, Sf, _ = oracle.run(flat(q), flat(k), flat(v), flat(la), flat(b), flat(g),
+                            [i * steps for i in range(P + 1)], S0p, floor, scale)
+    return out.reshape(P, steps, -1).transpose(1, 0, 2), Sf[:, 0]
+
+
+def run_steps(inp, state, steps, **kw):
+    outs = []
+    for s in range(steps):
+        outs.append(kda.decode_step(inp["q"][s], inp["k"][s], inp["v"][s],
+                                    inp["log_alpha"][s], inp["beta"][s], inp["gate"][s],
+                                    state, **kw))
+    torch.cuda.synchronize()
+    return torch.stack(outs)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64), (128, 128)])
+def test_decode_small(dtype, dk, dv):
+    N, H, steps = 5, 3, 4
+    log(f"decode small dtype={dtype} dk={dk} dv={dv}")
+    inp = ki.make_decode_inputs(steps, N, H, dk, dv, dtype, seed=100 + dk + dv,
+                                device="cuda")
+    S0 = ki.make_state(N, H, dk, dv, 0.5, seed=7, device="cuda")
+    state = S0.clone()
+    out = run_steps(inp, state, steps, scale=0.8)
+    pairs = [(n, h) for n in range(N) for h in range(H)]
+    ro, rS = decode_oracle(inp, S0, pairs, scale=0.8)
+    got_o = host(out).reshape(steps, N * H, dv)
+    assert_close("o", got_o, ro, DT[dtype])
+    assert_close("S", host(state).reshape(N * H, dk, dv), rS, DT[dtype])
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128)])
+def test_decode_256_steps_match_prefill_oracle(dtype, d):
+    """256 consecutive decode steps of one sequence (H=2) equal the oracle's prefill."""
+    log(f"decode 256 steps dtype={dtype} d={d}")
+    x = ki.make_prefill_inputs((256,), 2, d, d, dtype, 0.0, seed=31, device="cuda")
+    state = torch.zeros((1, 2, d, d), dtype=torch.float32, device="cuda")
+    outs = []
+    for t in range(256):
+        outs.append(kda.decode_step(x.q[t:t + 1], x.k[t:t + 1], x.v[t:t + 1],
+                                    x.log_alpha[t:t + 1], x.beta[t:t + 1], x.gate[t:t + 1],
+                                    state))
+    torch.cuda.synchronize()
+    o = torch.cat(outs)
+    ref_o, ref_S, _ = oracle.run(host(x.q), host(x.k), host(x.v), host(x.log_alpha),
+                                 host(x.beta), host(x.gate), x.cu_seqlens_host, None)
+    assert_close("o", host(o), ref_o, DT[dtype])
+    assert_close("S", host(state), ref_S, DT[dtype])
+
+
+def test_decode_full_size_sampled():
+    """256 sequences x 32 heads, 128x128 fp32 states (537 MB), bf16 tokens: several
+    steps, sampled (sequence, head) pairs against the oracle; the rest must be finite."""
+    N, H, d, steps = 256, 32, 128, 3
+    log("decode full size 256x32 d=128 bf16")
+    inp = ki.make_decode_inputs(steps, N, H, d, d, "bf16", seed=5, device="cuda")
+    S0 = ki.make_state(N, H, d, d, 0.02, seed=5, device="cuda")
+    state = S0.clone()
+    out = run_steps(inp, state, steps)
+    pairs = [(0, 0), (17, 5), (128, 31), (255, 31), (255, 0), (99, 16)]
+    ro, rS = decode_oracle(inp, S0, pairs)
+    got_o = np.stack([host(out[:, n, h]) for n, h in pairs], axis=1)
+    got_S = np.stack([host(state[n, h]) for n, h in pairs])
+    assert_close("o", got_o, ro, torch.bfloat16)
+    assert_close("S", got_S, rS, torch.bfloat16)
+    assert torch.isfinite(state).all() and torch.isfinite(out.float()).all()
+
+
+def test_decode_deterministic_and_no_stray_writes():
+    N, H, d = 7, 4, 128
+    log("decode determinism / guards")
+    inp = ki.make_decode_inputs(1, N, H, d, d, "bf16", seed=9, device="cuda")
+    S0 = ki.make_state(N, H, d, d, 0.1, seed=9, device="cuda")
+    guard = 4096
+    results = []
+    for _ in range(2):
+        buf = torch.full((N * H * d * d + 2 * guard,), 7.25, dtype=torch.float32,
+                         device="cuda")
+        st = buf[guard:guard + N * H * d * d].view(N, H, d, d)
+        st.copy_(S0)
+        obuf = torch.full((N * H * d + 2 * guard,), float("nan"), dtype=torch.bfloat16,
+                          device="cuda")
+        o = obuf[guard:guard + N * H * d].view(N, H, d)
+        kda.decode_step(inp["q"][0], inp["k"][0], inp["v"][0], inp["log_alpha"][0],
+                        inp["beta"][0], inp["gate"][0], st, out=o)
+        torch.cuda.synchronize()
+        assert torch.all(buf[:guard] == 7.25) and torch.all(buf[-guard:] == 7.25)
+        assert torch.isnan(obuf[:guard].float()).all() and torch.isnan(obuf[-guard:].float()).all()
+        assert torch.isfinite(o.float()).all()
+        results.append((st.clone(), o.clone()))
+    assert torch.equal(results[0][0], results[1][0])
+    assert torch.equal(results[0][1], results[1][1])
