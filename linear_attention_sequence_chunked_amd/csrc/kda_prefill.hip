@@ -59,6 +59,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const KArgs<T> a) {
     constexpr int OWN = (NCB + NW - 1) / NW;  // column blocks per wave (upper bound)
     typedef Mma<T> M;
     typedef typename M::frag frag;
+    constexpr bool kSplit = sizeof(T) == 2;  // bf16 operands carry a second (low) half
 
     __shared__ __attribute__((aligned(16))) T s_q[kChunk * RS], s_k[kChunk * RS],
         s_la[kChunk * RS], s_v[kChunk * VS];
@@ -66,6 +67,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const KArgs<T> a) {
         s_Kc[kChunk * RS], s_W[kChunk * RS];
     __shared__ __attribute__((aligned(16))) T s_KhT[DK * CS], s_KbT[DK * CS];
     __shared__ __attribute__((aligned(16))) T s_T[16 * TS], s_P[16 * TS];
+    // low halves of the split operands (bf16 path): x = hi + lo to ~16 bits
+    __shared__ __attribute__((aligned(16))) T s_Ql[kSplit ? kChunk * RS : 4],
+        s_Kcl[kSplit ? kChunk * RS : 4], s_KblT[kSplit ? DK * CS : 4], s_Pl[kSplit ? 16 * TS : 4];
     __shared__ __attribute__((aligned(16))) float s_gamma[DK];
     __shared__ float s_A[16][17];
     __shared__ float s_beta[kChunk];
@@ -158,11 +162,18 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const KArgs<T> a) {
                 const float e = __expf(G[rr]), ei = __expf(-G[rr]), eb = __expf(GC - G[rr]);
                 const float qv = a.scale * to_f32(s_q[rr * RS + c]);
                 const float kv = to_f32(s_k[rr * RS + c]);
-                s_Qh[rr * RS + c] = from_f32<T>(qv * e);
+                const float qh = qv * e, kc = kv * ei, kb = kv * eb;
+                const T qh_hi = from_f32<T>(qh), kc_hi = from_f32<T>(kc), kb_hi = from_f32<T>(kb);
+                s_Qh[rr * RS + c] = qh_hi;
                 s_Kh[rr * RS + c] = from_f32<T>(kv * e);
-                s_Kc[rr * RS + c] = from_f32<T>(kv * ei);
+                s_Kc[rr * RS + c] = kc_hi;
                 s_KhT[c * CS + rr] = from_f32<T>(kv * e);
-                s_KbT[c * CS + rr] = from_f32<T>(kv * eb);
+                s_KbT[c * CS + rr] = kb_hi;
+                if constexpr (kSplit) {
+                    s_Ql[rr * RS + c] = from_f32<T>(qh - to_f32(qh_hi));
+                    s_Kcl[rr * RS + c] = from_f32<T>(kc - to_f32(kc_hi));
+                    s_KblT[c * CS + rr] = from_f32<T>(kb - to_f32(kb_hi));
+                }
             }
         }
         __syncthreads();
@@ -179,16 +190,25 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const KArgs<T> a) {
                 const int row = 4 * g + i;  // acc[i] = (Kh Kc^T)[row][r]
                 s_A[row][r] = r < row ? s_beta[row] * acc[i] : 0.f;
             }
-        } else if (wave == 1) {  // P = lower_incl_diag(Qh Kc^T)
+        } else if (wave == 1) {  // P = lower_incl_diag(Qh Kc^T), split operands
             f32x4 acc = zero4();
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-                acc = M::run(load4(&s_Qh[r * RS + 16 * kb + 4 * g]),
-                             load4(&s_Kc[r * RS + 16 * kb + 4 * g]), acc);
+            for (int kb = 0; kb < KB; ++kb) {
+                const frag qh = load4(&s_Qh[r * RS + 16 * kb + 4 * g]);
+                const frag kc = load4(&s_Kc[r * RS + 16 * kb + 4 * g]);
+                acc = M::run(qh, kc, acc);
+                if constexpr (kSplit) {
+                    acc = M::run(qh, load4(&s_Kcl[r * RS + 16 * kb + 4 * g]), acc);
+                    acc = M::run(load4(&s_Ql[r * RS + 16 * kb + 4 * g]), kc, acc);
+                }
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 4 * g + i;
-                s_P[row * TS + r] = from_f32<T>(r <= row ? acc[i] : 0.f);
+                const float pv = r <= row ? acc[i] : 0.f;
+                const T hi = from_f32<T>(pv);
+                s_P[row * TS + r] = hi;
+                if constexpr (kSplit) s_Pl[row * TS + r] = from_f32<T>(pv - to_f32(hi));
             }
         }
         __syncthreads();
@@ -247,11 +267,27 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const KArgs<T> a) {
                 O = M::run(load4(&s_Qh[r * RS + 16 * b + 4 * g]), Sb[b], O);   // O = Qh S
             }
             const frag Ub = M::pack(U);
-            O = M::run(load4(&s_P[r * TS + 4 * g]), Ub, O);                     // O += P U
+            const frag Ph = load4(&s_P[r * TS + 4 * g]);
+            O = M::run(Ph, Ub, O);                                               // O += P U
+            frag Ul;
+            if constexpr (kSplit) {
+                Ul = M::pack(U - f32x4{to_f32(Ub[0]), to_f32(Ub[1]), to_f32(Ub[2]), to_f32(Ub[3])});
+                O = M::run(Ph, Ul, O);
+                O = M::run(load4(&s_Pl[r * TS + 4 * g]), Ub, O);
+#pragma unroll
+                for (int b = 0; b < KB; ++b)
+                    O = M::run(load4(&s_Ql[r * RS + 16 * b + 4 * g]), Sb[b], O);  // lo(Qh) S
+            }
 #pragma unroll
             for (int b = 0; b < KB; ++b) {
                 const f32x4 gam = *reinterpret_cast<const f32x4*>(&s_gamma[16 * b + 4 * g]);
-                S[jj][b] = M::run(load4(&s_KbT[(16 * b + r) * CS + 4 * g]), Ub, S[jj][b] * gam);
+                const frag kbh = load4(&s_KbT[(16 * b + r) * CS + 4 * g]);
+                f32x4 acc = M::run(kbh, Ub, S[jj][b] * gam);
+                if constexpr (kSplit) {
+                    acc = M::run(kbh, Ul, acc);
+                    acc = M::run(load4(&s_KblT[(16 * b + r) * CS + 4 * g]), Ub, acc);
+                }
+                S[jj][b] = acc;
             }
             const int col = col0 + 16 * j + r;
 #pragma unroll
