@@ -37,6 +37,9 @@ struct PrefillArgs {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+// bf16 path (kda_prefill_bf16.hip) and the value-slice widths it implements
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
+bool prefill_bf16_supports(int dk, int dv, int nv);
 
 // value-slice width the prefill would pick for this problem (exposed for tests)
 int prefill_pick_nv(int dv, int64_t num_pairs, int64_t longest_chunks, int cu_count);

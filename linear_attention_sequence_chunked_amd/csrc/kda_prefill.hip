@@ -1,4 +1,6 @@
-// kda_prefill.hip -- chunked KDA prefill over packed varlen sequences (gfx950).
+// kda_prefill.hip -- chunked KDA prefill over packed varlen sequences (gfx950): the
+// fp32-input path (fp32 MFMA throughout) and the dispatch; bf16 inputs run the
+// pipelined kernel of kda_prefill_bf16.hip.
 //
 // Chunked form (16-token chunks; per chunk of C' <= 16 rows, G_r = sum_{s<=r}
 // max(lambda_s, floor) inclusive, G_C = G_{C'}):
@@ -359,14 +361,20 @@ hipError_t launch_dims(const PrefillArgs& p, hipStream_t st) {
 
 int prefill_pick_nv(int dv, int64_t num_pairs, int64_t longest_chunks, int cu_count) {
     (void)longest_chunks;
-    // enough workgroups to cover the chip twice, never narrower than 16 columns
+    // one workgroup per compute unit at a time (the bf16 kernel holds ~130 KB of LDS):
+    // split the value columns until the (sequence, head) pairs cover every unit once
     int slices = 1;
-    while (slices < dv / 16 && num_pairs * slices < 2LL * cu_count) slices *= 2;
+    while (slices < dv / 16 && num_pairs * slices < (int64_t)cu_count) slices *= 2;
     return dv / slices;
 }
 
 hipError_t launch_prefill(const PrefillArgs& p, hipStream_t st) {
-    return p.dtype == DTYPE_BF16 ? launch_dims<bf16>(p, st) : launch_dims<float>(p, st);
+    if (p.dtype == DTYPE_BF16) {
+        PrefillArgs q = p;
+        while (!prefill_bf16_supports(q.dk, q.dv, q.nv) && q.nv > 16) q.nv /= 2;
+        return launch_prefill_bf16(q, st);
+    }
+    return launch_dims<float>(p, st);
 }
 
 }  // namespace kda

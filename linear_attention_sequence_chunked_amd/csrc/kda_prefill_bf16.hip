@@ -1,0 +1,572 @@
+// kda_prefill_bf16.hip -- chunked KDA prefill, bf16 inputs, fp32 state (gfx950).
+//
+// Chunked form used here, per 16-token chunk (rows r; G_r = sum_{s<=r} max(lambda_s, floor),
+// inclusive; G_C its value at the chunk's last row; gamma = e^{G_C} per key channel):
+//   Qt = (scale q) e^{G - G_C},  Kt = k e^{G - G_C},  Kb = k e^{G_C - G}
+//   A  = strict_lower(Diag(beta) Kt Kb^T),   T = (I + A)^-1 Diag(beta)
+//   P  = lower_incl_diag(Qt Kb^T),           Wt = T Kt,   Ut = T V
+//   S' = Diag(gamma) S;   U = Ut - Wt S';   O = Qt S' + P U;   S <- S' + Kb^T U;  o = gate*O
+// This equals the token recurrence exactly in exact arithmetic (rows of the chunk unroll
+// into (I + A) U = Diag(beta) (V - Kt S')).  Because the per-step log-decay has a lower
+// bound, e^{G - G_C} <= e^{16 |floor|} inside a chunk, so the causal 16x16 block is a
+// dense matrix-core product instead of a per-position-pair computation (digest of
+// "Kimi K3: Open Frontier Intelligence", section "KDA：百万上下文先要过「数值 算子」这一关",
+// Fig. 3; the transition (I - beta k k^T) Diag(alpha) is the DPLR form of "Kimi K3
+// 深度拆解" 突破一).  Key-side work of later chunks runs while the state step of the
+// current chunk runs (same digest, section "基础设施": intra-chunk work overlapped with
+// inter-chunk state propagation).
+//
+// Precision.  Products whose bf16 rounding would cost accuracy carry a second bf16 half
+// (x = hi + lo, ~16 significant bits): P and the Qt/Kb it is built from, the chunk's
+// writes U, Kb in the state update, and Qt in the readout.  The fp32 state is kept in
+// MFMA accumulators; its bf16 copy only feeds the Wt S' and Qt S' products.
+//
+// Workgroup = one (sequence, head, slice of NV = 16*NCB value columns).  Waves:
+//   chain  (NCB)   : one 16-column block of S each; state step of chunk c
+//   decay  (DK/16) : one 16-channel block each; operands of chunk c+3, from registers
+//                    loaded four chunks earlier
+//   gram           : A, A^T of chunk c+2 and T through the nilpotent product
+//                    (I+A)^-1 = (I-A)(I+A^2)(I+A^4)(I+A^8)  (A^16 = 0), all in registers
+//   pw             : P of chunk c+2, then Wt of chunk c+1
+// One barrier per iteration; LDS rings carry each product from its producer to its
+// consumers.
+//
+// MFMA fragment conventions (lane l: r = l & 15, g = l >> 4):
+//   C(M) / B-fragment of M : M[4g + i][r]   (i = 0..3)
+//   A-fragment of M        : M[r][4g + i]   == C(M^T)
+//   v_mfma_f32_16x16x16_bf16(Afrag(L), Bfrag(R)) = C(L R)
+//   A 32-deep step pairs element j of the A operand with element j of the B operand on
+//   each lane, so two 16-deep operands can be stacked into one 32-deep one.
+#include <math.h>
+
+#include <type_traits>
+
+#include "kda_device.h"
+#include "kda_launch.h"
+
+namespace kda {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// A 32-deep product issued as two 16-deep ones.  v_mfma_f32_16x16x32_bf16 gives wrong
+// results with this toolchain when a register of its A/B operand is rewritten by the next
+// few instructions (the scheduler does so freely; reproduced on gfx950: the 16x16x32 form
+// reads its upper operand half after issue and no wait states are inserted).  The pair of
+// 16-deep instructions computes the same sum with the same operand pairing.
+__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
+    const bf16x4 a0{a[0], a[1], a[2], a[3]}, a1{a[4], a[5], a[6], a[7]};
+    const bf16x4 b0{b[0], b[1], b[2], b[3]}, b1{b[4], b[5], b[6], b[7]};
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a0, b0, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a1, b1, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
+    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+__device__ __forceinline__ bf16x4 to_bf4(f32x4 x) {
+    return bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
+}
+__device__ __forceinline__ f32x4 to_f4(bf16x4 x) {
+    return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+}
+// x = hi + lo, each bf16 (hi round-to-nearest-even, lo the rounded remainder)
+__device__ __forceinline__ void split4(f32x4 x, bf16x4& hi, bf16x4& lo) {
+    hi = to_bf4(x);
+    lo = to_bf4(x - to_f4(hi));
+}
+// C(L R) to ~16 bits from fp32 operands given as A-fragment of L (== C(L^T)) and C(R)
+__device__ __forceinline__ f32x4 prod3(f32x4 aL, f32x4 cR) {
+    bf16x4 lh, ll, rh, rl;
+    split4(aL, lh, ll);
+    split4(cR, rh, rl);
+    f32x4 acc = mfma32(cat8(lh, lh), cat8(rh, rl), zero4());
+    return mfma16(ll, rh, acc);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                 CTRL, 0xF, 0xF, true));
+}
+// inclusive prefix sum over the 16 lanes of each DPP row
+__device__ __forceinline__ float row_scan(float x) {
+    x += dpp<0x111>(x);
+    x += dpp<0x112>(x);
+    x += dpp<0x114>(x);
+    x += dpp<0x118>(x);
+    return x;
+}
+__device__ __forceinline__ float row_last(float x) { return dpp<0x15F>(x); }  // lane 15 of row
+
+__device__ __forceinline__ f32x4 unpack_bf4(u32x2 w) {
+    return f32x4{__builtin_bit_cast(float, w[0] << 16), __builtin_bit_cast(float, w[0] & 0xffff0000u),
+                 __builtin_bit_cast(float, w[1] << 16), __builtin_bit_cast(float, w[1] & 0xffff0000u)};
+}
+
+template <int DK, int NCB>
+struct Cfg {
+    static constexpr int KB = DK / 16;        // 16-channel blocks (= decay waves)
+    static constexpr int KP = DK / 32;        // 32-channel steps of the state products
+    static constexpr int NCHAIN = NCB;
+    static constexpr int W_DECAY0 = NCHAIN;
+    static constexpr int W_GRAM = NCHAIN + KB;
+    static constexpr int W_PW = W_GRAM + 1;   // P of chunk c+2, then Wt of chunk c+1
+    static constexpr int NWAVES = W_GRAM + 2;
+    static constexpr int THREADS = 64 * NWAVES;
+    // row-major [16][DK] bf16 tiles, padded rows (bytes)
+    static constexpr int RSB = DK * 2 + 16;
+    static constexpr int ROWT = 16 * RSB;
+    // long ring (4): Qt hi, Qt lo rows; Kb^T hi/lo fragments; gamma; value and gate
+    // fragments C(V block), C(gate block) of each 16-column block
+    static constexpr int L_QH = 0, L_QL = ROWT, L_KBH = 2 * ROWT, L_KBL = L_KBH + KB * 512,
+                         L_GAM = L_KBL + KB * 512, L_VG = L_GAM + DK * 4,
+                         L_SIZE = L_VG + 2 * NCB * 512;
+    // value/gate fragment sets staged per decay wave (set f: block f >> 1, gate if f & 1)
+    static constexpr int VG_PER_WAVE = (2 * NCB + KB - 1) / KB;
+    // short ring (2): Kt, Kb hi, Kb lo rows; beta
+    static constexpr int S_KT = 0, S_KBH = ROWT, S_KBL = 2 * ROWT, S_BETA = 3 * ROWT,
+                         S_SIZE = 3 * ROWT + 64;
+    // mid ring (3): Kt^T fragments
+    static constexpr int M_KTT = 0, M_SIZE = KB * 512;
+    // gram ring (3): T^T fragment (C(T^T) = A-fragment of T), P hi/lo A-fragments
+    static constexpr int G_TT = 0, G_PH = 512, G_PL = 1024, G_SIZE = 1536;
+    // wgen ring (2): -Wt A-fragments for 32-deep steps
+    static constexpr int W_WT = 0, W_SIZE = KP * 1024;
+    static constexpr int OFF_L = 0, OFF_S = OFF_L + 4 * L_SIZE, OFF_M = OFF_S + 2 * S_SIZE,
+                         OFF_G = OFF_M + 3 * M_SIZE, OFF_W = OFF_G + 3 * G_SIZE,
+                         LDS_BYTES = OFF_W + 2 * W_SIZE;
+};
+
+struct BArgs {
+    const bf16 *q, *k, *v, *la, *beta, *gate;
+    const int32_t* cu;
+    const float* S0;
+    float* Sf;
+    bf16* out;
+    int H, n_slices, num_groups, groups_padded, num_ordered;
+    float floor_, scale;
+    int32_t order[kMaxOrdered];
+};
+
+template <int DK, int DV, int NCB>
+__global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(const BArgs a) {
+    typedef Cfg<DK, NCB> C;
+    constexpr int KB = C::KB, KP = C::KP, NV = 16 * NCB;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int r = lane & 15, g = lane >> 4;
+
+    // blockIdx -> (group, slice): the slices of one (sequence, head) share an XCD
+    // (consecutive workgroup ids go round-robin over the 8 XCDs), groups in launch order
+    const int xcd = blockIdx.x & 7, kk = blockIdx.x >> 3;
+    const int group = (kk / a.n_slices) * 8 + xcd;
+    const int slice = kk % a.n_slices;
+    if (group >= a.num_groups) return;
+    const int H = a.H, seq_pos = group / H, h = group % H;
+    const int seq = a.num_ordered ? a.order[seq_pos] : seq_pos;
+    const int64_t tbeg = a.cu[seq], tend = a.cu[seq + 1];
+    const int nch = (int)((tend - tbeg + 15) / 16);
+    const int col0 = slice * NV;
+    const int64_t rowq = (int64_t)H * DK, rowv = (int64_t)H * DV;
+    const int64_t sbase = ((int64_t)seq * H + h) * DK * DV;
+
+    auto lslot = [&](int c) { return smem + C::OFF_L + (c & 3) * C::L_SIZE; };
+    auto sslot = [&](int c) { return smem + C::OFF_S + (c & 1) * C::S_SIZE; };
+    auto mslot = [&](int c) { return smem + C::OFF_M + (c % 3) * C::M_SIZE; };
+    auto gslot = [&](int c) { return smem + C::OFF_G + (c % 3) * C::G_SIZE; };
+    auto wslot = [&](int c) { return smem + C::OFF_W + (c & 1) * C::W_SIZE; };
+
+    const bool is_chain = wave < C::NCHAIN;
+    const bool is_decay = wave >= C::W_DECAY0 && wave < C::W_GRAM;
+    const int cb = wave - C::W_DECAY0;  // decay: channel block
+
+    // ---------------------------------------------------------------- loop-carried registers
+    // One register array carries the state of whichever role this wave has, so the
+    // per-thread register budget is the larger role's, not the sum of all roles:
+    //   chain: [0, 4KB) fp32 state S (rows 16b+4g+i, column ccol); [4KB, 4KB+4KP) bf16 S'
+    //          as 32-deep B operands
+    //   decay: four prefetched (q, k, log_alpha) fragments, beta values and value/gate
+    //          row fragments
+    constexpr int R_SB = 4 * KB, R_CH = R_SB + 4 * KP;
+    constexpr int D_Q = 0, D_K = 8, D_L = 16, D_B = 24, D_VG = 28,
+                  D_N = D_VG + 8 * C::VG_PER_WAVE;
+    constexpr int R_N = R_CH > D_N ? R_CH : D_N;
+    // (integer storage: round-tripping integer data through a float array miscompiles
+    // with this toolchain -- the second dword of a pair is read back as the first)
+    uint32_t R[R_N];
+#pragma unroll
+    for (int i = 0; i < R_N; ++i) R[i] = 0u;
+    auto fl = [](uint32_t x) { return __builtin_bit_cast(float, x); };
+    auto ui = [](float x) { return __builtin_bit_cast(uint32_t, x); };
+    auto getS = [&](int b) {
+        return f32x4{fl(R[4 * b]), fl(R[4 * b + 1]), fl(R[4 * b + 2]), fl(R[4 * b + 3])};
+    };
+    auto setS = [&](int b, f32x4 x) {
+        R[4 * b] = ui(x[0]); R[4 * b + 1] = ui(x[1]); R[4 * b + 2] = ui(x[2]); R[4 * b + 3] = ui(x[3]);
+    };
+    auto getSb = [&](int p) {
+        const int o = R_SB + 4 * p;
+        return __builtin_bit_cast(bf16x8, u32x4{R[o], R[o + 1], R[o + 2], R[o + 3]});
+    };
+    auto setSb = [&](int p, bf16x8 x) {
+        const u32x4 f = __builtin_bit_cast(u32x4, x);
+        const int o = R_SB + 4 * p;
+        R[o] = f[0]; R[o + 1] = f[1]; R[o + 2] = f[2]; R[o + 3] = f[3];
+    };
+    auto get2 = [&](int o) { return u32x2{R[o], R[o + 1]}; };
+    auto set2 = [&](int o, u32x2 x) { R[o] = x[0]; R[o + 1] = x[1]; };
+
+    const int ccol = col0 + 16 * wave + r;  // chain wave's value column
+    const int dch = 16 * cb + 4 * g;  // decay wave's first channel
+    auto load_qkl = [&](int c, int slot) {
+        u32x2 qq{0u, 0u}, kq{0u, 0u}, lq{0u, 0u};
+        float bq = 0.f;
+        if (c < nch) {
+            const int64_t t0 = tbeg + 16 * c;
+            if (t0 + r < tend) {
+                const int64_t off = (t0 + r) * rowq + (int64_t)h * DK + dch;
+                qq = *reinterpret_cast<const u32x2*>(a.q + off);
+                kq = *reinterpret_cast<const u32x2*>(a.k + off);
+                lq = *reinterpret_cast<const u32x2*>(a.la + off);
+                bq = (float)a.beta[(t0 + r) * H + h];
+            }
+        }
+        set2(D_Q + 2 * slot, qq);
+        set2(D_K + 2 * slot, kq);
+        set2(D_L + 2 * slot, lq);
+        R[D_B + slot] = ui(bq);
+        // value / gate rows of this wave's fragment sets: token r, columns +4g..+3
+#pragma unroll
+        for (int e = 0; e < C::VG_PER_WAVE; ++e) {
+            const int f = cb + KB * e;
+            u32x2 x{0u, 0u};
+            if (f < 2 * NCB && c < nch) {
+                const int64_t t0 = tbeg + 16 * c;
+                if (t0 + r < tend) {
+                    const bf16* src = (f & 1) ? a.gate : a.v;
+                    x = *reinterpret_cast<const u32x2*>(
+                        src + (t0 + r) * rowv + (int64_t)h * DV + col0 + 16 * (f >> 1) + 4 * g);
+                }
+            }
+            set2(D_VG + 8 * e + 2 * slot, x);
+        }
+    };
+
+    if (is_chain) {
+#pragma unroll
+        for (int b = 0; b < KB; ++b) {
+            f32x4 x;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                x[i] = a.S0 ? a.S0[sbase + (16 * b + 4 * g + i) * DV + ccol] : 0.f;
+            setS(b, x);
+        }
+    } else if (is_decay) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) load_qkl(c, (c + 1) & 3);
+    }
+    // identity as a B fragment (for exact register transposes through the matrix core)
+    bf16x4 ident;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ident[i] = (bf16)((4 * g + i) == r ? 1.f : 0.f);
+
+    const float floor2 = a.floor_;
+
+    // ---------------------------------------------------------------- one iteration
+    auto body = [&](const int it, auto PH) {
+        constexpr int ph = decltype(PH)::value;
+        if (is_decay) {
+            // ---- decay-folded operands of chunk it + 3 (row layout: token r, channels dch..+3)
+            const int c = it + 3;
+            if (c < nch) {
+                const f32x4 q4 = unpack_bf4(get2(D_Q + 2 * ph)) * a.scale;
+                const f32x4 k4 = unpack_bf4(get2(D_K + 2 * ph));
+                const f32x4 l4 = unpack_bf4(get2(D_L + 2 * ph));
+                const float bet = fl(R[D_B + ph]);
+                f32x4 F, Fi, gam;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float lam = fmaxf(l4[i], floor2);
+                    const float G = row_scan(lam);          // inclusive cumsum over tokens
+                    const float GC = row_last(G);           // chunk total (rows >= C' add 0)
+                    const float d = (G - GC) * kLog2e;      // >= 0
+                    F[i] = __builtin_amdgcn_exp2f(d);
+                    Fi[i] = __builtin_amdgcn_exp2f(-d);
+                    gam[i] = GC;
+                }
+                const f32x4 qt = q4 * F, kt = k4 * F, kb = k4 * Fi;
+                bf16x4 qh, ql, kbh, kbl;
+                split4(qt, qh, ql);
+                split4(kb, kbh, kbl);
+                const bf16x4 kth = to_bf4(kt);
+                unsigned char* L = lslot(c);
+                unsigned char* Sh = sslot(c);
+                const int rowoff = r * C::RSB + 2 * dch;
+                *reinterpret_cast<bf16x4*>(L + C::L_QH + rowoff) = qh;
+                *reinterpret_cast<bf16x4*>(L + C::L_QL + rowoff) = ql;
+                *reinterpret_cast<bf16x4*>(Sh + C::S_KT + rowoff) = kth;
+                *reinterpret_cast<bf16x4*>(Sh + C::S_KBH + rowoff) = kbh;
+                *reinterpret_cast<bf16x4*>(Sh + C::S_KBL + rowoff) = kbl;
+                // transposed fragments through the matrix core (exact: products with 1)
+                const bf16x4 kbth = to_bf4(mfma16(kbh, ident, zero4()));
+                const bf16x4 kbtl = to_bf4(mfma16(kbl, ident, zero4()));
+                const bf16x4 ktt = to_bf4(mfma16(kth, ident, zero4()));
+                *reinterpret_cast<bf16x4*>(L + C::L_KBH + cb * 512 + lane * 8) = kbth;
+                *reinterpret_cast<bf16x4*>(L + C::L_KBL + cb * 512 + lane * 8) = kbtl;
+                *reinterpret_cast<bf16x4*>(mslot(c) + C::M_KTT + cb * 512 + lane * 8) = ktt;
+                if (r == 0) {
+                    f32x4 e;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) e[i] = __builtin_amdgcn_exp2f(gam[i] * kLog2e);
+                    *reinterpret_cast<f32x4*>(L + C::L_GAM + 4 * dch) = e;
+                }
+                if (cb == 0 && g == 0) *reinterpret_cast<float*>(Sh + C::S_BETA + 4 * r) = bet;
+#pragma unroll
+                for (int e = 0; e < C::VG_PER_WAVE; ++e) {
+                    const int f = cb + KB * e;
+                    if (f < 2 * NCB) {
+                        const bf16x4 x = __builtin_bit_cast(bf16x4, get2(D_VG + 8 * e + 2 * ph));
+                        const bf16x4 xt = to_bf4(mfma16(x, ident, zero4()));  // C(block)
+                        *reinterpret_cast<bf16x4*>(L + C::L_VG + f * 512 + lane * 8) = xt;
+                    }
+                }
+            }
+            load_qkl(it + 7, ph);
+        } else if (wave == C::W_GRAM) {
+            // ---- A, A^T of chunk it + 2 and T = (I + A)^-1 Diag(beta), kept as C(T^T)
+            const int c = it + 2;
+            if (c >= 0 && c < nch) {
+                const unsigned char* Sh = sslot(c);
+                f32x4 ac = zero4(), atc = zero4();
+#pragma unroll
+                for (int p = 0; p < KP; ++p) {
+                    const int off = r * C::RSB + 2 * (32 * p + 8 * g);
+                    const bf16x8 kt = *reinterpret_cast<const bf16x8*>(Sh + C::S_KT + off);
+                    const bf16x8 kb = *reinterpret_cast<const bf16x8*>(Sh + C::S_KBH + off);
+                    ac = mfma32(kt, kb, ac);    // C(Kt Kb^T)
+                    atc = mfma32(kb, kt, atc);  // C(Kb Kt^T)
+                }
+                const float* beta = reinterpret_cast<const float*>(Sh + C::S_BETA);
+                const float br = beta[r];
+                const f32x4 bi = *reinterpret_cast<const f32x4*>(beta + 4 * g);
+                f32x4 cA, cAT;  // C(A), C(A^T)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 4 * g + i;
+                    cA[i] = r < row ? bi[i] * ac[i] : 0.f;
+                    cAT[i] = row < r ? br * atc[i] : 0.f;
+                }
+                // A-fragment(X) == C(X^T): powers of A and of A^T in both layouts
+                const f32x4 cA2 = prod3(cAT, cA);      // C(A A)
+                const f32x4 cAT2 = prod3(cA, cAT);     // C(A^T A^T)
+                const f32x4 cA4 = prod3(cAT2, cA2);
+                const f32x4 cAT4 = prod3(cA2, cAT2);
+                const f32x4 cAT8 = prod3(cA4, cAT4);
+                f32x4 y = cAT8;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) y[i] += (4 * g + i) == r ? 1.f : 0.f;  // I + (A^T)^8
+                y += prod3(cA4, y);   // (I + (A^T)^4) y
+                y += prod3(cA2, y);   // (I + (A^T)^2) y
+                y -= prod3(cA, y);    // (I - A^T) y   ->  X^T = ((I + A)^-1)^T
+                const bf16x4 tt = to_bf4(y * bi);  // C(T^T): row 4g+i of X^T scaled by beta
+                *reinterpret_cast<bf16x4*>(gslot(c) + C::G_TT + lane * 8) = tt;
+            }
+        } else if (wave == C::W_PW) {
+          {
+            // ---- P of chunk it + 2, as A-fragments hi/lo: C(P^T) = C(Kb Qt^T)
+            const int c = it + 2;
+            if (c >= 0 && c < nch) {
+                const unsigned char* Sh = sslot(c);
+                const unsigned char* L = lslot(c);
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int p = 0; p < KP; ++p) {
+                    const int off = r * C::RSB + 2 * (32 * p + 8 * g);
+                    const bf16x8 kbh = *reinterpret_cast<const bf16x8*>(Sh + C::S_KBH + off);
+                    const bf16x8 kbl = *reinterpret_cast<const bf16x8*>(Sh + C::S_KBL + off);
+                    const bf16x8 qh = *reinterpret_cast<const bf16x8*>(L + C::L_QH + off);
+                    const bf16x8 ql = *reinterpret_cast<const bf16x8*>(L + C::L_QL + off);
+                    acc = mfma32(kbh, qh, acc);
+                    acc = mfma32(kbh, ql, acc);
+                    acc = mfma32(kbl, qh, acc);
+                }
+                // acc[i] = P[r][4g+i]; keep the causal part (key position <= query position)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] = (4 * g + i) <= r ? acc[i] : 0.f;
+                bf16x4 ph_, pl_;
+                split4(acc, ph_, pl_);
+                *reinterpret_cast<bf16x4*>(gslot(c) + C::G_PH + lane * 8) = ph_;
+                *reinterpret_cast<bf16x4*>(gslot(c) + C::G_PL + lane * 8) = pl_;
+            }
+          }
+          {
+            // ---- -Wt of chunk it + 1 as 32-deep A-fragments: C(Wt^T) blocks = Kt^T T^T
+            const int c = it + 1;
+            if (c >= 0 && c < nch) {
+                const bf16x4 tt = *reinterpret_cast<const bf16x4*>(gslot(c) + C::G_TT + lane * 8);
+                const unsigned char* M = mslot(c);
+                unsigned char* W = wslot(c);
+#pragma unroll
+                for (int nb = 0; nb < KB; ++nb) {
+                    const bf16x4 ktt = *reinterpret_cast<const bf16x4*>(M + C::M_KTT + nb * 512 + lane * 8);
+                    const f32x4 w = mfma16(ktt, tt, zero4());  // w[i] = Wt[r][16nb + 4g + i]
+                    *reinterpret_cast<bf16x4*>(W + C::W_WT + (nb >> 1) * 1024 + lane * 16 + (nb & 1) * 8) =
+                        to_bf4(-w);
+                }
+            }
+          }
+        } else if (is_chain) {
+            // ---- state step of chunk it for value columns col0 + 16*wave .. +15
+            const int c = it;
+            if (c >= 0 && c < nch) {
+                const unsigned char* L = lslot(c);
+                const unsigned char* Gs = gslot(c);
+                const unsigned char* W = wslot(c);
+                // Ut = T V
+                const bf16x4 tt = *reinterpret_cast<const bf16x4*>(Gs + C::G_TT + lane * 8);
+                const bf16x4 vb = *reinterpret_cast<const bf16x4*>(L + C::L_VG + (2 * wave) * 512 + lane * 8);
+                f32x4 U = mfma16(tt, vb, zero4());
+                f32x4 O = zero4();
+#pragma unroll
+                for (int p = 0; p < KP; ++p) {
+                    const bf16x8 w = *reinterpret_cast<const bf16x8*>(W + C::W_WT + p * 1024 + lane * 16);
+                    U = mfma32(w, getSb(p), U);  // U = Ut - Wt S'
+                }
+#pragma unroll
+                for (int p = 0; p < KP; ++p) {
+                    const int off = r * C::RSB + 2 * (32 * p + 4 * g);
+                    const bf16x4 q0 = *reinterpret_cast<const bf16x4*>(L + C::L_QH + off);
+                    const bf16x4 q1 = *reinterpret_cast<const bf16x4*>(L + C::L_QH + off + 32);
+                    const bf16x4 l0 = *reinterpret_cast<const bf16x4*>(L + C::L_QL + off);
+                    const bf16x4 l1 = *reinterpret_cast<const bf16x4*>(L + C::L_QL + off + 32);
+                    O = mfma32(cat8(q0, q1), getSb(p), O);  // Qt S'
+                    O = mfma32(cat8(l0, l1), getSb(p), O);
+                }
+                bf16x4 uh, ul;
+                split4(U, uh, ul);
+                const bf16x8 u8 = cat8(uh, ul);
+                const bf16x4 ph_ = *reinterpret_cast<const bf16x4*>(Gs + C::G_PH + lane * 8);
+                const bf16x4 pl_ = *reinterpret_cast<const bf16x4*>(Gs + C::G_PL + lane * 8);
+                O = mfma32(cat8(ph_, ph_), u8, O);  // + P U
+                O = mfma16(pl_, uh, O);
+                // S <- S' + Kb^T U, row block by row block; then S' of the next chunk
+                const bool last = c + 1 >= nch;
+                const float* gn = reinterpret_cast<const float*>(lslot(c + 1) + C::L_GAM);
+#pragma unroll
+                for (int b = 0; b < KB; ++b) {
+                    const bf16x4 kh = *reinterpret_cast<const bf16x4*>(L + C::L_KBH + b * 512 + lane * 8);
+                    const bf16x4 kl = *reinterpret_cast<const bf16x4*>(L + C::L_KBL + b * 512 + lane * 8);
+                    f32x4 s = mfma32(cat8(kh, kh), u8, getS(b));
+                    s = mfma16(kl, uh, s);
+                    setS(b, s);
+                }
+                // gated output rows of this chunk
+                const int64_t t0 = tbeg + 16 * c;
+                const int cp = (int)min<int64_t>(16, tend - t0);
+                const f32x4 gt = to_f4(*reinterpret_cast<const bf16x4*>(L + C::L_VG + (2 * wave + 1) * 512 + lane * 8));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 4 * g + i;
+                    if (row < cp) a.out[(t0 + row) * rowv + (int64_t)h * DV + ccol] = (bf16)(gt[i] * O[i]);
+                }
+                if (!last) {
+#pragma unroll
+                    for (int b = 0; b < KB; ++b)
+                        setS(b, getS(b) * *reinterpret_cast<const f32x4*>(gn + 16 * b + 4 * g));
+#pragma unroll
+                    for (int p = 0; p < KP; ++p) setSb(p, cat8(to_bf4(getS(2 * p)), to_bf4(getS(2 * p + 1))));
+                }
+            } else if (c == -1 && nch > 0) {
+                // S' of chunk 0
+                const float* g0 = reinterpret_cast<const float*>(lslot(0) + C::L_GAM);
+#pragma unroll
+                for (int b = 0; b < KB; ++b)
+                    setS(b, getS(b) * *reinterpret_cast<const f32x4*>(g0 + 16 * b + 4 * g));
+#pragma unroll
+                for (int p = 0; p < KP; ++p) setSb(p, cat8(to_bf4(getS(2 * p)), to_bf4(getS(2 * p + 1))));
+            }
+        }
+        __syncthreads();
+    };
+
+    // iterations it = -3 .. nch-1; prefetch slot = (it + 4) & 3 (compile-time per unrolled body)
+    int it = -3;
+    while (it < nch) {
+        body(it, std::integral_constant<int, 1>{});
+        if (++it >= nch) break;
+        body(it, std::integral_constant<int, 2>{});
+        if (++it >= nch) break;
+        body(it, std::integral_constant<int, 3>{});
+        if (++it >= nch) break;
+        body(it, std::integral_constant<int, 0>{});
+        ++it;
+    }
+
+    if (is_chain && a.Sf) {
+#pragma unroll
+        for (int b = 0; b < KB; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a.Sf[sbase + (16 * b + 4 * g + i) * DV + ccol] = fl(R[4 * b + i]);
+    }
+}
+
+template <int DK, int DV, int NCB>
+hipError_t launch_bf16(const PrefillArgs& p, hipStream_t st) {
+    typedef Cfg<DK, NCB> C;
+    static_assert(C::LDS_BYTES <= 160 * 1024, "LDS budget");
+    BArgs a;
+    a.q = (const bf16*)p.q; a.k = (const bf16*)p.k; a.v = (const bf16*)p.v;
+    a.la = (const bf16*)p.log_alpha; a.beta = (const bf16*)p.beta; a.gate = (const bf16*)p.gate;
+    a.cu = p.cu_seqlens; a.S0 = p.initial_state; a.Sf = p.final_state; a.out = (bf16*)p.out;
+    a.H = p.H; a.n_slices = DV / (16 * NCB); a.num_groups = p.num_seqs * p.H;
+    a.groups_padded = (a.num_groups + 7) / 8 * 8;
+    a.num_ordered = p.num_ordered; a.floor_ = p.floor_; a.scale = p.scale;
+    for (int i = 0; i < p.num_ordered; ++i) a.order[i] = p.order[i];
+    const int64_t blocks = (int64_t)a.groups_padded * a.n_slices;
+    if (a.num_groups == 0) return hipSuccess;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)prefill_bf16_kernel<DK, DV, NCB>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL((prefill_bf16_kernel<DK, DV, NCB>), dim3((unsigned)blocks), dim3(C::THREADS),
+                       C::LDS_BYTES, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// value-slice widths this path supports for (dk, dv)
+bool prefill_bf16_supports(int dk, int dv, int nv) {
+    if (nv < 16 || nv > dv) return false;
+    if (dk == 128) return nv <= 64;
+    return dk == 64 && nv <= 128;
+}
+
+hipError_t launch_prefill_bf16(const PrefillArgs& p, hipStream_t st) {
+#define KDA_NV_CASES(DK, DV)                                          \
+    switch (p.nv) {                                                   \
+        case 16: return launch_bf16<DK, DV, 1>(p, st);                \
+        case 32: return launch_bf16<DK, DV, 2>(p, st);                \
+        case 64: if constexpr (DV >= 64) return launch_bf16<DK, DV, 4>(p, st); break; \
+        case 128: if constexpr (DK == 64 && DV >= 128) return launch_bf16<DK, DV, 8>(p, st); break; \
+    }                                                                 \
+    return hipErrorInvalidValue;
+    if (p.dk == 128 && p.dv == 128) { KDA_NV_CASES(128, 128) }
+    if (p.dk == 128 && p.dv == 64) { KDA_NV_CASES(128, 64) }
+    if (p.dk == 64 && p.dv == 128) { KDA_NV_CASES(64, 128) }
+    if (p.dk == 64 && p.dv == 64) { KDA_NV_CASES(64, 64) }
+#undef KDA_NV_CASES
+    return hipErrorInvalidValue;
+}
+
+}  // namespace kda
