@@ -53,22 +53,18 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// A 32-deep product issued as two 16-deep ones.  v_mfma_f32_16x16x32_bf16 gives wrong
-// results with this toolchain when a register of its A/B operand is rewritten by the next
-// few instructions (the scheduler does so freely; reproduced on gfx950: the 16x16x32 form
-// reads its upper operand half after issue and no wait states are inserted).  The pair of
-// 16-deep instructions computes the same sum with the same operand pairing.
-__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
-    const bf16x4 a0{a[0], a[1], a[2], a[3]}, a1{a[4], a[5], a[6], a[7]};
-    const bf16x4 b0{b[0], b[1], b[2], b[3]}, b1{b[4], b[5], b[6], b[7]};
-    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a0, b0, c, 0, 0, 0);
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a1, b1, c, 0, 0, 0);
-}
 __device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
-    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+// 32-deep steps are issued as two 16-deep v_mfma_f32_16x16x16_bf16.  The 16x16x32 form
+// gave wrong results with this toolchain when a register of its A/B operand was
+// rewritten within the next few instructions (the scheduler does this freely; seen on
+// gfx950: the upper operand half is read after issue and no wait states were inserted).
+__device__ __forceinline__ bf16x4 lo4(bf16x8 x) { return bf16x4{x[0], x[1], x[2], x[3]}; }
+__device__ __forceinline__ bf16x4 hi4(bf16x8 x) { return bf16x4{x[4], x[5], x[6], x[7]}; }
+// sum over both 16-deep halves: lo(a) lo(b) + hi(a) hi(b)
+__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return mfma16(hi4(a), hi4(b), mfma16(lo4(a), lo4(b), c));
 }
 __device__ __forceinline__ bf16x4 to_bf4(f32x4 x) {
     return bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
@@ -86,7 +82,8 @@ __device__ __forceinline__ f32x4 prod3(f32x4 aL, f32x4 cR) {
     bf16x4 lh, ll, rh, rl;
     split4(aL, lh, ll);
     split4(cR, rh, rl);
-    f32x4 acc = mfma32(cat8(lh, lh), cat8(rh, rl), zero4());
+    f32x4 acc = mfma16(lh, rh, zero4());
+    acc = mfma16(lh, rl, acc);
     return mfma16(ll, rh, acc);
 }
 template <int CTRL>
@@ -103,6 +100,14 @@ __device__ __forceinline__ float row_scan(float x) {
     return x;
 }
 __device__ __forceinline__ float row_last(float x) { return dpp<0x15F>(x); }  // lane 15 of row
+
+// Workgroup barrier that orders LDS only.  __syncthreads() also waits for every
+// outstanding global load, which would drain the multi-chunk prefetch at each chunk.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 __device__ __forceinline__ f32x4 unpack_bf4(u32x2 w) {
     return f32x4{__builtin_bit_cast(float, w[0] << 16), __builtin_bit_cast(float, w[0] & 0xffff0000u),
@@ -174,6 +179,15 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
     const int64_t tbeg = a.cu[seq], tend = a.cu[seq + 1];
     const int nch = (int)((tend - tbeg + 15) / 16);
     const int col0 = slice * NV;
+    if (nch == 0) {  // empty sequence: the final state is the initial state
+        if (a.Sf && wave < NCB) {
+            const int64_t base = ((int64_t)seq * H + h) * DK * DV;
+            for (int row = lane >> 4; row < DK; row += 4)
+                a.Sf[base + row * DV + col0 + 16 * wave + (lane & 15)] =
+                    a.S0 ? a.S0[base + row * DV + col0 + 16 * wave + (lane & 15)] : 0.f;
+        }
+        return;
+    }
     const int64_t rowq = (int64_t)H * DK, rowv = (int64_t)H * DV;
     const int64_t sbase = ((int64_t)seq * H + h) * DK * DV;
 
@@ -190,11 +204,11 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
     // ---------------------------------------------------------------- loop-carried registers
     // One register array carries the state of whichever role this wave has, so the
     // per-thread register budget is the larger role's, not the sum of all roles:
-    //   chain: [0, 4KB) fp32 state S (rows 16b+4g+i, column ccol); [4KB, 4KB+4KP) bf16 S'
-    //          as 32-deep B operands
+    //   chain: [0, 4KB) fp32 state S' (rows 16b+4g+i, column ccol); its bf16 copy (the B
+    //          operands of Wt S' and Qt S') is rebuilt at the start of each step
     //   decay: four prefetched (q, k, log_alpha) fragments, beta values and value/gate
     //          row fragments
-    constexpr int R_SB = 4 * KB, R_CH = R_SB + 4 * KP;
+    constexpr int R_CH = 4 * KB;
     constexpr int D_Q = 0, D_K = 8, D_L = 16, D_B = 24, D_VG = 28,
                   D_N = D_VG + 8 * C::VG_PER_WAVE;
     constexpr int R_N = R_CH > D_N ? R_CH : D_N;
@@ -211,51 +225,32 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
     auto setS = [&](int b, f32x4 x) {
         R[4 * b] = ui(x[0]); R[4 * b + 1] = ui(x[1]); R[4 * b + 2] = ui(x[2]); R[4 * b + 3] = ui(x[3]);
     };
-    auto getSb = [&](int p) {
-        const int o = R_SB + 4 * p;
-        return __builtin_bit_cast(bf16x8, u32x4{R[o], R[o + 1], R[o + 2], R[o + 3]});
-    };
-    auto setSb = [&](int p, bf16x8 x) {
-        const u32x4 f = __builtin_bit_cast(u32x4, x);
-        const int o = R_SB + 4 * p;
-        R[o] = f[0]; R[o + 1] = f[1]; R[o + 2] = f[2]; R[o + 3] = f[3];
-    };
     auto get2 = [&](int o) { return u32x2{R[o], R[o + 1]}; };
     auto set2 = [&](int o, u32x2 x) { R[o] = x[0]; R[o + 1] = x[1]; };
 
     const int ccol = col0 + 16 * wave + r;  // chain wave's value column
     const int dch = 16 * cb + 4 * g;  // decay wave's first channel
+    // Prefetch loads are unconditional (no branch around them, so each lands directly in
+    // its loop-carried register and stays in flight across iterations): the token index is
+    // clamped into the sequence and rows past its end are zeroed when consumed.
+    const bf16* vg_src[C::VG_PER_WAVE];  // value or gate rows staged by this decay wave
+#pragma unroll
+    for (int e = 0; e < C::VG_PER_WAVE; ++e) vg_src[e] = ((cb + KB * e) & 1) ? a.gate : a.v;
     auto load_qkl = [&](int c, int slot) {
-        u32x2 qq{0u, 0u}, kq{0u, 0u}, lq{0u, 0u};
-        float bq = 0.f;
-        if (c < nch) {
-            const int64_t t0 = tbeg + 16 * c;
-            if (t0 + r < tend) {
-                const int64_t off = (t0 + r) * rowq + (int64_t)h * DK + dch;
-                qq = *reinterpret_cast<const u32x2*>(a.q + off);
-                kq = *reinterpret_cast<const u32x2*>(a.k + off);
-                lq = *reinterpret_cast<const u32x2*>(a.la + off);
-                bq = (float)a.beta[(t0 + r) * H + h];
-            }
-        }
-        set2(D_Q + 2 * slot, qq);
-        set2(D_K + 2 * slot, kq);
-        set2(D_L + 2 * slot, lq);
-        R[D_B + slot] = ui(bq);
+        const int64_t t = min<int64_t>(tbeg + 16 * c + r, tend - 1);
+        const int64_t off = t * rowq + (int64_t)h * DK + dch;
+        set2(D_Q + 2 * slot, *reinterpret_cast<const u32x2*>(a.q + off));
+        set2(D_K + 2 * slot, *reinterpret_cast<const u32x2*>(a.k + off));
+        set2(D_L + 2 * slot, *reinterpret_cast<const u32x2*>(a.la + off));
+        R[D_B + slot] = __builtin_bit_cast(uint16_t, a.beta[t * H + h]);
         // value / gate rows of this wave's fragment sets: token r, columns +4g..+3
 #pragma unroll
         for (int e = 0; e < C::VG_PER_WAVE; ++e) {
             const int f = cb + KB * e;
-            u32x2 x{0u, 0u};
-            if (f < 2 * NCB && c < nch) {
-                const int64_t t0 = tbeg + 16 * c;
-                if (t0 + r < tend) {
-                    const bf16* src = (f & 1) ? a.gate : a.v;
-                    x = *reinterpret_cast<const u32x2*>(
-                        src + (t0 + r) * rowv + (int64_t)h * DV + col0 + 16 * (f >> 1) + 4 * g);
-                }
+            if (f < 2 * NCB) {
+                set2(D_VG + 8 * e + 2 * slot, *reinterpret_cast<const u32x2*>(
+                    vg_src[e] + t * rowv + (int64_t)h * DV + col0 + 16 * (f >> 1) + 4 * g));
             }
-            set2(D_VG + 8 * e + 2 * slot, x);
         }
     };
 
@@ -286,10 +281,12 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
             // ---- decay-folded operands of chunk it + 3 (row layout: token r, channels dch..+3)
             const int c = it + 3;
             if (c < nch) {
-                const f32x4 q4 = unpack_bf4(get2(D_Q + 2 * ph)) * a.scale;
-                const f32x4 k4 = unpack_bf4(get2(D_K + 2 * ph));
-                const f32x4 l4 = unpack_bf4(get2(D_L + 2 * ph));
-                const float bet = fl(R[D_B + ph]);
+                const bool valid = tbeg + 16 * c + r < tend;  // rows past the end: identity
+                const u32x2 zero2{0u, 0u};
+                const f32x4 q4 = unpack_bf4(valid ? get2(D_Q + 2 * ph) : zero2) * a.scale;
+                const f32x4 k4 = unpack_bf4(valid ? get2(D_K + 2 * ph) : zero2);
+                const f32x4 l4 = unpack_bf4(valid ? get2(D_L + 2 * ph) : zero2);
+                const float bet = valid ? fl(R[D_B + ph] << 16) : 0.f;
                 f32x4 F, Fi, gam;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -332,13 +329,13 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
                 for (int e = 0; e < C::VG_PER_WAVE; ++e) {
                     const int f = cb + KB * e;
                     if (f < 2 * NCB) {
-                        const bf16x4 x = __builtin_bit_cast(bf16x4, get2(D_VG + 8 * e + 2 * ph));
+                        const bf16x4 x = __builtin_bit_cast(bf16x4, valid ? get2(D_VG + 8 * e + 2 * ph) : zero2);
                         const bf16x4 xt = to_bf4(mfma16(x, ident, zero4()));  // C(block)
                         *reinterpret_cast<bf16x4*>(L + C::L_VG + f * 512 + lane * 8) = xt;
                     }
                 }
             }
-            load_qkl(it + 7, ph);
+            load_qkl(it + 7, ph);  // past the last chunk: reads the last row, never used
         } else if (wave == C::W_GRAM) {
             // ---- A, A^T of chunk it + 2 and T = (I + A)^-1 Diag(beta), kept as C(T^T)
             const int c = it + 2;
@@ -429,43 +426,44 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
                 const unsigned char* L = lslot(c);
                 const unsigned char* Gs = gslot(c);
                 const unsigned char* W = wslot(c);
+                bf16x4 Sb[KB];  // bf16 copy of S' (B operands)
+#pragma unroll
+                for (int b = 0; b < KB; ++b) Sb[b] = to_bf4(getS(b));
                 // Ut = T V
                 const bf16x4 tt = *reinterpret_cast<const bf16x4*>(Gs + C::G_TT + lane * 8);
                 const bf16x4 vb = *reinterpret_cast<const bf16x4*>(L + C::L_VG + (2 * wave) * 512 + lane * 8);
                 f32x4 U = mfma16(tt, vb, zero4());
+#pragma unroll
+                for (int p = 0; p < KP; ++p) {  // U = Ut - Wt S'
+                    const bf16x8 w = *reinterpret_cast<const bf16x8*>(W + C::W_WT + p * 1024 + lane * 16);
+                    U = mfma16(lo4(w), Sb[2 * p], U);
+                    U = mfma16(hi4(w), Sb[2 * p + 1], U);
+                }
                 f32x4 O = zero4();
 #pragma unroll
-                for (int p = 0; p < KP; ++p) {
-                    const bf16x8 w = *reinterpret_cast<const bf16x8*>(W + C::W_WT + p * 1024 + lane * 16);
-                    U = mfma32(w, getSb(p), U);  // U = Ut - Wt S'
-                }
-#pragma unroll
-                for (int p = 0; p < KP; ++p) {
-                    const int off = r * C::RSB + 2 * (32 * p + 4 * g);
-                    const bf16x4 q0 = *reinterpret_cast<const bf16x4*>(L + C::L_QH + off);
-                    const bf16x4 q1 = *reinterpret_cast<const bf16x4*>(L + C::L_QH + off + 32);
-                    const bf16x4 l0 = *reinterpret_cast<const bf16x4*>(L + C::L_QL + off);
-                    const bf16x4 l1 = *reinterpret_cast<const bf16x4*>(L + C::L_QL + off + 32);
-                    O = mfma32(cat8(q0, q1), getSb(p), O);  // Qt S'
-                    O = mfma32(cat8(l0, l1), getSb(p), O);
+                for (int b = 0; b < KB; ++b) {  // O = Qt S' (hi and lo halves of Qt)
+                    const int off = r * C::RSB + 2 * (16 * b + 4 * g);
+                    O = mfma16(*reinterpret_cast<const bf16x4*>(L + C::L_QH + off), Sb[b], O);
+                    O = mfma16(*reinterpret_cast<const bf16x4*>(L + C::L_QL + off), Sb[b], O);
                 }
                 bf16x4 uh, ul;
                 split4(U, uh, ul);
-                const bf16x8 u8 = cat8(uh, ul);
                 const bf16x4 ph_ = *reinterpret_cast<const bf16x4*>(Gs + C::G_PH + lane * 8);
                 const bf16x4 pl_ = *reinterpret_cast<const bf16x4*>(Gs + C::G_PL + lane * 8);
-                O = mfma32(cat8(ph_, ph_), u8, O);  // + P U
+                O = mfma16(ph_, uh, O);  // + P U
+                O = mfma16(ph_, ul, O);
                 O = mfma16(pl_, uh, O);
-                // S <- S' + Kb^T U, row block by row block; then S' of the next chunk
+                // S <- S' + Kb^T U, row block by row block
                 const bool last = c + 1 >= nch;
                 const float* gn = reinterpret_cast<const float*>(lslot(c + 1) + C::L_GAM);
 #pragma unroll
                 for (int b = 0; b < KB; ++b) {
                     const bf16x4 kh = *reinterpret_cast<const bf16x4*>(L + C::L_KBH + b * 512 + lane * 8);
                     const bf16x4 kl = *reinterpret_cast<const bf16x4*>(L + C::L_KBL + b * 512 + lane * 8);
-                    f32x4 s = mfma32(cat8(kh, kh), u8, getS(b));
-                    s = mfma16(kl, uh, s);
-                    setS(b, s);
+                    f32x4 sb = mfma16(kh, uh, getS(b));
+                    sb = mfma16(kh, ul, sb);
+                    sb = mfma16(kl, uh, sb);
+                    setS(b, sb);
                 }
                 // gated output rows of this chunk
                 const int64_t t0 = tbeg + 16 * c;
@@ -476,12 +474,10 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
                     const int row = 4 * g + i;
                     if (row < cp) a.out[(t0 + row) * rowv + (int64_t)h * DV + ccol] = (bf16)(gt[i] * O[i]);
                 }
-                if (!last) {
+                if (!last) {  // S' of the next chunk
 #pragma unroll
                     for (int b = 0; b < KB; ++b)
                         setS(b, getS(b) * *reinterpret_cast<const f32x4*>(gn + 16 * b + 4 * g));
-#pragma unroll
-                    for (int p = 0; p < KP; ++p) setSb(p, cat8(to_bf4(getS(2 * p)), to_bf4(getS(2 * p + 1))));
                 }
             } else if (c == -1 && nch > 0) {
                 // S' of chunk 0
@@ -489,11 +485,9 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
 #pragma unroll
                 for (int b = 0; b < KB; ++b)
                     setS(b, getS(b) * *reinterpret_cast<const f32x4*>(g0 + 16 * b + 4 * g));
-#pragma unroll
-                for (int p = 0; p < KP; ++p) setSb(p, cat8(to_bf4(getS(2 * p)), to_bf4(getS(2 * p + 1))));
             }
         }
-        __syncthreads();
+        lds_barrier();
     };
 
     // iterations it = -3 .. nch-1; prefetch slot = (it + 4) & 3 (compile-time per unrolled body)
