@@ -197,96 +197,74 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
     auto gslot = [&](int c) { return smem + C::OFF_G + (c % 3) * C::G_SIZE; };
     auto wslot = [&](int c) { return smem + C::OFF_W + (c & 1) * C::W_SIZE; };
 
-    const bool is_chain = wave < C::NCHAIN;
-    const bool is_decay = wave >= C::W_DECAY0 && wave < C::W_GRAM;
-    const int cb = wave - C::W_DECAY0;  // decay: channel block
-
-    // ---------------------------------------------------------------- loop-carried registers
-    // One register array carries the state of whichever role this wave has, so the
-    // per-thread register budget is the larger role's, not the sum of all roles:
-    //   chain: [0, 4KB) fp32 state S' (rows 16b+4g+i, column ccol); its bf16 copy (the B
-    //          operands of Wt S' and Qt S') is rebuilt at the start of each step
-    //   decay: four prefetched (q, k, log_alpha) fragments, beta values and value/gate
-    //          row fragments
-    constexpr int R_CH = 4 * KB;
-    constexpr int D_Q = 0, D_K = 8, D_L = 16, D_B = 24, D_VG = 28,
-                  D_N = D_VG + 8 * C::VG_PER_WAVE;
-    constexpr int R_N = R_CH > D_N ? R_CH : D_N;
-    // (integer storage: round-tripping integer data through a float array miscompiles
-    // with this toolchain -- the second dword of a pair is read back as the first)
-    uint32_t R[R_N];
-#pragma unroll
-    for (int i = 0; i < R_N; ++i) R[i] = 0u;
-    auto fl = [](uint32_t x) { return __builtin_bit_cast(float, x); };
-    auto ui = [](float x) { return __builtin_bit_cast(uint32_t, x); };
-    auto getS = [&](int b) {
-        return f32x4{fl(R[4 * b]), fl(R[4 * b + 1]), fl(R[4 * b + 2]), fl(R[4 * b + 3])};
-    };
-    auto setS = [&](int b, f32x4 x) {
-        R[4 * b] = ui(x[0]); R[4 * b + 1] = ui(x[1]); R[4 * b + 2] = ui(x[2]); R[4 * b + 3] = ui(x[3]);
-    };
-    auto get2 = [&](int o) { return u32x2{R[o], R[o + 1]}; };
-    auto set2 = [&](int o, u32x2 x) { R[o] = x[0]; R[o + 1] = x[1]; };
-
-    const int ccol = col0 + 16 * wave + r;  // chain wave's value column
-    const int dch = 16 * cb + 4 * g;  // decay wave's first channel
-    // Prefetch loads are unconditional (no branch around them, so each lands directly in
-    // its loop-carried register and stays in flight across iterations): the token index is
-    // clamped into the sequence and rows past its end are zeroed when consumed.
-    const bf16* vg_src[C::VG_PER_WAVE];  // value or gate rows staged by this decay wave
-#pragma unroll
-    for (int e = 0; e < C::VG_PER_WAVE; ++e) vg_src[e] = ((cb + KB * e) & 1) ? a.gate : a.v;
-    auto load_qkl = [&](int c, int slot) {
-        const int64_t t = min<int64_t>(tbeg + 16 * c + r, tend - 1);
-        const int64_t off = t * rowq + (int64_t)h * DK + dch;
-        set2(D_Q + 2 * slot, *reinterpret_cast<const u32x2*>(a.q + off));
-        set2(D_K + 2 * slot, *reinterpret_cast<const u32x2*>(a.k + off));
-        set2(D_L + 2 * slot, *reinterpret_cast<const u32x2*>(a.la + off));
-        R[D_B + slot] = __builtin_bit_cast(uint16_t, a.beta[t * H + h]);
-        // value / gate rows of this wave's fragment sets: token r, columns +4g..+3
-#pragma unroll
-        for (int e = 0; e < C::VG_PER_WAVE; ++e) {
-            const int f = cb + KB * e;
-            if (f < 2 * NCB) {
-                set2(D_VG + 8 * e + 2 * slot, *reinterpret_cast<const u32x2*>(
-                    vg_src[e] + t * rowv + (int64_t)h * DV + col0 + 16 * (f >> 1) + 4 * g));
-            }
-        }
-    };
-
-    if (is_chain) {
-#pragma unroll
-        for (int b = 0; b < KB; ++b) {
-            f32x4 x;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                x[i] = a.S0 ? a.S0[sbase + (16 * b + 4 * g + i) * DV + ccol] : 0.f;
-            setS(b, x);
-        }
-    } else if (is_decay) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) load_qkl(c, (c + 1) & 3);
-    }
+    // Each role runs its own loop over iterations it = -3 .. it_end-1 with one LDS barrier
+    // per iteration, so the loop-carried registers of one role never share a register (or a
+    // merge point) with another's, and a load target is never copied (which would wait for
+    // the load).  Iteration it: decay builds chunk it+3, gram and P chunk it+2, Wt chunk
+    // it+1, the chain steps chunk it.  The count is padded to a multiple of four (the
+    // decay ring's period; padded iterations only pass the barrier).
+    const int it_end = -3 + ((nch + 3 + 3) & ~3);
+    const float floor2 = a.floor_;
     // identity as a B fragment (for exact register transposes through the matrix core)
     bf16x4 ident;
 #pragma unroll
     for (int i = 0; i < 4; ++i) ident[i] = (bf16)((4 * g + i) == r ? 1.f : 0.f);
 
-    const float floor2 = a.floor_;
-
-    // ---------------------------------------------------------------- one iteration
-    auto body = [&](const int it, auto PH) {
-        constexpr int ph = decltype(PH)::value;
-        if (is_decay) {
-            // ---- decay-folded operands of chunk it + 3 (row layout: token r, channels dch..+3)
-            const int c = it + 3;
+    if (wave >= C::W_DECAY0 && wave < C::W_GRAM) {
+        // ================================================================ decay waves
+        const int cb = wave - C::W_DECAY0;  // 16-channel block
+        const int dch = 16 * cb + 4 * g;    // this lane's first channel
+        // Prefetch ring of four chunks; chunk c lives in slot (c + 1) & 3.  Loads are
+        // unconditional (the token index is clamped into the sequence; rows past its end
+        // are zeroed when consumed), so each lands in its own register and stays in flight.
+        u32x2 rq[4], rk[4], rl[4], rvg[C::VG_PER_WAVE][4];
+        uint32_t rb[4];
+        // value / gate fragment sets staged by this wave: set f = cb + KB*e (block f >> 1,
+        // gate if f is odd); the loads are unconditional, so a wave past the last set
+        // reloads set cb % (2 NCB) and discards it
+        const bf16* vg_src[C::VG_PER_WAVE];
+        int vg_col[C::VG_PER_WAVE];
+#pragma unroll
+        for (int e = 0; e < C::VG_PER_WAVE; ++e) {
+            const int f = cb + KB * e < 2 * NCB ? cb + KB * e : cb % (2 * NCB);
+            vg_src[e] = (f & 1) ? a.gate : a.v;
+            vg_col[e] = col0 + 16 * (f >> 1) + 4 * g;
+        }
+        auto load = [&](int c, auto SLOT) {
+            constexpr int sl = decltype(SLOT)::value;
+            const int64_t t = min<int64_t>(tbeg + 16 * c + r, tend - 1);
+            const int64_t off = t * rowq + (int64_t)h * DK + dch;
+            rq[sl] = *reinterpret_cast<const u32x2*>(a.q + off);
+            rk[sl] = *reinterpret_cast<const u32x2*>(a.k + off);
+            rl[sl] = *reinterpret_cast<const u32x2*>(a.la + off);
+            rb[sl] = __builtin_bit_cast(uint16_t, a.beta[t * H + h]);
+            // value / gate rows of this wave's fragment sets: token r, columns +4g..+3
+            // (a wave with fewer sets than VG_PER_WAVE reloads its set; never stored)
+#pragma unroll
+            for (int e = 0; e < C::VG_PER_WAVE; ++e)
+                rvg[e][sl] = *reinterpret_cast<const u32x2*>(
+                    vg_src[e] + t * rowv + (int64_t)h * DV + vg_col[e]);
+        };
+        // issued in slot order (kept by the scheduling barriers), so the loads of the
+        // slot consumed next are always the oldest in flight
+        load(0, std::integral_constant<int, 1>{});
+        __builtin_amdgcn_sched_barrier(0);
+        load(1, std::integral_constant<int, 2>{});
+        __builtin_amdgcn_sched_barrier(0);
+        load(2, std::integral_constant<int, 3>{});
+        __builtin_amdgcn_sched_barrier(0);
+        load(3, std::integral_constant<int, 0>{});
+        __builtin_amdgcn_sched_barrier(0);
+        auto step = [&](const int it, auto PH) {
+            constexpr int ph = decltype(PH)::value;
+            const int c = it + 3;  // decay-folded operands of chunk c (row layout: token r)
             if (c < nch) {
                 const bool valid = tbeg + 16 * c + r < tend;  // rows past the end: identity
                 const u32x2 zero2{0u, 0u};
-                const f32x4 q4 = unpack_bf4(valid ? get2(D_Q + 2 * ph) : zero2) * a.scale;
-                const f32x4 k4 = unpack_bf4(valid ? get2(D_K + 2 * ph) : zero2);
-                const f32x4 l4 = unpack_bf4(valid ? get2(D_L + 2 * ph) : zero2);
-                const float bet = valid ? fl(R[D_B + ph] << 16) : 0.f;
+                const f32x4 q4 = unpack_bf4(valid ? rq[ph] : zero2) * a.scale;
+                const f32x4 k4 = unpack_bf4(valid ? rk[ph] : zero2);
+                const f32x4 l4 = unpack_bf4(valid ? rl[ph] : zero2);
+                const float bet = valid ? __builtin_bit_cast(float, rb[ph] << 16) : 0.f;
                 f32x4 F, Fi, gam;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -329,15 +307,25 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
                 for (int e = 0; e < C::VG_PER_WAVE; ++e) {
                     const int f = cb + KB * e;
                     if (f < 2 * NCB) {
-                        const bf16x4 x = __builtin_bit_cast(bf16x4, valid ? get2(D_VG + 8 * e + 2 * ph) : zero2);
+                        const bf16x4 x = __builtin_bit_cast(bf16x4, valid ? rvg[e][ph] : zero2);
                         const bf16x4 xt = to_bf4(mfma16(x, ident, zero4()));  // C(block)
                         *reinterpret_cast<bf16x4*>(L + C::L_VG + f * 512 + lane * 8) = xt;
                     }
                 }
             }
-            load_qkl(it + 7, ph);  // past the last chunk: reads the last row, never used
-        } else if (wave == C::W_GRAM) {
-            // ---- A, A^T of chunk it + 2 and T = (I + A)^-1 Diag(beta), kept as C(T^T)
+            load(it + 7, PH);  // past the last chunk: reads the last row, never used
+            lds_barrier();
+        };
+        for (int it = -3; it < it_end; it += 4) {  // no exit between the four slots
+            step(it, std::integral_constant<int, 1>{});
+            step(it + 1, std::integral_constant<int, 2>{});
+            step(it + 2, std::integral_constant<int, 3>{});
+            step(it + 3, std::integral_constant<int, 0>{});
+        }
+    } else if (wave == C::W_GRAM) {
+        // ================================================================ gram wave
+        for (int it = -3; it < it_end; ++it) {
+            // A, A^T of chunk it + 2 and T = (I + A)^-1 Diag(beta), kept as C(T^T)
             const int c = it + 2;
             if (c >= 0 && c < nch) {
                 const unsigned char* Sh = sslot(c);
@@ -375,60 +363,75 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
                 const bf16x4 tt = to_bf4(y * bi);  // C(T^T): row 4g+i of X^T scaled by beta
                 *reinterpret_cast<bf16x4*>(gslot(c) + C::G_TT + lane * 8) = tt;
             }
-        } else if (wave == C::W_PW) {
-          {
-            // ---- P of chunk it + 2, as A-fragments hi/lo: C(P^T) = C(Kb Qt^T)
-            const int c = it + 2;
-            if (c >= 0 && c < nch) {
-                const unsigned char* Sh = sslot(c);
-                const unsigned char* L = lslot(c);
-                f32x4 acc = zero4();
+            lds_barrier();
+        }
+    } else if (wave == C::W_PW) {
+        // ================================================================ P / Wt wave
+        for (int it = -3; it < it_end; ++it) {
+            {
+                // P of chunk it + 2, as A-fragments hi/lo: C(P^T) = C(Kb Qt^T)
+                const int c = it + 2;
+                if (c >= 0 && c < nch) {
+                    const unsigned char* Sh = sslot(c);
+                    const unsigned char* L = lslot(c);
+                    f32x4 acc = zero4();
 #pragma unroll
-                for (int p = 0; p < KP; ++p) {
-                    const int off = r * C::RSB + 2 * (32 * p + 8 * g);
-                    const bf16x8 kbh = *reinterpret_cast<const bf16x8*>(Sh + C::S_KBH + off);
-                    const bf16x8 kbl = *reinterpret_cast<const bf16x8*>(Sh + C::S_KBL + off);
-                    const bf16x8 qh = *reinterpret_cast<const bf16x8*>(L + C::L_QH + off);
-                    const bf16x8 ql = *reinterpret_cast<const bf16x8*>(L + C::L_QL + off);
-                    acc = mfma32(kbh, qh, acc);
-                    acc = mfma32(kbh, ql, acc);
-                    acc = mfma32(kbl, qh, acc);
-                }
-                // acc[i] = P[r][4g+i]; keep the causal part (key position <= query position)
+                    for (int p = 0; p < KP; ++p) {
+                        const int off = r * C::RSB + 2 * (32 * p + 8 * g);
+                        const bf16x8 kbh = *reinterpret_cast<const bf16x8*>(Sh + C::S_KBH + off);
+                        const bf16x8 kbl = *reinterpret_cast<const bf16x8*>(Sh + C::S_KBL + off);
+                        const bf16x8 qh = *reinterpret_cast<const bf16x8*>(L + C::L_QH + off);
+                        const bf16x8 ql = *reinterpret_cast<const bf16x8*>(L + C::L_QL + off);
+                        acc = mfma32(kbh, qh, acc);
+                        acc = mfma32(kbh, ql, acc);
+                        acc = mfma32(kbl, qh, acc);
+                    }
+                    // acc[i] = P[r][4g+i]; keep the causal part (key position <= query position)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] = (4 * g + i) <= r ? acc[i] : 0.f;
-                bf16x4 ph_, pl_;
-                split4(acc, ph_, pl_);
-                *reinterpret_cast<bf16x4*>(gslot(c) + C::G_PH + lane * 8) = ph_;
-                *reinterpret_cast<bf16x4*>(gslot(c) + C::G_PL + lane * 8) = pl_;
-            }
-          }
-          {
-            // ---- -Wt of chunk it + 1 as 32-deep A-fragments: C(Wt^T) blocks = Kt^T T^T
-            const int c = it + 1;
-            if (c >= 0 && c < nch) {
-                const bf16x4 tt = *reinterpret_cast<const bf16x4*>(gslot(c) + C::G_TT + lane * 8);
-                const unsigned char* M = mslot(c);
-                unsigned char* W = wslot(c);
-#pragma unroll
-                for (int nb = 0; nb < KB; ++nb) {
-                    const bf16x4 ktt = *reinterpret_cast<const bf16x4*>(M + C::M_KTT + nb * 512 + lane * 8);
-                    const f32x4 w = mfma16(ktt, tt, zero4());  // w[i] = Wt[r][16nb + 4g + i]
-                    *reinterpret_cast<bf16x4*>(W + C::W_WT + (nb >> 1) * 1024 + lane * 16 + (nb & 1) * 8) =
-                        to_bf4(-w);
+                    for (int i = 0; i < 4; ++i) acc[i] = (4 * g + i) <= r ? acc[i] : 0.f;
+                    bf16x4 ph_, pl_;
+                    split4(acc, ph_, pl_);
+                    *reinterpret_cast<bf16x4*>(gslot(c) + C::G_PH + lane * 8) = ph_;
+                    *reinterpret_cast<bf16x4*>(gslot(c) + C::G_PL + lane * 8) = pl_;
                 }
             }
-          }
-        } else if (is_chain) {
-            // ---- state step of chunk it for value columns col0 + 16*wave .. +15
-            const int c = it;
+            {
+                // -Wt of chunk it + 1 as 32-deep A-fragments: C(Wt^T) blocks = Kt^T T^T
+                const int c = it + 1;
+                if (c >= 0 && c < nch) {
+                    const bf16x4 tt = *reinterpret_cast<const bf16x4*>(gslot(c) + C::G_TT + lane * 8);
+                    const unsigned char* M = mslot(c);
+                    unsigned char* W = wslot(c);
+#pragma unroll
+                    for (int nb = 0; nb < KB; ++nb) {
+                        const bf16x4 ktt = *reinterpret_cast<const bf16x4*>(M + C::M_KTT + nb * 512 + lane * 8);
+                        const f32x4 w = mfma16(ktt, tt, zero4());  // w[i] = Wt[r][16nb + 4g + i]
+                        *reinterpret_cast<bf16x4*>(W + C::W_WT + (nb >> 1) * 1024 + lane * 16 + (nb & 1) * 8) =
+                            to_bf4(-w);
+                    }
+                }
+            }
+            lds_barrier();
+        }
+    } else {
+        // ================================================================ chain waves
+        // fp32 state S' of rows 16b+4g+i, value column ccol, in MFMA accumulator layout
+        const int ccol = col0 + 16 * wave + r;
+        f32x4 S[KB];
+#pragma unroll
+        for (int b = 0; b < KB; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                S[b][i] = a.S0 ? a.S0[sbase + (16 * b + 4 * g + i) * DV + ccol] : 0.f;
+        for (int it = -3; it < it_end; ++it) {
+            const int c = it;  // state step of chunk c
             if (c >= 0 && c < nch) {
                 const unsigned char* L = lslot(c);
                 const unsigned char* Gs = gslot(c);
                 const unsigned char* W = wslot(c);
                 bf16x4 Sb[KB];  // bf16 copy of S' (B operands)
 #pragma unroll
-                for (int b = 0; b < KB; ++b) Sb[b] = to_bf4(getS(b));
+                for (int b = 0; b < KB; ++b) Sb[b] = to_bf4(S[b]);
                 // Ut = T V
                 const bf16x4 tt = *reinterpret_cast<const bf16x4*>(Gs + C::G_TT + lane * 8);
                 const bf16x4 vb = *reinterpret_cast<const bf16x4*>(L + C::L_VG + (2 * wave) * 512 + lane * 8);
@@ -454,16 +457,13 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
                 O = mfma16(ph_, ul, O);
                 O = mfma16(pl_, uh, O);
                 // S <- S' + Kb^T U, row block by row block
-                const bool last = c + 1 >= nch;
-                const float* gn = reinterpret_cast<const float*>(lslot(c + 1) + C::L_GAM);
 #pragma unroll
                 for (int b = 0; b < KB; ++b) {
                     const bf16x4 kh = *reinterpret_cast<const bf16x4*>(L + C::L_KBH + b * 512 + lane * 8);
                     const bf16x4 kl = *reinterpret_cast<const bf16x4*>(L + C::L_KBL + b * 512 + lane * 8);
-                    f32x4 sb = mfma16(kh, uh, getS(b));
-                    sb = mfma16(kh, ul, sb);
-                    sb = mfma16(kl, uh, sb);
-                    setS(b, sb);
+                    S[b] = mfma16(kh, uh, S[b]);
+                    S[b] = mfma16(kh, ul, S[b]);
+                    S[b] = mfma16(kl, uh, S[b]);
                 }
                 // gated output rows of this chunk
                 const int64_t t0 = tbeg + 16 * c;
@@ -474,40 +474,25 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
                     const int row = 4 * g + i;
                     if (row < cp) a.out[(t0 + row) * rowv + (int64_t)h * DV + ccol] = (bf16)(gt[i] * O[i]);
                 }
-                if (!last) {  // S' of the next chunk
+                if (c + 1 < nch) {  // S' of the next chunk
+                    const float* gn = reinterpret_cast<const float*>(lslot(c + 1) + C::L_GAM);
 #pragma unroll
-                    for (int b = 0; b < KB; ++b)
-                        setS(b, getS(b) * *reinterpret_cast<const f32x4*>(gn + 16 * b + 4 * g));
+                    for (int b = 0; b < KB; ++b) S[b] *= *reinterpret_cast<const f32x4*>(gn + 16 * b + 4 * g);
                 }
-            } else if (c == -1 && nch > 0) {
+            } else if (c == -1) {
                 // S' of chunk 0
                 const float* g0 = reinterpret_cast<const float*>(lslot(0) + C::L_GAM);
 #pragma unroll
-                for (int b = 0; b < KB; ++b)
-                    setS(b, getS(b) * *reinterpret_cast<const f32x4*>(g0 + 16 * b + 4 * g));
+                for (int b = 0; b < KB; ++b) S[b] *= *reinterpret_cast<const f32x4*>(g0 + 16 * b + 4 * g);
             }
+            lds_barrier();
         }
-        lds_barrier();
-    };
-
-    // iterations it = -3 .. nch-1; prefetch slot = (it + 4) & 3 (compile-time per unrolled body)
-    int it = -3;
-    while (it < nch) {
-        body(it, std::integral_constant<int, 1>{});
-        if (++it >= nch) break;
-        body(it, std::integral_constant<int, 2>{});
-        if (++it >= nch) break;
-        body(it, std::integral_constant<int, 3>{});
-        if (++it >= nch) break;
-        body(it, std::integral_constant<int, 0>{});
-        ++it;
-    }
-
-    if (is_chain && a.Sf) {
+        if (a.Sf) {
 #pragma unroll
-        for (int b = 0; b < KB; ++b)
+            for (int b = 0; b < KB; ++b)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) a.Sf[sbase + (16 * b + 4 * g + i) * DV + ccol] = fl(R[4 * b + i]);
+                for (int i = 0; i < 4; ++i) a.Sf[sbase + (16 * b + 4 * g + i) * DV + ccol] = S[b][i];
+        }
     }
 }
 
