@@ -2,10 +2,11 @@
 //
 // Chunked form used here, per 16-token chunk (rows r; G_r = sum_{s<=r} max(lambda_s, floor),
 // inclusive; G_C its value at the chunk's last row; gamma = e^{G_C} per key channel):
-//   Qt = (scale q) e^{G - G_C},  Kt = k e^{G - G_C},  Kb = k e^{G_C - G}
+//   Qt = q e^{G - G_C},  Kt = k e^{G - G_C},  Kb = k e^{G_C - G}
 //   A  = strict_lower(Diag(beta) Kt Kb^T),   T = (I + A)^-1 Diag(beta)
 //   P  = lower_incl_diag(Qt Kb^T),           Wt = T Kt,   Ut = T V
-//   S' = Diag(gamma) S;   U = Ut - Wt S';   O = Qt S' + P U;   S <- S' + Kb^T U;  o = gate*O
+//   S' = Diag(gamma) S;   U = Ut - Wt S';   O = Qt S' + P U;   S <- S' + Kb^T U
+//   o  = gate * scale * O                    (O is linear in q, so scale is applied last)
 // This equals the token recurrence exactly in exact arithmetic (rows of the chunk unroll
 // into (I + A) U = Diag(beta) (V - Kt S')).  Because the per-step log-decay has a lower
 // bound, e^{G - G_C} <= e^{16 |floor|} inside a chunk, so the causal 16x16 block is a
@@ -19,17 +20,20 @@
 // Precision.  Products whose bf16 rounding would cost accuracy carry a second bf16 half
 // (x = hi + lo, ~16 significant bits): P and the Qt/Kb it is built from, the chunk's
 // writes U, Kb in the state update, and Qt in the readout.  The fp32 state is kept in
-// MFMA accumulators; its bf16 copy only feeds the Wt S' and Qt S' products.
+// MFMA accumulators; its bf16 copy only feeds the Wt S' and Qt S' products.  The powers
+// of A in the inverse are plain bf16 products (A is strictly lower triangular with
+// entries below one in size, and T only enters through bf16 operands anyway).
 //
 // Workgroup = one (sequence, head, slice of NV = 16*NCB value columns).  Waves:
 //   chain  (NCB)   : one 16-column block of S each; state step of chunk c
-//   decay  (DK/16) : one 16-channel block each; operands of chunk c+3, from registers
+//   decay  (DK/16) : one 16-channel block each; row tiles of chunk c+3 from registers
 //                    loaded four chunks earlier
 //   gram           : A, A^T of chunk c+2 and T through the nilpotent product
 //                    (I+A)^-1 = (I-A)(I+A^2)(I+A^4)(I+A^8)  (A^16 = 0), all in registers
 //   pw             : P of chunk c+2, then Wt of chunk c+1
 // One barrier per iteration; LDS rings carry each product from its producer to its
-// consumers.
+// consumers.  Every tile goes to LDS row-major (token rows); operands that contract over
+// tokens (Kb^T, Kt^T, V, gate) are read back transposed with ds_read_b64_tr_b16.
 //
 // MFMA fragment conventions (lane l: r = l & 15, g = l >> 4):
 //   C(M) / B-fragment of M : M[4g + i][r]   (i = 0..3)
@@ -37,6 +41,11 @@
 //   v_mfma_f32_16x16x16_bf16(Afrag(L), Bfrag(R)) = C(L R)
 //   A 32-deep step pairs element j of the A operand with element j of the B operand on
 //   each lane, so two 16-deep operands can be stacked into one 32-deep one.
+// Transposed LDS read (ds_read_b64_tr_b16): within each 16-lane group the four 16-bit
+// elements read by the group form a 16x4 matrix M[lane][e]; lane m receives
+// M[4j + m/4][m%4] for j = 0..3.  With lane 16g + 4j + q pointing at row 4g + j, columns
+// c0 + 4q .. c0 + 4q + 3 of a row-major tile X, lane (r, g) receives X[4g + i][c0 + r]:
+// the B-fragment of X's 16x16 block at c0 (equivalently the A-fragment of its transpose).
 #include <math.h>
 
 #include <type_traits>
@@ -49,7 +58,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -66,25 +75,28 @@ __device__ __forceinline__ bf16x4 hi4(bf16x8 x) { return bf16x4{x[4], x[5], x[6]
 __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
     return mfma16(hi4(a), hi4(b), mfma16(lo4(a), lo4(b), c));
 }
+// round to bf16 pairwise: the four-wide conversion of MFMA results is split by the
+// compiler into single conversions plus permutes; two-wide ones map to v_cvt_pk_bf16_f32
 __device__ __forceinline__ bf16x4 to_bf4(f32x4 x) {
-    return bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 lo = __builtin_convertvector(f32x2{x[0], x[1]}, bf16x2);
+    const bf16x2 hi = __builtin_convertvector(f32x2{x[2], x[3]}, bf16x2);
+    return __builtin_bit_cast(bf16x4, u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)});
 }
-__device__ __forceinline__ f32x4 to_f4(bf16x4 x) {
-    return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
-}
-// x = hi + lo, each bf16 (hi round-to-nearest-even, lo the rounded remainder)
+__device__ __forceinline__ f32x4 to_f4(bf16x4 x) { return __builtin_convertvector(x, f32x4); }
+// x = hi + lo, each bf16 (hi round-to-nearest-even, lo the rounded remainder); hi is
+// widened back from its packed form (a shift for the low half, a mask for the high half)
 __device__ __forceinline__ void split4(f32x4 x, bf16x4& hi, bf16x4& lo) {
     hi = to_bf4(x);
-    lo = to_bf4(x - to_f4(hi));
+    const u32x2 w = __builtin_bit_cast(u32x2, hi);
+    const f32x4 hf{__builtin_bit_cast(float, w[0] << 16), __builtin_bit_cast(float, w[0] & 0xffff0000u),
+                   __builtin_bit_cast(float, w[1] << 16), __builtin_bit_cast(float, w[1] & 0xffff0000u)};
+    lo = to_bf4(x - hf);
 }
-// C(L R) to ~16 bits from fp32 operands given as A-fragment of L (== C(L^T)) and C(R)
-__device__ __forceinline__ f32x4 prod3(f32x4 aL, f32x4 cR) {
-    bf16x4 lh, ll, rh, rl;
-    split4(aL, lh, ll);
-    split4(cR, rh, rl);
-    f32x4 acc = mfma16(lh, rh, zero4());
-    acc = mfma16(lh, rl, acc);
-    return mfma16(ll, rh, acc);
+// C(L R) in bf16 from fp32 operands given as the A-fragment of L (== C(L^T)) and C(R)
+__device__ __forceinline__ f32x4 prod(f32x4 aL, f32x4 cR) {
+    return mfma16(to_bf4(aL), to_bf4(cR), zero4());
 }
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
@@ -109,15 +121,35 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-__device__ __forceinline__ f32x4 unpack_bf4(u32x2 w) {
-    return f32x4{__builtin_bit_cast(float, w[0] << 16), __builtin_bit_cast(float, w[0] & 0xffff0000u),
-                 __builtin_bit_cast(float, w[1] << 16), __builtin_bit_cast(float, w[1] & 0xffff0000u)};
+// 8 bytes at p (LDS), four lanes' worth transposed per 16-lane group (see above)
+__device__ __forceinline__ bf16x4 lds_tr(const unsigned char* p) {
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    return __builtin_bit_cast(
+        bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(const_cast<unsigned char*>(p))));
 }
+template <typename T>
+__device__ __forceinline__ T lds_ld(const unsigned char* p) { return *reinterpret_cast<const T*>(p); }
+template <typename T>
+__device__ __forceinline__ void lds_st(unsigned char* p, T x) { *reinterpret_cast<T*>(p) = x; }
+
+// Buffer resource over [p, p + bytes): loads at offsets past the end return zero without
+// touching memory (raw buffer range check), which gives the identity rows past the end of
+// a sequence for free.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x2 bload8(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
+}
+
+// eight bytes of bf16 pairs -> four floats
+__device__ __forceinline__ f32x4 unpack_bf4(u32x2 w) { return to_f4(__builtin_bit_cast(bf16x4, w)); }
 
 template <int DK, int NCB>
 struct Cfg {
     static constexpr int KB = DK / 16;        // 16-channel blocks (= decay waves)
     static constexpr int KP = DK / 32;        // 32-channel steps of the state products
+    static constexpr int NV = 16 * NCB;       // value columns per workgroup
     static constexpr int NCHAIN = NCB;
     static constexpr int W_DECAY0 = NCHAIN;
     static constexpr int W_GRAM = NCHAIN + KB;
@@ -127,25 +159,30 @@ struct Cfg {
     // row-major [16][DK] bf16 tiles, padded rows (bytes)
     static constexpr int RSB = DK * 2 + 16;
     static constexpr int ROWT = 16 * RSB;
-    // long ring (4): Qt hi, Qt lo rows; Kb^T hi/lo fragments; gamma; value and gate
-    // fragments C(V block), C(gate block) of each 16-column block
-    static constexpr int L_QH = 0, L_QL = ROWT, L_KBH = 2 * ROWT, L_KBL = L_KBH + KB * 512,
-                         L_GAM = L_KBL + KB * 512, L_VG = L_GAM + DK * 4,
-                         L_SIZE = L_VG + 2 * NCB * 512;
-    // value/gate fragment sets staged per decay wave (set f: block f >> 1, gate if f & 1)
+    // row-major [16][NV] bf16 value and gate tiles
+    static constexpr int VRS = NV * 2 + 16;
+    static constexpr int VT = 16 * VRS;
+    // value/gate 16x16 blocks staged per decay wave (block f: columns 16 (f >> 1), gate if
+    // f is odd)
     static constexpr int VG_PER_WAVE = (2 * NCB + KB - 1) / KB;
-    // short ring (2): Kt, Kb hi, Kb lo rows; beta
-    static constexpr int S_KT = 0, S_KBH = ROWT, S_KBL = 2 * ROWT, S_BETA = 3 * ROWT,
-                         S_SIZE = 3 * ROWT + 64;
-    // mid ring (3): Kt^T fragments
-    static constexpr int M_KTT = 0, M_SIZE = KB * 512;
+    // long ring (4 slots, chunk c written at iteration c-3, read up to iteration c):
+    // Qt hi/lo, Kb hi/lo rows, gamma, value and gate rows
+    static constexpr int L_QH = 0, L_QL = ROWT, L_KBH = 2 * ROWT, L_KBL = 3 * ROWT,
+                         L_GAM = 4 * ROWT, L_V = L_GAM + DK * 4, L_G = L_V + VT,
+                         L_SIZE = L_G + VT;
+    // Kt ring (3): Kt rows (gram at c-2, Wt at c-1)
+    static constexpr int K_SIZE = ROWT;
+    // beta ring (2)
+    static constexpr int B_SIZE = 64;
     // gram ring (3): T^T fragment (C(T^T) = A-fragment of T), P hi/lo A-fragments
     static constexpr int G_TT = 0, G_PH = 512, G_PL = 1024, G_SIZE = 1536;
     // wgen ring (2): -Wt A-fragments for 32-deep steps
     static constexpr int W_WT = 0, W_SIZE = KP * 1024;
-    static constexpr int OFF_L = 0, OFF_S = OFF_L + 4 * L_SIZE, OFF_M = OFF_S + 2 * S_SIZE,
-                         OFF_G = OFF_M + 3 * M_SIZE, OFF_W = OFF_G + 3 * G_SIZE,
-                         LDS_BYTES = OFF_W + 2 * W_SIZE;
+    // per chain wave: its 16x16 output block, transposed to rows before the store
+    static constexpr int O_SIZE = 512;
+    static constexpr int OFF_L = 0, OFF_K = OFF_L + 4 * L_SIZE, OFF_B = OFF_K + 3 * K_SIZE,
+                         OFF_G = OFF_B + 2 * B_SIZE, OFF_W = OFF_G + 3 * G_SIZE,
+                         OFF_O = OFF_W + 2 * W_SIZE, LDS_BYTES = OFF_O + NCHAIN * O_SIZE;
 };
 
 struct BArgs {
@@ -162,10 +199,11 @@ struct BArgs {
 template <int DK, int DV, int NCB>
 __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(const BArgs a) {
     typedef Cfg<DK, NCB> C;
-    constexpr int KB = C::KB, KP = C::KP, NV = 16 * NCB;
+    constexpr int KB = C::KB, KP = C::KP, NV = C::NV;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
     const int r = lane & 15, g = lane >> 4;
 
     // blockIdx -> (group, slice): the slices of one (sequence, head) share an XCD
@@ -177,7 +215,8 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
     const int H = a.H, seq_pos = group / H, h = group % H;
     const int seq = a.num_ordered ? a.order[seq_pos] : seq_pos;
     const int64_t tbeg = a.cu[seq], tend = a.cu[seq + 1];
-    const int nch = (int)((tend - tbeg + 15) / 16);
+    const int64_t len = tend - tbeg;
+    const int nch = (int)((len + 15) / 16);
     const int col0 = slice * NV;
     if (nch == 0) {  // empty sequence: the final state is the initial state
         if (a.Sf && wave < NCB) {
@@ -192,10 +231,15 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
     const int64_t sbase = ((int64_t)seq * H + h) * DK * DV;
 
     auto lslot = [&](int c) { return smem + C::OFF_L + (c & 3) * C::L_SIZE; };
-    auto sslot = [&](int c) { return smem + C::OFF_S + (c & 1) * C::S_SIZE; };
-    auto mslot = [&](int c) { return smem + C::OFF_M + (c % 3) * C::M_SIZE; };
+    auto kslot = [&](int c) { return smem + C::OFF_K + (c % 3) * C::K_SIZE; };
+    auto bslot = [&](int c) { return smem + C::OFF_B + (c & 1) * C::B_SIZE; };
     auto gslot = [&](int c) { return smem + C::OFF_G + (c % 3) * C::G_SIZE; };
     auto wslot = [&](int c) { return smem + C::OFF_W + (c & 1) * C::W_SIZE; };
+    // per-lane byte offsets of the transposed reads (row 4g + j, columns +4q)
+    const int trj = (lane & 15) >> 2, trq = lane & 3;
+    const int tr_k = (4 * g + trj) * C::RSB + 8 * trq;   // [16][DK] tiles
+    const int tr_v = (4 * g + trj) * C::VRS + 8 * trq;   // [16][NV] tiles
+    const int tr_o = (4 * g + trj) * 32 + 8 * trq;       // [16][16] output block
 
     // Each role runs its own loop over iterations it = -3 .. it_end-1 with one LDS barrier
     // per iteration, so the loop-carried registers of one role never share a register (or a
@@ -205,115 +249,115 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
     // decay ring's period; padded iterations only pass the barrier).
     const int it_end = -3 + ((nch + 3 + 3) & ~3);
     const float floor2 = a.floor_;
-    // identity as a B fragment (for exact register transposes through the matrix core)
-    bf16x4 ident;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ident[i] = (bf16)((4 * g + i) == r ? 1.f : 0.f);
 
     if (wave >= C::W_DECAY0 && wave < C::W_GRAM) {
         // ================================================================ decay waves
         const int cb = wave - C::W_DECAY0;  // 16-channel block
         const int dch = 16 * cb + 4 * g;    // this lane's first channel
+        // value / gate blocks staged by this wave: block f = cb + KB*e; a wave past the last
+        // block reloads block cb % (2 NCB) and discards it (the loads stay unconditional)
+        int vg_f[C::VG_PER_WAVE];
+#pragma unroll
+        for (int e = 0; e < C::VG_PER_WAVE; ++e)
+            vg_f[e] = cb + KB * e < 2 * NCB ? cb + KB * e : cb % (2 * NCB);
         // Prefetch ring of four chunks; chunk c lives in slot (c + 1) & 3.  Loads are
-        // unconditional (the token index is clamped into the sequence; rows past its end
-        // are zeroed when consumed), so each lands in its own register and stays in flight.
+        // unconditional buffer loads bounded at the end of the sequence: rows past the end
+        // (and every row of chunks past the last) read as zero, which is the identity row
+        // (k = 0, lambda' = max(0, floor) = 0, beta = 0), so each load lands in its own
+        // register and stays in flight, and nothing is masked when consumed.
         u32x2 rq[4], rk[4], rl[4], rvg[C::VG_PER_WAVE][4];
         uint32_t rb[4];
-        // value / gate fragment sets staged by this wave: set f = cb + KB*e (block f >> 1,
-        // gate if f is odd); the loads are unconditional, so a wave past the last set
-        // reloads set cb % (2 NCB) and discards it
-        const bf16* vg_src[C::VG_PER_WAVE];
-        int vg_col[C::VG_PER_WAVE];
+        const uint32_t oq = (uint32_t)(r * (int)(2 * rowq) + 2 * dch);   // lane offsets (bytes)
+        const uint32_t ob = (uint32_t)(r * 2 * H);
+        uint32_t ov[C::VG_PER_WAVE];
 #pragma unroll
-        for (int e = 0; e < C::VG_PER_WAVE; ++e) {
-            const int f = cb + KB * e < 2 * NCB ? cb + KB * e : cb % (2 * NCB);
-            vg_src[e] = (f & 1) ? a.gate : a.v;
-            vg_col[e] = col0 + 16 * (f >> 1) + 4 * g;
-        }
-        auto load = [&](int c, auto SLOT) {
+        for (int e = 0; e < C::VG_PER_WAVE; ++e)
+            ov[e] = (uint32_t)(r * (int)(2 * rowv) + 2 * (col0 + 16 * (vg_f[e] >> 1) + 4 * g));
+        // uniform chunk bases, advanced by one chunk per load (loads go in chunk order)
+        const char* pq = reinterpret_cast<const char*>(a.q + tbeg * rowq + (int64_t)h * DK);
+        const char* pk = reinterpret_cast<const char*>(a.k + tbeg * rowq + (int64_t)h * DK);
+        const char* pl = reinterpret_cast<const char*>(a.la + tbeg * rowq + (int64_t)h * DK);
+        const char* pb = reinterpret_cast<const char*>(a.beta + tbeg * H + h);
+        const char* pv[C::VG_PER_WAVE];
+#pragma unroll
+        for (int e = 0; e < C::VG_PER_WAVE; ++e)
+            pv[e] = reinterpret_cast<const char*>(((vg_f[e] & 1) ? a.gate : a.v) + tbeg * rowv + (int64_t)h * DV);
+        const int64_t sq = 32 * rowq, sb = 32 * (int64_t)H, sv = 32 * rowv;  // bytes per chunk
+        int lrem = (int)min<int64_t>(len, 1 << 20);  // rows left at the next load's chunk
+        auto load = [&](auto SLOT) {
             constexpr int sl = decltype(SLOT)::value;
-            const int64_t t = min<int64_t>(tbeg + 16 * c + r, tend - 1);
-            const int64_t off = t * rowq + (int64_t)h * DK + dch;
-            rq[sl] = *reinterpret_cast<const u32x2*>(a.q + off);
-            rk[sl] = *reinterpret_cast<const u32x2*>(a.k + off);
-            rl[sl] = *reinterpret_cast<const u32x2*>(a.la + off);
-            rb[sl] = __builtin_bit_cast(uint16_t, a.beta[t * H + h]);
-            // value / gate rows of this wave's fragment sets: token r, columns +4g..+3
-            // (a wave with fewer sets than VG_PER_WAVE reloads its set; never stored)
+            const int rem = min(max(lrem, 0), 16);  // rows of this chunk (0: past the end)
+            const int nq = rem ? (rem - 1) * (int)(2 * rowq) + 2 * DK : 0;
+            const int nb = rem ? (rem - 1) * 2 * H + 2 : 0;
+            const int nv = rem ? (rem - 1) * (int)(2 * rowv) + 2 * DV : 0;
+            rq[sl] = bload8(rsrc(pq, nq), oq);
+            rk[sl] = bload8(rsrc(pk, nq), oq);
+            rl[sl] = bload8(rsrc(pl, nq), oq);
+            rb[sl] = __builtin_amdgcn_raw_buffer_load_b16(rsrc(pb, nb), ob, 0, 0);
 #pragma unroll
-            for (int e = 0; e < C::VG_PER_WAVE; ++e)
-                rvg[e][sl] = *reinterpret_cast<const u32x2*>(
-                    vg_src[e] + t * rowv + (int64_t)h * DV + vg_col[e]);
+            for (int e = 0; e < C::VG_PER_WAVE; ++e) rvg[e][sl] = bload8(rsrc(pv[e], nv), ov[e]);
+            if (rem) {  // chunks past the end keep their (unread) base
+                pq += sq; pk += sq; pl += sq; pb += sb;
+#pragma unroll
+                for (int e = 0; e < C::VG_PER_WAVE; ++e) pv[e] += sv;
+            }
+            lrem -= 16;
         };
         // issued in slot order (kept by the scheduling barriers), so the loads of the
         // slot consumed next are always the oldest in flight
-        load(0, std::integral_constant<int, 1>{});
+        load(std::integral_constant<int, 1>{});  // chunks 0..3
         __builtin_amdgcn_sched_barrier(0);
-        load(1, std::integral_constant<int, 2>{});
+        load(std::integral_constant<int, 2>{});
         __builtin_amdgcn_sched_barrier(0);
-        load(2, std::integral_constant<int, 3>{});
+        load(std::integral_constant<int, 3>{});
         __builtin_amdgcn_sched_barrier(0);
-        load(3, std::integral_constant<int, 0>{});
+        load(std::integral_constant<int, 0>{});
         __builtin_amdgcn_sched_barrier(0);
+        const int rowoff = r * C::RSB + 2 * dch;
         auto step = [&](const int it, auto PH) {
             constexpr int ph = decltype(PH)::value;
-            const int c = it + 3;  // decay-folded operands of chunk c (row layout: token r)
+            const int c = it + 3;  // decay-folded row tiles of chunk c (token r, channels dch..+3)
             if (c < nch) {
-                const bool valid = tbeg + 16 * c + r < tend;  // rows past the end: identity
-                const u32x2 zero2{0u, 0u};
-                const f32x4 q4 = unpack_bf4(valid ? rq[ph] : zero2) * a.scale;
-                const f32x4 k4 = unpack_bf4(valid ? rk[ph] : zero2);
-                const f32x4 l4 = unpack_bf4(valid ? rl[ph] : zero2);
-                const float bet = valid ? __builtin_bit_cast(float, rb[ph] << 16) : 0.f;
+                const f32x4 q4 = unpack_bf4(rq[ph]);
+                const f32x4 k4 = unpack_bf4(rk[ph]);
+                const f32x4 l4 = unpack_bf4(rl[ph]);
+                const float bet = __builtin_bit_cast(float, rb[ph] << 16);
+                f32x4 lam;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) lam[i] = fmaxf(l4[i], floor2);
                 f32x4 F, Fi, gam;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float lam = fmaxf(l4[i], floor2);
-                    const float G = row_scan(lam);          // inclusive cumsum over tokens
-                    const float GC = row_last(G);           // chunk total (rows >= C' add 0)
+                    const float G = row_scan(lam[i]);       // inclusive cumsum over tokens
+                    const float GC = row_last(G);           // chunk total
                     const float d = (G - GC) * kLog2e;      // >= 0
                     F[i] = __builtin_amdgcn_exp2f(d);
                     Fi[i] = __builtin_amdgcn_exp2f(-d);
                     gam[i] = GC;
                 }
-                const f32x4 qt = q4 * F, kt = k4 * F, kb = k4 * Fi;
                 bf16x4 qh, ql, kbh, kbl;
-                split4(qt, qh, ql);
-                split4(kb, kbh, kbl);
-                const bf16x4 kth = to_bf4(kt);
+                split4(q4 * F, qh, ql);
+                split4(k4 * Fi, kbh, kbl);
                 unsigned char* L = lslot(c);
-                unsigned char* Sh = sslot(c);
-                const int rowoff = r * C::RSB + 2 * dch;
-                *reinterpret_cast<bf16x4*>(L + C::L_QH + rowoff) = qh;
-                *reinterpret_cast<bf16x4*>(L + C::L_QL + rowoff) = ql;
-                *reinterpret_cast<bf16x4*>(Sh + C::S_KT + rowoff) = kth;
-                *reinterpret_cast<bf16x4*>(Sh + C::S_KBH + rowoff) = kbh;
-                *reinterpret_cast<bf16x4*>(Sh + C::S_KBL + rowoff) = kbl;
-                // transposed fragments through the matrix core (exact: products with 1)
-                const bf16x4 kbth = to_bf4(mfma16(kbh, ident, zero4()));
-                const bf16x4 kbtl = to_bf4(mfma16(kbl, ident, zero4()));
-                const bf16x4 ktt = to_bf4(mfma16(kth, ident, zero4()));
-                *reinterpret_cast<bf16x4*>(L + C::L_KBH + cb * 512 + lane * 8) = kbth;
-                *reinterpret_cast<bf16x4*>(L + C::L_KBL + cb * 512 + lane * 8) = kbtl;
-                *reinterpret_cast<bf16x4*>(mslot(c) + C::M_KTT + cb * 512 + lane * 8) = ktt;
-                if (r == 0) {
-                    f32x4 e;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) e[i] = __builtin_amdgcn_exp2f(gam[i] * kLog2e);
-                    *reinterpret_cast<f32x4*>(L + C::L_GAM + 4 * dch) = e;
-                }
-                if (cb == 0 && g == 0) *reinterpret_cast<float*>(Sh + C::S_BETA + 4 * r) = bet;
+                lds_st(L + C::L_QH + rowoff, qh);
+                lds_st(L + C::L_QL + rowoff, ql);
+                lds_st(L + C::L_KBH + rowoff, kbh);
+                lds_st(L + C::L_KBL + rowoff, kbl);
+                lds_st(kslot(c) + rowoff, to_bf4(k4 * F));
+                // gamma of channel dch + r from lanes r < 4 (one exponential per lane)
+                const float gsel = r == 0 ? gam[0] : r == 1 ? gam[1] : r == 2 ? gam[2] : gam[3];
+                const float ge = __builtin_amdgcn_exp2f(gsel * kLog2e);
+                if (r < 4) lds_st(L + C::L_GAM + 4 * (dch + r), ge);
+                if (cb == 0 && g == 0) lds_st(bslot(c) + 4 * r, bet);
 #pragma unroll
                 for (int e = 0; e < C::VG_PER_WAVE; ++e) {
                     const int f = cb + KB * e;
-                    if (f < 2 * NCB) {
-                        const bf16x4 x = __builtin_bit_cast(bf16x4, valid ? rvg[e][ph] : zero2);
-                        const bf16x4 xt = to_bf4(mfma16(x, ident, zero4()));  // C(block)
-                        *reinterpret_cast<bf16x4*>(L + C::L_VG + f * 512 + lane * 8) = xt;
-                    }
+                    if (f < 2 * NCB)  // row r, columns 16 (f >> 1) + 4g .. +3
+                        lds_st(L + ((f & 1) ? C::L_G : C::L_V) + r * C::VRS + 2 * (16 * (f >> 1) + 4 * g),
+                               rvg[e][ph]);
                 }
             }
-            load(it + 7, PH);  // past the last chunk: reads the last row, never used
+            load(PH);  // chunk it + 7; past the last chunk: reads nothing (zero rows), never used
             lds_barrier();
         };
         for (int it = -3; it < it_end; it += 4) {  // no exit between the four slots
@@ -328,17 +372,18 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
             // A, A^T of chunk it + 2 and T = (I + A)^-1 Diag(beta), kept as C(T^T)
             const int c = it + 2;
             if (c >= 0 && c < nch) {
-                const unsigned char* Sh = sslot(c);
+                const unsigned char* Kt = kslot(c);
+                const unsigned char* Kb = lslot(c) + C::L_KBH;
                 f32x4 ac = zero4(), atc = zero4();
 #pragma unroll
                 for (int p = 0; p < KP; ++p) {
                     const int off = r * C::RSB + 2 * (32 * p + 8 * g);
-                    const bf16x8 kt = *reinterpret_cast<const bf16x8*>(Sh + C::S_KT + off);
-                    const bf16x8 kb = *reinterpret_cast<const bf16x8*>(Sh + C::S_KBH + off);
+                    const bf16x8 kt = lds_ld<bf16x8>(Kt + off);
+                    const bf16x8 kb = lds_ld<bf16x8>(Kb + off);
                     ac = mfma32(kt, kb, ac);    // C(Kt Kb^T)
                     atc = mfma32(kb, kt, atc);  // C(Kb Kt^T)
                 }
-                const float* beta = reinterpret_cast<const float*>(Sh + C::S_BETA);
+                const float* beta = reinterpret_cast<const float*>(bslot(c));
                 const float br = beta[r];
                 const f32x4 bi = *reinterpret_cast<const f32x4*>(beta + 4 * g);
                 f32x4 cA, cAT;  // C(A), C(A^T)
@@ -349,19 +394,18 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
                     cAT[i] = row < r ? br * atc[i] : 0.f;
                 }
                 // A-fragment(X) == C(X^T): powers of A and of A^T in both layouts
-                const f32x4 cA2 = prod3(cAT, cA);      // C(A A)
-                const f32x4 cAT2 = prod3(cA, cAT);     // C(A^T A^T)
-                const f32x4 cA4 = prod3(cAT2, cA2);
-                const f32x4 cAT4 = prod3(cA2, cAT2);
-                const f32x4 cAT8 = prod3(cA4, cAT4);
+                const f32x4 cA2 = prod(cAT, cA);      // C(A A)
+                const f32x4 cAT2 = prod(cA, cAT);     // C(A^T A^T)
+                const f32x4 cA4 = prod(cAT2, cA2);
+                const f32x4 cAT4 = prod(cA2, cAT2);
+                const f32x4 cAT8 = prod(cA4, cAT4);
                 f32x4 y = cAT8;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) y[i] += (4 * g + i) == r ? 1.f : 0.f;  // I + (A^T)^8
-                y += prod3(cA4, y);   // (I + (A^T)^4) y
-                y += prod3(cA2, y);   // (I + (A^T)^2) y
-                y -= prod3(cA, y);    // (I - A^T) y   ->  X^T = ((I + A)^-1)^T
-                const bf16x4 tt = to_bf4(y * bi);  // C(T^T): row 4g+i of X^T scaled by beta
-                *reinterpret_cast<bf16x4*>(gslot(c) + C::G_TT + lane * 8) = tt;
+                y += prod(cA4, y);   // (I + (A^T)^4) y
+                y += prod(cA2, y);   // (I + (A^T)^2) y
+                y -= prod(cA, y);    // (I - A^T) y   ->  X^T = ((I + A)^-1)^T
+                lds_st(gslot(c) + C::G_TT + lane * 8, to_bf4(y * bi));  // C(T^T), rows scaled by beta
             }
             lds_barrier();
         }
@@ -372,16 +416,15 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
                 // P of chunk it + 2, as A-fragments hi/lo: C(P^T) = C(Kb Qt^T)
                 const int c = it + 2;
                 if (c >= 0 && c < nch) {
-                    const unsigned char* Sh = sslot(c);
                     const unsigned char* L = lslot(c);
                     f32x4 acc = zero4();
 #pragma unroll
                     for (int p = 0; p < KP; ++p) {
                         const int off = r * C::RSB + 2 * (32 * p + 8 * g);
-                        const bf16x8 kbh = *reinterpret_cast<const bf16x8*>(Sh + C::S_KBH + off);
-                        const bf16x8 kbl = *reinterpret_cast<const bf16x8*>(Sh + C::S_KBL + off);
-                        const bf16x8 qh = *reinterpret_cast<const bf16x8*>(L + C::L_QH + off);
-                        const bf16x8 ql = *reinterpret_cast<const bf16x8*>(L + C::L_QL + off);
+                        const bf16x8 kbh = lds_ld<bf16x8>(L + C::L_KBH + off);
+                        const bf16x8 kbl = lds_ld<bf16x8>(L + C::L_KBL + off);
+                        const bf16x8 qh = lds_ld<bf16x8>(L + C::L_QH + off);
+                        const bf16x8 ql = lds_ld<bf16x8>(L + C::L_QL + off);
                         acc = mfma32(kbh, qh, acc);
                         acc = mfma32(kbh, ql, acc);
                         acc = mfma32(kbl, qh, acc);
@@ -391,23 +434,23 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
                     for (int i = 0; i < 4; ++i) acc[i] = (4 * g + i) <= r ? acc[i] : 0.f;
                     bf16x4 ph_, pl_;
                     split4(acc, ph_, pl_);
-                    *reinterpret_cast<bf16x4*>(gslot(c) + C::G_PH + lane * 8) = ph_;
-                    *reinterpret_cast<bf16x4*>(gslot(c) + C::G_PL + lane * 8) = pl_;
+                    lds_st(gslot(c) + C::G_PH + lane * 8, ph_);
+                    lds_st(gslot(c) + C::G_PL + lane * 8, pl_);
                 }
             }
             {
                 // -Wt of chunk it + 1 as 32-deep A-fragments: C(Wt^T) blocks = Kt^T T^T
                 const int c = it + 1;
                 if (c >= 0 && c < nch) {
-                    const bf16x4 tt = *reinterpret_cast<const bf16x4*>(gslot(c) + C::G_TT + lane * 8);
-                    const unsigned char* M = mslot(c);
+                    // -T^T: flip the bf16 sign bits once, so the products come out negated
+                    const bf16x4 ntt = __builtin_bit_cast(
+                        bf16x4, lds_ld<u32x2>(gslot(c) + C::G_TT + lane * 8) ^ 0x80008000u);
+                    const unsigned char* Kt = kslot(c) + tr_k;
                     unsigned char* W = wslot(c);
 #pragma unroll
                     for (int nb = 0; nb < KB; ++nb) {
-                        const bf16x4 ktt = *reinterpret_cast<const bf16x4*>(M + C::M_KTT + nb * 512 + lane * 8);
-                        const f32x4 w = mfma16(ktt, tt, zero4());  // w[i] = Wt[r][16nb + 4g + i]
-                        *reinterpret_cast<bf16x4*>(W + C::W_WT + (nb >> 1) * 1024 + lane * 16 + (nb & 1) * 8) =
-                            to_bf4(-w);
+                        const f32x4 w = mfma16(lds_tr(Kt + 32 * nb), ntt, zero4());  // -Wt[r][16nb + 4g + i]
+                        lds_st(W + C::W_WT + (nb >> 1) * 1024 + lane * 16 + (nb & 1) * 8, to_bf4(w));
                     }
                 }
             }
@@ -423,6 +466,7 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 S[b][i] = a.S0 ? a.S0[sbase + (16 * b + 4 * g + i) * DV + ccol] : 0.f;
+        const float scale = a.scale;
         for (int it = -3; it < it_end; ++it) {
             const int c = it;  // state step of chunk c
             if (c >= 0 && c < nch) {
@@ -433,12 +477,11 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
 #pragma unroll
                 for (int b = 0; b < KB; ++b) Sb[b] = to_bf4(S[b]);
                 // Ut = T V
-                const bf16x4 tt = *reinterpret_cast<const bf16x4*>(Gs + C::G_TT + lane * 8);
-                const bf16x4 vb = *reinterpret_cast<const bf16x4*>(L + C::L_VG + (2 * wave) * 512 + lane * 8);
-                f32x4 U = mfma16(tt, vb, zero4());
+                const bf16x4 tt = lds_ld<bf16x4>(Gs + C::G_TT + lane * 8);
+                f32x4 U = mfma16(tt, lds_tr(L + C::L_V + tr_v + 32 * wave), zero4());
 #pragma unroll
                 for (int p = 0; p < KP; ++p) {  // U = Ut - Wt S'
-                    const bf16x8 w = *reinterpret_cast<const bf16x8*>(W + C::W_WT + p * 1024 + lane * 16);
+                    const bf16x8 w = lds_ld<bf16x8>(W + C::W_WT + p * 1024 + lane * 16);
                     U = mfma16(lo4(w), Sb[2 * p], U);
                     U = mfma16(hi4(w), Sb[2 * p + 1], U);
                 }
@@ -446,34 +489,34 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
 #pragma unroll
                 for (int b = 0; b < KB; ++b) {  // O = Qt S' (hi and lo halves of Qt)
                     const int off = r * C::RSB + 2 * (16 * b + 4 * g);
-                    O = mfma16(*reinterpret_cast<const bf16x4*>(L + C::L_QH + off), Sb[b], O);
-                    O = mfma16(*reinterpret_cast<const bf16x4*>(L + C::L_QL + off), Sb[b], O);
+                    O = mfma16(lds_ld<bf16x4>(L + C::L_QH + off), Sb[b], O);
+                    O = mfma16(lds_ld<bf16x4>(L + C::L_QL + off), Sb[b], O);
                 }
                 bf16x4 uh, ul;
                 split4(U, uh, ul);
-                const bf16x4 ph_ = *reinterpret_cast<const bf16x4*>(Gs + C::G_PH + lane * 8);
-                const bf16x4 pl_ = *reinterpret_cast<const bf16x4*>(Gs + C::G_PL + lane * 8);
+                const bf16x4 ph_ = lds_ld<bf16x4>(Gs + C::G_PH + lane * 8);
+                const bf16x4 pl_ = lds_ld<bf16x4>(Gs + C::G_PL + lane * 8);
                 O = mfma16(ph_, uh, O);  // + P U
                 O = mfma16(ph_, ul, O);
                 O = mfma16(pl_, uh, O);
                 // S <- S' + Kb^T U, row block by row block
 #pragma unroll
                 for (int b = 0; b < KB; ++b) {
-                    const bf16x4 kh = *reinterpret_cast<const bf16x4*>(L + C::L_KBH + b * 512 + lane * 8);
-                    const bf16x4 kl = *reinterpret_cast<const bf16x4*>(L + C::L_KBL + b * 512 + lane * 8);
+                    const bf16x4 kh = lds_tr(L + C::L_KBH + tr_k + 32 * b);
+                    const bf16x4 kl = lds_tr(L + C::L_KBL + tr_k + 32 * b);
                     S[b] = mfma16(kh, uh, S[b]);
                     S[b] = mfma16(kh, ul, S[b]);
                     S[b] = mfma16(kl, uh, S[b]);
                 }
-                // gated output rows of this chunk
-                const int64_t t0 = tbeg + 16 * c;
-                const int cp = (int)min<int64_t>(16, tend - t0);
-                const f32x4 gt = to_f4(*reinterpret_cast<const bf16x4*>(L + C::L_VG + (2 * wave + 1) * 512 + lane * 8));
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = 4 * g + i;
-                    if (row < cp) a.out[(t0 + row) * rowv + (int64_t)h * DV + ccol] = (bf16)(gt[i] * O[i]);
-                }
+                // gated output rows of this chunk: the block O[4g+i][r] goes through LDS as the
+                // rows of O^T and comes back transposed, O[r][4g..4g+3], one 8-byte store per lane
+                const f32x4 gt = to_f4(lds_tr(L + C::L_G + tr_v + 32 * wave)) * scale;
+                unsigned char* Ob = smem + C::OFF_O + wave * C::O_SIZE;
+                lds_st(Ob + r * 32 + 8 * g, to_bf4(gt * O));
+                const bf16x4 orow = lds_tr(Ob + tr_o);
+                const int64_t t0 = tbeg + 16 * (int64_t)c;
+                if (t0 + r < tend)
+                    *reinterpret_cast<bf16x4*>(a.out + (t0 + r) * rowv + (int64_t)h * DV + col0 + 16 * wave + 4 * g) = orow;
                 if (c + 1 < nch) {  // S' of the next chunk
                     const float* gn = reinterpret_cast<const float*>(lslot(c + 1) + C::L_GAM);
 #pragma unroll
