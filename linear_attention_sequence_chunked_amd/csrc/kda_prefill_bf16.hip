@@ -26,8 +26,8 @@
 //
 // Workgroup = one (sequence, head, slice of NV = 16*NCB value columns).  Waves:
 //   chain  (NCB)   : one 16-column block of S each; state step of chunk c
-//   decay  (DK/16) : one 16-channel block each; row tiles of chunk c+3 from registers
-//                    loaded four chunks earlier
+//   decay  (DK/32) : 32 key channels each; row tiles of chunk c+3 from registers
+//                    loaded PF chunks earlier
 //   gram           : A, A^T of chunk c+2 and T through the nilpotent product
 //                    (I+A)^-1 = (I-A)(I+A^2)(I+A^4)(I+A^8)  (A^16 = 0), all in registers
 //   pw             : P of chunk c+2, then Wt of chunk c+1
@@ -58,6 +58,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -71,6 +72,9 @@ __device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
 // gfx950: the upper operand half is read after issue and no wait states were inserted).
 __device__ __forceinline__ bf16x4 lo4(bf16x8 x) { return bf16x4{x[0], x[1], x[2], x[3]}; }
 __device__ __forceinline__ bf16x4 hi4(bf16x8 x) { return bf16x4{x[4], x[5], x[6], x[7]}; }
+__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
+    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
 // sum over both 16-deep halves: lo(a) lo(b) + hi(a) hi(b)
 __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
     return mfma16(hi4(a), hi4(b), mfma16(lo4(a), lo4(b), c));
@@ -142,44 +146,66 @@ __device__ __forceinline__ u32x2 bload8(__amdgpu_buffer_rsrc_t rs, uint32_t off)
     return __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
 }
 
+// f(integral_constant<J>) for J = J0 .. J1-1, in order (compile-time register-slot indices)
+template <int J0, int J1, typename F>
+__device__ __forceinline__ void unroll(F&& f) {
+    if constexpr (J0 < J1) {
+        f(std::integral_constant<int, J0>{});
+        unroll<J0 + 1, J1>(f);
+    }
+}
+
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+}
+
 // eight bytes of bf16 pairs -> four floats
 __device__ __forceinline__ f32x4 unpack_bf4(u32x2 w) { return to_f4(__builtin_bit_cast(bf16x4, w)); }
 
 template <int DK, int NCB>
 struct Cfg {
-    static constexpr int KB = DK / 16;        // 16-channel blocks (= decay waves)
+    static constexpr int KB = DK / 16;        // 16-channel blocks
+    static constexpr int NDW = DK / 32;       // decay waves (32 channels each)
     static constexpr int KP = DK / 32;        // 32-channel steps of the state products
     static constexpr int NV = 16 * NCB;       // value columns per workgroup
     static constexpr int NCHAIN = NCB;
+    static constexpr int PF = 4;              // chunks of input prefetched ahead (ring depth)
     static constexpr int W_DECAY0 = NCHAIN;
-    static constexpr int W_GRAM = NCHAIN + KB;
+    static constexpr int W_GRAM = NCHAIN + NDW;
     static constexpr int W_PW = W_GRAM + 1;   // P of chunk c+2, then Wt of chunk c+1
     static constexpr int NWAVES = W_GRAM + 2;
     static constexpr int THREADS = 64 * NWAVES;
-    // row-major [16][DK] bf16 tiles, padded rows (bytes)
-    static constexpr int RSB = DK * 2 + 16;
-    static constexpr int ROWT = 16 * RSB;
-    // row-major [16][NV] bf16 value and gate tiles
-    static constexpr int VRS = NV * 2 + 16;
+    // Row-major [16][DK] bf16 tiles with padded rows (bytes).  The padding is chosen per
+    // tile from how it is read (measured on gfx950, 64-lane wave):
+    //   Qt tiles, read as 8-byte row pieces (A-fragments): rows of 2 DK + 24 bytes
+    //   Kb / Kt tiles, read as 16-byte row pieces and by transposed reads: 2 DK + 32
+    // (2 DK + 16 costs a two-way bank conflict on both 8- and 16-byte row reads).
+    static constexpr int RSQ = DK * 2 + 24;
+    static constexpr int RSK = DK * 2 + 32;
+    static constexpr int ROWQ = 16 * RSQ, ROWK = 16 * RSK;
+    // row-major [16][NV] bf16 value and gate tiles, read transposed: 2 NV + 32 bytes puts
+    // the four rows of each transposed 16-lane group in distinct banks
+    static constexpr int VRS = NV * 2 + 32;
     static constexpr int VT = 16 * VRS;
     // value/gate 16x16 blocks staged per decay wave (block f: columns 16 (f >> 1), gate if
     // f is odd)
-    static constexpr int VG_PER_WAVE = (2 * NCB + KB - 1) / KB;
+    static constexpr int VG_PER_WAVE = (2 * NCB + NDW - 1) / NDW;
     // long ring (4 slots, chunk c written at iteration c-3, read up to iteration c):
     // Qt hi/lo, Kb hi/lo rows, gamma, value and gate rows
-    static constexpr int L_QH = 0, L_QL = ROWT, L_KBH = 2 * ROWT, L_KBL = 3 * ROWT,
-                         L_GAM = 4 * ROWT, L_V = L_GAM + DK * 4, L_G = L_V + VT,
+    static constexpr int L_QH = 0, L_QL = ROWQ, L_KBH = 2 * ROWQ, L_KBL = 2 * ROWQ + ROWK,
+                         L_GAM = 2 * ROWQ + 2 * ROWK, L_V = L_GAM + DK * 4, L_G = L_V + VT,
                          L_SIZE = L_G + VT;
     // Kt ring (3): Kt rows (gram at c-2, Wt at c-1)
-    static constexpr int K_SIZE = ROWT;
+    static constexpr int K_SIZE = ROWK;
     // beta ring (2)
     static constexpr int B_SIZE = 64;
     // gram ring (3): T^T fragment (C(T^T) = A-fragment of T), P hi/lo A-fragments
     static constexpr int G_TT = 0, G_PH = 512, G_PL = 1024, G_SIZE = 1536;
     // wgen ring (2): -Wt A-fragments for 32-deep steps
     static constexpr int W_WT = 0, W_SIZE = KP * 1024;
-    // per chain wave: its 16x16 output block, transposed to rows before the store
-    static constexpr int O_SIZE = 512;
+    // per chain wave: its 16x16 output block, transposed to rows before the store (rows
+    // of 40 bytes: conflict-free for both the 8-byte writes and the transposed reads)
+    static constexpr int ORS = 40, O_SIZE = 16 * ORS;
     static constexpr int OFF_L = 0, OFF_K = OFF_L + 4 * L_SIZE, OFF_B = OFF_K + 3 * K_SIZE,
                          OFF_G = OFF_B + 2 * B_SIZE, OFF_W = OFF_G + 3 * G_SIZE,
                          OFF_O = OFF_W + 2 * W_SIZE, LDS_BYTES = OFF_O + NCHAIN * O_SIZE;
@@ -237,36 +263,47 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
     auto wslot = [&](int c) { return smem + C::OFF_W + (c & 1) * C::W_SIZE; };
     // per-lane byte offsets of the transposed reads (row 4g + j, columns +4q)
     const int trj = (lane & 15) >> 2, trq = lane & 3;
-    const int tr_k = (4 * g + trj) * C::RSB + 8 * trq;   // [16][DK] tiles
+    const int tr_k = (4 * g + trj) * C::RSK + 8 * trq;   // Kb / Kt tiles
     const int tr_v = (4 * g + trj) * C::VRS + 8 * trq;   // [16][NV] tiles
-    const int tr_o = (4 * g + trj) * 32 + 8 * trq;       // [16][16] output block
+    const int tr_o = (4 * g + trj) * C::ORS + 8 * trq;   // [16][16] output block
 
     // Each role runs its own loop over iterations it = -3 .. it_end-1 with one LDS barrier
     // per iteration, so the loop-carried registers of one role never share a register (or a
     // merge point) with another's, and a load target is never copied (which would wait for
     // the load).  Iteration it: decay builds chunk it+3, gram and P chunk it+2, Wt chunk
-    // it+1, the chain steps chunk it.  The count is padded to a multiple of four (the
-    // decay ring's period; padded iterations only pass the barrier).
-    const int it_end = -3 + ((nch + 3 + 3) & ~3);
+    // it+1, the chain steps chunk it.  The count is padded to a multiple of the prefetch
+    // ring's depth (its period; padded iterations only pass the barrier).
+    constexpr int PF = C::PF;
+    const int it_end = -3 + (nch + 3 + PF - 1) / PF * PF;
     const float floor2 = a.floor_;
 
     if (wave >= C::W_DECAY0 && wave < C::W_GRAM) {
         // ================================================================ decay waves
-        const int cb = wave - C::W_DECAY0;  // 16-channel block
-        const int dch = 16 * cb + 4 * g;    // this lane's first channel
-        // value / gate blocks staged by this wave: block f = cb + KB*e; a wave past the last
-        // block reloads block cb % (2 NCB) and discards it (the loads stay unconditional)
+        // Each decay wave owns 32 key channels; lane (r, g) holds token r, channels
+        // dch .. dch+7 (two groups of four), so each 16-byte load fetches half a 128-byte
+        // line (fewer cache-line requests per byte than 8-byte pieces).
+        const int w = wave - C::W_DECAY0;   // 32-channel block
+        const int dch = 32 * w + 8 * g;     // this lane's first channel
+        // value / gate blocks staged by this wave: block f = w + NDW*e.  A wave past the last
+        // block still issues the load (the loads stay unconditional) over an empty range,
+        // which reads nothing.
+        constexpr int NDW = C::NDW;
         int vg_f[C::VG_PER_WAVE];
+        bool vg_own[C::VG_PER_WAVE];
 #pragma unroll
-        for (int e = 0; e < C::VG_PER_WAVE; ++e)
-            vg_f[e] = cb + KB * e < 2 * NCB ? cb + KB * e : cb % (2 * NCB);
-        // Prefetch ring of four chunks; chunk c lives in slot (c + 1) & 3.  Loads are
+        for (int e = 0; e < C::VG_PER_WAVE; ++e) {
+            vg_own[e] = w + NDW * e < 2 * NCB;
+            vg_f[e] = vg_own[e] ? w + NDW * e : w % (2 * NCB);
+        }
+        const bool own_beta = w == 0;
+        // Prefetch ring of PF chunks; chunk c lives in slot (c + 1) % PF.  Loads are
         // unconditional buffer loads bounded at the end of the sequence: rows past the end
         // (and every row of chunks past the last) read as zero, which is the identity row
         // (k = 0, lambda' = max(0, floor) = 0, beta = 0), so each load lands in its own
         // register and stays in flight, and nothing is masked when consumed.
-        u32x2 rq[4], rk[4], rl[4], rvg[C::VG_PER_WAVE][4];
-        uint32_t rb[4];
+        u32x4 rq[PF], rk[PF], rl[PF];
+        u32x2 rvg[C::VG_PER_WAVE][PF];
+        uint32_t rb[PF];
         const uint32_t oq = (uint32_t)(r * (int)(2 * rowq) + 2 * dch);   // lane offsets (bytes)
         const uint32_t ob = (uint32_t)(r * 2 * H);
         uint32_t ov[C::VG_PER_WAVE];
@@ -288,14 +325,15 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
             constexpr int sl = decltype(SLOT)::value;
             const int rem = min(max(lrem, 0), 16);  // rows of this chunk (0: past the end)
             const int nq = rem ? (rem - 1) * (int)(2 * rowq) + 2 * DK : 0;
-            const int nb = rem ? (rem - 1) * 2 * H + 2 : 0;
+            const int nb = (rem && own_beta) ? (rem - 1) * 2 * H + 2 : 0;
             const int nv = rem ? (rem - 1) * (int)(2 * rowv) + 2 * DV : 0;
-            rq[sl] = bload8(rsrc(pq, nq), oq);
-            rk[sl] = bload8(rsrc(pk, nq), oq);
-            rl[sl] = bload8(rsrc(pl, nq), oq);
+            rq[sl] = bload16(rsrc(pq, nq), oq);
+            rk[sl] = bload16(rsrc(pk, nq), oq);
+            rl[sl] = bload16(rsrc(pl, nq), oq);
             rb[sl] = __builtin_amdgcn_raw_buffer_load_b16(rsrc(pb, nb), ob, 0, 0);
 #pragma unroll
-            for (int e = 0; e < C::VG_PER_WAVE; ++e) rvg[e][sl] = bload8(rsrc(pv[e], nv), ov[e]);
+            for (int e = 0; e < C::VG_PER_WAVE; ++e)
+                rvg[e][sl] = bload8(rsrc(pv[e], vg_own[e] ? nv : 0), ov[e]);
             if (rem) {  // chunks past the end keep their (unread) base
                 pq += sq; pk += sq; pl += sq; pb += sb;
 #pragma unroll
@@ -305,66 +343,63 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
         };
         // issued in slot order (kept by the scheduling barriers), so the loads of the
         // slot consumed next are always the oldest in flight
-        load(std::integral_constant<int, 1>{});  // chunks 0..3
-        __builtin_amdgcn_sched_barrier(0);
-        load(std::integral_constant<int, 2>{});
-        __builtin_amdgcn_sched_barrier(0);
-        load(std::integral_constant<int, 3>{});
-        __builtin_amdgcn_sched_barrier(0);
-        load(std::integral_constant<int, 0>{});
-        __builtin_amdgcn_sched_barrier(0);
-        const int rowoff = r * C::RSB + 2 * dch;
+        unroll<0, PF>([&](auto J) {  // chunks 0 .. PF-1
+            load(std::integral_constant<int, (decltype(J)::value + 1) % PF>{});
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        const int rowq = r * C::RSQ + 2 * dch, rowk = r * C::RSK + 2 * dch;
         auto step = [&](const int it, auto PH) {
             constexpr int ph = decltype(PH)::value;
-            const int c = it + 3;  // decay-folded row tiles of chunk c (token r, channels dch..+3)
+            const int c = it + 3;  // decay-folded row tiles of chunk c (token r, channels dch..+7)
             if (c < nch) {
-                const f32x4 q4 = unpack_bf4(rq[ph]);
-                const f32x4 k4 = unpack_bf4(rk[ph]);
-                const f32x4 l4 = unpack_bf4(rl[ph]);
-                const float bet = __builtin_bit_cast(float, rb[ph] << 16);
-                f32x4 lam;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) lam[i] = fmaxf(l4[i], floor2);
-                f32x4 F, Fi, gam;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float G = row_scan(lam[i]);       // inclusive cumsum over tokens
-                    const float GC = row_last(G);           // chunk total
-                    const float d = (G - GC) * kLog2e;      // >= 0
-                    F[i] = __builtin_amdgcn_exp2f(d);
-                    Fi[i] = __builtin_amdgcn_exp2f(-d);
-                    gam[i] = GC;
-                }
-                bf16x4 qh, ql, kbh, kbl;
-                split4(q4 * F, qh, ql);
-                split4(k4 * Fi, kbh, kbl);
                 unsigned char* L = lslot(c);
-                lds_st(L + C::L_QH + rowoff, qh);
-                lds_st(L + C::L_QL + rowoff, ql);
-                lds_st(L + C::L_KBH + rowoff, kbh);
-                lds_st(L + C::L_KBL + rowoff, kbl);
-                lds_st(kslot(c) + rowoff, to_bf4(k4 * F));
-                // gamma of channel dch + r from lanes r < 4 (one exponential per lane)
-                const float gsel = r == 0 ? gam[0] : r == 1 ? gam[1] : r == 2 ? gam[2] : gam[3];
+                f32x4 gam[2];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {  // channels dch + 4hh .. +3
+                    const f32x4 q4 = unpack_bf4(u32x2{rq[ph][2 * hh], rq[ph][2 * hh + 1]});
+                    const f32x4 k4 = unpack_bf4(u32x2{rk[ph][2 * hh], rk[ph][2 * hh + 1]});
+                    const f32x4 l4 = unpack_bf4(u32x2{rl[ph][2 * hh], rl[ph][2 * hh + 1]});
+                    f32x4 F, Fi;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float G = row_scan(fmaxf(l4[i], floor2));  // inclusive cumsum over tokens
+                        const float GC = row_last(G);                    // chunk total
+                        const float d = (G - GC) * kLog2e;               // >= 0
+                        F[i] = __builtin_amdgcn_exp2f(d);
+                        Fi[i] = __builtin_amdgcn_exp2f(-d);
+                        gam[hh][i] = GC;
+                    }
+                    bf16x4 qh, ql, kbh, kbl;
+                    split4(q4 * F, qh, ql);
+                    split4(k4 * Fi, kbh, kbl);
+                    lds_st(L + C::L_QH + rowq + 8 * hh, qh);
+                    lds_st(L + C::L_QL + rowq + 8 * hh, ql);
+                    lds_st(L + C::L_KBH + rowk + 8 * hh, kbh);
+                    lds_st(L + C::L_KBL + rowk + 8 * hh, kbl);
+                    lds_st(kslot(c) + rowk + 8 * hh, to_bf4(k4 * F));
+                }
+                // gamma of channel dch + r from lanes r < 8 (one exponential per lane)
+                const f32x4 gh = r < 4 ? gam[0] : gam[1];
+                const int r4 = r & 3;
+                const float gsel = r4 == 0 ? gh[0] : r4 == 1 ? gh[1] : r4 == 2 ? gh[2] : gh[3];
                 const float ge = __builtin_amdgcn_exp2f(gsel * kLog2e);
-                if (r < 4) lds_st(L + C::L_GAM + 4 * (dch + r), ge);
-                if (cb == 0 && g == 0) lds_st(bslot(c) + 4 * r, bet);
+                if (r < 8) lds_st(L + C::L_GAM + 4 * (dch + r), ge);
+                if (own_beta && g == 0) lds_st(bslot(c) + 4 * r, __builtin_bit_cast(float, rb[ph] << 16));
 #pragma unroll
                 for (int e = 0; e < C::VG_PER_WAVE; ++e) {
-                    const int f = cb + KB * e;
+                    const int f = w + NDW * e;
                     if (f < 2 * NCB)  // row r, columns 16 (f >> 1) + 4g .. +3
                         lds_st(L + ((f & 1) ? C::L_G : C::L_V) + r * C::VRS + 2 * (16 * (f >> 1) + 4 * g),
                                rvg[e][ph]);
                 }
             }
-            load(PH);  // chunk it + 7; past the last chunk: reads nothing (zero rows), never used
+            load(PH);  // chunk it + 3 + PF; past the last chunk: reads nothing (zero rows)
             lds_barrier();
         };
-        for (int it = -3; it < it_end; it += 4) {  // no exit between the four slots
-            step(it, std::integral_constant<int, 1>{});
-            step(it + 1, std::integral_constant<int, 2>{});
-            step(it + 2, std::integral_constant<int, 3>{});
-            step(it + 3, std::integral_constant<int, 0>{});
+        for (int it = -3; it < it_end; it += PF) {  // no exit between the slots
+            unroll<0, PF>([&](auto J) {
+                step(it + decltype(J)::value, std::integral_constant<int, (decltype(J)::value + 1) % PF>{});
+            });
         }
     } else if (wave == C::W_GRAM) {
         // ================================================================ gram wave
@@ -377,7 +412,7 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
                 f32x4 ac = zero4(), atc = zero4();
 #pragma unroll
                 for (int p = 0; p < KP; ++p) {
-                    const int off = r * C::RSB + 2 * (32 * p + 8 * g);
+                    const int off = r * C::RSK + 2 * (32 * p + 8 * g);
                     const bf16x8 kt = lds_ld<bf16x8>(Kt + off);
                     const bf16x8 kb = lds_ld<bf16x8>(Kb + off);
                     ac = mfma32(kt, kb, ac);    // C(Kt Kb^T)
@@ -420,11 +455,13 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
                     f32x4 acc = zero4();
 #pragma unroll
                     for (int p = 0; p < KP; ++p) {
-                        const int off = r * C::RSB + 2 * (32 * p + 8 * g);
-                        const bf16x8 kbh = lds_ld<bf16x8>(L + C::L_KBH + off);
-                        const bf16x8 kbl = lds_ld<bf16x8>(L + C::L_KBL + off);
-                        const bf16x8 qh = lds_ld<bf16x8>(L + C::L_QH + off);
-                        const bf16x8 ql = lds_ld<bf16x8>(L + C::L_QL + off);
+                        const int offk = r * C::RSK + 2 * (32 * p + 8 * g);
+                        const int offq = r * C::RSQ + 2 * (32 * p + 8 * g);
+                        const bf16x8 kbh = lds_ld<bf16x8>(L + C::L_KBH + offk);
+                        const bf16x8 kbl = lds_ld<bf16x8>(L + C::L_KBL + offk);
+                        // Qt rows are padded for 8-byte reads: two per 16-byte piece
+                        const bf16x8 qh = cat8(lds_ld<bf16x4>(L + C::L_QH + offq), lds_ld<bf16x4>(L + C::L_QH + offq + 8));
+                        const bf16x8 ql = cat8(lds_ld<bf16x4>(L + C::L_QL + offq), lds_ld<bf16x4>(L + C::L_QL + offq + 8));
                         acc = mfma32(kbh, qh, acc);
                         acc = mfma32(kbh, ql, acc);
                         acc = mfma32(kbl, qh, acc);
@@ -458,6 +495,9 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
         }
     } else {
         // ================================================================ chain waves
+        // The state step is the serial critical path: its instructions win issue
+        // arbitration over the other roles' on the same SIMD.
+        __builtin_amdgcn_s_setprio(3);
         // fp32 state S' of rows 16b+4g+i, value column ccol, in MFMA accumulator layout
         const int ccol = col0 + 16 * wave + r;
         f32x4 S[KB];
@@ -473,9 +513,14 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
                 const unsigned char* L = lslot(c);
                 const unsigned char* Gs = gslot(c);
                 const unsigned char* W = wslot(c);
-                bf16x4 Sb[KB];  // bf16 copy of S' (B operands)
+                // S' = Diag(gamma) S, and its bf16 copy (the B operands of Wt S' and Qt S')
+                const float* gc = reinterpret_cast<const float*>(L + C::L_GAM);
+                bf16x4 Sb[KB];
 #pragma unroll
-                for (int b = 0; b < KB; ++b) Sb[b] = to_bf4(S[b]);
+                for (int b = 0; b < KB; ++b) {
+                    S[b] *= *reinterpret_cast<const f32x4*>(gc + 16 * b + 4 * g);
+                    Sb[b] = to_bf4(S[b]);
+                }
                 // Ut = T V
                 const bf16x4 tt = lds_ld<bf16x4>(Gs + C::G_TT + lane * 8);
                 f32x4 U = mfma16(tt, lds_tr(L + C::L_V + tr_v + 32 * wave), zero4());
@@ -488,7 +533,7 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
                 f32x4 O = zero4();
 #pragma unroll
                 for (int b = 0; b < KB; ++b) {  // O = Qt S' (hi and lo halves of Qt)
-                    const int off = r * C::RSB + 2 * (16 * b + 4 * g);
+                    const int off = r * C::RSQ + 2 * (16 * b + 4 * g);
                     O = mfma16(lds_ld<bf16x4>(L + C::L_QH + off), Sb[b], O);
                     O = mfma16(lds_ld<bf16x4>(L + C::L_QL + off), Sb[b], O);
                 }
@@ -512,21 +557,11 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
                 // rows of O^T and comes back transposed, O[r][4g..4g+3], one 8-byte store per lane
                 const f32x4 gt = to_f4(lds_tr(L + C::L_G + tr_v + 32 * wave)) * scale;
                 unsigned char* Ob = smem + C::OFF_O + wave * C::O_SIZE;
-                lds_st(Ob + r * 32 + 8 * g, to_bf4(gt * O));
+                lds_st(Ob + r * C::ORS + 8 * g, to_bf4(gt * O));
                 const bf16x4 orow = lds_tr(Ob + tr_o);
                 const int64_t t0 = tbeg + 16 * (int64_t)c;
                 if (t0 + r < tend)
                     *reinterpret_cast<bf16x4*>(a.out + (t0 + r) * rowv + (int64_t)h * DV + col0 + 16 * wave + 4 * g) = orow;
-                if (c + 1 < nch) {  // S' of the next chunk
-                    const float* gn = reinterpret_cast<const float*>(lslot(c + 1) + C::L_GAM);
-#pragma unroll
-                    for (int b = 0; b < KB; ++b) S[b] *= *reinterpret_cast<const f32x4*>(gn + 16 * b + 4 * g);
-                }
-            } else if (c == -1) {
-                // S' of chunk 0
-                const float* g0 = reinterpret_cast<const float*>(lslot(0) + C::L_GAM);
-#pragma unroll
-                for (int b = 0; b < KB; ++b) S[b] *= *reinterpret_cast<const f32x4*>(g0 + 16 * b + 4 * g);
             }
             lds_barrier();
         }
