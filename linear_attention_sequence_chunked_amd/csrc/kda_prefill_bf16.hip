@@ -66,19 +66,19 @@ constexpr float kLog2e = 1.4426950408889634f;
 __device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
-// 32-deep steps are issued as two 16-deep v_mfma_f32_16x16x16_bf16.  The 16x16x32 form
-// gave wrong results with this toolchain when a register of its A/B operand was
-// rewritten within the next few instructions (the scheduler does this freely; seen on
-// gfx950: the upper operand half is read after issue and no wait states were inserted).
-__device__ __forceinline__ bf16x4 lo4(bf16x8 x) { return bf16x4{x[0], x[1], x[2], x[3]}; }
-__device__ __forceinline__ bf16x4 hi4(bf16x8 x) { return bf16x4{x[4], x[5], x[6], x[7]}; }
+// 32-deep step (v_mfma_f32_16x16x32_bf16): the same issue cost as the 16-deep form for
+// twice the work.  Measured on gfx950: a VALU write of an A/B register needs one wait
+// state before this instruction reads it, the result is readable by the VALU eight wait
+// states after issue (the compiler inserts both), and A/B may be overwritten right after
+// issue.  Each accumulator below is fed by one instruction shape only, and every result
+// goes through a VALU conversion before it is stored or used as an operand.
+__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
 __device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
     return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
-// sum over both 16-deep halves: lo(a) lo(b) + hi(a) hi(b)
-__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
-    return mfma16(hi4(a), hi4(b), mfma16(lo4(a), lo4(b), c));
-}
+__device__ __forceinline__ bf16x4 zero_bf4() { return __builtin_bit_cast(bf16x4, u32x2{0u, 0u}); }
 // round to bf16 pairwise: the four-wide conversion of MFMA results is split by the
 // compiler into single conversions plus permutes; two-wide ones map to v_cvt_pk_bf16_f32
 __device__ __forceinline__ bf16x4 to_bf4(f32x4 x) {
@@ -89,6 +89,16 @@ __device__ __forceinline__ bf16x4 to_bf4(f32x4 x) {
     return __builtin_bit_cast(bf16x4, u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)});
 }
 __device__ __forceinline__ f32x4 to_f4(bf16x4 x) { return __builtin_convertvector(x, f32x4); }
+__device__ __forceinline__ bf16x8 to_bf8(f32x4 a, f32x4 b) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 p0 = __builtin_convertvector(f32x2{a[0], a[1]}, bf16x2);
+    const bf16x2 p1 = __builtin_convertvector(f32x2{a[2], a[3]}, bf16x2);
+    const bf16x2 p2 = __builtin_convertvector(f32x2{b[0], b[1]}, bf16x2);
+    const bf16x2 p3 = __builtin_convertvector(f32x2{b[2], b[3]}, bf16x2);
+    return __builtin_bit_cast(bf16x8, u32x4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                                            __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)});
+}
 // x = hi + lo, each bf16 (hi round-to-nearest-even, lo the rounded remainder); hi is
 // widened back from its packed form (a shift for the low half, a mask for the high half)
 __device__ __forceinline__ void split4(f32x4 x, bf16x4& hi, bf16x4& lo) {
@@ -175,12 +185,14 @@ struct Cfg {
     static constexpr int W_PW = W_GRAM + 1;   // P of chunk c+2, then Wt of chunk c+1
     static constexpr int NWAVES = W_GRAM + 2;
     static constexpr int THREADS = 64 * NWAVES;
-    // Row-major [16][DK] bf16 tiles with padded rows (bytes).  The padding is chosen per
-    // tile from how it is read (measured on gfx950, 64-lane wave):
-    //   Qt tiles, read as 8-byte row pieces (A-fragments): rows of 2 DK + 24 bytes
-    //   Kb / Kt tiles, read as 16-byte row pieces and by transposed reads: 2 DK + 32
-    // (2 DK + 16 costs a two-way bank conflict on both 8- and 16-byte row reads).
-    static constexpr int RSQ = DK * 2 + 24;
+    // [16][DK] bf16 row tiles with padded rows (bytes).  Every tile is read as 16-byte row
+    // pieces and/or by transposed reads; rows of 2 DK + 32 bytes are conflict-free for both
+    // on gfx950 (2 DK + 16 costs a two-way bank conflict on 16-byte row reads).
+    // Column order inside a tile: position 32p + 8g + 4h + i holds channel 32p + 16h + 4g + i,
+    // so the 16 bytes at position 32p + 8g are the A-fragments of channel blocks 2p and
+    // 2p+1 for lane group g side by side -- the operand of a 32-deep step against the
+    // state rows of those two blocks.
+    static constexpr int RSQ = DK * 2 + 32;
     static constexpr int RSK = DK * 2 + 32;
     static constexpr int ROWQ = 16 * RSQ, ROWK = 16 * RSK;
     // row-major [16][NV] bf16 value and gate tiles, read transposed: 2 NV + 32 bytes puts
@@ -199,8 +211,9 @@ struct Cfg {
     static constexpr int K_SIZE = ROWK;
     // beta ring (2)
     static constexpr int B_SIZE = 64;
-    // gram ring (3): T^T fragment (C(T^T) = A-fragment of T), P hi/lo A-fragments
-    static constexpr int G_TT = 0, G_PH = 512, G_PL = 1024, G_SIZE = 1536;
+    // gram ring (3): T^T fragment (C(T^T) = A-fragment of T) padded to 16 bytes per lane
+    // with zeros (a 32-deep operand), and P hi|lo A-fragments side by side (16 bytes)
+    static constexpr int G_TT = 0, G_P = 1024, G_SIZE = 2048;
     // wgen ring (2): -Wt A-fragments for 32-deep steps
     static constexpr int W_WT = 0, W_SIZE = KP * 1024;
     // per chain wave: its 16x16 output block, transposed to rows before the store (rows
@@ -263,7 +276,10 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
     auto wslot = [&](int c) { return smem + C::OFF_W + (c & 1) * C::W_SIZE; };
     // per-lane byte offsets of the transposed reads (row 4g + j, columns +4q)
     const int trj = (lane & 15) >> 2, trq = lane & 3;
-    const int tr_k = (4 * g + trj) * C::RSK + 8 * trq;   // Kb / Kt tiles
+    // Kb / Kt tiles: lane 16g + 4j + q reads row 4g + j at the four positions holding
+    // channels 16b + 4q .. +3, i.e. positions 32 (b >> 1) + 8q + 4 (b & 1) (see Cfg)
+    const int tr_k = (4 * g + trj) * C::RSK + 16 * trq;
+    auto tr_blk = [](int b) { return 64 * (b >> 1) + 8 * (b & 1); };
     const int tr_v = (4 * g + trj) * C::VRS + 8 * trq;   // [16][NV] tiles
     const int tr_o = (4 * g + trj) * C::ORS + 8 * trq;   // [16][16] output block
 
@@ -347,7 +363,9 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
             load(std::integral_constant<int, (decltype(J)::value + 1) % PF>{});
             __builtin_amdgcn_sched_barrier(0);
         });
-        const int rowq = r * C::RSQ + 2 * dch, rowk = r * C::RSK + 2 * dch;
+        // positions of this lane's channel groups dch..dch+3 and dch+4..dch+7 (see Cfg)
+        const int pos = 32 * w + 16 * (g & 1) + 4 * (g >> 1);
+        const int rowq = r * C::RSQ + 2 * pos, rowk = r * C::RSK + 2 * pos;
         auto step = [&](const int it, auto PH) {
             constexpr int ph = decltype(PH)::value;
             const int c = it + 3;  // decay-folded row tiles of chunk c (token r, channels dch..+7)
@@ -372,11 +390,11 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
                     bf16x4 qh, ql, kbh, kbl;
                     split4(q4 * F, qh, ql);
                     split4(k4 * Fi, kbh, kbl);
-                    lds_st(L + C::L_QH + rowq + 8 * hh, qh);
-                    lds_st(L + C::L_QL + rowq + 8 * hh, ql);
-                    lds_st(L + C::L_KBH + rowk + 8 * hh, kbh);
-                    lds_st(L + C::L_KBL + rowk + 8 * hh, kbl);
-                    lds_st(kslot(c) + rowk + 8 * hh, to_bf4(k4 * F));
+                    lds_st(L + C::L_QH + rowq + 16 * hh, qh);
+                    lds_st(L + C::L_QL + rowq + 16 * hh, ql);
+                    lds_st(L + C::L_KBH + rowk + 16 * hh, kbh);
+                    lds_st(L + C::L_KBL + rowk + 16 * hh, kbl);
+                    lds_st(kslot(c) + rowk + 16 * hh, to_bf4(k4 * F));
                 }
                 // gamma of channel dch + r from lanes r < 8 (one exponential per lane)
                 const f32x4 gh = r < 4 ? gam[0] : gam[1];
@@ -440,7 +458,8 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
                 y += prod(cA4, y);   // (I + (A^T)^4) y
                 y += prod(cA2, y);   // (I + (A^T)^2) y
                 y -= prod(cA, y);    // (I - A^T) y   ->  X^T = ((I + A)^-1)^T
-                lds_st(gslot(c) + C::G_TT + lane * 8, to_bf4(y * bi));  // C(T^T), rows scaled by beta
+                // C(T^T), rows scaled by beta, as the lower half of a 32-deep operand
+                lds_st(gslot(c) + C::G_TT + lane * 16, cat8(to_bf4(y * bi), zero_bf4()));
             }
             lds_barrier();
         }
@@ -459,9 +478,8 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
                         const int offq = r * C::RSQ + 2 * (32 * p + 8 * g);
                         const bf16x8 kbh = lds_ld<bf16x8>(L + C::L_KBH + offk);
                         const bf16x8 kbl = lds_ld<bf16x8>(L + C::L_KBL + offk);
-                        // Qt rows are padded for 8-byte reads: two per 16-byte piece
-                        const bf16x8 qh = cat8(lds_ld<bf16x4>(L + C::L_QH + offq), lds_ld<bf16x4>(L + C::L_QH + offq + 8));
-                        const bf16x8 ql = cat8(lds_ld<bf16x4>(L + C::L_QL + offq), lds_ld<bf16x4>(L + C::L_QL + offq + 8));
+                        const bf16x8 qh = lds_ld<bf16x8>(L + C::L_QH + offq);
+                        const bf16x8 ql = lds_ld<bf16x8>(L + C::L_QL + offq);
                         acc = mfma32(kbh, qh, acc);
                         acc = mfma32(kbh, ql, acc);
                         acc = mfma32(kbl, qh, acc);
@@ -471,8 +489,7 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
                     for (int i = 0; i < 4; ++i) acc[i] = (4 * g + i) <= r ? acc[i] : 0.f;
                     bf16x4 ph_, pl_;
                     split4(acc, ph_, pl_);
-                    lds_st(gslot(c) + C::G_PH + lane * 8, ph_);
-                    lds_st(gslot(c) + C::G_PL + lane * 8, pl_);
+                    lds_st(gslot(c) + C::G_P + lane * 16, cat8(ph_, pl_));
                 }
             }
             {
@@ -481,12 +498,17 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
                 if (c >= 0 && c < nch) {
                     // -T^T: flip the bf16 sign bits once, so the products come out negated
                     const bf16x4 ntt = __builtin_bit_cast(
-                        bf16x4, lds_ld<u32x2>(gslot(c) + C::G_TT + lane * 8) ^ 0x80008000u);
+                        bf16x4, lds_ld<u32x2>(gslot(c) + C::G_TT + lane * 16) ^ 0x80008000u);
                     const unsigned char* Kt = kslot(c) + tr_k;
                     unsigned char* W = wslot(c);
+                    // all reads before the first write: the compiler cannot tell the transposed
+                    // reads from the writes apart, so interleaving them would serialize both
+                    bf16x4 ktt[KB];
+#pragma unroll
+                    for (int nb = 0; nb < KB; ++nb) ktt[nb] = lds_tr(Kt + tr_blk(nb));
 #pragma unroll
                     for (int nb = 0; nb < KB; ++nb) {
-                        const f32x4 w = mfma16(lds_tr(Kt + 32 * nb), ntt, zero4());  // -Wt[r][16nb + 4g + i]
+                        const f32x4 w = mfma16(ktt[nb], ntt, zero4());  // -Wt[r][16nb + 4g + i]
                         lds_st(W + C::W_WT + (nb >> 1) * 1024 + lane * 16 + (nb & 1) * 8, to_bf4(w));
                     }
                 }
@@ -513,45 +535,42 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
                 const unsigned char* L = lslot(c);
                 const unsigned char* Gs = gslot(c);
                 const unsigned char* W = wslot(c);
-                // S' = Diag(gamma) S, and its bf16 copy (the B operands of Wt S' and Qt S')
+                // S' = Diag(gamma) S, and its bf16 copy as 32-deep B operands: Sb2[p] holds
+                // the rows of channel blocks 2p and 2p+1 (the B operands of Wt S' and Qt S')
                 const float* gc = reinterpret_cast<const float*>(L + C::L_GAM);
-                bf16x4 Sb[KB];
+                bf16x8 Sb2[KP];
 #pragma unroll
-                for (int b = 0; b < KB; ++b) {
-                    S[b] *= *reinterpret_cast<const f32x4*>(gc + 16 * b + 4 * g);
-                    Sb[b] = to_bf4(S[b]);
-                }
+                for (int b = 0; b < KB; ++b) S[b] *= *reinterpret_cast<const f32x4*>(gc + 16 * b + 4 * g);
+#pragma unroll
+                for (int p = 0; p < KP; ++p) Sb2[p] = to_bf8(S[2 * p], S[2 * p + 1]);
                 // Ut = T V
-                const bf16x4 tt = lds_ld<bf16x4>(Gs + C::G_TT + lane * 8);
-                f32x4 U = mfma16(tt, lds_tr(L + C::L_V + tr_v + 32 * wave), zero4());
+                // Ut = T V: T^T is stored with a zero upper half (one 32-deep step; each
+                // accumulator is fed by one instruction shape only)
+                const bf16x8 tt0 = lds_ld<bf16x8>(Gs + C::G_TT + lane * 16);
+                f32x4 U = mfma32(tt0, cat8(lds_tr(L + C::L_V + tr_v + 32 * wave), zero_bf4()), zero4());
 #pragma unroll
-                for (int p = 0; p < KP; ++p) {  // U = Ut - Wt S'
-                    const bf16x8 w = lds_ld<bf16x8>(W + C::W_WT + p * 1024 + lane * 16);
-                    U = mfma16(lo4(w), Sb[2 * p], U);
-                    U = mfma16(hi4(w), Sb[2 * p + 1], U);
-                }
+                for (int p = 0; p < KP; ++p)  // U = Ut - Wt S' (channel blocks 2p, 2p+1 stacked)
+                    U = mfma32(lds_ld<bf16x8>(W + C::W_WT + p * 1024 + lane * 16), Sb2[p], U);
                 f32x4 O = zero4();
 #pragma unroll
-                for (int b = 0; b < KB; ++b) {  // O = Qt S' (hi and lo halves of Qt)
-                    const int off = r * C::RSQ + 2 * (16 * b + 4 * g);
-                    O = mfma16(lds_ld<bf16x4>(L + C::L_QH + off), Sb[b], O);
-                    O = mfma16(lds_ld<bf16x4>(L + C::L_QL + off), Sb[b], O);
+                for (int p = 0; p < KP; ++p) {  // O = Qt S' (hi and lo parts of Qt)
+                    const int off = r * C::RSQ + 2 * (32 * p + 8 * g);
+                    O = mfma32(lds_ld<bf16x8>(L + C::L_QH + off), Sb2[p], O);
+                    O = mfma32(lds_ld<bf16x8>(L + C::L_QL + off), Sb2[p], O);
                 }
                 bf16x4 uh, ul;
                 split4(U, uh, ul);
-                const bf16x4 ph_ = lds_ld<bf16x4>(Gs + C::G_PH + lane * 8);
-                const bf16x4 pl_ = lds_ld<bf16x4>(Gs + C::G_PL + lane * 8);
-                O = mfma16(ph_, uh, O);  // + P U
-                O = mfma16(ph_, ul, O);
-                O = mfma16(pl_, uh, O);
-                // S <- S' + Kb^T U, row block by row block
+                const bf16x8 uu = cat8(uh, uh), ul0 = cat8(ul, zero_bf4());
+                const bf16x8 pp = lds_ld<bf16x8>(Gs + C::G_P + lane * 16);  // P hi | P lo
+                O = mfma32(pp, uu, O);   // + P U: ph uh + pl uh
+                O = mfma32(pp, ul0, O);  //        + ph ul
+                // S <- S' + Kb^T U, row block by row block: kh uh + kl uh, then kh ul
 #pragma unroll
                 for (int b = 0; b < KB; ++b) {
-                    const bf16x4 kh = lds_tr(L + C::L_KBH + tr_k + 32 * b);
-                    const bf16x4 kl = lds_tr(L + C::L_KBL + tr_k + 32 * b);
-                    S[b] = mfma16(kh, uh, S[b]);
-                    S[b] = mfma16(kh, ul, S[b]);
-                    S[b] = mfma16(kl, uh, S[b]);
+                    const bf16x8 kk = cat8(lds_tr(L + C::L_KBH + tr_k + tr_blk(b)),
+                                           lds_tr(L + C::L_KBL + tr_k + tr_blk(b)));
+                    S[b] = mfma32(kk, uu, S[b]);
+                    S[b] = mfma32(kk, ul0, S[b]);
                 }
                 // gated output rows of this chunk: the block O[4g+i][r] goes through LDS as the
                 // rows of O^T and comes back transposed, O[r][4g..4g+3], one 8-byte store per lane
