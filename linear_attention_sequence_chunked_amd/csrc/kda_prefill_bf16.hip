@@ -99,14 +99,25 @@ __device__ __forceinline__ bf16x8 to_bf8(f32x4 a, f32x4 b) {
     return __builtin_bit_cast(bf16x8, u32x4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
                                             __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)});
 }
-// x = hi + lo, each bf16 (hi round-to-nearest-even, lo the rounded remainder); hi is
-// widened back from its packed form (a shift for the low half, a mask for the high half)
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi).  x - hi is exact in fp32, and the
+// bf16 dot product (-1, -0) . (hi0, hi1) + x0 forms it from the packed hi word directly,
+// with no conversion of hi back to fp32.  The zero is negative so that neither constant
+// pair has an inline-constant encoding: ROCm 7.2 encodes the pair (-1, +0) as the inline
+// constant -1.0, which gfx950 reads as the pair (+0, -1) (checked on the device).  The
+// dot products take the two converted pairs as they are; taking them back out of the
+// packed bf16x4 made the compiler feed the first pair to all four.
 __device__ __forceinline__ void split4(f32x4 x, bf16x4& hi, bf16x4& lo) {
-    hi = to_bf4(x);
-    const u32x2 w = __builtin_bit_cast(u32x2, hi);
-    const f32x4 hf{__builtin_bit_cast(float, w[0] << 16), __builtin_bit_cast(float, w[0] & 0xffff0000u),
-                   __builtin_bit_cast(float, w[1] << 16), __builtin_bit_cast(float, w[1] & 0xffff0000u)};
-    lo = to_bf4(x - hf);
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 h01 = __builtin_convertvector(f32x2{x[0], x[1]}, bf16x2);
+    const bf16x2 h23 = __builtin_convertvector(f32x2{x[2], x[3]}, bf16x2);
+    hi = __builtin_bit_cast(bf16x4, u32x2{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)});
+    const bf16x2 m0 = {(__bf16)-1.0f, (__bf16)-0.0f}, m1 = {(__bf16)-0.0f, (__bf16)-1.0f};
+    const f32x4 d{__builtin_amdgcn_fdot2_f32_bf16(h01, m0, x[0], false),
+                  __builtin_amdgcn_fdot2_f32_bf16(h01, m1, x[1], false),
+                  __builtin_amdgcn_fdot2_f32_bf16(h23, m0, x[2], false),
+                  __builtin_amdgcn_fdot2_f32_bf16(h23, m1, x[3], false)};
+    lo = to_bf4(d);
 }
 // C(L R) in bf16 from fp32 operands given as the A-fragment of L (== C(L^T)) and C(R)
 __device__ __forceinline__ f32x4 prod(f32x4 aL, f32x4 cR) {
@@ -126,6 +137,18 @@ __device__ __forceinline__ float row_scan(float x) {
     return x;
 }
 __device__ __forceinline__ float row_last(float x) { return dpp<0x15F>(x); }  // lane 15 of row
+// eight independent inclusive row scans, step by step, so the DPP reads of one channel
+// fill the wait states after the writes of another
+__device__ __forceinline__ void row_scan8(float (&x)[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] += dpp<0x111>(x[j]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] += dpp<0x112>(x[j]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] += dpp<0x114>(x[j]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] += dpp<0x118>(x[j]);
+}
 
 // Workgroup barrier that orders LDS only.  __syncthreads() also waits for every
 // outstanding global load, which would drain the multi-chunk prefetch at each chunk.
@@ -207,11 +230,12 @@ struct Cfg {
     static constexpr int L_QH = 0, L_QL = ROWQ, L_KBH = 2 * ROWQ, L_KBL = 2 * ROWQ + ROWK,
                          L_GAM = 2 * ROWQ + 2 * ROWK, L_V = L_GAM + DK * 4, L_G = L_V + VT,
                          L_SIZE = L_G + VT;
-    // Kt ring (3): Kt rows (gram at c-2, Wt at c-1)
+    // Kt ring (4 slots, so its slot index is a multiple of the loop's unroll): Kt rows
+    // (gram at c-2, Wt at c-1)
     static constexpr int K_SIZE = ROWK;
     // beta ring (2)
     static constexpr int B_SIZE = 64;
-    // gram ring (3): T^T fragment (C(T^T) = A-fragment of T) padded to 16 bytes per lane
+    // gram ring (4): T^T fragment (C(T^T) = A-fragment of T) padded to 16 bytes per lane
     // with zeros (a 32-deep operand), and P hi|lo A-fragments side by side (16 bytes)
     static constexpr int G_TT = 0, G_P = 1024, G_SIZE = 2048;
     // wgen ring (2): -Wt A-fragments for 32-deep steps
@@ -219,8 +243,8 @@ struct Cfg {
     // per chain wave: its 16x16 output block, transposed to rows before the store (rows
     // of 40 bytes: conflict-free for both the 8-byte writes and the transposed reads)
     static constexpr int ORS = 40, O_SIZE = 16 * ORS;
-    static constexpr int OFF_L = 0, OFF_K = OFF_L + 4 * L_SIZE, OFF_B = OFF_K + 3 * K_SIZE,
-                         OFF_G = OFF_B + 2 * B_SIZE, OFF_W = OFF_G + 3 * G_SIZE,
+    static constexpr int OFF_L = 0, OFF_K = OFF_L + 4 * L_SIZE, OFF_B = OFF_K + 4 * K_SIZE,
+                         OFF_G = OFF_B + 2 * B_SIZE, OFF_W = OFF_G + 4 * G_SIZE,
                          OFF_O = OFF_W + 2 * W_SIZE, LDS_BYTES = OFF_O + NCHAIN * O_SIZE;
 };
 
@@ -270,9 +294,9 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
     const int64_t sbase = ((int64_t)seq * H + h) * DK * DV;
 
     auto lslot = [&](int c) { return smem + C::OFF_L + (c & 3) * C::L_SIZE; };
-    auto kslot = [&](int c) { return smem + C::OFF_K + (c % 3) * C::K_SIZE; };
+    auto kslot = [&](int c) { return smem + C::OFF_K + (c & 3) * C::K_SIZE; };
     auto bslot = [&](int c) { return smem + C::OFF_B + (c & 1) * C::B_SIZE; };
-    auto gslot = [&](int c) { return smem + C::OFF_G + (c % 3) * C::G_SIZE; };
+    auto gslot = [&](int c) { return smem + C::OFF_G + (c & 3) * C::G_SIZE; };
     auto wslot = [&](int c) { return smem + C::OFF_W + (c & 1) * C::W_SIZE; };
     // per-lane byte offsets of the transposed reads (row 4g + j, columns +4q)
     const int trj = (lane & 15) >> 2, trq = lane & 3;
@@ -311,12 +335,13 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
             vg_own[e] = w + NDW * e < 2 * NCB;
             vg_f[e] = vg_own[e] ? w + NDW * e : w % (2 * NCB);
         }
-        const bool own_beta = w == 0;
-        // Prefetch ring of PF chunks; chunk c lives in slot (c + 1) % PF.  Loads are
-        // unconditional buffer loads bounded at the end of the sequence: rows past the end
-        // (and every row of chunks past the last) read as zero, which is the identity row
-        // (k = 0, lambda' = max(0, floor) = 0, beta = 0), so each load lands in its own
-        // register and stays in flight, and nothing is masked when consumed.
+        // Prefetch ring of PF chunks; chunk c lives in slot (c + 1) % PF.  One buffer
+        // resource per tensor covers the whole sequence (its records end at the last row),
+        // and the lane's byte offset advances one chunk per load: rows past the end (and
+        // every row of chunks past the last) read as zero, which is the identity row
+        // (k = 0, lambda' = max(0, floor) = 0, beta = 0).  So each load lands in its own
+        // register and stays in flight, and nothing is masked when consumed.  Offsets are
+        // 32-bit: once one passes 2^30 bytes the resource base moves up to the next chunk.
         u32x4 rq[PF], rk[PF], rl[PF];
         u32x2 rvg[C::VG_PER_WAVE][PF];
         uint32_t rb[PF];
@@ -326,7 +351,6 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
 #pragma unroll
         for (int e = 0; e < C::VG_PER_WAVE; ++e)
             ov[e] = (uint32_t)(r * (int)(2 * rowv) + 2 * (col0 + 16 * (vg_f[e] >> 1) + 4 * g));
-        // uniform chunk bases, advanced by one chunk per load (loads go in chunk order)
         const char* pq = reinterpret_cast<const char*>(a.q + tbeg * rowq + (int64_t)h * DK);
         const char* pk = reinterpret_cast<const char*>(a.k + tbeg * rowq + (int64_t)h * DK);
         const char* pl = reinterpret_cast<const char*>(a.la + tbeg * rowq + (int64_t)h * DK);
@@ -335,27 +359,40 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
 #pragma unroll
         for (int e = 0; e < C::VG_PER_WAVE; ++e)
             pv[e] = reinterpret_cast<const char*>(((vg_f[e] & 1) ? a.gate : a.v) + tbeg * rowv + (int64_t)h * DV);
-        const int64_t sq = 32 * rowq, sb = 32 * (int64_t)H, sv = 32 * rowv;  // bytes per chunk
-        int lrem = (int)min<int64_t>(len, 1 << 20);  // rows left at the next load's chunk
+        // bytes from the resource base to the end of the sequence's rows (the records)
+        int64_t eq = (len - 1) * 2 * rowq + 2 * DK, eb = (len - 1) * 2 * H + 2,
+                ev = (len - 1) * 2 * rowv + 2 * DV;
+        uint32_t uq = 0, ub = 0, uv = 0;  // chunk offsets of the next load (bytes)
+        const uint32_t sq = (uint32_t)(32 * rowq), sb = (uint32_t)(32 * H), sv = (uint32_t)(32 * rowv);
+        auto recs = [](int64_t e) { return e <= 0 ? 0 : e >= 0x7fffffff ? 0x7fffffff : (int)e; };
+        __amdgpu_buffer_rsrc_t Rq, Rk, Rl, Rb, Rv[C::VG_PER_WAVE];
+        auto make = [&]() {  // resources for the current bases (uniform)
+            const int nq = recs(eq), nv = recs(ev);
+            Rq = rsrc(pq, nq); Rk = rsrc(pk, nq); Rl = rsrc(pl, nq); Rb = rsrc(pb, recs(eb));
+#pragma unroll
+            for (int e = 0; e < C::VG_PER_WAVE; ++e) Rv[e] = rsrc(pv[e], vg_own[e] ? nv : 0);
+        };
+        make();
+        auto rebase = [&]() {  // keeps every offset below 2^30 + PF chunks
+            if (uq >= (1u << 30) || ub >= (1u << 30) || uv >= (1u << 30)) {
+                pq += uq; pk += uq; pl += uq; eq -= uq; uq = 0;
+                pb += ub; eb -= ub; ub = 0;
+#pragma unroll
+                for (int e = 0; e < C::VG_PER_WAVE; ++e) pv[e] += uv;
+                ev -= uv; uv = 0;
+                make();
+            }
+        };
         auto load = [&](auto SLOT) {
             constexpr int sl = decltype(SLOT)::value;
-            const int rem = min(max(lrem, 0), 16);  // rows of this chunk (0: past the end)
-            const int nq = rem ? (rem - 1) * (int)(2 * rowq) + 2 * DK : 0;
-            const int nb = (rem && own_beta) ? (rem - 1) * 2 * H + 2 : 0;
-            const int nv = rem ? (rem - 1) * (int)(2 * rowv) + 2 * DV : 0;
-            rq[sl] = bload16(rsrc(pq, nq), oq);
-            rk[sl] = bload16(rsrc(pk, nq), oq);
-            rl[sl] = bload16(rsrc(pl, nq), oq);
-            rb[sl] = __builtin_amdgcn_raw_buffer_load_b16(rsrc(pb, nb), ob, 0, 0);
+            const uint32_t vq = oq + uq;
+            rq[sl] = bload16(Rq, vq);
+            rk[sl] = bload16(Rk, vq);
+            rl[sl] = bload16(Rl, vq);
+            rb[sl] = __builtin_amdgcn_raw_buffer_load_b16(Rb, ob + ub, 0, 0);
 #pragma unroll
-            for (int e = 0; e < C::VG_PER_WAVE; ++e)
-                rvg[e][sl] = bload8(rsrc(pv[e], vg_own[e] ? nv : 0), ov[e]);
-            if (rem) {  // chunks past the end keep their (unread) base
-                pq += sq; pk += sq; pl += sq; pb += sb;
-#pragma unroll
-                for (int e = 0; e < C::VG_PER_WAVE; ++e) pv[e] += sv;
-            }
-            lrem -= 16;
+            for (int e = 0; e < C::VG_PER_WAVE; ++e) rvg[e][sl] = bload8(Rv[e], ov[e] + uv);
+            uq += sq; ub += sb; uv += sv;
         };
         // issued in slot order (kept by the scheduling barriers), so the loads of the
         // slot consumed next are always the oldest in flight
@@ -366,43 +403,54 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
         // positions of this lane's channel groups dch..dch+3 and dch+4..dch+7 (see Cfg)
         const int pos = 32 * w + 16 * (g & 1) + 4 * (g >> 1);
         const int rowq = r * C::RSQ + 2 * pos, rowk = r * C::RSK + 2 * pos;
+        // lane r stores gamma of channel dch + (r & 7); lanes r and r + 8 store the same
+        // value to the same word
+        const bool gb0 = r & 1, gb1 = r & 2, gb2 = r & 4;
         auto step = [&](const int it, auto PH) {
             constexpr int ph = decltype(PH)::value;
             const int c = it + 3;  // decay-folded row tiles of chunk c (token r, channels dch..+7)
             if (c < nch) {
                 unsigned char* L = lslot(c);
-                f32x4 gam[2];
+                f32x4 q4[2], k4[2];
+                float G[8];
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {  // channels dch + 4hh .. +3
-                    const f32x4 q4 = unpack_bf4(u32x2{rq[ph][2 * hh], rq[ph][2 * hh + 1]});
-                    const f32x4 k4 = unpack_bf4(u32x2{rk[ph][2 * hh], rk[ph][2 * hh + 1]});
+                    q4[hh] = unpack_bf4(u32x2{rq[ph][2 * hh], rq[ph][2 * hh + 1]});
+                    k4[hh] = unpack_bf4(u32x2{rk[ph][2 * hh], rk[ph][2 * hh + 1]});
                     const f32x4 l4 = unpack_bf4(u32x2{rl[ph][2 * hh], rl[ph][2 * hh + 1]});
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) G[4 * hh + i] = fmaxf(l4[i], floor2);
+                }
+                // inclusive cumsums over tokens, the eight channels side by side
+                row_scan8(G);
+                float GC[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) GC[j] = row_last(G[j]);  // chunk totals
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
                     f32x4 F, Fi;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const float G = row_scan(fmaxf(l4[i], floor2));  // inclusive cumsum over tokens
-                        const float GC = row_last(G);                    // chunk total
-                        const float d = (G - GC) * kLog2e;               // >= 0
+                        const float d = (G[4 * hh + i] - GC[4 * hh + i]) * kLog2e;  // >= 0
                         F[i] = __builtin_amdgcn_exp2f(d);
                         Fi[i] = __builtin_amdgcn_exp2f(-d);
-                        gam[hh][i] = GC;
                     }
                     bf16x4 qh, ql, kbh, kbl;
-                    split4(q4 * F, qh, ql);
-                    split4(k4 * Fi, kbh, kbl);
+                    split4(q4[hh] * F, qh, ql);
+                    split4(k4[hh] * Fi, kbh, kbl);
                     lds_st(L + C::L_QH + rowq + 16 * hh, qh);
                     lds_st(L + C::L_QL + rowq + 16 * hh, ql);
                     lds_st(L + C::L_KBH + rowk + 16 * hh, kbh);
                     lds_st(L + C::L_KBL + rowk + 16 * hh, kbl);
-                    lds_st(kslot(c) + rowk + 16 * hh, to_bf4(k4 * F));
+                    lds_st(kslot(c) + rowk + 16 * hh, to_bf4(k4[hh] * F));
                 }
-                // gamma of channel dch + r from lanes r < 8 (one exponential per lane)
-                const f32x4 gh = r < 4 ? gam[0] : gam[1];
-                const int r4 = r & 3;
-                const float gsel = r4 == 0 ? gh[0] : r4 == 1 ? gh[1] : r4 == 2 ? gh[2] : gh[3];
-                const float ge = __builtin_amdgcn_exp2f(gsel * kLog2e);
-                if (r < 8) lds_st(L + C::L_GAM + 4 * (dch + r), ge);
-                if (own_beta && g == 0) lds_st(bslot(c) + 4 * r, __builtin_bit_cast(float, rb[ph] << 16));
+                const float x01 = gb0 ? GC[1] : GC[0], x23 = gb0 ? GC[3] : GC[2];
+                const float x45 = gb0 ? GC[5] : GC[4], x67 = gb0 ? GC[7] : GC[6];
+                const float y0 = gb1 ? x23 : x01, y1 = gb1 ? x67 : x45;
+                const float ge = __builtin_amdgcn_exp2f((gb2 ? y1 : y0) * kLog2e);
+                lds_st(L + C::L_GAM + 4 * (dch + (r & 7)), ge);
+                // every decay wave loads beta and every lane stores it (same value per word)
+                lds_st(bslot(c) + 4 * r, __builtin_bit_cast(float, rb[ph] << 16));
 #pragma unroll
                 for (int e = 0; e < C::VG_PER_WAVE; ++e) {
                     const int f = w + NDW * e;
@@ -415,6 +463,7 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
             lds_barrier();
         };
         for (int it = -3; it < it_end; it += PF) {  // no exit between the slots
+            rebase();
             unroll<0, PF>([&](auto J) {
                 step(it + decltype(J)::value, std::integral_constant<int, (decltype(J)::value + 1) % PF>{});
             });
