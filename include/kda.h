@@ -98,6 +98,40 @@ kda_status kda_chunk_prefill(const kda_params* params, const void* q, const void
                              void* stream);
 
 /*
+ * kda_chunk_prefill_checkpointed -- kda_chunk_prefill that also writes state snapshots
+ * every `checkpoint_every` tokens, so that a later request sharing a prefix can resume
+ * prefill from the snapshot instead of recomputing the prefix.  Source: digest of
+ * "Kimi K3: Open Frontier Intelligence", section "基础设施" and Fig. 12 (prefix-cache
+ * hashing at a fine granularity such as 512 tokens, KDA state stored only at those
+ * boundaries; a hit restores the boundary's state and continues prefill from there);
+ * "Kimi-K3 为什么这么强？" §① KDA, prefix-cache paragraph (a state snapshot can be
+ * taken at any token position).
+ *
+ *   All arguments of kda_chunk_prefill, with the same meaning and rules, plus
+ *   checkpoint_every : m > 0, a multiple of 16 (snapshots fall on chunk boundaries).
+ *   checkpoints      : fp32 [T_total / m (rounded down), H, dk, dv].  For every
+ *                      sequence n and every j >= 1 with j*m <= T_n (its length), the
+ *                      state after its first j*m tokens is written to slot
+ *                          (cu_seqlens[n] + j*m) / m - 1        (integer division).
+ *                      Slots of different (n, j) never coincide (two snapshot positions
+ *                      of different sequences are at least m tokens apart in the packed
+ *                      order), and every slot lies inside the buffer.  Slots that no
+ *                      (n, j) maps to are not written.  Must not overlap any other
+ *                      argument; must be non-NULL when T_total >= m.
+ * The outputs and the final state are bit-identical to kda_chunk_prefill's.  Passing a
+ * snapshot as the initial state of the sequence's remaining tokens reproduces the rest of
+ * the uninterrupted run bit for bit (same chunk boundaries, same arithmetic).
+ */
+kda_status kda_chunk_prefill_checkpointed(const kda_params* params, const void* q,
+                                          const void* k, const void* v,
+                                          const void* log_alpha, const void* beta,
+                                          const void* gate, const int32_t* cu_seqlens,
+                                          const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                          const float* initial_state, float* final_state,
+                                          void* out, int32_t checkpoint_every,
+                                          float* checkpoints, void* stream);
+
+/*
  * kda_decode_step -- one token per sequence, state updated in place.
  *
  *   q, k, log_alpha : [num_seqs, H, dk];  v, gate, out : [num_seqs, H, dv];

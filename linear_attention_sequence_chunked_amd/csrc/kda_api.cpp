@@ -104,12 +104,16 @@ const char* kda_last_error(void) { return g_last_error.c_str(); }
 
 int32_t kda_abi_version(void) { return KDA_ABI_VERSION; }
 
-kda_status kda_chunk_prefill(const kda_params* params, const void* q, const void* k,
-                             const void* v, const void* log_alpha, const void* beta,
-                             const void* gate, const int32_t* cu_seqlens,
-                             const int32_t* cu_seqlens_host, int32_t num_seqs,
-                             const float* initial_state, float* final_state, void* out,
-                             void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by kda_chunk_prefill (ckpt_every == 0) and kda_chunk_prefill_checkpointed.
+kda_status prefill(const char* entry, const kda_params* params, const void* q, const void* k,
+                   const void* v, const void* log_alpha, const void* beta, const void* gate,
+                   const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                   int32_t num_seqs, const float* initial_state, float* final_state,
+                   void* out, int32_t ckpt_every, float* checkpoints, void* stream) {
     kda_status st = check_params(params);
     if (st != KDA_OK) return st;
     const kda_params& p = *params;
@@ -158,6 +162,23 @@ kda_status kda_chunk_prefill(const kda_params* params, const void* q, const void
             return fail(KDA_ERR_INVALID_ARGUMENT, "final_state overlaps %s", in.name);
         }
     }
+    const int64_t n_ckpt = ckpt_every > 0 ? T / ckpt_every : 0;
+    if (ckpt_every) {
+        if (ckpt_every < 0 || ckpt_every % 16)
+            return fail(KDA_ERR_INVALID_ARGUMENT,
+                        "checkpoint_every %d must be a positive multiple of 16", ckpt_every);
+        if (n_ckpt > 0) {
+            if ((st = check_ptr("checkpoints", checkpoints, 16)) != KDA_OK) return st;
+            const Range rc = range("checkpoints", checkpoints,
+                                   (uint64_t)n_ckpt * H * p.dk * p.dv * 4);
+            if (overlaps(rc, ro)) return fail(KDA_ERR_INVALID_ARGUMENT, "checkpoints overlaps out");
+            if (final_state && overlaps(rc, range("final_state", final_state, ns)))
+                return fail(KDA_ERR_INVALID_ARGUMENT, "checkpoints overlaps final_state");
+            for (const Range& in : inputs)
+                if (overlaps(rc, in))
+                    return fail(KDA_ERR_INVALID_ARGUMENT, "checkpoints overlaps %s", in.name);
+        }
+    }
 
     kda::PrefillArgs a;
     a.dtype = p.dtype; a.H = p.num_heads; a.dk = p.dk; a.dv = p.dv;
@@ -165,6 +186,8 @@ kda_status kda_chunk_prefill(const kda_params* params, const void* q, const void
     a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta; a.gate = gate;
     a.cu_seqlens = cu_seqlens; a.initial_state = initial_state; a.final_state = final_state;
     a.out = out;
+    a.checkpoints = n_ckpt > 0 ? checkpoints : nullptr;
+    a.ckpt_chunks = n_ckpt > 0 ? ckpt_every / 16 : 0;
     a.num_ordered = 0;
     if (num_seqs > 1 && num_seqs <= kda::kMaxOrdered) {
         // longest sequences first: they bound the launch's critical path
@@ -186,9 +209,39 @@ kda_status kda_chunk_prefill(const kda_params* params, const void* q, const void
                                     device_cu_count());
     }
     const hipError_t e = kda::launch_prefill(a, reinterpret_cast<hipStream_t>(stream));
-    if (e != hipSuccess)
-        return fail(KDA_ERR_HIP, "kda_chunk_prefill launch: %s", hipGetErrorString(e));
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s launch: %s", entry, hipGetErrorString(e));
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_chunk_prefill(const kda_params* params, const void* q, const void* k,
+                             const void* v, const void* log_alpha, const void* beta,
+                             const void* gate, const int32_t* cu_seqlens,
+                             const int32_t* cu_seqlens_host, int32_t num_seqs,
+                             const float* initial_state, float* final_state, void* out,
+                             void* stream) {
+    return prefill("kda_chunk_prefill", params, q, k, v, log_alpha, beta, gate, cu_seqlens,
+                   cu_seqlens_host, num_seqs, initial_state, final_state, out, 0, nullptr,
+                   stream);
+}
+
+kda_status kda_chunk_prefill_checkpointed(const kda_params* params, const void* q,
+                                          const void* k, const void* v,
+                                          const void* log_alpha, const void* beta,
+                                          const void* gate, const int32_t* cu_seqlens,
+                                          const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                          const float* initial_state, float* final_state,
+                                          void* out, int32_t checkpoint_every,
+                                          float* checkpoints, void* stream) {
+    if (checkpoint_every <= 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT,
+                    "checkpoint_every %d must be a positive multiple of 16", checkpoint_every);
+    return prefill("kda_chunk_prefill_checkpointed", params, q, k, v, log_alpha, beta, gate,
+                   cu_seqlens, cu_seqlens_host, num_seqs, initial_state, final_state, out,
+                   checkpoint_every, checkpoints, stream);
 }
 
 kda_status kda_decode_step(const kda_params* params, const void* q, const void* k,

@@ -30,6 +30,8 @@ struct PrefillArgs {
     const float* initial_state;  // may be null
     float* final_state;          // may be null
     void* out;
+    float* checkpoints;          // state snapshots, or null (see kda_chunk_prefill_checkpointed)
+    int ckpt_chunks;             // chunks between snapshots (checkpoint_every / 16); 0 = none
     int nv;                      // value columns per workgroup (dv-slice width)
     int num_ordered;             // entries of order[] in use (0 = natural order)
     int32_t order[kMaxOrdered];  // sequence ids, longest first

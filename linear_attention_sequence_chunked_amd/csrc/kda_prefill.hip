@@ -40,6 +40,8 @@ struct KArgs {
     const int32_t* cu;
     const float* S0;
     float* Sf;
+    float* ck;      // state snapshots or null
+    int ck_chunks;  // chunks between snapshots
     T* out;
     int H, n_slices, num_groups, num_ordered;
     float floor_, scale;
@@ -292,6 +294,15 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const KArgs<T> a) {
                 S[jj][b] = acc;
             }
             const int col = col0 + 16 * j + r;
+            // snapshot after every ck_chunks-th full chunk, at slot (position / m) - 1
+            const int64_t m = 16 * (int64_t)a.ck_chunks;
+            if (a.ck && t0 + kChunk <= tend && (t0 + kChunk - tbeg) % m == 0) {
+                float* dst = a.ck + ((t0 + kChunk) / m - 1) * H * DK * DV + (int64_t)h * DK * DV;
+#pragma unroll
+                for (int b = 0; b < KB; ++b)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) dst[(16 * b + 4 * g + i) * DV + col] = S[jj][b][i];
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 4 * g + i;
@@ -325,6 +336,7 @@ hipError_t launch_typed(const PrefillArgs& p, hipStream_t st) {
     a.q = (const T*)p.q; a.k = (const T*)p.k; a.v = (const T*)p.v;
     a.la = (const T*)p.log_alpha; a.beta = (const T*)p.beta; a.gate = (const T*)p.gate;
     a.cu = p.cu_seqlens; a.S0 = p.initial_state; a.Sf = p.final_state; a.out = (T*)p.out;
+    a.ck = p.checkpoints; a.ck_chunks = p.ckpt_chunks;
     a.H = p.H; a.n_slices = DV / (16 * NCB); a.num_groups = p.num_seqs * p.H;
     a.num_ordered = p.num_ordered; a.floor_ = p.floor_; a.scale = p.scale;
     for (int i = 0; i < p.num_ordered; ++i) a.order[i] = p.order[i];

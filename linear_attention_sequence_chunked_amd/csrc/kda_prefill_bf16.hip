@@ -253,6 +253,8 @@ struct BArgs {
     const int32_t* cu;
     const float* S0;
     float* Sf;
+    float* ck;      // state snapshots or null
+    int ck_chunks;  // chunks between snapshots
     bf16* out;
     int H, n_slices, num_groups, groups_padded, num_ordered;
     float floor_, scale;
@@ -578,6 +580,10 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
             for (int i = 0; i < 4; ++i)
                 S[b][i] = a.S0 ? a.S0[sbase + (16 * b + 4 * g + i) * DV + ccol] : 0.f;
         const float scale = a.scale;
+        // snapshots: the state after every ck_chunks-th chunk (when that chunk is full) goes
+        // to slot tbeg / m + j - 1 for the j-th snapshot, m = 16 ck_chunks tokens
+        int ck_left = a.ck_chunks;
+        int64_t ck_slot = a.ck ? tbeg / (16 * (int64_t)a.ck_chunks) : 0;
         for (int it = -3; it < it_end; ++it) {
             const int c = it;  // state step of chunk c
             if (c >= 0 && c < nch) {
@@ -621,6 +627,17 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
                     S[b] = mfma32(kk, uu, S[b]);
                     S[b] = mfma32(kk, ul0, S[b]);
                 }
+                if (a.ck && --ck_left == 0) {
+                    ck_left = a.ck_chunks;
+                    if (16 * (int64_t)(c + 1) <= len) {
+                        float* dst = a.ck + (ck_slot * H + h) * DK * DV;
+#pragma unroll
+                        for (int b = 0; b < KB; ++b)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) dst[(16 * b + 4 * g + i) * DV + ccol] = S[b][i];
+                    }
+                    ++ck_slot;
+                }
                 // gated output rows of this chunk: the block O[4g+i][r] goes through LDS as the
                 // rows of O^T and comes back transposed, O[r][4g..4g+3], one 8-byte store per lane
                 const f32x4 gt = to_f4(lds_tr(L + C::L_G + tr_v + 32 * wave)) * scale;
@@ -650,6 +667,7 @@ hipError_t launch_bf16(const PrefillArgs& p, hipStream_t st) {
     a.q = (const bf16*)p.q; a.k = (const bf16*)p.k; a.v = (const bf16*)p.v;
     a.la = (const bf16*)p.log_alpha; a.beta = (const bf16*)p.beta; a.gate = (const bf16*)p.gate;
     a.cu = p.cu_seqlens; a.S0 = p.initial_state; a.Sf = p.final_state; a.out = (bf16*)p.out;
+    a.ck = p.checkpoints; a.ck_chunks = p.ckpt_chunks;
     a.H = p.H; a.n_slices = DV / (16 * NCB); a.num_groups = p.num_seqs * p.H;
     a.groups_padded = (a.num_groups + 7) / 8 * 8;
     a.num_ordered = p.num_ordered; a.floor_ = p.floor_; a.scale = p.scale;

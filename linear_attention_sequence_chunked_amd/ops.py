@@ -34,13 +34,21 @@ def chunk_prefill(q, k, v, log_alpha, beta, gate, cu_seqlens=None, initial_state
                   output_final_state: bool = True, log_alpha_floor: float = -0.3,
                   scale: float = 1.0, cu_seqlens_host: Optional[Sequence[int]] = None,
                   out: Optional[torch.Tensor] = None,
-                  final_state: Optional[torch.Tensor] = None):
+                  final_state: Optional[torch.Tensor] = None,
+                  checkpoint_every: Optional[int] = None,
+                  checkpoints: Optional[torch.Tensor] = None):
     """KDA chunked prefill.
 
     Fixed length: q/k/log_alpha [B, T, H, dk], v/gate [B, T, H, dv], beta [B, T, H].
     Varlen: the same tensors packed as [T_total, H, .] with cu_seqlens (int32 tensor
     or list, N+1 entries).  initial_state: fp32 [N, H, dk, dv] or None.
     Returns (o, final_state or None); o has v's shape and dtype.
+
+    checkpoint_every=m (a multiple of 16) also writes the state after every m tokens of
+    each sequence (prefix-cache snapshots) and returns (o, final_state, checkpoints),
+    checkpoints fp32 [T_total // m, H, dk, dv]: sequence n's snapshot after j*m tokens is
+    at slot checkpoint_slot(cu_seqlens, n, j, m); slots no snapshot maps to keep their
+    contents (uninitialised when the tensor is allocated here).
     """
     dt = q.dtype
     if dt not in _DT:
@@ -93,12 +101,34 @@ def chunk_prefill(q, k, v, log_alpha, beta, gate, cu_seqlens=None, initial_state
         _check_dev("final_state", final_state, torch.float32)
     p = _lib.params(_DT[dt], H, dk, dv, log_alpha_floor, scale)
     lib = _lib.load()
-    st = lib.kda_chunk_prefill(ctypes.byref(p), _ptr(qf), _ptr(kf), _ptr(vf), _ptr(laf),
-                               _ptr(bf), _ptr(gf), _ptr(cu_dev), cu_h, N,
-                               _ptr(initial_state), _ptr(final_state), _ptr(out), _stream())
+    if checkpoint_every is None:
+        st = lib.kda_chunk_prefill(ctypes.byref(p), _ptr(qf), _ptr(kf), _ptr(vf), _ptr(laf),
+                                   _ptr(bf), _ptr(gf), _ptr(cu_dev), cu_h, N,
+                                   _ptr(initial_state), _ptr(final_state), _ptr(out),
+                                   _stream())
+        _lib.check(st)
+        o = out.reshape(v.shape) if q.dim() == 4 else out
+        return o, final_state
+    m = int(checkpoint_every)
+    if checkpoints is None:
+        checkpoints = torch.empty((Ttot // m if m > 0 else 0, H, dk, dv), dtype=torch.float32,
+                                  device=dev)
+    else:
+        _check_dev("checkpoints", checkpoints, torch.float32)
+        if m > 0 and tuple(checkpoints.shape) != (Ttot // m, H, dk, dv):
+            raise ValueError("checkpoints must be [T_total // checkpoint_every, H, dk, dv]")
+    st = lib.kda_chunk_prefill_checkpointed(
+        ctypes.byref(p), _ptr(qf), _ptr(kf), _ptr(vf), _ptr(laf), _ptr(bf), _ptr(gf),
+        _ptr(cu_dev), cu_h, N, _ptr(initial_state), _ptr(final_state), _ptr(out), m,
+        _ptr(checkpoints) if checkpoints.numel() else None, _stream())
     _lib.check(st)
     o = out.reshape(v.shape) if q.dim() == 4 else out
-    return o, final_state
+    return o, final_state, checkpoints
+
+
+def checkpoint_slot(cu_seqlens: Sequence[int], n: int, j: int, m: int) -> int:
+    """Slot of sequence n's snapshot after its first j*m tokens (1 <= j, j*m <= T_n)."""
+    return (int(cu_seqlens[n]) + j * m) // m - 1
 
 
 def decode_step(q, k, v, log_alpha, beta, gate, state, log_alpha_floor: float = -0.3,

@@ -129,3 +129,32 @@ def test_decode_rejects(kw, status, msg):
 def test_decode_zero_sequences_is_a_no_op():
     st, err = decode(n=0, q=None, state=None)
     assert st == _lib.KDA_OK and err == ""
+
+
+def prefill_ckpt(m=16, ck=A + 0x200000, cu_host=None, sf=None, out=A + 0x70000):
+    """Two sequences of 20 tokens (T_total = 40), H = 2, d = 64, bf16."""
+    lib = _lib.load()
+    p = _lib.params(_lib.KDA_DTYPE_BF16, 2, 64, 64)
+    if cu_host is None:
+        cu_host = cu(0, 20, 40)
+    st = lib.kda_chunk_prefill_checkpointed(ctypes.byref(p), A, A + 0x10000, A + 0x20000,
+                                            A + 0x30000, A + 0x40000, A + 0x50000, A + 0x60000,
+                                            cu_host, 2, None, sf, out, m, ck, None)
+    return st, lib.kda_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(m=0), "checkpoint_every 0"),
+    (dict(m=-16), "checkpoint_every -16"),
+    (dict(m=24), "checkpoint_every 24"),
+    (dict(ck=None), "checkpoints is NULL"),
+    (dict(ck=A + 0x200008), "checkpoints is not 16-byte aligned"),
+    (dict(ck=A + 0x70000 + 64), "checkpoints overlaps out"),
+    (dict(ck=A + 0x30000), "checkpoints overlaps log_alpha"),
+    (dict(sf=A + 0x200000 + 0x8000), "checkpoints overlaps final_state"),
+])
+def test_prefill_checkpointed_rejects(kw, msg):
+    st, err = prefill_ckpt(**kw)
+    assert st == INV, err
+    assert msg in err, err
+
