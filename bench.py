@@ -89,6 +89,8 @@ def main() -> int:
     ap.add_argument("--workload", default="prefill_b4_h16_t4096")
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--spec-rounds", type=int, default=50)
+    ap.add_argument("--spec-draft", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -211,6 +213,52 @@ def main() -> int:
             "state_bytes": state_bytes,
         }
         del inp, state
+        torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------------- speculative verify
+    if not args.no_decode and args.spec_rounds > 0:
+        d = ki.WORKLOADS["decode_n256_h32"]
+        N, K = len(d.lengths), args.spec_draft
+        sx = ki.make_prefill_inputs((K,) * N, d.H, d.dk, d.dv, d.dtype, d.s0_std, seed=6,
+                                    device="cuda")
+        state = sx.initial_state
+        sout = torch.empty_like(sx.v)
+        g = torch.Generator().manual_seed(6)
+        accepted = torch.randint(0, K + 1, (args.spec_rounds, N), generator=g,
+                                 dtype=torch.int32).cuda()
+        sd = torch.cuda.Stream()
+
+        def spec_round(i):
+            kda.spec_verify(sx.q, sx.k, sx.v, sx.log_alpha, sx.beta, sx.gate, state, out=sout)
+            kda.spec_commit(sx.k, sx.v, sx.log_alpha, sx.beta, state, accepted[i])
+
+        with torch.cuda.stream(sd):
+            for i in range(min(3, args.spec_rounds)):
+                spec_round(i)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            ev[0].record(sd)
+            for i in range(args.spec_rounds):
+                kda.spec_verify(sx.q, sx.k, sx.v, sx.log_alpha, sx.beta, sx.gate, state,
+                                out=sout)
+            ev[1].record(sd)
+            for i in range(args.spec_rounds):
+                kda.spec_commit(sx.k, sx.v, sx.log_alpha, sx.beta, state, accepted[i])
+            ev[2].record(sd)
+        torch.cuda.synchronize()
+        vus = ev[0].elapsed_time(ev[1]) / args.spec_rounds * 1e3
+        cus = ev[1].elapsed_time(ev[2]) / args.spec_rounds * 1e3
+        state_bytes = N * d.H * d.dk * d.dv * 4
+        frac_committed = float((accepted > 0).float().mean())
+        moved = state_bytes * (1 + 2 * frac_committed)  # verify reads; commit reads + writes
+        result["spec_verify"] = {
+            "workload": f"{d.name}, {K} bf16 drafts per sequence, accepted lengths uniform "
+                        f"in 0..{K}",
+            "rounds": args.spec_rounds, "verify_us": vus, "commit_us": cus,
+            "state_GBps": moved / ((vus + cus) * 1e-6) / 1e9,
+            "frac_hbm": moved / ((vus + cus) * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+            "draft_tokens_per_s": N * K / ((vus + cus) * 1e-6),
+        }
+        del sx, state, sout
         torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- CPU oracle

@@ -147,6 +147,43 @@ kda_status kda_decode_step(const kda_params* params, const void* q, const void* 
                            const void* gate, int32_t num_seqs, float* state, void* out,
                            void* stream);
 
+/*
+ * Speculative decoding.  The state is updated in place when decoding, so rejected drafts
+ * cannot be rolled back; instead the drafts' inputs are kept, kda_spec_verify computes
+ * every draft's output from the stored state without writing it, and kda_spec_commit
+ * replays the accepted prefix on chip and writes the state once -- no per-draft state is
+ * stored.  Source: digest of "Kimi K3: Open Frontier Intelligence", section "基础设施",
+ * speculative-decoding paragraph.
+ *
+ * Both take num_draft = K tokens per sequence (1 <= K <= 16), packed sequence-major:
+ *   q, k, log_alpha : [num_seqs * K, H, dk];  v, gate : [num_seqs * K, H, dv];
+ *   beta            : [num_seqs * K, H]       (row n*K + j is draft j of sequence n)
+ *   state           : fp32 [num_seqs, H, dk, dv]
+ *
+ * kda_spec_verify -- out[n*K + j] = the output kda_decode_step would give for draft j
+ * after drafts 0 .. j-1 had been decoded (equivalently, kda_chunk_prefill of the K drafts
+ * from `state`).  The state is only read.  out : [num_seqs * K, H, dv], params->dtype;
+ * must not overlap any other argument.
+ */
+kda_status kda_spec_verify(const kda_params* params, const void* q, const void* k,
+                           const void* v, const void* log_alpha, const void* beta,
+                           const void* gate, int32_t num_seqs, int32_t num_draft,
+                           const float* state, void* out, void* stream);
+
+/*
+ * kda_spec_commit -- advance each sequence's state over its first accepted[n] drafts,
+ * in place: afterwards state[n] equals what accepted[n] consecutive kda_decode_step calls
+ * on those drafts would have left (one read and one write of the state; a sequence with
+ * accepted[n] == 0 is not touched).  Only k, v, log_alpha and beta are read.
+ *   accepted : int32 [num_seqs], DEVICE memory (it is produced on the device by the
+ *              acceptance test); values are clamped to [0, num_draft].
+ * state must not overlap any other argument.
+ */
+kda_status kda_spec_commit(const kda_params* params, const void* k, const void* v,
+                           const void* log_alpha, const void* beta, int32_t num_seqs,
+                           int32_t num_draft, const int32_t* accepted, float* state,
+                           void* stream);
+
 /* Static English text for a status code (never NULL). */
 const char* kda_status_string(kda_status status);
 

@@ -284,3 +284,82 @@ kda_status kda_decode_step(const kda_params* params, const void* q, const void* 
 }
 
 }  // extern "C"
+
+namespace {
+
+kda_status spec(const char* entry, bool verify, const kda_params* params, const void* q,
+                const void* k, const void* v, const void* log_alpha, const void* beta,
+                const void* gate, int32_t num_seqs, int32_t num_draft,
+                const int32_t* accepted, float* state, void* out, void* stream) {
+    kda_status st = check_params(params);
+    if (st != KDA_OK) return st;
+    const kda_params& p = *params;
+    if (num_seqs < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "num_seqs %d < 0", num_seqs);
+    if (num_draft < 1 || num_draft > kda::kMaxDraft)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "num_draft %d outside [1, %d]", num_draft,
+                    kda::kMaxDraft);
+    if (num_seqs == 0) return ok();
+    const size_t es = p.dtype == KDA_DTYPE_BF16 ? 2 : 4;
+    const void* tens[] = {k, v, log_alpha};
+    const char* names[] = {"k", "v", "log_alpha"};
+    for (int i = 0; i < 3; ++i)
+        if ((st = check_ptr(names[i], tens[i], 16)) != KDA_OK) return st;
+    if ((st = check_ptr("beta", beta, es)) != KDA_OK) return st;
+    if (verify) {
+        if ((st = check_ptr("q", q, 16)) != KDA_OK) return st;
+        if ((st = check_ptr("gate", gate, 16)) != KDA_OK) return st;
+        if ((st = check_ptr("out", out, 16)) != KDA_OK) return st;
+    } else {
+        if ((st = check_ptr("accepted", accepted, 4)) != KDA_OK) return st;
+    }
+    if ((st = check_ptr("state", state, 16)) != KDA_OK) return st;
+    const int64_t NH = (int64_t)num_seqs * p.num_heads, NKH = NH * num_draft;
+    const uint64_t nk = NKH * p.dk * es, nv = NKH * p.dv * es;
+    const Range inputs[] = {range("q", verify ? q : nullptr, nk), range("k", k, nk),
+                            range("v", v, nv), range("log_alpha", log_alpha, nk),
+                            range("beta", beta, NKH * es),
+                            range("gate", verify ? gate : nullptr, nv),
+                            range("accepted", verify ? nullptr : accepted, num_seqs * 4ull)};
+    const Range rs = range("state", state, (uint64_t)NH * p.dk * p.dv * 4);
+    if (verify) {
+        const Range ro = range("out", out, nv);
+        if (overlaps(ro, rs)) return fail(KDA_ERR_INVALID_ARGUMENT, "out overlaps state");
+        for (const Range& in : inputs)
+            if (overlaps(ro, in)) return fail(KDA_ERR_INVALID_ARGUMENT, "out overlaps %s", in.name);
+    } else {
+        for (const Range& in : inputs)
+            if (overlaps(rs, in))
+                return fail(KDA_ERR_INVALID_ARGUMENT, "state overlaps %s", in.name);
+    }
+    kda::SpecArgs a;
+    a.dtype = p.dtype; a.H = p.num_heads; a.dk = p.dk; a.dv = p.dv;
+    a.floor_ = p.log_alpha_floor; a.scale = p.scale;
+    a.num_seqs = num_seqs; a.num_draft = num_draft; a.verify = verify;
+    a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta; a.gate = gate;
+    a.accepted = accepted; a.state = state; a.out = out;
+    const hipError_t e = kda::launch_spec(a, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s launch: %s", entry, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_spec_verify(const kda_params* params, const void* q, const void* k,
+                           const void* v, const void* log_alpha, const void* beta,
+                           const void* gate, int32_t num_seqs, int32_t num_draft,
+                           const float* state, void* out, void* stream) {
+    return spec("kda_spec_verify", true, params, q, k, v, log_alpha, beta, gate, num_seqs,
+                num_draft, nullptr, const_cast<float*>(state), out, stream);
+}
+
+kda_status kda_spec_commit(const kda_params* params, const void* k, const void* v,
+                           const void* log_alpha, const void* beta, int32_t num_seqs,
+                           int32_t num_draft, const int32_t* accepted, float* state,
+                           void* stream) {
+    return spec("kda_spec_commit", false, params, nullptr, k, v, log_alpha, beta, nullptr,
+                num_seqs, num_draft, accepted, state, nullptr, stream);
+}
+
+}  // extern "C"

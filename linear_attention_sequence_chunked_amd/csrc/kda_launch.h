@@ -37,7 +37,22 @@ struct PrefillArgs {
     int32_t order[kMaxOrdered];  // sequence ids, longest first
 };
 
+// Speculative verify / commit over num_draft tokens per sequence (kda_spec.hip).
+constexpr int kMaxDraft = 16;
+
+struct SpecArgs {
+    int dtype, H, dk, dv;
+    float floor_, scale;
+    int num_seqs, num_draft;
+    bool verify;               // true: outputs of every draft; false: commit accepted[n]
+    const void *q, *k, *v, *log_alpha, *beta, *gate;
+    const int32_t* accepted;   // device [num_seqs] (commit only)
+    float* state;
+    void* out;                 // verify only
+};
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_spec(const SpecArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 // bf16 path (kda_prefill_bf16.hip) and the value-slice widths it implements
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);

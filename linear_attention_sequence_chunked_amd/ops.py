@@ -157,3 +157,63 @@ def decode_step(q, k, v, log_alpha, beta, gate, state, log_alpha_floor: float = 
                                      _ptr(state), _ptr(out), _stream())
     _lib.check(st)
     return out
+
+
+def _drafts(name, t, dt, N, K, H, d):
+    _check_dev(name, t, dt)
+    shp = (N, K, H, d) if d else (N, K, H)
+    if t.dim() == len(shp) and tuple(t.shape) == shp:
+        return t
+    if tuple(t.shape) == (N * K,) + shp[2:]:
+        return t
+    raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shp} or "
+                     f"{(N * K,) + shp[2:]}")
+
+
+def spec_verify(q, k, v, log_alpha, beta, gate, state, log_alpha_floor: float = -0.3,
+                scale: float = 1.0, out: Optional[torch.Tensor] = None):
+    """Outputs of K draft tokens per sequence from `state` (fp32 [N, H, dk, dv], only
+    read).  q/k/log_alpha [N, K, H, dk], v/gate [N, K, H, dv], beta [N, K, H] (or the same
+    packed as [N*K, H, .]).  Returns o shaped like v."""
+    dt = q.dtype
+    if dt not in _DT:
+        raise ValueError(f"unsupported dtype {dt}")
+    _check_dev("state", state, torch.float32)
+    N, H, dk, dv = state.shape
+    K = q.shape[1] if q.dim() == 4 else q.shape[0] // max(N, 1)
+    for name, t, d in (("q", q, dk), ("k", k, dk), ("v", v, dv), ("log_alpha", log_alpha, dk),
+                       ("beta", beta, 0), ("gate", gate, dv)):
+        _drafts(name, t, dt, N, K, H, d)
+    if out is None:
+        out = torch.empty(v.shape, dtype=dt, device=q.device)
+    else:
+        _check_dev("out", out, dt)
+    p = _lib.params(_DT[dt], H, dk, dv, log_alpha_floor, scale)
+    st = _lib.load().kda_spec_verify(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
+                                     _ptr(log_alpha), _ptr(beta), _ptr(gate), N, K,
+                                     _ptr(state), _ptr(out), _stream())
+    _lib.check(st)
+    return out
+
+
+def spec_commit(k, v, log_alpha, beta, state, accepted, log_alpha_floor: float = -0.3):
+    """Advance state (fp32 [N, H, dk, dv], in place) over the first accepted[n] of the K
+    drafts of sequence n; accepted is an int32 GPU tensor [N] (clamped to [0, K])."""
+    dt = k.dtype
+    if dt not in _DT:
+        raise ValueError(f"unsupported dtype {dt}")
+    _check_dev("state", state, torch.float32)
+    _check_dev("accepted", accepted, torch.int32)
+    N, H, dk, dv = state.shape
+    if tuple(accepted.shape) != (N,):
+        raise ValueError("accepted must be [N]")
+    K = k.shape[1] if k.dim() == 4 else k.shape[0] // max(N, 1)
+    for name, t, d in (("k", k, dk), ("v", v, dv), ("log_alpha", log_alpha, dk),
+                       ("beta", beta, 0)):
+        _drafts(name, t, dt, N, K, H, d)
+    p = _lib.params(_DT[dt], H, dk, dv, log_alpha_floor, 1.0)
+    st = _lib.load().kda_spec_commit(ctypes.byref(p), _ptr(k), _ptr(v), _ptr(log_alpha),
+                                     _ptr(beta), N, K, _ptr(accepted), _ptr(state),
+                                     _stream())
+    _lib.check(st)
+    return state

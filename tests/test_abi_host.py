@@ -158,3 +158,63 @@ def test_prefill_checkpointed_rejects(kw, msg):
     assert st == INV, err
     assert msg in err, err
 
+
+
+def spec(verify=True, n=2, K=4, q=A, k=A + 0x10000, v=A + 0x20000, la=A + 0x30000,
+         beta=A + 0x40000, gate=A + 0x50000, acc=A + 0x60000, state=A + 0x100000,
+         out=A + 0x70000):
+    lib = _lib.load()
+    p = _lib.params(_lib.KDA_DTYPE_BF16, 2, 64, 64)
+    if verify:
+        st = lib.kda_spec_verify(ctypes.byref(p), q, k, v, la, beta, gate, n, K, state, out,
+                                 None)
+    else:
+        st = lib.kda_spec_commit(ctypes.byref(p), k, v, la, beta, n, K, acc, state, None)
+    return st, lib.kda_last_error().decode()
+
+
+@pytest.mark.parametrize("verify", [True, False])
+@pytest.mark.parametrize("kw,msg", [
+    (dict(K=0), "num_draft 0"),
+    (dict(K=17), "num_draft 17"),
+    (dict(n=-1), "num_seqs"),
+    (dict(k=None), "k is NULL"),
+    (dict(v=A + 0x20004), "v is not 16-byte aligned"),
+    (dict(beta=A + 0x40001), "beta is not 2-byte aligned"),
+    (dict(state=None), "state is NULL"),
+])
+def test_spec_rejects(verify, kw, msg):
+    st, err = spec(verify=verify, **kw)
+    assert st == INV, err
+    assert msg in err, err
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(q=None), "q is NULL"),
+    (dict(gate=None), "gate is NULL"),
+    (dict(out=None), "out is NULL"),
+    (dict(out=A + 0x100000), "out overlaps state"),
+    (dict(out=A + 0x20000), "out overlaps v"),
+])
+def test_spec_verify_rejects(kw, msg):
+    st, err = spec(verify=True, **kw)
+    assert st == INV, err
+    assert msg in err, err
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(acc=None), "accepted is NULL"),
+    (dict(acc=A + 0x60002), "accepted is not 4-byte aligned"),
+    (dict(state=A + 0x30000), "state overlaps log_alpha"),
+    (dict(state=A + 0x60000 - 16), "state overlaps"),
+])
+def test_spec_commit_rejects(kw, msg):
+    st, err = spec(verify=False, **kw)
+    assert st == INV, err
+    assert msg in err, err
+
+
+def test_spec_zero_sequences_is_a_no_op():
+    for verify in (True, False):
+        st, err = spec(verify=verify, n=0, q=None, state=None, acc=None)
+        assert st == _lib.KDA_OK, err
