@@ -91,6 +91,9 @@ def main() -> int:
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--spec-rounds", type=int, default=50)
     ap.add_argument("--spec-draft", type=int, default=4)
+    ap.add_argument("--segmented", action=argparse.BooleanOptionalAction, default=True,
+                    help="also time the segmented prefill on the few-head long workload")
+    ap.add_argument("--segment-len", type=int, default=16384)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -259,6 +262,48 @@ def main() -> int:
             "draft_tokens_per_s": N * K / ((vus + cus) * 1e-6),
         }
         del sx, state, sout
+        torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------------- segmented prefill
+    if args.segmented:
+        sw = ki.WORKLOADS["prefill_b1_h4_t524288"]
+        sxx = ki.make_workload_inputs(sw, seed=2, device="cuda")
+        L = args.segment_len
+        sout = torch.empty_like(sxx.v)
+        sSf = torch.empty((1, sw.H, sw.dk, sw.dv), dtype=torch.float32, device="cuda")
+        ws = torch.empty(1 << 28, dtype=torch.uint8, device="cuda")
+
+        def plain_run():
+            kda.chunk_prefill(sxx.q, sxx.k, sxx.v, sxx.log_alpha, sxx.beta, sxx.gate,
+                              cu_seqlens=sxx.cu_seqlens, cu_seqlens_host=sxx.cu_seqlens_host,
+                              out=sout, final_state=sSf)
+
+        def seg_run():
+            kda.chunk_prefill_segmented(sxx.q, sxx.k, sxx.v, sxx.log_alpha, sxx.beta, sxx.gate,
+                                        sxx.cu_seqlens_host, L, out=sout, final_state=sSf,
+                                        workspace=ws)
+
+        def med_ms(fn, reps=5):
+            fn()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(reps):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            return float(np.median(ts))
+
+        pms, sms = med_ms(plain_run), med_ms(seg_run)
+        ttok = sum(sw.lengths)
+        result["segmented"] = {
+            "workload": sw.name, "segment_len": L, "plain_ms": pms, "segmented_ms": sms,
+            "speedup": pms / sms, "segmented_tokens_per_s": ttok / (sms * 1e-3),
+        }
+        del sxx, sout, ws
         torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- CPU oracle

@@ -132,6 +132,45 @@ kda_status kda_chunk_prefill_checkpointed(const kda_params* params, const void* 
                                           float* checkpoints, void* stream);
 
 /*
+ * kda_chunk_prefill_segmented -- kda_chunk_prefill for long sequences with few heads,
+ * where one (sequence, head) chain per value slice leaves most of the GPU idle.  Each
+ * sequence is cut into segments of segment_len tokens that run side by side; per
+ * segment the library computes the state it grows from zero and its state transition
+ * (the product of the chunk transitions, a dk x dk matrix, by running the same chain
+ * with zero values from the identity), joins the segments with a scan to get the true
+ * state entering each, and reruns every segment from it to write the outputs.  Source:
+ * digest of "Kimi K3: Open Frontier Intelligence", section "基础设施" (KDA context
+ * parallelism: each segment's effect = its own grown state + the incoming state carried
+ * through the segment's transition, joined by a prefix scan); here the segments share one
+ * GPU instead of spanning several.
+ *
+ *   The arguments of kda_chunk_prefill (cu_seqlens_host only: the library writes its own
+ *   device tables into the workspace), plus
+ *   segment_len     : tokens per segment, a positive multiple of 16 (chunk boundaries
+ *                     stay aligned at the sequence start).
+ *   workspace       : device memory of at least kda_prefill_segmented_workspace(...)
+ *                     bytes, 256-byte aligned, overlapping no other argument; its
+ *                     contents on entry do not matter.  Calls that share a workspace
+ *                     must be ordered on one stream.
+ * Work is about three prefills' worth, spread over (segments x heads) instead of heads;
+ * results agree with kda_chunk_prefill to the operator's tolerance (not bit for bit:
+ * the segment states are joined in fp32).  dtype may be bf16 or fp32.
+ */
+kda_status kda_chunk_prefill_segmented(const kda_params* params, const void* q,
+                                       const void* k, const void* v, const void* log_alpha,
+                                       const void* beta, const void* gate,
+                                       const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                       const float* initial_state, float* final_state,
+                                       void* out, int32_t segment_len, void* workspace,
+                                       int64_t workspace_bytes, void* stream);
+
+/* Bytes of workspace kda_chunk_prefill_segmented needs for these arguments, or -1 if
+ * they are invalid (kda_last_error() says why). */
+int64_t kda_prefill_segmented_workspace(const kda_params* params,
+                                        const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                        int32_t segment_len);
+
+/*
  * kda_decode_step -- one token per sequence, state updated in place.
  *
  *   q, k, log_alpha : [num_seqs, H, dk];  v, gate, out : [num_seqs, H, dv];

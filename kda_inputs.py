@@ -71,6 +71,9 @@ WORKLOADS = {
     # varlen packed prefill: 64 sequences, H=32, d=128, per-sequence S0
     "varlen_n64_h32": Workload("varlen_n64_h32", varlen_lengths(), 32, 128, 128, "bf16",
                                0.02),
+    # few heads, long context (the segmented prefill's case): B=1, H=4, T=524288, d=128
+    "prefill_b1_h4_t524288": Workload("prefill_b1_h4_t524288", (524288,), 4, 128, 128,
+                                      "bf16", 0.0),
 }
 
 

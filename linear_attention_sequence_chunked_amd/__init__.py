@@ -4,8 +4,8 @@ The compute runs in libkda.so (hand-written HIP kernels behind the C ABI of
 include/kda.h); this package only marshals torch tensors and the current stream.
 """
 from ._lib import KdaError, LIB_PATH, load as load_library  # noqa: F401
-from .ops import (checkpoint_slot, chunk_prefill, decode_step, spec_commit,  # noqa: F401
-                  spec_verify)
+from .ops import (checkpoint_slot, chunk_prefill, chunk_prefill_segmented,  # noqa: F401
+                  decode_step, spec_commit, spec_verify)
 
-__all__ = ["chunk_prefill", "checkpoint_slot", "decode_step", "spec_verify", "spec_commit",
+__all__ = ["chunk_prefill", "chunk_prefill_segmented", "checkpoint_slot", "decode_step", "spec_verify", "spec_commit",
            "KdaError", "load_library", "LIB_PATH"]

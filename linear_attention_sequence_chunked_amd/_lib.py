@@ -10,7 +10,8 @@ LIB_PATH = os.path.join(HERE, "libkda.so")
 KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP = 0, 1, 2, 3
 KDA_DTYPE_BF16, KDA_DTYPE_F32 = 0, 1
 EXPORTED = ("kda_chunk_prefill", "kda_chunk_prefill_checkpointed", "kda_decode_step",
-            "kda_spec_verify", "kda_spec_commit", "kda_status_string", "kda_last_error",
+            "kda_spec_verify", "kda_spec_commit", "kda_chunk_prefill_segmented",
+            "kda_prefill_segmented_workspace", "kda_status_string", "kda_last_error",
             "kda_abi_version")
 
 
@@ -54,6 +55,13 @@ def load() -> ctypes.CDLL:
     lib.kda_spec_verify.restype = ctypes.c_int
     lib.kda_spec_commit.argtypes = [ctypes.POINTER(KdaParams), P, P, P, P, I32, I32, P, P, P]
     lib.kda_spec_commit.restype = ctypes.c_int
+    lib.kda_chunk_prefill_segmented.argtypes = [ctypes.POINTER(KdaParams), P, P, P, P, P, P,
+                                                ctypes.POINTER(I32), I32, P, P, P, I32, P,
+                                                ctypes.c_int64, P]
+    lib.kda_chunk_prefill_segmented.restype = ctypes.c_int
+    lib.kda_prefill_segmented_workspace.argtypes = [ctypes.POINTER(KdaParams),
+                                                    ctypes.POINTER(I32), I32, I32]
+    lib.kda_prefill_segmented_workspace.restype = ctypes.c_int64
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_last_error.argtypes = []

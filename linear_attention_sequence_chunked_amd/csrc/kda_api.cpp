@@ -186,6 +186,7 @@ kda_status prefill(const char* entry, const kda_params* params, const void* q, c
     a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta; a.gate = gate;
     a.cu_seqlens = cu_seqlens; a.initial_state = initial_state; a.final_state = final_state;
     a.out = out;
+    a.v_zero = false; a.s0_identity = false;
     a.checkpoints = n_ckpt > 0 ? checkpoints : nullptr;
     a.ckpt_chunks = n_ckpt > 0 ? ckpt_every / 16 : 0;
     a.num_ordered = 0;
@@ -360,6 +361,176 @@ kda_status kda_spec_commit(const kda_params* params, const void* k, const void* 
                            void* stream) {
     return spec("kda_spec_commit", false, params, nullptr, k, v, log_alpha, beta, nullptr,
                 num_seqs, num_draft, accepted, state, nullptr, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+struct SegPlan {
+    std::vector<int32_t> seg_cu, seg_first;
+    int64_t nseg = 0;
+    uint64_t off_cu = 0, off_first = 0, off_M = 0, off_loc = 0, off_in = 0, total = 0;
+};
+
+uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+
+kda_status seg_plan(const kda_params* params, const int32_t* cu, int32_t N, int32_t L,
+                    SegPlan& pl) {
+    kda_status st = check_params(params);
+    if (st != KDA_OK) return st;
+    if (N < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "num_seqs %d < 1", N);
+    if (!cu) return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens_host is NULL");
+    if (cu[0] != 0) return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens_host[0] = %d, must be 0", cu[0]);
+    if (L <= 0 || L % 16)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "segment_len %d must be a positive multiple of 16", L);
+    pl.seg_first.assign(N + 1, 0);
+    pl.seg_cu.clear();
+    for (int32_t n = 0; n < N; ++n) {
+        if (cu[n + 1] < cu[n])
+            return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens_host decreases at index %d", n + 1);
+        pl.seg_first[n] = (int32_t)pl.seg_cu.size();
+        for (int64_t t = cu[n]; t < cu[n + 1]; t += L) pl.seg_cu.push_back((int32_t)t);
+    }
+    pl.nseg = (int64_t)pl.seg_cu.size();
+    pl.seg_first[N] = (int32_t)pl.nseg;
+    pl.seg_cu.push_back(cu[N]);
+    const int64_t H = params->num_heads, dk = params->dk, dv = params->dv;
+    pl.off_cu = 0;
+    pl.off_first = align256(pl.off_cu + 4 * (uint64_t)(pl.nseg + 1));
+    pl.off_M = align256(pl.off_first + 4 * (uint64_t)(N + 1));
+    pl.off_loc = align256(pl.off_M + 4 * (uint64_t)pl.nseg * H * dk * dk);
+    pl.off_in = align256(pl.off_loc + 4 * (uint64_t)pl.nseg * H * dk * dv);
+    pl.total = align256(pl.off_in + 4 * (uint64_t)pl.nseg * H * dk * dv);
+    return KDA_OK;
+}
+
+hipError_t write_table(int32_t* dst, const std::vector<int32_t>& vals, hipStream_t st) {
+    for (size_t i = 0; i < vals.size(); i += kda::kTableChunk) {
+        kda::TableArgs t;
+        t.dst = dst;
+        t.offset = (int)i;
+        t.count = (int)std::min<size_t>(kda::kTableChunk, vals.size() - i);
+        std::copy(vals.begin() + i, vals.begin() + i + t.count, t.vals);
+        const hipError_t e = kda::launch_table(t, st);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t kda_prefill_segmented_workspace(const kda_params* params,
+                                        const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                        int32_t segment_len) {
+    SegPlan pl;
+    if (seg_plan(params, cu_seqlens_host, num_seqs, segment_len, pl) != KDA_OK) return -1;
+    ok();
+    return (int64_t)pl.total;
+}
+
+kda_status kda_chunk_prefill_segmented(const kda_params* params, const void* q,
+                                       const void* k, const void* v, const void* log_alpha,
+                                       const void* beta, const void* gate,
+                                       const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                       const float* initial_state, float* final_state,
+                                       void* out, int32_t segment_len, void* workspace,
+                                       int64_t workspace_bytes, void* stream) {
+    SegPlan pl;
+    kda_status st = seg_plan(params, cu_seqlens_host, num_seqs, segment_len, pl);
+    if (st != KDA_OK) return st;
+    const kda_params& p = *params;
+    const int64_t T = cu_seqlens_host[num_seqs];
+    const int64_t H = p.num_heads;
+    const size_t es = p.dtype == KDA_DTYPE_BF16 ? 2 : 4;
+    const void* tens[] = {q, k, v, log_alpha, gate, out};
+    const char* names[] = {"q", "k", "v", "log_alpha", "gate", "out"};
+    if (T > 0) {
+        for (int i = 0; i < 6; ++i)
+            if ((st = check_ptr(names[i], tens[i], 16)) != KDA_OK) return st;
+        if ((st = check_ptr("beta", beta, es)) != KDA_OK) return st;
+    }
+    if (initial_state && (st = check_ptr("initial_state", initial_state, 16)) != KDA_OK) return st;
+    if (final_state && (st = check_ptr("final_state", final_state, 16)) != KDA_OK) return st;
+    if ((st = check_ptr("workspace", workspace, 256)) != KDA_OK) return st;
+    if (workspace_bytes < (int64_t)pl.total)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "workspace_bytes %lld < %llu needed",
+                    (long long)workspace_bytes, (unsigned long long)pl.total);
+    const uint64_t nk = (uint64_t)T * H * p.dk * es, nv = (uint64_t)T * H * p.dv * es;
+    const uint64_t ns = (uint64_t)num_seqs * H * p.dk * p.dv * 4;
+    const Range args[] = {range("q", q, nk), range("k", k, nk), range("v", v, nv),
+                          range("log_alpha", log_alpha, nk), range("beta", beta, (uint64_t)T * H * es),
+                          range("gate", gate, nv), range("initial_state", initial_state, ns),
+                          range("final_state", final_state, ns), range("out", out, nv)};
+    const Range rw = range("workspace", workspace, pl.total);
+    for (const Range& r : args)
+        if (overlaps(rw, r)) return fail(KDA_ERR_INVALID_ARGUMENT, "workspace overlaps %s", r.name);
+    const Range ro = args[8];
+    for (int i = 0; i < 8; ++i)
+        if (overlaps(ro, args[i])) return fail(KDA_ERR_INVALID_ARGUMENT, "out overlaps %s", args[i].name);
+    if (final_state) {
+        const Range rf = args[7];
+        for (int i = 0; i < 6; ++i)
+            if (overlaps(rf, args[i]))
+                return fail(KDA_ERR_INVALID_ARGUMENT, "final_state overlaps %s", args[i].name);
+        if (overlaps(rf, args[6]) && args[6].lo != rf.lo)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "final_state overlaps initial_state");
+    }
+
+    char* ws = static_cast<char*>(workspace);
+    int32_t* seg_cu = reinterpret_cast<int32_t*>(ws + pl.off_cu);
+    int32_t* seg_first = reinterpret_cast<int32_t*>(ws + pl.off_first);
+    float* M = reinterpret_cast<float*>(ws + pl.off_M);
+    float* Sloc = reinterpret_cast<float*>(ws + pl.off_loc);
+    float* Sin = reinterpret_cast<float*>(ws + pl.off_in);
+    const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = write_table(seg_cu, pl.seg_cu, hs);
+    if (e == hipSuccess) e = write_table(seg_first, pl.seg_first, hs);
+    if (e != hipSuccess)
+        return fail(KDA_ERR_HIP, "kda_chunk_prefill_segmented tables: %s", hipGetErrorString(e));
+
+    const int cus = device_cu_count();
+    kda::PrefillArgs a;
+    a.dtype = p.dtype; a.H = p.num_heads; a.dk = p.dk; a.dv = p.dv;
+    a.floor_ = p.log_alpha_floor; a.scale = p.scale; a.num_seqs = (int)pl.nseg;
+    a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta; a.gate = gate;
+    a.cu_seqlens = seg_cu; a.checkpoints = nullptr; a.ckpt_chunks = 0; a.num_ordered = 0;
+    const int64_t pairs = pl.nseg * H, seg_chunks = segment_len / 16;
+    const char* phase = "";
+    // 1: each segment's own state, from zero (outputs not written)
+    a.v_zero = false; a.s0_identity = false;
+    a.initial_state = nullptr; a.final_state = Sloc; a.out = nullptr;
+    a.nv = kda::prefill_pick_nv(p.dv, pairs, seg_chunks, cus);
+    e = kda::launch_prefill(a, hs);
+    phase = "segment states";
+    // 2: each segment's transition: the chain from the identity with zero values
+    if (e == hipSuccess) {
+        a.dv = p.dk; a.v_zero = true; a.s0_identity = true; a.final_state = M;
+        a.nv = kda::prefill_pick_nv(p.dk, pairs, seg_chunks, cus);
+        e = kda::launch_prefill(a, hs);
+        phase = "segment transitions";
+    }
+    // 3: the scan over each sequence's segments (and the final states)
+    if (e == hipSuccess) {
+        kda::CombineArgs c;
+        c.M = M; c.Sloc = Sloc; c.Sin = Sin; c.S0 = initial_state; c.Sf = final_state;
+        c.seg_first = seg_first; c.H = p.num_heads;
+        e = kda::launch_combine(c, num_seqs, p.dk, p.dv, hs);
+        phase = "combine";
+    }
+    // 4: every segment again from its true incoming state, writing the outputs
+    if (e == hipSuccess) {
+        a.dv = p.dv; a.v_zero = false; a.s0_identity = false;
+        a.initial_state = Sin; a.final_state = nullptr; a.out = out;
+        a.nv = kda::prefill_pick_nv(p.dv, pairs, seg_chunks, cus);
+        e = kda::launch_prefill(a, hs);
+        phase = "outputs";
+    }
+    if (e != hipSuccess)
+        return fail(KDA_ERR_HIP, "kda_chunk_prefill_segmented (%s): %s", phase, hipGetErrorString(e));
+    return ok();
 }
 
 }  // extern "C"

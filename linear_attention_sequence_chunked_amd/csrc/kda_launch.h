@@ -30,6 +30,8 @@ struct PrefillArgs {
     const float* initial_state;  // may be null
     float* final_state;          // may be null
     void* out;
+    bool v_zero;                 // read V as zeros (segment transitions of the segmented path)
+    bool s0_identity;            // initial state = identity (needs dk == dv)
     float* checkpoints;          // state snapshots, or null (see kda_chunk_prefill_checkpointed)
     int ckpt_chunks;             // chunks between snapshots (checkpoint_every / 16); 0 = none
     int nv;                      // value columns per workgroup (dv-slice width)
@@ -50,6 +52,26 @@ struct SpecArgs {
     float* state;
     void* out;                 // verify only
 };
+
+// Segmented prefill (kda_segment.hip): a small table written through kernel arguments
+// (no host-to-device copy), and the scan that joins the segments.
+constexpr int kTableChunk = 960;
+struct TableArgs {
+    int32_t* dst;
+    int offset, count;
+    int32_t vals[kTableChunk];
+};
+struct CombineArgs {
+    const float* M;          // [num_segments, H, dk, dk] segment transitions
+    const float* Sloc;       // [num_segments, H, dk, dv] segment states grown from zero
+    float* Sin;              // [num_segments, H, dk, dv] states entering the segments (out)
+    const float* S0;         // [num_seqs, H, dk, dv] or null
+    float* Sf;               // [num_seqs, H, dk, dv] or null
+    const int32_t* seg_first;  // device [num_seqs + 1]: first segment of each sequence
+    int H;
+};
+hipError_t launch_table(const TableArgs& a, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs& a, int num_seqs, int dk, int dv, hipStream_t stream);
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_spec(const SpecArgs& a, hipStream_t stream);

@@ -42,7 +42,8 @@ struct KArgs {
     float* Sf;
     float* ck;      // state snapshots or null
     int ck_chunks;  // chunks between snapshots
-    T* out;
+    int v_zero, s0_identity;
+    T* out;         // null: no output rows
     int H, n_slices, num_groups, num_ordered;
     float floor_, scale;
     int32_t order[kMaxOrdered];
@@ -103,6 +104,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const KArgs<T> a) {
             for (int i = 0; i < 4; ++i) {
                 float x = 0.f;
                 if (a.S0 && j < NCB) x = a.S0[sbase + (16 * b + 4 * g + i) * DV + col0 + 16 * j + r];
+                if (a.s0_identity && 16 * b + 4 * g + i == col0 + 16 * j + r) x = 1.f;
                 S[jj][b][i] = x;
             }
         }
@@ -140,7 +142,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const KArgs<T> a) {
             typedef typename Vec4<T>::type V4;
             for (int row = tid / TPR; row < kChunk; row += RPP) {
                 V4 x = {};
-                if (row < Cp)
+                if (row < Cp && !a.v_zero)
                     x = *reinterpret_cast<const V4*>(a.v + (t0 + row) * rowv + (int64_t)h * DV +
                                                      col0 + col);
                 *reinterpret_cast<V4*>(&s_v[row * VS + col]) = x;
@@ -306,7 +308,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const KArgs<T> a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 4 * g + i;
-                if (row < Cp) {
+                if (a.out && row < Cp) {
                     const int64_t off = (t0 + row) * rowv + (int64_t)h * DV + col;
                     a.out[off] = from_f32<T>(to_f32(a.gate[off]) * O[i]);
                 }
@@ -337,6 +339,7 @@ hipError_t launch_typed(const PrefillArgs& p, hipStream_t st) {
     a.la = (const T*)p.log_alpha; a.beta = (const T*)p.beta; a.gate = (const T*)p.gate;
     a.cu = p.cu_seqlens; a.S0 = p.initial_state; a.Sf = p.final_state; a.out = (T*)p.out;
     a.ck = p.checkpoints; a.ck_chunks = p.ckpt_chunks;
+    a.v_zero = p.v_zero; a.s0_identity = p.s0_identity;
     a.H = p.H; a.n_slices = DV / (16 * NCB); a.num_groups = p.num_seqs * p.H;
     a.num_ordered = p.num_ordered; a.floor_ = p.floor_; a.scale = p.scale;
     for (int i = 0; i < p.num_ordered; ++i) a.order[i] = p.order[i];

@@ -255,7 +255,8 @@ struct BArgs {
     float* Sf;
     float* ck;      // state snapshots or null
     int ck_chunks;  // chunks between snapshots
-    bf16* out;
+    int v_zero, s0_identity;
+    bf16* out;      // null: no output rows
     int H, n_slices, num_groups, groups_padded, num_ordered;
     float floor_, scale;
     int32_t order[kMaxOrdered];
@@ -288,7 +289,8 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
             const int64_t base = ((int64_t)seq * H + h) * DK * DV;
             for (int row = lane >> 4; row < DK; row += 4)
                 a.Sf[base + row * DV + col0 + 16 * wave + (lane & 15)] =
-                    a.S0 ? a.S0[base + row * DV + col0 + 16 * wave + (lane & 15)] : 0.f;
+                    a.S0 ? a.S0[base + row * DV + col0 + 16 * wave + (lane & 15)]
+                         : (a.s0_identity && row == col0 + 16 * wave + (lane & 15)) ? 1.f : 0.f;
         }
         return;
     }
@@ -372,7 +374,11 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
             const int nq = recs(eq), nv = recs(ev);
             Rq = rsrc(pq, nq); Rk = rsrc(pk, nq); Rl = rsrc(pl, nq); Rb = rsrc(pb, recs(eb));
 #pragma unroll
-            for (int e = 0; e < C::VG_PER_WAVE; ++e) Rv[e] = rsrc(pv[e], vg_own[e] ? nv : 0);
+            for (int e = 0; e < C::VG_PER_WAVE; ++e) {  // V read as zeros, or the gate unused:
+                const bool gate = vg_f[e] & 1;           // an empty range (nothing is read)
+                const bool read = vg_own[e] && (gate ? a.out != nullptr : !a.v_zero);
+                Rv[e] = rsrc(pv[e], read ? nv : 0);
+            }
         };
         make();
         auto rebase = [&]() {  // keeps every offset below 2^30 + PF chunks
@@ -578,7 +584,8 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
         for (int b = 0; b < KB; ++b)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                S[b][i] = a.S0 ? a.S0[sbase + (16 * b + 4 * g + i) * DV + ccol] : 0.f;
+                S[b][i] = a.S0 ? a.S0[sbase + (16 * b + 4 * g + i) * DV + ccol]
+                               : (a.s0_identity && 16 * b + 4 * g + i == ccol) ? 1.f : 0.f;
         const float scale = a.scale;
         // snapshots: the state after every ck_chunks-th chunk (when that chunk is full) goes
         // to slot tbeg / m + j - 1 for the j-th snapshot, m = 16 ck_chunks tokens
@@ -645,7 +652,7 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
                 lds_st(Ob + r * C::ORS + 8 * g, to_bf4(gt * O));
                 const bf16x4 orow = lds_tr(Ob + tr_o);
                 const int64_t t0 = tbeg + 16 * (int64_t)c;
-                if (t0 + r < tend)
+                if (a.out && t0 + r < tend)
                     *reinterpret_cast<bf16x4*>(a.out + (t0 + r) * rowv + (int64_t)h * DV + col0 + 16 * wave + 4 * g) = orow;
             }
             lds_barrier();
@@ -668,6 +675,7 @@ hipError_t launch_bf16(const PrefillArgs& p, hipStream_t st) {
     a.la = (const bf16*)p.log_alpha; a.beta = (const bf16*)p.beta; a.gate = (const bf16*)p.gate;
     a.cu = p.cu_seqlens; a.S0 = p.initial_state; a.Sf = p.final_state; a.out = (bf16*)p.out;
     a.ck = p.checkpoints; a.ck_chunks = p.ckpt_chunks;
+    a.v_zero = p.v_zero; a.s0_identity = p.s0_identity;
     a.H = p.H; a.n_slices = DV / (16 * NCB); a.num_groups = p.num_seqs * p.H;
     a.groups_padded = (a.num_groups + 7) / 8 * 8;
     a.num_ordered = p.num_ordered; a.floor_ = p.floor_; a.scale = p.scale;

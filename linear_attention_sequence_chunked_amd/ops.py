@@ -217,3 +217,54 @@ def spec_commit(k, v, log_alpha, beta, state, accepted, log_alpha_floor: float =
                                      _stream())
     _lib.check(st)
     return state
+
+
+def chunk_prefill_segmented(q, k, v, log_alpha, beta, gate, cu_seqlens, segment_len: int,
+                            initial_state=None, output_final_state: bool = True,
+                            log_alpha_floor: float = -0.3, scale: float = 1.0,
+                            out: Optional[torch.Tensor] = None,
+                            final_state: Optional[torch.Tensor] = None,
+                            workspace: Optional[torch.Tensor] = None):
+    """chunk_prefill for long sequences with few heads: each sequence is cut into
+    segments of segment_len tokens (a multiple of 16) that run side by side and are
+    joined by a scan over the segment states.  Packed [T_total, H, .] inputs with
+    cu_seqlens (list, or tensor copied to the host).  Returns (o, final_state or None)."""
+    dt = q.dtype
+    if dt not in _DT:
+        raise ValueError(f"unsupported dtype {dt}")
+    cu_host = [int(x) for x in (cu_seqlens.tolist() if isinstance(cu_seqlens, torch.Tensor)
+                                else cu_seqlens)]
+    Ttot, H, dk = q.shape
+    dv = v.shape[-1]
+    N = len(cu_host) - 1
+    for name, t, shp in (("q", q, (Ttot, H, dk)), ("k", k, (Ttot, H, dk)),
+                         ("v", v, (Ttot, H, dv)), ("log_alpha", log_alpha, (Ttot, H, dk)),
+                         ("beta", beta, (Ttot, H)), ("gate", gate, (Ttot, H, dv))):
+        _check_dev(name, t, dt)
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shp}")
+    if initial_state is not None:
+        _check_dev("initial_state", initial_state, torch.float32)
+        if tuple(initial_state.shape) != (N, H, dk, dv):
+            raise ValueError("initial_state must be [N, H, dk, dv]")
+    cu_h = (ctypes.c_int32 * len(cu_host))(*cu_host)
+    p = _lib.params(_DT[dt], H, dk, dv, log_alpha_floor, scale)
+    lib = _lib.load()
+    need = lib.kda_prefill_segmented_workspace(ctypes.byref(p), cu_h, N, int(segment_len))
+    if need < 0:
+        raise _lib.KdaError(_lib.KDA_ERR_INVALID_ARGUMENT, lib.kda_last_error().decode())
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((Ttot, H, dv), dtype=dt, device=q.device)
+    else:
+        _check_dev("out", out, dt)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+    st = lib.kda_chunk_prefill_segmented(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
+                                         _ptr(log_alpha), _ptr(beta), _ptr(gate), cu_h, N,
+                                         _ptr(initial_state), _ptr(final_state), _ptr(out),
+                                         int(segment_len), _ptr(workspace), workspace.numel(),
+                                         _stream())
+    _lib.check(st)
+    return out, final_state

@@ -218,3 +218,52 @@ def test_spec_zero_sequences_is_a_no_op():
     for verify in (True, False):
         st, err = spec(verify=verify, n=0, q=None, state=None, acc=None)
         assert st == _lib.KDA_OK, err
+
+
+def seg_ws(cu_host, L, p=None):
+    lib = _lib.load()
+    p = p or _lib.params(_lib.KDA_DTYPE_BF16, 2, 64, 64)
+    n = len(cu_host) - 1
+    return lib.kda_prefill_segmented_workspace(ctypes.byref(p), cu(*cu_host), n, L)
+
+
+def test_segmented_workspace_size():
+    """cu = (0, 40, 40, 100), L = 32: segments [0,32) [32,40) [40,72) [72,100) -> 4.
+    Layout (256-byte aligned regions): segment table (5 int32), first-segment table
+    (4 int32), transitions 4*H*dk*dk fp32, own states and incoming states 4*H*dk*dv fp32
+    each."""
+    M = 4 * 2 * 64 * 64 * 4
+    assert seg_ws((0, 40, 40, 100), 32) == 512 + M + M + M
+    # one segment per sequence when L covers it; empty sequences have none
+    assert seg_ws((0, 16, 16), 512) == 256 + 256 + 3 * (1 * 2 * 64 * 64 * 4)
+
+
+@pytest.mark.parametrize("L", [0, -16, 24])
+def test_segmented_workspace_rejects_segment_len(L):
+    assert seg_ws((0, 40), L) == -1
+    assert "segment_len" in _lib.load().kda_last_error().decode()
+
+
+def prefill_seg(L=32, ws=A + 0x400000, ws_bytes=1 << 22, cu_host=None, out=A + 0x70000):
+    lib = _lib.load()
+    p = _lib.params(_lib.KDA_DTYPE_BF16, 2, 64, 64)
+    cu_host = cu_host or cu(0, 40, 100)
+    st = lib.kda_chunk_prefill_segmented(ctypes.byref(p), A, A + 0x10000, A + 0x20000,
+                                         A + 0x30000, A + 0x40000, A + 0x50000, cu_host, 2,
+                                         None, None, out, L, ws, ws_bytes, None)
+    return st, lib.kda_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(L=40), "segment_len 40"),
+    (dict(ws=None), "workspace is NULL"),
+    (dict(ws=A + 0x400010), "workspace is not 256-byte aligned"),
+    (dict(ws_bytes=1024), "workspace_bytes 1024"),
+    (dict(ws=A + 0x20000 - 0x100), "workspace overlaps"),
+    (dict(out=A + 0x10000), "out overlaps k"),
+    (dict(cu_host=cu(0, 50, 40)), "decreases"),
+])
+def test_segmented_rejects(kw, msg):
+    st, err = prefill_seg(**kw)
+    assert st == INV, err
+    assert msg in err, err
