@@ -233,8 +233,8 @@ struct Cfg {
     // Kt ring (4 slots, so its slot index is a multiple of the loop's unroll): Kt rows
     // (gram at c-2, Wt at c-1)
     static constexpr int K_SIZE = ROWK;
-    // beta ring (2)
-    static constexpr int B_SIZE = 64;
+    // beta ring (2): four copies of the 16 values (one per lane group of the writer)
+    static constexpr int B_SIZE = 256;
     // gram ring (4): T^T fragment (C(T^T) = A-fragment of T) padded to 16 bytes per lane
     // with zeros (a 32-deep operand), and P hi|lo A-fragments side by side (16 bytes)
     static constexpr int G_TT = 0, G_P = 1024, G_SIZE = 2048;
@@ -408,9 +408,20 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
             load(std::integral_constant<int, (decltype(J)::value + 1) % PF>{});
             __builtin_amdgcn_sched_barrier(0);
         });
-        // positions of this lane's channel groups dch..dch+3 and dch+4..dch+7 (see Cfg)
-        const int pos = 32 * w + 16 * (g & 1) + 4 * (g >> 1);
-        const int rowq = r * C::RSQ + 2 * pos, rowk = r * C::RSK + 2 * pos;
+        // Row-tile stores.  The lane holds channel quads 2g and 2g+1 of this wave's 32
+        // channels (relative numbering), but a 16-byte piece of the tile at position
+        // 32w + 8j holds quads j and j+4 (see Cfg).  Lanes 32 apart swap halves (lane g < 2
+        // gives quad 2g+1 and takes quad 2g+4 of lane g+2), after which lane g holds the
+        // piece j = 2 (g & 1) + (g >> 1) and stores it with one 16-byte write: a
+        // conflict-free row pattern, where two 8-byte halves 16 bytes apart conflict.
+        const int jp = 2 * (g & 1) + (g >> 1);
+        const int rowq = r * C::RSQ + 64 * w + 16 * jp, rowk = r * C::RSK + 64 * w + 16 * jp;
+        auto piece = [](bf16x4 a, bf16x4 b) {  // [quad 2g | quad 2g+1] -> the lane's piece
+            const u32x2 x = __builtin_bit_cast(u32x2, a), y = __builtin_bit_cast(u32x2, b);
+            const auto s0 = __builtin_amdgcn_permlane32_swap(x[0], y[0], false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(x[1], y[1], false, false);
+            return u32x4{s0[0], s1[0], s0[1], s1[1]};
+        };
         // lane r stores gamma of channel dch + (r & 7); lanes r and r + 8 store the same
         // value to the same word
         const bool gb0 = r & 1, gb1 = r & 2, gb2 = r & 4;
@@ -434,6 +445,7 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
                 float GC[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) GC[j] = row_last(G[j]);  // chunk totals
+                bf16x4 qh[2], ql[2], kbh[2], kbl[2], kt[2];
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
                     f32x4 F, Fi;
@@ -443,22 +455,23 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
                         F[i] = __builtin_amdgcn_exp2f(d);
                         Fi[i] = __builtin_amdgcn_exp2f(-d);
                     }
-                    bf16x4 qh, ql, kbh, kbl;
-                    split4(q4[hh] * F, qh, ql);
-                    split4(k4[hh] * Fi, kbh, kbl);
-                    lds_st(L + C::L_QH + rowq + 16 * hh, qh);
-                    lds_st(L + C::L_QL + rowq + 16 * hh, ql);
-                    lds_st(L + C::L_KBH + rowk + 16 * hh, kbh);
-                    lds_st(L + C::L_KBL + rowk + 16 * hh, kbl);
-                    lds_st(kslot(c) + rowk + 16 * hh, to_bf4(k4[hh] * F));
+                    split4(q4[hh] * F, qh[hh], ql[hh]);
+                    split4(k4[hh] * Fi, kbh[hh], kbl[hh]);
+                    kt[hh] = to_bf4(k4[hh] * F);
                 }
+                lds_st(L + C::L_QH + rowq, piece(qh[0], qh[1]));
+                lds_st(L + C::L_QL + rowq, piece(ql[0], ql[1]));
+                lds_st(L + C::L_KBH + rowk, piece(kbh[0], kbh[1]));
+                lds_st(L + C::L_KBL + rowk, piece(kbl[0], kbl[1]));
+                lds_st(kslot(c) + rowk, piece(kt[0], kt[1]));
                 const float x01 = gb0 ? GC[1] : GC[0], x23 = gb0 ? GC[3] : GC[2];
                 const float x45 = gb0 ? GC[5] : GC[4], x67 = gb0 ? GC[7] : GC[6];
                 const float y0 = gb1 ? x23 : x01, y1 = gb1 ? x67 : x45;
                 const float ge = __builtin_amdgcn_exp2f((gb2 ? y1 : y0) * kLog2e);
                 lds_st(L + C::L_GAM + 4 * (dch + (r & 7)), ge);
-                // every decay wave loads beta and every lane stores it (same value per word)
-                lds_st(bslot(c) + 4 * r, __builtin_bit_cast(float, rb[ph] << 16));
+                // wave 0 stores beta; lane (r, g) writes copy g, so no two lanes share a
+                // word (the readers use copy 0)
+                if (w == 0) lds_st(bslot(c) + 4 * r + 64 * g, __builtin_bit_cast(float, rb[ph] << 16));
 #pragma unroll
                 for (int e = 0; e < C::VG_PER_WAVE; ++e) {
                     const int f = w + NDW * e;
