@@ -96,6 +96,8 @@ def main() -> int:
     ap.add_argument("--segment-len", type=int, default=16384)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--flush", choices=("read", "write"), default="read",
+                    help="how the 1 GiB cache flush before each timed launch touches memory")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the 1 GiB copy used to scale the HBM byte counters")
     args = ap.parse_args()
@@ -122,8 +124,19 @@ def main() -> int:
     T_total = x.total_tokens
     out = torch.empty((T_total, w.H, w.dv), dtype=x.q.dtype, device="cuda")
     Sf = torch.empty((len(w.lengths), w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
-    flush = None if args.no_flush else torch.empty(256 << 20, dtype=torch.float32,
-                                                   device="cuda")  # 1 GiB
+    # Cache flush before every timed launch: reading a 1 GiB buffer evicts the inputs from
+    # L2 and the MALL and leaves only clean lines; writing it (--flush write) also leaves up
+    # to the MALL's size of dirty lines, whose write-back then runs inside the timed launch.
+    flush = None
+    if not args.no_flush:
+        flush = torch.ones(256 << 20, dtype=torch.float32, device="cuda")  # 1 GiB
+        flush_out = torch.empty((), dtype=torch.float32, device="cuda")
+
+    def do_flush():
+        if args.flush == "write":
+            flush.zero_()
+        else:
+            torch.sum(flush, dim=0, out=flush_out)
 
     def step():
         kda.chunk_prefill(x.q, x.k, x.v, x.log_alpha, x.beta, x.gate, cu_seqlens=x.cu_seqlens,
@@ -140,7 +153,7 @@ def main() -> int:
     wall0 = time.perf_counter()
     for i in range(args.steps):
         if flush is not None:
-            flush.zero_()
+            do_flush()
         starts[i].record(stream)
         step()
         ends[i].record(stream)
@@ -164,6 +177,7 @@ def main() -> int:
         "ms_per_step": ms,
         "ms_per_step_median": float(np.median(times_ms)),
         "wall_s_timed_region_incl_cache_flush": wall,
+        "cache_flush": None if flush is None else f"1 GiB {args.flush} before each launch",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -262,7 +262,9 @@ struct BArgs {
     int32_t order[kMaxOrdered];
 };
 
-template <int DK, int DV, int NCB>
+// CK: the variant that also writes state snapshots (its store addresses stay out of the
+// plain kernel's registers)
+template <int DK, int DV, int NCB, bool CK>
 __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(const BArgs a) {
     typedef Cfg<DK, NCB> C;
     constexpr int KB = C::KB, KP = C::KP, NV = C::NV;
@@ -603,7 +605,7 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
         // snapshots: the state after every ck_chunks-th chunk (when that chunk is full) goes
         // to slot tbeg / m + j - 1 for the j-th snapshot, m = 16 ck_chunks tokens
         int ck_left = a.ck_chunks;
-        int64_t ck_slot = a.ck ? tbeg / (16 * (int64_t)a.ck_chunks) : 0;
+        int64_t ck_slot = CK ? tbeg / (16 * (int64_t)a.ck_chunks) : 0;
         for (int it = -3; it < it_end; ++it) {
             const int c = it;  // state step of chunk c
             if (c >= 0 && c < nch) {
@@ -647,7 +649,7 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
                     S[b] = mfma32(kk, uu, S[b]);
                     S[b] = mfma32(kk, ul0, S[b]);
                 }
-                if (a.ck && --ck_left == 0) {
+                if (CK && --ck_left == 0) {
                     ck_left = a.ck_chunks;
                     if (16 * (int64_t)(c + 1) <= len) {
                         float* dst = a.ck + (ck_slot * H + h) * DK * DV;
@@ -679,7 +681,7 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
     }
 }
 
-template <int DK, int DV, int NCB>
+template <int DK, int DV, int NCB, bool CK>
 hipError_t launch_bf16(const PrefillArgs& p, hipStream_t st) {
     typedef Cfg<DK, NCB> C;
     static_assert(C::LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -697,14 +699,19 @@ hipError_t launch_bf16(const PrefillArgs& p, hipStream_t st) {
     if (a.num_groups == 0) return hipSuccess;
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)prefill_bf16_kernel<DK, DV, NCB>,
+        hipError_t e = hipFuncSetAttribute((const void*)prefill_bf16_kernel<DK, DV, NCB, CK>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL((prefill_bf16_kernel<DK, DV, NCB>), dim3((unsigned)blocks), dim3(C::THREADS),
+    hipLaunchKernelGGL((prefill_bf16_kernel<DK, DV, NCB, CK>), dim3((unsigned)blocks), dim3(C::THREADS),
                        C::LDS_BYTES, st, a);
     return hipGetLastError();
+}
+
+template <int DK, int DV, int NCB>
+hipError_t launch_ck(const PrefillArgs& p, hipStream_t st) {
+    return p.checkpoints ? launch_bf16<DK, DV, NCB, true>(p, st) : launch_bf16<DK, DV, NCB, false>(p, st);
 }
 
 }  // namespace
@@ -719,10 +726,10 @@ bool prefill_bf16_supports(int dk, int dv, int nv) {
 hipError_t launch_prefill_bf16(const PrefillArgs& p, hipStream_t st) {
 #define KDA_NV_CASES(DK, DV)                                          \
     switch (p.nv) {                                                   \
-        case 16: return launch_bf16<DK, DV, 1>(p, st);                \
-        case 32: return launch_bf16<DK, DV, 2>(p, st);                \
-        case 64: if constexpr (DV >= 64) return launch_bf16<DK, DV, 4>(p, st); break; \
-        case 128: if constexpr (DK == 64 && DV >= 128) return launch_bf16<DK, DV, 8>(p, st); break; \
+        case 16: return launch_ck<DK, DV, 1>(p, st);                  \
+        case 32: return launch_ck<DK, DV, 2>(p, st);                  \
+        case 64: if constexpr (DV >= 64) return launch_ck<DK, DV, 4>(p, st); break; \
+        case 128: if constexpr (DK == 64 && DV >= 128) return launch_ck<DK, DV, 8>(p, st); break; \
     }                                                                 \
     return hipErrorInvalidValue;
     if (p.dk == 128 && p.dv == 128) { KDA_NV_CASES(128, 128) }
