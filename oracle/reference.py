@@ -146,3 +146,61 @@ def run_packed(fn, q, k, v, log_alpha, beta, gate, cu_seqlens, S0=None, **kw):
             out[a:e, h] = o
             Sf[n, h] = S
     return out, Sf
+
+
+def recurrent_backward(q, k, v, log_alpha, beta, gate, do, dS_T=None, S0=None, floor=-0.3,
+                       scale=1.0):
+    """Gradients of the token recurrence (reverse mode, written out step by step).
+
+    The loss is sum(do * o) + sum(dS_T * S_T).  Forward step t (see recurrent()):
+        a = exp(max(lambda_t, floor)); S' = Diag(a) S_{t-1}; w = S'^T k_t;
+        u = beta_t (v_t - w); S_t = S' + k_t u^T; y = S_t^T (scale q_t); o_t = gate_t * y.
+    Going back through the same steps, with dS the gradient of S_t:
+        dgate = do * y;  dy = do * gate;  dS += (scale q) dy^T;  dq = scale S_t dy
+        dk = dS u;  du = dS^T k;  dbeta = du . (v - w);  dv = beta du;  dw = -beta du
+        dS' = dS + k dw^T;  dk += S' dw
+        da = rowsum(dS' * S_{t-1});  dlambda = da * a * [lambda > floor];  dS = Diag(a) dS'
+    and dS0 is the dS left after the first token.  max(lambda, floor) passes the
+    gradient only where lambda > floor (zero at a tie).
+    Returns a dict with dq, dk, dv, dlog_alpha [T, d], dbeta [T], dgate [T, dv], dS0.
+    """
+    q, k, v, la, beta, g, do, dS_T, S0 = _as64(q, k, v, log_alpha, beta, gate, do, dS_T, S0)
+    T, dk = q.shape
+    dv = v.shape[1]
+    S = np.zeros((dk, dv)) if S0 is None else S0.copy()
+    prev, decay, ws = [], [], []
+    for t in range(T):                       # forward, keeping what the reverse needs
+        a = np.exp(np.maximum(la[t], floor))
+        prev.append(S)
+        Sp = a[:, None] * S
+        w = Sp.T @ k[t]
+        S = Sp + beta[t] * np.outer(k[t], v[t] - w)
+        decay.append(a)
+        ws.append(w)
+    out = {n: np.zeros_like(x) for n, x in (("dq", q), ("dk", k), ("dv", v),
+                                            ("dlog_alpha", la), ("dgate", g))}
+    out["dbeta"] = np.zeros(T)
+    dS = np.zeros((dk, dv)) if dS_T is None else dS_T.copy()
+    for t in range(T - 1, -1, -1):
+        a, w, Sprev = decay[t], ws[t], prev[t]
+        Sp = a[:, None] * Sprev
+        u = beta[t] * (v[t] - w)
+        St = Sp + np.outer(k[t], u)
+        y = St.T @ (scale * q[t])
+        out["dgate"][t] = do[t] * y
+        dy = do[t] * g[t]
+        dS = dS + np.outer(scale * q[t], dy)
+        out["dq"][t] = scale * (St @ dy)
+        dkt = dS @ u
+        du = dS.T @ k[t]
+        out["dbeta"][t] = du @ (v[t] - w)
+        out["dv"][t] = beta[t] * du
+        dw = -beta[t] * du
+        dSp = dS + np.outer(k[t], dw)
+        dkt = dkt + Sp @ dw
+        out["dk"][t] = dkt
+        da = np.sum(dSp * Sprev, axis=1)
+        out["dlog_alpha"][t] = da * a * (la[t] > floor)
+        dS = a[:, None] * dSp
+    out["dS0"] = dS
+    return out
