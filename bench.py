@@ -91,6 +91,7 @@ def main() -> int:
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--spec-rounds", type=int, default=50)
     ap.add_argument("--spec-draft", type=int, default=4)
+    ap.add_argument("--backward-steps", type=int, default=3)
     ap.add_argument("--segmented", action=argparse.BooleanOptionalAction, default=True,
                     help="also time the segmented prefill on the few-head long workload")
     ap.add_argument("--segment-len", type=int, default=16384)
@@ -276,6 +277,42 @@ def main() -> int:
             "draft_tokens_per_s": N * K / ((vus + cus) * 1e-6),
         }
         del sx, state, sout
+        torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------------- backward
+    if args.backward_steps > 0:
+        g = torch.Generator().manual_seed(1)
+        dout = torch.randn(x.v.shape, generator=g).to(x.v.dtype).cuda()
+        bws = None
+
+        def bstep():
+            kda.prefill_backward(x.q, x.k, x.v, x.log_alpha, x.beta, x.gate, dout,
+                                 cu_seqlens=x.cu_seqlens, cu_seqlens_host=x.cu_seqlens_host,
+                                 initial_state=x.initial_state, workspace=bws)
+
+        lib = kda.load_library()
+        import ctypes
+        from linear_attention_sequence_chunked_amd import _lib as klib
+        pp = klib.params(klib.KDA_DTYPE_BF16 if w.dtype == "bf16" else klib.KDA_DTYPE_F32,
+                         w.H, w.dk, w.dv)
+        cu_h = (ctypes.c_int32 * len(x.cu_seqlens_host))(*x.cu_seqlens_host)
+        need = lib.kda_prefill_backward_workspace(ctypes.byref(pp), cu_h, len(w.lengths))
+        bws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        bstep()
+        torch.cuda.synchronize()
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b0.record(stream)
+        for _ in range(args.backward_steps):
+            bstep()
+        b1.record(stream)
+        torch.cuda.synchronize()
+        bms = b0.elapsed_time(b1) / args.backward_steps
+        result["backward"] = {
+            "workload": w.name, "steps": args.backward_steps, "ms_per_step": bms,
+            "tokens_per_s": T_total / (bms * 1e-3), "vs_forward": bms / ms,
+            "note": "fp32 token-recurrence walk, one workgroup per (sequence, head)",
+        }
+        del bws, dout
         torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- segmented prefill

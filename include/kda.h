@@ -171,6 +171,45 @@ int64_t kda_prefill_segmented_workspace(const kda_params* params,
                                         int32_t segment_len);
 
 /*
+ * kda_prefill_backward -- gradients of kda_chunk_prefill (the training form), fp32.
+ *
+ * Given the forward's inputs and the gradients of its outputs, writes the gradient of the
+ * loss with respect to every input.  The loss is the one whose gradients are d_out (of o)
+ * and d_final_state (of the final state, NULL = zero).  max(log_alpha, floor) passes the
+ * gradient only where log_alpha > floor.  Sources: the operator (see the top of this file)
+ * and its training-time use (digest of "Kimi K3: Open Frontier Intelligence", section
+ * "基础设施").
+ *
+ *   q, k, v, log_alpha, beta, gate, cu_seqlens, cu_seqlens_host, num_seqs, initial_state:
+ *                     as for kda_chunk_prefill (inputs of the forward)
+ *   d_out           : [T_total, H, dv], params->dtype
+ *   d_final_state   : fp32 [num_seqs, H, dk, dv] or NULL
+ *   dq, dk, dlog_alpha : fp32 [T_total, H, dk];  dv, dgate : fp32 [T_total, H, dv];
+ *   dbeta           : fp32 [T_total, H];  d_initial_state : fp32 [num_seqs, H, dk, dv]
+ *                     or NULL.  No output may overlap another argument.
+ *   workspace       : device memory of at least kda_prefill_backward_workspace(...) bytes,
+ *                     256-byte aligned, overlapping no other argument; holds the recomputed
+ *                     forward states (the state entering every 16-token chunk, and 16 token
+ *                     states per (sequence, head)).
+ * The gradients are computed in fp32 by walking the token recurrence backwards (one
+ * workgroup per (sequence, head)): a correctness-first path, several times slower than
+ * the forward.
+ */
+kda_status kda_prefill_backward(const kda_params* params, const void* q, const void* k,
+                                const void* v, const void* log_alpha, const void* beta,
+                                const void* gate, const int32_t* cu_seqlens,
+                                const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                const float* initial_state, const void* d_out,
+                                const float* d_final_state, float* dq, float* dk, float* dv,
+                                float* dlog_alpha, float* dbeta, float* dgate,
+                                float* d_initial_state, void* workspace,
+                                int64_t workspace_bytes, void* stream);
+
+/* Bytes of workspace kda_prefill_backward needs, or -1 if the arguments are invalid. */
+int64_t kda_prefill_backward_workspace(const kda_params* params,
+                                       const int32_t* cu_seqlens_host, int32_t num_seqs);
+
+/*
  * kda_decode_step -- one token per sequence, state updated in place.
  *
  *   q, k, log_alpha : [num_seqs, H, dk];  v, gate, out : [num_seqs, H, dv];

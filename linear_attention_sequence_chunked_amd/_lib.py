@@ -11,7 +11,8 @@ KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP = 0, 1, 2, 3
 KDA_DTYPE_BF16, KDA_DTYPE_F32 = 0, 1
 EXPORTED = ("kda_chunk_prefill", "kda_chunk_prefill_checkpointed", "kda_decode_step",
             "kda_spec_verify", "kda_spec_commit", "kda_chunk_prefill_segmented",
-            "kda_prefill_segmented_workspace", "kda_status_string", "kda_last_error",
+            "kda_prefill_segmented_workspace", "kda_prefill_backward",
+            "kda_prefill_backward_workspace", "kda_status_string", "kda_last_error",
             "kda_abi_version")
 
 
@@ -62,6 +63,13 @@ def load() -> ctypes.CDLL:
     lib.kda_prefill_segmented_workspace.argtypes = [ctypes.POINTER(KdaParams),
                                                     ctypes.POINTER(I32), I32, I32]
     lib.kda_prefill_segmented_workspace.restype = ctypes.c_int64
+    lib.kda_prefill_backward.argtypes = [ctypes.POINTER(KdaParams), P, P, P, P, P, P, P,
+                                         ctypes.POINTER(I32), I32, P, P, P, P, P, P, P, P, P,
+                                         P, P, ctypes.c_int64, P]
+    lib.kda_prefill_backward.restype = ctypes.c_int
+    lib.kda_prefill_backward_workspace.argtypes = [ctypes.POINTER(KdaParams),
+                                                   ctypes.POINTER(I32), I32]
+    lib.kda_prefill_backward_workspace.restype = ctypes.c_int64
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_last_error.argtypes = []

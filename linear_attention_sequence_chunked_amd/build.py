@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkda.so")
 SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_prefill.hip", "kda_prefill_bf16.hip",
-           "kda_spec.hip", "kda_segment.hip"]
+           "kda_spec.hip", "kda_segment.hip", "kda_backward.hip"]
 HEADERS = ["kda_device.h", "kda_launch.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -534,3 +534,106 @@ kda_status kda_chunk_prefill_segmented(const kda_params* params, const void* q,
 }
 
 }  // extern "C"
+
+namespace {
+
+kda_status bwd_size(const kda_params* params, const int32_t* cu, int32_t N, uint64_t& bytes,
+                    uint64_t& tok_off) {
+    kda_status st = check_params(params);
+    if (st != KDA_OK) return st;
+    if (N < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "num_seqs %d < 1", N);
+    if (!cu) return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens_host is NULL");
+    if (cu[0] != 0) return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens_host[0] = %d, must be 0", cu[0]);
+    for (int32_t n = 0; n < N; ++n)
+        if (cu[n + 1] < cu[n])
+            return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens_host decreases at index %d", n + 1);
+    const uint64_t H = params->num_heads, ss = (uint64_t)params->dk * params->dv;
+    // chunk entry states at slots cu[n]/16 + n + c (at most T_total/16 + N of them), then
+    // 16 token states per (sequence, head)
+    const uint64_t chunk_slots = (uint64_t)cu[N] / 16 + N;
+    tok_off = chunk_slots * H * ss;
+    bytes = 4 * (tok_off + (uint64_t)N * H * 16 * ss);
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t kda_prefill_backward_workspace(const kda_params* params,
+                                       const int32_t* cu_seqlens_host, int32_t num_seqs) {
+    uint64_t bytes = 0, tok = 0;
+    if (bwd_size(params, cu_seqlens_host, num_seqs, bytes, tok) != KDA_OK) return -1;
+    ok();
+    return (int64_t)bytes;
+}
+
+kda_status kda_prefill_backward(const kda_params* params, const void* q, const void* k,
+                                const void* v, const void* log_alpha, const void* beta,
+                                const void* gate, const int32_t* cu_seqlens,
+                                const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                const float* initial_state, const void* d_out,
+                                const float* d_final_state, float* dq, float* dk, float* dv,
+                                float* dlog_alpha, float* dbeta, float* dgate,
+                                float* d_initial_state, void* workspace,
+                                int64_t workspace_bytes, void* stream) {
+    uint64_t need = 0, tok_off = 0;
+    kda_status st = bwd_size(params, cu_seqlens_host, num_seqs, need, tok_off);
+    if (st != KDA_OK) return st;
+    const kda_params& p = *params;
+    const int64_t T = cu_seqlens_host[num_seqs];
+    const int64_t H = p.num_heads;
+    const size_t es = p.dtype == KDA_DTYPE_BF16 ? 2 : 4;
+    if ((st = check_ptr("cu_seqlens", cu_seqlens, 4)) != KDA_OK) return st;
+    if (T > 0) {
+        const void* in[] = {q, k, v, log_alpha, gate, d_out};
+        const char* nin[] = {"q", "k", "v", "log_alpha", "gate", "d_out"};
+        for (int i = 0; i < 6; ++i)
+            if ((st = check_ptr(nin[i], in[i], 16)) != KDA_OK) return st;
+        if ((st = check_ptr("beta", beta, es)) != KDA_OK) return st;
+        const void* outp[] = {dq, dk, dv, dlog_alpha, dgate};
+        const char* nout[] = {"dq", "dk", "dv", "dlog_alpha", "dgate"};
+        for (int i = 0; i < 5; ++i)
+            if ((st = check_ptr(nout[i], outp[i], 16)) != KDA_OK) return st;
+        if ((st = check_ptr("dbeta", dbeta, 4)) != KDA_OK) return st;
+    }
+    if (initial_state && (st = check_ptr("initial_state", initial_state, 16)) != KDA_OK) return st;
+    if (d_final_state && (st = check_ptr("d_final_state", d_final_state, 16)) != KDA_OK) return st;
+    if (d_initial_state && (st = check_ptr("d_initial_state", d_initial_state, 16)) != KDA_OK) return st;
+    if ((st = check_ptr("workspace", workspace, 256)) != KDA_OK) return st;
+    if (workspace_bytes < (int64_t)need)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "workspace_bytes %lld < %llu needed",
+                    (long long)workspace_bytes, (unsigned long long)need);
+    const uint64_t nk = (uint64_t)T * H * p.dk, nv = (uint64_t)T * H * p.dv;
+    const uint64_t ns = (uint64_t)num_seqs * H * p.dk * p.dv * 4;
+    const Range ins[] = {range("q", q, nk * es), range("k", k, nk * es), range("v", v, nv * es),
+                         range("log_alpha", log_alpha, nk * es), range("beta", beta, T * H * es),
+                         range("gate", gate, nv * es), range("initial_state", initial_state, ns),
+                         range("d_out", d_out, nv * es), range("d_final_state", d_final_state, ns)};
+    const Range outs[] = {range("dq", dq, nk * 4), range("dk", dk, nk * 4), range("dv", dv, nv * 4),
+                          range("dlog_alpha", dlog_alpha, nk * 4), range("dbeta", dbeta, T * H * 4),
+                          range("dgate", dgate, nv * 4), range("d_initial_state", d_initial_state, ns),
+                          range("workspace", workspace, need)};
+    for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+        for (const Range& in : ins)
+            if (overlaps(outs[i], in))
+                return fail(KDA_ERR_INVALID_ARGUMENT, "%s overlaps %s", outs[i].name, in.name);
+        for (size_t j = 0; j < i; ++j)
+            if (overlaps(outs[i], outs[j]))
+                return fail(KDA_ERR_INVALID_ARGUMENT, "%s overlaps %s", outs[i].name, outs[j].name);
+    }
+    kda::BackwardArgs a;
+    a.dtype = p.dtype; a.H = p.num_heads; a.dk = p.dk; a.dv = p.dv;
+    a.floor_ = p.log_alpha_floor; a.scale = p.scale; a.num_seqs = num_seqs;
+    a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta; a.gate = gate;
+    a.d_out = d_out; a.cu_seqlens = cu_seqlens; a.initial_state = initial_state;
+    a.d_final_state = d_final_state; a.dq = dq; a.dk_ = dk; a.dv_ = dv; a.dlog_alpha = dlog_alpha;
+    a.dbeta = dbeta; a.dgate = dgate; a.d_initial_state = d_initial_state;
+    a.workspace = static_cast<float*>(workspace); a.token_state_offset = (int64_t)tok_off;
+    const hipError_t e = kda::launch_backward(a, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(KDA_ERR_HIP, "kda_prefill_backward launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

@@ -73,6 +73,22 @@ struct CombineArgs {
 hipError_t launch_table(const TableArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, int num_seqs, int dk, int dv, hipStream_t stream);
 
+// Backward of the prefill (kda_backward.hip).
+struct BackwardArgs {
+    int dtype, H, dk, dv;
+    float floor_, scale;
+    int num_seqs;
+    const void *q, *k, *v, *log_alpha, *beta, *gate, *d_out;
+    const int32_t* cu_seqlens;          // device
+    const float* initial_state;         // may be null
+    const float* d_final_state;         // may be null
+    float *dq, *dk_, *dv_, *dlog_alpha, *dbeta, *dgate;
+    float* d_initial_state;             // may be null
+    float* workspace;                   // chunk entry states, then per-pair token states
+    int64_t token_state_offset;         // floats
+};
+hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream);
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_spec(const SpecArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);

@@ -268,3 +268,78 @@ def chunk_prefill_segmented(q, k, v, log_alpha, beta, gate, cu_seqlens, segment_
                                          _stream())
     _lib.check(st)
     return out, final_state
+
+
+def prefill_backward(q, k, v, log_alpha, beta, gate, d_out, cu_seqlens=None,
+                     initial_state=None, d_final_state=None, log_alpha_floor: float = -0.3,
+                     scale: float = 1.0, cu_seqlens_host: Optional[Sequence[int]] = None,
+                     workspace: Optional[torch.Tensor] = None):
+    """Gradients of chunk_prefill (fp32).  Inputs as for chunk_prefill ([B, T, H, d] or
+    packed [T_total, H, d] with cu_seqlens), d_out shaped like o, d_final_state fp32
+    [N, H, dk, dv] or None.  Returns a dict with dq, dk, dv, dlog_alpha, dbeta, dgate
+    (fp32, shaped like the inputs) and d_initial_state (fp32 [N, H, dk, dv])."""
+    dt = q.dtype
+    if dt not in _DT:
+        raise ValueError(f"unsupported dtype {dt}")
+    shapes = {n: t.shape for n, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha),
+                                      ("beta", beta), ("gate", gate))}
+    if q.dim() == 4:
+        B, T, H, dk = q.shape
+        if cu_seqlens is not None:
+            raise ValueError("cu_seqlens is for packed [T_total, H, d] inputs")
+        cu_host = [i * T for i in range(B + 1)]
+        flat = lambda x: x.reshape(B * T, *x.shape[2:])
+        q, k, v, log_alpha, beta, gate, d_out = (flat(x) for x in
+                                                 (q, k, v, log_alpha, beta, gate, d_out))
+    else:
+        if cu_seqlens is None:
+            raise ValueError("packed [T_total, H, d] inputs need cu_seqlens")
+        if cu_seqlens_host is not None:
+            cu_host = [int(x) for x in cu_seqlens_host]
+        elif isinstance(cu_seqlens, torch.Tensor):
+            cu_host = [int(x) for x in cu_seqlens.tolist()]
+        else:
+            cu_host = [int(x) for x in cu_seqlens]
+    Ttot, H, dk = q.shape
+    dv = v.shape[-1]
+    N = len(cu_host) - 1
+    for name, t, shp in (("q", q, (Ttot, H, dk)), ("k", k, (Ttot, H, dk)),
+                         ("v", v, (Ttot, H, dv)), ("log_alpha", log_alpha, (Ttot, H, dk)),
+                         ("beta", beta, (Ttot, H)), ("gate", gate, (Ttot, H, dv)),
+                         ("d_out", d_out, (Ttot, H, dv))):
+        _check_dev(name, t, dt)
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shp}")
+    for name, t in (("initial_state", initial_state), ("d_final_state", d_final_state)):
+        if t is not None:
+            _check_dev(name, t, torch.float32)
+            if tuple(t.shape) != (N, H, dk, dv):
+                raise ValueError(f"{name} must be [N, H, dk, dv]")
+    dev = q.device
+    if isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.is_cuda:
+        cu_dev = cu_seqlens.to(torch.int32).contiguous()
+    else:
+        cu_dev = torch.tensor(cu_host, dtype=torch.int32, device=dev)
+    cu_h = (ctypes.c_int32 * len(cu_host))(*cu_host)
+    p = _lib.params(_DT[dt], H, dk, dv, log_alpha_floor, scale)
+    lib = _lib.load()
+    need = lib.kda_prefill_backward_workspace(ctypes.byref(p), cu_h, N)
+    if need < 0:
+        raise _lib.KdaError(_lib.KDA_ERR_INVALID_ARGUMENT, lib.kda_last_error().decode())
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    f32 = lambda shp: torch.empty(shp, dtype=torch.float32, device=dev)
+    g = dict(dq=f32((Ttot, H, dk)), dk=f32((Ttot, H, dk)), dv=f32((Ttot, H, dv)),
+             dlog_alpha=f32((Ttot, H, dk)), dbeta=f32((Ttot, H)), dgate=f32((Ttot, H, dv)),
+             d_initial_state=f32((N, H, dk, dv)))
+    st = lib.kda_prefill_backward(
+        ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(gate),
+        _ptr(cu_dev), cu_h, N, _ptr(initial_state), _ptr(d_out), _ptr(d_final_state),
+        _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dlog_alpha"]), _ptr(g["dbeta"]),
+        _ptr(g["dgate"]), _ptr(g["d_initial_state"]), _ptr(workspace), workspace.numel(),
+        _stream())
+    _lib.check(st)
+    for name, key in (("q", "dq"), ("k", "dk"), ("v", "dv"), ("log_alpha", "dlog_alpha"),
+                      ("beta", "dbeta"), ("gate", "dgate")):
+        g[key] = g[key].reshape(shapes[name])
+    return g

@@ -267,3 +267,43 @@ def test_segmented_rejects(kw, msg):
     st, err = prefill_seg(**kw)
     assert st == INV, err
     assert msg in err, err
+
+
+def test_backward_workspace_size():
+    """cu = (0, 40, 40, 100), H = 2, d = 64: chunk entry states at slots cu[n]/16 + n + c,
+    i.e. at most 100//16 + 3 = 9 slots per head, then 16 token states per (sequence, head)."""
+    lib = _lib.load()
+    p = _lib.params(_lib.KDA_DTYPE_BF16, 2, 64, 64)
+    ss = 64 * 64 * 4
+    assert lib.kda_prefill_backward_workspace(ctypes.byref(p), cu(0, 40, 40, 100), 3) == \
+        (9 * 2 + 3 * 2 * 16) * ss
+    assert lib.kda_prefill_backward_workspace(ctypes.byref(p), cu(0, 40, 30), 2) == -1
+
+
+def backward(dq=A + 0x100000, dk=A + 0x110000, dv=A + 0x120000, dla=A + 0x130000,
+             dbeta=A + 0x140000, dgate=A + 0x150000, ds0=None, ws=A + 0x400000,
+             ws_bytes=1 << 24, q=A, d_out=A + 0x80000):
+    lib = _lib.load()
+    p = _lib.params(_lib.KDA_DTYPE_BF16, 2, 64, 64)
+    st = lib.kda_prefill_backward(ctypes.byref(p), q, A + 0x10000, A + 0x20000, A + 0x30000,
+                                  A + 0x40000, A + 0x50000, A + 0x60000, cu(0, 3, 5), 2, None,
+                                  d_out, None, dq, dk, dv, dla, dbeta, dgate, ds0, ws, ws_bytes,
+                                  None)
+    return st, lib.kda_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(dq=None), "dq is NULL"),
+    (dict(dgate=A + 0x150008), "dgate is not 16-byte aligned"),
+    (dict(d_out=None), "d_out is NULL"),
+    (dict(ws=None), "workspace is NULL"),
+    (dict(ws_bytes=100), "workspace_bytes 100"),
+    (dict(dq=A + 0x10000), "dq overlaps k"),
+    (dict(dk=A + 0x100000 + 64), "dk overlaps dq"),
+    (dict(ws=A + 0x100000), "workspace overlaps dq"),
+    (dict(ds0=A + 0x20000), "d_initial_state overlaps v"),
+])
+def test_backward_rejects(kw, msg):
+    st, err = backward(**kw)
+    assert st == INV, err
+    assert msg in err, err
