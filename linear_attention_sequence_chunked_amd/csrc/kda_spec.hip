@@ -18,6 +18,8 @@
 // inputs are staged in LDS before the first step; each step reduces its column sums
 // inside the wave with cross-lane adds and across the four waves through an LDS buffer
 // that alternates between steps, so a step costs one barrier.
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -36,7 +38,9 @@ struct SArgs {
     float floor_, scale;
 };
 
-template <typename T, int DK, int DV, bool VERIFY>
+// KM: LDS capacity in draft tokens (K <= KM); a smaller capacity lets more workgroups
+// share a compute unit, which this memory-bound kernel needs.
+template <typename T, int DK, int DV, bool VERIFY, int KM>
 __global__ __launch_bounds__(kSpecThreads) void spec_kernel(const SArgs<T> a) {
     constexpr int COLG = DV / 4;                 // float4 column groups per row
     constexpr int ROWG = kSpecThreads / COLG;    // row groups
@@ -44,9 +48,9 @@ __global__ __launch_bounds__(kSpecThreads) void spec_kernel(const SArgs<T> a) {
     constexpr int WAVES = kSpecThreads / 64;
     static_assert(DK % ROWG == 0 && 64 % COLG == 0, "shape");
 
-    __shared__ float s_k[kMaxDraft][DK], s_q[VERIFY ? kMaxDraft : 1][DK], s_a[kMaxDraft][DK];
-    __shared__ float s_v[kMaxDraft][DV], s_g[VERIFY ? kMaxDraft : 1][DV];
-    __shared__ float s_beta[kMaxDraft], s_kq[kMaxDraft];
+    __shared__ float s_k[KM][DK], s_q[VERIFY ? KM : 1][DK], s_a[KM][DK];
+    __shared__ float s_v[KM][DV], s_g[VERIFY ? KM : 1][DV];
+    __shared__ float s_beta[KM], s_kq[KM];
     __shared__ f32x4 s_red[2][WAVES][COLG][VERIFY ? 2 : 1];
 
     const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
@@ -146,8 +150,8 @@ __global__ __launch_bounds__(kSpecThreads) void spec_kernel(const SArgs<T> a) {
     }
     if constexpr (!VERIFY) {
 #pragma unroll
-        for (int i = 0; i < RPT; ++i)
-            *reinterpret_cast<f32x4*>(S + (rg + ROWG * i) * DV + 4 * cg) = s[i];
+        for (int i = 0; i < RPT; ++i)  // streamed past the caches, as in the decode step
+            __builtin_nontemporal_store(s[i], reinterpret_cast<f32x4*>(S + (rg + ROWG * i) * DV + 4 * cg));
     }
 }
 
@@ -160,12 +164,18 @@ hipError_t launch_typed(const SpecArgs& p, hipStream_t st) {
     a.H = p.H; a.K = p.num_draft; a.floor_ = p.floor_; a.scale = p.scale;
     const int64_t pairs = (int64_t)p.num_seqs * p.H;
     if (pairs == 0) return hipSuccess;
-    if (p.verify)
-        hipLaunchKernelGGL((spec_kernel<T, DK, DV, true>), dim3((unsigned)pairs),
-                           dim3(kSpecThreads), 0, st, a);
-    else
-        hipLaunchKernelGGL((spec_kernel<T, DK, DV, false>), dim3((unsigned)pairs),
-                           dim3(kSpecThreads), 0, st, a);
+    auto go = [&](auto KMC) {
+        constexpr int KM = decltype(KMC)::value;
+        if (p.verify)
+            hipLaunchKernelGGL((spec_kernel<T, DK, DV, true, KM>), dim3((unsigned)pairs),
+                               dim3(kSpecThreads), 0, st, a);
+        else
+            hipLaunchKernelGGL((spec_kernel<T, DK, DV, false, KM>), dim3((unsigned)pairs),
+                               dim3(kSpecThreads), 0, st, a);
+    };
+    if (a.K <= 4) go(std::integral_constant<int, 4>{});
+    else if (a.K <= 8) go(std::integral_constant<int, 8>{});
+    else go(std::integral_constant<int, kMaxDraft>{});
     return hipGetLastError();
 }
 
