@@ -188,12 +188,13 @@ int64_t kda_prefill_segmented_workspace(const kda_params* params,
  *   dbeta           : fp32 [T_total, H];  d_initial_state : fp32 [num_seqs, H, dk, dv]
  *                     or NULL.  No output may overlap another argument.
  *   workspace       : device memory of at least kda_prefill_backward_workspace(...) bytes,
- *                     256-byte aligned, overlapping no other argument; holds the recomputed
- *                     forward states (the state entering every 16-token chunk, and 16 token
- *                     states per (sequence, head)).
- * The gradients are computed in fp32 by walking the token recurrence backwards (one
- * workgroup per (sequence, head)): a correctness-first path, several times slower than
- * the forward.
+ *                     256-byte aligned, overlapping no other argument; receives the state
+ *                     entering every 16-token chunk and the gradient of the state leaving
+ *                     it (fp32, dk x dv each per chunk and head).
+ * The gradients are computed in fp32 with the 16-token chunk algebra of the forward: one
+ * launch walks every sequence forwards (the chunk-entering states) and backwards (the
+ * state gradient) side by side, a second forms each chunk's input gradients from those,
+ * all chunks in parallel.
  */
 kda_status kda_prefill_backward(const kda_params* params, const void* q, const void* k,
                                 const void* v, const void* log_alpha, const void* beta,

@@ -538,7 +538,7 @@ kda_status kda_chunk_prefill_segmented(const kda_params* params, const void* q,
 namespace {
 
 kda_status bwd_size(const kda_params* params, const int32_t* cu, int32_t N, uint64_t& bytes,
-                    uint64_t& tok_off) {
+                    uint64_t& grad_off) {
     kda_status st = check_params(params);
     if (st != KDA_OK) return st;
     if (N < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "num_seqs %d < 1", N);
@@ -548,11 +548,11 @@ kda_status bwd_size(const kda_params* params, const int32_t* cu, int32_t N, uint
         if (cu[n + 1] < cu[n])
             return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens_host decreases at index %d", n + 1);
     const uint64_t H = params->num_heads, ss = (uint64_t)params->dk * params->dv;
-    // chunk entry states at slots cu[n]/16 + n + c (at most T_total/16 + N of them), then
-    // 16 token states per (sequence, head)
-    const uint64_t chunk_slots = (uint64_t)cu[N] / 16 + N;
-    tok_off = chunk_slots * H * ss;
-    bytes = 4 * (tok_off + (uint64_t)N * H * 16 * ss);
+    // the state entering chunk c of sequence n at slot cu[n]/16 + n + c (at most
+    // T_total/16 + N slots), then the gradient leaving the chunk at the same slot
+    const uint64_t slots = (uint64_t)cu[N] / 16 + N;
+    grad_off = slots * H * ss;
+    bytes = 4 * 2 * grad_off;
     return KDA_OK;
 }
 
@@ -562,8 +562,8 @@ extern "C" {
 
 int64_t kda_prefill_backward_workspace(const kda_params* params,
                                        const int32_t* cu_seqlens_host, int32_t num_seqs) {
-    uint64_t bytes = 0, tok = 0;
-    if (bwd_size(params, cu_seqlens_host, num_seqs, bytes, tok) != KDA_OK) return -1;
+    uint64_t bytes = 0, grad = 0;
+    if (bwd_size(params, cu_seqlens_host, num_seqs, bytes, grad) != KDA_OK) return -1;
     ok();
     return (int64_t)bytes;
 }
@@ -577,8 +577,8 @@ kda_status kda_prefill_backward(const kda_params* params, const void* q, const v
                                 float* dlog_alpha, float* dbeta, float* dgate,
                                 float* d_initial_state, void* workspace,
                                 int64_t workspace_bytes, void* stream) {
-    uint64_t need = 0, tok_off = 0;
-    kda_status st = bwd_size(params, cu_seqlens_host, num_seqs, need, tok_off);
+    uint64_t need = 0, grad_off = 0;
+    kda_status st = bwd_size(params, cu_seqlens_host, num_seqs, need, grad_off);
     if (st != KDA_OK) return st;
     const kda_params& p = *params;
     const int64_t T = cu_seqlens_host[num_seqs];
@@ -629,7 +629,10 @@ kda_status kda_prefill_backward(const kda_params* params, const void* q, const v
     a.d_out = d_out; a.cu_seqlens = cu_seqlens; a.initial_state = initial_state;
     a.d_final_state = d_final_state; a.dq = dq; a.dk_ = dk; a.dv_ = dv; a.dlog_alpha = dlog_alpha;
     a.dbeta = dbeta; a.dgate = dgate; a.d_initial_state = d_initial_state;
-    a.workspace = static_cast<float*>(workspace); a.token_state_offset = (int64_t)tok_off;
+    a.workspace = static_cast<float*>(workspace); a.grad_offset = (int64_t)grad_off;
+    a.T_total = T;
+    // value slices of the two sequential passes: enough workgroups for every compute unit
+    a.nv = std::min(64, kda::prefill_pick_nv(p.dv, (int64_t)num_seqs * H, 0, device_cu_count()));
     const hipError_t e = kda::launch_backward(a, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return fail(KDA_ERR_HIP, "kda_prefill_backward launch: %s", hipGetErrorString(e));

@@ -1,313 +1,600 @@
 // kda_backward.hip -- gradients of the KDA prefill (training form), gfx950.
 //
-// Forward token step (the operator, per sequence and head):
-//   a = exp(max(lambda, floor));  S' = Diag(a) S;  w = S'^T k;  u = beta (v - w);
-//   S <- S' + k u^T;  y = S^T (scale q);  o = gate * y
-// Reverse step, with dS the gradient of the state after the token (carried backwards):
-//   dgate = do * y;  dy = do * gate;  dS += (scale q) dy^T;  dq = scale S dy
-//   du = dS^T k;  dbeta = du . (v - w);  dv = beta du;  dw = -beta du
-//   dk = dS u + S' dw;  dS' = dS + k dw^T
-//   dlambda = rowsum(dS' * S_prev) * a * [lambda > floor];  dS <- Diag(a) dS'
-// and the gradient of the initial state is the dS left after the first token.
-// (Operator: "Kimi-K3 为什么这么强？" §① part ②; "Kimi K3 深度拆解" 突破一; digest of
-// "Kimi K3: Open Frontier Intelligence", KDA section; the training-time use of the same
-// operator: digest, section "基础设施".)
+// The operator (per sequence and head, token by token):
+//   a = exp(max(lambda, floor));  S' = Diag(a) S;  u = beta (v - S'^T k);  S <- S' + k u^T;
+//   y = S^T (scale q);  o = gate * y
+// ("Kimi-K3 为什么这么强？" §① part ②; "Kimi K3 深度拆解" 突破一; digest of "Kimi K3: Open
+// Frontier Intelligence", KDA section, and section "基础设施" for its use in training.)
 //
-// One workgroup per (sequence, head) walks the recurrence in fp32:
-//   1. forward over the sequence, storing the state that enters every 16-token chunk;
-//   2. for each chunk from the last: recompute the chunk's token states from its entry
-//      state (stored per token), then step backwards through its tokens.
-// Wave w owns state rows [w DK/4, (w+1) DK/4), lane l owns columns l (and l + 64), so a
-// sum over rows (S^T x) is a sum inside the thread plus one cross-wave LDS add, and a sum
-// over columns (S x) is a reduction across the 64 lanes by recursive halving.
+// Chunk form (16 tokens; G = inclusive cumsum of max(lambda, floor) over the chunk's rows,
+// G_C its last row; padding rows past the end of a sequence have zero decay and zero k, q):
+//   Qh = (scale q) e^G,  Kh = k e^G,  Kc = k e^-G,  Kb = k e^(G_C - G),  gamma = e^G_C
+//   A' = strict_lower(Kh Kc^T),  X = (I + Diag(beta) A')^-1,  T = X Diag(beta)
+//   P  = lower_incl_diag(Qh Kc^T)
+//   R  = V - Kh S,  U = T R,  Y = Qh S + P U,  S_C = Diag(gamma) S + Kb^T U
+// Its reverse, given dO and the gradient dS_C of the state leaving the chunk:
+//   dgate = dO * Y,  dY = dO * gate,  dU = P^T dY + Kb dS_C,  dR = T^T dU,  dv = dR
+//   dS (entering)  = Diag(gamma) dS_C + Qh^T dY - Kh^T dR
+//   dT = dU R^T -> dX = dT Diag(beta), dbeta += colsum(X * dT), dA = -X^T dX X^T (strict lower)
+//   dA' = Diag(beta) dA,  dbeta += rowsum(dA * A')
+//   dP = lower_incl_diag(dY U^T)
+//   dQh = dY S^T + dP Kc,  dKh = -dR S^T + dA' Kc,  dKc = dP^T Qh + dA'^T Kh,  dKb = U dS_C^T
+//   dgamma = rowsum(dS_C * S)
+//   dq = scale e^G dQh,  dk = e^G dKh + e^-G dKc + e^(G_C - G) dKb
+//   dG = Qh dQh + Kh dKh - Kc dKc - Kb dKb  (elementwise), plus on the row of G_C:
+//        sum_rows(Kb dKb) + gamma dgamma
+//   dlambda = reverse cumsum of dG over the chunk's rows, where lambda > floor (else 0)
+//
+// Two launches:
+//   1. walk_kernel walks every (sequence, head, value slice) twice, as two halves of one
+//      grid that run side by side: forwards from the initial state, storing the state
+//      entering every chunk, and backwards from dS_final, storing the gradient leaving
+//      every chunk (dS in MFMA accumulators, as the forward keeps S);
+//   2. grad_kernel takes one (chunk, head) per workgroup -- all chunks in parallel -- and
+//      forms every input gradient of the chunk from its entering state and leaving
+//      gradient.
+// Everything is fp32 (v_mfma_f32_16x16x4_f32), whatever the input dtype.
+#include <math.h>
+
 #include "kda_device.h"
 #include "kda_launch.h"
 
 namespace kda {
 namespace {
 
-constexpr int kBwdThreads = 256;
-constexpr int kC = 16;  // tokens per chunk
+constexpr int kThreads = 256;
+constexpr int kC = 16;   // tokens per chunk
+constexpr int kNW = 4;   // waves per workgroup
+constexpr int kTS = 20;  // row stride of 16x16 fp32 tiles (float4-aligned, padded)
 
+typedef Mma<float> M;
+
+__device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+// A-fragment of X^T for a row-major 16x16 tile X: element i of lane (r, g) = X[4g + i][r]
+__device__ __forceinline__ f32x4 ld4_col(const float* X, int r, int g) {
+    return f32x4{X[(4 * g) * kTS + r], X[(4 * g + 1) * kTS + r], X[(4 * g + 2) * kTS + r],
+                 X[(4 * g + 3) * kTS + r]};
+}
+// LDS writes of this wave made visible to its own later reads (no workgroup barrier)
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
+// Per-channel cumulative log-decay of one chunk and the decay-folded operands.  Thread ch
+// (< DK) owns channel ch: it keeps G (16 rows) and a bit mask of the rows with lambda > floor.
+template <typename T, int RS>
+__device__ __forceinline__ void chunk_decay(const T* __restrict__ q, const T* __restrict__ k,
+                                            const T* __restrict__ la, int64_t base, int64_t rowq,
+                                            int Cp, int ch, float floor_, float scale,
+                                            float (&G)[kC], uint32_t& live, float& GC,
+                                            float* s_Qh, float* s_Kh, float* s_Kc) {
+    float qv[kC], kv[kC];
+    float acc = 0.f;
+    live = 0;
+#pragma unroll
+    for (int rr = 0; rr < kC; ++rr) {
+        const bool in = rr < Cp;
+        const int64_t off = base + rr * rowq + ch;
+        const float lam = in ? to_f32(la[off]) : 0.f;
+        qv[rr] = in ? to_f32(q[off]) : 0.f;
+        kv[rr] = in ? to_f32(k[off]) : 0.f;
+        if (in && lam > floor_) live |= 1u << rr;
+        acc += in ? fmaxf(lam, floor_) : 0.f;
+        G[rr] = acc;
+    }
+    GC = acc;
+#pragma unroll
+    for (int rr = 0; rr < kC; ++rr) {
+        const float e = __expf(G[rr]), ei = __expf(-G[rr]);
+        s_Qh[rr * RS + ch] = scale * qv[rr] * e;
+        s_Kh[rr * RS + ch] = kv[rr] * e;
+        s_Kc[rr * RS + ch] = kv[rr] * ei;
+    }
+}
+
+// Gram products of the chunk (wave 0: A', wave 1: P), then X and T by forward substitution.
+// s_A receives A' (unscaled, strict lower); s_X may be null.
+template <int DK, int RS>
+__device__ __forceinline__ void chunk_gram(const float* s_Qh, const float* s_Kh, const float* s_Kc,
+                                           const float* s_beta, float* s_A, float* s_P, float* s_X,
+                                           float* s_T, int wave, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+    if (wave < 2) {
+        const float* L = wave == 0 ? s_Kh : s_Qh;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kb = 0; kb < DK / 16; ++kb)
+            acc = M::run(ld4(&L[r * RS + 16 * kb + 4 * g]), ld4(&s_Kc[r * RS + 16 * kb + 4 * g]), acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 4 * g + i;  // acc[i] = (L Kc^T)[row][r]
+            if (wave == 0) s_A[row * kTS + r] = r < row ? acc[i] : 0.f;
+            else s_P[row * kTS + r] = r <= row ? acc[i] : 0.f;
+        }
+    }
+    __syncthreads();
+    if (wave == 0 && lane < 16) {  // column `lane` of X = (I + Diag(beta) A')^-1
+        const int col = lane;
+        float x[kC];
+#pragma unroll
+        for (int i = 0; i < kC; ++i) {
+            float d = 0.f;
+#pragma unroll
+            for (int j = 0; j < i; ++j) d += s_A[i * kTS + j] * x[j];
+            x[i] = (i == col ? 1.f : 0.f) - s_beta[i] * d;
+        }
+        const float bc = s_beta[col];
+#pragma unroll
+        for (int i = 0; i < kC; ++i) {
+            if (s_X) s_X[i * kTS + col] = x[i];
+            s_T[i * kTS + col] = x[i] * bc;
+        }
+    }
+    __syncthreads();
+}
+
+// ---------------------------------------------------------------------------------------------
+// 1. The two sequential walks.  Blocks [0, half) run forwards, [half, 2 half) backwards.
 template <typename T>
-struct BwdArgs {
+struct WalkArgs {
     const T *q, *k, *v, *la, *beta, *gate, *dout;
     const int32_t* cu;
-    const float *S0, *dSf;
-    float *dq, *dk, *dv, *dla, *dbeta, *dgate, *dS0;
-    float* ws;            // chunk entry states, then per-pair token states
-    int64_t tok_base;     // float offset of the token-state area in ws
-    int H;
+    const float* S0;    // initial state, or null
+    const float* dSf;   // gradient of the final state, or null
+    float* dS0;         // gradient of the initial state, or null
+    float* states;      // state entering chunk c of sequence n: slot cu[n]/16 + n + c
+    float* dsc;         // gradient leaving chunk c of sequence n: same slot
+    int H, n_slices, half;
     float floor_, scale;
 };
 
-// Sum over the 64 lanes of the wave of N per-lane values (x[i] = the lane's part of row i),
-// by recursive halving: after the call, lane l holds the total of row rowsel(l), with
-// rowsel(l) = (l >> 1) & 31 for N = 32 and (l >> 2) & 15 for N = 16.
-template <int N>
-__device__ __forceinline__ float rows_reduce(const float (&p)[N], int lane) {
-    float x[N];
-#pragma unroll
-    for (int i = 0; i < N; ++i) x[i] = p[i];
-    int n = N;
-    int m = 32;
-#pragma unroll
-    for (; n > 1; m >>= 1) {
-        const int half = n / 2;
-        const bool b = lane & m;
-#pragma unroll
-        for (int i = 0; i < half; ++i) {
-            const float lo = x[i], hi = x[i + half];
-            const float keep = b ? hi : lo, send = b ? lo : hi;
-            x[i] = keep + __shfl_xor(send, m);
-        }
-        n = half;
-    }
-#pragma unroll
-    for (; m >= 1; m >>= 1) x[0] += __shfl_xor(x[0], m);
-    return x[0];
-}
+template <typename T, int DK, int DV, int NCB>
+__global__ __launch_bounds__(kThreads) void walk_kernel(const WalkArgs<T> a) {
+    constexpr int NV = 16 * NCB;
+    constexpr int RS = DK + 4;
+    constexpr int CS = 16 + 4;
+    constexpr int KB = DK / 16;
+    constexpr int OWN = (NCB + kNW - 1) / kNW;
 
-template <int N>
-__device__ __forceinline__ int rowsel(int lane) {
-    return N == 32 ? (lane >> 1) & 31 : (lane >> 2) & 15;
-}
-
-template <typename T, int DK, int DV>
-__global__ __launch_bounds__(kBwdThreads) void backward_kernel(const BwdArgs<T> a) {
-    constexpr int RPW = DK / 4;   // rows per wave
-    constexpr int CPL = DV / 64;  // columns per lane
-    static_assert(RPW == 16 || RPW == 32, "shape");
-    __shared__ float s_k[kC][DK], s_a[kC][DK], s_q[kC][DK];
-    __shared__ float s_v[kC][DV], s_g[kC][DV], s_do[kC][DV], s_w[kC][DV], s_u[kC][DV];
-    __shared__ float s_beta[kC], s_qk[kC];
-    __shared__ float s_red[2][2][4][DV];  // [buffer][quantity][wave][column]
+    __shared__ __attribute__((aligned(16))) float s_Qh[kC * RS], s_Kh[kC * RS], s_Kc[kC * RS];
+    // channel-major [DK][16]: forwards Kb^T; backwards Qh^T and -Kh^T
+    __shared__ __attribute__((aligned(16))) float s_T1[DK * CS], s_T2[DK * CS];
+    __shared__ __attribute__((aligned(16))) float s_gamma[DK];
+    __shared__ __attribute__((aligned(16))) float s_A[16 * kTS], s_P[16 * kTS], s_T[16 * kTS];
+    __shared__ float s_beta[kC];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int pair = blockIdx.x;
+    const int r = lane & 15, g = lane >> 4;
+    const bool rev = (int)blockIdx.x >= a.half;
+    const int bid = rev ? (int)blockIdx.x - a.half : (int)blockIdx.x;
+    const int pair = bid / a.n_slices, slice = bid % a.n_slices;
     const int H = a.H, n = pair / H, h = pair % H;
     const int64_t tbeg = a.cu[n], tend = a.cu[n + 1];
-    const int64_t len = tend - tbeg;
-    const int nch = (int)((len + kC - 1) / kC);
-    const int64_t rowq = (int64_t)H * DK, rowv = (int64_t)H * DV;
-    const int64_t SS = (int64_t)DK * DV;
-    const int row0 = wave * RPW;
-    // chunk entry states: slot tbeg/16 + n + c (distinct for every sequence and chunk)
-    float* ws_chunk = a.ws + ((tbeg / kC + n) * H + h) * SS;
-    float* ws_tok = a.ws + a.tok_base + (int64_t)pair * kC * SS;
+    const int nch = (int)((tend - tbeg + kC - 1) / kC);
+    const int col0 = slice * NV;
+    const int64_t rowq = (int64_t)H * DK, rowv = (int64_t)H * DV, SS = (int64_t)DK * DV;
+    const int64_t sbase = (int64_t)pair * SS;
+    float* const out = (rev ? a.dsc : a.states) + ((tbeg / kC + n) * H + h) * SS;
 
-    auto sidx = [&](int i, int c) { return (row0 + i) * DV + lane + 64 * c; };
+    // X[jj][b] holds rows 16b + 4g + i, column col0 + 16j + r (j = wave + 4 jj) of S
+    // (forwards) or dS (backwards)
+    const float* init = rev ? a.dSf : a.S0;
+    f32x4 X[OWN][KB];
+#pragma unroll
+    for (int jj = 0; jj < OWN; ++jj) {
+        const int j = wave + kNW * jj;
+#pragma unroll
+        for (int b = 0; b < KB; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                X[jj][b][i] = (init && j < NCB)
+                                  ? init[sbase + (16 * b + 4 * g + i) * DV + col0 + 16 * j + r]
+                                  : 0.f;
+    }
 
-    // stage chunk c's inputs (rows past the end are zero: identity tokens)
-    auto stage = [&](int c, bool full) {
+    for (int it = 0; it < nch; ++it) {
+        const int c = rev ? nch - 1 - it : it;
         const int64_t t0 = tbeg + (int64_t)kC * c;
-        for (int idx = tid; idx < kC * DK; idx += kBwdThreads) {
-            const int j = idx / DK, ch = idx % DK;
-            const bool in = t0 + j < tend;
-            const int64_t off = (t0 + j) * rowq + (int64_t)h * DK + ch;
-            s_k[j][ch] = in ? to_f32(a.k[off]) : 0.f;
-            s_a[j][ch] = in ? __expf(fmaxf(to_f32(a.la[off]), a.floor_)) : 1.f;
-            if (full) s_q[j][ch] = in ? a.scale * to_f32(a.q[off]) : 0.f;
-        }
-        for (int idx = tid; idx < kC * DV; idx += kBwdThreads) {
-            const int j = idx / DV, col = idx % DV;
-            const bool in = t0 + j < tend;
-            const int64_t off = (t0 + j) * rowv + (int64_t)h * DV + col;
-            s_v[j][col] = in ? to_f32(a.v[off]) : 0.f;
-            if (full) {
-                s_g[j][col] = in ? to_f32(a.gate[off]) : 0.f;
-                s_do[j][col] = in ? to_f32(a.dout[off]) : 0.f;
+        const int Cp = (int)min<int64_t>(kC, tend - t0);
+        if (tid < DK) {
+            float G[kC], GC;
+            uint32_t live;
+            chunk_decay<T, RS>(a.q, a.k, a.la, t0 * rowq + (int64_t)h * DK, rowq, Cp, tid,
+                               a.floor_, a.scale, G, live, GC, s_Qh, s_Kh, s_Kc);
+            const float gam = __expf(GC);
+            s_gamma[tid] = gam;
+            if (rev) {
+#pragma unroll
+                for (int rr = 0; rr < kC; ++rr) {
+                    s_T1[tid * CS + rr] = s_Qh[rr * RS + tid];
+                    s_T2[tid * CS + rr] = -s_Kh[rr * RS + tid];
+                }
+            } else {
+#pragma unroll
+                for (int rr = 0; rr < kC; ++rr) s_T1[tid * CS + rr] = s_Kc[rr * RS + tid] * gam;
             }
         }
-        if (tid < kC) s_beta[tid] = t0 + tid < tend ? to_f32(a.beta[(t0 + tid) * H + h]) : 0.f;
+        if (tid < kC) s_beta[tid] = tid < Cp ? to_f32(a.beta[(t0 + tid) * H + h]) : 0.f;
         __syncthreads();
-        if (full) {  // (scale q) . k per token, one wave per token
-            for (int j = wave; j < kC; j += 4) {
-                float x = 0.f;
-                for (int ch = lane; ch < DK; ch += 64) x += s_q[j][ch] * s_k[j][ch];
-#pragma unroll
-                for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
-                if (lane == 0) s_qk[j] = x;
-            }
-            __syncthreads();
-        }
-    };
+        chunk_gram<DK, RS>(s_Qh, s_Kh, s_Kc, s_beta, s_A, s_P, nullptr, s_T, wave, lane);
 
-    // one forward token step on the state held in S (and, when kept, w and u to LDS)
-    int buf = 0;
-    auto fwd_step = [&](float (&S)[RPW][CPL], int j, bool keep) {
-        float wp[CPL];
+        const f32x4 Tr = ld4(&s_T[r * kTS + 4 * g]);  // A-fragment of T
+        const f32x4 PT = ld4_col(s_P, r, g);           // A-fragment of P^T
+        const f32x4 TT = ld4_col(s_T, r, g);           // A-fragment of T^T
+        float* dst = out + (int64_t)c * H * SS;
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) wp[c] = 0.f;
+        for (int jj = 0; jj < OWN; ++jj) {
+            const int j = wave + kNW * jj;
+            if (j >= NCB) continue;
+            const int col = col0 + 16 * j + r;
 #pragma unroll
-        for (int i = 0; i < RPW; ++i) {
-            const float ai = s_a[j][row0 + i], ki = s_k[j][row0 + i];
+            for (int b = 0; b < KB; ++b)
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-                S[i][c] *= ai;
-                wp[c] += S[i][c] * ki;
+                for (int i = 0; i < 4; ++i) dst[(16 * b + 4 * g + i) * DV + col] = X[jj][b][i];
+            if (!rev) {  // U = T (V - Kh S);  S <- Diag(gamma) S + Kb^T U
+                f32x4 KhS = zero4();
+#pragma unroll
+                for (int b = 0; b < KB; ++b)
+                    KhS = M::run(ld4(&s_Kh[r * RS + 16 * b + 4 * g]), X[jj][b], KhS);
+                f32x4 Rt;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 4 * g + i;
+                    Rt[i] = (row < Cp ? to_f32(a.v[(t0 + row) * rowv + (int64_t)h * DV + col]) : 0.f) -
+                            KhS[i];
+                }
+                const f32x4 U = M::run(Tr, Rt, zero4());
+#pragma unroll
+                for (int b = 0; b < KB; ++b) {
+                    const f32x4 gam = ld4(&s_gamma[16 * b + 4 * g]);
+                    X[jj][b] = M::run(ld4(&s_T1[(16 * b + r) * CS + 4 * g]), U, X[jj][b] * gam);
+                }
+            } else {  // dU = P^T dY + Kb dS_C;  dR = T^T dU;  dS = Diag(gamma) dS_C + Qh^T dY - Kh^T dR
+                f32x4 dY;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 4 * g + i;
+                    const int64_t off = (t0 + row) * rowv + (int64_t)h * DV + col;
+                    dY[i] = row < Cp ? to_f32(a.dout[off]) * to_f32(a.gate[off]) : 0.f;
+                }
+                f32x4 dU = M::run(PT, dY, zero4());
+#pragma unroll
+                for (int b = 0; b < KB; ++b) {
+                    const f32x4 gam = ld4(&s_gamma[16 * b + 4 * g]);
+                    dU = M::run(ld4(&s_Kc[r * RS + 16 * b + 4 * g]) * gam, X[jj][b], dU);
+                }
+                const f32x4 dR = M::run(TT, dU, zero4());
+#pragma unroll
+                for (int b = 0; b < KB; ++b) {
+                    const f32x4 gam = ld4(&s_gamma[16 * b + 4 * g]);
+                    f32x4 acc = X[jj][b] * gam;
+                    acc = M::run(ld4(&s_T1[(16 * b + r) * CS + 4 * g]), dY, acc);
+                    acc = M::run(ld4(&s_T2[(16 * b + r) * CS + 4 * g]), dR, acc);
+                    X[jj][b] = acc;
+                }
             }
         }
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) s_red[buf][0][wave][lane + 64 * c] = wp[c];
         __syncthreads();
-        float u[CPL];
+    }
+    if (rev && a.dS0) {
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            const int col = lane + 64 * c;
-            const float w = s_red[buf][0][0][col] + s_red[buf][0][1][col] + s_red[buf][0][2][col] +
-                            s_red[buf][0][3][col];
-            u[c] = s_beta[j] * (s_v[j][col] - w);
-            if (keep && wave == 0) { s_w[j][col] = w; s_u[j][col] = u[c]; }
+        for (int jj = 0; jj < OWN; ++jj) {
+            const int j = wave + kNW * jj;
+            if (j >= NCB) continue;
+#pragma unroll
+            for (int b = 0; b < KB; ++b)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    a.dS0[sbase + (16 * b + 4 * g + i) * DV + col0 + 16 * j + r] = X[jj][b][i];
         }
-        buf ^= 1;
-#pragma unroll
-        for (int i = 0; i < RPW; ++i) {
-            const float ki = s_k[j][row0 + i];
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) S[i][c] += ki * u[c];
-        }
-    };
+    }
+}
 
-    // ---- 1. forward: the state entering every chunk
-    float S[RPW][CPL];
+// ---------------------------------------------------------------------------------------------
+// 3. Per-chunk gradients, one workgroup per (chunk slot, head).
+template <typename T>
+struct GradArgs {
+    const T *q, *k, *v, *la, *beta, *gate, *dout;
+    const int32_t* cu;
+    const float* states;  // state entering chunk c of sequence n: slot cu[n]/16 + n + c
+    const float* dsc;     // gradient leaving chunk c of sequence n: same slot
+    float *dq, *dk, *dv, *dla, *dbeta, *dgate;
+    int H, N;
+    float floor_, scale;
+};
+
+template <typename T, int DK, int DV>
+__global__ __launch_bounds__(kThreads) void grad_kernel(const GradArgs<T> a) {
+    constexpr int RS = DK + 4;  // [16][DK] tiles
+    constexpr int VS = DV + 4;  // [16][DV] tiles
+    constexpr int WS = RS > VS ? RS : VS;
+    constexpr int KB = DK / 16, VB = DV / 16;
+    constexpr int OWNC = (KB + kNW - 1) / kNW;
+
+    __shared__ __attribute__((aligned(16))) float s_Qh[kC * RS], s_Kh[kC * RS], s_Kc[kC * RS];
+    // U, dY, dR [16][DV] during the value-block phase; dQh, dKh, dKc, dKb [16][DK] afterwards
+    __shared__ __attribute__((aligned(16))) float s_big[4 * kC * WS];
+    // per wave: R and dU of the current value block, then the wave's parts of dT and dP
+    __shared__ __attribute__((aligned(16))) float s_wv[kNW][2][16 * kTS];
+    __shared__ __attribute__((aligned(16))) float s_A[16 * kTS], s_X[16 * kTS], s_T[16 * kTS],
+        s_P[16 * kTS], s_dT[16 * kTS], s_dP[16 * kTS];
+    __shared__ __attribute__((aligned(16))) float s_gamma[DK], s_dgam[DK];
+    __shared__ float s_beta[kC], s_dbT[kC], s_dbA[kC];
+    float* const s_U = s_big;
+    float* const s_dY = s_big + kC * WS;
+    float* const s_dR = s_big + 2 * kC * WS;
+    float* const s_M = &s_wv[0][0][0];   // X^T dT Diag(beta), once the wave parts are summed
+    float* const s_dA = &s_wv[1][0][0];  // Diag(beta) dA
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int r = lane & 15, g = lane >> 4;
+    const int H = a.H;
+    const int slot = blockIdx.x / H, h = blockIdx.x % H;
+    // sequence n owns slots [cu[n]/16 + n, cu[n+1]/16 + n + 1): the largest n with
+    // cu[n]/16 + n <= slot
+    int lo = 0, hi = a.N - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (a.cu[mid] / kC + mid <= slot) lo = mid;
+        else hi = mid - 1;
+    }
+    const int n = lo;
+    const int64_t tbeg = a.cu[n], tend = a.cu[n + 1];
+    const int c = slot - (int)(tbeg / kC) - n;
+    if ((int64_t)kC * c >= tend - tbeg) return;  // a slot past the sequence's last chunk
+    const int64_t t0 = tbeg + (int64_t)kC * c;
+    const int Cp = (int)min<int64_t>(kC, tend - t0);
+    const int64_t rowq = (int64_t)H * DK, rowv = (int64_t)H * DV, SS = (int64_t)DK * DV;
+    const float* Sin = a.states + ((int64_t)slot * H + h) * SS;
+    const float* dSC = a.dsc + ((int64_t)slot * H + h) * SS;
+
+    float G[kC], GC = 0.f;
+    uint32_t live = 0;
+    if (tid < DK) {
+        chunk_decay<T, RS>(a.q, a.k, a.la, t0 * rowq + (int64_t)h * DK, rowq, Cp, tid, a.floor_,
+                           a.scale, G, live, GC, s_Qh, s_Kh, s_Kc);
+        s_gamma[tid] = __expf(GC);
+    }
+    if (tid < kC) s_beta[tid] = tid < Cp ? to_f32(a.beta[(t0 + tid) * H + h]) : 0.f;
+    __syncthreads();
+    chunk_gram<DK, RS>(s_Qh, s_Kh, s_Kc, s_beta, s_A, s_P, s_X, s_T, wave, lane);
+
+    // ---- A: value blocks (wave w takes blocks w, w + 4, ...)
+    {
+        const f32x4 Tr = ld4(&s_T[r * kTS + 4 * g]), Pr = ld4(&s_P[r * kTS + 4 * g]);
+        const f32x4 PT = ld4_col(s_P, r, g), TT = ld4_col(s_T, r, g);
+        float* const sR = s_wv[wave][0];
+        float* const sdU = s_wv[wave][1];
+        f32x4 dTw = zero4(), dPw = zero4();
+        for (int vb = wave; vb < VB; vb += kNW) {
+            const int col = 16 * vb + r;
+            f32x4 S1[KB], D1[KB];  // rows 16b + 4g + i, column col
 #pragma unroll
-    for (int i = 0; i < RPW; ++i)
+            for (int b = 0; b < KB; ++b)
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) S[i][c] = a.S0 ? a.S0[(int64_t)pair * SS + sidx(i, c)] : 0.f;
-    for (int c = 0; c < nch; ++c) {
+                for (int i = 0; i < 4; ++i) {
+                    S1[b][i] = Sin[(16 * b + 4 * g + i) * DV + col];
+                    D1[b][i] = dSC[(16 * b + 4 * g + i) * DV + col];
+                }
+            f32x4 KhS = zero4(), QhS = zero4();
 #pragma unroll
-        for (int i = 0; i < RPW; ++i)
+            for (int b = 0; b < KB; ++b) {
+                KhS = M::run(ld4(&s_Kh[r * RS + 16 * b + 4 * g]), S1[b], KhS);
+                QhS = M::run(ld4(&s_Qh[r * RS + 16 * b + 4 * g]), S1[b], QhS);
+            }
+            f32x4 Rt, dO, gt;
 #pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) ws_chunk[(int64_t)c * H * SS + sidx(i, cc)] = S[i][cc];
-        stage(c, false);
-        const int cl = (int)min<int64_t>(kC, len - (int64_t)kC * c);
-        for (int j = 0; j < cl; ++j) fwd_step(S, j, false);
-        __syncthreads();  // the next chunk's staging overwrites the inputs
+            for (int i = 0; i < 4; ++i) {
+                const int row = 4 * g + i;
+                const int64_t off = (t0 + row) * rowv + (int64_t)h * DV + col;
+                const bool in = row < Cp;
+                Rt[i] = (in ? to_f32(a.v[off]) : 0.f) - KhS[i];
+                dO[i] = in ? to_f32(a.dout[off]) : 0.f;
+                gt[i] = in ? to_f32(a.gate[off]) : 0.f;
+            }
+            const f32x4 U = M::run(Tr, Rt, zero4());
+            const f32x4 Y = M::run(Pr, U, QhS);
+            const f32x4 dY = dO * gt;
+            f32x4 dU = M::run(PT, dY, zero4());
+#pragma unroll
+            for (int b = 0; b < KB; ++b) {
+                const f32x4 gam = ld4(&s_gamma[16 * b + 4 * g]);
+                dU = M::run(ld4(&s_Kc[r * RS + 16 * b + 4 * g]) * gam, D1[b], dU);  // Kb dS_C
+            }
+            const f32x4 dR = M::run(TT, dU, zero4());
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 4 * g + i;
+                if (row < Cp) {
+                    const int64_t off = (t0 + row) * rowv + (int64_t)h * DV + col;
+                    a.dgate[off] = dO[i] * Y[i];
+                    a.dv[off] = dR[i];
+                }
+                s_U[row * VS + col] = U[i];
+                s_dY[row * VS + col] = dY[i];
+                s_dR[row * VS + col] = dR[i];
+                sR[row * kTS + r] = Rt[i];
+                sdU[row * kTS + r] = dU[i];
+            }
+            wave_lds_sync();
+            // dT += dU R^T and dP += dY U^T over this block's 16 columns
+            dTw = M::run(ld4(&sdU[r * kTS + 4 * g]), ld4(&sR[r * kTS + 4 * g]), dTw);
+            dPw = M::run(ld4(&s_dY[r * VS + 16 * vb + 4 * g]), ld4(&s_U[r * VS + 16 * vb + 4 * g]), dPw);
+            wave_lds_sync();
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sR[(4 * g + i) * kTS + r] = dTw[i];
+            sdU[(4 * g + i) * kTS + r] = dPw[i];
+        }
+    }
+    __syncthreads();
+    {  // dT, dP: sums of the wave parts (one element per thread)
+        const int i = tid >> 4, j = tid & 15;
+        float t = 0.f, p = 0.f;
+#pragma unroll
+        for (int w = 0; w < kNW; ++w) {
+            t += s_wv[w][0][i * kTS + j];
+            p += s_wv[w][1][i * kTS + j];
+        }
+        s_dT[i * kTS + j] = t;
+        s_dP[i * kTS + j] = j <= i ? p : 0.f;
     }
 
-    // ---- 2. backward over the chunks
-    float dS[RPW][CPL];
+    // ---- B: channel blocks (wave w takes blocks w, w + 4, ...): the sums over value columns
+    f32x4 aQ[OWNC], aK[OWNC], aB[OWNC];
 #pragma unroll
-    for (int i = 0; i < RPW; ++i)
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) dS[i][c] = a.dSf ? a.dSf[(int64_t)pair * SS + sidx(i, c)] : 0.f;
-    for (int c = nch - 1; c >= 0; --c) {
-        const int cl = (int)min<int64_t>(kC, len - (int64_t)kC * c);
-        const int64_t t0 = tbeg + (int64_t)kC * c;
-        stage(c, true);
-        // recompute the chunk's token states: ws_tok[j] = state entering token j
-#pragma unroll
-        for (int i = 0; i < RPW; ++i)
-#pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) S[i][cc] = ws_chunk[(int64_t)c * H * SS + sidx(i, cc)];
-        for (int j = 0; j < cl; ++j) {
-#pragma unroll
-            for (int i = 0; i < RPW; ++i)
-#pragma unroll
-                for (int cc = 0; cc < CPL; ++cc) ws_tok[(int64_t)j * SS + sidx(i, cc)] = S[i][cc];
-            fwd_step(S, j, true);
+    for (int jc = 0; jc < OWNC; ++jc) {
+        const int cb = wave + kNW * jc;
+        aQ[jc] = aK[jc] = aB[jc] = zero4();
+        if (cb >= KB) continue;
+        float dg = 0.f;
+        for (int vb = 0; vb < VB; ++vb) {
+            // S[16cb + r][16vb + 4g + i]: B-fragment of S^T over this value block
+            const int64_t off = (int64_t)(16 * cb + r) * DV + 16 * vb + 4 * g;
+            const f32x4 S2 = ld4(Sin + off);
+            const f32x4 D2 = ld4(dSC + off);
+            aQ[jc] = M::run(ld4(&s_dY[r * VS + 16 * vb + 4 * g]), S2, aQ[jc]);
+            aK[jc] = M::run(ld4(&s_dR[r * VS + 16 * vb + 4 * g]), S2, aK[jc]);
+            aB[jc] = M::run(ld4(&s_U[r * VS + 16 * vb + 4 * g]), D2, aB[jc]);
+            dg += D2[0] * S2[0] + D2[1] * S2[1] + D2[2] * S2[2] + D2[3] * S2[3];
         }
-        __syncthreads();  // s_w / s_u complete
-        for (int j = cl - 1; j >= 0; --j) {
-            const int64_t t = t0 + j;
-            // S_prev (state entering the token); S' = Diag(a) S_prev and S_t = S' + k u^T
-            // are recomputed where they are used
-            float Sprev[RPW][CPL];
-            float yp[CPL], kp[CPL];
+        dg += __shfl_xor(dg, 16);
+        dg += __shfl_xor(dg, 32);
+        if (g == 0) s_dgam[16 * cb + r] = dg;
+    }
+    __syncthreads();
+
+    // ---- C: the 16x16 algebra (one element per thread: row i, column j)
+    {
+        const int i = tid >> 4, j = tid & 15;
+        float m = 0.f;  // (X^T dT)[i][j] beta_j = (X^T dX)[i][j]
 #pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) { yp[cc] = 0.f; kp[cc] = 0.f; }
+        for (int kk = 0; kk < kC; ++kk) m += s_X[kk * kTS + i] * s_dT[kk * kTS + j];
+        s_M[i * kTS + j] = m * s_beta[j];
+        if (tid < kC) {  // column sums of X * dT
+            float s = 0.f;
 #pragma unroll
-            for (int i = 0; i < RPW; ++i) {
-                const float ai = s_a[j][row0 + i], ki = s_k[j][row0 + i], qi = s_q[j][row0 + i];
+            for (int kk = 0; kk < kC; ++kk) s += s_X[kk * kTS + tid] * s_dT[kk * kTS + tid];
+            s_dbT[tid] = s;
+        }
+    }
+    __syncthreads();
+    {
+        const int i = tid >> 4, j = tid & 15;
+        float d = 0.f;  // dA[i][j] = -(M X^T)[i][j] on the strict lower triangle
 #pragma unroll
-                for (int cc = 0; cc < CPL; ++cc) {
-                    Sprev[i][cc] = ws_tok[(int64_t)j * SS + sidx(i, cc)];
-                    const float St = ai * Sprev[i][cc] + ki * s_u[j][lane + 64 * cc];
-                    yp[cc] += St * qi;
-                    kp[cc] += dS[i][cc] * ki;
-                }
+        for (int kk = 0; kk < kC; ++kk) d -= s_M[i * kTS + kk] * s_X[j * kTS + kk];
+        d = j < i ? d : 0.f;
+        s_dA[i * kTS + j] = s_beta[i] * d;
+        float e = d * s_A[i * kTS + j];
+        e += __shfl_xor(e, 8);
+        e += __shfl_xor(e, 4);
+        e += __shfl_xor(e, 2);
+        e += __shfl_xor(e, 1);
+        if (j == 0) s_dbA[i] = e;
+    }
+    __syncthreads();
+
+    // ---- D: the chunk-local terms, then the four operand gradients into LDS (the
+    // value-phase tiles are dead: every wave has passed two barriers since reading them)
+    {
+        const f32x4 dPr = ld4(&s_dP[r * kTS + 4 * g]), dPc = ld4_col(s_dP, r, g);
+        const f32x4 dAr = ld4(&s_dA[r * kTS + 4 * g]), dAc = ld4_col(s_dA, r, g);
+#pragma unroll
+        for (int jc = 0; jc < OWNC; ++jc) {
+            const int cb = wave + kNW * jc;
+            if (cb >= KB) continue;
+            f32x4 KcB, QhB, KhB;  // B-fragments: X[4g + i][16cb + r]
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                KcB[i] = s_Kc[(4 * g + i) * RS + 16 * cb + r];
+                QhB[i] = s_Qh[(4 * g + i) * RS + 16 * cb + r];
+                KhB[i] = s_Kh[(4 * g + i) * RS + 16 * cb + r];
             }
+            const f32x4 dQh = M::run(dPr, KcB, aQ[jc]);
+            const f32x4 dKh = M::run(dAr, KcB, -aK[jc]);
+            const f32x4 dKc = M::run(dAc, KhB, M::run(dPc, QhB, zero4()));
 #pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) {
-                s_red[buf][0][wave][lane + 64 * cc] = yp[cc];
-                s_red[buf][1][wave][lane + 64 * cc] = kp[cc];
-            }
-            __syncthreads();
-            float dy[CPL], du[CPL], dw[CPL], bp = 0.f;
-            const float bt = s_beta[j], qk = s_qk[j];
-#pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) {
-                const int col = lane + 64 * cc;
-                float y = 0.f, dSk = 0.f;
-#pragma unroll
-                for (int wv = 0; wv < 4; ++wv) { y += s_red[buf][0][wv][col]; dSk += s_red[buf][1][wv][col]; }
-                const float dov = s_do[j][col];
-                dy[cc] = dov * s_g[j][col];
-                du[cc] = dSk + dy[cc] * qk;
-                dw[cc] = -bt * du[cc];
-                bp += du[cc] * (s_v[j][col] - s_w[j][col]);
-                if (wave == 0) {
-                    a.dgate[t * rowv + (int64_t)h * DV + col] = dov * y;
-                    a.dv[t * rowv + (int64_t)h * DV + col] = bt * du[cc];
-                }
-            }
-            buf ^= 1;
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) bp += __shfl_xor(bp, off);
-            if (tid == 0) a.dbeta[t * H + h] = bp;
-            // row sums: dq = scale S_t dy, dk = dS u + S' dw, da = rowsum(dS' * S_prev)
-            float pq[RPW], pk[RPW], pa[RPW];
-#pragma unroll
-            for (int i = 0; i < RPW; ++i) {
-                const float ai = s_a[j][row0 + i], ki = s_k[j][row0 + i], qi = s_q[j][row0 + i];
-                pq[i] = 0.f; pk[i] = 0.f; pa[i] = 0.f;
-#pragma unroll
-                for (int cc = 0; cc < CPL; ++cc) {
-                    const float u = s_u[j][lane + 64 * cc];
-                    const float Sp = ai * Sprev[i][cc], St = Sp + ki * u;
-                    dS[i][cc] += qi * dy[cc];
-                    pq[i] += St * dy[cc];
-                    pk[i] += dS[i][cc] * u + Sp * dw[cc];
-                    const float dSp = dS[i][cc] + ki * dw[cc];
-                    pa[i] += dSp * Sprev[i][cc];
-                    dS[i][cc] = ai * dSp;
-                }
-            }
-            const float rq = rows_reduce<RPW>(pq, lane), rk = rows_reduce<RPW>(pk, lane),
-                        ra = rows_reduce<RPW>(pa, lane);
-            const int row = row0 + rowsel<RPW>(lane);
-            if ((lane & (64 / RPW - 1)) == 0) {  // one of the lanes holding this row
-                const int64_t off = t * rowq + (int64_t)h * DK + row;
-                a.dq[off] = a.scale * rq;
-                a.dk[off] = rk;
-                const float lam = to_f32(a.la[off]);
-                a.dla[off] = lam > a.floor_ ? ra * s_a[j][row] : 0.f;
+            for (int i = 0; i < 4; ++i) {
+                const int idx = (4 * g + i) * RS + 16 * cb + r;
+                s_big[idx] = dQh[i];
+                s_big[kC * WS + idx] = dKh[i];
+                s_big[2 * kC * WS + idx] = dKc[i];
+                s_big[3 * kC * WS + idx] = aB[jc][i];
             }
         }
-        __syncthreads();  // the next chunk's staging overwrites the inputs
     }
-    if (a.dS0) {
+    __syncthreads();
+
+    // ---- E: per channel -- dq, dk, and dlambda by the reverse cumsum of dG over the rows
+    if (tid < DK) {
+        const int ch = tid;
+        const float gam = s_gamma[ch];
+        float dGC = gam * s_dgam[ch];
+        float dG[kC];
 #pragma unroll
-        for (int i = 0; i < RPW; ++i)
+        for (int rr = 0; rr < kC; ++rr) {
+            const int idx = rr * RS + ch;
+            const float qh = s_Qh[idx], kh = s_Kh[idx], kc = s_Kc[idx], kb = kc * gam;
+            const float dqh = s_big[idx], dkh = s_big[kC * WS + idx];
+            const float dkc = s_big[2 * kC * WS + idx], dkb = s_big[3 * kC * WS + idx];
+            dG[rr] = qh * dqh + kh * dkh - kc * dkc - kb * dkb;
+            dGC += kb * dkb;
+            if (rr < Cp) {
+                const float e = __expf(G[rr]), ei = __expf(-G[rr]), eb = __expf(GC - G[rr]);
+                const int64_t off = (t0 + rr) * rowq + (int64_t)h * DK + ch;
+                a.dq[off] = a.scale * e * dqh;
+                a.dk[off] = e * dkh + ei * dkc + eb * dkb;
+            }
+        }
+        dG[kC - 1] += dGC;  // G_C is the last row's G (padding rows add no decay)
+        float acc = 0.f;
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) a.dS0[(int64_t)pair * SS + sidx(i, c)] = dS[i][c];
+        for (int rr = kC - 1; rr >= 0; --rr) {
+            acc += dG[rr];
+            if (rr < Cp)
+                a.dla[(t0 + rr) * rowq + (int64_t)h * DK + ch] = (live >> rr) & 1u ? acc : 0.f;
+        }
     }
+    if (tid < Cp) a.dbeta[(t0 + tid) * H + h] = s_dbT[tid] + s_dbA[tid];
+}
+
+template <typename T, int DK, int DV, int NCB>
+hipError_t launch_walk(const BackwardArgs& p, hipStream_t st) {
+    WalkArgs<T> a;
+    a.q = (const T*)p.q; a.k = (const T*)p.k; a.v = (const T*)p.v; a.la = (const T*)p.log_alpha;
+    a.beta = (const T*)p.beta; a.gate = (const T*)p.gate; a.dout = (const T*)p.d_out;
+    a.cu = p.cu_seqlens; a.S0 = p.initial_state; a.dSf = p.d_final_state;
+    a.dS0 = p.d_initial_state; a.states = p.workspace; a.dsc = p.workspace + p.grad_offset;
+    a.H = p.H; a.n_slices = DV / (16 * NCB); a.floor_ = p.floor_; a.scale = p.scale;
+    a.half = p.num_seqs * p.H * a.n_slices;
+    hipLaunchKernelGGL((walk_kernel<T, DK, DV, NCB>), dim3(2u * (unsigned)a.half), dim3(kThreads),
+                       0, st, a);
+    return hipGetLastError();
 }
 
 template <typename T, int DK, int DV>
 hipError_t launch_typed(const BackwardArgs& p, hipStream_t st) {
-    BwdArgs<T> a;
+    if (p.num_seqs == 0 || p.H == 0) return hipSuccess;
+    hipError_t e;
+    switch (p.nv) {
+        case 16: e = launch_walk<T, DK, DV, 1>(p, st); break;
+        case 32: e = launch_walk<T, DK, DV, 2>(p, st); break;
+        case 64: e = launch_walk<T, DK, DV, 4>(p, st); break;
+        default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess || p.T_total == 0) return e;
+    GradArgs<T> a;
     a.q = (const T*)p.q; a.k = (const T*)p.k; a.v = (const T*)p.v; a.la = (const T*)p.log_alpha;
     a.beta = (const T*)p.beta; a.gate = (const T*)p.gate; a.dout = (const T*)p.d_out;
-    a.cu = p.cu_seqlens; a.S0 = p.initial_state; a.dSf = p.d_final_state;
+    a.cu = p.cu_seqlens; a.states = p.workspace; a.dsc = p.workspace + p.grad_offset;
     a.dq = p.dq; a.dk = p.dk_; a.dv = p.dv_; a.dla = p.dlog_alpha; a.dbeta = p.dbeta;
-    a.dgate = p.dgate; a.dS0 = p.d_initial_state;
-    a.ws = p.workspace; a.tok_base = p.token_state_offset;
-    a.H = p.H; a.floor_ = p.floor_; a.scale = p.scale;
-    const int64_t pairs = (int64_t)p.num_seqs * p.H;
-    if (pairs == 0) return hipSuccess;
-    hipLaunchKernelGGL((backward_kernel<T, DK, DV>), dim3((unsigned)pairs), dim3(kBwdThreads), 0,
+    a.dgate = p.dgate; a.H = p.H; a.N = p.num_seqs; a.floor_ = p.floor_; a.scale = p.scale;
+    const int64_t slots = p.T_total / kC + p.num_seqs;
+    hipLaunchKernelGGL((grad_kernel<T, DK, DV>), dim3((unsigned)(slots * p.H)), dim3(kThreads), 0,
                        st, a);
     return hipGetLastError();
 }

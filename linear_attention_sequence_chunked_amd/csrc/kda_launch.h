@@ -84,8 +84,10 @@ struct BackwardArgs {
     const float* d_final_state;         // may be null
     float *dq, *dk_, *dv_, *dlog_alpha, *dbeta, *dgate;
     float* d_initial_state;             // may be null
-    float* workspace;                   // chunk entry states, then per-pair token states
-    int64_t token_state_offset;         // floats
+    float* workspace;                   // chunk-entering states, then chunk-leaving gradients
+    int64_t grad_offset;                // floats: start of the chunk-leaving gradients
+    int64_t T_total;
+    int nv;                             // value-slice width of the two sequential passes
 };
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream);
 

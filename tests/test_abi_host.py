@@ -270,13 +270,14 @@ def test_segmented_rejects(kw, msg):
 
 
 def test_backward_workspace_size():
-    """cu = (0, 40, 40, 100), H = 2, d = 64: chunk entry states at slots cu[n]/16 + n + c,
-    i.e. at most 100//16 + 3 = 9 slots per head, then 16 token states per (sequence, head)."""
+    """cu = (0, 40, 40, 100), H = 2, d = 64: the state entering every chunk at slot
+    cu[n]/16 + n + c (at most 100 // 16 + 3 = 9 slots per head), then the gradient leaving
+    every chunk at the same slots."""
     lib = _lib.load()
     p = _lib.params(_lib.KDA_DTYPE_BF16, 2, 64, 64)
     ss = 64 * 64 * 4
     assert lib.kda_prefill_backward_workspace(ctypes.byref(p), cu(0, 40, 40, 100), 3) == \
-        (9 * 2 + 3 * 2 * 16) * ss
+        2 * 9 * 2 * ss
     assert lib.kda_prefill_backward_workspace(ctypes.byref(p), cu(0, 40, 30), 2) == -1
 
 
