@@ -62,6 +62,14 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 }
 
+// Workgroup barrier that orders LDS only: __syncthreads() would also wait for every
+// outstanding global access, including loads issued a chunk ahead and the state stores.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Per-channel cumulative log-decay of one chunk and the decay-folded operands.  Thread ch
 // (< DK) owns channel ch: it keeps G (16 rows) and a bit mask of the rows with lambda > floor.
 template <typename T, int RS>
@@ -114,7 +122,7 @@ __device__ __forceinline__ void chunk_gram(const float* s_Qh, const float* s_Kh,
             else s_P[row * kTS + r] = r <= row ? acc[i] : 0.f;
         }
     }
-    __syncthreads();
+    lds_barrier();
     if (wave == 0 && lane < 16) {  // column `lane` of X = (I + Diag(beta) A')^-1
         const int col = lane;
         float x[kC];
@@ -132,7 +140,7 @@ __device__ __forceinline__ void chunk_gram(const float* s_Qh, const float* s_Kh,
             s_T[i * kTS + col] = x[i] * bc;
         }
     }
-    __syncthreads();
+    lds_barrier();
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -150,19 +158,22 @@ struct WalkArgs {
     float floor_, scale;
 };
 
+// One workgroup = NCB consumer waves (one 16-column block of S or dS each) + one producer
+// wave.  The producer builds the chunk's key-side operands (decay-folded Qh, Kh, Kc, gamma,
+// the Gram products, T) one walk step ahead into a double buffer; the consumers run the
+// state step on the previous buffer.  Each kind of wave runs its own loop with exactly one
+// workgroup barrier per step.
 template <typename T, int DK, int DV, int NCB>
-__global__ __launch_bounds__(kThreads) void walk_kernel(const WalkArgs<T> a) {
+__global__ __launch_bounds__(64 * (NCB + 1)) void walk_kernel(const WalkArgs<T> a) {
     constexpr int NV = 16 * NCB;
     constexpr int RS = DK + 4;
-    constexpr int CS = 16 + 4;
     constexpr int KB = DK / 16;
-    constexpr int OWN = (NCB + kNW - 1) / kNW;
+    constexpr int CPL = DK / 64;  // channels per producer lane
 
-    __shared__ __attribute__((aligned(16))) float s_Qh[kC * RS], s_Kh[kC * RS], s_Kc[kC * RS];
-    // channel-major [DK][16]: forwards Kb^T; backwards Qh^T and -Kh^T
-    __shared__ __attribute__((aligned(16))) float s_T1[DK * CS], s_T2[DK * CS];
-    __shared__ __attribute__((aligned(16))) float s_gamma[DK];
-    __shared__ __attribute__((aligned(16))) float s_A[16 * kTS], s_P[16 * kTS], s_T[16 * kTS];
+    __shared__ __attribute__((aligned(16))) float s_Qh[2][kC * RS], s_Kh[2][kC * RS], s_Kc[2][kC * RS];
+    __shared__ __attribute__((aligned(16))) float s_gamma[2][DK];
+    __shared__ __attribute__((aligned(16))) float s_T[2][16 * kTS], s_P[2][16 * kTS];
+    __shared__ __attribute__((aligned(16))) float s_A[16 * kTS];
     __shared__ float s_beta[kC];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -173,122 +184,186 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(const WalkArgs<T> a) {
     const int H = a.H, n = pair / H, h = pair % H;
     const int64_t tbeg = a.cu[n], tend = a.cu[n + 1];
     const int nch = (int)((tend - tbeg + kC - 1) / kC);
-    const int col0 = slice * NV;
     const int64_t rowq = (int64_t)H * DK, rowv = (int64_t)H * DV, SS = (int64_t)DK * DV;
     const int64_t sbase = (int64_t)pair * SS;
-    float* const out = (rev ? a.dsc : a.states) + ((tbeg / kC + n) * H + h) * SS;
+    // chunk of walk step `it` (steps past the end re-use the last chunk: loads stay in bounds)
+    auto chunk_of = [&](int it) {
+        const int s = it < nch ? it : nch - 1;
+        return rev ? nch - 1 - s : s;
+    };
+    // rows past the end of the sequence re-read its last row; they are masked where used
+    auto row_at = [&](int c, int rr) { return min<int64_t>(tbeg + (int64_t)kC * c + rr, tend - 1); };
 
-    // X[jj][b] holds rows 16b + 4g + i, column col0 + 16j + r (j = wave + 4 jj) of S
-    // (forwards) or dS (backwards)
-    const float* init = rev ? a.dSf : a.S0;
-    f32x4 X[OWN][KB];
+    if (wave == NCB) {
+        // ---------------- producer
+        if (nch == 0) return;
+        T rq[CPL][kC], rk[CPL][kC], rl[CPL][kC], rb;
+        auto fetch = [&](int it) {
+            const int c = chunk_of(it);
 #pragma unroll
-    for (int jj = 0; jj < OWN; ++jj) {
-        const int j = wave + kNW * jj;
-#pragma unroll
-        for (int b = 0; b < KB; ++b)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                X[jj][b][i] = (init && j < NCB)
-                                  ? init[sbase + (16 * b + 4 * g + i) * DV + col0 + 16 * j + r]
-                                  : 0.f;
-    }
-
-    for (int it = 0; it < nch; ++it) {
-        const int c = rev ? nch - 1 - it : it;
-        const int64_t t0 = tbeg + (int64_t)kC * c;
-        const int Cp = (int)min<int64_t>(kC, tend - t0);
-        if (tid < DK) {
-            float G[kC], GC;
-            uint32_t live;
-            chunk_decay<T, RS>(a.q, a.k, a.la, t0 * rowq + (int64_t)h * DK, rowq, Cp, tid,
-                               a.floor_, a.scale, G, live, GC, s_Qh, s_Kh, s_Kc);
-            const float gam = __expf(GC);
-            s_gamma[tid] = gam;
-            if (rev) {
+            for (int cc = 0; cc < CPL; ++cc)
 #pragma unroll
                 for (int rr = 0; rr < kC; ++rr) {
-                    s_T1[tid * CS + rr] = s_Qh[rr * RS + tid];
-                    s_T2[tid * CS + rr] = -s_Kh[rr * RS + tid];
+                    const int64_t off = row_at(c, rr) * rowq + (int64_t)h * DK + lane + 64 * cc;
+                    rq[cc][rr] = a.q[off];
+                    rk[cc][rr] = a.k[off];
+                    rl[cc][rr] = a.la[off];
                 }
-            } else {
+            if (lane < kC) rb = a.beta[row_at(c, lane) * H + h];
+        };
+        auto build = [&](int it) {  // operands of step it into buffer it & 1; loads step it + 1
+            const int buf = it & 1;
+            const int c = chunk_of(it);
+            const int Cp = (int)min<int64_t>(kC, tend - tbeg - (int64_t)kC * c);
 #pragma unroll
-                for (int rr = 0; rr < kC; ++rr) s_T1[tid * CS + rr] = s_Kc[rr * RS + tid] * gam;
+            for (int cc = 0; cc < CPL; ++cc) {
+                const int ch = lane + 64 * cc;
+                float acc = 0.f, G[kC];
+#pragma unroll
+                for (int rr = 0; rr < kC; ++rr) {
+                    acc += rr < Cp ? fmaxf(to_f32(rl[cc][rr]), a.floor_) : 0.f;
+                    G[rr] = acc;
+                }
+                s_gamma[buf][ch] = __expf(acc);
+#pragma unroll
+                for (int rr = 0; rr < kC; ++rr) {
+                    const bool in = rr < Cp;
+                    const float kv = in ? to_f32(rk[cc][rr]) : 0.f, qv = in ? to_f32(rq[cc][rr]) : 0.f;
+                    const float e = __expf(G[rr]), ei = __expf(-G[rr]);
+                    s_Qh[buf][rr * RS + ch] = a.scale * qv * e;
+                    s_Kh[buf][rr * RS + ch] = kv * e;
+                    s_Kc[buf][rr * RS + ch] = kv * ei;
+                }
             }
-        }
-        if (tid < kC) s_beta[tid] = tid < Cp ? to_f32(a.beta[(t0 + tid) * H + h]) : 0.f;
-        __syncthreads();
-        chunk_gram<DK, RS>(s_Qh, s_Kh, s_Kc, s_beta, s_A, s_P, nullptr, s_T, wave, lane);
-
-        const f32x4 Tr = ld4(&s_T[r * kTS + 4 * g]);  // A-fragment of T
-        const f32x4 PT = ld4_col(s_P, r, g);           // A-fragment of P^T
-        const f32x4 TT = ld4_col(s_T, r, g);           // A-fragment of T^T
-        float* dst = out + (int64_t)c * H * SS;
+            if (lane < kC) s_beta[lane] = lane < Cp ? to_f32(rb) : 0.f;
+            fetch(it + 1);
+            __builtin_amdgcn_sched_barrier(0);  // the loads fly during the products below
+            wave_lds_sync();
+            // A' = strict_lower(Kh Kc^T) and P = lower_incl_diag(Qh Kc^T)
+            f32x4 accA = zero4(), accP = zero4();
 #pragma unroll
-        for (int jj = 0; jj < OWN; ++jj) {
-            const int j = wave + kNW * jj;
-            if (j >= NCB) continue;
-            const int col = col0 + 16 * j + r;
+            for (int kb = 0; kb < KB; ++kb) {
+                const f32x4 kc = ld4(&s_Kc[buf][r * RS + 16 * kb + 4 * g]);
+                accA = M::run(ld4(&s_Kh[buf][r * RS + 16 * kb + 4 * g]), kc, accA);
+                accP = M::run(ld4(&s_Qh[buf][r * RS + 16 * kb + 4 * g]), kc, accP);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 4 * g + i;
+                s_A[row * kTS + r] = r < row ? accA[i] : 0.f;
+                s_P[buf][row * kTS + r] = r <= row ? accP[i] : 0.f;
+            }
+            wave_lds_sync();
+            if (lane < 16) {  // column `lane` of X = (I + Diag(beta) A')^-1, then T = X Diag(beta)
+                float x[kC];
+#pragma unroll
+                for (int i = 0; i < kC; ++i) {
+                    float d = 0.f;
+#pragma unroll
+                    for (int j = 0; j < i; ++j) d += s_A[i * kTS + j] * x[j];
+                    x[i] = (i == lane ? 1.f : 0.f) - s_beta[i] * d;
+                }
+                const float bc = s_beta[lane];
+#pragma unroll
+                for (int i = 0; i < kC; ++i) s_T[buf][i * kTS + lane] = x[i] * bc;
+            }
+        };
+        fetch(0);
+        build(0);
+        lds_barrier();
+        for (int it = 0; it < nch; ++it) {
+            if (it + 1 < nch) build(it + 1);
+            lds_barrier();
+        }
+        return;
+    }
+
+    // ---------------- consumers: wave w owns value columns slice NV + 16 w + [0, 16)
+    const int col = slice * NV + 16 * wave + r;
+    float* const out = (rev ? a.dsc : a.states) + ((tbeg / kC + n) * H + h) * SS;
+    // X[b] holds rows 16b + 4g + i, column col of S (forwards) or dS (backwards)
+    const float* init = rev ? a.dSf : a.S0;
+    f32x4 X[KB];
+#pragma unroll
+    for (int b = 0; b < KB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) X[b][i] = init ? init[sbase + (16 * b + 4 * g + i) * DV + col] : 0.f;
+    if (nch > 0) {
+        const T* const vsrc = rev ? a.dout : a.v;  // backwards: dO (times the gate)
+        T rv[4], rg[4];
+        auto fetch = [&](int it) {
+            const int c = chunk_of(it);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t off = row_at(c, 4 * g + i) * rowv + (int64_t)h * DV + col;
+                rv[i] = vsrc[off];
+                rg[i] = a.gate[off];
+            }
+        };
+        fetch(0);
+        lds_barrier();
+        for (int it = 0; it < nch; ++it) {
+            const int buf = it & 1;
+            const int c = chunk_of(it);
+            const int Cp = (int)min<int64_t>(kC, tend - tbeg - (int64_t)kC * c);
+            const float* Qh = s_Qh[buf];
+            const float* Kh = s_Kh[buf];
+            const float* Kc = s_Kc[buf];
+            const float* gm = s_gamma[buf];
+            f32x4 in4;  // V (forwards) or dY = dO * gate (backwards), rows 4g + i, column col
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                in4[i] = 4 * g + i < Cp ? (rev ? to_f32(rv[i]) * to_f32(rg[i]) : to_f32(rv[i])) : 0.f;
+            fetch(it + 1);
+            float* dst = out + (int64_t)c * H * SS;
 #pragma unroll
             for (int b = 0; b < KB; ++b)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) dst[(16 * b + 4 * g + i) * DV + col] = X[jj][b][i];
+                for (int i = 0; i < 4; ++i) dst[(16 * b + 4 * g + i) * DV + col] = X[b][i];
+            __builtin_amdgcn_sched_barrier(0);
             if (!rev) {  // U = T (V - Kh S);  S <- Diag(gamma) S + Kb^T U
-                f32x4 KhS = zero4();
+                f32x4 Rt = in4;
 #pragma unroll
                 for (int b = 0; b < KB; ++b)
-                    KhS = M::run(ld4(&s_Kh[r * RS + 16 * b + 4 * g]), X[jj][b], KhS);
-                f32x4 Rt;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = 4 * g + i;
-                    Rt[i] = (row < Cp ? to_f32(a.v[(t0 + row) * rowv + (int64_t)h * DV + col]) : 0.f) -
-                            KhS[i];
-                }
-                const f32x4 U = M::run(Tr, Rt, zero4());
+                    Rt = M::run(-ld4(&Kh[r * RS + 16 * b + 4 * g]), X[b], Rt);
+                const f32x4 U = M::run(ld4(&s_T[buf][r * kTS + 4 * g]), Rt, zero4());
 #pragma unroll
                 for (int b = 0; b < KB; ++b) {
-                    const f32x4 gam = ld4(&s_gamma[16 * b + 4 * g]);
-                    X[jj][b] = M::run(ld4(&s_T1[(16 * b + r) * CS + 4 * g]), U, X[jj][b] * gam);
+                    // A-fragment of Kb^T: Kb[4g + i][16b + r] = Kc[4g + i][16b + r] gamma[16b + r]
+                    const float gr = gm[16 * b + r];
+                    f32x4 kbt;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) kbt[i] = Kc[(4 * g + i) * RS + 16 * b + r] * gr;
+                    X[b] = M::run(kbt, U, X[b] * ld4(&gm[16 * b + 4 * g]));
                 }
             } else {  // dU = P^T dY + Kb dS_C;  dR = T^T dU;  dS = Diag(gamma) dS_C + Qh^T dY - Kh^T dR
-                f32x4 dY;
+                f32x4 dU = M::run(ld4_col(s_P[buf], r, g), in4, zero4());
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = 4 * g + i;
-                    const int64_t off = (t0 + row) * rowv + (int64_t)h * DV + col;
-                    dY[i] = row < Cp ? to_f32(a.dout[off]) * to_f32(a.gate[off]) : 0.f;
-                }
-                f32x4 dU = M::run(PT, dY, zero4());
+                for (int b = 0; b < KB; ++b)
+                    dU = M::run(ld4(&Kc[r * RS + 16 * b + 4 * g]) * ld4(&gm[16 * b + 4 * g]), X[b], dU);
+                const f32x4 dR = M::run(ld4_col(s_T[buf], r, g), dU, zero4());
 #pragma unroll
                 for (int b = 0; b < KB; ++b) {
-                    const f32x4 gam = ld4(&s_gamma[16 * b + 4 * g]);
-                    dU = M::run(ld4(&s_Kc[r * RS + 16 * b + 4 * g]) * gam, X[jj][b], dU);
-                }
-                const f32x4 dR = M::run(TT, dU, zero4());
+                    f32x4 qt, kt;  // A-fragments of Qh^T and -Kh^T
 #pragma unroll
-                for (int b = 0; b < KB; ++b) {
-                    const f32x4 gam = ld4(&s_gamma[16 * b + 4 * g]);
-                    f32x4 acc = X[jj][b] * gam;
-                    acc = M::run(ld4(&s_T1[(16 * b + r) * CS + 4 * g]), dY, acc);
-                    acc = M::run(ld4(&s_T2[(16 * b + r) * CS + 4 * g]), dR, acc);
-                    X[jj][b] = acc;
+                    for (int i = 0; i < 4; ++i) {
+                        qt[i] = Qh[(4 * g + i) * RS + 16 * b + r];
+                        kt[i] = -Kh[(4 * g + i) * RS + 16 * b + r];
+                    }
+                    f32x4 acc = X[b] * ld4(&gm[16 * b + 4 * g]);
+                    acc = M::run(qt, in4, acc);
+                    acc = M::run(kt, dR, acc);
+                    X[b] = acc;
                 }
             }
+            lds_barrier();
         }
-        __syncthreads();
     }
     if (rev && a.dS0) {
 #pragma unroll
-        for (int jj = 0; jj < OWN; ++jj) {
-            const int j = wave + kNW * jj;
-            if (j >= NCB) continue;
+        for (int b = 0; b < KB; ++b)
 #pragma unroll
-            for (int b = 0; b < KB; ++b)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    a.dS0[sbase + (16 * b + 4 * g + i) * DV + col0 + 16 * j + r] = X[jj][b][i];
-        }
+            for (int i = 0; i < 4; ++i) a.dS0[sbase + (16 * b + 4 * g + i) * DV + col] = X[b][i];
     }
 }
 
@@ -306,7 +381,7 @@ struct GradArgs {
 };
 
 template <typename T, int DK, int DV>
-__global__ __launch_bounds__(kThreads) void grad_kernel(const GradArgs<T> a) {
+__global__ __launch_bounds__(kThreads, 2) void grad_kernel(const GradArgs<T> a) {
     constexpr int RS = DK + 4;  // [16][DK] tiles
     constexpr int VS = DV + 4;  // [16][DV] tiles
     constexpr int WS = RS > VS ? RS : VS;
@@ -350,15 +425,15 @@ __global__ __launch_bounds__(kThreads) void grad_kernel(const GradArgs<T> a) {
     const float* Sin = a.states + ((int64_t)slot * H + h) * SS;
     const float* dSC = a.dsc + ((int64_t)slot * H + h) * SS;
 
-    float G[kC], GC = 0.f;
-    uint32_t live = 0;
     if (tid < DK) {
+        float G[kC], GC;
+        uint32_t live;
         chunk_decay<T, RS>(a.q, a.k, a.la, t0 * rowq + (int64_t)h * DK, rowq, Cp, tid, a.floor_,
                            a.scale, G, live, GC, s_Qh, s_Kh, s_Kc);
         s_gamma[tid] = __expf(GC);
     }
     if (tid < kC) s_beta[tid] = tid < Cp ? to_f32(a.beta[(t0 + tid) * H + h]) : 0.f;
-    __syncthreads();
+    lds_barrier();
     chunk_gram<DK, RS>(s_Qh, s_Kh, s_Kc, s_beta, s_A, s_P, s_X, s_T, wave, lane);
 
     // ---- A: value blocks (wave w takes blocks w, w + 4, ...)
@@ -368,21 +443,17 @@ __global__ __launch_bounds__(kThreads) void grad_kernel(const GradArgs<T> a) {
         float* const sR = s_wv[wave][0];
         float* const sdU = s_wv[wave][1];
         f32x4 dTw = zero4(), dPw = zero4();
+#pragma unroll 1
         for (int vb = wave; vb < VB; vb += kNW) {
             const int col = 16 * vb + r;
-            f32x4 S1[KB], D1[KB];  // rows 16b + 4g + i, column col
-#pragma unroll
-            for (int b = 0; b < KB; ++b)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    S1[b][i] = Sin[(16 * b + 4 * g + i) * DV + col];
-                    D1[b][i] = dSC[(16 * b + 4 * g + i) * DV + col];
-                }
             f32x4 KhS = zero4(), QhS = zero4();
 #pragma unroll
             for (int b = 0; b < KB; ++b) {
-                KhS = M::run(ld4(&s_Kh[r * RS + 16 * b + 4 * g]), S1[b], KhS);
-                QhS = M::run(ld4(&s_Qh[r * RS + 16 * b + 4 * g]), S1[b], QhS);
+                f32x4 S1;  // rows 16b + 4g + i, column col
+#pragma unroll
+                for (int i = 0; i < 4; ++i) S1[i] = Sin[(16 * b + 4 * g + i) * DV + col];
+                KhS = M::run(ld4(&s_Kh[r * RS + 16 * b + 4 * g]), S1, KhS);
+                QhS = M::run(ld4(&s_Qh[r * RS + 16 * b + 4 * g]), S1, QhS);
             }
             f32x4 Rt, dO, gt;
 #pragma unroll
@@ -400,8 +471,11 @@ __global__ __launch_bounds__(kThreads) void grad_kernel(const GradArgs<T> a) {
             f32x4 dU = M::run(PT, dY, zero4());
 #pragma unroll
             for (int b = 0; b < KB; ++b) {
+                f32x4 D1;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) D1[i] = dSC[(16 * b + 4 * g + i) * DV + col];
                 const f32x4 gam = ld4(&s_gamma[16 * b + 4 * g]);
-                dU = M::run(ld4(&s_Kc[r * RS + 16 * b + 4 * g]) * gam, D1[b], dU);  // Kb dS_C
+                dU = M::run(ld4(&s_Kc[r * RS + 16 * b + 4 * g]) * gam, D1, dU);  // Kb dS_C
             }
             const f32x4 dR = M::run(TT, dU, zero4());
 #pragma unroll
@@ -430,7 +504,7 @@ __global__ __launch_bounds__(kThreads) void grad_kernel(const GradArgs<T> a) {
             sdU[(4 * g + i) * kTS + r] = dPw[i];
         }
     }
-    __syncthreads();
+    lds_barrier();
     {  // dT, dP: sums of the wave parts (one element per thread)
         const int i = tid >> 4, j = tid & 15;
         float t = 0.f, p = 0.f;
@@ -451,6 +525,7 @@ __global__ __launch_bounds__(kThreads) void grad_kernel(const GradArgs<T> a) {
         aQ[jc] = aK[jc] = aB[jc] = zero4();
         if (cb >= KB) continue;
         float dg = 0.f;
+#pragma unroll 2
         for (int vb = 0; vb < VB; ++vb) {
             // S[16cb + r][16vb + 4g + i]: B-fragment of S^T over this value block
             const int64_t off = (int64_t)(16 * cb + r) * DV + 16 * vb + 4 * g;
@@ -465,7 +540,7 @@ __global__ __launch_bounds__(kThreads) void grad_kernel(const GradArgs<T> a) {
         dg += __shfl_xor(dg, 32);
         if (g == 0) s_dgam[16 * cb + r] = dg;
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- C: the 16x16 algebra (one element per thread: row i, column j)
     {
@@ -481,7 +556,7 @@ __global__ __launch_bounds__(kThreads) void grad_kernel(const GradArgs<T> a) {
             s_dbT[tid] = s;
         }
     }
-    __syncthreads();
+    lds_barrier();
     {
         const int i = tid >> 4, j = tid & 15;
         float d = 0.f;  // dA[i][j] = -(M X^T)[i][j] on the strict lower triangle
@@ -496,7 +571,7 @@ __global__ __launch_bounds__(kThreads) void grad_kernel(const GradArgs<T> a) {
         e += __shfl_xor(e, 1);
         if (j == 0) s_dbA[i] = e;
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- D: the chunk-local terms, then the four operand gradients into LDS (the
     // value-phase tiles are dead: every wave has passed two barriers since reading them)
@@ -527,11 +602,21 @@ __global__ __launch_bounds__(kThreads) void grad_kernel(const GradArgs<T> a) {
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- E: per channel -- dq, dk, and dlambda by the reverse cumsum of dG over the rows
     if (tid < DK) {
         const int ch = tid;
+        // the cumulative decay again (not kept in registers through the phases above)
+        float G[kC], GC = 0.f;
+        uint32_t live = 0;
+#pragma unroll
+        for (int rr = 0; rr < kC; ++rr) {
+            const float lam = rr < Cp ? to_f32(a.la[(t0 + rr) * rowq + (int64_t)h * DK + ch]) : 0.f;
+            if (rr < Cp && lam > a.floor_) live |= 1u << rr;
+            GC += rr < Cp ? fmaxf(lam, a.floor_) : 0.f;
+            G[rr] = GC;
+        }
         const float gam = s_gamma[ch];
         float dGC = gam * s_dgam[ch];
         float dG[kC];
@@ -571,8 +656,8 @@ hipError_t launch_walk(const BackwardArgs& p, hipStream_t st) {
     a.dS0 = p.d_initial_state; a.states = p.workspace; a.dsc = p.workspace + p.grad_offset;
     a.H = p.H; a.n_slices = DV / (16 * NCB); a.floor_ = p.floor_; a.scale = p.scale;
     a.half = p.num_seqs * p.H * a.n_slices;
-    hipLaunchKernelGGL((walk_kernel<T, DK, DV, NCB>), dim3(2u * (unsigned)a.half), dim3(kThreads),
-                       0, st, a);
+    hipLaunchKernelGGL((walk_kernel<T, DK, DV, NCB>), dim3(2u * (unsigned)a.half),
+                       dim3(64 * (NCB + 1)), 0, st, a);
     return hipGetLastError();
 }
 
