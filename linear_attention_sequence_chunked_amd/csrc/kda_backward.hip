@@ -434,7 +434,44 @@ __global__ __launch_bounds__(kThreads, 2) void grad_kernel(const GradArgs<T> a) 
     }
     if (tid < kC) s_beta[tid] = tid < Cp ? to_f32(a.beta[(t0 + tid) * H + h]) : 0.f;
     lds_barrier();
+    // Global operands of one value block -- rows 16b + 4g + i, column 16 vb + r of S and
+    // dS_C; rows 4g + i of V, dO and the gate -- loaded ahead of their use.  Rows past the
+    // end of the sequence re-read its last row and are masked where used.
+    constexpr int NA = VB / kNW;  // value blocks per wave
+    f32x4 S1[KB], D1[KB];
+    T rv[4], rdo[4], rgt[4];
+    auto loadA = [&](int vb) {
+        const int col = 16 * vb + r;
+#pragma unroll
+        for (int b = 0; b < KB; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                S1[b][i] = Sin[(16 * b + 4 * g + i) * DV + col];
+                D1[b][i] = dSC[(16 * b + 4 * g + i) * DV + col];
+            }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t off = (t0 + min(4 * g + i, Cp - 1)) * rowv + (int64_t)h * DV + col;
+            rv[i] = a.v[off];
+            rdo[i] = a.dout[off];
+            rgt[i] = a.gate[off];
+        }
+    };
+    loadA(wave);
+    __builtin_amdgcn_sched_barrier(0);  // in flight during the Gram products and T
     chunk_gram<DK, RS>(s_Qh, s_Kh, s_Kc, s_beta, s_A, s_P, s_X, s_T, wave, lane);
+
+    // S and dS_C of one channel block, read along rows (B-fragments of S^T over each value
+    // block), for the sums over value columns
+    f32x4 S2[VB], D2[VB];
+    auto loadB = [&](int cb) {
+#pragma unroll
+        for (int vb = 0; vb < VB; ++vb) {
+            const int64_t off = (int64_t)(16 * cb + r) * DV + 16 * vb + 4 * g;
+            S2[vb] = ld4(Sin + off);
+            D2[vb] = ld4(dSC + off);
+        }
+    };
 
     // ---- A: value blocks (wave w takes blocks w, w + 4, ...)
     {
@@ -443,27 +480,23 @@ __global__ __launch_bounds__(kThreads, 2) void grad_kernel(const GradArgs<T> a) 
         float* const sR = s_wv[wave][0];
         float* const sdU = s_wv[wave][1];
         f32x4 dTw = zero4(), dPw = zero4();
-#pragma unroll 1
-        for (int vb = wave; vb < VB; vb += kNW) {
+#pragma unroll
+        for (int ia = 0; ia < NA; ++ia) {
+            const int vb = wave + kNW * ia;
             const int col = 16 * vb + r;
             f32x4 KhS = zero4(), QhS = zero4();
 #pragma unroll
             for (int b = 0; b < KB; ++b) {
-                f32x4 S1;  // rows 16b + 4g + i, column col
-#pragma unroll
-                for (int i = 0; i < 4; ++i) S1[i] = Sin[(16 * b + 4 * g + i) * DV + col];
-                KhS = M::run(ld4(&s_Kh[r * RS + 16 * b + 4 * g]), S1, KhS);
-                QhS = M::run(ld4(&s_Qh[r * RS + 16 * b + 4 * g]), S1, QhS);
+                KhS = M::run(ld4(&s_Kh[r * RS + 16 * b + 4 * g]), S1[b], KhS);
+                QhS = M::run(ld4(&s_Qh[r * RS + 16 * b + 4 * g]), S1[b], QhS);
             }
             f32x4 Rt, dO, gt;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int row = 4 * g + i;
-                const int64_t off = (t0 + row) * rowv + (int64_t)h * DV + col;
-                const bool in = row < Cp;
-                Rt[i] = (in ? to_f32(a.v[off]) : 0.f) - KhS[i];
-                dO[i] = in ? to_f32(a.dout[off]) : 0.f;
-                gt[i] = in ? to_f32(a.gate[off]) : 0.f;
+                const bool in = 4 * g + i < Cp;
+                Rt[i] = (in ? to_f32(rv[i]) : 0.f) - KhS[i];
+                dO[i] = in ? to_f32(rdo[i]) : 0.f;
+                gt[i] = in ? to_f32(rgt[i]) : 0.f;
             }
             const f32x4 U = M::run(Tr, Rt, zero4());
             const f32x4 Y = M::run(Pr, U, QhS);
@@ -471,12 +504,12 @@ __global__ __launch_bounds__(kThreads, 2) void grad_kernel(const GradArgs<T> a) 
             f32x4 dU = M::run(PT, dY, zero4());
 #pragma unroll
             for (int b = 0; b < KB; ++b) {
-                f32x4 D1;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) D1[i] = dSC[(16 * b + 4 * g + i) * DV + col];
                 const f32x4 gam = ld4(&s_gamma[16 * b + 4 * g]);
-                dU = M::run(ld4(&s_Kc[r * RS + 16 * b + 4 * g]) * gam, D1, dU);  // Kb dS_C
+                dU = M::run(ld4(&s_Kc[r * RS + 16 * b + 4 * g]) * gam, D1[b], dU);  // Kb dS_C
             }
+            if (ia + 1 < NA) loadA(vb + kNW);
+            else loadB(wave);
+            __builtin_amdgcn_sched_barrier(0);
             const f32x4 dR = M::run(TT, dU, zero4());
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -519,26 +552,30 @@ __global__ __launch_bounds__(kThreads, 2) void grad_kernel(const GradArgs<T> a) 
 
     // ---- B: channel blocks (wave w takes blocks w, w + 4, ...): the sums over value columns
     f32x4 aQ[OWNC], aK[OWNC], aB[OWNC];
+    T rla[kC];  // log-decays of channel tid for the last phase, loaded ahead
 #pragma unroll
     for (int jc = 0; jc < OWNC; ++jc) {
         const int cb = wave + kNW * jc;
         aQ[jc] = aK[jc] = aB[jc] = zero4();
         if (cb >= KB) continue;
         float dg = 0.f;
-#pragma unroll 2
+#pragma unroll
         for (int vb = 0; vb < VB; ++vb) {
-            // S[16cb + r][16vb + 4g + i]: B-fragment of S^T over this value block
-            const int64_t off = (int64_t)(16 * cb + r) * DV + 16 * vb + 4 * g;
-            const f32x4 S2 = ld4(Sin + off);
-            const f32x4 D2 = ld4(dSC + off);
-            aQ[jc] = M::run(ld4(&s_dY[r * VS + 16 * vb + 4 * g]), S2, aQ[jc]);
-            aK[jc] = M::run(ld4(&s_dR[r * VS + 16 * vb + 4 * g]), S2, aK[jc]);
-            aB[jc] = M::run(ld4(&s_U[r * VS + 16 * vb + 4 * g]), D2, aB[jc]);
-            dg += D2[0] * S2[0] + D2[1] * S2[1] + D2[2] * S2[2] + D2[3] * S2[3];
+            aQ[jc] = M::run(ld4(&s_dY[r * VS + 16 * vb + 4 * g]), S2[vb], aQ[jc]);
+            aK[jc] = M::run(ld4(&s_dR[r * VS + 16 * vb + 4 * g]), S2[vb], aK[jc]);
+            aB[jc] = M::run(ld4(&s_U[r * VS + 16 * vb + 4 * g]), D2[vb], aB[jc]);
+            dg += D2[vb][0] * S2[vb][0] + D2[vb][1] * S2[vb][1] + D2[vb][2] * S2[vb][2] +
+                  D2[vb][3] * S2[vb][3];
         }
+        if (jc + 1 < OWNC && cb + kNW < KB) loadB(cb + kNW);
         dg += __shfl_xor(dg, 16);
         dg += __shfl_xor(dg, 32);
         if (g == 0) s_dgam[16 * cb + r] = dg;
+    }
+    if (tid < DK) {
+#pragma unroll
+        for (int rr = 0; rr < kC; ++rr)
+            rla[rr] = a.la[(t0 + min(rr, Cp - 1)) * rowq + (int64_t)h * DK + tid];
     }
     lds_barrier();
 
@@ -612,7 +649,7 @@ __global__ __launch_bounds__(kThreads, 2) void grad_kernel(const GradArgs<T> a) 
         uint32_t live = 0;
 #pragma unroll
         for (int rr = 0; rr < kC; ++rr) {
-            const float lam = rr < Cp ? to_f32(a.la[(t0 + rr) * rowq + (int64_t)h * DK + ch]) : 0.f;
+            const float lam = rr < Cp ? to_f32(rla[rr]) : 0.f;
             if (rr < Cp && lam > a.floor_) live |= 1u << rr;
             GC += rr < Cp ? fmaxf(lam, a.floor_) : 0.f;
             G[rr] = GC;
