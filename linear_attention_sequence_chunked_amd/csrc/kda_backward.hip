@@ -62,6 +62,48 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 }
 
+// eight consecutive channels (16 bytes of bf16 or 32 of fp32) to floats
+template <typename T>
+__device__ __forceinline__ void unpack8(const uint4 (&w)[sizeof(T) / 2], float (&x)[8]) {
+    if constexpr (sizeof(T) == 2) {
+        const uint32_t u[4] = {w[0].x, w[0].y, w[0].z, w[0].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = __uint_as_float(u[i] << 16);
+            x[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            x[4 * j] = __uint_as_float(w[j].x);
+            x[4 * j + 1] = __uint_as_float(w[j].y);
+            x[4 * j + 2] = __uint_as_float(w[j].z);
+            x[4 * j + 3] = __uint_as_float(w[j].w);
+        }
+    }
+}
+__device__ __forceinline__ void store8(float* p, const float (&x)[8]) {
+    *reinterpret_cast<f32x4*>(p) = f32x4{x[0], x[1], x[2], x[3]};
+    *reinterpret_cast<f32x4*>(p + 4) = f32x4{x[4], x[5], x[6], x[7]};
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                 CTRL, 0xF, 0xF, true));
+}
+// eight independent inclusive prefix sums over the 16 lanes of each DPP row
+__device__ __forceinline__ void row_scan8(float (&x)[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] += dpp<0x111>(x[j]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] += dpp<0x112>(x[j]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] += dpp<0x114>(x[j]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] += dpp<0x118>(x[j]);
+}
+__device__ __forceinline__ float row_last(float x) { return dpp<0x15F>(x); }  // lane 15 of the row
+
 // Workgroup barrier that orders LDS only: __syncthreads() would also wait for every
 // outstanding global access, including loads issued a chunk ahead and the state stores.
 __device__ __forceinline__ void lds_barrier() {
@@ -168,7 +210,6 @@ __global__ __launch_bounds__(64 * (NCB + 1)) void walk_kernel(const WalkArgs<T> 
     constexpr int NV = 16 * NCB;
     constexpr int RS = DK + 4;
     constexpr int KB = DK / 16;
-    constexpr int CPL = DK / 64;  // channels per producer lane
 
     __shared__ __attribute__((aligned(16))) float s_Qh[2][kC * RS], s_Kh[2][kC * RS], s_Kc[2][kC * RS];
     __shared__ __attribute__((aligned(16))) float s_gamma[2][DK];
@@ -197,17 +238,23 @@ __global__ __launch_bounds__(64 * (NCB + 1)) void walk_kernel(const WalkArgs<T> 
     if (wave == NCB) {
         // ---------------- producer
         if (nch == 0) return;
-        T rq[CPL][kC], rk[CPL][kC], rl[CPL][kC], rb;
+        // lane (pr, pg) holds row pr of the chunk, channels [pg CW, (pg + 1) CW), loaded as
+        // 16-byte pieces of 8 channels; the cumulative decay runs across the 16 lanes of a row
+        constexpr int CW = DK / 4, NP = CW / 8, NWD = (int)sizeof(T) / 2;
+        const int pr = lane & 15, pg = lane >> 4;
+        uint4 rq[NP][NWD], rk[NP][NWD], rl[NP][NWD];
+        T rb;
         auto fetch = [&](int it) {
             const int c = chunk_of(it);
+            const int64_t base = row_at(c, pr) * rowq + (int64_t)h * DK + pg * CW;
 #pragma unroll
-            for (int cc = 0; cc < CPL; ++cc)
+            for (int p = 0; p < NP; ++p)
 #pragma unroll
-                for (int rr = 0; rr < kC; ++rr) {
-                    const int64_t off = row_at(c, rr) * rowq + (int64_t)h * DK + lane + 64 * cc;
-                    rq[cc][rr] = a.q[off];
-                    rk[cc][rr] = a.k[off];
-                    rl[cc][rr] = a.la[off];
+                for (int w = 0; w < NWD; ++w) {
+                    const int64_t off = base + 8 * p + 4 * w;
+                    rq[p][w] = *reinterpret_cast<const uint4*>(a.q + off);
+                    rk[p][w] = *reinterpret_cast<const uint4*>(a.k + off);
+                    rl[p][w] = *reinterpret_cast<const uint4*>(a.la + off);
                 }
             if (lane < kC) rb = a.beta[row_at(c, lane) * H + h];
         };
@@ -215,25 +262,31 @@ __global__ __launch_bounds__(64 * (NCB + 1)) void walk_kernel(const WalkArgs<T> 
             const int buf = it & 1;
             const int c = chunk_of(it);
             const int Cp = (int)min<int64_t>(kC, tend - tbeg - (int64_t)kC * c);
+            const bool in = pr < Cp;
 #pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) {
-                const int ch = lane + 64 * cc;
-                float acc = 0.f, G[kC];
+            for (int p = 0; p < NP; ++p) {
+                float xq[8], xk[8], G[8];
+                unpack8<T>(rq[p], xq);
+                unpack8<T>(rk[p], xk);
+                unpack8<T>(rl[p], G);
 #pragma unroll
-                for (int rr = 0; rr < kC; ++rr) {
-                    acc += rr < Cp ? fmaxf(to_f32(rl[cc][rr]), a.floor_) : 0.f;
-                    G[rr] = acc;
+                for (int i = 0; i < 8; ++i) G[i] = in ? fmaxf(G[i], a.floor_) : 0.f;
+                row_scan8(G);
+                const int ch0 = pg * CW + 8 * p;
+                float qh[8], kh[8], kc[8], gm[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float e = __expf(G[i]), ei = __expf(-G[i]);
+                    const float qv = in ? xq[i] : 0.f, kv = in ? xk[i] : 0.f;
+                    qh[i] = a.scale * qv * e;
+                    kh[i] = kv * e;
+                    kc[i] = kv * ei;
+                    gm[i] = __expf(row_last(G[i]));  // G of the chunk's last row
                 }
-                s_gamma[buf][ch] = __expf(acc);
-#pragma unroll
-                for (int rr = 0; rr < kC; ++rr) {
-                    const bool in = rr < Cp;
-                    const float kv = in ? to_f32(rk[cc][rr]) : 0.f, qv = in ? to_f32(rq[cc][rr]) : 0.f;
-                    const float e = __expf(G[rr]), ei = __expf(-G[rr]);
-                    s_Qh[buf][rr * RS + ch] = a.scale * qv * e;
-                    s_Kh[buf][rr * RS + ch] = kv * e;
-                    s_Kc[buf][rr * RS + ch] = kv * ei;
-                }
+                store8(&s_Qh[buf][pr * RS + ch0], qh);
+                store8(&s_Kh[buf][pr * RS + ch0], kh);
+                store8(&s_Kc[buf][pr * RS + ch0], kc);
+                if (pr == 15) store8(&s_gamma[buf][ch0], gm);
             }
             if (lane < kC) s_beta[lane] = lane < Cp ? to_f32(rb) : 0.f;
             fetch(it + 1);

@@ -28,6 +28,14 @@ namespace {
 
 constexpr int kSpecThreads = 256;
 
+// Workgroup barrier that orders LDS only: __syncthreads() would also wait for the previous
+// draft's output stores to reach memory.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 template <typename T>
 struct SArgs {
     const T *q, *k, *v, *la, *beta, *gate;
@@ -125,7 +133,7 @@ __global__ __launch_bounds__(kSpecThreads) void spec_kernel(const SArgs<T> a) {
             s_red[buf][wave][lane][0] = w;
             if constexpr (VERIFY) s_red[buf][wave][lane][1] = b;
         }
-        __syncthreads();  // the other buffer is rewritten only after the next barrier
+        lds_barrier();  // the other buffer is rewritten only after the next barrier
         w = zero4();
         b = zero4();
 #pragma unroll
