@@ -631,8 +631,6 @@ kda_status kda_prefill_backward(const kda_params* params, const void* q, const v
     a.dbeta = dbeta; a.dgate = dgate; a.d_initial_state = d_initial_state;
     a.workspace = static_cast<float*>(workspace); a.grad_offset = (int64_t)grad_off;
     a.T_total = T;
-    // value slices of the two sequential passes: enough workgroups for every compute unit
-    a.nv = std::min(64, kda::prefill_pick_nv(p.dv, (int64_t)num_seqs * H, 0, device_cu_count()));
     const hipError_t e = kda::launch_backward(a, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return fail(KDA_ERR_HIP, "kda_prefill_backward launch: %s", hipGetErrorString(e));

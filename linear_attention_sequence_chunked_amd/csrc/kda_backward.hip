@@ -201,20 +201,96 @@ struct WalkArgs {
 };
 
 // One workgroup = NCB consumer waves (one 16-column block of S or dS each) + one producer
-// wave.  The producer builds the chunk's key-side operands (decay-folded Qh, Kh, Kc, gamma,
-// the Gram products, T) one walk step ahead into a double buffer; the consumers run the
-// state step on the previous buffer.  Each kind of wave runs its own loop with exactly one
-// workgroup barrier per step.
+// wave, over three LDS buffers.  In the interval between two workgroup barriers that steps
+// the walk to chunk step `it`:
+//   consumers  state step of `it` (buffer it % 3), then the decay-folded operands of step
+//              it + 2 into buffer (it + 2) % 3, one 8-channel piece per consumer wave;
+//   producer   the Gram products and T of step it + 1 (buffer (it + 1) % 3).
+// Each kind of wave runs its own loop with exactly one barrier per step; global inputs are
+// loaded two steps ahead (bf16; one step for fp32) into alternating register sets.
+//
+// Operands relative to the chunk's end (as in the forward): Kt = k e^(G - G_C),
+// Qt = (scale q) e^(G - G_C), Kb = k e^(G_C - G).  Then A' = strict_lower(Kt Kb^T),
+// P = lower_incl_diag(Qt Kb^T), and with S' = Diag(gamma) S:
+//   forwards   U = T (V - Kt S'),   S <- S' + Kb^T U
+//   backwards  dU = P^T dY + Kb dS_C,  dR = T^T dU,  dS <- Diag(gamma) (dS_C + Qt^T dY - Kt^T dR)
+//
+// All products are split-bf16: x = hi + lo with hi = bf16(x), lo = bf16(x - hi), and
+// a b = ah bh + ah bl + al bh (three v_mfma_f32_16x16x16_bf16, relative error ~2^-17) in
+// place of four 32-cycle fp32 MFMAs.  The key-side operands are stored already split,
+// row-major (token rows); operands that contract over the key channels are read back
+// transposed with ds_read_b64_tr_b16: within each 16-lane group, with lane 16g + 4j + q
+// pointing at row 4g + j, columns c0 + 4q .. +3 of a row-major tile X, lane (r, g) receives
+// X[4g + i][c0 + r] -- the A-fragment of the transpose of X's 16x16 block at column c0.
+template <int DK>
+struct alignas(16) WalkBuf {
+    static constexpr int RSB = DK + 8;  // bf16 row stride of [16][DK] tiles
+    static constexpr int TSB = 16 + 8;  // bf16 row stride of 16x16 tiles
+    bf16 kt[2][16 * RSB];               // [hi, lo] Kt
+    bf16 kb[2][16 * RSB];               // Kb
+    bf16 qt[2][16 * RSB];               // Qt (backwards only)
+    bf16 sq1[2][16 * TSB];              // T (forwards) or P^T (backwards)
+    bf16 sq2[2][16 * TSB];              // T^T (backwards)
+    float gamma[DK];
+};
+
+struct Split4 {
+    bf16x4 h, l;
+};
+__device__ __forceinline__ Split4 split4(f32x4 x) {
+    Split4 s;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const bf16 hi = (bf16)x[i];
+        s.h[i] = hi;
+        s.l[i] = (bf16)(x[i] - (float)hi);
+    }
+    return s;
+}
+__device__ __forceinline__ bf16x4 ldb4(const bf16* p) { return *reinterpret_cast<const bf16x4*>(p); }
+__device__ __forceinline__ Split4 lds_split(const bf16* hi, const bf16* lo) { return Split4{ldb4(hi), ldb4(lo)}; }
+// transposed read (see above)
+__device__ __forceinline__ bf16x4 lds_tr(const bf16* p) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(const_cast<bf16*>(p))));
+}
+__device__ __forceinline__ Split4 lds_split_tr(const bf16* hi, const bf16* lo) { return Split4{lds_tr(hi), lds_tr(lo)}; }
+// c + a b, both split: three bf16 MFMAs
+__device__ __forceinline__ f32x4 mma3(const Split4& a, const Split4& b, f32x4 c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.l, b.h, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.h, b.l, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.h, b.h, c, 0, 0, 0);
+}
+// eight floats, split, to 16-byte hi and lo pieces at the same offset of two tiles
+__device__ __forceinline__ void store_split8(bf16* hi, bf16* lo, const float (&x)[8]) {
+    bf16x4 h0, h1, l0, l1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        h0[i] = (bf16)x[i];
+        l0[i] = (bf16)(x[i] - (float)h0[i]);
+        h1[i] = (bf16)x[4 + i];
+        l1[i] = (bf16)(x[4 + i] - (float)h1[i]);
+    }
+    *reinterpret_cast<bf16x4*>(hi) = h0;
+    *reinterpret_cast<bf16x4*>(hi + 4) = h1;
+    *reinterpret_cast<bf16x4*>(lo) = l0;
+    *reinterpret_cast<bf16x4*>(lo + 4) = l1;
+}
+
 template <typename T, int DK, int DV, int NCB>
 __global__ __launch_bounds__(64 * (NCB + 1)) void walk_kernel(const WalkArgs<T> a) {
     constexpr int NV = 16 * NCB;
-    constexpr int RS = DK + 4;
     constexpr int KB = DK / 16;
+    constexpr int PF = sizeof(T) == 2 ? 2 : 1;  // steps of input prefetch (register sets)
+    constexpr int CW = DK / 4, NP = CW / 8;      // decay: channels per lane group, pieces
+    constexpr int NWD = (int)sizeof(T) / 2;      // 16-byte words per 8-channel piece
+    static_assert(NP <= NCB, "one decay piece per consumer wave");
+    typedef WalkBuf<DK> B;
+    constexpr int RSB = B::RSB, TSB = B::TSB;
 
-    __shared__ __attribute__((aligned(16))) float s_Qh[2][kC * RS], s_Kh[2][kC * RS], s_Kc[2][kC * RS];
-    __shared__ __attribute__((aligned(16))) float s_gamma[2][DK];
-    __shared__ __attribute__((aligned(16))) float s_T[2][16 * kTS], s_P[2][16 * kTS];
-    __shared__ __attribute__((aligned(16))) float s_A[16 * kTS];
+    __shared__ B s_buf[3];
+    __shared__ __attribute__((aligned(16))) float s_A[16 * kTS];  // producer only: A'
     __shared__ float s_beta[kC];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -227,6 +303,19 @@ __global__ __launch_bounds__(64 * (NCB + 1)) void walk_kernel(const WalkArgs<T> 
     const int nch = (int)((tend - tbeg + kC - 1) / kC);
     const int64_t rowq = (int64_t)H * DK, rowv = (int64_t)H * DV, SS = (int64_t)DK * DV;
     const int64_t sbase = (int64_t)pair * SS;
+    if (nch == 0) {  // nothing to walk: dS_0 = dS_final
+        if (rev && a.dS0 && wave < NCB) {
+            const int col = slice * NV + 16 * wave + r;
+#pragma unroll
+            for (int b = 0; b < KB; ++b)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int64_t o = sbase + (16 * b + 4 * g + i) * DV + col;
+                    a.dS0[o] = a.dSf ? a.dSf[o] : 0.f;
+                }
+        }
+        return;
+    }
     // chunk of walk step `it` (steps past the end re-use the last chunk: loads stay in bounds)
     auto chunk_of = [&](int it) {
         const int s = it < nch ? it : nch - 1;
@@ -234,106 +323,155 @@ __global__ __launch_bounds__(64 * (NCB + 1)) void walk_kernel(const WalkArgs<T> 
     };
     // rows past the end of the sequence re-read its last row; they are masked where used
     auto row_at = [&](int c, int rr) { return min<int64_t>(tbeg + (int64_t)kC * c + rr, tend - 1); };
+    auto rows_of = [&](int c) { return (int)min<int64_t>(kC, tend - tbeg - (int64_t)kC * c); };
+    const int fr = r * RSB + 4 * g;  // row fragment in [16][DK] tiles (block b: + 16 b)
+    const int fq = r * TSB + 4 * g;  // row fragment in 16x16 tiles
+    const int ft = (4 * g + ((lane & 15) >> 2)) * RSB + 4 * (lane & 3);  // transposed (+ 16 b)
 
     if (wave == NCB) {
-        // ---------------- producer
-        if (nch == 0) return;
-        // lane (pr, pg) holds row pr of the chunk, channels [pg CW, (pg + 1) CW), loaded as
-        // 16-byte pieces of 8 channels; the cumulative decay runs across the 16 lanes of a row
-        constexpr int CW = DK / 4, NP = CW / 8, NWD = (int)sizeof(T) / 2;
-        const int pr = lane & 15, pg = lane >> 4;
-        uint4 rq[NP][NWD], rk[NP][NWD], rl[NP][NWD];
-        T rb;
-        auto fetch = [&](int it) {
-            const int c = chunk_of(it);
-            const int64_t base = row_at(c, pr) * rowq + (int64_t)h * DK + pg * CW;
-#pragma unroll
-            for (int p = 0; p < NP; ++p)
-#pragma unroll
-                for (int w = 0; w < NWD; ++w) {
-                    const int64_t off = base + 8 * p + 4 * w;
-                    rq[p][w] = *reinterpret_cast<const uint4*>(a.q + off);
-                    rk[p][w] = *reinterpret_cast<const uint4*>(a.k + off);
-                    rl[p][w] = *reinterpret_cast<const uint4*>(a.la + off);
-                }
-            if (lane < kC) rb = a.beta[row_at(c, lane) * H + h];
+        // ---------------- producer: Gram products and T, one step ahead of the consumers
+        T rb[PF];
+        auto fetch = [&](T& x, int it) {
+            if (lane < kC) x = a.beta[row_at(chunk_of(it), lane) * H + h];
         };
-        auto build = [&](int it) {  // operands of step it into buffer it & 1; loads step it + 1
-            const int buf = it & 1;
-            const int c = chunk_of(it);
-            const int Cp = (int)min<int64_t>(kC, tend - tbeg - (int64_t)kC * c);
-            const bool in = pr < Cp;
-#pragma unroll
-            for (int p = 0; p < NP; ++p) {
-                float xq[8], xk[8], G[8];
-                unpack8<T>(rq[p], xq);
-                unpack8<T>(rk[p], xk);
-                unpack8<T>(rl[p], G);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) G[i] = in ? fmaxf(G[i], a.floor_) : 0.f;
-                row_scan8(G);
-                const int ch0 = pg * CW + 8 * p;
-                float qh[8], kh[8], kc[8], gm[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float e = __expf(G[i]), ei = __expf(-G[i]);
-                    const float qv = in ? xq[i] : 0.f, kv = in ? xk[i] : 0.f;
-                    qh[i] = a.scale * qv * e;
-                    kh[i] = kv * e;
-                    kc[i] = kv * ei;
-                    gm[i] = __expf(row_last(G[i]));  // G of the chunk's last row
-                }
-                store8(&s_Qh[buf][pr * RS + ch0], qh);
-                store8(&s_Kh[buf][pr * RS + ch0], kh);
-                store8(&s_Kc[buf][pr * RS + ch0], kc);
-                if (pr == 15) store8(&s_gamma[buf][ch0], gm);
-            }
-            if (lane < kC) s_beta[lane] = lane < Cp ? to_f32(rb) : 0.f;
-            fetch(it + 1);
-            __builtin_amdgcn_sched_barrier(0);  // the loads fly during the products below
-            wave_lds_sync();
-            // A' = strict_lower(Kh Kc^T) and P = lower_incl_diag(Qh Kc^T)
+        auto gram = [&](T& xb, int it) {  // step it, buffer it % 3; xb then loads step it + PF
+            B& o = s_buf[it % 3];
+            const int Cp = rows_of(chunk_of(it));
+            if (lane < kC) s_beta[lane] = lane < Cp ? to_f32(xb) : 0.f;
+            fetch(xb, it + PF);
+            // A' = strict_lower(Kt Kb^T) and P = lower_incl_diag(Qt Kb^T)
             f32x4 accA = zero4(), accP = zero4();
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
-                const f32x4 kc = ld4(&s_Kc[buf][r * RS + 16 * kb + 4 * g]);
-                accA = M::run(ld4(&s_Kh[buf][r * RS + 16 * kb + 4 * g]), kc, accA);
-                accP = M::run(ld4(&s_Qh[buf][r * RS + 16 * kb + 4 * g]), kc, accP);
+                const Split4 kbf = lds_split(&o.kb[0][fr + 16 * kb], &o.kb[1][fr + 16 * kb]);
+                accA = mma3(lds_split(&o.kt[0][fr + 16 * kb], &o.kt[1][fr + 16 * kb]), kbf, accA);
+                if (rev) accP = mma3(lds_split(&o.qt[0][fr + 16 * kb], &o.qt[1][fr + 16 * kb]), kbf, accP);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 4 * g + i;
                 s_A[row * kTS + r] = r < row ? accA[i] : 0.f;
-                s_P[buf][row * kTS + r] = r <= row ? accP[i] : 0.f;
+            }
+            if (rev) {  // P^T[r][4g + i] = P[4g + i][r]: lane (r, g) holds it already
+                f32x4 pm;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pm[i] = r <= 4 * g + i ? accP[i] : 0.f;
+                const Split4 ps = split4(pm);
+                *reinterpret_cast<bf16x4*>(&o.sq1[0][fq]) = ps.h;
+                *reinterpret_cast<bf16x4*>(&o.sq1[1][fq]) = ps.l;
             }
             wave_lds_sync();
             if (lane < 16) {  // column `lane` of X = (I + Diag(beta) A')^-1, then T = X Diag(beta)
-                float x[kC];
+                float xs[kC];
 #pragma unroll
                 for (int i = 0; i < kC; ++i) {
                     float d = 0.f;
 #pragma unroll
-                    for (int j = 0; j < i; ++j) d += s_A[i * kTS + j] * x[j];
-                    x[i] = (i == lane ? 1.f : 0.f) - s_beta[i] * d;
+                    for (int j = 0; j < i; ++j) d += s_A[i * kTS + j] * xs[j];
+                    xs[i] = (i == lane ? 1.f : 0.f) - s_beta[i] * d;
                 }
                 const float bc = s_beta[lane];
+                float t[kC];
 #pragma unroll
-                for (int i = 0; i < kC; ++i) s_T[buf][i * kTS + lane] = x[i] * bc;
+                for (int i = 0; i < kC; ++i) t[i] = xs[i] * bc;
+                if (rev) {  // T^T[lane][i] = T[i][lane]: one row per lane
+                    float t0[8], t1[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        t0[i] = t[i];
+                        t1[i] = t[8 + i];
+                    }
+                    store_split8(&o.sq2[0][lane * TSB], &o.sq2[1][lane * TSB], t0);
+                    store_split8(&o.sq2[0][lane * TSB + 8], &o.sq2[1][lane * TSB + 8], t1);
+                } else {  // T[i][lane]: one column per lane
+#pragma unroll
+                    for (int i = 0; i < kC; ++i) {
+                        const bf16 hi = (bf16)t[i];
+                        o.sq1[0][i * TSB + lane] = hi;
+                        o.sq1[1][i * TSB + lane] = (bf16)(t[i] - (float)hi);
+                    }
+                }
             }
+            wave_lds_sync();  // s_A and s_beta are rewritten by the next step
         };
-        fetch(0);
-        build(0);
-        lds_barrier();
-        for (int it = 0; it < nch; ++it) {
-            if (it + 1 < nch) build(it + 1);
-            lds_barrier();
+#pragma unroll
+        for (int j = 0; j < PF; ++j) fetch(rb[j], j);
+        lds_barrier();  // decay of step 0 written
+        gram(rb[0], 0);
+        lds_barrier();  // decay of step 1 written
+        for (int it = 0; it < nch; it += PF) {
+#pragma unroll
+            for (int j = 0; j < PF; ++j) {
+                if (it + j < nch) {
+                    if (it + j + 1 < nch) gram(rb[(j + 1) % PF], it + j + 1);
+                    lds_barrier();
+                }
+            }
         }
         return;
     }
 
-    // ---------------- consumers: wave w owns value columns slice NV + 16 w + [0, 16)
+    // ---------------- consumers: wave w owns value columns slice NV + 16 w + [0, 16) and
+    // decay piece w: row pr = lane & 15, channels pg CW + 8 w + [0, 8) (pg = lane >> 4)
     const int col = slice * NV + 16 * wave + r;
+    const int pr = lane & 15, pg = lane >> 4;
+    const int ch0 = pg * CW + 8 * wave;
+    const bool decays = wave < NP;
     float* const out = (rev ? a.dsc : a.states) + ((tbeg / kC + n) * H + h) * SS;
+    const T* const vsrc = rev ? a.dout : a.v;  // backwards: dO (times the gate)
+    struct Regs {
+        T v[4], g[4];               // V or dO, gate: rows 4g + i, column col
+        uint4 q[NWD], k[NWD], l[NWD];  // the decay piece
+    } R[PF];
+    // inputs of step it into x: the state step's values, and the decay piece of step it + 2
+    auto fetch = [&](Regs& x, int it) {
+        const int c = chunk_of(it);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t off = row_at(c, 4 * g + i) * rowv + (int64_t)h * DV + col;
+            x.v[i] = vsrc[off];
+            x.g[i] = a.gate[off];
+        }
+        if (decays) {
+            const int64_t off = row_at(chunk_of(it + 2), pr) * rowq + (int64_t)h * DK + ch0;
+#pragma unroll
+            for (int w = 0; w < NWD; ++w) {
+                x.q[w] = *reinterpret_cast<const uint4*>(a.q + off + 4 * w);
+                x.k[w] = *reinterpret_cast<const uint4*>(a.k + off + 4 * w);
+                x.l[w] = *reinterpret_cast<const uint4*>(a.la + off + 4 * w);
+            }
+        }
+    };
+    // decay-folded operands of step s from the raw piece in x, into buffer s % 3
+    auto decay = [&](const Regs& x, int s) {
+        if (!decays) return;
+        B& o = s_buf[s % 3];
+        const bool in = pr < rows_of(chunk_of(s));
+        float xq[8], xk[8], G[8];
+        unpack8<T>(x.q, xq);
+        unpack8<T>(x.k, xk);
+        unpack8<T>(x.l, G);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) G[i] = in ? fmaxf(G[i], a.floor_) : 0.f;
+        row_scan8(G);
+        float qt[8], kt[8], kb[8], gm[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float GC = row_last(G[i]);  // G of the chunk's last row
+            const float d = G[i] - GC;        // >= 0
+            const float e = __expf(d), ei = __expf(-d);
+            const float qv = in ? xq[i] : 0.f, kv = in ? xk[i] : 0.f;
+            gm[i] = __expf(GC);
+            qt[i] = a.scale * qv * e;
+            kt[i] = kv * e;
+            kb[i] = kv * ei;
+        }
+        const int off = pr * RSB + ch0;
+        store_split8(&o.kt[0][off], &o.kt[1][off], kt);
+        store_split8(&o.kb[0][off], &o.kb[1][off], kb);
+        if (rev) store_split8(&o.qt[0][off], &o.qt[1][off], qt);
+        if (pr == 15) store8(&o.gamma[ch0], gm);
+    };
     // X[b] holds rows 16b + 4g + i, column col of S (forwards) or dS (backwards)
     const float* init = rev ? a.dSf : a.S0;
     f32x4 X[KB];
@@ -341,76 +479,74 @@ __global__ __launch_bounds__(64 * (NCB + 1)) void walk_kernel(const WalkArgs<T> 
     for (int b = 0; b < KB; ++b)
 #pragma unroll
         for (int i = 0; i < 4; ++i) X[b][i] = init ? init[sbase + (16 * b + 4 * g + i) * DV + col] : 0.f;
-    if (nch > 0) {
-        const T* const vsrc = rev ? a.dout : a.v;  // backwards: dO (times the gate)
-        T rv[4], rg[4];
-        auto fetch = [&](int it) {
-            const int c = chunk_of(it);
+    auto step = [&](Regs& x, int it) {
+        const B& o = s_buf[it % 3];
+        const int c = chunk_of(it);
+        const int Cp = rows_of(c);
+        f32x4 in4;  // V (forwards) or dY = dO * gate (backwards), rows 4g + i, column col
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t off = row_at(c, 4 * g + i) * rowv + (int64_t)h * DV + col;
-                rv[i] = vsrc[off];
-                rg[i] = a.gate[off];
+        for (int i = 0; i < 4; ++i)
+            in4[i] = 4 * g + i < Cp ? (rev ? to_f32(x.v[i]) * to_f32(x.g[i]) : to_f32(x.v[i])) : 0.f;
+        float* dst = out + (int64_t)c * H * SS;
+#pragma unroll
+        for (int b = 0; b < KB; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[(16 * b + 4 * g + i) * DV + col] = X[b][i];
+        if (!rev) {  // S' = Diag(gamma) S;  U = T (V - Kt S');  S <- S' + Kb^T U
+            f32x4 KtS = zero4();
+#pragma unroll
+            for (int b = 0; b < KB; ++b) {
+                X[b] *= ld4(&o.gamma[16 * b + 4 * g]);
+                KtS = mma3(lds_split(&o.kt[0][fr + 16 * b], &o.kt[1][fr + 16 * b]), split4(X[b]), KtS);
             }
-        };
-        fetch(0);
-        lds_barrier();
-        for (int it = 0; it < nch; ++it) {
-            const int buf = it & 1;
-            const int c = chunk_of(it);
-            const int Cp = (int)min<int64_t>(kC, tend - tbeg - (int64_t)kC * c);
-            const float* Qh = s_Qh[buf];
-            const float* Kh = s_Kh[buf];
-            const float* Kc = s_Kc[buf];
-            const float* gm = s_gamma[buf];
-            f32x4 in4;  // V (forwards) or dY = dO * gate (backwards), rows 4g + i, column col
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                in4[i] = 4 * g + i < Cp ? (rev ? to_f32(rv[i]) * to_f32(rg[i]) : to_f32(rv[i])) : 0.f;
-            fetch(it + 1);
-            float* dst = out + (int64_t)c * H * SS;
+            const Split4 Rs = split4(in4 - KtS);
+            const Split4 Us = split4(mma3(lds_split(&o.sq1[0][fq], &o.sq1[1][fq]), Rs, zero4()));
 #pragma unroll
             for (int b = 0; b < KB; ++b)
+                X[b] = mma3(lds_split_tr(&o.kb[0][ft + 16 * b], &o.kb[1][ft + 16 * b]), Us, X[b]);
+        } else {  // dU = P^T dY + Kb dS_C;  dR = T^T dU;  dS = Diag(gamma) (dS_C + Qt^T dY - Kt^T dR)
+            const Split4 Ys = split4(in4);
+            f32x4 dU = mma3(lds_split(&o.sq1[0][fq], &o.sq1[1][fq]), Ys, zero4());
 #pragma unroll
-                for (int i = 0; i < 4; ++i) dst[(16 * b + 4 * g + i) * DV + col] = X[b][i];
-            __builtin_amdgcn_sched_barrier(0);
-            if (!rev) {  // U = T (V - Kh S);  S <- Diag(gamma) S + Kb^T U
-                f32x4 Rt = in4;
+            for (int b = 0; b < KB; ++b)
+                dU = mma3(lds_split(&o.kb[0][fr + 16 * b], &o.kb[1][fr + 16 * b]), split4(X[b]), dU);
+            const f32x4 dR = mma3(lds_split(&o.sq2[0][fq], &o.sq2[1][fq]), split4(dU), zero4());
+            const Split4 nRs = split4(-dR);
 #pragma unroll
-                for (int b = 0; b < KB; ++b)
-                    Rt = M::run(-ld4(&Kh[r * RS + 16 * b + 4 * g]), X[b], Rt);
-                const f32x4 U = M::run(ld4(&s_T[buf][r * kTS + 4 * g]), Rt, zero4());
-#pragma unroll
-                for (int b = 0; b < KB; ++b) {
-                    // A-fragment of Kb^T: Kb[4g + i][16b + r] = Kc[4g + i][16b + r] gamma[16b + r]
-                    const float gr = gm[16 * b + r];
-                    f32x4 kbt;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) kbt[i] = Kc[(4 * g + i) * RS + 16 * b + r] * gr;
-                    X[b] = M::run(kbt, U, X[b] * ld4(&gm[16 * b + 4 * g]));
-                }
-            } else {  // dU = P^T dY + Kb dS_C;  dR = T^T dU;  dS = Diag(gamma) dS_C + Qh^T dY - Kh^T dR
-                f32x4 dU = M::run(ld4_col(s_P[buf], r, g), in4, zero4());
-#pragma unroll
-                for (int b = 0; b < KB; ++b)
-                    dU = M::run(ld4(&Kc[r * RS + 16 * b + 4 * g]) * ld4(&gm[16 * b + 4 * g]), X[b], dU);
-                const f32x4 dR = M::run(ld4_col(s_T[buf], r, g), dU, zero4());
-#pragma unroll
-                for (int b = 0; b < KB; ++b) {
-                    f32x4 qt, kt;  // A-fragments of Qh^T and -Kh^T
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        qt[i] = Qh[(4 * g + i) * RS + 16 * b + r];
-                        kt[i] = -Kh[(4 * g + i) * RS + 16 * b + r];
-                    }
-                    f32x4 acc = X[b] * ld4(&gm[16 * b + 4 * g]);
-                    acc = M::run(qt, in4, acc);
-                    acc = M::run(kt, dR, acc);
-                    X[b] = acc;
-                }
+            for (int b = 0; b < KB; ++b) {
+                f32x4 acc = mma3(lds_split_tr(&o.qt[0][ft + 16 * b], &o.qt[1][ft + 16 * b]), Ys, X[b]);
+                acc = mma3(lds_split_tr(&o.kt[0][ft + 16 * b], &o.kt[1][ft + 16 * b]), nRs, acc);
+                X[b] = acc * ld4(&o.gamma[16 * b + 4 * g]);
             }
-            lds_barrier();
         }
+        decay(x, it + 2);
+        fetch(x, it + PF);
+        lds_barrier();
+    };
+    // prologue: the decay of steps 0 and 1 (their pieces are loaded here, not prefetched)
+#pragma unroll
+    for (int s0 = 0; s0 < 2; ++s0) {
+        Regs t;
+        if (decays) {
+            const int64_t off = row_at(chunk_of(s0), pr) * rowq + (int64_t)h * DK + ch0;
+#pragma unroll
+            for (int w = 0; w < NWD; ++w) {
+                t.q[w] = *reinterpret_cast<const uint4*>(a.q + off + 4 * w);
+                t.k[w] = *reinterpret_cast<const uint4*>(a.k + off + 4 * w);
+                t.l[w] = *reinterpret_cast<const uint4*>(a.la + off + 4 * w);
+            }
+        }
+        if (s0 == 0) {
+#pragma unroll
+            for (int j = 0; j < PF; ++j) fetch(R[j], j);
+        }
+        decay(t, s0);
+        lds_barrier();
+    }
+    for (int it = 0; it < nch; it += PF) {
+#pragma unroll
+        for (int j = 0; j < PF; ++j)
+            if (it + j < nch) step(R[j], it + j);
     }
     if (rev && a.dS0) {
 #pragma unroll
@@ -754,13 +890,9 @@ hipError_t launch_walk(const BackwardArgs& p, hipStream_t st) {
 template <typename T, int DK, int DV>
 hipError_t launch_typed(const BackwardArgs& p, hipStream_t st) {
     if (p.num_seqs == 0 || p.H == 0) return hipSuccess;
-    hipError_t e;
-    switch (p.nv) {
-        case 16: e = launch_walk<T, DK, DV, 1>(p, st); break;
-        case 32: e = launch_walk<T, DK, DV, 2>(p, st); break;
-        case 64: e = launch_walk<T, DK, DV, 4>(p, st); break;
-        default: return hipErrorInvalidValue;
-    }
+    // 64 value columns per workgroup: four consumer waves (the walk's double buffer takes
+    // ~100 KB of LDS, one workgroup per compute unit)
+    hipError_t e = launch_walk<T, DK, DV, 4>(p, st);
     if (e != hipSuccess || p.T_total == 0) return e;
     GradArgs<T> a;
     a.q = (const T*)p.q; a.k = (const T*)p.k; a.v = (const T*)p.v; a.la = (const T*)p.log_alpha;

@@ -87,7 +87,6 @@ struct BackwardArgs {
     float* workspace;                   // chunk-entering states, then chunk-leaving gradients
     int64_t grad_offset;                // floats: start of the chunk-leaving gradients
     int64_t T_total;
-    int nv;                             // value-slice width of the two sequential passes
 };
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream);
 
