@@ -82,6 +82,14 @@ __device__ __forceinline__ void unpack8(const uint4 (&w)[sizeof(T) / 2], float (
         }
     }
 }
+__device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[i] = a[i];
+        x[4 + i] = b[i];
+    }
+}
 __device__ __forceinline__ void store8(float* p, const float (&x)[8]) {
     *reinterpret_cast<f32x4*>(p) = f32x4{x[0], x[1], x[2], x[3]};
     *reinterpret_cast<f32x4*>(p + 4) = f32x4{x[4], x[5], x[6], x[7]};
@@ -614,12 +622,49 @@ __global__ __launch_bounds__(kThreads, 2) void grad_kernel(const GradArgs<T> a) 
     const float* Sin = a.states + ((int64_t)slot * H + h) * SS;
     const float* dSC = a.dsc + ((int64_t)slot * H + h) * SS;
 
-    if (tid < DK) {
-        float G[kC], GC;
-        uint32_t live;
-        chunk_decay<T, RS>(a.q, a.k, a.la, t0 * rowq + (int64_t)h * DK, rowq, Cp, tid, a.floor_,
-                           a.scale, G, live, GC, s_Qh, s_Kh, s_Kc);
-        s_gamma[tid] = __expf(GC);
+    // Per-channel decay, row layout: wave w < NPC takes lane (pr, pg) = (row, channel group)
+    // and channels ch0 = pg CW + 8 w + [0, 8), loaded as 16-byte pieces; the cumulative sum
+    // over rows runs across the 16 lanes of a row.  The wave keeps G of its piece for the
+    // last phase.
+    constexpr int CW = DK / 4, NPC = CW / 8, NWD = (int)sizeof(T) / 2;
+    const int pr = lane & 15, pg = lane >> 4;
+    const int ch0 = pg * CW + 8 * wave;
+    const bool rin = pr < Cp;
+    float Gp[8];
+    uint32_t livep = 0;
+    if (wave < NPC) {
+        const int64_t off = (t0 + min(pr, Cp - 1)) * rowq + (int64_t)h * DK + ch0;
+        uint4 wq[NWD], wk[NWD], wl[NWD];
+#pragma unroll
+        for (int w = 0; w < NWD; ++w) {
+            wq[w] = *reinterpret_cast<const uint4*>(a.q + off + 4 * w);
+            wk[w] = *reinterpret_cast<const uint4*>(a.k + off + 4 * w);
+            wl[w] = *reinterpret_cast<const uint4*>(a.la + off + 4 * w);
+        }
+        float xq[8], xk[8];
+        unpack8<T>(wq, xq);
+        unpack8<T>(wk, xk);
+        unpack8<T>(wl, Gp);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (rin && Gp[i] > a.floor_) livep |= 1u << i;
+            Gp[i] = rin ? fmaxf(Gp[i], a.floor_) : 0.f;
+        }
+        row_scan8(Gp);
+        float qh[8], kh[8], kc[8], gm[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float e = __expf(Gp[i]), ei = __expf(-Gp[i]);
+            const float qv = rin ? xq[i] : 0.f, kv = rin ? xk[i] : 0.f;
+            gm[i] = __expf(row_last(Gp[i]));
+            qh[i] = a.scale * qv * e;
+            kh[i] = kv * e;
+            kc[i] = kv * ei;
+        }
+        store8(&s_Qh[pr * RS + ch0], qh);
+        store8(&s_Kh[pr * RS + ch0], kh);
+        store8(&s_Kc[pr * RS + ch0], kc);
+        if (pr == 15) store8(&s_gamma[ch0], gm);
     }
     if (tid < kC) s_beta[tid] = tid < Cp ? to_f32(a.beta[(t0 + tid) * H + h]) : 0.f;
     lds_barrier();
@@ -741,7 +786,6 @@ __global__ __launch_bounds__(kThreads, 2) void grad_kernel(const GradArgs<T> a) 
 
     // ---- B: channel blocks (wave w takes blocks w, w + 4, ...): the sums over value columns
     f32x4 aQ[OWNC], aK[OWNC], aB[OWNC];
-    T rla[kC];  // log-decays of channel tid for the last phase, loaded ahead
 #pragma unroll
     for (int jc = 0; jc < OWNC; ++jc) {
         const int cb = wave + kNW * jc;
@@ -760,11 +804,6 @@ __global__ __launch_bounds__(kThreads, 2) void grad_kernel(const GradArgs<T> a) 
         dg += __shfl_xor(dg, 16);
         dg += __shfl_xor(dg, 32);
         if (g == 0) s_dgam[16 * cb + r] = dg;
-    }
-    if (tid < DK) {
-#pragma unroll
-        for (int rr = 0; rr < kC; ++rr)
-            rla[rr] = a.la[(t0 + min(rr, Cp - 1)) * rowq + (int64_t)h * DK + tid];
     }
     lds_barrier();
 
@@ -830,44 +869,50 @@ __global__ __launch_bounds__(kThreads, 2) void grad_kernel(const GradArgs<T> a) 
     }
     lds_barrier();
 
-    // ---- E: per channel -- dq, dk, and dlambda by the reverse cumsum of dG over the rows
-    if (tid < DK) {
-        const int ch = tid;
-        // the cumulative decay again (not kept in registers through the phases above)
-        float G[kC], GC = 0.f;
-        uint32_t live = 0;
+    // ---- E: dq, dk, and dlambda by the reverse cumulative sum of dG over the rows, in the
+    // decay's row layout (the 16 lanes of a row hold the chunk's rows of 8 channels)
+    if (wave < NPC) {
+        const int idx = pr * RS + ch0;
+        float qh[8], kh[8], kc[8], dqh[8], dkh[8], dkc[8], dkb[8], gm[8], dgm[8];
+        load8(&s_Qh[idx], qh);
+        load8(&s_Kh[idx], kh);
+        load8(&s_Kc[idx], kc);
+        load8(&s_big[idx], dqh);
+        load8(&s_big[kC * WS + idx], dkh);
+        load8(&s_big[2 * kC * WS + idx], dkc);
+        load8(&s_big[3 * kC * WS + idx], dkb);
+        load8(&s_gamma[ch0], gm);
+        load8(&s_dgam[ch0], dgm);
+        float dq8[8], dk8[8], dl8[8], kbs[8];
 #pragma unroll
-        for (int rr = 0; rr < kC; ++rr) {
-            const float lam = rr < Cp ? to_f32(rla[rr]) : 0.f;
-            if (rr < Cp && lam > a.floor_) live |= 1u << rr;
-            GC += rr < Cp ? fmaxf(lam, a.floor_) : 0.f;
-            G[rr] = GC;
+        for (int i = 0; i < 8; ++i) {
+            kbs[i] = kc[i] * gm[i] * dkb[i];  // Kb dKb
+            dl8[i] = qh[i] * dqh[i] + kh[i] * dkh[i] - kc[i] * dkc[i] - kbs[i];  // dG
+            const float e = __expf(Gp[i]), ei = __expf(-Gp[i]);
+            dq8[i] = a.scale * e * dqh[i];
+            dk8[i] = e * dkh[i] + ei * dkc[i] + gm[i] * ei * dkb[i];
         }
-        const float gam = s_gamma[ch];
-        float dGC = gam * s_dgam[ch];
-        float dG[kC];
+        // G_C is the last row's G (padding rows add no decay): row 15 also takes the gradient
+        // reaching G_C, the sum over rows of Kb dKb plus gamma dgamma
+        row_scan8(kbs);
+        float inc[8];
 #pragma unroll
-        for (int rr = 0; rr < kC; ++rr) {
-            const int idx = rr * RS + ch;
-            const float qh = s_Qh[idx], kh = s_Kh[idx], kc = s_Kc[idx], kb = kc * gam;
-            const float dqh = s_big[idx], dkh = s_big[kC * WS + idx];
-            const float dkc = s_big[2 * kC * WS + idx], dkb = s_big[3 * kC * WS + idx];
-            dG[rr] = qh * dqh + kh * dkh - kc * dkc - kb * dkb;
-            dGC += kb * dkb;
-            if (rr < Cp) {
-                const float e = __expf(G[rr]), ei = __expf(-G[rr]), eb = __expf(GC - G[rr]);
-                const int64_t off = (t0 + rr) * rowq + (int64_t)h * DK + ch;
-                a.dq[off] = a.scale * e * dqh;
-                a.dk[off] = e * dkh + ei * dkc + eb * dkb;
-            }
+        for (int i = 0; i < 8; ++i) {
+            const float tot_kb = row_last(kbs[i]);
+            if (pr == 15) dl8[i] += tot_kb + gm[i] * dgm[i];
+            inc[i] = dl8[i];
         }
-        dG[kC - 1] += dGC;  // G_C is the last row's G (padding rows add no decay)
-        float acc = 0.f;
+        row_scan8(inc);  // inclusive sums over rows <= pr
 #pragma unroll
-        for (int rr = kC - 1; rr >= 0; --rr) {
-            acc += dG[rr];
-            if (rr < Cp)
-                a.dla[(t0 + rr) * rowq + (int64_t)h * DK + ch] = (live >> rr) & 1u ? acc : 0.f;
+        for (int i = 0; i < 8; ++i) {
+            const float rev = row_last(inc[i]) - inc[i] + dl8[i];  // sum over rows >= pr
+            dl8[i] = (livep >> i) & 1u ? rev : 0.f;
+        }
+        if (rin) {
+            const int64_t off = (t0 + pr) * rowq + (int64_t)h * DK + ch0;
+            store8(a.dq + off, dq8);
+            store8(a.dk + off, dk8);
+            store8(a.dla + off, dl8);
         }
     }
     if (tid < Cp) a.dbeta[(t0 + tid) * H + h] = s_dbT[tid] + s_dbA[tid];
