@@ -310,7 +310,7 @@ def main() -> int:
         result["backward"] = {
             "workload": w.name, "steps": args.backward_steps, "ms_per_step": bms,
             "tokens_per_s": T_total / (bms * 1e-3), "vs_forward": bms / ms,
-            "note": "chunked, fp32 MFMA: forward and reverse chunk walks in one launch, then all chunks in parallel",
+            "note": "chunk form, fp32 state and sums: forward and reverse chunk walks in one launch (split-bf16 products), then all chunks in parallel (fp32 MFMA)",
         }
         del bws, dout
         torch.cuda.empty_cache()

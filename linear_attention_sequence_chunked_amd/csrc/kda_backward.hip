@@ -33,7 +33,9 @@
 //   2. grad_kernel takes one (chunk, head) per workgroup -- all chunks in parallel -- and
 //      forms every input gradient of the chunk from its entering state and leaving
 //      gradient.
-// Everything is fp32 (v_mfma_f32_16x16x4_f32), whatever the input dtype.
+// Whatever the input dtype, the state, its gradient and every sum are fp32: the walks'
+// products are split-bf16 (three bf16 MFMAs per product, relative error ~2^-17), the
+// gradient kernel's are fp32 MFMAs (v_mfma_f32_16x16x4_f32).
 #include <math.h>
 
 #include "kda_device.h"
@@ -118,38 +120,6 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-// Per-channel cumulative log-decay of one chunk and the decay-folded operands.  Thread ch
-// (< DK) owns channel ch: it keeps G (16 rows) and a bit mask of the rows with lambda > floor.
-template <typename T, int RS>
-__device__ __forceinline__ void chunk_decay(const T* __restrict__ q, const T* __restrict__ k,
-                                            const T* __restrict__ la, int64_t base, int64_t rowq,
-                                            int Cp, int ch, float floor_, float scale,
-                                            float (&G)[kC], uint32_t& live, float& GC,
-                                            float* s_Qh, float* s_Kh, float* s_Kc) {
-    float qv[kC], kv[kC];
-    float acc = 0.f;
-    live = 0;
-#pragma unroll
-    for (int rr = 0; rr < kC; ++rr) {
-        const bool in = rr < Cp;
-        const int64_t off = base + rr * rowq + ch;
-        const float lam = in ? to_f32(la[off]) : 0.f;
-        qv[rr] = in ? to_f32(q[off]) : 0.f;
-        kv[rr] = in ? to_f32(k[off]) : 0.f;
-        if (in && lam > floor_) live |= 1u << rr;
-        acc += in ? fmaxf(lam, floor_) : 0.f;
-        G[rr] = acc;
-    }
-    GC = acc;
-#pragma unroll
-    for (int rr = 0; rr < kC; ++rr) {
-        const float e = __expf(G[rr]), ei = __expf(-G[rr]);
-        s_Qh[rr * RS + ch] = scale * qv[rr] * e;
-        s_Kh[rr * RS + ch] = kv[rr] * e;
-        s_Kc[rr * RS + ch] = kv[rr] * ei;
-    }
 }
 
 // Gram products of the chunk (wave 0: A', wave 1: P), then X and T by forward substitution.
