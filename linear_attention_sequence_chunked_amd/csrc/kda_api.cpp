@@ -549,10 +549,11 @@ kda_status bwd_size(const kda_params* params, const int32_t* cu, int32_t N, uint
             return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens_host decreases at index %d", n + 1);
     const uint64_t H = params->num_heads, ss = (uint64_t)params->dk * params->dv;
     // the state entering chunk c of sequence n at slot cu[n]/16 + n + c (at most
-    // T_total/16 + N slots), then the gradient leaving the chunk at the same slot
+    // T_total/16 + N slots), then the gradient leaving the chunk at the same slot, then
+    // four [16][dv] arrays per slot (R, Y, dU, dR of the chunk)
     const uint64_t slots = (uint64_t)cu[N] / 16 + N;
     grad_off = slots * H * ss;
-    bytes = 4 * 2 * grad_off;
+    bytes = 4 * (2 * grad_off + 4 * slots * H * 16 * (uint64_t)params->dv);
     return KDA_OK;
 }
 

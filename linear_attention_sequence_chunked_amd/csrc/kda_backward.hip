@@ -122,14 +122,14 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Gram products of the chunk (wave 0: A', wave 1: P), then X and T by forward substitution.
-// s_A receives A' (unscaled, strict lower); s_X may be null.
+// Gram products of the chunk (wave 0: A', wave 1: P unless s_P is null), then X and T by
+// forward substitution.  s_A receives A' (unscaled, strict lower); s_X may be null.
 template <int DK, int RS>
 __device__ __forceinline__ void chunk_gram(const float* s_Qh, const float* s_Kh, const float* s_Kc,
                                            const float* s_beta, float* s_A, float* s_P, float* s_X,
                                            float* s_T, int wave, int lane) {
     const int r = lane & 15, g = lane >> 4;
-    if (wave < 2) {
+    if (wave == 0 || (wave == 1 && s_P)) {
         const float* L = wave == 0 ? s_Kh : s_Qh;
         f32x4 acc = zero4();
 #pragma unroll
@@ -174,6 +174,8 @@ struct WalkArgs {
     float* dS0;         // gradient of the initial state, or null
     float* states;      // state entering chunk c of sequence n: slot cu[n]/16 + n + c
     float* dsc;         // gradient leaving chunk c of sequence n: same slot
+    float* aux;         // per slot [16][dv] rows: R, Y (forwards), dU, dR (backwards)
+    int64_t aux_stride; // floats between those four arrays
     int H, n_slices, half;
     float floor_, scale;
 };
@@ -190,7 +192,7 @@ struct WalkArgs {
 // Operands relative to the chunk's end (as in the forward): Kt = k e^(G - G_C),
 // Qt = (scale q) e^(G - G_C), Kb = k e^(G_C - G).  Then A' = strict_lower(Kt Kb^T),
 // P = lower_incl_diag(Qt Kb^T), and with S' = Diag(gamma) S:
-//   forwards   U = T (V - Kt S'),   S <- S' + Kb^T U
+//   forwards   R = V - Kt S',  U = T R,  Y = Qt S' + P U,  S <- S' + Kb^T U
 //   backwards  dU = P^T dY + Kb dS_C,  dR = T^T dU,  dS <- Diag(gamma) (dS_C + Qt^T dY - Kt^T dR)
 //
 // All products are split-bf16: x = hi + lo with hi = bf16(x), lo = bf16(x - hi), and
@@ -206,9 +208,9 @@ struct alignas(16) WalkBuf {
     static constexpr int TSB = 16 + 8;  // bf16 row stride of 16x16 tiles
     bf16 kt[2][16 * RSB];               // [hi, lo] Kt
     bf16 kb[2][16 * RSB];               // Kb
-    bf16 qt[2][16 * RSB];               // Qt (backwards only)
+    bf16 qt[2][16 * RSB];               // Qt
     bf16 sq1[2][16 * TSB];              // T (forwards) or P^T (backwards)
-    bf16 sq2[2][16 * TSB];              // T^T (backwards)
+    bf16 sq2[2][16 * TSB];              // P (forwards) or T^T (backwards)
     float gamma[DK];
 };
 
@@ -323,20 +325,28 @@ __global__ __launch_bounds__(64 * (NCB + 1)) void walk_kernel(const WalkArgs<T> 
             for (int kb = 0; kb < KB; ++kb) {
                 const Split4 kbf = lds_split(&o.kb[0][fr + 16 * kb], &o.kb[1][fr + 16 * kb]);
                 accA = mma3(lds_split(&o.kt[0][fr + 16 * kb], &o.kt[1][fr + 16 * kb]), kbf, accA);
-                if (rev) accP = mma3(lds_split(&o.qt[0][fr + 16 * kb], &o.qt[1][fr + 16 * kb]), kbf, accP);
+                accP = mma3(lds_split(&o.qt[0][fr + 16 * kb], &o.qt[1][fr + 16 * kb]), kbf, accP);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 4 * g + i;
                 s_A[row * kTS + r] = r < row ? accA[i] : 0.f;
             }
-            if (rev) {  // P^T[r][4g + i] = P[4g + i][r]: lane (r, g) holds it already
+            {  // lane (r, g) holds P[4g + i][r]
                 f32x4 pm;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) pm[i] = r <= 4 * g + i ? accP[i] : 0.f;
                 const Split4 ps = split4(pm);
-                *reinterpret_cast<bf16x4*>(&o.sq1[0][fq]) = ps.h;
-                *reinterpret_cast<bf16x4*>(&o.sq1[1][fq]) = ps.l;
+                if (rev) {  // P^T, row-major: P^T[r][4g + i]
+                    *reinterpret_cast<bf16x4*>(&o.sq1[0][fq]) = ps.h;
+                    *reinterpret_cast<bf16x4*>(&o.sq1[1][fq]) = ps.l;
+                } else {  // P, row-major: P[4g + i][r]
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        o.sq2[0][(4 * g + i) * TSB + r] = ps.h[i];
+                        o.sq2[1][(4 * g + i) * TSB + r] = ps.l[i];
+                    }
+                }
             }
             wave_lds_sync();
             if (lane < 16) {  // column `lane` of X = (I + Diag(beta) A')^-1, then T = X Diag(beta)
@@ -396,6 +406,7 @@ __global__ __launch_bounds__(64 * (NCB + 1)) void walk_kernel(const WalkArgs<T> 
     const int ch0 = pg * CW + 8 * wave;
     const bool decays = wave < NP;
     float* const out = (rev ? a.dsc : a.states) + ((tbeg / kC + n) * H + h) * SS;
+    const int64_t aslot = (tbeg / kC + n) * H + h;  // (slot, head) row of chunk 0
     const T* const vsrc = rev ? a.dout : a.v;  // backwards: dO (times the gate)
     struct Regs {
         T v[4], g[4];               // V or dO, gate: rows 4g + i, column col
@@ -447,7 +458,7 @@ __global__ __launch_bounds__(64 * (NCB + 1)) void walk_kernel(const WalkArgs<T> 
         const int off = pr * RSB + ch0;
         store_split8(&o.kt[0][off], &o.kt[1][off], kt);
         store_split8(&o.kb[0][off], &o.kb[1][off], kb);
-        if (rev) store_split8(&o.qt[0][off], &o.qt[1][off], qt);
+        store_split8(&o.qt[0][off], &o.qt[1][off], qt);
         if (pr == 15) store8(&o.gamma[ch0], gm);
     };
     // X[b] holds rows 16b + 4g + i, column col of S (forwards) or dS (backwards)
@@ -470,15 +481,26 @@ __global__ __launch_bounds__(64 * (NCB + 1)) void walk_kernel(const WalkArgs<T> 
         for (int b = 0; b < KB; ++b)
 #pragma unroll
             for (int i = 0; i < 4; ++i) dst[(16 * b + 4 * g + i) * DV + col] = X[b][i];
-        if (!rev) {  // S' = Diag(gamma) S;  U = T (V - Kt S');  S <- S' + Kb^T U
-            f32x4 KtS = zero4();
+        // rows 4g + i, column col of this chunk's [16][dv] vectors for the gradient kernel
+        float* const ax = a.aux + (rev ? 2 : 0) * a.aux_stride + (aslot + (int64_t)c * H) * kC * DV +
+                          (4 * g) * DV + col;
+        auto put = [&](float* p, f32x4 x) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) p[i * DV] = x[i];
+        };
+        if (!rev) {  // S' = Diag(gamma) S;  R = V - Kt S';  U = T R;  Y = Qt S' + P U;  S <- S' + Kb^T U
+            f32x4 KtS = zero4(), QtS = zero4();
 #pragma unroll
             for (int b = 0; b < KB; ++b) {
                 X[b] *= ld4(&o.gamma[16 * b + 4 * g]);
-                KtS = mma3(lds_split(&o.kt[0][fr + 16 * b], &o.kt[1][fr + 16 * b]), split4(X[b]), KtS);
+                const Split4 xs = split4(X[b]);
+                KtS = mma3(lds_split(&o.kt[0][fr + 16 * b], &o.kt[1][fr + 16 * b]), xs, KtS);
+                QtS = mma3(lds_split(&o.qt[0][fr + 16 * b], &o.qt[1][fr + 16 * b]), xs, QtS);
             }
-            const Split4 Rs = split4(in4 - KtS);
-            const Split4 Us = split4(mma3(lds_split(&o.sq1[0][fq], &o.sq1[1][fq]), Rs, zero4()));
+            const f32x4 Rv = in4 - KtS;
+            const Split4 Us = split4(mma3(lds_split(&o.sq1[0][fq], &o.sq1[1][fq]), split4(Rv), zero4()));
+            put(ax, Rv);
+            put(ax + a.aux_stride, mma3(lds_split(&o.sq2[0][fq], &o.sq2[1][fq]), Us, QtS));
 #pragma unroll
             for (int b = 0; b < KB; ++b)
                 X[b] = mma3(lds_split_tr(&o.kb[0][ft + 16 * b], &o.kb[1][ft + 16 * b]), Us, X[b]);
@@ -489,6 +511,8 @@ __global__ __launch_bounds__(64 * (NCB + 1)) void walk_kernel(const WalkArgs<T> 
             for (int b = 0; b < KB; ++b)
                 dU = mma3(lds_split(&o.kb[0][fr + 16 * b], &o.kb[1][fr + 16 * b]), split4(X[b]), dU);
             const f32x4 dR = mma3(lds_split(&o.sq2[0][fq], &o.sq2[1][fq]), split4(dU), zero4());
+            put(ax, dU);
+            put(ax + a.aux_stride, dR);
             const Split4 nRs = split4(-dR);
 #pragma unroll
             for (int b = 0; b < KB; ++b) {
@@ -542,6 +566,8 @@ struct GradArgs {
     const int32_t* cu;
     const float* states;  // state entering chunk c of sequence n: slot cu[n]/16 + n + c
     const float* dsc;     // gradient leaving chunk c of sequence n: same slot
+    const float* aux;     // per slot [16][dv]: R, Y, dU, dR, aux_stride floats apart
+    int64_t aux_stride;
     float *dq, *dk, *dv, *dla, *dbeta, *dgate;
     int H, N;
     float floor_, scale;
@@ -638,32 +664,30 @@ __global__ __launch_bounds__(kThreads, 2) void grad_kernel(const GradArgs<T> a) 
     }
     if (tid < kC) s_beta[tid] = tid < Cp ? to_f32(a.beta[(t0 + tid) * H + h]) : 0.f;
     lds_barrier();
-    // Global operands of one value block -- rows 16b + 4g + i, column 16 vb + r of S and
-    // dS_C; rows 4g + i of V, dO and the gate -- loaded ahead of their use.  Rows past the
-    // end of the sequence re-read its last row and are masked where used.
+    // Global operands of one value block, rows 4g + i, column 16 vb + r: the walks' R, Y
+    // (forwards) and dU, dR (backwards) of this chunk, dO and the gate -- loaded ahead of
+    // their use.  Rows past the end of the sequence re-read its last row and are masked.
     constexpr int NA = VB / kNW;  // value blocks per wave
-    f32x4 S1[KB], D1[KB];
-    T rv[4], rdo[4], rgt[4];
+    const float* const ax = a.aux + ((int64_t)slot * H + h) * kC * DV;
+    f32x4 Rv, Yv, dUv, dRv;
+    T rdo[4], rgt[4];
     auto loadA = [&](int vb) {
         const int col = 16 * vb + r;
 #pragma unroll
-        for (int b = 0; b < KB; ++b)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                S1[b][i] = Sin[(16 * b + 4 * g + i) * DV + col];
-                D1[b][i] = dSC[(16 * b + 4 * g + i) * DV + col];
-            }
-#pragma unroll
         for (int i = 0; i < 4; ++i) {
+            const int64_t o = (int64_t)(4 * g + i) * DV + col;
+            Rv[i] = ax[o];
+            Yv[i] = ax[a.aux_stride + o];
+            dUv[i] = ax[2 * a.aux_stride + o];
+            dRv[i] = ax[3 * a.aux_stride + o];
             const int64_t off = (t0 + min(4 * g + i, Cp - 1)) * rowv + (int64_t)h * DV + col;
-            rv[i] = a.v[off];
             rdo[i] = a.dout[off];
             rgt[i] = a.gate[off];
         }
     };
     loadA(wave);
-    __builtin_amdgcn_sched_barrier(0);  // in flight during the Gram products and T
-    chunk_gram<DK, RS>(s_Qh, s_Kh, s_Kc, s_beta, s_A, s_P, s_X, s_T, wave, lane);
+    __builtin_amdgcn_sched_barrier(0);  // in flight during the Gram product and T
+    chunk_gram<DK, RS>(s_Qh, s_Kh, s_Kc, s_beta, s_A, nullptr, s_X, s_T, wave, lane);
 
     // S and dS_C of one channel block, read along rows (B-fragments of S^T over each value
     // block), for the sums over value columns
@@ -679,8 +703,7 @@ __global__ __launch_bounds__(kThreads, 2) void grad_kernel(const GradArgs<T> a) 
 
     // ---- A: value blocks (wave w takes blocks w, w + 4, ...)
     {
-        const f32x4 Tr = ld4(&s_T[r * kTS + 4 * g]), Pr = ld4(&s_P[r * kTS + 4 * g]);
-        const f32x4 PT = ld4_col(s_P, r, g), TT = ld4_col(s_T, r, g);
+        const f32x4 Tr = ld4(&s_T[r * kTS + 4 * g]);
         float* const sR = s_wv[wave][0];
         float* const sdU = s_wv[wave][1];
         f32x4 dTw = zero4(), dPw = zero4();
@@ -688,33 +711,19 @@ __global__ __launch_bounds__(kThreads, 2) void grad_kernel(const GradArgs<T> a) 
         for (int ia = 0; ia < NA; ++ia) {
             const int vb = wave + kNW * ia;
             const int col = 16 * vb + r;
-            f32x4 KhS = zero4(), QhS = zero4();
-#pragma unroll
-            for (int b = 0; b < KB; ++b) {
-                KhS = M::run(ld4(&s_Kh[r * RS + 16 * b + 4 * g]), S1[b], KhS);
-                QhS = M::run(ld4(&s_Qh[r * RS + 16 * b + 4 * g]), S1[b], QhS);
-            }
-            f32x4 Rt, dO, gt;
+            f32x4 dO, gt;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const bool in = 4 * g + i < Cp;
-                Rt[i] = (in ? to_f32(rv[i]) : 0.f) - KhS[i];
                 dO[i] = in ? to_f32(rdo[i]) : 0.f;
                 gt[i] = in ? to_f32(rgt[i]) : 0.f;
             }
-            const f32x4 U = M::run(Tr, Rt, zero4());
-            const f32x4 Y = M::run(Pr, U, QhS);
-            const f32x4 dY = dO * gt;
-            f32x4 dU = M::run(PT, dY, zero4());
-#pragma unroll
-            for (int b = 0; b < KB; ++b) {
-                const f32x4 gam = ld4(&s_gamma[16 * b + 4 * g]);
-                dU = M::run(ld4(&s_Kc[r * RS + 16 * b + 4 * g]) * gam, D1[b], dU);  // Kb dS_C
-            }
+            const f32x4 Rt = Rv, Y = Yv, dU = dUv, dR = dRv;
             if (ia + 1 < NA) loadA(vb + kNW);
             else loadB(wave);
             __builtin_amdgcn_sched_barrier(0);
-            const f32x4 dR = M::run(TT, dU, zero4());
+            const f32x4 U = M::run(Tr, Rt, zero4());
+            const f32x4 dY = dO * gt;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 4 * g + i;
@@ -895,6 +904,8 @@ hipError_t launch_walk(const BackwardArgs& p, hipStream_t st) {
     a.beta = (const T*)p.beta; a.gate = (const T*)p.gate; a.dout = (const T*)p.d_out;
     a.cu = p.cu_seqlens; a.S0 = p.initial_state; a.dSf = p.d_final_state;
     a.dS0 = p.d_initial_state; a.states = p.workspace; a.dsc = p.workspace + p.grad_offset;
+    a.aux = p.workspace + 2 * p.grad_offset;
+    a.aux_stride = (p.grad_offset / ((int64_t)DK * DV)) * kC * DV;
     a.H = p.H; a.n_slices = DV / (16 * NCB); a.floor_ = p.floor_; a.scale = p.scale;
     a.half = p.num_seqs * p.H * a.n_slices;
     hipLaunchKernelGGL((walk_kernel<T, DK, DV, NCB>), dim3(2u * (unsigned)a.half),
@@ -913,6 +924,8 @@ hipError_t launch_typed(const BackwardArgs& p, hipStream_t st) {
     a.q = (const T*)p.q; a.k = (const T*)p.k; a.v = (const T*)p.v; a.la = (const T*)p.log_alpha;
     a.beta = (const T*)p.beta; a.gate = (const T*)p.gate; a.dout = (const T*)p.d_out;
     a.cu = p.cu_seqlens; a.states = p.workspace; a.dsc = p.workspace + p.grad_offset;
+    a.aux = p.workspace + 2 * p.grad_offset;
+    a.aux_stride = (p.grad_offset / ((int64_t)DK * DV)) * kC * DV;
     a.dq = p.dq; a.dk = p.dk_; a.dv = p.dv_; a.dla = p.dlog_alpha; a.dbeta = p.dbeta;
     a.dgate = p.dgate; a.H = p.H; a.N = p.num_seqs; a.floor_ = p.floor_; a.scale = p.scale;
     const int64_t slots = p.T_total / kC + p.num_seqs;
