@@ -196,8 +196,8 @@ struct WalkArgs {
 //   backwards  dU = P^T dY + Kb dS_C,  dR = T^T dU,  dS <- Diag(gamma) (dS_C + Qt^T dY - Kt^T dR)
 //
 // All products are split-bf16: x = hi + lo with hi = bf16(x), lo = bf16(x - hi), and
-// a b = ah bh + ah bl + al bh (three v_mfma_f32_16x16x16_bf16, relative error ~2^-17) in
-// place of four 32-cycle fp32 MFMAs.  The key-side operands are stored already split,
+// a b = ah bh + ah bl + al bh (relative error ~2^-17), in place of four 32-cycle fp32 MFMAs
+// per 16-deep product.  The key-side operands are stored already split,
 // row-major (token rows); operands that contract over the key channels are read back
 // transposed with ds_read_b64_tr_b16: within each 16-lane group, with lane 16g + 4j + q
 // pointing at row 4g + j, columns c0 + 4q .. +3 of a row-major tile X, lane (r, g) receives
@@ -236,11 +236,28 @@ __device__ __forceinline__ bf16x4 lds_tr(const bf16* p) {
     return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(const_cast<bf16*>(p))));
 }
 __device__ __forceinline__ Split4 lds_split_tr(const bf16* hi, const bf16* lo) { return Split4{lds_tr(hi), lds_tr(lo)}; }
-// c + a b, both split: three bf16 MFMAs
+// The products use the 32-deep v_mfma_f32_16x16x32_bf16, which issues at the cost of the
+// 16-deep form; a 32-deep step pairs element j of the A operand with element j of the B
+// operand on each lane, so two 16-deep operands stack into one.  Every accumulator is fed
+// by this one instruction shape only.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
+    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// c + a b, both split (ah bh + al bh + ah bl): two 32-deep MFMAs
 __device__ __forceinline__ f32x4 mma3(const Split4& a, const Split4& b, f32x4 c) {
-    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.l, b.h, c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.h, b.l, c, 0, 0, 0);
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.h, b.h, c, 0, 0, 0);
+    c = mfma32(cat8(a.h, a.h), cat8(b.l, bf16x4{}), c);
+    return mfma32(cat8(a.h, a.l), cat8(b.h, b.h), c);
+}
+// c + a0 b0 + a1 b1, all split: three 32-deep MFMAs
+__device__ __forceinline__ f32x4 mma3x2(const Split4& a0, const Split4& a1, const Split4& b0,
+                                        const Split4& b1, f32x4 c) {
+    c = mfma32(cat8(a0.l, a1.l), cat8(b0.h, b1.h), c);
+    c = mfma32(cat8(a0.h, a1.h), cat8(b0.l, b1.l), c);
+    return mfma32(cat8(a0.h, a1.h), cat8(b0.h, b1.h), c);
 }
 // eight floats, split, to 16-byte hi and lo pieces at the same offset of two tiles
 __device__ __forceinline__ void store_split8(bf16* hi, bf16* lo, const float (&x)[8]) {
@@ -322,10 +339,14 @@ __global__ __launch_bounds__(64 * (NCB + 1)) void walk_kernel(const WalkArgs<T> 
             // A' = strict_lower(Kt Kb^T) and P = lower_incl_diag(Qt Kb^T)
             f32x4 accA = zero4(), accP = zero4();
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                const Split4 kbf = lds_split(&o.kb[0][fr + 16 * kb], &o.kb[1][fr + 16 * kb]);
-                accA = mma3(lds_split(&o.kt[0][fr + 16 * kb], &o.kt[1][fr + 16 * kb]), kbf, accA);
-                accP = mma3(lds_split(&o.qt[0][fr + 16 * kb], &o.qt[1][fr + 16 * kb]), kbf, accP);
+            for (int kb = 0; kb < KB; kb += 2) {
+                const int f0 = fr + 16 * kb, f1 = f0 + 16;
+                const Split4 kb0 = lds_split(&o.kb[0][f0], &o.kb[1][f0]);
+                const Split4 kb1 = lds_split(&o.kb[0][f1], &o.kb[1][f1]);
+                accA = mma3x2(lds_split(&o.kt[0][f0], &o.kt[1][f0]), lds_split(&o.kt[0][f1], &o.kt[1][f1]),
+                              kb0, kb1, accA);
+                accP = mma3x2(lds_split(&o.qt[0][f0], &o.qt[1][f0]), lds_split(&o.qt[0][f1], &o.qt[1][f1]),
+                              kb0, kb1, accP);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -491,11 +512,15 @@ __global__ __launch_bounds__(64 * (NCB + 1)) void walk_kernel(const WalkArgs<T> 
         if (!rev) {  // S' = Diag(gamma) S;  R = V - Kt S';  U = T R;  Y = Qt S' + P U;  S <- S' + Kb^T U
             f32x4 KtS = zero4(), QtS = zero4();
 #pragma unroll
-            for (int b = 0; b < KB; ++b) {
+            for (int b = 0; b < KB; b += 2) {
+                const int f0 = fr + 16 * b, f1 = f0 + 16;
                 X[b] *= ld4(&o.gamma[16 * b + 4 * g]);
-                const Split4 xs = split4(X[b]);
-                KtS = mma3(lds_split(&o.kt[0][fr + 16 * b], &o.kt[1][fr + 16 * b]), xs, KtS);
-                QtS = mma3(lds_split(&o.qt[0][fr + 16 * b], &o.qt[1][fr + 16 * b]), xs, QtS);
+                X[b + 1] *= ld4(&o.gamma[16 * b + 16 + 4 * g]);
+                const Split4 x0 = split4(X[b]), x1 = split4(X[b + 1]);
+                KtS = mma3x2(lds_split(&o.kt[0][f0], &o.kt[1][f0]), lds_split(&o.kt[0][f1], &o.kt[1][f1]),
+                             x0, x1, KtS);
+                QtS = mma3x2(lds_split(&o.qt[0][f0], &o.qt[1][f0]), lds_split(&o.qt[0][f1], &o.qt[1][f1]),
+                             x0, x1, QtS);
             }
             const f32x4 Rv = in4 - KtS;
             const Split4 Us = split4(mma3(lds_split(&o.sq1[0][fq], &o.sq1[1][fq]), split4(Rv), zero4()));
@@ -508,16 +533,20 @@ __global__ __launch_bounds__(64 * (NCB + 1)) void walk_kernel(const WalkArgs<T> 
             const Split4 Ys = split4(in4);
             f32x4 dU = mma3(lds_split(&o.sq1[0][fq], &o.sq1[1][fq]), Ys, zero4());
 #pragma unroll
-            for (int b = 0; b < KB; ++b)
-                dU = mma3(lds_split(&o.kb[0][fr + 16 * b], &o.kb[1][fr + 16 * b]), split4(X[b]), dU);
+            for (int b = 0; b < KB; b += 2) {
+                const int f0 = fr + 16 * b, f1 = f0 + 16;
+                dU = mma3x2(lds_split(&o.kb[0][f0], &o.kb[1][f0]), lds_split(&o.kb[0][f1], &o.kb[1][f1]),
+                            split4(X[b]), split4(X[b + 1]), dU);
+            }
             const f32x4 dR = mma3(lds_split(&o.sq2[0][fq], &o.sq2[1][fq]), split4(dU), zero4());
             put(ax, dU);
             put(ax + a.aux_stride, dR);
             const Split4 nRs = split4(-dR);
 #pragma unroll
             for (int b = 0; b < KB; ++b) {
-                f32x4 acc = mma3(lds_split_tr(&o.qt[0][ft + 16 * b], &o.qt[1][ft + 16 * b]), Ys, X[b]);
-                acc = mma3(lds_split_tr(&o.kt[0][ft + 16 * b], &o.kt[1][ft + 16 * b]), nRs, acc);
+                const f32x4 acc = mma3x2(lds_split_tr(&o.qt[0][ft + 16 * b], &o.qt[1][ft + 16 * b]),
+                                         lds_split_tr(&o.kt[0][ft + 16 * b], &o.kt[1][ft + 16 * b]),
+                                         Ys, nRs, X[b]);
                 X[b] = acc * ld4(&o.gamma[16 * b + 4 * g]);
             }
         }
