@@ -122,24 +122,21 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Gram products of the chunk (wave 0: A', wave 1: P unless s_P is null), then X and T by
-// forward substitution.  s_A receives A' (unscaled, strict lower); s_X may be null.
+// A' = strict_lower(Kh Kc^T) of the chunk (wave 0), then X and T by forward substitution.
 template <int DK, int RS>
-__device__ __forceinline__ void chunk_gram(const float* s_Qh, const float* s_Kh, const float* s_Kc,
-                                           const float* s_beta, float* s_A, float* s_P, float* s_X,
+__device__ __forceinline__ void chunk_gram(const float* s_Kh, const float* s_Kc,
+                                           const float* s_beta, float* s_A, float* s_X,
                                            float* s_T, int wave, int lane) {
     const int r = lane & 15, g = lane >> 4;
-    if (wave == 0 || (wave == 1 && s_P)) {
-        const float* L = wave == 0 ? s_Kh : s_Qh;
+    if (wave == 0) {
         f32x4 acc = zero4();
 #pragma unroll
         for (int kb = 0; kb < DK / 16; ++kb)
-            acc = M::run(ld4(&L[r * RS + 16 * kb + 4 * g]), ld4(&s_Kc[r * RS + 16 * kb + 4 * g]), acc);
+            acc = M::run(ld4(&s_Kh[r * RS + 16 * kb + 4 * g]), ld4(&s_Kc[r * RS + 16 * kb + 4 * g]), acc);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int row = 4 * g + i;  // acc[i] = (L Kc^T)[row][r]
-            if (wave == 0) s_A[row * kTS + r] = r < row ? acc[i] : 0.f;
-            else s_P[row * kTS + r] = r <= row ? acc[i] : 0.f;
+            const int row = 4 * g + i;  // acc[i] = (Kh Kc^T)[row][r]
+            s_A[row * kTS + r] = r < row ? acc[i] : 0.f;
         }
     }
     lds_barrier();
@@ -156,7 +153,7 @@ __device__ __forceinline__ void chunk_gram(const float* s_Qh, const float* s_Kh,
         const float bc = s_beta[col];
 #pragma unroll
         for (int i = 0; i < kC; ++i) {
-            if (s_X) s_X[i * kTS + col] = x[i];
+            s_X[i * kTS + col] = x[i];
             s_T[i * kTS + col] = x[i] * bc;
         }
     }
@@ -588,7 +585,7 @@ __global__ __launch_bounds__(64 * (NCB + 1)) void walk_kernel(const WalkArgs<T> 
 }
 
 // ---------------------------------------------------------------------------------------------
-// 3. Per-chunk gradients, one workgroup per (chunk slot, head).
+// 2. Per-chunk gradients, one workgroup per (chunk slot, head).
 template <typename T>
 struct GradArgs {
     const T *q, *k, *v, *la, *beta, *gate, *dout;
@@ -616,7 +613,7 @@ __global__ __launch_bounds__(kThreads, 2) void grad_kernel(const GradArgs<T> a) 
     // per wave: R and dU of the current value block, then the wave's parts of dT and dP
     __shared__ __attribute__((aligned(16))) float s_wv[kNW][2][16 * kTS];
     __shared__ __attribute__((aligned(16))) float s_A[16 * kTS], s_X[16 * kTS], s_T[16 * kTS],
-        s_P[16 * kTS], s_dT[16 * kTS], s_dP[16 * kTS];
+        s_dT[16 * kTS], s_dP[16 * kTS];
     __shared__ __attribute__((aligned(16))) float s_gamma[DK], s_dgam[DK];
     __shared__ float s_beta[kC], s_dbT[kC], s_dbA[kC];
     float* const s_U = s_big;
@@ -716,7 +713,7 @@ __global__ __launch_bounds__(kThreads, 2) void grad_kernel(const GradArgs<T> a) 
     };
     loadA(wave);
     __builtin_amdgcn_sched_barrier(0);  // in flight during the Gram product and T
-    chunk_gram<DK, RS>(s_Qh, s_Kh, s_Kc, s_beta, s_A, nullptr, s_X, s_T, wave, lane);
+    chunk_gram<DK, RS>(s_Kh, s_Kc, s_beta, s_A, s_X, s_T, wave, lane);
 
     // S and dS_C of one channel block, read along rows (B-fragments of S^T over each value
     // block), for the sums over value columns
