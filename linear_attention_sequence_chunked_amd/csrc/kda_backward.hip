@@ -214,15 +214,31 @@ struct alignas(16) WalkBuf {
 struct Split4 {
     bf16x4 h, l;
 };
+// x = hi + lo, hi = bf16(x), lo = bf16(x - hi), with packed conversions: two-wide
+// conversions map to v_cvt_pk_bf16_f32 (four-wide ones become single conversions plus
+// permutes), and x - hi comes from the bf16 dot product (-1, -0) . (hi0, hi1) + x0 on the
+// packed hi pair, with no conversion of hi back to fp32 (x - hi is exact in fp32).  The
+// zero is negative so that neither constant pair has an inline-constant encoding: ROCm 7.2
+// encodes the pair (-1, +0) as the inline constant -1.0, which gfx950 reads as (+0, -1).
+// The dot products take the converted pairs as they are (not extracted again from the
+// packed four-vector, which made the compiler feed the first pair to every use).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf16x4 pack4(bf16x2 a, bf16x2 b) {
+    return __builtin_bit_cast(bf16x4, u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)});
+}
 __device__ __forceinline__ Split4 split4(f32x4 x) {
-    Split4 s;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const bf16 hi = (bf16)x[i];
-        s.h[i] = hi;
-        s.l[i] = (bf16)(x[i] - (float)hi);
-    }
-    return s;
+    const bf16x2 h01 = __builtin_convertvector(f32x2{x[0], x[1]}, bf16x2);
+    const bf16x2 h23 = __builtin_convertvector(f32x2{x[2], x[3]}, bf16x2);
+    const bf16x2 m0 = {(__bf16)-1.0f, (__bf16)-0.0f}, m1 = {(__bf16)-0.0f, (__bf16)-1.0f};
+    const float d0 = __builtin_amdgcn_fdot2_f32_bf16(h01, m0, x[0], false);
+    const float d1 = __builtin_amdgcn_fdot2_f32_bf16(h01, m1, x[1], false);
+    const float d2 = __builtin_amdgcn_fdot2_f32_bf16(h23, m0, x[2], false);
+    const float d3 = __builtin_amdgcn_fdot2_f32_bf16(h23, m1, x[3], false);
+    const bf16x2 l01 = __builtin_convertvector(f32x2{d0, d1}, bf16x2);
+    const bf16x2 l23 = __builtin_convertvector(f32x2{d2, d3}, bf16x2);
+    return Split4{pack4(h01, h23), pack4(l01, l23)};
 }
 __device__ __forceinline__ bf16x4 ldb4(const bf16* p) { return *reinterpret_cast<const bf16x4*>(p); }
 __device__ __forceinline__ Split4 lds_split(const bf16* hi, const bf16* lo) { return Split4{ldb4(hi), ldb4(lo)}; }
@@ -258,18 +274,12 @@ __device__ __forceinline__ f32x4 mma3x2(const Split4& a0, const Split4& a1, cons
 }
 // eight floats, split, to 16-byte hi and lo pieces at the same offset of two tiles
 __device__ __forceinline__ void store_split8(bf16* hi, bf16* lo, const float (&x)[8]) {
-    bf16x4 h0, h1, l0, l1;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        h0[i] = (bf16)x[i];
-        l0[i] = (bf16)(x[i] - (float)h0[i]);
-        h1[i] = (bf16)x[4 + i];
-        l1[i] = (bf16)(x[4 + i] - (float)h1[i]);
-    }
-    *reinterpret_cast<bf16x4*>(hi) = h0;
-    *reinterpret_cast<bf16x4*>(hi + 4) = h1;
-    *reinterpret_cast<bf16x4*>(lo) = l0;
-    *reinterpret_cast<bf16x4*>(lo + 4) = l1;
+    const Split4 a = split4(f32x4{x[0], x[1], x[2], x[3]});
+    const Split4 b = split4(f32x4{x[4], x[5], x[6], x[7]});
+    *reinterpret_cast<bf16x4*>(hi) = a.h;
+    *reinterpret_cast<bf16x4*>(hi + 4) = b.h;
+    *reinterpret_cast<bf16x4*>(lo) = a.l;
+    *reinterpret_cast<bf16x4*>(lo + 4) = b.l;
 }
 
 template <typename T, int DK, int DV, int NCB>
