@@ -87,3 +87,16 @@ def test_backward_bench_workload_sampled():
     g = torch.Generator().manual_seed(1)
     do = torch.randn(x.v.shape, generator=g).to(x.v.dtype).cuda()
     run_case(x, do, None, floor=-0.3, scale=1.0, pairs=[(0, 3), (3, 12)])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_strongest_decay_floor(dtype):
+    """Floor -5 with log-decays drawn down to -5: decay-folded operands span ~e^80 within a
+    chunk (finite in fp32 and in bf16 hi/lo pairs)."""
+    log(f"backward floor=-5 dtype={dtype}")
+    x = ki.make_prefill_inputs((40, 64, 17), 2, 128, 128, dtype, 0.3, seed=56, device="cuda",
+                               log_alpha_min=-5.0)
+    g = torch.Generator().manual_seed(56)
+    do = torch.randn(x.v.shape, generator=g).to(x.v.dtype).cuda()
+    dSf = (torch.randn(x.initial_state.shape, generator=g) * 0.1).cuda()
+    run_case(x, do, dSf, floor=-5.0, scale=1.0)

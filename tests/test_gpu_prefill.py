@@ -159,3 +159,14 @@ def test_workload_varlen_n64_h32_sampled():
     sampled_check(x, [(short, 0), (mid, 31), (longest, 17)], o, S)
     del x, o, S
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_strongest_decay_floor(dtype):
+    """The lowest accepted floor (-5): log-decays drawn down to -5, so a chunk's cumulative
+    decay reaches tens of nats and e^(G_C - G), e^-G span ~e^80 -- the range the lower
+    bound on the log-decay exists to keep finite."""
+    log(f"prefill floor=-5 dtype={dtype}")
+    x = ki.make_prefill_inputs((40, 64, 17), 2, 128, 128, dtype, 0.3, seed=55, device="cuda",
+                               log_alpha_min=-5.0)
+    check_full(x, dtype, log_alpha_floor=-5.0)
