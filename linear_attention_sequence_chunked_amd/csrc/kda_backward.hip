@@ -169,22 +169,24 @@ struct WalkArgs {
     const float* S0;    // initial state, or null
     const float* dSf;   // gradient of the final state, or null
     float* dS0;         // gradient of the initial state, or null
-    float* states;      // state entering chunk c of sequence n: slot cu[n]/16 + n + c
-    float* dsc;         // gradient leaving chunk c of sequence n: same slot
-    float* aux;         // per slot [16][dv] rows: R, Y (forwards), dU, dR (backwards)
+    float* states;      // state entering chunk c of sequence n: slot cu[n]/16 + n + c, [dv][dk]
+    float* dsc;         // gradient leaving chunk c of sequence n: same slot, [dv][dk]
+    float* aux;         // per slot [dv][16]: R, Y (forwards), dU, dR (backwards)
     int64_t aux_stride; // floats between those four arrays
     int H, n_slices, half;
     float floor_, scale;
 };
 
 // One workgroup = NCB consumer waves (one 16-column block of S or dS each) + one producer
-// wave, over three LDS buffers.  In the interval between two workgroup barriers that steps
-// the walk to chunk step `it`:
-//   consumers  state step of `it` (buffer it % 3), then the decay-folded operands of step
-//              it + 2 into buffer (it + 2) % 3, one 8-channel piece per consumer wave;
-//   producer   the Gram products and T of step it + 1 (buffer (it + 1) % 3).
-// Each kind of wave runs its own loop with exactly one barrier per step; global inputs are
-// loaded two steps ahead (bf16; one step for fp32) into alternating register sets.
+// wave + ND decay waves, over three LDS buffers.  In the interval between two workgroup
+// barriers that steps the walk to chunk step `it`:
+//   consumers  state step of `it` (buffer it % 3);
+//   producer   the Gram products and T of step it + 1 (buffer (it + 1) % 3);
+//   decay      the decay-folded operands of step it + 2 into buffer (it + 2) % 3, a share
+//              of the 8-channel pieces per decay wave.
+// Each kind of wave runs its own loop with exactly one barrier per step, nch + 2 in all;
+// global inputs are loaded two steps ahead (the consumers' for fp32: one) into alternating
+// register sets.
 //
 // Operands relative to the chunk's end (as in the forward): Kt = k e^(G - G_C),
 // Qt = (scale q) e^(G - G_C), Kb = k e^(G_C - G).  Then A' = strict_lower(Kt Kb^T),
@@ -282,14 +284,16 @@ __device__ __forceinline__ void store_split8(bf16* hi, bf16* lo, const float (&x
     *reinterpret_cast<bf16x4*>(lo + 4) = b.l;
 }
 
-template <typename T, int DK, int DV, int NCB>
-__global__ __launch_bounds__(64 * (NCB + 1)) void walk_kernel(const WalkArgs<T> a) {
+template <typename T, int DK, int DV, int NCB, int ND>
+__global__ __launch_bounds__(64 * (NCB + 1 + ND)) void walk_kernel(const WalkArgs<T> a) {
     constexpr int NV = 16 * NCB;
     constexpr int KB = DK / 16;
     constexpr int PF = sizeof(T) == 2 ? 2 : 1;  // steps of input prefetch (register sets)
     constexpr int CW = DK / 4, NP = CW / 8;      // decay: channels per lane group, pieces
     constexpr int NWD = (int)sizeof(T) / 2;      // 16-byte words per 8-channel piece
-    static_assert(NP <= NCB, "one decay piece per consumer wave");
+    constexpr int PPW = NP / ND;                 // decay pieces per decay wave
+    constexpr int PFD = 2;                       // steps of decay-input prefetch
+    static_assert(NP % ND == 0, "decay pieces split evenly over the decay waves");
     typedef WalkBuf<DK> B;
     constexpr int RSB = B::RSB, TSB = B::TSB;
 
@@ -427,67 +431,96 @@ __global__ __launch_bounds__(64 * (NCB + 1)) void walk_kernel(const WalkArgs<T> 
         return;
     }
 
-    // ---------------- consumers: wave w owns value columns slice NV + 16 w + [0, 16) and
-    // decay piece w: row pr = lane & 15, channels pg CW + 8 w + [0, 8) (pg = lane >> 4)
+    if (wave > NCB) {
+        // ---------------- decay waves: the decay-folded operands of step s into buffer s % 3,
+        // two steps ahead of the state step.  Decay wave j owns pieces j PPW + [0, PPW); in
+        // piece p, lane (pr, pg) = (lane & 15, lane >> 4) holds row pr, channels
+        // pg CW + 8 p + [0, 8).
+        const int jd = wave - NCB - 1;
+        const int pr = lane & 15, pg = lane >> 4;
+        struct Piece {
+            uint4 q[NWD], k[NWD], l[NWD];
+        };
+        Piece ring[PFD][PPW];
+        auto dfetch = [&](Piece (&x)[PPW], int s) {
+            const int64_t off = row_at(chunk_of(s), pr) * rowq + (int64_t)h * DK + pg * CW + 8 * PPW * jd;
+#pragma unroll
+            for (int p = 0; p < PPW; ++p)
+#pragma unroll
+                for (int w = 0; w < NWD; ++w) {
+                    x[p].q[w] = *reinterpret_cast<const uint4*>(a.q + off + 8 * p + 4 * w);
+                    x[p].k[w] = *reinterpret_cast<const uint4*>(a.k + off + 8 * p + 4 * w);
+                    x[p].l[w] = *reinterpret_cast<const uint4*>(a.la + off + 8 * p + 4 * w);
+                }
+        };
+        auto decay = [&](const Piece (&x)[PPW], int s) {
+            B& o = s_buf[s % 3];
+            const bool in = pr < rows_of(chunk_of(s));
+#pragma unroll
+            for (int p = 0; p < PPW; ++p) {
+                const int ch0 = pg * CW + 8 * (PPW * jd + p);
+                float xq[8], xk[8], G[8];
+                unpack8<T>(x[p].q, xq);
+                unpack8<T>(x[p].k, xk);
+                unpack8<T>(x[p].l, G);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) G[i] = in ? fmaxf(G[i], a.floor_) : 0.f;
+                row_scan8(G);
+                float qt[8], kt[8], kb[8], gm[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float GC = row_last(G[i]);  // G of the chunk's last row
+                    const float d = G[i] - GC;        // >= 0
+                    const float e = __expf(d), ei = __expf(-d);
+                    const float qv = in ? xq[i] : 0.f, kv = in ? xk[i] : 0.f;
+                    gm[i] = __expf(GC);
+                    qt[i] = a.scale * qv * e;
+                    kt[i] = kv * e;
+                    kb[i] = kv * ei;
+                }
+                const int off = pr * RSB + ch0;
+                store_split8(&o.kt[0][off], &o.kt[1][off], kt);
+                store_split8(&o.kb[0][off], &o.kb[1][off], kb);
+                store_split8(&o.qt[0][off], &o.qt[1][off], qt);
+                if (pr == 15) store8(&o.gamma[ch0], gm);
+            }
+        };
+        // steps 0 .. nch + 1, one barrier each (the last two write buffers nobody reads)
+#pragma unroll
+        for (int j = 0; j < PFD; ++j) dfetch(ring[j], j);
+        for (int s = 0; s < nch + 2; s += PFD) {
+#pragma unroll
+            for (int j = 0; j < PFD; ++j) {
+                if (s + j < nch + 2) {
+                    decay(ring[j], s + j);
+                    dfetch(ring[j], s + j + PFD);
+                    lds_barrier();
+                }
+            }
+        }
+        return;
+    }
+
+    // ---------------- consumers: wave w owns value columns slice NV + 16 w + [0, 16)
     const int col = slice * NV + 16 * wave + r;
-    const int pr = lane & 15, pg = lane >> 4;
-    const int ch0 = pg * CW + 8 * wave;
-    const bool decays = wave < NP;
     float* const out = (rev ? a.dsc : a.states) + ((tbeg / kC + n) * H + h) * SS;
     const int64_t aslot = (tbeg / kC + n) * H + h;  // (slot, head) row of chunk 0
     const T* const vsrc = rev ? a.dout : a.v;  // backwards: dO (times the gate)
+    // two named register sets (PF == 2; R1 is unused for PF == 1): an array indexed by the
+    // step would be placed in LDS
     struct Regs {
-        T v[4], g[4];               // V or dO, gate: rows 4g + i, column col
-        uint4 q[NWD], k[NWD], l[NWD];  // the decay piece
-    } R[PF];
-    // inputs of step it into x: the state step's values, and the decay piece of step it + 2
-    auto fetch = [&](Regs& x, int it) {
+        T v[4], g[4];  // V or dO, gate: rows 4g + i, column col
+    } R0, R1;
+    auto fetch = [&](int it) {
+        Regs x;
         const int c = chunk_of(it);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int64_t off = row_at(c, 4 * g + i) * rowv + (int64_t)h * DV + col;
             x.v[i] = vsrc[off];
-            x.g[i] = a.gate[off];
+            x.g[i] = rev ? a.gate[off] : T{};  // the gate enters the backward walk only
         }
-        if (decays) {
-            const int64_t off = row_at(chunk_of(it + 2), pr) * rowq + (int64_t)h * DK + ch0;
-#pragma unroll
-            for (int w = 0; w < NWD; ++w) {
-                x.q[w] = *reinterpret_cast<const uint4*>(a.q + off + 4 * w);
-                x.k[w] = *reinterpret_cast<const uint4*>(a.k + off + 4 * w);
-                x.l[w] = *reinterpret_cast<const uint4*>(a.la + off + 4 * w);
-            }
-        }
-    };
-    // decay-folded operands of step s from the raw piece in x, into buffer s % 3
-    auto decay = [&](const Regs& x, int s) {
-        if (!decays) return;
-        B& o = s_buf[s % 3];
-        const bool in = pr < rows_of(chunk_of(s));
-        float xq[8], xk[8], G[8];
-        unpack8<T>(x.q, xq);
-        unpack8<T>(x.k, xk);
-        unpack8<T>(x.l, G);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) G[i] = in ? fmaxf(G[i], a.floor_) : 0.f;
-        row_scan8(G);
-        float qt[8], kt[8], kb[8], gm[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float GC = row_last(G[i]);  // G of the chunk's last row
-            const float d = G[i] - GC;        // >= 0
-            const float e = __expf(d), ei = __expf(-d);
-            const float qv = in ? xq[i] : 0.f, kv = in ? xk[i] : 0.f;
-            gm[i] = __expf(GC);
-            qt[i] = a.scale * qv * e;
-            kt[i] = kv * e;
-            kb[i] = kv * ei;
-        }
-        const int off = pr * RSB + ch0;
-        store_split8(&o.kt[0][off], &o.kt[1][off], kt);
-        store_split8(&o.kb[0][off], &o.kb[1][off], kb);
-        store_split8(&o.qt[0][off], &o.qt[1][off], qt);
-        if (pr == 15) store8(&o.gamma[ch0], gm);
+        return x;
     };
     // X[b] holds rows 16b + 4g + i, column col of S (forwards) or dS (backwards)
     const float* init = rev ? a.dSf : a.S0;
@@ -496,6 +529,9 @@ __global__ __launch_bounds__(64 * (NCB + 1)) void walk_kernel(const WalkArgs<T> 
     for (int b = 0; b < KB; ++b)
 #pragma unroll
         for (int i = 0; i < 4; ++i) X[b][i] = init ? init[sbase + (16 * b + 4 * g + i) * DV + col] : 0.f;
+    // Let the initial loads land here: otherwise the loop's first use of X carries a wait for
+    // them, merged at the loop head into a wait on the previous step's stores every step.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     auto step = [&](Regs& x, int it) {
         const B& o = s_buf[it % 3];
         const int c = chunk_of(it);
@@ -504,18 +540,15 @@ __global__ __launch_bounds__(64 * (NCB + 1)) void walk_kernel(const WalkArgs<T> 
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             in4[i] = 4 * g + i < Cp ? (rev ? to_f32(x.v[i]) * to_f32(x.g[i]) : to_f32(x.v[i])) : 0.f;
-        float* dst = out + (int64_t)c * H * SS;
+        // the state (or gradient) is stored transposed, [dv][dk]: rows 16b + 4g .. +3 of
+        // column col are one 16-byte piece
+        float* const dst = out + (int64_t)c * H * SS + col * DK + 4 * g;
 #pragma unroll
-        for (int b = 0; b < KB; ++b)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dst[(16 * b + 4 * g + i) * DV + col] = X[b][i];
-        // rows 4g + i, column col of this chunk's [16][dv] vectors for the gradient kernel
+        for (int b = 0; b < KB; ++b) *reinterpret_cast<f32x4*>(dst + 16 * b) = X[b];
+        // this chunk's [16][dv] vectors for the gradient kernel, also transposed ([dv][16])
         float* const ax = a.aux + (rev ? 2 : 0) * a.aux_stride + (aslot + (int64_t)c * H) * kC * DV +
-                          (4 * g) * DV + col;
-        auto put = [&](float* p, f32x4 x) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) p[i * DV] = x[i];
-        };
+                          col * kC + 4 * g;
+        auto put = [&](float* p, f32x4 x) { *reinterpret_cast<f32x4*>(p) = x; };
         if (!rev) {  // S' = Diag(gamma) S;  R = V - Kt S';  U = T R;  Y = Qt S' + P U;  S <- S' + Kb^T U
             f32x4 KtS = zero4(), QtS = zero4();
 #pragma unroll
@@ -557,34 +590,18 @@ __global__ __launch_bounds__(64 * (NCB + 1)) void walk_kernel(const WalkArgs<T> 
                 X[b] = acc * ld4(&o.gamma[16 * b + 4 * g]);
             }
         }
-        decay(x, it + 2);
-        fetch(x, it + PF);
+        x = fetch(it + PF);
         lds_barrier();
     };
-    // prologue: the decay of steps 0 and 1 (their pieces are loaded here, not prefetched)
-#pragma unroll
-    for (int s0 = 0; s0 < 2; ++s0) {
-        Regs t;
-        if (decays) {
-            const int64_t off = row_at(chunk_of(s0), pr) * rowq + (int64_t)h * DK + ch0;
-#pragma unroll
-            for (int w = 0; w < NWD; ++w) {
-                t.q[w] = *reinterpret_cast<const uint4*>(a.q + off + 4 * w);
-                t.k[w] = *reinterpret_cast<const uint4*>(a.k + off + 4 * w);
-                t.l[w] = *reinterpret_cast<const uint4*>(a.la + off + 4 * w);
-            }
-        }
-        if (s0 == 0) {
-#pragma unroll
-            for (int j = 0; j < PF; ++j) fetch(R[j], j);
-        }
-        decay(t, s0);
-        lds_barrier();
-    }
+    // prologue: the decay waves write steps 0 and 1, the producer the Gram products of step 0
+    static_assert(PF == 1 || PF == 2, "register sets");
+    R0 = fetch(0);
+    if (PF == 2) R1 = fetch(1);
+    lds_barrier();
+    lds_barrier();
     for (int it = 0; it < nch; it += PF) {
-#pragma unroll
-        for (int j = 0; j < PF; ++j)
-            if (it + j < nch) step(R[j], it + j);
+        step(R0, it);
+        if (PF == 2 && it + 1 < nch) step(R1, it + 1);
     }
     if (rev && a.dS0) {
 #pragma unroll
@@ -600,9 +617,9 @@ template <typename T>
 struct GradArgs {
     const T *q, *k, *v, *la, *beta, *gate, *dout;
     const int32_t* cu;
-    const float* states;  // state entering chunk c of sequence n: slot cu[n]/16 + n + c
-    const float* dsc;     // gradient leaving chunk c of sequence n: same slot
-    const float* aux;     // per slot [16][dv]: R, Y, dU, dR, aux_stride floats apart
+    const float* states;  // state entering chunk c of sequence n: slot cu[n]/16 + n + c, [dv][dk]
+    const float* dsc;     // gradient leaving chunk c of sequence n: same slot, [dv][dk]
+    const float* aux;     // per slot [dv][16]: R, Y, dU, dR, aux_stride floats apart
     int64_t aux_stride;
     float *dq, *dk, *dv, *dla, *dbeta, *dgate;
     int H, N;
@@ -709,13 +726,13 @@ __global__ __launch_bounds__(kThreads, 2) void grad_kernel(const GradArgs<T> a) 
     T rdo[4], rgt[4];
     auto loadA = [&](int vb) {
         const int col = 16 * vb + r;
+        const int64_t o = (int64_t)col * kC + 4 * g;  // stored transposed: [dv][16]
+        Rv = ld4(ax + o);
+        Yv = ld4(ax + a.aux_stride + o);
+        dUv = ld4(ax + 2 * a.aux_stride + o);
+        dRv = ld4(ax + 3 * a.aux_stride + o);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int64_t o = (int64_t)(4 * g + i) * DV + col;
-            Rv[i] = ax[o];
-            Yv[i] = ax[a.aux_stride + o];
-            dUv[i] = ax[2 * a.aux_stride + o];
-            dRv[i] = ax[3 * a.aux_stride + o];
             const int64_t off = (t0 + min(4 * g + i, Cp - 1)) * rowv + (int64_t)h * DV + col;
             rdo[i] = a.dout[off];
             rgt[i] = a.gate[off];
@@ -731,9 +748,12 @@ __global__ __launch_bounds__(kThreads, 2) void grad_kernel(const GradArgs<T> a) 
     auto loadB = [&](int cb) {
 #pragma unroll
         for (int vb = 0; vb < VB; ++vb) {
-            const int64_t off = (int64_t)(16 * cb + r) * DV + 16 * vb + 4 * g;
-            S2[vb] = ld4(Sin + off);
-            D2[vb] = ld4(dSC + off);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {  // stored transposed: [dv][dk]
+                const int64_t off = (int64_t)(16 * vb + 4 * g + i) * DK + 16 * cb + r;
+                S2[vb][i] = Sin[off];
+                D2[vb][i] = dSC[off];
+            }
         }
     };
 
@@ -933,7 +953,7 @@ __global__ __launch_bounds__(kThreads, 2) void grad_kernel(const GradArgs<T> a) 
     if (tid < Cp) a.dbeta[(t0 + tid) * H + h] = s_dbT[tid] + s_dbA[tid];
 }
 
-template <typename T, int DK, int DV, int NCB>
+template <typename T, int DK, int DV, int NCB, int ND>
 hipError_t launch_walk(const BackwardArgs& p, hipStream_t st) {
     WalkArgs<T> a;
     a.q = (const T*)p.q; a.k = (const T*)p.k; a.v = (const T*)p.v; a.la = (const T*)p.log_alpha;
@@ -944,8 +964,8 @@ hipError_t launch_walk(const BackwardArgs& p, hipStream_t st) {
     a.aux_stride = (p.grad_offset / ((int64_t)DK * DV)) * kC * DV;
     a.H = p.H; a.n_slices = DV / (16 * NCB); a.floor_ = p.floor_; a.scale = p.scale;
     a.half = p.num_seqs * p.H * a.n_slices;
-    hipLaunchKernelGGL((walk_kernel<T, DK, DV, NCB>), dim3(2u * (unsigned)a.half),
-                       dim3(64 * (NCB + 1)), 0, st, a);
+    hipLaunchKernelGGL((walk_kernel<T, DK, DV, NCB, ND>), dim3(2u * (unsigned)a.half),
+                       dim3(64 * (NCB + 1 + ND)), 0, st, a);
     return hipGetLastError();
 }
 
@@ -954,7 +974,7 @@ hipError_t launch_typed(const BackwardArgs& p, hipStream_t st) {
     if (p.num_seqs == 0 || p.H == 0) return hipSuccess;
     // 64 value columns per workgroup: four consumer waves (the walk's double buffer takes
     // ~100 KB of LDS, one workgroup per compute unit)
-    hipError_t e = launch_walk<T, DK, DV, 4>(p, st);
+    hipError_t e = launch_walk<T, DK, DV, 4, 2>(p, st);
     if (e != hipSuccess || p.T_total == 0) return e;
     GradArgs<T> a;
     a.q = (const T*)p.q; a.k = (const T*)p.k; a.v = (const T*)p.v; a.la = (const T*)p.log_alpha;
