@@ -173,7 +173,7 @@ struct WalkArgs {
     float* dsc;         // gradient leaving chunk c of sequence n: same slot, [dv][dk]
     float* aux;         // per slot [dv][16]: R, Y (forwards), dU, dR (backwards)
     int64_t aux_stride; // floats between those four arrays
-    int H, n_slices, half;
+    int H, n_slices, half, pairs;
     float floor_, scale;
 };
 
@@ -305,7 +305,12 @@ __global__ __launch_bounds__(64 * (NCB + 1 + ND)) void walk_kernel(const WalkArg
     const int r = lane & 15, g = lane >> 4;
     const bool rev = (int)blockIdx.x >= a.half;
     const int bid = rev ? (int)blockIdx.x - a.half : (int)blockIdx.x;
-    const int pair = bid / a.n_slices, slice = bid % a.n_slices;
+    // bid -> (pair, slice): the slices of one (sequence, head) share an XCD and so its L2
+    // for the key-side reads (consecutive workgroup ids go round-robin over the 8 XCDs;
+    // half is padded to a multiple of 8 slices' worth)
+    const int xcd = bid & 7, kk = bid >> 3;
+    const int pair = (kk / a.n_slices) * 8 + xcd, slice = kk % a.n_slices;
+    if (pair >= a.pairs) return;
     const int H = a.H, n = pair / H, h = pair % H;
     const int64_t tbeg = a.cu[n], tend = a.cu[n + 1];
     const int nch = (int)((tend - tbeg + kC - 1) / kC);
@@ -963,7 +968,8 @@ hipError_t launch_walk(const BackwardArgs& p, hipStream_t st) {
     a.aux = p.workspace + 2 * p.grad_offset;
     a.aux_stride = (p.grad_offset / ((int64_t)DK * DV)) * kC * DV;
     a.H = p.H; a.n_slices = DV / (16 * NCB); a.floor_ = p.floor_; a.scale = p.scale;
-    a.half = p.num_seqs * p.H * a.n_slices;
+    a.pairs = p.num_seqs * p.H;
+    a.half = (a.pairs + 7) / 8 * 8 * a.n_slices;
     hipLaunchKernelGGL((walk_kernel<T, DK, DV, NCB, ND>), dim3(2u * (unsigned)a.half),
                        dim3(64 * (NCB + 1 + ND)), 0, st, a);
     return hipGetLastError();
