@@ -978,8 +978,9 @@ hipError_t launch_walk(const BackwardArgs& p, hipStream_t st) {
 template <typename T, int DK, int DV>
 hipError_t launch_typed(const BackwardArgs& p, hipStream_t st) {
     if (p.num_seqs == 0 || p.H == 0) return hipSuccess;
-    // 64 value columns per workgroup: four consumer waves (the walk's double buffer takes
-    // ~100 KB of LDS, one workgroup per compute unit)
+    // 64 value columns per workgroup: four consumer waves, one producer and two decay waves
+    // (the walk's three buffers take ~90 KB of LDS at dk = 128: one workgroup per compute
+    // unit; four decay waves, nine waves in all, measured slower)
     hipError_t e = launch_walk<T, DK, DV, 4, 2>(p, st);
     if (e != hipSuccess || p.T_total == 0) return e;
     GradArgs<T> a;
