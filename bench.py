@@ -85,7 +85,10 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # A few warmup launches leave the GPU below its steady clocks: the bench workload's
+    # prefill measured ~256 us per launch after 3 warmup launches and ~235 us after 200
+    # (0.5 s or 2 s of warmup: ~238 us).
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="prefill_b4_h16_t4096")
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
