@@ -53,6 +53,35 @@ def stored_traffic(workload: str):
     return t.get("traffic_bytes_per_launch")
 
 
+# the decode kernel's sources, and the committed counter summaries of MFMA use (prefill)
+# and HBM bytes (decode)
+DECODE_SOURCES = ("kda_decode.hip", "kda_device.h", "kda_launch.h", "kda_api.cpp")
+MFMA_FILE = os.path.join(ROOT, "profiles", "prefill_bf16_b4_h16_t4096_mfma_counters.json")
+DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_n256_h32_traffic.json")
+
+
+def decode_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for name in DECODE_SOURCES:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def stored_summary(path: str, workload: str, source_hash: str):
+    """A committed counter summary, or None when it is missing, is for another workload or
+    predates the current kernel source."""
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("workload") != workload or t.get("kernel_source_sha256") != source_hash:
+        return None
+    return t
+
+
 def copy_calibration(steps: int) -> int:
     """Plain device copy of COPY_BYTES, the reference kernel for scaling the FETCH_SIZE /
     WRITE_SIZE counters (each launch must read and write exactly COPY_BYTES)."""
@@ -200,6 +229,15 @@ def main() -> int:
                  "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
                  "algorithmic_flops_per_launch": alg_flops},
     }
+    mc = (stored_summary(MFMA_FILE, w.name, prefill_source_hash()) if w.dtype == "bf16" else None)
+    if mc is not None:  # rocprofv3 counters of the same kernel, this launch's time
+        ex = mc["executed_bf16_flops_per_launch"]
+        result["mfma"]["rocprof"] = {
+            "executed_bf16_flops_per_launch": ex,
+            "executed_TFLOPs": ex / (ms * 1e-3) / 1e12,
+            "executed_frac": ex / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "mfma_busy_frac": mc["mfma_busy_frac"],
+            "source": os.path.basename(MFMA_FILE)}
 
     # ---------------------------------------------------------------- decode step
     if not args.no_decode and args.decode_steps > 0:
@@ -233,6 +271,11 @@ def main() -> int:
             "total_GBps_incl_token_io": (2 * state_bytes + io_bytes) / (dms * 1e-3) / 1e9,
             "state_bytes": state_bytes,
         }
+        dt = stored_summary(DECODE_TRAFFIC_FILE, d.name, decode_source_hash())
+        if dt is not None:  # rocprofv3 HBM byte counters of the same kernel, this step's time
+            result["decode"]["traffic_bytes_per_step"] = dt["traffic_bytes_per_step"]
+            result["decode"]["traffic_GBps"] = dt["traffic_bytes_per_step"] / (dms * 1e-3) / 1e9
+            result["decode"]["traffic_frac_hbm"] = result["decode"]["traffic_GBps"] / HBM_PEAK_GBPS
         del inp, state
         torch.cuda.empty_cache()
 
