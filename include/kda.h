@@ -190,7 +190,7 @@ int64_t kda_prefill_segmented_workspace(const kda_params* params,
  *   workspace       : device memory of at least kda_prefill_backward_workspace(...) bytes,
  *                     256-byte aligned, overlapping no other argument; receives the state
  *                     entering every 16-token chunk and the gradient of the state leaving
- *                     it (fp32, dk x dv each per chunk and head), and four 16 x dv fp32
+ *                     it (fp32, dk x dv each per chunk and head), and three 16 x dv fp32
  *                     blocks per chunk and head passed from the walks to the gradients.
  * The gradients are computed in fp32 with the 16-token chunk algebra of the forward: one
  * launch walks every sequence forwards (the chunk-entering states) and backwards (the

@@ -550,10 +550,10 @@ kda_status bwd_size(const kda_params* params, const int32_t* cu, int32_t N, uint
     const uint64_t H = params->num_heads, ss = (uint64_t)params->dk * params->dv;
     // the state entering chunk c of sequence n at slot cu[n]/16 + n + c (at most
     // T_total/16 + N slots), then the gradient leaving the chunk at the same slot, then
-    // four [16][dv] arrays per slot (R, Y, dU, dR of the chunk)
+    // three [16][dv] arrays per slot (R, Y, dU of the chunk)
     const uint64_t slots = (uint64_t)cu[N] / 16 + N;
     grad_off = slots * H * ss;
-    bytes = 4 * (2 * grad_off + 4 * slots * H * 16 * (uint64_t)params->dv);
+    bytes = 4 * (2 * grad_off + 3 * slots * H * 16 * (uint64_t)params->dv);
     return KDA_OK;
 }
 

@@ -171,8 +171,8 @@ struct WalkArgs {
     float* dS0;         // gradient of the initial state, or null
     float* states;      // state entering chunk c of sequence n: slot cu[n]/16 + n + c, [dv][dk]
     float* dsc;         // gradient leaving chunk c of sequence n: same slot, [dv][dk]
-    float* aux;         // per slot [dv][16]: R, Y (forwards), dU, dR (backwards)
-    int64_t aux_stride; // floats between those four arrays
+    float* aux;         // per slot [dv][16]: R, Y (forwards), dU (backwards)
+    int64_t aux_stride; // floats between those three arrays
     int H, n_slices, half, pairs;
     float floor_, scale;
 };
@@ -584,8 +584,7 @@ __global__ __launch_bounds__(64 * (NCB + 1 + ND)) void walk_kernel(const WalkArg
                             split4(X[b]), split4(X[b + 1]), dU);
             }
             const f32x4 dR = mma3(lds_split(&o.sq2[0][fq], &o.sq2[1][fq]), split4(dU), zero4());
-            put(ax, dU);
-            put(ax + a.aux_stride, dR);
+            put(ax, dU);  // dR = T^T dU is formed again by the gradient kernel
             const Split4 nRs = split4(-dR);
 #pragma unroll
             for (int b = 0; b < KB; ++b) {
@@ -624,7 +623,7 @@ struct GradArgs {
     const int32_t* cu;
     const float* states;  // state entering chunk c of sequence n: slot cu[n]/16 + n + c, [dv][dk]
     const float* dsc;     // gradient leaving chunk c of sequence n: same slot, [dv][dk]
-    const float* aux;     // per slot [dv][16]: R, Y, dU, dR, aux_stride floats apart
+    const float* aux;     // per slot [dv][16]: R, Y, dU, aux_stride floats apart
     int64_t aux_stride;
     float *dq, *dk, *dv, *dla, *dbeta, *dgate;
     int H, N;
@@ -723,11 +722,11 @@ __global__ __launch_bounds__(kThreads, 2) void grad_kernel(const GradArgs<T> a) 
     if (tid < kC) s_beta[tid] = tid < Cp ? to_f32(a.beta[(t0 + tid) * H + h]) : 0.f;
     lds_barrier();
     // Global operands of one value block, rows 4g + i, column 16 vb + r: the walks' R, Y
-    // (forwards) and dU, dR (backwards) of this chunk, dO and the gate -- loaded ahead of
+    // (forwards) and dU (backwards) of this chunk, dO and the gate -- loaded ahead of
     // their use.  Rows past the end of the sequence re-read its last row and are masked.
     constexpr int NA = VB / kNW;  // value blocks per wave
     const float* const ax = a.aux + ((int64_t)slot * H + h) * kC * DV;
-    f32x4 Rv, Yv, dUv, dRv;
+    f32x4 Rv, Yv, dUv;
     T rdo[4], rgt[4];
     auto loadA = [&](int vb) {
         const int col = 16 * vb + r;
@@ -735,7 +734,6 @@ __global__ __launch_bounds__(kThreads, 2) void grad_kernel(const GradArgs<T> a) 
         Rv = ld4(ax + o);
         Yv = ld4(ax + a.aux_stride + o);
         dUv = ld4(ax + 2 * a.aux_stride + o);
-        dRv = ld4(ax + 3 * a.aux_stride + o);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int64_t off = (t0 + min(4 * g + i, Cp - 1)) * rowv + (int64_t)h * DV + col;
@@ -764,7 +762,7 @@ __global__ __launch_bounds__(kThreads, 2) void grad_kernel(const GradArgs<T> a) 
 
     // ---- A: value blocks (wave w takes blocks w, w + 4, ...)
     {
-        const f32x4 Tr = ld4(&s_T[r * kTS + 4 * g]);
+        const f32x4 Tr = ld4(&s_T[r * kTS + 4 * g]), Tc = ld4_col(s_T, r, g);  // T, T^T
         float* const sR = s_wv[wave][0];
         float* const sdU = s_wv[wave][1];
         f32x4 dTw = zero4(), dPw = zero4();
@@ -779,11 +777,12 @@ __global__ __launch_bounds__(kThreads, 2) void grad_kernel(const GradArgs<T> a) 
                 dO[i] = in ? to_f32(rdo[i]) : 0.f;
                 gt[i] = in ? to_f32(rgt[i]) : 0.f;
             }
-            const f32x4 Rt = Rv, Y = Yv, dU = dUv, dR = dRv;
+            const f32x4 Rt = Rv, Y = Yv, dU = dUv;
             if (ia + 1 < NA) loadA(vb + kNW);
             else loadB(wave);
             __builtin_amdgcn_sched_barrier(0);
             const f32x4 U = M::run(Tr, Rt, zero4());
+            const f32x4 dR = M::run(Tc, dU, zero4());  // T^T dU
             const f32x4 dY = dO * gt;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {

@@ -272,12 +272,12 @@ def test_segmented_rejects(kw, msg):
 def test_backward_workspace_size():
     """cu = (0, 40, 40, 100), H = 2, d = 64: the state entering every chunk at slot
     cu[n]/16 + n + c (at most 100 // 16 + 3 = 9 slots per head), then the gradient leaving
-    every chunk at the same slots, then four [16][dv] vectors per slot and head."""
+    every chunk at the same slots, then three [16][dv] vectors per slot and head."""
     lib = _lib.load()
     p = _lib.params(_lib.KDA_DTYPE_BF16, 2, 64, 64)
     ss = 64 * 64 * 4
     assert lib.kda_prefill_backward_workspace(ctypes.byref(p), cu(0, 40, 40, 100), 3) == \
-        2 * 9 * 2 * ss + 4 * 9 * 2 * 16 * 64 * 4
+        2 * 9 * 2 * ss + 3 * 9 * 2 * 16 * 64 * 4
     assert lib.kda_prefill_backward_workspace(ctypes.byref(p), cu(0, 40, 30), 2) == -1
 
 
