@@ -31,13 +31,21 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_bf16_b4_h16_t4096_traffic
 COPY_BYTES = 1 << 30  # calibration copy: 1 GiB read + 1 GiB written
 
 
-def prefill_source_hash() -> str:
+BUILD_SCRIPT = os.path.join(ROOT, "linear_attention_sequence_chunked_amd", "build.py")
+
+
+def _source_hash(names) -> str:
+    """SHA-256 over the kernel sources and the build script (its flags shape the code)."""
     import hashlib
     h = hashlib.sha256()
-    for name in PREFILL_SOURCES:
-        with open(os.path.join(CSRC, name), "rb") as f:
+    for path in [os.path.join(CSRC, n) for n in names] + [BUILD_SCRIPT]:
+        with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()
+
+
+def prefill_source_hash() -> str:
+    return _source_hash(PREFILL_SOURCES)
 
 
 def stored_traffic(workload: str):
@@ -61,12 +69,7 @@ DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_n256_h32_traffic.js
 
 
 def decode_source_hash() -> str:
-    import hashlib
-    h = hashlib.sha256()
-    for name in DECODE_SOURCES:
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()
+    return _source_hash(DECODE_SOURCES)
 
 
 def stored_summary(path: str, workload: str, source_hash: str):

@@ -32,9 +32,12 @@ FLAGS = [
 ]
 
 
-# per-source extra flags: the backward's kernels are latency-bound loops, where the
-# scheduler's ILP strategy measured 1-3% faster (bit-identical results)
-EXTRA_FLAGS = {"kda_backward.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+# per-source extra flags: the compiler's ILP scheduling strategy measured faster with
+# bit-identical results for these (backward 1-3%, decode 1.4%, verify/commit 1-1.5%,
+# bf16 prefill 0.7%, each against the default strategy on one box)
+_ILP = ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]
+EXTRA_FLAGS = {"kda_backward.hip": _ILP, "kda_decode.hip": _ILP, "kda_spec.hip": _ILP,
+               "kda_prefill_bf16.hip": _ILP}
 
 
 def _obj(src: str) -> str:
