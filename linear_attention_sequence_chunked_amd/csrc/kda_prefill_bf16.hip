@@ -19,8 +19,10 @@
 //
 // Precision.  Products whose bf16 rounding would cost accuracy carry a second bf16 half
 // (x = hi + lo, ~16 significant bits): P and the Qt/Kb it is built from, the chunk's
-// writes U, Kb in the state update, and Qt in the readout.  The fp32 state is kept in
-// MFMA accumulators; its bf16 copy only feeds the Wt S' and Qt S' products.  The powers
+// writes U, Kb in the state update, and both Qt and S' in the readout Qt S' (the
+// readout of the state is where a single bf16 copy costs the most: outputs are small
+// differences of larger terms).  The fp32 state is kept in MFMA accumulators; its bf16
+// hi copy alone feeds the Wt S' product.  The powers
 // of A in the inverse are plain bf16 products (A is strictly lower triangular with
 // entries below one in size, and T only enters through bf16 operands anyway).
 //
@@ -615,11 +617,17 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
                 // S' = Diag(gamma) S, and its bf16 copy as 32-deep B operands: Sb2[p] holds
                 // the rows of channel blocks 2p and 2p+1 (the B operands of Wt S' and Qt S')
                 const float* gc = reinterpret_cast<const float*>(L + C::L_GAM);
-                bf16x8 Sb2[KP];
+                bf16x8 Sb2[KP], Sl2[KP];
 #pragma unroll
                 for (int b = 0; b < KB; ++b) S[b] *= *reinterpret_cast<const f32x4*>(gc + 16 * b + 4 * g);
 #pragma unroll
-                for (int p = 0; p < KP; ++p) Sb2[p] = to_bf8(S[2 * p], S[2 * p + 1]);
+                for (int p = 0; p < KP; ++p) {  // S' = hi + lo; the readout takes both halves
+                    bf16x4 h0, l0, h1, l1;
+                    split4(S[2 * p], h0, l0);
+                    split4(S[2 * p + 1], h1, l1);
+                    Sb2[p] = cat8(h0, h1);
+                    Sl2[p] = cat8(l0, l1);
+                }
                 // Ut = T V
                 // Ut = T V: T^T is stored with a zero upper half (one 32-deep step; each
                 // accumulator is fed by one instruction shape only)
@@ -630,10 +638,12 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
                     U = mfma32(lds_ld<bf16x8>(W + C::W_WT + p * 1024 + lane * 16), Sb2[p], U);
                 f32x4 O = zero4();
 #pragma unroll
-                for (int p = 0; p < KP; ++p) {  // O = Qt S' (hi and lo parts of Qt)
+                for (int p = 0; p < KP; ++p) {  // O = Qt S': qh sh + ql sh + qh sl
                     const int off = r * C::RSQ + 2 * (32 * p + 8 * g);
-                    O = mfma32(lds_ld<bf16x8>(L + C::L_QH + off), Sb2[p], O);
+                    const bf16x8 qh = lds_ld<bf16x8>(L + C::L_QH + off);
+                    O = mfma32(qh, Sb2[p], O);
                     O = mfma32(lds_ld<bf16x8>(L + C::L_QL + off), Sb2[p], O);
+                    O = mfma32(qh, Sl2[p], O);
                 }
                 bf16x4 uh, ul;
                 split4(U, uh, ul);

@@ -4,6 +4,7 @@ CPU or PyTorch fallback."""
 from __future__ import annotations
 
 import ctypes
+import weakref
 from typing import Optional, Sequence, Union
 
 import torch
@@ -17,8 +18,12 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _on_gpu(t: torch.Tensor) -> bool:
+    return t.is_cuda
+
+
 def _check_dev(name, t, dtype=None):
-    if not t.is_cuda:
+    if not _on_gpu(t):
         raise ValueError(f"{name} must be a GPU tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
@@ -28,6 +33,62 @@ def _check_dev(name, t, dtype=None):
 
 def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
+
+
+def _check_out(name, t, shape, dtype, device):
+    """A caller-supplied output buffer: the kernels write exactly `shape` elements of
+    `dtype` at its address, so anything else is refused before the launch."""
+    _check_dev(name, t, dtype)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the inputs on {device}")
+
+
+def _check_cu_host(cu_host: Sequence[int], Ttot: int) -> None:
+    if len(cu_host) < 2:
+        raise ValueError("cu_seqlens needs at least two entries (N + 1, N >= 1)")
+    if cu_host[0] != 0:
+        raise ValueError(f"cu_seqlens[0] = {cu_host[0]}, must be 0")
+    for i in range(1, len(cu_host)):
+        if cu_host[i] < cu_host[i - 1]:
+            raise ValueError(f"cu_seqlens decreases at index {i}")
+    if cu_host[-1] != Ttot:
+        raise ValueError(f"cu_seqlens[-1] = {cu_host[-1]} but the inputs hold {Ttot} tokens")
+
+
+# device cu_seqlens tensors already compared with their host copy: id -> (weak reference,
+# version, host tuple).  A tensor whose version counter is unchanged has not been written
+# through torch since, so the comparison (a device-to-host copy and a synchronisation)
+# runs once per tensor and content, not per call.
+_cu_checked: dict = {}
+
+
+def _check_cu_device(cu_dev: torch.Tensor, cu_host: Sequence[int]) -> None:
+    hit = _cu_checked.get(id(cu_dev))
+    if hit is not None and hit[0]() is cu_dev and hit[1:] == (cu_dev._version, tuple(cu_host)):
+        return
+    if cu_dev.dim() != 1 or cu_dev.numel() != len(cu_host):
+        raise ValueError(f"cu_seqlens has shape {tuple(cu_dev.shape)}, expected "
+                         f"({len(cu_host)},)")
+    if [int(v) for v in cu_dev.tolist()] != [int(v) for v in cu_host]:
+        raise ValueError("cu_seqlens (device) differs from cu_seqlens_host")
+    if len(_cu_checked) > 64:
+        for key in [k for k, v in _cu_checked.items() if v[0]() is None]:
+            del _cu_checked[key]
+    _cu_checked[id(cu_dev)] = (weakref.ref(cu_dev), cu_dev._version, tuple(cu_host))
+
+
+def _device_cu(cu_seqlens, cu_host, dev) -> torch.Tensor:
+    """The device copy of cu_seqlens the kernels read, equal to cu_host."""
+    if isinstance(cu_seqlens, torch.Tensor) and _on_gpu(cu_seqlens):
+        if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_contiguous():
+            raise ValueError("a device cu_seqlens must be a contiguous int32 tensor")
+        if cu_seqlens.device != dev:
+            raise ValueError(f"cu_seqlens is on {cu_seqlens.device}, the inputs on {dev}")
+        _check_cu_device(cu_seqlens, cu_host)
+        return cu_seqlens
+    return torch.tensor(cu_host, dtype=torch.int32, device=dev)
 
 
 def chunk_prefill(q, k, v, log_alpha, beta, gate, cu_seqlens=None, initial_state=None,
@@ -82,23 +143,23 @@ def chunk_prefill(q, k, v, log_alpha, beta, gate, cu_seqlens=None, initial_state
         if tuple(t.shape) != shp:
             raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shp}")
     dev = qf.device
-    if isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.is_cuda:
-        cu_dev = cu_seqlens.to(torch.int32).contiguous()
-    else:
-        cu_dev = torch.tensor(cu_host, dtype=torch.int32, device=dev)
+    for name, t in (("k", kf), ("v", vf), ("log_alpha", laf), ("beta", bf), ("gate", gf)):
+        if t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, q on {dev}")
+    _check_cu_host(cu_host, Ttot)
+    cu_dev = _device_cu(cu_seqlens, cu_host, dev)
     cu_h = (ctypes.c_int32 * len(cu_host))(*cu_host)
     if initial_state is not None:
-        _check_dev("initial_state", initial_state, torch.float32)
-        if tuple(initial_state.shape) != (N, H, dk, dv):
-            raise ValueError("initial_state must be [N, H, dk, dv]")
+        _check_out("initial_state", initial_state, (N, H, dk, dv), torch.float32, dev)
     if out is None:
         out = torch.empty((Ttot, H, dv), dtype=dt, device=dev)
-    else:
-        _check_dev("out", out, dt)
+    else:  # [T_total, H, dv], or v's [B, T, H, dv]
+        _check_out("out", out, v.shape if q.dim() == 4 else (Ttot, H, dv), dt, dev)
+        out = out.reshape(Ttot, H, dv)
     if final_state is None and output_final_state:
         final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     elif final_state is not None:
-        _check_dev("final_state", final_state, torch.float32)
+        _check_out("final_state", final_state, (N, H, dk, dv), torch.float32, dev)
     p = _lib.params(_DT[dt], H, dk, dv, log_alpha_floor, scale)
     lib = _lib.load()
     if checkpoint_every is None:
@@ -114,9 +175,9 @@ def chunk_prefill(q, k, v, log_alpha, beta, gate, cu_seqlens=None, initial_state
         checkpoints = torch.empty((Ttot // m if m > 0 else 0, H, dk, dv), dtype=torch.float32,
                                   device=dev)
     else:
-        _check_dev("checkpoints", checkpoints, torch.float32)
-        if m > 0 and tuple(checkpoints.shape) != (Ttot // m, H, dk, dv):
-            raise ValueError("checkpoints must be [T_total // checkpoint_every, H, dk, dv]")
+        if m <= 0:
+            raise ValueError(f"checkpoint_every {m} must be a positive multiple of 16")
+        _check_out("checkpoints", checkpoints, (Ttot // m, H, dk, dv), torch.float32, dev)
     st = lib.kda_chunk_prefill_checkpointed(
         ctypes.byref(p), _ptr(qf), _ptr(kf), _ptr(vf), _ptr(laf), _ptr(bf), _ptr(gf),
         _ptr(cu_dev), cu_h, N, _ptr(initial_state), _ptr(final_state), _ptr(out), m,
@@ -146,11 +207,13 @@ def decode_step(q, k, v, log_alpha, beta, gate, state, log_alpha_floor: float = 
         _check_dev(name, t, dt)
         if tuple(t.shape) != shp:
             raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shp}")
-    _check_dev("state", state, torch.float32)
-    if tuple(state.shape) != (N, H, dk, dv):
-        raise ValueError("state must be [N, H, dk, dv]")
+        if t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q on {q.device}")
+    _check_out("state", state, (N, H, dk, dv), torch.float32, q.device)
     if out is None:
         out = torch.empty((N, H, dv), dtype=dt, device=q.device)
+    else:
+        _check_out("out", out, (N, H, dv), dt, q.device)
     p = _lib.params(_DT[dt], H, dk, dv, log_alpha_floor, scale)
     st = _lib.load().kda_decode_step(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
                                      _ptr(log_alpha), _ptr(beta), _ptr(gate), N,
@@ -184,10 +247,14 @@ def spec_verify(q, k, v, log_alpha, beta, gate, state, log_alpha_floor: float = 
     for name, t, d in (("q", q, dk), ("k", k, dk), ("v", v, dv), ("log_alpha", log_alpha, dk),
                        ("beta", beta, 0), ("gate", gate, dv)):
         _drafts(name, t, dt, N, K, H, d)
+    for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("beta", beta),
+                    ("gate", gate)):
+        if t.device != state.device:
+            raise ValueError(f"{name} is on {t.device}, state on {state.device}")
     if out is None:
         out = torch.empty(v.shape, dtype=dt, device=q.device)
     else:
-        _check_dev("out", out, dt)
+        _check_out("out", out, v.shape, dt, q.device)
     p = _lib.params(_DT[dt], H, dk, dv, log_alpha_floor, scale)
     st = _lib.load().kda_spec_verify(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
                                      _ptr(log_alpha), _ptr(beta), _ptr(gate), N, K,
@@ -211,6 +278,10 @@ def spec_commit(k, v, log_alpha, beta, state, accepted, log_alpha_floor: float =
     for name, t, d in (("k", k, dk), ("v", v, dv), ("log_alpha", log_alpha, dk),
                        ("beta", beta, 0)):
         _drafts(name, t, dt, N, K, H, d)
+        if t.device != state.device:
+            raise ValueError(f"{name} is on {t.device}, state on {state.device}")
+    if accepted.device != state.device:
+        raise ValueError(f"accepted is on {accepted.device}, state on {state.device}")
     p = _lib.params(_DT[dt], H, dk, dv, log_alpha_floor, 1.0)
     st = _lib.load().kda_spec_commit(ctypes.byref(p), _ptr(k), _ptr(v), _ptr(log_alpha),
                                      _ptr(beta), N, K, _ptr(accepted), _ptr(state),
@@ -243,10 +314,19 @@ def chunk_prefill_segmented(q, k, v, log_alpha, beta, gate, cu_seqlens, segment_
         _check_dev(name, t, dt)
         if tuple(t.shape) != shp:
             raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shp}")
+        if t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q on {q.device}")
+    _check_cu_host(cu_host, Ttot)
     if initial_state is not None:
-        _check_dev("initial_state", initial_state, torch.float32)
-        if tuple(initial_state.shape) != (N, H, dk, dv):
-            raise ValueError("initial_state must be [N, H, dk, dv]")
+        _check_out("initial_state", initial_state, (N, H, dk, dv), torch.float32, q.device)
+    if out is not None:
+        _check_out("out", out, (Ttot, H, dv), dt, q.device)
+    if final_state is not None:
+        _check_out("final_state", final_state, (N, H, dk, dv), torch.float32, q.device)
+    if workspace is not None:
+        _check_dev("workspace", workspace, torch.uint8)
+        if workspace.device != q.device:
+            raise ValueError(f"workspace is on {workspace.device}, q on {q.device}")
     cu_h = (ctypes.c_int32 * len(cu_host))(*cu_host)
     p = _lib.params(_DT[dt], H, dk, dv, log_alpha_floor, scale)
     lib = _lib.load()
@@ -257,8 +337,6 @@ def chunk_prefill_segmented(q, k, v, log_alpha, beta, gate, cu_seqlens, segment_
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     if out is None:
         out = torch.empty((Ttot, H, dv), dtype=dt, device=q.device)
-    else:
-        _check_dev("out", out, dt)
     if final_state is None and output_final_state:
         final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
     st = lib.kda_chunk_prefill_segmented(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
@@ -310,16 +388,14 @@ def prefill_backward(q, k, v, log_alpha, beta, gate, d_out, cu_seqlens=None,
         _check_dev(name, t, dt)
         if tuple(t.shape) != shp:
             raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shp}")
+        if t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q on {q.device}")
+    dev = q.device
     for name, t in (("initial_state", initial_state), ("d_final_state", d_final_state)):
         if t is not None:
-            _check_dev(name, t, torch.float32)
-            if tuple(t.shape) != (N, H, dk, dv):
-                raise ValueError(f"{name} must be [N, H, dk, dv]")
-    dev = q.device
-    if isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.is_cuda:
-        cu_dev = cu_seqlens.to(torch.int32).contiguous()
-    else:
-        cu_dev = torch.tensor(cu_host, dtype=torch.int32, device=dev)
+            _check_out(name, t, (N, H, dk, dv), torch.float32, dev)
+    _check_cu_host(cu_host, Ttot)
+    cu_dev = _device_cu(cu_seqlens, cu_host, dev)
     cu_h = (ctypes.c_int32 * len(cu_host))(*cu_host)
     p = _lib.params(_DT[dt], H, dk, dv, log_alpha_floor, scale)
     lib = _lib.load()
@@ -328,6 +404,10 @@ def prefill_backward(q, k, v, log_alpha, beta, gate, d_out, cu_seqlens=None,
         raise _lib.KdaError(_lib.KDA_ERR_INVALID_ARGUMENT, lib.kda_last_error().decode())
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    else:
+        _check_dev("workspace", workspace, torch.uint8)
+        if workspace.device != dev:
+            raise ValueError(f"workspace is on {workspace.device}, q on {dev}")
     f32 = lambda shp: torch.empty(shp, dtype=torch.float32, device=dev)
     g = dict(dq=f32((Ttot, H, dk)), dk=f32((Ttot, H, dk)), dv=f32((Ttot, H, dv)),
              dlog_alpha=f32((Ttot, H, dk)), dbeta=f32((Ttot, H)), dgate=f32((Ttot, H, dv)),

@@ -43,14 +43,11 @@ def plain_and_checkpointed(x, m, **kw):
     return o1, S1, ck
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128)])
-@pytest.mark.parametrize("m", [16, 48, 64])
-def test_snapshots_match_oracle_prefix_states(dtype, dk, dv, m):
+def snapshot_case(dtype, dk, dv, m, floor, log_alpha_min):
     lengths = (100, 0, 48, 129, 31, 64)
-    log(f"checkpoints dtype={dtype} dk={dk} dv={dv} m={m} lengths={lengths}")
-    x = ki.make_prefill_inputs(lengths, 2, dk, dv, dtype, 0.3, seed=7 * m + dk, device="cuda")
-    floor, scale = -0.4, 0.8
+    x = ki.make_prefill_inputs(lengths, 2, dk, dv, dtype, 0.3, seed=7 * m + dk, device="cuda",
+                               log_alpha_min=log_alpha_min)
+    scale = 0.8
     _, _, ck = plain_and_checkpointed(x, m, log_alpha_floor=floor, scale=scale)
     used = set()
     cu = x.cu_seqlens_host
@@ -64,6 +61,22 @@ def test_snapshots_match_oracle_prefix_states(dtype, dk, dv, m):
     for slot in range(ck.shape[0]):
         if slot not in used:
             assert torch.isnan(ck[slot]).all(), f"slot {slot} was written"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128)])
+@pytest.mark.parametrize("m", [16, 48, 64])
+def test_snapshots_match_oracle_prefix_states(dtype, dk, dv, m):
+    log(f"checkpoints dtype={dtype} dk={dk} dv={dv} m={m}")
+    snapshot_case(dtype, dk, dv, m, floor=-0.4, log_alpha_min=-0.3)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("floor", [-0.3, -0.5])
+def test_snapshots_log_decay_below_floor(dtype, floor):
+    """Log-decays drawn down to -2 with the floor at -0.3 / -0.5."""
+    log(f"checkpoints below-floor decays dtype={dtype} floor={floor}")
+    snapshot_case(dtype, 128, 128, 48, floor=floor, log_alpha_min=-2.0)
 
 
 def test_fewer_tokens_than_one_interval():

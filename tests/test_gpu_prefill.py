@@ -7,7 +7,7 @@ import torch
 
 import kda_inputs as ki
 import linear_attention_sequence_chunked_amd as kda
-from parity import assert_close, host, log, oracle_full, oracle_pairs
+from parity import assert_close, check_pairs, host, log, oracle_full
 
 pytestmark = pytest.mark.gpu
 DT = {"bf16": torch.bfloat16, "f32": torch.float32}
@@ -112,53 +112,77 @@ def test_guards_nan_poison_and_determinism():
     assert torch.equal(runs[0][0], runs[1][0]) and torch.equal(runs[0][1], runs[1][1])
 
 
-def sampled_check(x, pairs, o, S, dtype=torch.bfloat16):
-    ref = oracle_pairs(x, pairs)
-    got_o = np.concatenate([host(o[x.cu_seqlens_host[n]:x.cu_seqlens_host[n + 1], h])
-                            for n, h in pairs])
-    ref_o = np.concatenate([ref[p][0] for p in pairs])
-    assert_close("o (sampled)", got_o, ref_o, dtype)
-    assert_close("S_T (sampled)", np.stack([host(S[n, h]) for n, h in pairs]),
-                 np.stack([ref[p][1] for p in pairs]), dtype)
-
-
-def test_workload_b4_h16_t4096_sampled():
-    """B=4, H=16, T=4096, d=128, bf16, S0 ~ N(0, 0.02^2): the benchmark's workload and
-    launch configuration; sampled (sequence, head) pairs against the oracle."""
+def test_workload_b4_h16_t4096_every_pair():
+    """B=4, H=16, T=4096, d=128, bf16, S0 ~ N(0, 0.02^2): the whole workload (all 64
+    (sequence, head) pairs, every output row and final state) against the oracle, in the
+    launch configuration the benchmark times."""
     w = ki.WORKLOADS["prefill_b4_h16_t4096"]
-    log("prefill workload b4_h16_t4096")
+    log("prefill workload b4_h16_t4096, every pair")
     x = ki.make_workload_inputs(w, seed=1, device="cuda")
     o, S = run(x)
-    assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
-    sampled_check(x, [(0, 0), (1, 7), (2, 15), (3, 3)], o, S)
+    ro, rS = oracle_full(x)
+    assert_close("o", host(o), ro, torch.bfloat16)
+    assert_close("S_T", host(S), rS, torch.bfloat16)
 
 
-def test_workload_b1_h32_t131072_sampled():
-    """Long context: B=1, H=32, T=131072, d=128, bf16, zero S0; three heads checked."""
+def test_workload_b1_h32_t131072_every_head():
+    """Long context: B=1, H=32, T=131072, d=128, bf16, zero S0: every head against the
+    oracle, downloaded and checked eight heads at a time."""
     w = ki.WORKLOADS["prefill_b1_h32_t131072"]
-    log("prefill workload b1_h32_t131072")
+    log("prefill workload b1_h32_t131072, every head")
     x = ki.make_workload_inputs(w, seed=2, device="cuda")
     o, S = run(x)
     assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
-    sampled_check(x, [(0, 0), (0, 13), (0, 31)], o, S)
+    for h0 in range(0, w.H, 8):
+        check_pairs(x, [(0, h) for h in range(h0, h0 + 8)], o, S,
+                    label=f"heads {h0}..{h0 + 7}")
+
+
+def varlen_pairs(lengths, H, per_class=16):
+    """per_class (sequence, head) pairs from every length class of the varlen mix,
+    spread over the class's sequences and over the heads."""
+    classes = sorted(set(lengths))
+    out = {}
+    for c in classes:
+        seqs = [n for n, L in enumerate(lengths) if L == c]
+        out[c] = [(seqs[j % len(seqs)], (5 * j + c // 8192) % H)
+                  for j in range(per_class)]
+        assert len(set(out[c])) == per_class
+    return out
 
 
 @pytest.mark.skipif(os.environ.get("KDA_SKIP_HUGE") == "1", reason="KDA_SKIP_HUGE=1")
-def test_workload_varlen_n64_h32_sampled():
+def test_workload_varlen_n64_h32_every_length_class():
     """64 packed sequences, lengths 40% 8K / 42% 32K / 15% 128K / 3% 256K (3.77M tokens,
-    ~185 GB of device tensors), H=32, d=128, per-sequence S0."""
+    ~185 GB of device tensors), H=32, d=128, per-sequence S0: 16 (sequence, head) pairs
+    of every length class (64 pairs, 6.9M token-heads) against the oracle."""
     w = ki.WORKLOADS["varlen_n64_h32"]
     log(f"prefill workload varlen_n64_h32 T_total={sum(w.lengths)}")
     x = ki.make_workload_inputs(w, seed=4, device="cuda")
     o, S = run(x)
-    lens = w.lengths
-    short = lens.index(8192)
-    mid = lens.index(32768)
-    longest = lens.index(max(lens))
     assert torch.isfinite(S).all()
-    sampled_check(x, [(short, 0), (mid, 31), (longest, 17)], o, S)
+    for L, pairs in varlen_pairs(w.lengths, w.H).items():
+        check_pairs(x, pairs, o, S, label=f"length {L}")
     del x, o, S
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("floor", [-0.3, -0.5])
+def test_log_decay_below_floor(dtype, floor):
+    """Log-decays drawn down to -2 with the floor at -0.3 / -0.5, so most of them are
+    clamped: a kernel that skipped the clamp (or clamped elsewhere) fails."""
+    log(f"prefill below-floor decays dtype={dtype} floor={floor}")
+    x = ki.make_prefill_inputs((37, 0, 16, 1, 50, 200), 3, 128, 128, dtype, 0.3,
+                               seed=77, device="cuda", log_alpha_min=-2.0)
+    assert float(x.log_alpha.float().min()) < floor - 1.0
+    check_full(x, dtype, log_alpha_floor=floor, scale=0.9)
+    # the same inputs with the clamp applied beforehand give the same result
+    xc = ki.KdaInputs(x.q, x.k, x.v, torch.clamp(x.log_alpha, min=floor), x.beta, x.gate,
+                      x.cu_seqlens, x.cu_seqlens_host, x.initial_state)
+    o, S = run(x, log_alpha_floor=floor, scale=0.9)
+    oc, Sc = run(xc, log_alpha_floor=floor, scale=0.9)
+    assert torch.equal(o, oc) and torch.equal(S, Sc)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])

@@ -38,6 +38,22 @@ def test_segmented_matches_oracle(dtype, dk, dv, L):
     assert_close("S_T", host(S), rS, DT[dtype])
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("floor", [-0.3, -0.5])
+def test_segmented_log_decay_below_floor(dtype, floor):
+    """Log-decays drawn from [-2, 0] with the floor at -0.3 / -0.5: the clamp acts in the
+    segment states, the segment transitions and the output pass alike."""
+    lengths = (300, 17, 1000)
+    log(f"segmented below-floor decays dtype={dtype} floor={floor}")
+    x = ki.make_prefill_inputs(lengths, 2, 128, 128, dtype, 0.3, seed=91, device="cuda",
+                               log_alpha_min=-2.0)
+    assert float(x.log_alpha.float().min()) < floor - 1.0
+    o, S = segmented(x, 64, scale=0.9, log_alpha_floor=floor)
+    ro, rS = oracle_full(x, floor=floor, scale=0.9)
+    assert_close("o", host(o), ro, DT[dtype])
+    assert_close("S_T", host(S), rS, DT[dtype])
+
+
 def test_segmented_in_place_state_and_empty_batch():
     x = ki.make_prefill_inputs((0, 0), 2, 64, 64, "bf16", 0.3, seed=1, device="cuda")
     st = x.initial_state.clone()

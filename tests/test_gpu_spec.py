@@ -19,9 +19,10 @@ pytestmark = pytest.mark.gpu
 DT = {"bf16": torch.bfloat16, "f32": torch.float32}
 
 
-def drafts(N, K, H, dk, dv, dtype, seed):
+def drafts(N, K, H, dk, dv, dtype, seed, log_alpha_min=-0.3):
     """N sequences of K drafts, packed sequence-major ([N*K, H, .]), plus states."""
-    x = ki.make_prefill_inputs((K,) * N, H, dk, dv, dtype, 0.3, seed=seed, device="cuda")
+    x = ki.make_prefill_inputs((K,) * N, H, dk, dv, dtype, 0.3, seed=seed, device="cuda",
+                               log_alpha_min=log_alpha_min)
     return x
 
 
@@ -62,14 +63,10 @@ def decode_steps(x, N, K, a, floor, scale):
     return outs, res
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64), (128, 128)])
-@pytest.mark.parametrize("K", [1, 4, 16])
-def test_verify_and_every_accepted_length(dtype, dk, dv, K):
+def verify_and_commit_case(dtype, dk, dv, K, floor, log_alpha_min):
     N, H = K + 3, 2
-    log(f"spec dtype={dtype} dk={dk} dv={dv} K={K}")
-    x = drafts(N, K, H, dk, dv, dtype, seed=100 + K + dk)
-    floor, scale = -0.4, 0.9
+    x = drafts(N, K, H, dk, dv, dtype, seed=100 + K + dk, log_alpha_min=log_alpha_min)
+    scale = 0.9
     # every length 0..K once, then values past both ends (clamped)
     a = list(range(K + 1)) + [K + 5, -2]
     assert len(a) == N
@@ -90,6 +87,23 @@ def test_verify_and_every_accepted_length(dtype, dk, dv, K):
     torch.cuda.synchronize()
     assert torch.equal(o, do), "verify differs from consecutive decode steps"
     assert torch.equal(state, dS), "commit differs from consecutive decode steps"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64), (128, 128)])
+@pytest.mark.parametrize("K", [1, 4, 16])
+def test_verify_and_every_accepted_length(dtype, dk, dv, K):
+    log(f"spec dtype={dtype} dk={dk} dv={dv} K={K}")
+    verify_and_commit_case(dtype, dk, dv, K, floor=-0.4, log_alpha_min=-0.3)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("floor", [-0.3, -0.5])
+@pytest.mark.parametrize("K", [4, 16])
+def test_log_decay_below_floor(dtype, floor, K):
+    """Draft log-decays drawn down to -2 with the floor at -0.3 / -0.5."""
+    log(f"spec below-floor decays dtype={dtype} floor={floor} K={K}")
+    verify_and_commit_case(dtype, 128, 128, K, floor=floor, log_alpha_min=-2.0)
 
 
 def test_decode_workload_with_four_drafts():
