@@ -171,6 +171,36 @@ int64_t kda_prefill_segmented_workspace(const kda_params* params,
                                         int32_t segment_len);
 
 /*
+ * kda_chunk_prefill_segmented_noalloc -- kda_chunk_prefill_segmented without a workspace
+ * argument, for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  It allocates nothing
+ * (no hipMalloc, hipFree or allocating library routine); the workspace is the library's
+ * fixed device buffer of kda_noalloc_scratch_bytes() bytes (64 MiB), which each GPU the
+ * library runs on holds from the first such call until the process ends.
+ *
+ *   Arguments, results and errors are those of kda_chunk_prefill_segmented without
+ *   workspace / workspace_bytes.  A problem whose workspace
+ *   (kda_prefill_segmented_workspace) exceeds kda_noalloc_scratch_bytes() is rejected
+ *   with KDA_ERR_INVALID_ARGUMENT before any HIP call; about 192 KB per
+ *   (segment, head) at dk = dv = 128, e.g. up to 340 (segment, head) pairs.
+ *   Every call on one GPU uses that GPU's one buffer: calls that overlap on a GPU
+ *   (different streams or threads without ordering between them) race and give wrong
+ *   results.  Calls ordered on one stream are safe; nothing in the buffer has to start
+ *   at zero (each call writes every byte it later reads).
+ */
+kda_status kda_chunk_prefill_segmented_noalloc(const kda_params* params, const void* q,
+                                               const void* k, const void* v,
+                                               const void* log_alpha, const void* beta,
+                                               const void* gate,
+                                               const int32_t* cu_seqlens_host,
+                                               int32_t num_seqs, const float* initial_state,
+                                               float* final_state, void* out,
+                                               int32_t segment_len, void* stream);
+
+/* Size in bytes of the fixed device buffer behind kda_chunk_prefill_segmented_noalloc. */
+int64_t kda_noalloc_scratch_bytes(void);
+
+/*
  * kda_prefill_backward -- gradients of kda_chunk_prefill (the training form), fp32.
  *
  * Given the forward's inputs and the gradients of its outputs, writes the gradient of the

@@ -11,7 +11,8 @@ KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP = 0, 1, 2, 3
 KDA_DTYPE_BF16, KDA_DTYPE_F32 = 0, 1
 EXPORTED = ("kda_chunk_prefill", "kda_chunk_prefill_checkpointed", "kda_decode_step",
             "kda_spec_verify", "kda_spec_commit", "kda_chunk_prefill_segmented",
-            "kda_prefill_segmented_workspace", "kda_prefill_backward",
+            "kda_prefill_segmented_workspace", "kda_chunk_prefill_segmented_noalloc",
+            "kda_noalloc_scratch_bytes", "kda_prefill_backward",
             "kda_prefill_backward_workspace", "kda_status_string", "kda_last_error",
             "kda_abi_version")
 
@@ -63,6 +64,11 @@ def load() -> ctypes.CDLL:
     lib.kda_prefill_segmented_workspace.argtypes = [ctypes.POINTER(KdaParams),
                                                     ctypes.POINTER(I32), I32, I32]
     lib.kda_prefill_segmented_workspace.restype = ctypes.c_int64
+    lib.kda_chunk_prefill_segmented_noalloc.argtypes = [
+        ctypes.POINTER(KdaParams), P, P, P, P, P, P, ctypes.POINTER(I32), I32, P, P, P, I32, P]
+    lib.kda_chunk_prefill_segmented_noalloc.restype = ctypes.c_int
+    lib.kda_noalloc_scratch_bytes.argtypes = []
+    lib.kda_noalloc_scratch_bytes.restype = ctypes.c_int64
     lib.kda_prefill_backward.argtypes = [ctypes.POINTER(KdaParams), P, P, P, P, P, P, P,
                                          ctypes.POINTER(I32), I32, P, P, P, P, P, P, P, P, P,
                                          P, P, ctypes.c_int64, P]

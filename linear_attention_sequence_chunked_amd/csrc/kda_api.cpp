@@ -431,16 +431,28 @@ int64_t kda_prefill_segmented_workspace(const kda_params* params,
     return (int64_t)pl.total;
 }
 
-kda_status kda_chunk_prefill_segmented(const kda_params* params, const void* q,
-                                       const void* k, const void* v, const void* log_alpha,
-                                       const void* beta, const void* gate,
-                                       const int32_t* cu_seqlens_host, int32_t num_seqs,
-                                       const float* initial_state, float* final_state,
-                                       void* out, int32_t segment_len, void* workspace,
-                                       int64_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// kda_chunk_prefill_segmented's work on a workspace the caller or the library provides;
+// `noalloc` resolves the library's fixed buffer once the arguments have been checked.
+kda_status segmented(const char* entry, const kda_params* params, const void* q,
+                     const void* k, const void* v, const void* log_alpha, const void* beta,
+                     const void* gate, const int32_t* cu_seqlens_host, int32_t num_seqs,
+                     const float* initial_state, float* final_state, void* out,
+                     int32_t segment_len, void* workspace, int64_t workspace_bytes,
+                     bool noalloc, void* stream) {
     SegPlan pl;
     kda_status st = seg_plan(params, cu_seqlens_host, num_seqs, segment_len, pl);
     if (st != KDA_OK) return st;
+    if (noalloc && pl.total > kda::kScratchBytes)
+        return fail(KDA_ERR_INVALID_ARGUMENT,
+                    "%s: the segments need %llu bytes of scratch, more than the %llu bytes "
+                    "of the library's fixed buffer (use longer segments, fewer heads or "
+                    "sequences per call, or kda_chunk_prefill_segmented with a workspace)",
+                    entry, (unsigned long long)pl.total,
+                    (unsigned long long)kda::kScratchBytes);
     const kda_params& p = *params;
     const int64_t T = cu_seqlens_host[num_seqs];
     const int64_t H = p.num_heads;
@@ -454,19 +466,24 @@ kda_status kda_chunk_prefill_segmented(const kda_params* params, const void* q,
     }
     if (initial_state && (st = check_ptr("initial_state", initial_state, 16)) != KDA_OK) return st;
     if (final_state && (st = check_ptr("final_state", final_state, 16)) != KDA_OK) return st;
-    if ((st = check_ptr("workspace", workspace, 256)) != KDA_OK) return st;
-    if (workspace_bytes < (int64_t)pl.total)
-        return fail(KDA_ERR_INVALID_ARGUMENT, "workspace_bytes %lld < %llu needed",
-                    (long long)workspace_bytes, (unsigned long long)pl.total);
+    if (!noalloc) {
+        if ((st = check_ptr("workspace", workspace, 256)) != KDA_OK) return st;
+        if (workspace_bytes < (int64_t)pl.total)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "workspace_bytes %lld < %llu needed",
+                        (long long)workspace_bytes, (unsigned long long)pl.total);
+    }
     const uint64_t nk = (uint64_t)T * H * p.dk * es, nv = (uint64_t)T * H * p.dv * es;
     const uint64_t ns = (uint64_t)num_seqs * H * p.dk * p.dv * 4;
     const Range args[] = {range("q", q, nk), range("k", k, nk), range("v", v, nv),
                           range("log_alpha", log_alpha, nk), range("beta", beta, (uint64_t)T * H * es),
                           range("gate", gate, nv), range("initial_state", initial_state, ns),
                           range("final_state", final_state, ns), range("out", out, nv)};
-    const Range rw = range("workspace", workspace, pl.total);
-    for (const Range& r : args)
-        if (overlaps(rw, r)) return fail(KDA_ERR_INVALID_ARGUMENT, "workspace overlaps %s", r.name);
+    if (!noalloc) {
+        const Range rw = range("workspace", workspace, pl.total);
+        for (const Range& r : args)
+            if (overlaps(rw, r))
+                return fail(KDA_ERR_INVALID_ARGUMENT, "workspace overlaps %s", r.name);
+    }
     const Range ro = args[8];
     for (int i = 0; i < 8; ++i)
         if (overlaps(ro, args[i])) return fail(KDA_ERR_INVALID_ARGUMENT, "out overlaps %s", args[i].name);
@@ -479,6 +496,11 @@ kda_status kda_chunk_prefill_segmented(const kda_params* params, const void* q,
             return fail(KDA_ERR_INVALID_ARGUMENT, "final_state overlaps initial_state");
     }
 
+    if (noalloc) {  // every argument is valid: resolve this device's fixed buffer
+        const hipError_t e = kda::scratch_address(&workspace);
+        if (e != hipSuccess)
+            return fail(KDA_ERR_HIP, "%s: scratch buffer address: %s", entry, hipGetErrorString(e));
+    }
     char* ws = static_cast<char*>(workspace);
     int32_t* seg_cu = reinterpret_cast<int32_t*>(ws + pl.off_cu);
     int32_t* seg_first = reinterpret_cast<int32_t*>(ws + pl.off_first);
@@ -489,7 +511,7 @@ kda_status kda_chunk_prefill_segmented(const kda_params* params, const void* q,
     hipError_t e = write_table(seg_cu, pl.seg_cu, hs);
     if (e == hipSuccess) e = write_table(seg_first, pl.seg_first, hs);
     if (e != hipSuccess)
-        return fail(KDA_ERR_HIP, "kda_chunk_prefill_segmented tables: %s", hipGetErrorString(e));
+        return fail(KDA_ERR_HIP, "%s tables: %s", entry, hipGetErrorString(e));
 
     const int cus = device_cu_count();
     kda::PrefillArgs a;
@@ -529,9 +551,40 @@ kda_status kda_chunk_prefill_segmented(const kda_params* params, const void* q,
         phase = "outputs";
     }
     if (e != hipSuccess)
-        return fail(KDA_ERR_HIP, "kda_chunk_prefill_segmented (%s): %s", phase, hipGetErrorString(e));
+        return fail(KDA_ERR_HIP, "%s (%s): %s", entry, phase, hipGetErrorString(e));
     return ok();
 }
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_chunk_prefill_segmented(const kda_params* params, const void* q,
+                                       const void* k, const void* v, const void* log_alpha,
+                                       const void* beta, const void* gate,
+                                       const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                       const float* initial_state, float* final_state,
+                                       void* out, int32_t segment_len, void* workspace,
+                                       int64_t workspace_bytes, void* stream) {
+    return segmented("kda_chunk_prefill_segmented", params, q, k, v, log_alpha, beta, gate,
+                     cu_seqlens_host, num_seqs, initial_state, final_state, out, segment_len,
+                     workspace, workspace_bytes, false, stream);
+}
+
+kda_status kda_chunk_prefill_segmented_noalloc(const kda_params* params, const void* q,
+                                               const void* k, const void* v,
+                                               const void* log_alpha, const void* beta,
+                                               const void* gate,
+                                               const int32_t* cu_seqlens_host,
+                                               int32_t num_seqs, const float* initial_state,
+                                               float* final_state, void* out,
+                                               int32_t segment_len, void* stream) {
+    return segmented("kda_chunk_prefill_segmented_noalloc", params, q, k, v, log_alpha, beta,
+                     gate, cu_seqlens_host, num_seqs, initial_state, final_state, out,
+                     segment_len, nullptr, 0, true, stream);
+}
+
+int64_t kda_noalloc_scratch_bytes(void) { return (int64_t)kda::kScratchBytes; }
 
 }  // extern "C"
 

@@ -71,6 +71,11 @@ struct CombineArgs {
     int H;
 };
 hipError_t launch_table(const TableArgs& a, hipStream_t stream);
+
+// The fixed device buffer behind kda_chunk_prefill_segmented_noalloc (kda_scratch.hip):
+// its size, and its address on the current device (resolved once per device).
+constexpr uint64_t kScratchBytes = 64ull << 20;
+hipError_t scratch_address(void** ptr);
 hipError_t launch_combine(const CombineArgs& a, int num_seqs, int dk, int dv, hipStream_t stream);
 
 // Backward of the prefill (kda_backward.hip).

@@ -308,3 +308,19 @@ def test_backward_rejects(kw, msg):
     st, err = backward(**kw)
     assert st == INV, err
     assert msg in err, err
+
+
+def test_noalloc_rejects_problems_beyond_its_fixed_buffer():
+    """The no-alloc segmented prefill refuses, before any HIP call, a problem whose
+    workspace would not fit the library's fixed buffer."""
+    lib = _lib.load()
+    assert lib.kda_noalloc_scratch_bytes() == 64 << 20
+    p = _lib.params(_lib.KDA_DTYPE_BF16, 64, 128, 128)
+    cu_h = cu(0, 1 << 20)
+    need = lib.kda_prefill_segmented_workspace(ctypes.byref(p), cu_h, 1, 16384)
+    assert need > lib.kda_noalloc_scratch_bytes()
+    st = lib.kda_chunk_prefill_segmented_noalloc(ctypes.byref(p), A, A + 0x10000, A + 0x20000,
+                                                 A + 0x30000, A + 0x40000, A + 0x50000, cu_h,
+                                                 1, None, None, A + 0x70000, 16384, None)
+    assert st == INV
+    assert "fixed buffer" in lib.kda_last_error().decode()
