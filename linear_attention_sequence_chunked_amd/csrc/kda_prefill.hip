@@ -386,7 +386,8 @@ int prefill_pick_nv(int dv, int64_t num_pairs, int64_t longest_chunks, int cu_co
 hipError_t launch_prefill(const PrefillArgs& p, hipStream_t st) {
     if (p.dtype == DTYPE_BF16) {
         PrefillArgs q = p;
-        while (!prefill_bf16_supports(q.dk, q.dv, q.nv) && q.nv > 16) q.nv /= 2;
+        while (!prefill_bf16_supports(q.dk, q.dv, q.nv, q.checkpoints != nullptr) && q.nv > 16)
+            q.nv /= 2;
         return launch_prefill_bf16(q, st);
     }
     return launch_dims<float>(p, st);

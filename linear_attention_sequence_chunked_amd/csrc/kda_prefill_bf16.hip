@@ -27,7 +27,8 @@
 // entries below one in size, and T only enters through bf16 operands anyway).
 //
 // Workgroup = one (sequence, head, slice of NV = 16*NCB value columns).  Waves:
-//   chain  (NCB)   : one 16-column block of S each; state step of chunk c
+//   chain  (NCB/2) : two 16-column blocks of S each (one when NCB = 1), so every operand
+//                    read from LDS serves 32 columns; state step of chunk c
 //   decay  (DK/32) : 32 key channels each; row tiles of chunk c+3 from registers
 //                    loaded PF chunks earlier
 //   gram           : A, A^T of chunk c+2 and T through the nilpotent product
@@ -203,7 +204,11 @@ struct Cfg {
     static constexpr int NDW = DK / 32;       // decay waves (32 channels each)
     static constexpr int KP = DK / 32;        // 32-channel steps of the state products
     static constexpr int NV = 16 * NCB;       // value columns per workgroup
-    static constexpr int NCHAIN = NCB;
+    // column blocks per chain wave: two in the full-width (eight-block) workgroup, so each
+    // operand a chain wave reads from LDS (Wt, Qt, P, Kb, T) serves 32 columns and four
+    // chain waves cover 128 columns; one otherwise (the shortest state step per chunk)
+    static constexpr int CPW = NCB >= 8 ? 2 : 1;
+    static constexpr int NCHAIN = NCB / CPW;
     static constexpr int PF = 4;              // chunks of input prefetched ahead (ring depth)
     static constexpr int W_DECAY0 = NCHAIN;
     static constexpr int W_GRAM = NCHAIN + NDW;
@@ -247,7 +252,7 @@ struct Cfg {
     static constexpr int ORS = 40, O_SIZE = 16 * ORS;
     static constexpr int OFF_L = 0, OFF_K = OFF_L + 4 * L_SIZE, OFF_B = OFF_K + 4 * K_SIZE,
                          OFF_G = OFF_B + 2 * B_SIZE, OFF_W = OFF_G + 4 * G_SIZE,
-                         OFF_O = OFF_W + 2 * W_SIZE, LDS_BYTES = OFF_O + NCHAIN * O_SIZE;
+                         OFF_O = OFF_W + 2 * W_SIZE, LDS_BYTES = OFF_O + NCB * O_SIZE;
 };
 
 struct BArgs {
@@ -289,12 +294,14 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
     const int nch = (int)((len + 15) / 16);
     const int col0 = slice * NV;
     if (nch == 0) {  // empty sequence: the final state is the initial state
-        if (a.Sf && wave < NCB) {
+        if (a.Sf && wave < C::NCHAIN) {
             const int64_t base = ((int64_t)seq * H + h) * DK * DV;
-            for (int row = lane >> 4; row < DK; row += 4)
-                a.Sf[base + row * DV + col0 + 16 * wave + (lane & 15)] =
-                    a.S0 ? a.S0[base + row * DV + col0 + 16 * wave + (lane & 15)]
-                         : (a.s0_identity && row == col0 + 16 * wave + (lane & 15)) ? 1.f : 0.f;
+            for (int cb = 0; cb < C::CPW; ++cb) {
+                const int col = col0 + 16 * (C::CPW * wave + cb) + (lane & 15);
+                for (int row = lane >> 4; row < DK; row += 4)
+                    a.Sf[base + row * DV + col] =
+                        a.S0 ? a.S0[base + row * DV + col] : (a.s0_identity && row == col) ? 1.f : 0.f;
+            }
         }
         return;
     }
@@ -484,6 +491,8 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
                                rvg[e][ph]);
                 }
             }
+            if (c == nch)  // one past the last chunk: gamma = 1 (the chain's decay step after its last update)
+                lds_st(lslot(c) + C::L_GAM + 4 * (dch + (r & 7)), 1.0f);
             load(PH);  // chunk it + 3 + PF; past the last chunk: reads nothing (zero rows)
             lds_barrier();
         };
@@ -594,99 +603,192 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
         // The state step is the serial critical path: its instructions win issue
         // arbitration over the other roles' on the same SIMD.
         __builtin_amdgcn_s_setprio(3);
-        // fp32 state S' of rows 16b+4g+i, value column ccol, in MFMA accumulator layout
-        const int ccol = col0 + 16 * wave + r;
-        f32x4 S[KB];
+        constexpr int CPW = C::CPW;
+        // fp32 state S' of rows 16b+4g+i, value column ccol[cb], in MFMA accumulator layout
+        int ccol[CPW];
 #pragma unroll
-        for (int b = 0; b < KB; ++b)
+        for (int cb = 0; cb < CPW; ++cb) ccol[cb] = col0 + 16 * (CPW * wave + cb) + r;
+        f32x4 S[CPW][KB];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                S[b][i] = a.S0 ? a.S0[sbase + (16 * b + 4 * g + i) * DV + ccol]
-                               : (a.s0_identity && 16 * b + 4 * g + i == ccol) ? 1.f : 0.f;
+        for (int cb = 0; cb < CPW; ++cb)
+#pragma unroll
+            for (int b = 0; b < KB; ++b)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    S[cb][b][i] = a.S0 ? a.S0[sbase + (16 * b + 4 * g + i) * DV + ccol[cb]]
+                                       : (a.s0_identity && 16 * b + 4 * g + i == ccol[cb]) ? 1.f : 0.f;
         const float scale = a.scale;
+        // A-fragments of -I in the lower or upper half of a 32-deep operand (element j of
+        // lane (r, g) is row r, K-slot 4g + j): -I hi + C selects one channel block of the
+        // stacked B operand, exactly.
+        bf16x4 nid4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) nid4[j] = (4 * g + j == r) ? (bf16)-1.0f : (bf16)0.0f;
+        const bf16x8 nid_lo = cat8(nid4, zero_bf4()), nid_hi = cat8(zero_bf4(), nid4);
         // snapshots: the state after every ck_chunks-th chunk (when that chunk is full) goes
         // to slot tbeg / m + j - 1 for the j-th snapshot, m = 16 ck_chunks tokens
         int ck_left = a.ck_chunks;
         int64_t ck_slot = CK ? tbeg / (16 * (int64_t)a.ck_chunks) : 0;
         for (int it = -3; it < it_end; ++it) {
             const int c = it;  // state step of chunk c
+            if (c == -1 && nch > 0) {  // S' of chunk 0 (its gamma was written at iteration -3)
+                const float* g0 = reinterpret_cast<const float*>(lslot(0) + C::L_GAM);
+#pragma unroll
+                for (int b = 0; b < KB; ++b) {
+                    const f32x4 gm = *reinterpret_cast<const f32x4*>(g0 + 16 * b + 4 * g);
+#pragma unroll
+                    for (int cb = 0; cb < CPW; ++cb) S[cb][b] *= gm;
+                }
+            }
             if (c >= 0 && c < nch) {
                 const unsigned char* L = lslot(c);
                 const unsigned char* Gs = gslot(c);
                 const unsigned char* W = wslot(c);
-                // S' = Diag(gamma) S, and its bf16 copy as 32-deep B operands: Sb2[p] holds
-                // the rows of channel blocks 2p and 2p+1 (the B operands of Wt S' and Qt S')
-                const float* gc = reinterpret_cast<const float*>(L + C::L_GAM);
-                bf16x8 Sb2[KP], Sl2[KP];
-#pragma unroll
-                for (int b = 0; b < KB; ++b) S[b] *= *reinterpret_cast<const f32x4*>(gc + 16 * b + 4 * g);
-#pragma unroll
-                for (int p = 0; p < KP; ++p) {  // S' = hi + lo; the readout takes both halves
-                    bf16x4 h0, l0, h1, l1;
-                    split4(S[2 * p], h0, l0);
-                    split4(S[2 * p + 1], h1, l1);
-                    Sb2[p] = cat8(h0, h1);
-                    Sl2[p] = cat8(l0, l1);
-                }
-                // Ut = T V
+                // S holds S' = Diag(gamma) S (the decay of this chunk was applied after the
+                // previous update).  It is split as S' = hi + lo: hi = bf16(S'),
+                // lo = bf16(S' - hi).  The residual S' - hi (exact in fp32) comes from the
+                // matrix core as -I hi + S', which keeps it off the VALU and leaves S' in place
+                // as the accumulator of the state update.
+                // Operands are read from LDS one step ahead of the products that use them
+                // (the scheduling barriers keep each step's reads ahead of the previous
+                // step's products), so LDS latency overlaps the matrix core instead of
+                // stalling it once per step.
+                struct Ops { bf16x8 wt, qh, ql; };
+                auto ldp = [&](int p) {
+                    Ops o;
+                    o.wt = lds_ld<bf16x8>(W + C::W_WT + p * 1024 + lane * 16);
+                    const int off = r * C::RSQ + 2 * (32 * p + 8 * g);
+                    o.qh = lds_ld<bf16x8>(L + C::L_QH + off);
+                    o.ql = lds_ld<bf16x8>(L + C::L_QL + off);
+                    return o;
+                };
+                auto ldk = [&](int b) {  // Kb^T fragments of row block b, hi | lo
+                    return cat8(lds_tr(L + C::L_KBH + tr_k + tr_blk(b)), lds_tr(L + C::L_KBL + tr_k + tr_blk(b)));
+                };
+                // the next chunk's gamma (its decay tiles were written three iterations ago;
+                // past the last chunk the decay waves store gamma = 1)
+                const float* gn = reinterpret_cast<const float*>(lslot(c + 1) + C::L_GAM);
+                auto ldg = [&](int b) { return *reinterpret_cast<const f32x4*>(gn + 16 * b + 4 * g); };
                 // Ut = T V: T^T is stored with a zero upper half (one 32-deep step; each
                 // accumulator is fed by one instruction shape only)
                 const bf16x8 tt0 = lds_ld<bf16x8>(Gs + C::G_TT + lane * 16);
-                f32x4 U = mfma32(tt0, cat8(lds_tr(L + C::L_V + tr_v + 32 * wave), zero_bf4()), zero4());
+                bf16x4 vt[CPW];
 #pragma unroll
-                for (int p = 0; p < KP; ++p)  // U = Ut - Wt S' (channel blocks 2p, 2p+1 stacked)
-                    U = mfma32(lds_ld<bf16x8>(W + C::W_WT + p * 1024 + lane * 16), Sb2[p], U);
-                f32x4 O = zero4();
+                for (int cb = 0; cb < CPW; ++cb) vt[cb] = lds_tr(L + C::L_V + tr_v + 32 * (CPW * wave + cb));
+                Ops o0 = ldp(0), o1;
+                __builtin_amdgcn_sched_barrier(0);
+                f32x4 U[CPW], O[CPW];
 #pragma unroll
-                for (int p = 0; p < KP; ++p) {  // O = Qt S': qh sh + ql sh + qh sl
-                    const int off = r * C::RSQ + 2 * (32 * p + 8 * g);
-                    const bf16x8 qh = lds_ld<bf16x8>(L + C::L_QH + off);
-                    O = mfma32(qh, Sb2[p], O);
-                    O = mfma32(lds_ld<bf16x8>(L + C::L_QL + off), Sb2[p], O);
-                    O = mfma32(qh, Sl2[p], O);
+                for (int cb = 0; cb < CPW; ++cb) {
+                    U[cb] = mfma32(tt0, cat8(vt[cb], zero_bf4()), zero4());
+                    O[cb] = zero4();
                 }
-                bf16x4 uh, ul;
-                split4(U, uh, ul);
-                const bf16x8 uu = cat8(uh, uh), ul0 = cat8(ul, zero_bf4());
-                const bf16x8 pp = lds_ld<bf16x8>(Gs + C::G_P + lane * 16);  // P hi | P lo
-                O = mfma32(pp, uu, O);   // + P U: ph uh + pl uh
-                O = mfma32(pp, ul0, O);  //        + ph ul
-                // S <- S' + Kb^T U, row block by row block: kh uh + kl uh, then kh ul
+                unroll<0, KP>([&](auto PI) {  // channel blocks 2p, 2p+1 stacked
+                    constexpr int p = decltype(PI)::value;
+                    Ops& cur = (p & 1) ? o1 : o0;
+                    Ops& nxt = (p & 1) ? o0 : o1;
+                    if constexpr (p + 1 < KP) nxt = ldp(p + 1);
+                    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int b = 0; b < KB; ++b) {
-                    const bf16x8 kk = cat8(lds_tr(L + C::L_KBH + tr_k + tr_blk(b)),
-                                           lds_tr(L + C::L_KBL + tr_k + tr_blk(b)));
-                    S[b] = mfma32(kk, uu, S[b]);
-                    S[b] = mfma32(kk, ul0, S[b]);
+                    for (int cb = 0; cb < CPW; ++cb) {  // S holds S' = Diag(gamma) S already
+                        const bf16x8 sh = to_bf8(S[cb][2 * p], S[cb][2 * p + 1]);
+                        const bf16x8 sl = to_bf8(mfma32(nid_lo, sh, S[cb][2 * p]),       // S' - hi
+                                                 mfma32(nid_hi, sh, S[cb][2 * p + 1]));
+                        U[cb] = mfma32(cur.wt, sh, U[cb]);  // U = Ut - Wt S'
+                        O[cb] = mfma32(cur.qh, sh, O[cb]);  // O = Qt S': qh sh + ql sh + qh sl
+                        O[cb] = mfma32(cur.ql, sh, O[cb]);
+                        O[cb] = mfma32(cur.qh, sl, O[cb]);
+                    }
+                });
+                const bf16x8 pp = lds_ld<bf16x8>(Gs + C::G_P + lane * 16);  // P hi | P lo
+                bf16x8 k0 = ldk(0), k1;
+                f32x4 gm0 = ldg(0), gm1;
+                __builtin_amdgcn_sched_barrier(0);
+                bf16x8 uu[CPW];
+                bf16x4 ul[CPW];
+#pragma unroll
+                for (int cb = 0; cb < CPW; ++cb) {
+                    bf16x4 uh;
+                    split4(U[cb], uh, ul[cb]);
+                    uu[cb] = cat8(uh, uh);
+                }
+#pragma unroll
+                for (int cb = 0; cb < CPW; ++cb) {
+                    O[cb] = mfma32(pp, uu[cb], O[cb]);                      // + P U: ph uh + pl uh
+                    O[cb] = mfma32(pp, cat8(ul[cb], zero_bf4()), O[cb]);   //        + ph ul
+                }
+                // S <- S' + Kb^T U, row block by row block: kh uh + kl uh, then kh ul.  Then
+                // the next chunk's decay: S' = Diag(gamma) S, one block behind the products
+                // (so the multiply finds its block's results ready); with snapshots, after
+                // the snapshot instead.
+                unroll<0, KB>([&](auto BI) {
+                    constexpr int b = decltype(BI)::value;
+                    bf16x8& kc = (b & 1) ? k1 : k0;
+                    bf16x8& kn = (b & 1) ? k0 : k1;
+                    f32x4& gp = (b & 1) ? gm0 : gm1;  // gamma of block b - 1
+                    if constexpr (b + 1 < KB) kn = ldk(b + 1);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int cb = 0; cb < CPW; ++cb) {
+                        S[cb][b] = mfma32(kc, uu[cb], S[cb][b]);
+                        S[cb][b] = mfma32(kc, cat8(ul[cb], zero_bf4()), S[cb][b]);
+                    }
+                    if constexpr (!CK && b > 0) {
+#pragma unroll
+                        for (int cb = 0; cb < CPW; ++cb) S[cb][b - 1] *= gp;
+                    }
+                    if constexpr (b + 1 < KB) gp = ldg(b + 1);  // gamma of block b + 1
+                });
+                if constexpr (!CK) {
+#pragma unroll
+                    for (int cb = 0; cb < CPW; ++cb) S[cb][KB - 1] *= ((KB - 1) & 1) ? gm1 : gm0;
                 }
                 if (CK && --ck_left == 0) {
                     ck_left = a.ck_chunks;
                     if (16 * (int64_t)(c + 1) <= len) {
                         float* dst = a.ck + (ck_slot * H + h) * DK * DV;
 #pragma unroll
-                        for (int b = 0; b < KB; ++b)
+                        for (int cb = 0; cb < CPW; ++cb)
 #pragma unroll
-                            for (int i = 0; i < 4; ++i) dst[(16 * b + 4 * g + i) * DV + ccol] = S[b][i];
+                            for (int b = 0; b < KB; ++b)
+#pragma unroll
+                                for (int i = 0; i < 4; ++i)
+                                    dst[(16 * b + 4 * g + i) * DV + ccol[cb]] = S[cb][b][i];
                     }
                     ++ck_slot;
                 }
+                if constexpr (CK) {
+#pragma unroll
+                    for (int b = 0; b < KB; ++b) {
+                        const f32x4 gm = ldg(b);
+#pragma unroll
+                        for (int cb = 0; cb < CPW; ++cb) S[cb][b] *= gm;
+                    }
+                }
                 // gated output rows of this chunk: the block O[4g+i][r] goes through LDS as the
                 // rows of O^T and comes back transposed, O[r][4g..4g+3], one 8-byte store per lane
-                const f32x4 gt = to_f4(lds_tr(L + C::L_G + tr_v + 32 * wave)) * scale;
-                unsigned char* Ob = smem + C::OFF_O + wave * C::O_SIZE;
-                lds_st(Ob + r * C::ORS + 8 * g, to_bf4(gt * O));
-                const bf16x4 orow = lds_tr(Ob + tr_o);
                 const int64_t t0 = tbeg + 16 * (int64_t)c;
-                if (a.out && t0 + r < tend)
-                    *reinterpret_cast<bf16x4*>(a.out + (t0 + r) * rowv + (int64_t)h * DV + col0 + 16 * wave + 4 * g) = orow;
+#pragma unroll
+                for (int cb = 0; cb < CPW; ++cb) {
+                    const int blk = CPW * wave + cb;
+                    const f32x4 gt = to_f4(lds_tr(L + C::L_G + tr_v + 32 * blk)) * scale;
+                    unsigned char* Ob = smem + C::OFF_O + blk * C::O_SIZE;
+                    lds_st(Ob + r * C::ORS + 8 * g, to_bf4(gt * O[cb]));
+                    const bf16x4 orow = lds_tr(Ob + tr_o);
+                    if (a.out && t0 + r < tend)
+                        *reinterpret_cast<bf16x4*>(a.out + (t0 + r) * rowv + (int64_t)h * DV + col0 + 16 * blk + 4 * g) =
+                            orow;
+                }
             }
             lds_barrier();
         }
         if (a.Sf) {
 #pragma unroll
-            for (int b = 0; b < KB; ++b)
+            for (int cb = 0; cb < CPW; ++cb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) a.Sf[sbase + (16 * b + 4 * g + i) * DV + ccol] = S[b][i];
+                for (int b = 0; b < KB; ++b)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) a.Sf[sbase + (16 * b + 4 * g + i) * DV + ccol[cb]] = S[cb][b][i];
         }
     }
 }
@@ -727,10 +829,10 @@ hipError_t launch_ck(const PrefillArgs& p, hipStream_t st) {
 }  // namespace
 
 // value-slice widths this path supports for (dk, dv)
-bool prefill_bf16_supports(int dk, int dv, int nv) {
-    if (nv < 16 || nv > dv) return false;
-    if (dk == 128) return nv <= 64;
-    return dk == 64 && nv <= 128;
+bool prefill_bf16_supports(int dk, int dv, int nv, bool checkpoints) {
+    if (nv < 16 || nv > dv || nv > 128 || (dk != 128 && dk != 64)) return false;
+    // the snapshot stores of a full-width dk = 128 workgroup would not fit its registers
+    return !(checkpoints && dk == 128 && nv > 64);
 }
 
 hipError_t launch_prefill_bf16(const PrefillArgs& p, hipStream_t st) {
@@ -739,7 +841,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs& p, hipStream_t st) {
         case 16: return launch_ck<DK, DV, 1>(p, st);                  \
         case 32: return launch_ck<DK, DV, 2>(p, st);                  \
         case 64: if constexpr (DV >= 64) return launch_ck<DK, DV, 4>(p, st); break; \
-        case 128: if constexpr (DK == 64 && DV >= 128) return launch_ck<DK, DV, 8>(p, st); break; \
+        case 128: if constexpr (DV >= 128) return launch_ck<DK, DV, 8>(p, st); break; \
     }                                                                 \
     return hipErrorInvalidValue;
     if (p.dk == 128 && p.dv == 128) { KDA_NV_CASES(128, 128) }
