@@ -2,18 +2,29 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-One step = one chunked-prefill launch over the whole workload (default: B=4, H=16,
-T=4096, dk=dv=128, bf16 inputs, fp32 state).  Inputs are generated once on the GPU and are
-resident in HBM before timing; the 256 MB last-level cache is flushed between timed steps
-so no step reuses the previous step's inputs from cache.  Each step is timed with HIP
-events on the stream the kernel runs on.  Prints one JSON line.
+One step = one chunked-prefill launch over the whole workload.  The default (headline)
+workload is the packed varlen batch: 64 sequences whose lengths follow the pages' mix
+(8K / 32K / 128K / 256K), 3,768,320 tokens, H=32, dk=dv=128, bf16 inputs, fp32 per-sequence
+states.  Inputs are generated once on the GPU and are resident in HBM before timing; a
+1 GiB read flushes L2 and the MALL before every timed launch; each launch is timed with
+HIP events on the stream the kernel runs on.  Prints one JSON line.
 
-The decode step (256 sequences x 32 heads, 128x128 fp32 states, 1000 consecutive steps)
-is measured in the same run and reported under "decode".
+In the same run, each with its own timing: the fixed-length prefill B=4 H=16 T=4096 and
+the long-context prefill B=1 H=32 T=131072 (keys under "other_prefill"), the decode step
+(256 sequences x 32 heads, 128x128 fp32 states, 1000 consecutive steps), speculative
+verify/commit, the backward of the B=4 prefill, the segmented prefill, and the CPU oracle
+on a sample of the headline workload ("cpu_baseline").
+
+    python bench.py --summarize {traffic,mfma,trace} ...
+
+turns rocprofv3 CSV output of bench.py runs into the summaries under profiles/ (see
+summarize()).
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
 import json
 import os
 import sys
@@ -25,13 +36,15 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2516.6  # dense bf16 (256 CU x 4096 flop/clk x 2.4 GHz)
 CSRC = os.path.join(ROOT, "linear_attention_sequence_chunked_amd", "csrc")
-# sources whose change invalidates a stored traffic measurement of the prefill kernel
-PREFILL_SOURCES = ("kda_prefill_bf16.hip", "kda_device.h", "kda_launch.h", "kda_api.cpp")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_bf16_b4_h16_t4096_traffic.json")
-COPY_BYTES = 1 << 30  # calibration copy: 1 GiB read + 1 GiB written
-
-
+PROFILES = os.path.join(ROOT, "profiles")
 BUILD_SCRIPT = os.path.join(ROOT, "linear_attention_sequence_chunked_amd", "build.py")
+# sources whose change invalidates a stored counter summary of the prefill / decode kernels
+PREFILL_SOURCES = ("kda_prefill_bf16.hip", "kda_prefill.hip", "kda_device.h", "kda_launch.h",
+                   "kda_api.cpp")
+DECODE_SOURCES = ("kda_decode.hip", "kda_device.h", "kda_launch.h", "kda_api.cpp")
+COPY_BYTES = 1 << 30  # calibration copy: 1 GiB read + 1 GiB written
+HEADLINE = "varlen_n64_h32"
+OTHER_PREFILL = ("prefill_b4_h16_t4096", "prefill_b1_h32_t131072")
 
 
 def _source_hash(names) -> str:
@@ -48,28 +61,19 @@ def prefill_source_hash() -> str:
     return _source_hash(PREFILL_SOURCES)
 
 
-def stored_traffic(workload: str):
-    """HBM bytes per prefill launch from the committed counter summary, or None when the
-    summary is missing, is for another workload or predates the current kernel source."""
-    try:
-        with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
-        return None
-    if t.get("workload") != workload or t.get("kernel_source_sha256") != prefill_source_hash():
-        return None
-    return t.get("traffic_bytes_per_launch")
-
-
-# the decode kernel's sources, and the committed counter summaries of MFMA use (prefill)
-# and HBM bytes (decode)
-DECODE_SOURCES = ("kda_decode.hip", "kda_device.h", "kda_launch.h", "kda_api.cpp")
-MFMA_FILE = os.path.join(ROOT, "profiles", "prefill_bf16_b4_h16_t4096_mfma_counters.json")
-DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_n256_h32_traffic.json")
-
-
 def decode_source_hash() -> str:
     return _source_hash(DECODE_SOURCES)
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(PROFILES, f"{workload}_prefill_traffic.json")
+
+
+def mfma_file(workload: str) -> str:
+    return os.path.join(PROFILES, f"{workload}_prefill_mfma_counters.json")
+
+
+DECODE_TRAFFIC_FILE = os.path.join(PROFILES, "decode_n256_h32_traffic.json")
 
 
 def stored_summary(path: str, workload: str, source_hash: str):
@@ -83,19 +87,6 @@ def stored_summary(path: str, workload: str, source_hash: str):
     if t.get("workload") != workload or t.get("kernel_source_sha256") != source_hash:
         return None
     return t
-
-
-def copy_calibration(steps: int) -> int:
-    """Plain device copy of COPY_BYTES, the reference kernel for scaling the FETCH_SIZE /
-    WRITE_SIZE counters (each launch must read and write exactly COPY_BYTES)."""
-    import torch
-    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
-    dst = torch.empty_like(src)
-    for _ in range(steps):
-        dst.copy_(src)
-    torch.cuda.synchronize()
-    print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "launches": steps}), flush=True)
-    return 0
 
 
 def prefill_algorithmic(lengths, H, dk, dv, es, has_s0, chunk=16):
@@ -113,15 +104,192 @@ def prefill_algorithmic(lengths, H, dk, dv, es, has_s0, chunk=16):
     return bytes_, flops
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def varlen_sample(lengths, H, per_class: int):
+    """per_class (sequence, head) pairs of every length class, spread over the class's
+    sequences and the heads (the pairs the CPU baseline and the parity test use)."""
+    out = []
+    for c in sorted(set(lengths)):
+        seqs = [n for n, L in enumerate(lengths) if L == c]
+        out += [(seqs[j % len(seqs)], (5 * j + c // 8192) % H) for j in range(per_class)]
+    return out
+
+
+# ------------------------------------------------------------------------ measurement
+
+def copy_calibration(steps: int) -> int:
+    """Plain device copy of COPY_BYTES, the reference kernel for scaling the FETCH_SIZE /
+    WRITE_SIZE counters (each launch must read and write exactly COPY_BYTES)."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "launches": steps}), flush=True)
+    return 0
+
+
+class Flush:
+    """Evicts L2 and the MALL before a timed launch by reading 1 GiB (leaves only clean
+    lines; a write would leave dirty lines whose write-back lands in the timed launch)."""
+
+    def __init__(self, enabled: bool):
+        import torch
+        self.buf = torch.ones(256 << 20, dtype=torch.float32, device="cuda") if enabled else None
+        self.out = torch.empty((), dtype=torch.float32, device="cuda")
+
+    def __call__(self):
+        import torch
+        if self.buf is not None:
+            torch.sum(self.buf, dim=0, out=self.out)
+
+
+def time_launches(fn, steps: int, warmup: int, min_warmup_s: float, flush: Flush):
+    """Warm up (at least `warmup` launches and `min_warmup_s` seconds, so the clocks have
+    settled), then time `steps` launches, each after a cache flush, with HIP events on the
+    current stream (the one the library launches on).  Returns (times in ms, wall s)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    n, t0 = 0, time.perf_counter()
+    while n < warmup or time.perf_counter() - t0 < min_warmup_s:
+        fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    wall0 = time.perf_counter()
+    for i in range(steps):
+        flush()
+        starts[i].record(stream)
+        fn()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    return [s.elapsed_time(e) for s, e in zip(starts, ends)], wall
+
+
+def prefill_record(w, x, times_ms, wall):
+    """Throughput, roofline fractions and the stored counter summaries of one workload."""
+    import numpy as np
+    es = 2 if w.dtype == "bf16" else 4
+    ms = float(np.mean(times_ms))
+    tokens = sum(w.lengths)
+    alg_bytes, alg_flops = prefill_algorithmic(w.lengths, w.H, w.dk, w.dv, es,
+                                               x.initial_state is not None)
+    gbps = alg_bytes / (ms * 1e-3) / 1e9
+    tflops = alg_flops / (ms * 1e-3) / 1e12
+    rec = {
+        "workload": w.name, "tokens": tokens, "ms_per_step": ms,
+        "ms_per_step_median": float(np.median(times_ms)), "tokens_per_s": tokens / (ms * 1e-3),
+        "wall_s_timed_region_incl_cache_flush": wall,
+        "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "prefill_bf16_kernel" if w.dtype == "bf16" else "prefill_kernel",
+                     "algorithmic_bytes_per_launch": alg_bytes},
+        "mfma": {"achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                 "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "algorithmic_flops_per_launch": alg_flops},
+    }
+    src = prefill_source_hash()
+    t = stored_summary(traffic_file(w.name), w.name, src)
+    if t is not None:  # rocprofv3 FETCH_SIZE/WRITE_SIZE of the same kernel and workload
+        rec["roofline"]["traffic"] = t["traffic_bytes_per_launch"]
+        rec["roofline"]["traffic_over_algorithmic"] = t["traffic_bytes_per_launch"] / alg_bytes
+        rec["roofline"]["traffic_source"] = os.path.relpath(traffic_file(w.name), ROOT)
+    mc = stored_summary(mfma_file(w.name), w.name, src)
+    if mc is not None:  # rocprofv3 MFMA counters of the same kernel, this launch's time
+        ex = mc["executed_bf16_flops_per_launch"]
+        rec["mfma"]["rocprof"] = {
+            "executed_bf16_flops_per_launch": ex,
+            "executed_TFLOPs": ex / (ms * 1e-3) / 1e12,
+            "executed_frac": ex / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "mfma_busy_frac": mc["mfma_busy_frac"],
+            "source": os.path.relpath(mfma_file(w.name), ROOT)}
+    return rec
+
+
+def run_prefill_workload(name, args, flush, seed=1):
+    import torch
+    import kda_inputs as ki
+    import linear_attention_sequence_chunked_amd as kda
+    w = ki.WORKLOADS[name]
+    x = ki.make_workload_inputs(w, seed=seed, device="cuda")
+    out = torch.empty((x.total_tokens, w.H, w.dv), dtype=x.q.dtype, device="cuda")
+    Sf = torch.empty((len(w.lengths), w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+
+    def step():
+        kda.chunk_prefill(x.q, x.k, x.v, x.log_alpha, x.beta, x.gate, cu_seqlens=x.cu_seqlens,
+                          cu_seqlens_host=x.cu_seqlens_host, initial_state=x.initial_state,
+                          out=out, final_state=Sf)
+
+    times, wall = time_launches(step, args.steps, args.warmup, args.min_warmup_s, flush)
+    return w, x, prefill_record(w, x, times, wall)
+
+
+def cpu_baseline(w, x, per_class: int, repeat_s: float):
+    """The fp64 oracle (threads over (sequence, head) pairs) on a sample of the workload:
+    per_class pairs of every length class, timed until repeat_s seconds have passed, scaled
+    to the whole workload by its token-head count."""
+    import oracle
+    pairs = varlen_sample(w.lengths, w.H, per_class) if len(set(w.lengths)) > 1 else [
+        (n, h) for n in range(len(w.lengths)) for h in range(w.H)]
+    cu = x.cu_seqlens_host
+    host = lambda t: t.detach().float().cpu().numpy()
+    import numpy as np
+    cat = lambda ts: np.concatenate(ts, axis=0)
+    q, k, v, la, b, g, s0, cuh = [], [], [], [], [], [], [], [0]
+    for n, h in pairs:
+        a, e = cu[n], cu[n + 1]
+        for lst, t in ((q, x.q), (k, x.k), (v, x.v), (la, x.log_alpha), (b, x.beta), (g, x.gate)):
+            lst.append(host(t[a:e, h:h + 1]))
+        if x.initial_state is not None:
+            s0.append(host(x.initial_state[n, h:h + 1]))
+        cuh.append(cuh[-1] + e - a)
+    q, k, v, la, b, g = (cat(t) for t in (q, k, v, la, b, g))
+    S0 = np.stack(s0) if s0 else None
+    oracle.ensure_built()
+    runs, t0 = 0, time.perf_counter()
+    used = 0
+    while runs == 0 or time.perf_counter() - t0 < repeat_s:
+        _, _, used = oracle.run(q, k, v, la, b, g, cuh, S0, want_out=True)
+        runs += 1
+    dt = (time.perf_counter() - t0) / runs
+    sample_th = cuh[-1]                     # token-heads in the sample
+    rate = sample_th / dt                   # token-heads per second
+    total_th = sum(w.lengths) * w.H
+    return {"value": rate / w.H, "unit": "tokens/s", "cores": used, "cpu_model": cpu_model(),
+            "kind": "oracle",
+            "sample": f"{len(pairs)} (sequence, head) pairs of {w.name} ({per_class} per length "
+                      f"class), {sample_th} token-heads = {sample_th / total_th:.4f} of the "
+                      f"workload; fp64 token loop with outputs, {runs} run(s) of {dt:.2f} s; "
+                      f"tokens/s = token-heads/s / H, i.e. the whole workload's rate"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    # A few warmup launches leave the GPU below its steady clocks: the bench workload's
-    # prefill measured ~256 us per launch after 3 warmup launches and ~235 us after 200
-    # (0.5 s or 2 s of warmup: ~238 us).
-    ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", default="prefill_b4_h16_t4096")
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--min-warmup-s", type=float, default=1.0,
+                    help="warm up for at least this long (clocks settle); the B=4 T=4096 "
+                         "prefill measured ~256 us per launch after 3 launches, ~235 us after "
+                         "0.5-2 s of them")
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--other-prefill", action=argparse.BooleanOptionalAction, default=True,
+                    help="also time the B=4 T=4096 and B=1 T=131072 prefills")
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--spec-rounds", type=int, default=50)
@@ -131,18 +299,24 @@ def main() -> int:
                     help="also time the segmented prefill on the few-head long workload")
     ap.add_argument("--segment-len", type=int, default=16384)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-pairs-per-class", type=int, default=16)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-flush", action="store_true")
-    ap.add_argument("--flush", choices=("read", "write"), default="read",
-                    help="how the 1 GiB cache flush before each timed launch touches memory")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the 1 GiB copy used to scale the HBM byte counters")
+    ap.add_argument("--summarize", choices=("traffic", "mfma", "trace"))
+    ap.add_argument("--pmc-dirs", nargs="*", default=[])
+    ap.add_argument("--kernel", default="prefill_bf16_kernel")
+    ap.add_argument("--command", action="append", default=[])
+    ap.add_argument("--out")
     args = ap.parse_args()
+    if args.summarize:
+        return summarize(args)
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
               "the operator shards over (sequence, head) with no communication, so the "
               "N-GPU figure is N independent copies of this one.", file=sys.stderr)
         return 2
-
     if args.copy_calibration:
         return copy_calibration(args.steps)
 
@@ -154,93 +328,52 @@ def main() -> int:
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
-    w = ki.WORKLOADS[args.workload]
-    x = ki.make_workload_inputs(w, seed=1, device="cuda")
-    es = 2 if w.dtype == "bf16" else 4
-    T_total = x.total_tokens
-    out = torch.empty((T_total, w.H, w.dv), dtype=x.q.dtype, device="cuda")
-    Sf = torch.empty((len(w.lengths), w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
-    # Cache flush before every timed launch: reading a 1 GiB buffer evicts the inputs from
-    # L2 and the MALL and leaves only clean lines; writing it (--flush write) also leaves up
-    # to the MALL's size of dirty lines, whose write-back then runs inside the timed launch.
-    flush = None
-    if not args.no_flush:
-        flush = torch.ones(256 << 20, dtype=torch.float32, device="cuda")  # 1 GiB
-        flush_out = torch.empty((), dtype=torch.float32, device="cuda")
-
-    def do_flush():
-        if args.flush == "write":
-            flush.zero_()
-        else:
-            torch.sum(flush, dim=0, out=flush_out)
-
-    def step():
-        kda.chunk_prefill(x.q, x.k, x.v, x.log_alpha, x.beta, x.gate, cu_seqlens=x.cu_seqlens,
-                          cu_seqlens_host=x.cu_seqlens_host, initial_state=x.initial_state,
-                          out=out, final_state=Sf)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    for i in range(args.steps):
-        if flush is not None:
-            do_flush()
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    times_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    ms = float(np.mean(times_ms))
-    tokens_per_s = T_total / (ms * 1e-3)
-    alg_bytes, alg_flops = prefill_algorithmic(w.lengths, w.H, w.dk, w.dv, es,
-                                               x.initial_state is not None)
-    gbps = alg_bytes / (ms * 1e-3) / 1e9
-    tflops = alg_flops / (ms * 1e-3) / 1e12
+    flush = Flush(not args.no_flush)
 
+    w, x, head = run_prefill_workload(args.workload, args, flush)
     result = {
         "metric": "KDA prefill tokens/s (%MFMA peak); decode state GB/s (%HBM peak), 1 MI355X",
-        "value": tokens_per_s,
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms,
-        "ms_per_step_median": float(np.median(times_ms)),
-        "wall_s_timed_region_incl_cache_flush": wall,
-        "cache_flush": None if flush is None else f"1 GiB {args.flush} before each launch",
+        "ms_per_step": head["ms_per_step"],
+        "ms_per_step_median": head["ms_per_step_median"],
+        "wall_s_timed_region_incl_cache_flush": head["wall_s_timed_region_incl_cache_flush"],
+        "cache_flush": None if args.no_flush else "1 GiB read before each launch",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic (seeded; q,k L2-normalised N(0,1); v N(0,1); beta, gate "
-                "sigmoid(N(0,1)); log_alpha max(-softplus(N(0,1)),-0.3))",
-        "config": {"workload": w.name, "batch": len(w.lengths), "seq_len": max(w.lengths),
-                   "tokens": T_total, "heads": w.H, "dk": w.dk, "dv": w.dv, "chunk": 16,
-                   "state": "fp32", "initial_state": x.initial_state is not None},
-        "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": gbps / HBM_PEAK_GBPS,
-                     "traffic": stored_traffic(w.name) if w.dtype == "bf16" else None,
-                     "kernel": "prefill_bf16_kernel" if w.dtype == "bf16" else "prefill_kernel",
-                     "algorithmic_bytes_per_launch": alg_bytes},
-        "mfma": {"achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                 "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
-                 "algorithmic_flops_per_launch": alg_flops},
+                "sigmoid(N(0,1)); log_alpha max(-softplus(N(0,1)),-0.3); per-sequence S0 "
+                "N(0,0.02^2) where the workload has one)",
+        "config": {"workload": w.name, "sequences": len(w.lengths),
+                   "length_classes": {str(L): w.lengths.count(L) for L in sorted(set(w.lengths))},
+                   "longest": max(w.lengths), "tokens": x.total_tokens, "heads": w.H,
+                   "dk": w.dk, "dv": w.dv, "chunk": 16, "state": "fp32",
+                   "initial_state": x.initial_state is not None},
+        "roofline": head["roofline"],
+        "mfma": head["mfma"],
     }
-    mc = (stored_summary(MFMA_FILE, w.name, prefill_source_hash()) if w.dtype == "bf16" else None)
-    if mc is not None:  # rocprofv3 counters of the same kernel, this launch's time
-        ex = mc["executed_bf16_flops_per_launch"]
-        result["mfma"]["rocprof"] = {
-            "executed_bf16_flops_per_launch": ex,
-            "executed_TFLOPs": ex / (ms * 1e-3) / 1e12,
-            "executed_frac": ex / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-            "mfma_busy_frac": mc["mfma_busy_frac"],
-            "source": os.path.basename(MFMA_FILE)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, x, args.cpu_pairs_per_class, args.cpu_seconds)
+    del x
+    torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------------- other prefill shapes
+    if args.other_prefill:
+        result["other_prefill"] = {}
+        for name in OTHER_PREFILL:
+            if name == args.workload:
+                continue
+            _, xo, rec = run_prefill_workload(name, args, flush)
+            result["other_prefill"][name] = rec
+            del xo
+            torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- decode step
     if not args.no_decode and args.decode_steps > 0:
@@ -294,14 +427,10 @@ def main() -> int:
         accepted = torch.randint(0, K + 1, (args.spec_rounds, N), generator=g,
                                  dtype=torch.int32).cuda()
         sd = torch.cuda.Stream()
-
-        def spec_round(i):
-            kda.spec_verify(sx.q, sx.k, sx.v, sx.log_alpha, sx.beta, sx.gate, state, out=sout)
-            kda.spec_commit(sx.k, sx.v, sx.log_alpha, sx.beta, state, accepted[i])
-
         with torch.cuda.stream(sd):
             for i in range(min(3, args.spec_rounds)):
-                spec_round(i)
+                kda.spec_verify(sx.q, sx.k, sx.v, sx.log_alpha, sx.beta, sx.gate, state, out=sout)
+                kda.spec_commit(sx.k, sx.v, sx.log_alpha, sx.beta, state, accepted[i])
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
             ev[0].record(sd)
             for i in range(args.spec_rounds):
@@ -330,38 +459,41 @@ def main() -> int:
 
     # ---------------------------------------------------------------- backward
     if args.backward_steps > 0:
-        g = torch.Generator().manual_seed(1)
-        dout = torch.randn(x.v.shape, generator=g).to(x.v.dtype).cuda()
-        bws = None
-
-        def bstep():
-            kda.prefill_backward(x.q, x.k, x.v, x.log_alpha, x.beta, x.gate, dout,
-                                 cu_seqlens=x.cu_seqlens, cu_seqlens_host=x.cu_seqlens_host,
-                                 initial_state=x.initial_state, workspace=bws)
-
-        lib = kda.load_library()
         import ctypes
         from linear_attention_sequence_chunked_amd import _lib as klib
-        pp = klib.params(klib.KDA_DTYPE_BF16 if w.dtype == "bf16" else klib.KDA_DTYPE_F32,
-                         w.H, w.dk, w.dv)
-        cu_h = (ctypes.c_int32 * len(x.cu_seqlens_host))(*x.cu_seqlens_host)
-        need = lib.kda_prefill_backward_workspace(ctypes.byref(pp), cu_h, len(w.lengths))
+        bw = ki.WORKLOADS["prefill_b4_h16_t4096"]
+        bx = ki.make_workload_inputs(bw, seed=1, device="cuda")
+        g = torch.Generator().manual_seed(1)
+        dout = torch.randn(bx.v.shape, generator=g).to(bx.v.dtype).cuda()
+        lib = kda.load_library()
+        pp = klib.params(klib.KDA_DTYPE_BF16, bw.H, bw.dk, bw.dv)
+        cu_h = (ctypes.c_int32 * len(bx.cu_seqlens_host))(*bx.cu_seqlens_host)
+        need = lib.kda_prefill_backward_workspace(ctypes.byref(pp), cu_h, len(bw.lengths))
         bws = torch.empty(need, dtype=torch.uint8, device="cuda")
-        bstep()
-        torch.cuda.synchronize()
-        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        b0.record(stream)
-        for _ in range(args.backward_steps):
-            bstep()
-        b1.record(stream)
-        torch.cuda.synchronize()
-        bms = b0.elapsed_time(b1) / args.backward_steps
+        fout = torch.empty_like(bx.v)
+
+        def bstep():
+            kda.prefill_backward(bx.q, bx.k, bx.v, bx.log_alpha, bx.beta, bx.gate, dout,
+                                 cu_seqlens=bx.cu_seqlens, cu_seqlens_host=bx.cu_seqlens_host,
+                                 initial_state=bx.initial_state, workspace=bws)
+
+        def fstep():
+            kda.chunk_prefill(bx.q, bx.k, bx.v, bx.log_alpha, bx.beta, bx.gate,
+                              cu_seqlens=bx.cu_seqlens, cu_seqlens_host=bx.cu_seqlens_host,
+                              initial_state=bx.initial_state, out=fout)
+
+        bt, _ = time_launches(bstep, args.backward_steps, 2, 0.0, flush)
+        ft, _ = time_launches(fstep, args.backward_steps, 2, 0.0, flush)
+        bms, fms = float(np.mean(bt)), float(np.mean(ft))
         result["backward"] = {
-            "workload": w.name, "steps": args.backward_steps, "ms_per_step": bms,
-            "tokens_per_s": T_total / (bms * 1e-3), "vs_forward": bms / ms,
-            "note": "chunk form, fp32 state and sums: forward and reverse chunk walks in one launch (split-bf16 products), then all chunks in parallel (fp32 MFMA)",
+            "workload": bw.name, "steps": args.backward_steps, "ms_per_step": bms,
+            "tokens_per_s": bx.total_tokens / (bms * 1e-3), "forward_ms": fms,
+            "vs_forward": bms / fms,
+            "note": "chunk form, fp32 state and sums: forward and reverse chunk walks in one "
+                    "launch (split-bf16 products), then all chunks in parallel (fp32 MFMA); "
+                    "each launch after the same cache flush as the forward",
         }
-        del bws, dout
+        del bws, dout, bx, fout
         torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- segmented prefill
@@ -383,21 +515,9 @@ def main() -> int:
                                         sxx.cu_seqlens_host, L, out=sout, final_state=sSf,
                                         workspace=ws)
 
-        def med_ms(fn, reps=5):
-            fn()
-            torch.cuda.synchronize()
-            ts = []
-            for _ in range(reps):
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                fn()
-                e1.record(stream)
-                torch.cuda.synchronize()
-                ts.append(e0.elapsed_time(e1))
-            return float(np.median(ts))
-
-        pms, sms = med_ms(plain_run), med_ms(seg_run)
+        pt, _ = time_launches(plain_run, 3, 1, 0.0, flush)
+        st, _ = time_launches(seg_run, 5, 1, 0.0, flush)
+        pms, sms = float(np.median(pt)), float(np.median(st))
         ttok = sum(sw.lengths)
         result["segmented"] = {
             "workload": sw.name, "segment_len": L, "plain_ms": pms, "segmented_ms": sms,
@@ -406,27 +526,133 @@ def main() -> int:
         del sxx, sout, ws
         torch.cuda.empty_cache()
 
-    # ---------------------------------------------------------------- CPU oracle
-    if not args.no_cpu_baseline:
-        import oracle
-        f = lambda t: None if t is None else t.detach().float().cpu().numpy()
-        hq, hk, hv, hla, hb, hg, hs = (f(t) for t in (x.q, x.k, x.v, x.log_alpha, x.beta,
-                                                      x.gate, x.initial_state))
-        oracle.ensure_built()
-        # the whole workload, repeated until about 10 s of CPU time have been spent
-        runs, t0 = 0, time.perf_counter()
-        while runs == 0 or (time.perf_counter() - t0 < 10.0 and runs < 50):
-            _, _, used = oracle.run(hq, hk, hv, hla, hb, hg, x.cu_seqlens_host, hs,
-                                    want_out=True)
-            runs += 1
-        dt = (time.perf_counter() - t0) / runs
-        result["cpu_baseline"] = {
-            "value": T_total / dt, "unit": "tokens/s", "cores": used, "kind": "oracle",
-            "sample": f"the whole workload: all {len(w.lengths) * w.H} (sequence, head) "
-                      f"pairs, {T_total} tokens, fp64 token loop with outputs; mean of "
-                      f"{runs} runs of {dt:.2f} s each"}
-
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
+    return 0
+
+
+# ------------------------------------------------------------------------ counter summaries
+
+def _read_counters(dirs, kernel_substr):
+    """{counter: [value per dispatch in dispatch order]} and the durations (us) of the
+    dispatches whose kernel name contains kernel_substr, from rocprofv3 CSV directories."""
+    vals, dur, names = {}, {}, {}
+    for d in dirs:
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    if kernel_substr not in r["Kernel_Name"]:
+                        continue
+                    did = int(r["Dispatch_Id"])
+                    vals.setdefault(r["Counter_Name"], {})[did] = float(r["Counter_Value"])
+                    dur[did] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                    names[did] = r["Kernel_Name"]
+    out = {c: [v[k] for k in sorted(v)] for c, v in vals.items()}
+    order = sorted(dur)
+    return out, [dur[k] for k in order], [names[k] for k in order]
+
+
+def summarize(args) -> int:
+    """traffic: --pmc-dirs FETCH WRITE COPYFETCH COPYWRITE (rocprofv3 --pmc FETCH_SIZE /
+    WRITE_SIZE runs of `bench.py --steps S` and of `bench.py --copy-calibration`): HBM
+    bytes per launch of the last S launches, each counter scaled by the factor that makes it
+    read exactly 1 GiB for the plain 1 GiB copy.
+    mfma: --pmc-dirs DIR (SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES
+    GRBM_GUI_ACTIVE): executed bf16 MFMA flops and the MFMA busy fraction.
+    trace: --pmc-dirs DIR (--kernel-trace --stats): per-kernel call counts and durations."""
+    import numpy as np
+    import kda_inputs as ki
+    w = ki.WORKLOADS.get(getattr(args, "workload", ""), None)
+    steps = args.steps
+    res = {"workload": args.workload, "commands": args.command}
+    if args.summarize in ("traffic", "mfma"):
+        res["kernel_source_sha256"] = (decode_source_hash() if "decode" in args.kernel
+                                       else prefill_source_hash())
+    if args.summarize == "traffic":
+        fetch, fdur, names = _read_counters([args.pmc_dirs[0]], args.kernel)
+        write, _, _ = _read_counters([args.pmc_dirs[1]], args.kernel)
+        cf, _, _ = _read_counters([args.pmc_dirs[2]], "copyBuffer")
+        cw, _, _ = _read_counters([args.pmc_dirs[3]], "copyBuffer")
+        if not cf:  # torch's copy kernel, if the runtime did not use its blit
+            cf, _, _ = _read_counters([args.pmc_dirs[2]], "copy")
+            cw, _, _ = _read_counters([args.pmc_dirs[3]], "copy")
+        f = fetch["FETCH_SIZE"][-steps:]
+        wr = write["WRITE_SIZE"][-steps:]
+        gib_kib = COPY_BYTES / 1024
+        ff = gib_kib / float(np.mean(cf["FETCH_SIZE"]))
+        wf = gib_kib / float(np.mean(cw["WRITE_SIZE"]))
+        traffic = (float(np.mean(f)) * ff + float(np.mean(wr)) * wf) * 1024
+        res.update({"kernel": names[-1], "fetch_kib_per_dispatch": float(np.mean(f)),
+                    "write_kib_per_dispatch": float(np.mean(wr)), "fetch_dispatches": f,
+                    "write_dispatches": wr,
+                    "copy_calibration": {"bytes_read_and_written": COPY_BYTES,
+                                         "fetch_kib": cf["FETCH_SIZE"],
+                                         "write_kib": cw["WRITE_SIZE"], "fetch_factor": ff,
+                                         "write_factor": wf},
+                    "traffic_bytes_per_launch": traffic})
+        key = "traffic_bytes_per_step" if "decode" in args.kernel else "traffic_bytes_per_launch"
+        res[key] = traffic
+        if w is not None and "decode" not in args.kernel:
+            alg, _ = prefill_algorithmic(w.lengths, w.H, w.dk, w.dv, 2, w.s0_std > 0)
+            res["algorithmic_bytes_per_launch"] = alg
+            res["traffic_over_algorithmic"] = traffic / alg
+        res["note"] = ("HBM bytes per launch = FETCH_SIZE*fetch_factor + WRITE_SIZE*write_factor "
+                       "(KiB, mean over the last launches, each after the 1 GiB cache flush); the "
+                       "factors make the counters read exactly 1 GiB for a plain 1 GiB copy.")
+    elif args.summarize == "mfma":
+        c, dur, names = _read_counters(args.pmc_dirs, args.kernel)
+        mops = float(np.mean(c["SQ_INSTS_VALU_MFMA_MOPS_BF16"][-steps:]))
+        busy = float(np.mean(c["SQ_VALU_MFMA_BUSY_CYCLES"][-steps:]))
+        act = float(np.mean(c["GRBM_GUI_ACTIVE"][-steps:]))
+        us = float(np.mean(dur[-steps:]))
+        ex = mops * 512
+        res.update({"kernel": names[-1], "dispatches": steps,
+                    "SQ_INSTS_VALU_MFMA_MOPS_BF16_per_launch": mops,
+                    "SQ_VALU_MFMA_BUSY_CYCLES_per_launch": busy,
+                    "GRBM_GUI_ACTIVE_per_launch": act,
+                    "kernel_duration_us_under_counters": us,
+                    "executed_bf16_flops_per_launch": ex,
+                    "mfma_busy_frac": busy / (act * 1024 / 8) if act else None})
+        if w is not None:
+            _, alg_f = prefill_algorithmic(w.lengths, w.H, w.dk, w.dv, 2, w.s0_std > 0)
+            res["algorithmic_flops_per_launch"] = alg_f
+            res["executed_over_algorithmic"] = ex / alg_f
+        res["note"] = ("executed flops = MOPS x 512 (the counter's unit); mfma_busy_frac = MFMA "
+                       "busy cycles summed over the 1024 SIMDs / (GPU-active cycles per XCD x "
+                       "1024), the MfmaUtil of rocprofv3 (GRBM_GUI_ACTIVE sums the 8 XCDs).")
+    else:  # trace
+        rows = []
+        for path in glob.glob(os.path.join(args.pmc_dirs[0], "**", "*kernel_stats.csv"),
+                              recursive=True):
+            with open(path) as f:
+                rows += list(csv.DictReader(f))
+        lines = [f"rocprofv3 kernel trace of bench.py, one MI355X; workload {args.workload}",
+                 "", "command:"] + [f"  {c}" for c in args.command] + ["",
+                 f"{'kernel':70s} {'calls':>7s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} "
+                 f"{'share%':>7s}"]
+        for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"]))[:16]:
+            lines.append(f"{r['Name'][:70]:70s} {int(r['Calls']):7d} "
+                         f"{float(r['AverageNs']) / 1e3:10.1f} {float(r['MinNs']) / 1e3:10.1f} "
+                         f"{float(r['MaxNs']) / 1e3:10.1f} {float(r['Percentage']):7.2f}")
+        traces = glob.glob(os.path.join(args.pmc_dirs[0], "**", "*kernel_trace.csv"), recursive=True)
+        durs = []
+        for path in traces:
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    if args.kernel in r["Kernel_Name"]:
+                        durs.append((int(r["Start_Timestamp"]),
+                                     (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+        durs = [d for _, d in sorted(durs)]
+        if durs:
+            tail = durs[-steps:]
+            lines += ["", f"{args.kernel} dispatches: {len(durs)}; the timed ones (last {steps}): "
+                          f"mean {np.mean(tail):.1f} us, median {np.median(tail):.1f} us"]
+        with open(args.out, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        return 0
+    with open(args.out, "w") as f:
+        json.dump(res, f, indent=1)
     return 0
 
 

@@ -1,5 +1,6 @@
 """Host-side checks of bench.py's measurement arithmetic and its refusal of several GPUs
 (no GPU needed)."""
+import glob
 import json
 import os
 import subprocess
@@ -49,10 +50,39 @@ def test_stored_summaries_are_ignored_when_stale(tmp_path):
     assert bench.stored_summary(str(p), "w", "abc") is None
 
 
-@pytest.mark.parametrize("path", [bench.TRAFFIC_FILE, bench.MFMA_FILE, bench.DECODE_TRAFFIC_FILE])
+SUMMARIES = sorted(glob.glob(os.path.join(ROOT, "profiles", "*_traffic.json")) +
+                   glob.glob(os.path.join(ROOT, "profiles", "*_mfma_counters.json")))
+
+
+@pytest.mark.parametrize("path", SUMMARIES, ids=os.path.basename)
 def test_committed_summaries_name_their_workload_and_command(path):
+    """Every committed counter summary names a workload of kda_inputs, the kernel source it
+    was measured on, and the rocprofv3 commands (over bench.py) that produced it."""
+    import kda_inputs as ki
     t = json.load(open(path))
-    assert t["workload"] in ("prefill_b4_h16_t4096", "decode_n256_h32")
+    assert t["workload"] in ki.WORKLOADS
+    assert os.path.basename(path).startswith(t["workload"])
     assert len(t["kernel_source_sha256"]) == 64
     cmds = t.get("commands") or [t["command"]]
-    assert all("rocprofv3 --pmc" in c and "bench.py" in c for c in cmds)
+    assert any("rocprofv3 --pmc" in c and "bench.py" in c for c in cmds)
+
+
+def test_varlen_sample_covers_every_length_class_with_distinct_pairs():
+    import kda_inputs as ki
+    w = ki.WORKLOADS[bench.HEADLINE]
+    pairs = bench.varlen_sample(w.lengths, w.H, 16)
+    assert len(pairs) == 16 * len(set(w.lengths)) == len(set(pairs))
+    for L in set(w.lengths):
+        assert sum(1 for n, _ in pairs if w.lengths[n] == L) == 16
+
+
+def test_headline_workload_is_the_packed_varlen_batch():
+    """The headline is the largest single-GPU workload: 64 packed sequences (3,768,320
+    tokens), H=32, d=128; its algorithmic bytes per launch are 1538 per token-head plus
+    the per-sequence initial and final states."""
+    import kda_inputs as ki
+    w = ki.WORKLOADS[bench.HEADLINE]
+    assert sum(w.lengths) == 3_768_320 and len(w.lengths) == 64 and w.H == 32
+    b, f = bench.prefill_algorithmic(w.lengths, w.H, w.dk, w.dv, 2, True)
+    assert b == 3_768_320 * 32 * 1538 + 64 * 32 * 2 * 128 * 128 * 4
+    assert f == 3_768_320 * 32 * 118_784
