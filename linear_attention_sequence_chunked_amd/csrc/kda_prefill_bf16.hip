@@ -229,9 +229,12 @@ struct Cfg {
     // the four rows of each transposed 16-lane group in distinct banks
     static constexpr int VRS = NV * 2 + 32;
     static constexpr int VT = 16 * VRS;
-    // value/gate 16x16 blocks staged per decay wave (block f: columns 16 (f >> 1), gate if
-    // f is odd)
-    static constexpr int VG_PER_WAVE = (2 * NCB + NDW - 1) / NDW;
+    // value and gate rows are staged by the decay waves with 16-byte loads that cover whole
+    // row segments of the slice (NV / 8 lanes per row): VGI_T loads per tensor and chunk,
+    // VGI in all, load i going to decay wave i % NDW (VG_PER_WAVE per wave)
+    static constexpr int VGI_T = NV >= 32 ? NV / 32 : 1;
+    static constexpr int VGI = 2 * VGI_T;
+    static constexpr int VG_PER_WAVE = (VGI + NDW - 1) / NDW;
     // long ring (4 slots, chunk c written at iteration c-3, read up to iteration c):
     // Qt hi/lo, Kb hi/lo rows, gamma, value and gate rows
     static constexpr int L_QH = 0, L_QL = ROWQ, L_KBH = 2 * ROWQ, L_KBL = 2 * ROWQ + ROWK,
@@ -339,16 +342,24 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
         // line (fewer cache-line requests per byte than 8-byte pieces).
         const int w = wave - C::W_DECAY0;   // 32-channel block
         const int dch = 32 * w + 8 * g;     // this lane's first channel
-        // value / gate blocks staged by this wave: block f = w + NDW*e.  A wave past the last
-        // block still issues the load (the loads stay unconditional) over an empty range,
-        // which reads nothing.
+        // value / gate loads of this wave: load i = w + NDW*e covers tensor i / VGI_T (0: V,
+        // 1: gate), 16-byte piece q = 64 (i % VGI_T) + lane of that tensor's [16][NV] tile:
+        // row q / (NV/8), bytes 16 (q % (NV/8)).  A wave past the last load still issues it,
+        // over an empty range, which reads nothing; a lane past the tile repeats piece 0 and
+        // stores nothing.
         constexpr int NDW = C::NDW;
-        int vg_f[C::VG_PER_WAVE];
-        bool vg_own[C::VG_PER_WAVE];
+        constexpr int PPR = NV / 8;  // 16-byte pieces per row
+        int vg_t[C::VG_PER_WAVE], vg_row[C::VG_PER_WAVE], vg_col[C::VG_PER_WAVE];
+        bool vg_own[C::VG_PER_WAVE], vg_lane[C::VG_PER_WAVE];
 #pragma unroll
         for (int e = 0; e < C::VG_PER_WAVE; ++e) {
-            vg_own[e] = w + NDW * e < 2 * NCB;
-            vg_f[e] = vg_own[e] ? w + NDW * e : w % (2 * NCB);
+            const int i = w + NDW * e;
+            vg_own[e] = i < C::VGI;
+            vg_t[e] = vg_own[e] ? i / C::VGI_T : 0;
+            const int q = 64 * (i % C::VGI_T) + lane;
+            vg_lane[e] = q < 16 * PPR;
+            vg_row[e] = vg_lane[e] ? q / PPR : 0;
+            vg_col[e] = vg_lane[e] ? q % PPR : 0;
         }
         // Prefetch ring of PF chunks; chunk c lives in slot (c + 1) % PF.  One buffer
         // resource per tensor covers the whole sequence (its records end at the last row),
@@ -358,14 +369,14 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
         // register and stays in flight, and nothing is masked when consumed.  Offsets are
         // 32-bit: once one passes 2^30 bytes the resource base moves up to the next chunk.
         u32x4 rq[PF], rk[PF], rl[PF];
-        u32x2 rvg[C::VG_PER_WAVE][PF];
+        u32x4 rvg[C::VG_PER_WAVE][PF];
         uint32_t rb[PF];
         const uint32_t oq = (uint32_t)(r * (int)(2 * rowq) + 2 * dch);   // lane offsets (bytes)
         const uint32_t ob = (uint32_t)(r * 2 * H);
         uint32_t ov[C::VG_PER_WAVE];
 #pragma unroll
-        for (int e = 0; e < C::VG_PER_WAVE; ++e)
-            ov[e] = (uint32_t)(r * (int)(2 * rowv) + 2 * (col0 + 16 * (vg_f[e] >> 1) + 4 * g));
+        for (int e = 0; e < C::VG_PER_WAVE; ++e)  // lanes past the tile repeat piece 0 (unused)
+            ov[e] = (uint32_t)(vg_row[e] * (int)(2 * rowv) + 2 * col0 + 16 * vg_col[e]);
         const char* pq = reinterpret_cast<const char*>(a.q + tbeg * rowq + (int64_t)h * DK);
         const char* pk = reinterpret_cast<const char*>(a.k + tbeg * rowq + (int64_t)h * DK);
         const char* pl = reinterpret_cast<const char*>(a.la + tbeg * rowq + (int64_t)h * DK);
@@ -373,7 +384,7 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
         const char* pv[C::VG_PER_WAVE];
 #pragma unroll
         for (int e = 0; e < C::VG_PER_WAVE; ++e)
-            pv[e] = reinterpret_cast<const char*>(((vg_f[e] & 1) ? a.gate : a.v) + tbeg * rowv + (int64_t)h * DV);
+            pv[e] = reinterpret_cast<const char*>((vg_t[e] ? a.gate : a.v) + tbeg * rowv + (int64_t)h * DV);
         // bytes from the resource base to the end of the sequence's rows (the records)
         int64_t eq = (len - 1) * 2 * rowq + 2 * DK, eb = (len - 1) * 2 * H + 2,
                 ev = (len - 1) * 2 * rowv + 2 * DV;
@@ -383,10 +394,11 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
         __amdgpu_buffer_rsrc_t Rq, Rk, Rl, Rb, Rv[C::VG_PER_WAVE];
         auto make = [&]() {  // resources for the current bases (uniform)
             const int nq = recs(eq), nv = recs(ev);
-            Rq = rsrc(pq, nq); Rk = rsrc(pk, nq); Rl = rsrc(pl, nq); Rb = rsrc(pb, recs(eb));
+            // beta is read by decay wave 0 only (the others load over an empty range)
+            Rq = rsrc(pq, nq); Rk = rsrc(pk, nq); Rl = rsrc(pl, nq); Rb = rsrc(pb, w == 0 ? recs(eb) : 0);
 #pragma unroll
             for (int e = 0; e < C::VG_PER_WAVE; ++e) {  // V read as zeros, or the gate unused:
-                const bool gate = vg_f[e] & 1;           // an empty range (nothing is read)
+                const bool gate = vg_t[e] == 1;          // an empty range (nothing is read)
                 const bool read = vg_own[e] && (gate ? a.out != nullptr : !a.v_zero);
                 Rv[e] = rsrc(pv[e], read ? nv : 0);
             }
@@ -410,7 +422,7 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
             rl[sl] = bload16(Rl, vq);
             rb[sl] = __builtin_amdgcn_raw_buffer_load_b16(Rb, ob + ub, 0, 0);
 #pragma unroll
-            for (int e = 0; e < C::VG_PER_WAVE; ++e) rvg[e][sl] = bload8(Rv[e], ov[e] + uv);
+            for (int e = 0; e < C::VG_PER_WAVE; ++e) rvg[e][sl] = bload16(Rv[e], ov[e] + uv);
             uq += sq; ub += sb; uv += sv;
         };
         // issued in slot order (kept by the scheduling barriers), so the loads of the
@@ -484,12 +496,9 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
                 // word (the readers use copy 0)
                 if (w == 0) lds_st(bslot(c) + 4 * r + 64 * g, __builtin_bit_cast(float, rb[ph] << 16));
 #pragma unroll
-                for (int e = 0; e < C::VG_PER_WAVE; ++e) {
-                    const int f = w + NDW * e;
-                    if (f < 2 * NCB)  // row r, columns 16 (f >> 1) + 4g .. +3
-                        lds_st(L + ((f & 1) ? C::L_G : C::L_V) + r * C::VRS + 2 * (16 * (f >> 1) + 4 * g),
-                               rvg[e][ph]);
-                }
+                for (int e = 0; e < C::VG_PER_WAVE; ++e)
+                    if (vg_own[e] && vg_lane[e])
+                        lds_st(L + (vg_t[e] ? C::L_G : C::L_V) + vg_row[e] * C::VRS + 16 * vg_col[e], rvg[e][ph]);
             }
             if (c == nch)  // one past the last chunk: gamma = 1 (the chain's decay step after its last update)
                 lds_st(lslot(c) + C::L_GAM + 4 * (dch + (r & 7)), 1.0f);
