@@ -201,6 +201,18 @@ kda_status kda_chunk_prefill_segmented_noalloc(const kda_params* params, const v
 int64_t kda_noalloc_scratch_bytes(void);
 
 /*
+ * kda_prefill_segment_plan -- the segment length (tokens, a multiple of 16) at which
+ * kda_chunk_prefill_segmented is the faster schedule for this batch on the current device,
+ * or 0 when kda_chunk_prefill is (too many (sequence, head) chains to gain from splitting
+ * them, too short sequences, or fp32 inputs); -1 on invalid arguments (kda_last_error()
+ * says why).  Host-only: reads the device's compute-unit count once, launches nothing.
+ * A caller that can provide the workspace uses it to pick between the two entry points
+ * (the torch binding's chunk_prefill does).
+ */
+int32_t kda_prefill_segment_plan(const kda_params* params, const int32_t* cu_seqlens_host,
+                                 int32_t num_seqs);
+
+/*
  * kda_prefill_backward -- gradients of kda_chunk_prefill (the training form), fp32.
  *
  * Given the forward's inputs and the gradients of its outputs, writes the gradient of the

@@ -12,7 +12,7 @@ KDA_DTYPE_BF16, KDA_DTYPE_F32 = 0, 1
 EXPORTED = ("kda_chunk_prefill", "kda_chunk_prefill_checkpointed", "kda_decode_step",
             "kda_spec_verify", "kda_spec_commit", "kda_chunk_prefill_segmented",
             "kda_prefill_segmented_workspace", "kda_chunk_prefill_segmented_noalloc",
-            "kda_noalloc_scratch_bytes", "kda_prefill_backward",
+            "kda_noalloc_scratch_bytes", "kda_prefill_segment_plan", "kda_prefill_backward",
             "kda_prefill_backward_workspace", "kda_status_string", "kda_last_error",
             "kda_abi_version")
 
@@ -69,6 +69,8 @@ def load() -> ctypes.CDLL:
     lib.kda_chunk_prefill_segmented_noalloc.restype = ctypes.c_int
     lib.kda_noalloc_scratch_bytes.argtypes = []
     lib.kda_noalloc_scratch_bytes.restype = ctypes.c_int64
+    lib.kda_prefill_segment_plan.argtypes = [ctypes.POINTER(KdaParams), ctypes.POINTER(I32), I32]
+    lib.kda_prefill_segment_plan.restype = I32
     lib.kda_prefill_backward.argtypes = [ctypes.POINTER(KdaParams), P, P, P, P, P, P, P,
                                          ctypes.POINTER(I32), I32, P, P, P, P, P, P, P, P, P,
                                          P, P, ctypes.c_int64, P]

@@ -586,6 +586,27 @@ kda_status kda_chunk_prefill_segmented_noalloc(const kda_params* params, const v
 
 int64_t kda_noalloc_scratch_bytes(void) { return (int64_t)kda::kScratchBytes; }
 
+int32_t kda_prefill_segment_plan(const kda_params* params, const int32_t* cu_seqlens_host,
+                                 int32_t num_seqs) {
+    if (check_params(params) != KDA_OK) return -1;
+    if (num_seqs < 1 || !cu_seqlens_host || cu_seqlens_host[0] != 0) {
+        fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill_segment_plan: bad cu_seqlens_host/num_seqs");
+        return -1;
+    }
+    int64_t longest = 0;
+    for (int32_t n = 0; n < num_seqs; ++n) {
+        const int64_t len = (int64_t)cu_seqlens_host[n + 1] - cu_seqlens_host[n];
+        if (len < 0) {
+            fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill_segment_plan: cu_seqlens_host decreases");
+            return -1;
+        }
+        longest = std::max(longest, len);
+    }
+    ok();
+    return kda::prefill_segment_plan((int64_t)num_seqs * params->num_heads, (longest + 15) / 16,
+                                     params->dtype, device_cu_count());
+}
+
 }  // extern "C"
 
 namespace {

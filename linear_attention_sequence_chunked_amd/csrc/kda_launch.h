@@ -104,5 +104,8 @@ bool prefill_bf16_supports(int dk, int dv, int nv, bool checkpoints);
 
 // value-slice width the prefill would pick for this problem (exposed for tests)
 int prefill_pick_nv(int dv, int64_t num_pairs, int64_t longest_chunks, int cu_count);
+// tokens per segment for the segmented prefill, or 0 when the plain one is the better
+// schedule (kda_prefill_segment_plan)
+int32_t prefill_segment_plan(int64_t num_pairs, int64_t longest_chunks, int dtype, int cu_count);
 
 }  // namespace kda

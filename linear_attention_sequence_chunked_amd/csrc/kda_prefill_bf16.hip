@@ -273,8 +273,10 @@ struct BArgs {
 };
 
 // CK: the variant that also writes state snapshots (its store addresses stay out of the
-// plain kernel's registers)
-template <int DK, int DV, int NCB, bool CK>
+// plain kernel's registers).  OUT: outputs are written; without them (the state and
+// transition passes of the segmented prefill) the readout Qt S' + P U, P and Qt are not
+// formed at all.
+template <int DK, int DV, int NCB, bool CK, bool OUT>
 __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(const BArgs a) {
     typedef Cfg<DK, NCB> C;
     constexpr int KB = C::KB, KP = C::KP, NV = C::NV;
@@ -395,7 +397,7 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
         auto make = [&]() {  // resources for the current bases (uniform)
             const int nq = recs(eq), nv = recs(ev);
             // beta is read by decay wave 0 only (the others load over an empty range)
-            Rq = rsrc(pq, nq); Rk = rsrc(pk, nq); Rl = rsrc(pl, nq); Rb = rsrc(pb, w == 0 ? recs(eb) : 0);
+            Rq = rsrc(pq, OUT ? nq : 0); Rk = rsrc(pk, nq); Rl = rsrc(pl, nq); Rb = rsrc(pb, w == 0 ? recs(eb) : 0);
 #pragma unroll
             for (int e = 0; e < C::VG_PER_WAVE; ++e) {  // V read as zeros, or the gate unused:
                 const bool gate = vg_t[e] == 1;          // an empty range (nothing is read)
@@ -478,12 +480,14 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
                         F[i] = __builtin_amdgcn_exp2f(d);
                         Fi[i] = __builtin_amdgcn_exp2f(-d);
                     }
-                    split4(q4[hh] * F, qh[hh], ql[hh]);
+                    if constexpr (OUT) split4(q4[hh] * F, qh[hh], ql[hh]);
                     split4(k4[hh] * Fi, kbh[hh], kbl[hh]);
                     kt[hh] = to_bf4(k4[hh] * F);
                 }
-                lds_st(L + C::L_QH + rowq, piece(qh[0], qh[1]));
-                lds_st(L + C::L_QL + rowq, piece(ql[0], ql[1]));
+                if constexpr (OUT) {
+                    lds_st(L + C::L_QH + rowq, piece(qh[0], qh[1]));
+                    lds_st(L + C::L_QL + rowq, piece(ql[0], ql[1]));
+                }
                 lds_st(L + C::L_KBH + rowk, piece(kbh[0], kbh[1]));
                 lds_st(L + C::L_KBL + rowk, piece(kbl[0], kbl[1]));
                 lds_st(kslot(c) + rowk, piece(kt[0], kt[1]));
@@ -561,7 +565,7 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
             {
                 // P of chunk it + 2, as A-fragments hi/lo: C(P^T) = C(Kb Qt^T)
                 const int c = it + 2;
-                if (c >= 0 && c < nch) {
+                if (OUT && c >= 0 && c < nch) {
                     const unsigned char* L = lslot(c);
                     f32x4 acc = zero4();
 #pragma unroll
@@ -666,9 +670,11 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
                 auto ldp = [&](int p) {
                     Ops o;
                     o.wt = lds_ld<bf16x8>(W + C::W_WT + p * 1024 + lane * 16);
-                    const int off = r * C::RSQ + 2 * (32 * p + 8 * g);
-                    o.qh = lds_ld<bf16x8>(L + C::L_QH + off);
-                    o.ql = lds_ld<bf16x8>(L + C::L_QL + off);
+                    if constexpr (OUT) {
+                        const int off = r * C::RSQ + 2 * (32 * p + 8 * g);
+                        o.qh = lds_ld<bf16x8>(L + C::L_QH + off);
+                        o.ql = lds_ld<bf16x8>(L + C::L_QL + off);
+                    }
                     return o;
                 };
                 auto ldk = [&](int b) {  // Kb^T fragments of row block b, hi | lo
@@ -701,15 +707,17 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
 #pragma unroll
                     for (int cb = 0; cb < CPW; ++cb) {  // S holds S' = Diag(gamma) S already
                         const bf16x8 sh = to_bf8(S[cb][2 * p], S[cb][2 * p + 1]);
-                        const bf16x8 sl = to_bf8(mfma32(nid_lo, sh, S[cb][2 * p]),       // S' - hi
-                                                 mfma32(nid_hi, sh, S[cb][2 * p + 1]));
                         U[cb] = mfma32(cur.wt, sh, U[cb]);  // U = Ut - Wt S'
-                        O[cb] = mfma32(cur.qh, sh, O[cb]);  // O = Qt S': qh sh + ql sh + qh sl
-                        O[cb] = mfma32(cur.ql, sh, O[cb]);
-                        O[cb] = mfma32(cur.qh, sl, O[cb]);
+                        if constexpr (OUT) {
+                            const bf16x8 sl = to_bf8(mfma32(nid_lo, sh, S[cb][2 * p]),       // S' - hi
+                                                     mfma32(nid_hi, sh, S[cb][2 * p + 1]));
+                            O[cb] = mfma32(cur.qh, sh, O[cb]);  // O = Qt S': qh sh + ql sh + qh sl
+                            O[cb] = mfma32(cur.ql, sh, O[cb]);
+                            O[cb] = mfma32(cur.qh, sl, O[cb]);
+                        }
                     }
                 });
-                const bf16x8 pp = lds_ld<bf16x8>(Gs + C::G_P + lane * 16);  // P hi | P lo
+                const bf16x8 pp = OUT ? lds_ld<bf16x8>(Gs + C::G_P + lane * 16) : tt0;  // P hi | P lo
                 bf16x8 k0 = ldk(0), k1;
                 f32x4 gm0 = ldg(0), gm1;
                 __builtin_amdgcn_sched_barrier(0);
@@ -721,10 +729,12 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
                     split4(U[cb], uh, ul[cb]);
                     uu[cb] = cat8(uh, uh);
                 }
+                if constexpr (OUT) {
 #pragma unroll
-                for (int cb = 0; cb < CPW; ++cb) {
-                    O[cb] = mfma32(pp, uu[cb], O[cb]);                      // + P U: ph uh + pl uh
-                    O[cb] = mfma32(pp, cat8(ul[cb], zero_bf4()), O[cb]);   //        + ph ul
+                    for (int cb = 0; cb < CPW; ++cb) {
+                        O[cb] = mfma32(pp, uu[cb], O[cb]);                      // + P U: ph uh + pl uh
+                        O[cb] = mfma32(pp, cat8(ul[cb], zero_bf4()), O[cb]);   //        + ph ul
+                    }
                 }
                 // S <- S' + Kb^T U, row block by row block: kh uh + kl uh, then kh ul.  Then
                 // the next chunk's decay: S' = Diag(gamma) S, one block behind the products
@@ -774,19 +784,21 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
                         for (int cb = 0; cb < CPW; ++cb) S[cb][b] *= gm;
                     }
                 }
-                // gated output rows of this chunk: the block O[4g+i][r] goes through LDS as the
-                // rows of O^T and comes back transposed, O[r][4g..4g+3], one 8-byte store per lane
-                const int64_t t0 = tbeg + 16 * (int64_t)c;
+                if constexpr (OUT) {
+                    // gated output rows of this chunk: the block O[4g+i][r] goes through LDS as the
+                    // rows of O^T and comes back transposed, O[r][4g..4g+3], one 8-byte store per lane
+                    const int64_t t0 = tbeg + 16 * (int64_t)c;
 #pragma unroll
-                for (int cb = 0; cb < CPW; ++cb) {
-                    const int blk = CPW * wave + cb;
-                    const f32x4 gt = to_f4(lds_tr(L + C::L_G + tr_v + 32 * blk)) * scale;
-                    unsigned char* Ob = smem + C::OFF_O + blk * C::O_SIZE;
-                    lds_st(Ob + r * C::ORS + 8 * g, to_bf4(gt * O[cb]));
-                    const bf16x4 orow = lds_tr(Ob + tr_o);
-                    if (a.out && t0 + r < tend)
-                        *reinterpret_cast<bf16x4*>(a.out + (t0 + r) * rowv + (int64_t)h * DV + col0 + 16 * blk + 4 * g) =
-                            orow;
+                    for (int cb = 0; cb < CPW; ++cb) {
+                        const int blk = CPW * wave + cb;
+                        const f32x4 gt = to_f4(lds_tr(L + C::L_G + tr_v + 32 * blk)) * scale;
+                        unsigned char* Ob = smem + C::OFF_O + blk * C::O_SIZE;
+                        lds_st(Ob + r * C::ORS + 8 * g, to_bf4(gt * O[cb]));
+                        const bf16x4 orow = lds_tr(Ob + tr_o);
+                        if (a.out && t0 + r < tend)
+                            *reinterpret_cast<bf16x4*>(a.out + (t0 + r) * rowv + (int64_t)h * DV + col0 + 16 * blk + 4 * g) =
+                                orow;
+                    }
                 }
             }
             lds_barrier();
@@ -802,7 +814,7 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
     }
 }
 
-template <int DK, int DV, int NCB, bool CK>
+template <int DK, int DV, int NCB, bool CK, bool OUT>
 hipError_t launch_bf16(const PrefillArgs& p, hipStream_t st) {
     typedef Cfg<DK, NCB> C;
     static_assert(C::LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -820,19 +832,22 @@ hipError_t launch_bf16(const PrefillArgs& p, hipStream_t st) {
     if (a.num_groups == 0) return hipSuccess;
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)prefill_bf16_kernel<DK, DV, NCB, CK>,
+        hipError_t e = hipFuncSetAttribute((const void*)prefill_bf16_kernel<DK, DV, NCB, CK, OUT>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL((prefill_bf16_kernel<DK, DV, NCB, CK>), dim3((unsigned)blocks), dim3(C::THREADS),
+    hipLaunchKernelGGL((prefill_bf16_kernel<DK, DV, NCB, CK, OUT>), dim3((unsigned)blocks), dim3(C::THREADS),
                        C::LDS_BYTES, st, a);
     return hipGetLastError();
 }
 
 template <int DK, int DV, int NCB>
 hipError_t launch_ck(const PrefillArgs& p, hipStream_t st) {
-    return p.checkpoints ? launch_bf16<DK, DV, NCB, true>(p, st) : launch_bf16<DK, DV, NCB, false>(p, st);
+    // snapshots come with outputs only (the variant without outputs serves the segmented
+    // prefill's state and transition passes)
+    if (p.checkpoints) return launch_bf16<DK, DV, NCB, true, true>(p, st);
+    return p.out ? launch_bf16<DK, DV, NCB, false, true>(p, st) : launch_bf16<DK, DV, NCB, false, false>(p, st);
 }
 
 }  // namespace

@@ -97,7 +97,8 @@ def chunk_prefill(q, k, v, log_alpha, beta, gate, cu_seqlens=None, initial_state
                   out: Optional[torch.Tensor] = None,
                   final_state: Optional[torch.Tensor] = None,
                   checkpoint_every: Optional[int] = None,
-                  checkpoints: Optional[torch.Tensor] = None):
+                  checkpoints: Optional[torch.Tensor] = None,
+                  segment_len: Optional[int] = None):
     """KDA chunked prefill.
 
     Fixed length: q/k/log_alpha [B, T, H, dk], v/gate [B, T, H, dv], beta [B, T, H].
@@ -110,6 +111,11 @@ def chunk_prefill(q, k, v, log_alpha, beta, gate, cu_seqlens=None, initial_state
     checkpoints fp32 [T_total // m, H, dk, dv]: sequence n's snapshot after j*m tokens is
     at slot checkpoint_slot(cu_seqlens, n, j, m); slots no snapshot maps to keep their
     contents (uninitialised when the tensor is allocated here).
+
+    segment_len: None lets the library choose the schedule (kda_prefill_segment_plan): for
+    batches with too few (sequence, head) chains to fill the GPU, each sequence is cut into
+    segments that run side by side (kda_chunk_prefill_segmented, with a workspace allocated
+    here); 0 forces the plain schedule, a positive multiple of 16 that segment length.
     """
     dt = q.dtype
     if dt not in _DT:
@@ -163,6 +169,23 @@ def chunk_prefill(q, k, v, log_alpha, beta, gate, cu_seqlens=None, initial_state
     p = _lib.params(_DT[dt], H, dk, dv, log_alpha_floor, scale)
     lib = _lib.load()
     if checkpoint_every is None:
+        seg = segment_len
+        if seg is None:
+            seg = lib.kda_prefill_segment_plan(ctypes.byref(p), cu_h, N)
+            if seg < 0:
+                raise _lib.KdaError(_lib.KDA_ERR_INVALID_ARGUMENT, lib.kda_last_error().decode())
+        if seg > 0:
+            need = lib.kda_prefill_segmented_workspace(ctypes.byref(p), cu_h, N, int(seg))
+            if need < 0:
+                raise _lib.KdaError(_lib.KDA_ERR_INVALID_ARGUMENT, lib.kda_last_error().decode())
+            ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+            st = lib.kda_chunk_prefill_segmented(
+                ctypes.byref(p), _ptr(qf), _ptr(kf), _ptr(vf), _ptr(laf), _ptr(bf), _ptr(gf), cu_h,
+                N, _ptr(initial_state), _ptr(final_state), _ptr(out), int(seg), _ptr(ws),
+                ws.numel(), _stream())
+            _lib.check(st)
+            o = out.reshape(v.shape) if q.dim() == 4 else out
+            return o, final_state
         st = lib.kda_chunk_prefill(ctypes.byref(p), _ptr(qf), _ptr(kf), _ptr(vf), _ptr(laf),
                                    _ptr(bf), _ptr(gf), _ptr(cu_dev), cu_h, N,
                                    _ptr(initial_state), _ptr(final_state), _ptr(out),

@@ -324,3 +324,18 @@ def test_noalloc_rejects_problems_beyond_its_fixed_buffer():
                                                  1, None, None, A + 0x70000, 16384, None)
     assert st == INV
     assert "fixed buffer" in lib.kda_last_error().decode()
+
+
+def test_segment_plan_picks_segments_only_for_few_long_chains():
+    """kda_prefill_segment_plan (host-only; 256 compute units assumed without a GPU): the
+    long single sequence with 32 heads is cut into 8 segments of 16384 tokens; short
+    sequences, many (sequence, head) chains and fp32 inputs keep the plain schedule."""
+    lib = _lib.load()
+    bf = lambda H: _lib.params(_lib.KDA_DTYPE_BF16, H, 128, 128)
+    plan = lambda p, *c: lib.kda_prefill_segment_plan(ctypes.byref(p), cu(*c), len(c) - 1)
+    assert plan(bf(32), 0, 131072) == 16384
+    assert plan(bf(4), 0, 524288) == 8192
+    assert plan(bf(16), 0, 4096, 8192, 12288, 16384) == 0          # 64 chains of 256 chunks
+    assert plan(bf(32), *[4096 * i for i in range(65)]) == 0        # 2048 chains
+    assert plan(_lib.params(_lib.KDA_DTYPE_F32, 32, 128, 128), 0, 131072) == 0
+    assert plan(bf(32), 0, 100, 50) == -1                           # decreasing
