@@ -186,7 +186,7 @@ kda_status prefill(const char* entry, const kda_params* params, const void* q, c
     a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta; a.gate = gate;
     a.cu_seqlens = cu_seqlens; a.initial_state = initial_state; a.final_state = final_state;
     a.out = out;
-    a.v_zero = false; a.s0_identity = false;
+    a.v_zero = false; a.s0_identity = false; a.dual = false; a.transitions = nullptr;
     a.checkpoints = n_ckpt > 0 ? checkpoints : nullptr;
     a.ckpt_chunks = n_ckpt > 0 ? ckpt_every / 16 : 0;
     a.num_ordered = 0;
@@ -521,14 +521,22 @@ kda_status segmented(const char* entry, const kda_params* params, const void* q,
     a.cu_seqlens = seg_cu; a.checkpoints = nullptr; a.ckpt_chunks = 0; a.num_ordered = 0;
     const int64_t pairs = pl.nseg * H, seg_chunks = segment_len / 16;
     const char* phase = "";
-    // 1: each segment's own state, from zero (outputs not written)
+    a.dual = false; a.transitions = nullptr;
+    // 1: each segment's own state, from zero (outputs not written); with bf16 inputs and
+    // dk == dv, its transition in the same pass (2), sharing the key-side work
     a.v_zero = false; a.s0_identity = false;
     a.initial_state = nullptr; a.final_state = Sloc; a.out = nullptr;
-    a.nv = kda::prefill_pick_nv(p.dv, pairs, seg_chunks, cus);
+    const bool dual = p.dtype == KDA_DTYPE_BF16 && kda::prefill_bf16_dual_supports(p.dk, p.dv);
+    if (dual) {
+        a.dual = true; a.transitions = M; a.nv = p.dv;
+    } else {
+        a.nv = kda::prefill_pick_nv(p.dv, pairs, seg_chunks, cus);
+    }
     e = kda::launch_prefill(a, hs);
-    phase = "segment states";
+    a.dual = false; a.transitions = nullptr;
+    phase = dual ? "segment states and transitions" : "segment states";
     // 2: each segment's transition: the chain from the identity with zero values
-    if (e == hipSuccess) {
+    if (e == hipSuccess && !dual) {
         a.dv = p.dk; a.v_zero = true; a.s0_identity = true; a.final_state = M;
         a.nv = kda::prefill_pick_nv(p.dk, pairs, seg_chunks, cus);
         e = kda::launch_prefill(a, hs);

@@ -36,6 +36,9 @@ struct PrefillArgs {
     int ckpt_chunks;             // chunks between snapshots (checkpoint_every / 16); 0 = none
     int nv;                      // value columns per workgroup (dv-slice width)
     int num_ordered;             // entries of order[] in use (0 = natural order)
+    bool dual;                   // bf16 only: one pass writes final_state (the value columns
+                                 // stepped from initial_state) and transitions (dk == dv)
+    float* transitions;          // dual: [num_seqs, H, dk, dk] products of the transitions
     int32_t order[kMaxOrdered];  // sequence ids, longest first
 };
 
@@ -101,6 +104,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 // bf16 path (kda_prefill_bf16.hip) and the value-slice widths it implements
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 bool prefill_bf16_supports(int dk, int dv, int nv, bool checkpoints);
+bool prefill_bf16_dual_supports(int dk, int dv);
 
 // value-slice width the prefill would pick for this problem (exposed for tests)
 int prefill_pick_nv(int dv, int64_t num_pairs, int64_t longest_chunks, int cu_count);

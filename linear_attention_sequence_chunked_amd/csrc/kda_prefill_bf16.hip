@@ -198,7 +198,7 @@ __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t rs, uint32_t off
 // eight bytes of bf16 pairs -> four floats
 __device__ __forceinline__ f32x4 unpack_bf4(u32x2 w) { return to_f4(__builtin_bit_cast(bf16x4, w)); }
 
-template <int DK, int NCB>
+template <int DK, int NCB, bool DUAL = false>
 struct Cfg {
     static constexpr int KB = DK / 16;        // 16-channel blocks
     static constexpr int NDW = DK / 32;       // decay waves (32 channels each)
@@ -227,12 +227,16 @@ struct Cfg {
     static constexpr int ROWQ = 16 * RSQ, ROWK = 16 * RSK;
     // row-major [16][NV] bf16 value and gate tiles, read transposed: 2 NV + 32 bytes puts
     // the four rows of each transposed 16-lane group in distinct banks
-    static constexpr int VRS = NV * 2 + 32;
+    // value columns staged in LDS: all of them, or in the dual workgroup (the segmented
+    // prefill's state and transition passes fused) the first half: the other half are
+    // columns of the identity, whose values are zero
+    static constexpr int NVS = DUAL ? NV / 2 : NV;
+    static constexpr int VRS = NVS * 2 + 32;
     static constexpr int VT = 16 * VRS;
     // value and gate rows are staged by the decay waves with 16-byte loads that cover whole
     // row segments of the slice (NV / 8 lanes per row): VGI_T loads per tensor and chunk,
     // VGI in all, load i going to decay wave i % NDW (VG_PER_WAVE per wave)
-    static constexpr int VGI_T = NV >= 32 ? NV / 32 : 1;
+    static constexpr int VGI_T = NVS >= 32 ? NVS / 32 : 1;
     static constexpr int VGI = 2 * VGI_T;
     static constexpr int VG_PER_WAVE = (VGI + NDW - 1) / NDW;
     // long ring (4 slots, chunk c written at iteration c-3, read up to iteration c):
@@ -255,7 +259,7 @@ struct Cfg {
     static constexpr int ORS = 40, O_SIZE = 16 * ORS;
     static constexpr int OFF_L = 0, OFF_K = OFF_L + 4 * L_SIZE, OFF_B = OFF_K + 4 * K_SIZE,
                          OFF_G = OFF_B + 2 * B_SIZE, OFF_W = OFF_G + 4 * G_SIZE,
-                         OFF_O = OFF_W + 2 * W_SIZE, LDS_BYTES = OFF_O + NCB * O_SIZE;
+                         OFF_O = OFF_W + 2 * W_SIZE, LDS_BYTES = OFF_O + (DUAL ? 0 : NCB) * O_SIZE;
 };
 
 struct BArgs {
@@ -264,6 +268,7 @@ struct BArgs {
     const float* S0;
     float* Sf;
     float* ck;      // state snapshots or null
+    float* M;       // dual workgroup: the transitions (columns of the identity stepped)
     int ck_chunks;  // chunks between snapshots
     int v_zero, s0_identity;
     bf16* out;      // null: no output rows
@@ -276,9 +281,14 @@ struct BArgs {
 // plain kernel's registers).  OUT: outputs are written; without them (the state and
 // transition passes of the segmented prefill) the readout Qt S' + P U, P and Qt are not
 // formed at all.
-template <int DK, int DV, int NCB, bool CK, bool OUT>
-__global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(const BArgs a) {
-    typedef Cfg<DK, NCB> C;
+// DUAL (no outputs, no snapshots, DK == DV): the chain waves of the first half step the
+// state of the value columns from the given initial state, those of the second half the
+// columns of the identity with zero values, i.e. the chunk transitions' product; one pass
+// of key-side work serves both.
+template <int DK, int DV, int NCB, bool CK, bool OUT, bool DUAL>
+__global__ __launch_bounds__((Cfg<DK, NCB, DUAL>::THREADS)) void prefill_bf16_kernel(const BArgs a) {
+    typedef Cfg<DK, NCB, DUAL> C;
+    static_assert(!DUAL || (!OUT && !CK && DK == DV), "the dual workgroup has no outputs");
     constexpr int KB = C::KB, KP = C::KP, NV = C::NV;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
@@ -299,13 +309,17 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
     const int nch = (int)((len + 15) / 16);
     const int col0 = slice * NV;
     if (nch == 0) {  // empty sequence: the final state is the initial state
-        if (a.Sf && wave < C::NCHAIN) {
+        const bool ident = DUAL && wave >= C::NCHAIN / 2;
+        const int vw = ident ? wave - C::NCHAIN / 2 : wave;
+        float* dst = ident ? a.M : a.Sf;
+        if (dst && wave < C::NCHAIN) {
             const int64_t base = ((int64_t)seq * H + h) * DK * DV;
             for (int cb = 0; cb < C::CPW; ++cb) {
-                const int col = col0 + 16 * (C::CPW * wave + cb) + (lane & 15);
+                const int col = col0 + 16 * (C::CPW * vw + cb) + (lane & 15);
                 for (int row = lane >> 4; row < DK; row += 4)
-                    a.Sf[base + row * DV + col] =
-                        a.S0 ? a.S0[base + row * DV + col] : (a.s0_identity && row == col) ? 1.f : 0.f;
+                    dst[base + row * DV + col] =
+                        ident ? (row == col ? 1.f : 0.f)
+                              : a.S0 ? a.S0[base + row * DV + col] : (a.s0_identity && row == col) ? 1.f : 0.f;
             }
         }
         return;
@@ -324,7 +338,7 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
     // channels 16b + 4q .. +3, i.e. positions 32 (b >> 1) + 8q + 4 (b & 1) (see Cfg)
     const int tr_k = (4 * g + trj) * C::RSK + 16 * trq;
     auto tr_blk = [](int b) { return 64 * (b >> 1) + 8 * (b & 1); };
-    const int tr_v = (4 * g + trj) * C::VRS + 8 * trq;   // [16][NV] tiles
+    const int tr_v = (4 * g + trj) * C::VRS + 8 * trq;   // [16][NVS] tiles
     const int tr_o = (4 * g + trj) * C::ORS + 8 * trq;   // [16][16] output block
 
     // Each role runs its own loop over iterations it = -3 .. it_end-1 with one LDS barrier
@@ -345,12 +359,12 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
         const int w = wave - C::W_DECAY0;   // 32-channel block
         const int dch = 32 * w + 8 * g;     // this lane's first channel
         // value / gate loads of this wave: load i = w + NDW*e covers tensor i / VGI_T (0: V,
-        // 1: gate), 16-byte piece q = 64 (i % VGI_T) + lane of that tensor's [16][NV] tile:
-        // row q / (NV/8), bytes 16 (q % (NV/8)).  A wave past the last load still issues it,
+        // 1: gate), 16-byte piece q = 64 (i % VGI_T) + lane of that tensor's [16][NVS] tile:
+        // row q / (NVS/8), bytes 16 (q % (NVS/8)).  A wave past the last load still issues it,
         // over an empty range, which reads nothing; a lane past the tile repeats piece 0 and
         // stores nothing.
         constexpr int NDW = C::NDW;
-        constexpr int PPR = NV / 8;  // 16-byte pieces per row
+        constexpr int PPR = C::NVS / 8;  // 16-byte pieces per row of the staged tiles
         int vg_t[C::VG_PER_WAVE], vg_row[C::VG_PER_WAVE], vg_col[C::VG_PER_WAVE];
         bool vg_own[C::VG_PER_WAVE], vg_lane[C::VG_PER_WAVE];
 #pragma unroll
@@ -617,10 +631,13 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
         // arbitration over the other roles' on the same SIMD.
         __builtin_amdgcn_s_setprio(3);
         constexpr int CPW = C::CPW;
+        // dual workgroup: the second half of the chain waves step columns of the identity
+        const bool ident = DUAL && wave >= C::NCHAIN / 2;
+        const int vw = ident ? wave - C::NCHAIN / 2 : wave;  // column-block group in its half
         // fp32 state S' of rows 16b+4g+i, value column ccol[cb], in MFMA accumulator layout
         int ccol[CPW];
 #pragma unroll
-        for (int cb = 0; cb < CPW; ++cb) ccol[cb] = col0 + 16 * (CPW * wave + cb) + r;
+        for (int cb = 0; cb < CPW; ++cb) ccol[cb] = col0 + 16 * (CPW * vw + cb) + r;
         f32x4 S[CPW][KB];
 #pragma unroll
         for (int cb = 0; cb < CPW; ++cb)
@@ -628,7 +645,8 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
             for (int b = 0; b < KB; ++b)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    S[cb][b][i] = a.S0 ? a.S0[sbase + (16 * b + 4 * g + i) * DV + ccol[cb]]
+                    S[cb][b][i] = ident ? (16 * b + 4 * g + i == ccol[cb] ? 1.f : 0.f)
+                                  : a.S0 ? a.S0[sbase + (16 * b + 4 * g + i) * DV + ccol[cb]]
                                        : (a.s0_identity && 16 * b + 4 * g + i == ccol[cb]) ? 1.f : 0.f;
         const float scale = a.scale;
         // A-fragments of -I in the lower or upper half of a 32-deep operand (element j of
@@ -689,7 +707,8 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
                 const bf16x8 tt0 = lds_ld<bf16x8>(Gs + C::G_TT + lane * 16);
                 bf16x4 vt[CPW];
 #pragma unroll
-                for (int cb = 0; cb < CPW; ++cb) vt[cb] = lds_tr(L + C::L_V + tr_v + 32 * (CPW * wave + cb));
+                for (int cb = 0; cb < CPW; ++cb)  // columns of the identity have zero values
+                    vt[cb] = ident ? zero_bf4() : lds_tr(L + C::L_V + tr_v + 32 * (CPW * vw + cb));
                 Ops o0 = ldp(0), o1;
                 __builtin_amdgcn_sched_barrier(0);
                 f32x4 U[CPW], O[CPW];
@@ -803,28 +822,29 @@ __global__ __launch_bounds__((Cfg<DK, NCB>::THREADS)) void prefill_bf16_kernel(c
             }
             lds_barrier();
         }
-        if (a.Sf) {
+        float* dst = ident ? a.M : a.Sf;
+        if (dst) {
 #pragma unroll
             for (int cb = 0; cb < CPW; ++cb)
 #pragma unroll
                 for (int b = 0; b < KB; ++b)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) a.Sf[sbase + (16 * b + 4 * g + i) * DV + ccol[cb]] = S[cb][b][i];
+                    for (int i = 0; i < 4; ++i) dst[sbase + (16 * b + 4 * g + i) * DV + ccol[cb]] = S[cb][b][i];
         }
     }
 }
 
-template <int DK, int DV, int NCB, bool CK, bool OUT>
+template <int DK, int DV, int NCB, bool CK, bool OUT, bool DUAL = false>
 hipError_t launch_bf16(const PrefillArgs& p, hipStream_t st) {
-    typedef Cfg<DK, NCB> C;
+    typedef Cfg<DK, NCB, DUAL> C;
     static_assert(C::LDS_BYTES <= 160 * 1024, "LDS budget");
     BArgs a;
     a.q = (const bf16*)p.q; a.k = (const bf16*)p.k; a.v = (const bf16*)p.v;
     a.la = (const bf16*)p.log_alpha; a.beta = (const bf16*)p.beta; a.gate = (const bf16*)p.gate;
     a.cu = p.cu_seqlens; a.S0 = p.initial_state; a.Sf = p.final_state; a.out = (bf16*)p.out;
-    a.ck = p.checkpoints; a.ck_chunks = p.ckpt_chunks;
+    a.ck = p.checkpoints; a.ck_chunks = p.ckpt_chunks; a.M = DUAL ? p.transitions : nullptr;
     a.v_zero = p.v_zero; a.s0_identity = p.s0_identity;
-    a.H = p.H; a.n_slices = DV / (16 * NCB); a.num_groups = p.num_seqs * p.H;
+    a.H = p.H; a.n_slices = DUAL ? 1 : DV / (16 * NCB); a.num_groups = p.num_seqs * p.H;
     a.groups_padded = (a.num_groups + 7) / 8 * 8;
     a.num_ordered = p.num_ordered; a.floor_ = p.floor_; a.scale = p.scale;
     for (int i = 0; i < p.num_ordered; ++i) a.order[i] = p.order[i];
@@ -832,12 +852,12 @@ hipError_t launch_bf16(const PrefillArgs& p, hipStream_t st) {
     if (a.num_groups == 0) return hipSuccess;
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)prefill_bf16_kernel<DK, DV, NCB, CK, OUT>,
+        hipError_t e = hipFuncSetAttribute((const void*)prefill_bf16_kernel<DK, DV, NCB, CK, OUT, DUAL>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL((prefill_bf16_kernel<DK, DV, NCB, CK, OUT>), dim3((unsigned)blocks), dim3(C::THREADS),
+    hipLaunchKernelGGL((prefill_bf16_kernel<DK, DV, NCB, CK, OUT, DUAL>), dim3((unsigned)blocks), dim3(C::THREADS),
                        C::LDS_BYTES, st, a);
     return hipGetLastError();
 }
@@ -853,6 +873,8 @@ hipError_t launch_ck(const PrefillArgs& p, hipStream_t st) {
 }  // namespace
 
 // value-slice widths this path supports for (dk, dv)
+bool prefill_bf16_dual_supports(int dk, int dv) { return dk == dv && (dk == 128 || dk == 64); }
+
 bool prefill_bf16_supports(int dk, int dv, int nv, bool checkpoints) {
     if (nv < 16 || nv > dv || nv > 128 || (dk != 128 && dk != 64)) return false;
     // the snapshot stores of a full-width dk = 128 workgroup would not fit its registers
@@ -860,6 +882,11 @@ bool prefill_bf16_supports(int dk, int dv, int nv, bool checkpoints) {
 }
 
 hipError_t launch_prefill_bf16(const PrefillArgs& p, hipStream_t st) {
+    if (p.dual) {  // state and transition passes of the segmented prefill, fused
+        if (p.dk == 128 && p.dv == 128) return launch_bf16<128, 128, 16, false, false, true>(p, st);
+        if (p.dk == 64 && p.dv == 64) return launch_bf16<64, 64, 8, false, false, true>(p, st);
+        return hipErrorInvalidValue;
+    }
 #define KDA_NV_CASES(DK, DV)                                          \
     switch (p.nv) {                                                   \
         case 16: return launch_ck<DK, DV, 1>(p, st);                  \
