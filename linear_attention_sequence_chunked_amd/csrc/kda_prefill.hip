@@ -374,29 +374,6 @@ hipError_t launch_dims(const PrefillArgs& p, hipStream_t st) {
 
 }  // namespace
 
-int prefill_pick_nv(int dv, int64_t num_pairs, int64_t longest_chunks, int cu_count) {
-    (void)longest_chunks;
-    // one workgroup per compute unit at a time (the bf16 kernel holds ~130 KB of LDS):
-    // split the value columns until the (sequence, head) pairs cover every unit once
-    int slices = 1;
-    while (slices < dv / 16 && num_pairs * slices < (int64_t)cu_count) slices *= 2;
-    return dv / slices;
-}
-
-int32_t prefill_segment_plan(int64_t num_pairs, int64_t longest_chunks, int dtype, int cu_count) {
-    // Segments pay when the (sequence, head) chains are too few to give every compute unit
-    // a full-width workgroup and long enough that each segment still spans many chunks:
-    // the state and transition passes (without outputs) and the scan cost about two
-    // output-less passes on top of the output pass, while the chains get `segments` times
-    // shorter.  One segment count per problem: enough for a workgroup per compute unit.
-    if (dtype != DTYPE_BF16 || num_pairs <= 0 || 2 * num_pairs > cu_count) return 0;
-    const int64_t segments = (cu_count + num_pairs - 1) / num_pairs;
-    const int64_t seg_chunks = (longest_chunks + segments - 1) / segments;
-    constexpr int64_t kMinSegmentChunks = 256;  // 4096 tokens
-    if (segments < 2 || seg_chunks < kMinSegmentChunks) return 0;
-    return (int32_t)(16 * seg_chunks);
-}
-
 hipError_t launch_prefill(const PrefillArgs& p, hipStream_t st) {
     if (p.dtype == DTYPE_BF16) {
         PrefillArgs q = p;

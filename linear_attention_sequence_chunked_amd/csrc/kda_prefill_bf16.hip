@@ -873,14 +873,6 @@ hipError_t launch_ck(const PrefillArgs& p, hipStream_t st) {
 }  // namespace
 
 // value-slice widths this path supports for (dk, dv)
-bool prefill_bf16_dual_supports(int dk, int dv) { return dk == dv && (dk == 128 || dk == 64); }
-
-bool prefill_bf16_supports(int dk, int dv, int nv, bool checkpoints) {
-    if (nv < 16 || nv > dv || nv > 128 || (dk != 128 && dk != 64)) return false;
-    // the snapshot stores of a full-width dk = 128 workgroup would not fit its registers
-    return !(checkpoints && dk == 128 && nv > 64);
-}
-
 hipError_t launch_prefill_bf16(const PrefillArgs& p, hipStream_t st) {
     if (p.dual) {  // state and transition passes of the segmented prefill, fused
         if (p.dk == 128 && p.dv == 128) return launch_bf16<128, 128, 16, false, false, true>(p, st);
