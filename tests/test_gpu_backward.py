@@ -2,8 +2,17 @@
 (oracle/reference.py recurrent_backward, pinned by finite differences in
 tests/test_oracle_backward.py), per (sequence, head), on the same rounded inputs.
 
-The GPU walks the recurrence in fp32 whatever the input dtype, so one tolerance applies:
-max|err| <= 1e-3 * RMS(ref) per gradient tensor."""
+Tolerance, per gradient tensor: max|err| <= TOL * RMS(ref), TOL = 32 * 2^-16 (~4.9e-4),
+the same for bf16 and fp32 inputs because the backward computes the same way for both (the
+inputs are exact in fp32; the state, its gradient and every sum are fp32).  Where it comes
+from: the two walks form every product of the chunk recurrence from split-bf16 operands,
+x = hi + lo with hi = bf16(x) and lo = bf16(x - hi), and drop the lo*lo term, so each
+product carries a relative error of at most ~3 * 2^-16 (each half rounds to within 2^-8
+of what it represents); a sum of 128 such products over the key channels can grow that by
+up to sqrt(128) ~ 11 relative to its own size where its terms cancel; and the transition
+of a chunk is non-expansive, so the errors carried along the recurrence add up to a
+bounded multiple (about 3x on these inputs) of one chunk's.  The gradient kernel itself
+runs fp32 products (2^-24).  Measured errors are 1e-5 to 1.5e-4 of RMS."""
 import numpy as np
 import pytest
 import torch
@@ -14,7 +23,7 @@ from oracle import reference as ref
 from parity import host, log
 
 pytestmark = pytest.mark.gpu
-TOL = 1e-3
+TOL = 32 * 2.0 ** -16
 
 
 def check(name, got, want):
@@ -22,7 +31,7 @@ def check(name, got, want):
     assert np.all(np.isfinite(got)), f"{name}: non-finite values"
     rms = float(np.sqrt(np.mean(want * want)))
     err = float(np.max(np.abs(got - want))) / max(rms, 1e-30)
-    log(f"  {name}: max|err|/RMS = {err:.2e}")
+    log(f"  {name}: max|err|/RMS = {err:.2e} (tol {TOL:.2e}, margin {TOL / max(err, 1e-30):.1f}x)")
     assert err <= TOL, f"{name}: {err:.3e} > {TOL}"
 
 
