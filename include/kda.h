@@ -230,14 +230,15 @@ int32_t kda_prefill_segment_plan(const kda_params* params, const int32_t* cu_seq
  *   dbeta           : fp32 [T_total, H];  d_initial_state : fp32 [num_seqs, H, dk, dv]
  *                     or NULL.  No output may overlap another argument.
  *   workspace       : device memory of at least kda_prefill_backward_workspace(...) bytes,
- *                     256-byte aligned, overlapping no other argument; receives the state
- *                     entering every 16-token chunk and the gradient of the state leaving
- *                     it (fp32, dk x dv each per chunk and head), and three 16 x dv fp32
- *                     blocks per chunk and head passed from the walks to the gradients.
+ *                     256-byte aligned, overlapping no other argument; receives, per pair
+ *                     of 16-token chunks and head, the state entering the first and the
+ *                     gradient of the state leaving the second (fp32, dk x dv each), and
+ *                     three 16 x dv fp32 blocks per chunk and head passed from the walks to
+ *                     the gradients.
  * The gradients are computed in fp32 with the 16-token chunk algebra of the forward: one
- * launch walks every sequence forwards (the chunk-entering states) and backwards (the
- * state gradient) side by side, a second forms each chunk's input gradients from those,
- * all chunks in parallel.
+ * launch walks every sequence forwards (the states) and backwards (the state gradient) side
+ * by side, a second forms the input gradients of each pair of chunks from those, all pairs
+ * in parallel.
  */
 kda_status kda_prefill_backward(const kda_params* params, const void* q, const void* k,
                                 const void* v, const void* log_alpha, const void* beta,

@@ -620,7 +620,7 @@ int32_t kda_prefill_segment_plan(const kda_params* params, const int32_t* cu_seq
 namespace {
 
 kda_status bwd_size(const kda_params* params, const int32_t* cu, int32_t N, uint64_t& bytes,
-                    uint64_t& grad_off) {
+                    uint64_t& grad_off, uint64_t& aux_stride) {
     kda_status st = check_params(params);
     if (st != KDA_OK) return st;
     if (N < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "num_seqs %d < 1", N);
@@ -630,12 +630,13 @@ kda_status bwd_size(const kda_params* params, const int32_t* cu, int32_t N, uint
         if (cu[n + 1] < cu[n])
             return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens_host decreases at index %d", n + 1);
     const uint64_t H = params->num_heads, ss = (uint64_t)params->dk * params->dv;
-    // the state entering chunk c of sequence n at slot cu[n]/16 + n + c (at most
-    // T_total/16 + N slots), then the gradient leaving the chunk at the same slot, then
-    // three [16][dv] arrays per slot (R, Y, dU of the chunk)
-    const uint64_t slots = (uint64_t)cu[N] / 16 + N;
-    grad_off = slots * H * ss;
-    bytes = 4 * (2 * grad_off + 3 * slots * H * 16 * (uint64_t)params->dv);
+    // the state entering chunk 2j of sequence n at pair slot cu[n]/32 + n + j (at most
+    // T_total/32 + N slots), then the gradient leaving chunk 2j + 1 (2j if it is the last) at
+    // the same slot, then three [16][dv] arrays per chunk slot cu[n]/16 + n + c (R, Y, dU)
+    const uint64_t pair_slots = (uint64_t)cu[N] / 32 + N, slots = (uint64_t)cu[N] / 16 + N;
+    grad_off = pair_slots * H * ss;
+    aux_stride = slots * H * 16 * (uint64_t)params->dv;
+    bytes = 4 * (2 * grad_off + 3 * aux_stride);
     return KDA_OK;
 }
 
@@ -645,8 +646,8 @@ extern "C" {
 
 int64_t kda_prefill_backward_workspace(const kda_params* params,
                                        const int32_t* cu_seqlens_host, int32_t num_seqs) {
-    uint64_t bytes = 0, grad = 0;
-    if (bwd_size(params, cu_seqlens_host, num_seqs, bytes, grad) != KDA_OK) return -1;
+    uint64_t bytes = 0, grad = 0, aux = 0;
+    if (bwd_size(params, cu_seqlens_host, num_seqs, bytes, grad, aux) != KDA_OK) return -1;
     ok();
     return (int64_t)bytes;
 }
@@ -660,8 +661,8 @@ kda_status kda_prefill_backward(const kda_params* params, const void* q, const v
                                 float* dlog_alpha, float* dbeta, float* dgate,
                                 float* d_initial_state, void* workspace,
                                 int64_t workspace_bytes, void* stream) {
-    uint64_t need = 0, grad_off = 0;
-    kda_status st = bwd_size(params, cu_seqlens_host, num_seqs, need, grad_off);
+    uint64_t need = 0, grad_off = 0, aux_stride = 0;
+    kda_status st = bwd_size(params, cu_seqlens_host, num_seqs, need, grad_off, aux_stride);
     if (st != KDA_OK) return st;
     const kda_params& p = *params;
     const int64_t T = cu_seqlens_host[num_seqs];
@@ -713,6 +714,7 @@ kda_status kda_prefill_backward(const kda_params* params, const void* q, const v
     a.d_final_state = d_final_state; a.dq = dq; a.dk_ = dk; a.dv_ = dv; a.dlog_alpha = dlog_alpha;
     a.dbeta = dbeta; a.dgate = dgate; a.d_initial_state = d_initial_state;
     a.workspace = static_cast<float*>(workspace); a.grad_offset = (int64_t)grad_off;
+    a.aux_stride = (int64_t)aux_stride;
     a.T_total = T;
     const hipError_t e = kda::launch_backward(a, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess)

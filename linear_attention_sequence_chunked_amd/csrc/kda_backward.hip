@@ -28,14 +28,14 @@
 // Two launches:
 //   1. walk_kernel walks every (sequence, head, value slice) twice, as two halves of one
 //      grid that run side by side: forwards from the initial state, storing the state
-//      entering every chunk, and backwards from dS_final, storing the gradient leaving
-//      every chunk (dS in MFMA accumulators, as the forward keeps S);
-//   2. grad_kernel takes one (chunk, head) per workgroup -- all chunks in parallel -- and
-//      forms every input gradient of the chunk from its entering state and leaving
-//      gradient.
-// Whatever the input dtype, the state, its gradient and every sum are fp32: the walks'
-// products are split-bf16 (three bf16 MFMAs per product, relative error ~2^-17), the
-// gradient kernel's are fp32 MFMAs (v_mfma_f32_16x16x4_f32).
+//      entering every even chunk, and backwards from dS_final, storing the gradient leaving
+//      every odd chunk and the last (dS in MFMA accumulators, as the forward keeps S);
+//   2. grad_kernel takes one (pair of chunks, head) per workgroup -- all pairs in parallel --
+//      re-forms the pair's other state and gradient from the chunk-local terms, and forms
+//      every input gradient of both chunks.
+// Whatever the input dtype, the state, its gradient and every sum are fp32: the products
+// over key channels or value columns are split-bf16 (three bf16 MFMAs per product, relative
+// error ~2^-17), the 16x16 chunk-local ones fp32 MFMAs (v_mfma_f32_16x16x4_f32).
 #include <math.h>
 
 #include "kda_device.h"
@@ -122,13 +122,14 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// A' = strict_lower(Kh Kc^T) of the chunk (wave 0), then X and T by forward substitution.
+// A' = strict_lower(Kh Kc^T) of the chunk (by the one wave with `active` set), then X and T
+// by forward substitution.  Every thread of the workgroup calls it (two barriers).
 template <int DK, int RS>
 __device__ __forceinline__ void chunk_gram(const float* s_Kh, const float* s_Kc,
                                            const float* s_beta, float* s_A, float* s_X,
-                                           float* s_T, int wave, int lane) {
+                                           float* s_T, bool active, int lane) {
     const int r = lane & 15, g = lane >> 4;
-    if (wave == 0) {
+    if (active) {
         f32x4 acc = zero4();
 #pragma unroll
         for (int kb = 0; kb < DK / 16; ++kb)
@@ -140,7 +141,7 @@ __device__ __forceinline__ void chunk_gram(const float* s_Kh, const float* s_Kc,
         }
     }
     lds_barrier();
-    if (wave == 0 && lane < 16) {  // column `lane` of X = (I + Diag(beta) A')^-1
+    if (active && lane < 16) {  // column `lane` of X = (I + Diag(beta) A')^-1
         const int col = lane;
         float x[kC];
 #pragma unroll
@@ -169,9 +170,9 @@ struct WalkArgs {
     const float* S0;    // initial state, or null
     const float* dSf;   // gradient of the final state, or null
     float* dS0;         // gradient of the initial state, or null
-    float* states;      // state entering chunk c of sequence n: slot cu[n]/16 + n + c, [dv][dk]
-    float* dsc;         // gradient leaving chunk c of sequence n: same slot, [dv][dk]
-    float* aux;         // per slot [dv][16]: R, Y (forwards), dU (backwards)
+    float* states;      // state entering chunk 2j of sequence n: pair slot cu[n]/32 + n + j, [dv][dk]
+    float* dsc;         // gradient leaving chunk 2j + 1 (2j if the last): same slot, [dv][dk]
+    float* aux;         // per chunk slot cu[n]/16 + n + c [dv][16]: R, Y (forwards), dU (backwards)
     int64_t aux_stride; // floats between those three arrays
     int H, n_slices, half, pairs;
     float floor_, scale;
@@ -184,9 +185,12 @@ struct WalkArgs {
 //   producer   the Gram products and T of step it + 1 (buffer (it + 1) % 3);
 //   decay      the decay-folded operands of step it + 2 into buffer (it + 2) % 3, a share
 //              of the 8-channel pieces per decay wave.
-// Each kind of wave runs its own loop with exactly one barrier per step, nch + 2 in all;
-// global inputs are loaded two steps ahead (the consumers' for fp32: one) into alternating
-// register sets.
+// Each kind of wave runs its own loop with exactly one barrier per step, nch + 2 in all.
+// Only the producer and decay waves load global inputs (a few steps ahead, into register
+// rings): the decay waves also stage the consumers' [16][NV] value-side input (V forwards,
+// dO * gate backwards) in LDS, so the consumers issue nothing but stores to global memory
+// inside the walk and never wait on the memory counter, which counts stores and loads
+// alike.
 //
 // Operands relative to the chunk's end (as in the forward): Kt = k e^(G - G_C),
 // Qt = (scale q) e^(G - G_C), Kb = k e^(G_C - G).  Then A' = strict_lower(Kt Kb^T),
@@ -201,7 +205,7 @@ struct WalkArgs {
 // transposed with ds_read_b64_tr_b16: within each 16-lane group, with lane 16g + 4j + q
 // pointing at row 4g + j, columns c0 + 4q .. +3 of a row-major tile X, lane (r, g) receives
 // X[4g + i][c0 + r] -- the A-fragment of the transpose of X's 16x16 block at column c0.
-template <int DK>
+template <int DK, int NV>
 struct alignas(16) WalkBuf {
     static constexpr int RSB = DK + 8;  // bf16 row stride of [16][DK] tiles
     static constexpr int TSB = 16 + 8;  // bf16 row stride of 16x16 tiles
@@ -211,6 +215,7 @@ struct alignas(16) WalkBuf {
     bf16 sq1[2][16 * TSB];              // T (forwards) or P^T (backwards)
     bf16 sq2[2][16 * TSB];              // P (forwards) or T^T (backwards)
     float gamma[DK];
+    float vin[NV * kTS];                // V or dO * gate, transposed: [NV][16 + 4] fp32
 };
 
 struct Split4 {
@@ -288,13 +293,13 @@ template <typename T, int DK, int DV, int NCB, int ND>
 __global__ __launch_bounds__(64 * (NCB + 1 + ND)) void walk_kernel(const WalkArgs<T> a) {
     constexpr int NV = 16 * NCB;
     constexpr int KB = DK / 16;
-    constexpr int PF = sizeof(T) == 2 ? 2 : 1;  // steps of input prefetch (register sets)
+    constexpr int PF = 4;                        // steps of beta prefetch (producer)
     constexpr int CW = DK / 4, NP = CW / 8;      // decay: channels per lane group, pieces
     constexpr int NWD = (int)sizeof(T) / 2;      // 16-byte words per 8-channel piece
     constexpr int PPW = NP / ND;                 // decay pieces per decay wave
-    constexpr int PFD = 2;                       // steps of decay-input prefetch
+    constexpr int PFD = sizeof(T) == 2 ? 4 : 2;  // steps of decay-input prefetch
     static_assert(NP % ND == 0, "decay pieces split evenly over the decay waves");
-    typedef WalkBuf<DK> B;
+    typedef WalkBuf<DK, NV> B;
     constexpr int RSB = B::RSB, TSB = B::TSB;
 
     __shared__ B s_buf[3];
@@ -344,8 +349,8 @@ __global__ __launch_bounds__(64 * (NCB + 1 + ND)) void walk_kernel(const WalkArg
     if (wave == NCB) {
         // ---------------- producer: Gram products and T, one step ahead of the consumers
         T rb[PF];
-        auto fetch = [&](T& x, int it) {
-            if (lane < kC) x = a.beta[row_at(chunk_of(it), lane) * H + h];
+        auto fetch = [&](T& x, int it) {  // every lane loads (lanes 16.. repeat rows 0..15)
+            x = a.beta[row_at(chunk_of(it), lane & 15) * H + h];
         };
         auto gram = [&](T& xb, int it) {  // step it, buffer it % 3; xb then loads step it + PF
             B& o = s_buf[it % 3];
@@ -424,13 +429,14 @@ __global__ __launch_bounds__(64 * (NCB + 1 + ND)) void walk_kernel(const WalkArg
         lds_barrier();  // decay of step 0 written
         gram(rb[0], 0);
         lds_barrier();  // decay of step 1 written
+        // As in the decay waves, the Gram step and its load run unconditionally: gram(nch)
+        // writes a buffer nobody reads, and the (at most PF - 1) steps after it come after
+        // the last barrier.
         for (int it = 0; it < nch; it += PF) {
 #pragma unroll
             for (int j = 0; j < PF; ++j) {
-                if (it + j < nch) {
-                    if (it + j + 1 < nch) gram(rb[(j + 1) % PF], it + j + 1);
-                    lds_barrier();
-                }
+                gram(rb[(j + 1) % PF], it + j + 1);
+                if (it + j < nch) lds_barrier();
             }
         }
         return;
@@ -443,11 +449,28 @@ __global__ __launch_bounds__(64 * (NCB + 1 + ND)) void walk_kernel(const WalkArg
         // pg CW + 8 p + [0, 8).
         const int jd = wave - NCB - 1;
         const int pr = lane & 15, pg = lane >> 4;
+        // value side: decay lane t = 64 jd + lane takes row vr, columns vc + [0, 8) of the
+        // slice (one 16- or 32-byte piece of V, or of dO and of the gate)
+        constexpr int VPR = NV / 8;
+        static_assert(16 * VPR == 64 * ND, "one value piece per decay lane");
+        const int vt = 64 * jd + lane, vr = vt / VPR, vc = 8 * (vt % VPR);
+        const T* const vsrc = rev ? a.dout : a.v;
+        const int64_t vcol = (int64_t)h * DV + (int64_t)slice * NV + vc;
         struct Piece {
             uint4 q[NWD], k[NWD], l[NWD];
         };
+        struct VPiece {
+            uint4 v[NWD], gt[NWD];
+        };
         Piece ring[PFD][PPW];
-        auto dfetch = [&](Piece (&x)[PPW], int s) {
+        VPiece vring[PFD];
+        auto dfetch = [&](Piece (&x)[PPW], VPiece& y, int s) {
+            const int64_t vo = row_at(chunk_of(s), vr) * rowv + vcol;
+#pragma unroll
+            for (int w = 0; w < NWD; ++w) {
+                y.v[w] = *reinterpret_cast<const uint4*>(vsrc + vo + 4 * w);
+                if (rev) y.gt[w] = *reinterpret_cast<const uint4*>(a.gate + vo + 4 * w);
+            }
             const int64_t off = row_at(chunk_of(s), pr) * rowq + (int64_t)h * DK + pg * CW + 8 * PPW * jd;
 #pragma unroll
             for (int p = 0; p < PPW; ++p)
@@ -458,9 +481,23 @@ __global__ __launch_bounds__(64 * (NCB + 1 + ND)) void walk_kernel(const WalkArg
                     x[p].l[w] = *reinterpret_cast<const uint4*>(a.la + off + 8 * p + 4 * w);
                 }
         };
-        auto decay = [&](const Piece (&x)[PPW], int s) {
+        auto decay = [&](const Piece (&x)[PPW], const VPiece& y, int s) {
             B& o = s_buf[s % 3];
-            const bool in = pr < rows_of(chunk_of(s));
+            const int Cp = rows_of(chunk_of(s));
+            const bool in = pr < Cp;
+            {  // the consumers' input, zero on rows past the end of the sequence
+                float xv[8];
+                unpack8<T>(y.v, xv);
+                if (rev) {
+                    float xg[8];
+                    unpack8<T>(y.gt, xg);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) xv[i] *= xg[i];
+                }
+                float* const dst = &o.vin[vc * kTS + vr];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) dst[i * kTS] = vr < Cp ? xv[i] : 0.f;
+            }
 #pragma unroll
             for (int p = 0; p < PPW; ++p) {
                 const int ch0 = pg * CW + 8 * (PPW * jd + p);
@@ -490,17 +527,18 @@ __global__ __launch_bounds__(64 * (NCB + 1 + ND)) void walk_kernel(const WalkArg
                 if (pr == 15) store8(&o.gamma[ch0], gm);
             }
         };
-        // steps 0 .. nch + 1, one barrier each (the last two write buffers nobody reads)
+        // steps 0 .. nch + 1, one barrier each (the last two write buffers nobody reads).  The
+        // loads and the LDS writes run unconditionally, so that the memory-counter waits
+        // see the same number of loads in flight on every path: steps past nch + 1 (at
+        // most PFD - 1 of them) come after the last barrier, when no wave reads LDS.
 #pragma unroll
-        for (int j = 0; j < PFD; ++j) dfetch(ring[j], j);
+        for (int j = 0; j < PFD; ++j) dfetch(ring[j], vring[j], j);
         for (int s = 0; s < nch + 2; s += PFD) {
 #pragma unroll
             for (int j = 0; j < PFD; ++j) {
-                if (s + j < nch + 2) {
-                    decay(ring[j], s + j);
-                    dfetch(ring[j], s + j + PFD);
-                    lds_barrier();
-                }
+                decay(ring[j], vring[j], s + j);
+                dfetch(ring[j], vring[j], s + j + PFD);
+                if (s + j < nch + 2) lds_barrier();
             }
         }
         return;
@@ -508,25 +546,10 @@ __global__ __launch_bounds__(64 * (NCB + 1 + ND)) void walk_kernel(const WalkArg
 
     // ---------------- consumers: wave w owns value columns slice NV + 16 w + [0, 16)
     const int col = slice * NV + 16 * wave + r;
-    float* const out = (rev ? a.dsc : a.states) + ((tbeg / kC + n) * H + h) * SS;
+    // pair slots of the sequence: the state entering even chunks (forwards), the gradient
+    // leaving odd chunks and the last (backwards); the gradient kernel re-forms the others
+    float* const out = (rev ? a.dsc : a.states) + ((tbeg / (2 * kC) + n) * H + h) * SS;
     const int64_t aslot = (tbeg / kC + n) * H + h;  // (slot, head) row of chunk 0
-    const T* const vsrc = rev ? a.dout : a.v;  // backwards: dO (times the gate)
-    // two named register sets (PF == 2; R1 is unused for PF == 1): an array indexed by the
-    // step would be placed in LDS
-    struct Regs {
-        T v[4], g[4];  // V or dO, gate: rows 4g + i, column col
-    } R0, R1;
-    auto fetch = [&](int it) {
-        Regs x;
-        const int c = chunk_of(it);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t off = row_at(c, 4 * g + i) * rowv + (int64_t)h * DV + col;
-            x.v[i] = vsrc[off];
-            x.g[i] = rev ? a.gate[off] : T{};  // the gate enters the backward walk only
-        }
-        return x;
-    };
     // X[b] holds rows 16b + 4g + i, column col of S (forwards) or dS (backwards)
     const float* init = rev ? a.dSf : a.S0;
     f32x4 X[KB];
@@ -537,19 +560,18 @@ __global__ __launch_bounds__(64 * (NCB + 1 + ND)) void walk_kernel(const WalkArg
     // Let the initial loads land here: otherwise the loop's first use of X carries a wait for
     // them, merged at the loop head into a wait on the previous step's stores every step.
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    auto step = [&](Regs& x, int it) {
+    auto step = [&](int it) {
         const B& o = s_buf[it % 3];
         const int c = chunk_of(it);
-        const int Cp = rows_of(c);
-        f32x4 in4;  // V (forwards) or dY = dO * gate (backwards), rows 4g + i, column col
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            in4[i] = 4 * g + i < Cp ? (rev ? to_f32(x.v[i]) * to_f32(x.g[i]) : to_f32(x.v[i])) : 0.f;
+        // V (forwards) or dY = dO * gate (backwards), rows 4g + i, column col
+        const f32x4 in4 = ld4(&o.vin[(16 * wave + r) * kTS + 4 * g]);
         // the state (or gradient) is stored transposed, [dv][dk]: rows 16b + 4g .. +3 of
         // column col are one 16-byte piece
-        float* const dst = out + (int64_t)c * H * SS + col * DK + 4 * g;
+        float* const dst = out + (int64_t)(c >> 1) * H * SS + col * DK + 4 * g;
+        if (rev ? (c & 1) || c == nch - 1 : !(c & 1)) {
 #pragma unroll
-        for (int b = 0; b < KB; ++b) *reinterpret_cast<f32x4*>(dst + 16 * b) = X[b];
+            for (int b = 0; b < KB; ++b) *reinterpret_cast<f32x4*>(dst + 16 * b) = X[b];
+        }
         // this chunk's [16][dv] vectors for the gradient kernel, also transposed ([dv][16])
         float* const ax = a.aux + (rev ? 2 : 0) * a.aux_stride + (aslot + (int64_t)c * H) * kC * DV +
                           col * kC + 4 * g;
@@ -594,19 +616,12 @@ __global__ __launch_bounds__(64 * (NCB + 1 + ND)) void walk_kernel(const WalkArg
                 X[b] = acc * ld4(&o.gamma[16 * b + 4 * g]);
             }
         }
-        x = fetch(it + PF);
         lds_barrier();
     };
     // prologue: the decay waves write steps 0 and 1, the producer the Gram products of step 0
-    static_assert(PF == 1 || PF == 2, "register sets");
-    R0 = fetch(0);
-    if (PF == 2) R1 = fetch(1);
     lds_barrier();
     lds_barrier();
-    for (int it = 0; it < nch; it += PF) {
-        step(R0, it);
-        if (PF == 2 && it + 1 < nch) step(R1, it + 1);
-    }
+    for (int it = 0; it < nch; ++it) step(it);
     if (rev && a.dS0) {
 #pragma unroll
         for (int b = 0; b < KB; ++b)
@@ -616,86 +631,163 @@ __global__ __launch_bounds__(64 * (NCB + 1 + ND)) void walk_kernel(const WalkArg
 }
 
 // ---------------------------------------------------------------------------------------------
-// 2. Per-chunk gradients, one workgroup per (chunk slot, head).
+// 2. Per-chunk gradients, one workgroup per (pair of chunks, head).
+//
+// The walks store the state entering each even chunk 2j and the gradient leaving each odd
+// chunk 2j + 1 (leaving chunk 2j when that is the sequence's last); the workgroup of pair j
+// re-forms the other two from chunk-local terms it forms anyway,
+//   S (entering 2j + 1) = Diag(gamma_2j) S (entering 2j) + Kb_2j^T U_2j
+//   dS (leaving 2j)     = Diag(gamma_2j+1) dS (leaving 2j + 1) + Qh_2j+1^T dY_2j+1
+//                         - Kh_2j+1^T dR_2j+1,
+// which halves the state traffic of both launches.  Waves 0-3 take chunk 2j and waves 4-7
+// chunk 2j + 1 in the per-chunk phases; in the sums over value columns wave w takes channel
+// block w of both chunks and forms the re-formed blocks as it goes.
 template <typename T>
 struct GradArgs {
     const T *q, *k, *v, *la, *beta, *gate, *dout;
     const int32_t* cu;
-    const float* states;  // state entering chunk c of sequence n: slot cu[n]/16 + n + c, [dv][dk]
-    const float* dsc;     // gradient leaving chunk c of sequence n: same slot, [dv][dk]
-    const float* aux;     // per slot [dv][16]: R, Y, dU, aux_stride floats apart
+    const float* states;  // state entering chunk 2j of sequence n: pair slot cu[n]/32 + n + j, [dv][dk]
+    const float* dsc;     // gradient leaving chunk 2j + 1 (2j if the last): same slot, [dv][dk]
+    const float* aux;     // per chunk slot cu[n]/16 + n + c, [dv][16]: R, Y, dU, aux_stride floats apart
     int64_t aux_stride;
     float *dq, *dk, *dv, *dla, *dbeta, *dgate;
     int H, N;
     float floor_, scale;
 };
 
+constexpr int kGW = 2 * kNW;  // waves per gradient workgroup: kNW per chunk of the pair
+
+// A-fragment of the transpose of the 16x16 block at column c0 of a row-major tile X with
+// row stride `stride`: element i of lane (r, g) = X[4g + i][c0 + r]
+__device__ __forceinline__ f32x4 ld4_colv(const float* X, int stride, int c0, int r, int g) {
+    return f32x4{X[(4 * g) * stride + c0 + r], X[(4 * g + 1) * stride + c0 + r],
+                 X[(4 * g + 2) * stride + c0 + r], X[(4 * g + 3) * stride + c0 + r]};
+}
+
 template <typename T, int DK, int DV>
-__global__ __launch_bounds__(kThreads, 2) void grad_kernel(const GradArgs<T> a) {
+__global__ __launch_bounds__(64 * kGW, 1) void grad_kernel(const GradArgs<T> a) {
     constexpr int RS = DK + 4;  // [16][DK] tiles
     constexpr int VS = DV + 4;  // [16][DV] tiles
     constexpr int WS = RS > VS ? RS : VS;
     constexpr int KB = DK / 16, VB = DV / 16;
-    constexpr int OWNC = (KB + kNW - 1) / kNW;
+    static_assert(KB <= kGW, "one channel block per wave");
 
-    __shared__ __attribute__((aligned(16))) float s_Qh[kC * RS], s_Kh[kC * RS], s_Kc[kC * RS];
-    // U, dY, dR [16][DV] during the value-block phase; dQh, dKh, dKc, dKb [16][DK] afterwards
-    __shared__ __attribute__((aligned(16))) float s_big[4 * kC * WS];
+    // per chunk of the pair:
+    __shared__ __attribute__((aligned(16))) float s_Qh[2][kC * RS], s_Kh[2][kC * RS], s_Kc[2][kC * RS];
+    // U, dY, dR [16][DV] during the value-block phases; dQh, dKh, dKc, dKb [16][DK] afterwards
+    __shared__ __attribute__((aligned(16))) float s_big[2][4 * kC * WS];
     // per wave: R and dU of the current value block, then the wave's parts of dT and dP
-    __shared__ __attribute__((aligned(16))) float s_wv[kNW][2][16 * kTS];
-    __shared__ __attribute__((aligned(16))) float s_A[16 * kTS], s_X[16 * kTS], s_T[16 * kTS],
-        s_dT[16 * kTS], s_dP[16 * kTS];
-    __shared__ __attribute__((aligned(16))) float s_gamma[DK], s_dgam[DK];
-    __shared__ float s_beta[kC], s_dbT[kC], s_dbA[kC];
-    float* const s_U = s_big;
-    float* const s_dY = s_big + kC * WS;
-    float* const s_dR = s_big + 2 * kC * WS;
-    float* const s_M = &s_wv[0][0][0];   // X^T dT Diag(beta), once the wave parts are summed
-    float* const s_dA = &s_wv[1][0][0];  // Diag(beta) dA
+    __shared__ __attribute__((aligned(16))) float s_wv[2][kNW][2][16 * kTS];
+    __shared__ __attribute__((aligned(16))) float s_A[2][16 * kTS], s_X[2][16 * kTS],
+        s_T[2][16 * kTS], s_dT[2][16 * kTS], s_dP[2][16 * kTS];
+    __shared__ __attribute__((aligned(16))) float s_gamma[2][DK], s_dgam[2][DK];
+    __shared__ float s_beta[2][kC], s_dbT[2][kC], s_dbA[2][kC];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r = lane & 15, g = lane >> 4;
+    // z: the pair's chunk this half of the workgroup takes; wq, ht: wave and thread in the half
+    const int z = wave / kNW, wq = wave % kNW, ht = tid % (64 * kNW);
     const int H = a.H;
     const int slot = blockIdx.x / H, h = blockIdx.x % H;
-    // sequence n owns slots [cu[n]/16 + n, cu[n+1]/16 + n + 1): the largest n with
-    // cu[n]/16 + n <= slot
+    // sequence n owns pair slots [cu[n]/32 + n, cu[n+1]/32 + n + 1): the largest n with
+    // cu[n]/32 + n <= slot
     int lo = 0, hi = a.N - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (a.cu[mid] / kC + mid <= slot) lo = mid;
+        if (a.cu[mid] / (2 * kC) + mid <= slot) lo = mid;
         else hi = mid - 1;
     }
     const int n = lo;
     const int64_t tbeg = a.cu[n], tend = a.cu[n + 1];
-    const int c = slot - (int)(tbeg / kC) - n;
-    if ((int64_t)kC * c >= tend - tbeg) return;  // a slot past the sequence's last chunk
+    const int jp = slot - (int)(tbeg / (2 * kC)) - n;
+    const int nch = (int)((tend - tbeg + kC - 1) / kC);
+    if (2 * jp >= nch) return;  // a slot past the sequence's last pair
+    const bool has_b = 2 * jp + 1 < nch;
+    const bool live = z == 0 || has_b;  // this half has a chunk
+    const int c = 2 * jp + z;
     const int64_t t0 = tbeg + (int64_t)kC * c;
-    const int Cp = (int)min<int64_t>(kC, tend - t0);
+    const int Cp = live ? (int)min<int64_t>(kC, tend - t0) : 0;
     const int64_t rowq = (int64_t)H * DK, rowv = (int64_t)H * DV, SS = (int64_t)DK * DV;
-    const float* Sin = a.states + ((int64_t)slot * H + h) * SS;
-    const float* dSC = a.dsc + ((int64_t)slot * H + h) * SS;
+    const float* const Sa = a.states + ((int64_t)slot * H + h) * SS;
+    const float* const Dst = a.dsc + ((int64_t)slot * H + h) * SS;
+    // U, dY, dR of the value phases as split bf16 tiles [16][VSB] (hi, lo) in s_big
+    constexpr int VSB = DV + 8;
+    auto vtile = [&](int y, int t, int part) {
+        return reinterpret_cast<bf16*>(&s_big[y][0]) + (2 * t + part) * 16 * VSB;
+    };
+    static_assert(6 * 16 * VSB * 2 <= 4 * kC * WS * 4, "split value tiles fit in s_big");
 
-    // Per-channel decay, row layout: wave w < NPC takes lane (pr, pg) = (row, channel group)
-    // and channels ch0 = pg CW + 8 w + [0, 8), loaded as 16-byte pieces; the cumulative sum
-    // over rows runs across the 16 lanes of a row.  The wave keeps G of its piece for the
-    // last phase.
+    // The stored S (entering chunk 2j) and dS of channel block `wave`, read along rows
+    // (B-fragments of S^T over each value block), for the sums over value columns
+    const int cb = min(wave, KB - 1);
+    f32x4 S2[VB], D2[VB];
+    auto loadB = [&]() {
+#pragma unroll
+        for (int vb = 0; vb < VB; ++vb) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {  // stored transposed: [dv][dk]
+                const int64_t off = (int64_t)(16 * vb + 4 * g + i) * DK + 16 * cb + r;
+                S2[vb][i] = Sa[off];
+                D2[vb][i] = Dst[off];
+            }
+        }
+    };
+
+    // Per-channel decay of this half's chunk, row layout: wave wq < NPC takes lane (pr, pg) =
+    // (row, channel group) and channels ch0 = pg CW + 8 wq + [0, 8), loaded as 16-byte
+    // pieces; the cumulative sum over rows runs across the 16 lanes of a row.  The wave keeps
+    // G of its piece for the last phase.
     constexpr int CW = DK / 4, NPC = CW / 8, NWD = (int)sizeof(T) / 2;
     const int pr = lane & 15, pg = lane >> 4;
-    const int ch0 = pg * CW + 8 * wave;
+    const int ch0 = pg * CW + 8 * wq;
     const bool rin = pr < Cp;
-    float Gp[8];
-    uint32_t livep = 0;
-    if (wave < NPC) {
-        const int64_t off = (t0 + min(pr, Cp - 1)) * rowq + (int64_t)h * DK + ch0;
-        uint4 wq[NWD], wk[NWD], wl[NWD];
+    // Every wave issues its loads unconditionally (a half without a chunk, and waves past
+    // NPC, re-read rows and channels of chunk 2j that they then ignore), in the order the
+    // phases wait for them, so that each wait on the in-order memory counter leaves the later
+    // loads in flight: the decay inputs, beta and the value blocks here, S and dS during the
+    // value phase.
+    const int64_t tld = live ? t0 : tbeg + (int64_t)kC * 2 * jp;
+    const int Cld = live ? Cp : (int)min<int64_t>(kC, tend - tld);
+    uint4 wq4[NWD], wk[NWD], wl[NWD];
+    {
+        const int64_t off = (tld + min(pr, Cld - 1)) * rowq + (int64_t)h * DK + pg * CW +
+                            8 * min(wq, NPC - 1);
 #pragma unroll
         for (int w = 0; w < NWD; ++w) {
-            wq[w] = *reinterpret_cast<const uint4*>(a.q + off + 4 * w);
+            wq4[w] = *reinterpret_cast<const uint4*>(a.q + off + 4 * w);
             wk[w] = *reinterpret_cast<const uint4*>(a.k + off + 4 * w);
             wl[w] = *reinterpret_cast<const uint4*>(a.la + off + 4 * w);
         }
+    }
+    const T bt = a.beta[(tld + min(ht & 15, Cld - 1)) * H + h];
+    // Global operands of one value block of this half's chunk, rows 4g + i, column 16 vb + r:
+    // the walks' R, Y (forwards) and dU (backwards), dO and the gate -- loaded ahead of their
+    // use.  Rows past the end of the sequence re-read its last row and are masked.
+    constexpr int NA = VB / kNW;  // value blocks per wave of a half
+    const float* const ax = a.aux + ((tbeg / kC + n + (tld - tbeg) / kC) * H + h) * kC * DV;
+    f32x4 Rv[NA], Yv[NA], dUv[NA];
+    T rdo[NA][4], rgt[NA][4];
+#pragma unroll
+    for (int ia = 0; ia < NA; ++ia) {
+        const int col = 16 * (wq + kNW * ia) + r;
+        const int64_t o = (int64_t)col * kC + 4 * g;  // stored transposed: [dv][16]
+        Rv[ia] = ld4(ax + o);
+        Yv[ia] = ld4(ax + a.aux_stride + o);
+        dUv[ia] = ld4(ax + 2 * a.aux_stride + o);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t off = (tld + min(4 * g + i, Cld - 1)) * rowv + (int64_t)h * DV + col;
+            rdo[ia][i] = a.dout[off];
+            rgt[ia][i] = a.gate[off];
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    float Gp[8];
+    uint32_t livep = 0;
+    if (live && wq < NPC) {
         float xq[8], xk[8];
-        unpack8<T>(wq, xq);
+        unpack8<T>(wq4, xq);
         unpack8<T>(wk, xk);
         unpack8<T>(wl, Gp);
 #pragma unroll
@@ -714,72 +806,42 @@ __global__ __launch_bounds__(kThreads, 2) void grad_kernel(const GradArgs<T> a) 
             kh[i] = kv * e;
             kc[i] = kv * ei;
         }
-        store8(&s_Qh[pr * RS + ch0], qh);
-        store8(&s_Kh[pr * RS + ch0], kh);
-        store8(&s_Kc[pr * RS + ch0], kc);
-        if (pr == 15) store8(&s_gamma[ch0], gm);
+        store8(&s_Qh[z][pr * RS + ch0], qh);
+        store8(&s_Kh[z][pr * RS + ch0], kh);
+        store8(&s_Kc[z][pr * RS + ch0], kc);
+        if (pr == 15) store8(&s_gamma[z][ch0], gm);
     }
-    if (tid < kC) s_beta[tid] = tid < Cp ? to_f32(a.beta[(t0 + tid) * H + h]) : 0.f;
+    if (live && ht < kC) s_beta[z][ht] = ht < Cp ? to_f32(bt) : 0.f;
     lds_barrier();
-    // Global operands of one value block, rows 4g + i, column 16 vb + r: the walks' R, Y
-    // (forwards) and dU (backwards) of this chunk, dO and the gate -- loaded ahead of
-    // their use.  Rows past the end of the sequence re-read its last row and are masked.
-    constexpr int NA = VB / kNW;  // value blocks per wave
-    const float* const ax = a.aux + ((int64_t)slot * H + h) * kC * DV;
-    f32x4 Rv, Yv, dUv;
-    T rdo[4], rgt[4];
-    auto loadA = [&](int vb) {
-        const int col = 16 * vb + r;
-        const int64_t o = (int64_t)col * kC + 4 * g;  // stored transposed: [dv][16]
-        Rv = ld4(ax + o);
-        Yv = ld4(ax + a.aux_stride + o);
-        dUv = ld4(ax + 2 * a.aux_stride + o);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t off = (t0 + min(4 * g + i, Cp - 1)) * rowv + (int64_t)h * DV + col;
-            rdo[i] = a.dout[off];
-            rgt[i] = a.gate[off];
-        }
-    };
-    loadA(wave);
-    __builtin_amdgcn_sched_barrier(0);  // in flight during the Gram product and T
-    chunk_gram<DK, RS>(s_Kh, s_Kc, s_beta, s_A, s_X, s_T, wave, lane);
+    chunk_gram<DK, RS>(s_Kh[z], s_Kc[z], s_beta[z], s_A[z], s_X[z], s_T[z], live && wq == 0, lane);
 
-    // S and dS_C of one channel block, read along rows (B-fragments of S^T over each value
-    // block), for the sums over value columns
-    f32x4 S2[VB], D2[VB];
-    auto loadB = [&](int cb) {
-#pragma unroll
-        for (int vb = 0; vb < VB; ++vb) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {  // stored transposed: [dv][dk]
-                const int64_t off = (int64_t)(16 * vb + 4 * g + i) * DK + 16 * cb + r;
-                S2[vb][i] = Sin[off];
-                D2[vb][i] = dSC[off];
-            }
-        }
-    };
-
-    // ---- A: value blocks (wave w takes blocks w, w + 4, ...)
-    {
-        const f32x4 Tr = ld4(&s_T[r * kTS + 4 * g]), Tc = ld4_col(s_T, r, g);  // T, T^T
-        float* const sR = s_wv[wave][0];
-        float* const sdU = s_wv[wave][1];
+    // ---- A: value blocks of this half's chunk (wave wq takes blocks wq, wq + 4, ...)
+    if (live) {
+        const f32x4 Tr = ld4(&s_T[z][r * kTS + 4 * g]), Tc = ld4_col(s_T[z], r, g);  // T, T^T
+        bf16 *const Uh = vtile(z, 0, 0), *const Ul = vtile(z, 0, 1);
+        bf16 *const dYh = vtile(z, 1, 0), *const dYl = vtile(z, 1, 1);
+        bf16 *const dRh = vtile(z, 2, 0), *const dRl = vtile(z, 2, 1);
+        auto put = [](bf16* hi, bf16* lo, int idx, float x) {
+            const bf16 xh = (bf16)x;
+            hi[idx] = xh;
+            lo[idx] = (bf16)(x - (float)xh);
+        };
+        float* const sR = s_wv[z][wq][0];
+        float* const sdU = s_wv[z][wq][1];
         f32x4 dTw = zero4(), dPw = zero4();
 #pragma unroll
         for (int ia = 0; ia < NA; ++ia) {
-            const int vb = wave + kNW * ia;
+            const int vb = wq + kNW * ia;
             const int col = 16 * vb + r;
             f32x4 dO, gt;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const bool in = 4 * g + i < Cp;
-                dO[i] = in ? to_f32(rdo[i]) : 0.f;
-                gt[i] = in ? to_f32(rgt[i]) : 0.f;
+                dO[i] = in ? to_f32(rdo[ia][i]) : 0.f;
+                gt[i] = in ? to_f32(rgt[ia][i]) : 0.f;
             }
-            const f32x4 Rt = Rv, Y = Yv, dU = dUv;
-            if (ia + 1 < NA) loadA(vb + kNW);
-            else loadB(wave);
+            const f32x4 Rt = Rv[ia], Y = Yv[ia], dU = dUv[ia];
+            if (ia + 1 == NA) loadB();  // in flight during the rest of this phase
             __builtin_amdgcn_sched_barrier(0);
             const f32x4 U = M::run(Tr, Rt, zero4());
             const f32x4 dR = M::run(Tc, dU, zero4());  // T^T dU
@@ -792,16 +854,17 @@ __global__ __launch_bounds__(kThreads, 2) void grad_kernel(const GradArgs<T> a) 
                     a.dgate[off] = dO[i] * Y[i];
                     a.dv[off] = dR[i];
                 }
-                s_U[row * VS + col] = U[i];
-                s_dY[row * VS + col] = dY[i];
-                s_dR[row * VS + col] = dR[i];
+                put(Uh, Ul, row * VSB + col, U[i]);
+                put(dYh, dYl, row * VSB + col, dY[i]);
+                put(dRh, dRl, row * VSB + col, dR[i]);
                 sR[row * kTS + r] = Rt[i];
                 sdU[row * kTS + r] = dU[i];
             }
             wave_lds_sync();
             // dT += dU R^T and dP += dY U^T over this block's 16 columns
             dTw = M::run(ld4(&sdU[r * kTS + 4 * g]), ld4(&sR[r * kTS + 4 * g]), dTw);
-            dPw = M::run(ld4(&s_dY[r * VS + 16 * vb + 4 * g]), ld4(&s_U[r * VS + 16 * vb + 4 * g]), dPw);
+            const int fo = r * VSB + 16 * vb + 4 * g;
+            dPw = mma3(lds_split(&dYh[fo], &dYl[fo]), lds_split(&Uh[fo], &Ul[fo]), dPw);
             wave_lds_sync();
         }
 #pragma unroll
@@ -809,119 +872,180 @@ __global__ __launch_bounds__(kThreads, 2) void grad_kernel(const GradArgs<T> a) 
             sR[(4 * g + i) * kTS + r] = dTw[i];
             sdU[(4 * g + i) * kTS + r] = dPw[i];
         }
+    } else {
+        loadB();
     }
     lds_barrier();
-    {  // dT, dP: sums of the wave parts (one element per thread)
-        const int i = tid >> 4, j = tid & 15;
+    if (live) {  // dT, dP: sums of the wave parts (one element per thread of the half)
+        const int i = ht >> 4, j = ht & 15;
         float t = 0.f, p = 0.f;
 #pragma unroll
         for (int w = 0; w < kNW; ++w) {
-            t += s_wv[w][0][i * kTS + j];
-            p += s_wv[w][1][i * kTS + j];
+            t += s_wv[z][w][0][i * kTS + j];
+            p += s_wv[z][w][1][i * kTS + j];
         }
-        s_dT[i * kTS + j] = t;
-        s_dP[i * kTS + j] = j <= i ? p : 0.f;
+        s_dT[z][i * kTS + j] = t;
+        s_dP[z][i * kTS + j] = j <= i ? p : 0.f;
     }
 
-    // ---- B: channel blocks (wave w takes blocks w, w + 4, ...): the sums over value columns
-    f32x4 aQ[OWNC], aK[OWNC], aB[OWNC];
+    // ---- B: the sums over value columns, channel block `wave`, both chunks.  Chunk 2j uses
+    // the stored S and the re-formed dS leaving it; chunk 2j + 1 the re-formed S entering it
+    // and the stored dS.  Products are split-bf16 (as in the walks), two value blocks per
+    // 32-deep MFMA; the re-formed blocks are fp32 accumulators seeded with the decayed
+    // stored ones, and the sums for dgamma take the fp32 values.
+    f32x4 aQ[2], aK[2], aB[2];
 #pragma unroll
-    for (int jc = 0; jc < OWNC; ++jc) {
-        const int cb = wave + kNW * jc;
-        aQ[jc] = aK[jc] = aB[jc] = zero4();
-        if (cb >= KB) continue;
-        float dg = 0.f;
+    for (int y = 0; y < 2; ++y) aQ[y] = aK[y] = aB[y] = zero4();
+    if (wave < KB) {
+        const int kc0 = 16 * cb;
+        const float gA = s_gamma[0][kc0 + r], gB = has_b ? s_gamma[1][kc0 + r] : 0.f;
+        f32x4 KbA, QhB, nKhB;  // B-fragments over the chunk's rows: X[4g + i][kc0 + r]
 #pragma unroll
-        for (int vb = 0; vb < VB; ++vb) {
-            aQ[jc] = M::run(ld4(&s_dY[r * VS + 16 * vb + 4 * g]), S2[vb], aQ[jc]);
-            aK[jc] = M::run(ld4(&s_dR[r * VS + 16 * vb + 4 * g]), S2[vb], aK[jc]);
-            aB[jc] = M::run(ld4(&s_U[r * VS + 16 * vb + 4 * g]), D2[vb], aB[jc]);
-            dg += D2[vb][0] * S2[vb][0] + D2[vb][1] * S2[vb][1] + D2[vb][2] * S2[vb][2] +
-                  D2[vb][3] * S2[vb][3];
+        for (int i = 0; i < 4; ++i) {
+            const int idx = (4 * g + i) * RS + kc0 + r;
+            KbA[i] = s_Kc[0][idx] * gA;  // Kb = Kc Diag(gamma)
+            QhB[i] = s_Qh[1][idx];
+            nKhB[i] = -s_Kh[1][idx];
         }
-        if (jc + 1 < OWNC && cb + kNW < KB) loadB(cb + kNW);
-        dg += __shfl_xor(dg, 16);
-        dg += __shfl_xor(dg, 32);
-        if (g == 0) s_dgam[16 * cb + r] = dg;
+        const Split4 KbAs = split4(KbA), QhBs = split4(QhB), nKhBs = split4(nKhB);
+        // transposed reads of the value tiles (A-fragments of their transposes, see lds_tr)
+        const int ftv = (4 * g + (r >> 2)) * VSB + 4 * (r & 3);
+        float dgA = 0.f, dgB = 0.f;
+#pragma unroll
+        for (int vb = 0; vb < VB; vb += 2) {
+            const int vo0 = 16 * vb, vo1 = vo0 + 16;
+            const int fo0 = r * VSB + vo0 + 4 * g, fo1 = fo0 + 16;  // row fragments
+            f32x4 Da[2] = {D2[vb], D2[vb + 1]};  // dS leaving chunk 2j
+            f32x4 Sb[2];                         // S entering chunk 2j + 1
+            if (has_b) {
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int vo = vo0 + 16 * u;
+                    Sb[u] = mma3(lds_split_tr(vtile(0, 0, 0) + ftv + vo, vtile(0, 0, 1) + ftv + vo), KbAs,
+                                 S2[vb + u] * gA);
+                    Da[u] = mma3x2(lds_split_tr(vtile(1, 1, 0) + ftv + vo, vtile(1, 1, 1) + ftv + vo),
+                                   lds_split_tr(vtile(1, 2, 0) + ftv + vo, vtile(1, 2, 1) + ftv + vo),
+                                   QhBs, nKhBs, D2[vb + u] * gB);
+                }
+                const Split4 Sb0 = split4(Sb[0]), Sb1 = split4(Sb[1]);
+                aQ[1] = mma3x2(lds_split(vtile(1, 1, 0) + fo0, vtile(1, 1, 1) + fo0),
+                               lds_split(vtile(1, 1, 0) + fo1, vtile(1, 1, 1) + fo1), Sb0, Sb1, aQ[1]);
+                aK[1] = mma3x2(lds_split(vtile(1, 2, 0) + fo0, vtile(1, 2, 1) + fo0),
+                               lds_split(vtile(1, 2, 0) + fo1, vtile(1, 2, 1) + fo1), Sb0, Sb1, aK[1]);
+                aB[1] = mma3x2(lds_split(vtile(1, 0, 0) + fo0, vtile(1, 0, 1) + fo0),
+                               lds_split(vtile(1, 0, 0) + fo1, vtile(1, 0, 1) + fo1),
+                               split4(D2[vb]), split4(D2[vb + 1]), aB[1]);
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) dgB += D2[vb + u][i] * Sb[u][i];
+            }
+            const Split4 Sa0 = split4(S2[vb]), Sa1 = split4(S2[vb + 1]);
+            aQ[0] = mma3x2(lds_split(vtile(0, 1, 0) + fo0, vtile(0, 1, 1) + fo0),
+                           lds_split(vtile(0, 1, 0) + fo1, vtile(0, 1, 1) + fo1), Sa0, Sa1, aQ[0]);
+            aK[0] = mma3x2(lds_split(vtile(0, 2, 0) + fo0, vtile(0, 2, 1) + fo0),
+                           lds_split(vtile(0, 2, 0) + fo1, vtile(0, 2, 1) + fo1), Sa0, Sa1, aK[0]);
+            aB[0] = mma3x2(lds_split(vtile(0, 0, 0) + fo0, vtile(0, 0, 1) + fo0),
+                           lds_split(vtile(0, 0, 0) + fo1, vtile(0, 0, 1) + fo1),
+                           split4(Da[0]), split4(Da[1]), aB[0]);
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dgA += Da[u][i] * S2[vb + u][i];
+        }
+        dgA += __shfl_xor(dgA, 16);
+        dgA += __shfl_xor(dgA, 32);
+        dgB += __shfl_xor(dgB, 16);
+        dgB += __shfl_xor(dgB, 32);
+        if (g == 0) {
+            s_dgam[0][kc0 + r] = dgA;
+            s_dgam[1][kc0 + r] = dgB;
+        }
     }
     lds_barrier();
 
-    // ---- C: the 16x16 algebra (one element per thread: row i, column j)
-    {
-        const int i = tid >> 4, j = tid & 15;
+    // ---- C: the 16x16 algebra of this half's chunk (one element per thread: row i, column j)
+    float* const s_M = &s_wv[z][0][0][0];   // X^T dT Diag(beta), once the wave parts are summed
+    float* const s_dA = &s_wv[z][1][0][0];  // Diag(beta) dA
+    if (live) {
+        const int i = ht >> 4, j = ht & 15;
         float m = 0.f;  // (X^T dT)[i][j] beta_j = (X^T dX)[i][j]
 #pragma unroll
-        for (int kk = 0; kk < kC; ++kk) m += s_X[kk * kTS + i] * s_dT[kk * kTS + j];
-        s_M[i * kTS + j] = m * s_beta[j];
-        if (tid < kC) {  // column sums of X * dT
+        for (int kk = 0; kk < kC; ++kk) m += s_X[z][kk * kTS + i] * s_dT[z][kk * kTS + j];
+        s_M[i * kTS + j] = m * s_beta[z][j];
+        if (ht < kC) {  // column sums of X * dT
             float s = 0.f;
 #pragma unroll
-            for (int kk = 0; kk < kC; ++kk) s += s_X[kk * kTS + tid] * s_dT[kk * kTS + tid];
-            s_dbT[tid] = s;
+            for (int kk = 0; kk < kC; ++kk) s += s_X[z][kk * kTS + ht] * s_dT[z][kk * kTS + ht];
+            s_dbT[z][ht] = s;
         }
     }
     lds_barrier();
-    {
-        const int i = tid >> 4, j = tid & 15;
+    if (live) {
+        const int i = ht >> 4, j = ht & 15;
         float d = 0.f;  // dA[i][j] = -(M X^T)[i][j] on the strict lower triangle
 #pragma unroll
-        for (int kk = 0; kk < kC; ++kk) d -= s_M[i * kTS + kk] * s_X[j * kTS + kk];
+        for (int kk = 0; kk < kC; ++kk) d -= s_M[i * kTS + kk] * s_X[z][j * kTS + kk];
         d = j < i ? d : 0.f;
-        s_dA[i * kTS + j] = s_beta[i] * d;
-        float e = d * s_A[i * kTS + j];
+        s_dA[i * kTS + j] = s_beta[z][i] * d;
+        float e = d * s_A[z][i * kTS + j];
         e += __shfl_xor(e, 8);
         e += __shfl_xor(e, 4);
         e += __shfl_xor(e, 2);
         e += __shfl_xor(e, 1);
-        if (j == 0) s_dbA[i] = e;
+        if (j == 0) s_dbA[z][i] = e;
     }
     lds_barrier();
 
-    // ---- D: the chunk-local terms, then the four operand gradients into LDS (the
-    // value-phase tiles are dead: every wave has passed two barriers since reading them)
-    {
-        const f32x4 dPr = ld4(&s_dP[r * kTS + 4 * g]), dPc = ld4_col(s_dP, r, g);
-        const f32x4 dAr = ld4(&s_dA[r * kTS + 4 * g]), dAc = ld4_col(s_dA, r, g);
+    // ---- D: the chunk-local terms, then the four operand gradients into LDS, channel block
+    // `wave` of both chunks (the value-phase tiles are dead: every wave has passed two
+    // barriers since reading them)
+    if (wave < KB) {
+        const int kc0 = 16 * cb;
 #pragma unroll
-        for (int jc = 0; jc < OWNC; ++jc) {
-            const int cb = wave + kNW * jc;
-            if (cb >= KB) continue;
-            f32x4 KcB, QhB, KhB;  // B-fragments: X[4g + i][16cb + r]
+        for (int y = 0; y < 2; ++y) {
+            if (y == 1 && !has_b) break;
+            const float* const sdA_y = &s_wv[y][1][0][0];  // Diag(beta) dA of chunk y
+            const f32x4 dPr = ld4(&s_dP[y][r * kTS + 4 * g]), dPc = ld4_col(s_dP[y], r, g);
+            const f32x4 dAr = ld4(&sdA_y[r * kTS + 4 * g]), dAc = ld4_col(sdA_y, r, g);
+            f32x4 KcB, QhB, KhB;  // B-fragments: X[4g + i][kc0 + r]
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                KcB[i] = s_Kc[(4 * g + i) * RS + 16 * cb + r];
-                QhB[i] = s_Qh[(4 * g + i) * RS + 16 * cb + r];
-                KhB[i] = s_Kh[(4 * g + i) * RS + 16 * cb + r];
+                const int idx = (4 * g + i) * RS + kc0 + r;
+                KcB[i] = s_Kc[y][idx];
+                QhB[i] = s_Qh[y][idx];
+                KhB[i] = s_Kh[y][idx];
             }
-            const f32x4 dQh = M::run(dPr, KcB, aQ[jc]);
-            const f32x4 dKh = M::run(dAr, KcB, -aK[jc]);
+            const f32x4 dQh = M::run(dPr, KcB, aQ[y]);
+            const f32x4 dKh = M::run(dAr, KcB, -aK[y]);
             const f32x4 dKc = M::run(dAc, KhB, M::run(dPc, QhB, zero4()));
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int idx = (4 * g + i) * RS + 16 * cb + r;
-                s_big[idx] = dQh[i];
-                s_big[kC * WS + idx] = dKh[i];
-                s_big[2 * kC * WS + idx] = dKc[i];
-                s_big[3 * kC * WS + idx] = aB[jc][i];
+                const int idx = (4 * g + i) * RS + kc0 + r;
+                s_big[y][idx] = dQh[i];
+                s_big[y][kC * WS + idx] = dKh[i];
+                s_big[y][2 * kC * WS + idx] = dKc[i];
+                s_big[y][3 * kC * WS + idx] = aB[y][i];
             }
         }
     }
     lds_barrier();
 
-    // ---- E: dq, dk, and dlambda by the reverse cumulative sum of dG over the rows, in the
-    // decay's row layout (the 16 lanes of a row hold the chunk's rows of 8 channels)
-    if (wave < NPC) {
+    // ---- E: dq, dk, and dlambda of this half's chunk by the reverse cumulative sum of dG over
+    // the rows, in the decay's row layout (the 16 lanes of a row hold the chunk's rows of 8
+    // channels)
+    if (live && wq < NPC) {
         const int idx = pr * RS + ch0;
         float qh[8], kh[8], kc[8], dqh[8], dkh[8], dkc[8], dkb[8], gm[8], dgm[8];
-        load8(&s_Qh[idx], qh);
-        load8(&s_Kh[idx], kh);
-        load8(&s_Kc[idx], kc);
-        load8(&s_big[idx], dqh);
-        load8(&s_big[kC * WS + idx], dkh);
-        load8(&s_big[2 * kC * WS + idx], dkc);
-        load8(&s_big[3 * kC * WS + idx], dkb);
-        load8(&s_gamma[ch0], gm);
-        load8(&s_dgam[ch0], dgm);
+        load8(&s_Qh[z][idx], qh);
+        load8(&s_Kh[z][idx], kh);
+        load8(&s_Kc[z][idx], kc);
+        load8(&s_big[z][idx], dqh);
+        load8(&s_big[z][kC * WS + idx], dkh);
+        load8(&s_big[z][2 * kC * WS + idx], dkc);
+        load8(&s_big[z][3 * kC * WS + idx], dkb);
+        load8(&s_gamma[z][ch0], gm);
+        load8(&s_dgam[z][ch0], dgm);
         float dq8[8], dk8[8], dl8[8], kbs[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -954,7 +1078,7 @@ __global__ __launch_bounds__(kThreads, 2) void grad_kernel(const GradArgs<T> a) 
             store8(a.dla + off, dl8);
         }
     }
-    if (tid < Cp) a.dbeta[(t0 + tid) * H + h] = s_dbT[tid] + s_dbA[tid];
+    if (live && ht < Cp) a.dbeta[(t0 + ht) * H + h] = s_dbT[z][ht] + s_dbA[z][ht];
 }
 
 template <typename T, int DK, int DV, int NCB, int ND>
@@ -965,7 +1089,7 @@ hipError_t launch_walk(const BackwardArgs& p, hipStream_t st) {
     a.cu = p.cu_seqlens; a.S0 = p.initial_state; a.dSf = p.d_final_state;
     a.dS0 = p.d_initial_state; a.states = p.workspace; a.dsc = p.workspace + p.grad_offset;
     a.aux = p.workspace + 2 * p.grad_offset;
-    a.aux_stride = (p.grad_offset / ((int64_t)DK * DV)) * kC * DV;
+    a.aux_stride = p.aux_stride;
     a.H = p.H; a.n_slices = DV / (16 * NCB); a.floor_ = p.floor_; a.scale = p.scale;
     a.pairs = p.num_seqs * p.H;
     a.half = (a.pairs + 7) / 8 * 8 * a.n_slices;
@@ -987,11 +1111,11 @@ hipError_t launch_typed(const BackwardArgs& p, hipStream_t st) {
     a.beta = (const T*)p.beta; a.gate = (const T*)p.gate; a.dout = (const T*)p.d_out;
     a.cu = p.cu_seqlens; a.states = p.workspace; a.dsc = p.workspace + p.grad_offset;
     a.aux = p.workspace + 2 * p.grad_offset;
-    a.aux_stride = (p.grad_offset / ((int64_t)DK * DV)) * kC * DV;
+    a.aux_stride = p.aux_stride;
     a.dq = p.dq; a.dk = p.dk_; a.dv = p.dv_; a.dla = p.dlog_alpha; a.dbeta = p.dbeta;
     a.dgate = p.dgate; a.H = p.H; a.N = p.num_seqs; a.floor_ = p.floor_; a.scale = p.scale;
-    const int64_t slots = p.T_total / kC + p.num_seqs;
-    hipLaunchKernelGGL((grad_kernel<T, DK, DV>), dim3((unsigned)(slots * p.H)), dim3(kThreads), 0,
+    const int64_t slots = p.T_total / (2 * kC) + p.num_seqs;  // pair slots
+    hipLaunchKernelGGL((grad_kernel<T, DK, DV>), dim3((unsigned)(slots * p.H)), dim3(64 * kGW), 0,
                        st, a);
     return hipGetLastError();
 }

@@ -92,8 +92,9 @@ struct BackwardArgs {
     const float* d_final_state;         // may be null
     float *dq, *dk_, *dv_, *dlog_alpha, *dbeta, *dgate;
     float* d_initial_state;             // may be null
-    float* workspace;                   // chunk-entering states, then chunk-leaving gradients
-    int64_t grad_offset;                // floats: start of the chunk-leaving gradients
+    float* workspace;                   // pair states, pair gradients, then per-chunk R, Y, dU
+    int64_t grad_offset;                // floats: start of the pair gradients (= pair states' size)
+    int64_t aux_stride;                 // floats between the R, Y and dU arrays
     int64_t T_total;
 };
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream);

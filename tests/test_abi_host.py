@@ -270,14 +270,16 @@ def test_segmented_rejects(kw, msg):
 
 
 def test_backward_workspace_size():
-    """cu = (0, 40, 40, 100), H = 2, d = 64: the state entering every chunk at slot
-    cu[n]/16 + n + c (at most 100 // 16 + 3 = 9 slots per head), then the gradient leaving
-    every chunk at the same slots, then three [16][dv] vectors per slot and head."""
+    """cu = (0, 40, 40, 100), H = 2, d = 64: the state entering each even chunk 2j at pair
+    slot cu[n]/32 + n + j (at most 100 // 32 + 3 = 6 slots per head; the sequences of 3, 0
+    and 4 chunks take slots {0, 1} and {3, 4}), then the gradient leaving each odd chunk (or
+    the last) at the same slots, then three [16][dv] vectors per chunk slot cu[n]/16 + n + c
+    (100 // 16 + 3 = 9) and head."""
     lib = _lib.load()
     p = _lib.params(_lib.KDA_DTYPE_BF16, 2, 64, 64)
     ss = 64 * 64 * 4
     assert lib.kda_prefill_backward_workspace(ctypes.byref(p), cu(0, 40, 40, 100), 3) == \
-        2 * 9 * 2 * ss + 3 * 9 * 2 * 16 * 64 * 4
+        2 * 6 * 2 * ss + 3 * 9 * 2 * 16 * 64 * 4
     assert lib.kda_prefill_backward_workspace(ctypes.byref(p), cu(0, 40, 30), 2) == -1
 
 

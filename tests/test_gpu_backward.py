@@ -80,6 +80,21 @@ def test_backward_varlen(dtype, dk, dv):
     run_case(x, do, dSf, floor=-0.4, scale=0.8)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_chunk_pairs(dtype):
+    """Sequences of 7, 3, 4, 2, 0 and 3 chunks: pairs of chunks with and without a second
+    chunk, ragged last chunks, and pairs whose state and gradient are both re-formed from the
+    stored ones (the gradient kernel takes two chunks per workgroup)."""
+    lengths = (100, 33, 64, 17, 0, 48)
+    log(f"backward chunk pairs dtype={dtype} lengths={lengths}")
+    x = ki.make_prefill_inputs(lengths, 3, 128, 128, dtype, 0.3, seed=71, device="cuda",
+                               log_alpha_min=-0.6)
+    g = torch.Generator().manual_seed(71)
+    do = (torch.randn(x.v.shape, generator=g) * 0.5).to(x.v.dtype).cuda()
+    dSf = (torch.randn(x.initial_state.shape, generator=g) * 0.1).cuda()
+    run_case(x, do, dSf, floor=-0.4, scale=0.9)
+
+
 def test_backward_no_initial_state_no_state_gradient():
     x = ki.make_prefill_inputs((70, 33), 2, 64, 64, "bf16", 0.0, seed=9, device="cuda")
     assert x.initial_state is None
