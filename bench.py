@@ -294,10 +294,11 @@ def main() -> int:
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--spec-rounds", type=int, default=50)
     ap.add_argument("--spec-draft", type=int, default=4)
-    ap.add_argument("--backward-steps", type=int, default=3)
+    ap.add_argument("--backward-steps", type=int, default=10)
     ap.add_argument("--segmented", action=argparse.BooleanOptionalAction, default=True,
                     help="also time the segmented prefill on the few-head long workload")
-    ap.add_argument("--segment-len", type=int, default=16384)
+    ap.add_argument("--segment-len", type=int, default=0,
+                    help="segment length of the timed segmented prefill (0: the library's plan)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-pairs-per-class", type=int, default=16)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -482,16 +483,17 @@ def main() -> int:
                               cu_seqlens=bx.cu_seqlens, cu_seqlens_host=bx.cu_seqlens_host,
                               initial_state=bx.initial_state, out=fout)
 
-        bt, _ = time_launches(bstep, args.backward_steps, 2, 0.0, flush)
-        ft, _ = time_launches(fstep, args.backward_steps, 2, 0.0, flush)
-        bms, fms = float(np.mean(bt)), float(np.mean(ft))
+        bt, _ = time_launches(bstep, args.backward_steps, 3, 0.5, flush)
+        ft, _ = time_launches(fstep, args.backward_steps, 3, 0.5, flush)
+        bms, fms = float(np.median(bt)), float(np.median(ft))
         result["backward"] = {
             "workload": bw.name, "steps": args.backward_steps, "ms_per_step": bms,
             "tokens_per_s": bx.total_tokens / (bms * 1e-3), "forward_ms": fms,
             "vs_forward": bms / fms,
             "note": "chunk form, fp32 state and sums: forward and reverse chunk walks in one "
-                    "launch (split-bf16 products), then all chunks in parallel (fp32 MFMA); "
-                    "each launch after the same cache flush as the forward",
+                    "launch storing every other state and gradient, then all pairs of chunks "
+                    "in parallel (split-bf16 and fp32 MFMA); medians of launches each after "
+                    "the same cache flush as the forward's",
         }
         del bws, dout, bx, fout
         torch.cuda.empty_cache()
@@ -500,15 +502,20 @@ def main() -> int:
     if args.segmented:
         sw = ki.WORKLOADS["prefill_b1_h4_t524288"]
         sxx = ki.make_workload_inputs(sw, seed=2, device="cuda")
-        L = args.segment_len
+        import ctypes
+        from linear_attention_sequence_chunked_amd import _lib as klib
+        sp = klib.params(klib.KDA_DTYPE_BF16, sw.H, sw.dk, sw.dv)
+        scu = (ctypes.c_int32 * len(sxx.cu_seqlens_host))(*sxx.cu_seqlens_host)
+        plan = kda.load_library().kda_prefill_segment_plan(ctypes.byref(sp), scu, len(sw.lengths))
+        L = args.segment_len if args.segment_len else plan
         sout = torch.empty_like(sxx.v)
         sSf = torch.empty((1, sw.H, sw.dk, sw.dv), dtype=torch.float32, device="cuda")
         ws = torch.empty(1 << 28, dtype=torch.uint8, device="cuda")
 
-        def plain_run():
+        def plain_run():  # the plain schedule, forced
             kda.chunk_prefill(sxx.q, sxx.k, sxx.v, sxx.log_alpha, sxx.beta, sxx.gate,
                               cu_seqlens=sxx.cu_seqlens, cu_seqlens_host=sxx.cu_seqlens_host,
-                              out=sout, final_state=sSf)
+                              out=sout, final_state=sSf, segment_len=0)
 
         def seg_run():
             kda.chunk_prefill_segmented(sxx.q, sxx.k, sxx.v, sxx.log_alpha, sxx.beta, sxx.gate,
@@ -520,7 +527,8 @@ def main() -> int:
         pms, sms = float(np.median(pt)), float(np.median(st))
         ttok = sum(sw.lengths)
         result["segmented"] = {
-            "workload": sw.name, "segment_len": L, "plain_ms": pms, "segmented_ms": sms,
+            "workload": sw.name, "segment_len": L, "planned_segment_len": plan,
+            "plain_ms": pms, "segmented_ms": sms,
             "speedup": pms / sms, "segmented_tokens_per_s": ttok / (sms * 1e-3),
         }
         del sxx, sout, ws
