@@ -182,8 +182,10 @@ def time_launches(fn, steps: int, warmup: int, min_warmup_s: float, flush: Flush
     return [s.elapsed_time(e) for s, e in zip(starts, ends)], wall
 
 
-def prefill_record(w, x, times_ms, wall):
-    """Throughput, roofline fractions and the stored counter summaries of one workload."""
+def prefill_record(w, x, times_ms, wall, segment_len=0):
+    """Throughput, roofline fractions and the stored counter summaries of one workload
+    (segment_len > 0: the library's plan cut the sequences into segments of that many tokens,
+    and a step is the segmented schedule's three launches)."""
     import numpy as np
     es = 2 if w.dtype == "bf16" else 4
     ms = float(np.mean(times_ms))
@@ -200,6 +202,9 @@ def prefill_record(w, x, times_ms, wall):
                      "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
                      "kernel": "prefill_bf16_kernel" if w.dtype == "bf16" else "prefill_kernel",
                      "algorithmic_bytes_per_launch": alg_bytes},
+        "schedule": ("plain" if segment_len <= 0 else
+                     f"segmented, {segment_len}-token segments (the library's plan): a state and "
+                     f"transition pass, the combine, and the output pass, timed together"),
         "mfma": {"achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                  "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "algorithmic_flops_per_launch": alg_flops},
     }
@@ -235,8 +240,13 @@ def run_prefill_workload(name, args, flush, seed=1):
                           cu_seqlens_host=x.cu_seqlens_host, initial_state=x.initial_state,
                           out=out, final_state=Sf)
 
+    import ctypes
+    from linear_attention_sequence_chunked_amd import _lib as klib
+    p = klib.params(klib.KDA_DTYPE_BF16 if w.dtype == "bf16" else klib.KDA_DTYPE_F32, w.H, w.dk, w.dv)
+    cu_h = (ctypes.c_int32 * len(x.cu_seqlens_host))(*x.cu_seqlens_host)
+    plan = kda.load_library().kda_prefill_segment_plan(ctypes.byref(p), cu_h, len(w.lengths))
     times, wall = time_launches(step, args.steps, args.warmup, args.min_warmup_s, flush)
-    return w, x, prefill_record(w, x, times, wall)
+    return w, x, prefill_record(w, x, times, wall, segment_len=plan)
 
 
 def cpu_baseline(w, x, per_class: int, repeat_s: float):
@@ -308,6 +318,8 @@ def main() -> int:
     ap.add_argument("--summarize", choices=("traffic", "mfma", "trace"))
     ap.add_argument("--pmc-dirs", nargs="*", default=[])
     ap.add_argument("--kernel", default="prefill_bf16_kernel")
+    ap.add_argument("--per-step", action="store_true",
+                    help="sum the matching dispatches between two cache flushes (one step)")
     ap.add_argument("--command", action="append", default=[])
     ap.add_argument("--out")
     args = ap.parse_args()
@@ -561,6 +573,41 @@ def _read_counters(dirs, kernel_substr):
     return out, [dur[k] for k in order], [names[k] for k in order]
 
 
+def _read_steps(dirs, kernel_substr):
+    """Like _read_counters, but per step: the dispatches whose kernel name contains
+    kernel_substr, grouped into runs that other kernels (the cache flush before every timed
+    launch) separate, each run summed -- one entry per step, however many kernels a step
+    launches (the segmented schedule launches three)."""
+    rows = {}
+    for d in dirs:
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    did = int(r["Dispatch_Id"])
+                    e = rows.setdefault(did, {"name": r["Kernel_Name"], "c": {},
+                                              "dur": (int(r["End_Timestamp"]) -
+                                                      int(r["Start_Timestamp"])) / 1e3})
+                    e["c"][r["Counter_Name"]] = float(r["Counter_Value"])
+    steps, cur = [], None
+    for did in sorted(rows):
+        e = rows[did]
+        if kernel_substr not in e["name"]:
+            cur = None
+            continue
+        if cur is None:
+            cur = {"c": {}, "dur": 0.0, "names": []}
+            steps.append(cur)
+        for k, v in e["c"].items():
+            cur["c"][k] = cur["c"].get(k, 0.0) + v
+        cur["dur"] += e["dur"]
+        cur["names"].append(e["name"])
+    out = {}
+    for st in steps:
+        for k, v in st["c"].items():
+            out.setdefault(k, []).append(v)
+    return out, [st["dur"] for st in steps], [" + ".join(st["names"]) for st in steps]
+
+
 def summarize(args) -> int:
     """traffic: --pmc-dirs FETCH WRITE COPYFETCH COPYWRITE (rocprofv3 --pmc FETCH_SIZE /
     WRITE_SIZE runs of `bench.py --steps S` and of `bench.py --copy-calibration`): HBM
@@ -578,8 +625,9 @@ def summarize(args) -> int:
         res["kernel_source_sha256"] = (decode_source_hash() if "decode" in args.kernel
                                        else prefill_source_hash())
     if args.summarize == "traffic":
-        fetch, fdur, names = _read_counters([args.pmc_dirs[0]], args.kernel)
-        write, _, _ = _read_counters([args.pmc_dirs[1]], args.kernel)
+        rd = _read_steps if args.per_step else _read_counters
+        fetch, fdur, names = rd([args.pmc_dirs[0]], args.kernel)
+        write, _, _ = rd([args.pmc_dirs[1]], args.kernel)
         cf, _, _ = _read_counters([args.pmc_dirs[2]], "copyBuffer")
         cw, _, _ = _read_counters([args.pmc_dirs[3]], "copyBuffer")
         if not cf:  # torch's copy kernel, if the runtime did not use its blit
@@ -609,7 +657,7 @@ def summarize(args) -> int:
                        "(KiB, mean over the last launches, each after the 1 GiB cache flush); the "
                        "factors make the counters read exactly 1 GiB for a plain 1 GiB copy.")
     elif args.summarize == "mfma":
-        c, dur, names = _read_counters(args.pmc_dirs, args.kernel)
+        c, dur, names = (_read_steps if args.per_step else _read_counters)(args.pmc_dirs, args.kernel)
         mops = float(np.mean(c["SQ_INSTS_VALU_MFMA_MOPS_BF16"][-steps:]))
         busy = float(np.mean(c["SQ_VALU_MFMA_BUSY_CYCLES"][-steps:]))
         act = float(np.mean(c["GRBM_GUI_ACTIVE"][-steps:]))

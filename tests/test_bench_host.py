@@ -86,3 +86,21 @@ def test_headline_workload_is_the_packed_varlen_batch():
     b, f = bench.prefill_algorithmic(w.lengths, w.H, w.dk, w.dv, 2, True)
     assert b == 3_768_320 * 32 * 1538 + 64 * 32 * 2 * 128 * 128 * 4
     assert f == 3_768_320 * 32 * 118_784
+
+
+def test_counter_steps_sum_the_kernels_between_flushes(tmp_path):
+    """The counter summaries take one entry per timed step: the library's dispatches between
+    two cache flushes (other kernels) are summed, however many kernels a step launches."""
+    import csv
+    names = ["flush", "kda::a", "kda::b", "flush", "kda::a", "kda::c", "kda::b", "flush", "kda::a"]
+    with open(tmp_path / "x_counter_collection.csv", "w") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name",
+                                          "Counter_Value", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for i, n in enumerate(names):
+            w.writerow({"Dispatch_Id": i, "Kernel_Name": n, "Counter_Name": "FETCH_SIZE",
+                        "Counter_Value": i + 1, "Start_Timestamp": 0, "End_Timestamp": 1000})
+    out, dur, nm = bench._read_steps([str(tmp_path)], "kda::")
+    assert out == {"FETCH_SIZE": [2 + 3, 5 + 6 + 7, 9]}
+    assert dur == [2.0, 3.0, 1.0]
+    assert nm == ["kda::a + kda::b", "kda::a + kda::c + kda::b", "kda::a"]
