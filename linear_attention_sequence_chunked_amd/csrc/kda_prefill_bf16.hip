@@ -27,8 +27,9 @@
 // entries below one in size, and T only enters through bf16 operands anyway).
 //
 // Workgroup = one (sequence, head, slice of NV = 16*NCB value columns).  Waves:
-//   chain  (NCB/2) : two 16-column blocks of S each (one when NCB = 1), so every operand
-//                    read from LDS serves 32 columns; state step of chunk c
+//   chain  (NCB/CPW): CPW 16-column blocks of S each -- two in the full-width workgroup
+//                    (NCB = 8), so every operand read from LDS serves 32 columns, one
+//                    otherwise (the shortest state step); state step of chunk c
 //   decay  (DK/32) : 32 key channels each; row tiles of chunk c+3 from registers
 //                    loaded PF chunks earlier
 //   gram           : A, A^T of chunk c+2 and T through the nilpotent product
