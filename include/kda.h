@@ -229,12 +229,16 @@ int32_t kda_prefill_segment_plan(const kda_params* params, const int32_t* cu_seq
  *   dq, dk, dlog_alpha : fp32 [T_total, H, dk];  dv, dgate : fp32 [T_total, H, dv];
  *   dbeta           : fp32 [T_total, H];  d_initial_state : fp32 [num_seqs, H, dk, dv]
  *                     or NULL.  No output may overlap another argument.
- *   workspace       : device memory of at least kda_prefill_backward_workspace(...) bytes,
- *                     256-byte aligned, overlapping no other argument; receives, per pair
- *                     of 16-token chunks and head, the state entering the first and the
- *                     gradient of the state leaving the second (fp32, dk x dv each), and
- *                     three 16 x dv fp32 blocks per chunk and head passed from the walks to
- *                     the gradients.
+ *   workspace       : device memory, 256-byte aligned, overlapping no other argument, of
+ *                     workspace_bytes; receives, per pair of 16-token chunks and head, the
+ *                     state entering the first and the gradient of the state leaving the
+ *                     second (fp32, dk x dv each), and three 16 x dv fp32 blocks per chunk and
+ *                     head passed from the walks to the gradients.  With
+ *                     kda_prefill_backward_workspace(...) bytes the batch runs at once; with
+ *                     less, the call runs groups of consecutive sequences one after another
+ *                     on the stream, each as large as the workspace allows, and fails
+ *                     (KDA_ERR_INVALID_ARGUMENT) only if a single sequence needs more
+ *                     (kda_prefill_backward_workspace over that sequence alone).
  * The gradients are computed in fp32 with the 16-token chunk algebra of the forward: one
  * launch walks every sequence forwards (the states) and backwards (the state gradient) side
  * by side, a second forms the input gradients of each pair of chunks from those, all pairs

@@ -619,6 +619,19 @@ int32_t kda_prefill_segment_plan(const kda_params* params, const int32_t* cu_seq
 
 namespace {
 
+// Workspace of the backward over sequences [n0, n1): the state entering chunk 2j of sequence
+// n at pair slot (cu[n] - cu[n0])/32 + (n - n0) + j (at most (cu[n1] - cu[n0])/32 + n1 - n0
+// slots), then the gradient leaving chunk 2j + 1 (2j if it is the last) at the same slot, then
+// three [16][dv] arrays per chunk slot (cu[n] - cu[n0])/16 + (n - n0) + c (R, Y, dU).
+void bwd_group_size(const kda_params* params, const int32_t* cu, int32_t n0, int32_t n1,
+                    uint64_t& bytes, uint64_t& grad_off, uint64_t& aux_stride) {
+    const uint64_t H = params->num_heads, ss = (uint64_t)params->dk * params->dv;
+    const uint64_t T = (uint64_t)(cu[n1] - cu[n0]), N = (uint64_t)(n1 - n0);
+    grad_off = (T / 32 + N) * H * ss;
+    aux_stride = (T / 16 + N) * H * 16 * (uint64_t)params->dv;
+    bytes = 4 * (2 * grad_off + 3 * aux_stride);
+}
+
 kda_status bwd_size(const kda_params* params, const int32_t* cu, int32_t N, uint64_t& bytes,
                     uint64_t& grad_off, uint64_t& aux_stride) {
     kda_status st = check_params(params);
@@ -629,14 +642,7 @@ kda_status bwd_size(const kda_params* params, const int32_t* cu, int32_t N, uint
     for (int32_t n = 0; n < N; ++n)
         if (cu[n + 1] < cu[n])
             return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens_host decreases at index %d", n + 1);
-    const uint64_t H = params->num_heads, ss = (uint64_t)params->dk * params->dv;
-    // the state entering chunk 2j of sequence n at pair slot cu[n]/32 + n + j (at most
-    // T_total/32 + N slots), then the gradient leaving chunk 2j + 1 (2j if it is the last) at
-    // the same slot, then three [16][dv] arrays per chunk slot cu[n]/16 + n + c (R, Y, dU)
-    const uint64_t pair_slots = (uint64_t)cu[N] / 32 + N, slots = (uint64_t)cu[N] / 16 + N;
-    grad_off = pair_slots * H * ss;
-    aux_stride = slots * H * 16 * (uint64_t)params->dv;
-    bytes = 4 * (2 * grad_off + 3 * aux_stride);
+    bwd_group_size(params, cu, 0, N, bytes, grad_off, aux_stride);
     return KDA_OK;
 }
 
@@ -685,9 +691,20 @@ kda_status kda_prefill_backward(const kda_params* params, const void* q, const v
     if (d_final_state && (st = check_ptr("d_final_state", d_final_state, 16)) != KDA_OK) return st;
     if (d_initial_state && (st = check_ptr("d_initial_state", d_initial_state, 16)) != KDA_OK) return st;
     if ((st = check_ptr("workspace", workspace, 256)) != KDA_OK) return st;
-    if (workspace_bytes < (int64_t)need)
-        return fail(KDA_ERR_INVALID_ARGUMENT, "workspace_bytes %lld < %llu needed",
-                    (long long)workspace_bytes, (unsigned long long)need);
+    // A workspace short of the whole batch's need is used for groups of consecutive
+    // sequences, one after another: it must hold the largest single sequence's.
+    if (workspace_bytes < (int64_t)need) {
+        for (int32_t n = 0; n < num_seqs; ++n) {
+            uint64_t b = 0, g = 0, x = 0;
+            bwd_group_size(params, cu_seqlens_host, n, n + 1, b, g, x);
+            if (workspace_bytes < (int64_t)b)
+                return fail(KDA_ERR_INVALID_ARGUMENT,
+                            "workspace_bytes %lld < %llu needed by sequence %d (the whole batch "
+                            "needs %llu)", (long long)workspace_bytes, (unsigned long long)b, n,
+                            (unsigned long long)need);
+        }
+    }
+    const uint64_t ws_used = std::min<uint64_t>(need, (uint64_t)workspace_bytes);
     const uint64_t nk = (uint64_t)T * H * p.dk, nv = (uint64_t)T * H * p.dv;
     const uint64_t ns = (uint64_t)num_seqs * H * p.dk * p.dv * 4;
     const Range ins[] = {range("q", q, nk * es), range("k", k, nk * es), range("v", v, nv * es),
@@ -697,7 +714,7 @@ kda_status kda_prefill_backward(const kda_params* params, const void* q, const v
     const Range outs[] = {range("dq", dq, nk * 4), range("dk", dk, nk * 4), range("dv", dv, nv * 4),
                           range("dlog_alpha", dlog_alpha, nk * 4), range("dbeta", dbeta, T * H * 4),
                           range("dgate", dgate, nv * 4), range("d_initial_state", d_initial_state, ns),
-                          range("workspace", workspace, need)};
+                          range("workspace", workspace, ws_used)};
     for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
         for (const Range& in : ins)
             if (overlaps(outs[i], in))
@@ -713,12 +730,34 @@ kda_status kda_prefill_backward(const kda_params* params, const void* q, const v
     a.d_out = d_out; a.cu_seqlens = cu_seqlens; a.initial_state = initial_state;
     a.d_final_state = d_final_state; a.dq = dq; a.dk_ = dk; a.dv_ = dv; a.dlog_alpha = dlog_alpha;
     a.dbeta = dbeta; a.dgate = dgate; a.d_initial_state = d_initial_state;
-    a.workspace = static_cast<float*>(workspace); a.grad_offset = (int64_t)grad_off;
-    a.aux_stride = (int64_t)aux_stride;
-    a.T_total = T;
-    const hipError_t e = kda::launch_backward(a, reinterpret_cast<hipStream_t>(stream));
-    if (e != hipSuccess)
-        return fail(KDA_ERR_HIP, "kda_prefill_backward launch: %s", hipGetErrorString(e));
+    a.workspace = static_cast<float*>(workspace);
+    const uint64_t SSH = (uint64_t)H * p.dk * p.dv;  // floats of one sequence's states
+    int32_t n0 = 0;
+    while (n0 < num_seqs) {
+        // the longest run of sequences from n0 whose workspace fits
+        int32_t n1 = n0 + 1;
+        uint64_t b = 0, g = 0, x = 0;
+        while (n1 < num_seqs) {
+            bwd_group_size(params, cu_seqlens_host, n0, n1 + 1, b, g, x);
+            if (b > ws_used) break;
+            ++n1;
+        }
+        bwd_group_size(params, cu_seqlens_host, n0, n1, b, g, x);
+        kda::BackwardArgs ga = a;
+        ga.num_seqs = n1 - n0;
+        ga.cu_seqlens = cu_seqlens + n0;  // absolute token offsets: token tensors stay as given
+        ga.initial_state = initial_state ? initial_state + n0 * SSH : nullptr;
+        ga.d_final_state = d_final_state ? d_final_state + n0 * SSH : nullptr;
+        ga.d_initial_state = d_initial_state ? d_initial_state + n0 * SSH : nullptr;
+        ga.grad_offset = (int64_t)g;
+        ga.aux_stride = (int64_t)x;
+        ga.T_total = cu_seqlens_host[n1] - cu_seqlens_host[n0];
+        const hipError_t e = kda::launch_backward(ga, reinterpret_cast<hipStream_t>(stream));
+        if (e != hipSuccess)
+            return fail(KDA_ERR_HIP, "kda_prefill_backward launch (sequences %d..%d): %s", n0,
+                        n1 - 1, hipGetErrorString(e));
+        n0 = n1;
+    }
     return ok();
 }
 

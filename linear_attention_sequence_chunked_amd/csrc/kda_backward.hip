@@ -170,9 +170,9 @@ struct WalkArgs {
     const float* S0;    // initial state, or null
     const float* dSf;   // gradient of the final state, or null
     float* dS0;         // gradient of the initial state, or null
-    float* states;      // state entering chunk 2j of sequence n: pair slot cu[n]/32 + n + j, [dv][dk]
+    float* states;      // state entering chunk 2j of sequence n: pair slot (cu[n] - cu[0])/32 + n + j, [dv][dk]
     float* dsc;         // gradient leaving chunk 2j + 1 (2j if the last): same slot, [dv][dk]
-    float* aux;         // per chunk slot cu[n]/16 + n + c [dv][16]: R, Y (forwards), dU (backwards)
+    float* aux;         // per chunk slot (cu[n] - cu[0])/16 + n + c [dv][16]: R, Y (forwards), dU (backwards)
     int64_t aux_stride; // floats between those three arrays
     int H, n_slices, half, pairs;
     float floor_, scale;
@@ -548,8 +548,11 @@ __global__ __launch_bounds__(64 * (NCB + 1 + ND)) void walk_kernel(const WalkArg
     const int col = slice * NV + 16 * wave + r;
     // pair slots of the sequence: the state entering even chunks (forwards), the gradient
     // leaving odd chunks and the last (backwards); the gradient kernel re-forms the others
-    float* const out = (rev ? a.dsc : a.states) + ((tbeg / (2 * kC) + n) * H + h) * SS;
-    const int64_t aslot = (tbeg / kC + n) * H + h;  // (slot, head) row of chunk 0
+    // (slots count from the batch's first token, cu[0], so that a batch can be any range of
+    // a larger one's sequences)
+    const int64_t trel = tbeg - a.cu[0];
+    float* const out = (rev ? a.dsc : a.states) + ((trel / (2 * kC) + n) * H + h) * SS;
+    const int64_t aslot = (trel / kC + n) * H + h;  // (slot, head) row of chunk 0
     // X[b] holds rows 16b + 4g + i, column col of S (forwards) or dS (backwards)
     const float* init = rev ? a.dSf : a.S0;
     f32x4 X[KB];
@@ -646,9 +649,9 @@ template <typename T>
 struct GradArgs {
     const T *q, *k, *v, *la, *beta, *gate, *dout;
     const int32_t* cu;
-    const float* states;  // state entering chunk 2j of sequence n: pair slot cu[n]/32 + n + j, [dv][dk]
+    const float* states;  // state entering chunk 2j of sequence n: pair slot (cu[n] - cu[0])/32 + n + j, [dv][dk]
     const float* dsc;     // gradient leaving chunk 2j + 1 (2j if the last): same slot, [dv][dk]
-    const float* aux;     // per chunk slot cu[n]/16 + n + c, [dv][16]: R, Y, dU, aux_stride floats apart
+    const float* aux;     // per chunk slot (cu[n] - cu[0])/16 + n + c, [dv][16]: R, Y, dU, aux_stride floats apart
     int64_t aux_stride;
     float *dq, *dk, *dv, *dla, *dbeta, *dgate;
     int H, N;
@@ -689,17 +692,18 @@ __global__ __launch_bounds__(64 * kGW, 1) void grad_kernel(const GradArgs<T> a) 
     const int z = wave / kNW, wq = wave % kNW, ht = tid % (64 * kNW);
     const int H = a.H;
     const int slot = blockIdx.x / H, h = blockIdx.x % H;
-    // sequence n owns pair slots [cu[n]/32 + n, cu[n+1]/32 + n + 1): the largest n with
-    // cu[n]/32 + n <= slot
+    // sequence n owns pair slots [(cu[n] - cu[0])/32 + n, (cu[n+1] - cu[0])/32 + n + 1): the
+    // largest n with (cu[n] - cu[0])/32 + n <= slot
+    const int64_t cu0 = a.cu[0];
     int lo = 0, hi = a.N - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (a.cu[mid] / (2 * kC) + mid <= slot) lo = mid;
+        if ((a.cu[mid] - cu0) / (2 * kC) + mid <= slot) lo = mid;
         else hi = mid - 1;
     }
     const int n = lo;
     const int64_t tbeg = a.cu[n], tend = a.cu[n + 1];
-    const int jp = slot - (int)(tbeg / (2 * kC)) - n;
+    const int jp = slot - (int)((tbeg - cu0) / (2 * kC)) - n;
     const int nch = (int)((tend - tbeg + kC - 1) / kC);
     if (2 * jp >= nch) return;  // a slot past the sequence's last pair
     const bool has_b = 2 * jp + 1 < nch;
@@ -764,7 +768,7 @@ __global__ __launch_bounds__(64 * kGW, 1) void grad_kernel(const GradArgs<T> a) 
     // the walks' R, Y (forwards) and dU (backwards), dO and the gate -- loaded ahead of their
     // use.  Rows past the end of the sequence re-read its last row and are masked.
     constexpr int NA = VB / kNW;  // value blocks per wave of a half
-    const float* const ax = a.aux + ((tbeg / kC + n + (tld - tbeg) / kC) * H + h) * kC * DV;
+    const float* const ax = a.aux + (((tbeg - cu0) / kC + n + (tld - tbeg) / kC) * H + h) * kC * DV;
     f32x4 Rv[NA], Yv[NA], dUv[NA];
     T rdo[NA][4], rgt[NA][4];
 #pragma unroll
@@ -1114,7 +1118,7 @@ hipError_t launch_typed(const BackwardArgs& p, hipStream_t st) {
     a.aux_stride = p.aux_stride;
     a.dq = p.dq; a.dk = p.dk_; a.dv = p.dv_; a.dla = p.dlog_alpha; a.dbeta = p.dbeta;
     a.dgate = p.dgate; a.H = p.H; a.N = p.num_seqs; a.floor_ = p.floor_; a.scale = p.scale;
-    const int64_t slots = p.T_total / (2 * kC) + p.num_seqs;  // pair slots
+    const int64_t slots = p.T_total / (2 * kC) + p.num_seqs;  // pair slots (T_total: the batch's tokens)
     hipLaunchKernelGGL((grad_kernel<T, DK, DV>), dim3((unsigned)(slots * p.H)), dim3(64 * kGW), 0,
                        st, a);
     return hipGetLastError();

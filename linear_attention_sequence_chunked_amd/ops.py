@@ -374,11 +374,17 @@ def chunk_prefill_segmented(q, k, v, log_alpha, beta, gate, cu_seqlens, segment_
 def prefill_backward(q, k, v, log_alpha, beta, gate, d_out, cu_seqlens=None,
                      initial_state=None, d_final_state=None, log_alpha_floor: float = -0.3,
                      scale: float = 1.0, cu_seqlens_host: Optional[Sequence[int]] = None,
-                     workspace: Optional[torch.Tensor] = None):
+                     workspace: Optional[torch.Tensor] = None,
+                     max_workspace_bytes: Optional[int] = None):
     """Gradients of chunk_prefill (fp32).  Inputs as for chunk_prefill ([B, T, H, d] or
     packed [T_total, H, d] with cu_seqlens), d_out shaped like o, d_final_state fp32
     [N, H, dk, dv] or None.  Returns a dict with dq, dk, dv, dlog_alpha, dbeta, dgate
-    (fp32, shaped like the inputs) and d_initial_state (fp32 [N, H, dk, dv])."""
+    (fp32, shaped like the inputs) and d_initial_state (fp32 [N, H, dk, dv]).
+
+    workspace: a uint8 device tensor used as given (the library runs groups of sequences
+    that fit it; it must hold the largest single sequence's need).  Without one, a workspace
+    of the whole batch's need is allocated, or of max_workspace_bytes when that is smaller
+    (but never below the largest single sequence's need)."""
     dt = q.dtype
     if dt not in _DT:
         raise ValueError(f"unsupported dtype {dt}")
@@ -425,8 +431,14 @@ def prefill_backward(q, k, v, log_alpha, beta, gate, d_out, cu_seqlens=None,
     need = lib.kda_prefill_backward_workspace(ctypes.byref(p), cu_h, N)
     if need < 0:
         raise _lib.KdaError(_lib.KDA_ERR_INVALID_ARGUMENT, lib.kda_last_error().decode())
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    if workspace is None:
+        size = need
+        if max_workspace_bytes is not None and max_workspace_bytes < need:
+            one = max(lib.kda_prefill_backward_workspace(
+                ctypes.byref(p), (ctypes.c_int32 * 2)(0, cu_host[n + 1] - cu_host[n]), 1)
+                for n in range(N))
+            size = max(int(max_workspace_bytes), one)
+        workspace = torch.empty(max(size, 256), dtype=torch.uint8, device=dev)
     else:
         _check_dev("workspace", workspace, torch.uint8)
         if workspace.device != dev:

@@ -124,10 +124,22 @@ int main() {
     const int64_t bws = kda_prefill_backward_workspace(&p, cu, 3);
     if (bws <= 0) { std::fprintf(stderr, "backward workspace %lld\n", (long long)bws); ++failures; }
     EXPECT(kda_prefill_backward_workspace(&p, bad_cu, 2), -1);
+    // less than the whole batch's workspace: groups of sequences (the stubbed launch fails);
+    // less than the largest single sequence's: rejected before any launch
+    int64_t one = 0;
+    for (int n = 0; n < 3; ++n) {
+        const int32_t c1[] = {0, cu[n + 1] - cu[n]};
+        const int64_t b = kda_prefill_backward_workspace(&p, c1, 1);
+        one = b > one ? b : one;
+    }
     EXPECT(kda_prefill_backward(&p, A(1), A(2), A(3), A(4), A(5), A(6), dcu, cu, 3, nullptr,
                                 A(12), nullptr, (float*)A(13), (float*)A(14), (float*)A(15),
                                 (float*)A(16), (float*)A(17), (float*)A(18), nullptr, A(19),
-                                bws - 1, nullptr), KDA_ERR_INVALID_ARGUMENT);
+                                bws - 1, nullptr), KDA_ERR_HIP);
+    EXPECT(kda_prefill_backward(&p, A(1), A(2), A(3), A(4), A(5), A(6), dcu, cu, 3, nullptr,
+                                A(12), nullptr, (float*)A(13), (float*)A(14), (float*)A(15),
+                                (float*)A(16), (float*)A(17), (float*)A(18), nullptr, A(19),
+                                one - 1, nullptr), KDA_ERR_INVALID_ARGUMENT);
     EXPECT(kda_prefill_backward(&p, A(1), A(2), A(3), A(4), A(5), A(6), dcu, cu, 3, nullptr,
                                 A(12), nullptr, (float*)A(13), (float*)A(14), (float*)A(15),
                                 (float*)A(16), (float*)A(17), (float*)A(18), nullptr, A(19), bws,

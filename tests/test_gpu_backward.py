@@ -124,3 +124,39 @@ def test_backward_strongest_decay_floor(dtype):
     do = torch.randn(x.v.shape, generator=g).to(x.v.dtype).cuda()
     dSf = (torch.randn(x.initial_state.shape, generator=g) * 0.1).cuda()
     run_case(x, do, dSf, floor=-5.0, scale=1.0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_workspace_groups(dtype):
+    """A workspace short of the batch's need: the library runs groups of consecutive
+    sequences, one after another.  Every gradient equals the single-launch result bit for bit
+    (each chunk's arithmetic is the same), for a workspace of one sequence's need and one of
+    about half the batch's."""
+    lengths = (100, 33, 64, 17, 0, 48)
+    log(f"backward workspace groups dtype={dtype}")
+    x = ki.make_prefill_inputs(lengths, 3, 128, 128, dtype, 0.3, seed=73, device="cuda",
+                               log_alpha_min=-0.6)
+    g = torch.Generator().manual_seed(73)
+    do = (torch.randn(x.v.shape, generator=g) * 0.5).to(x.v.dtype).cuda()
+    dSf = (torch.randn(x.initial_state.shape, generator=g) * 0.1).cuda()
+    kw = dict(cu_seqlens=x.cu_seqlens, cu_seqlens_host=x.cu_seqlens_host,
+              initial_state=x.initial_state, d_final_state=dSf, log_alpha_floor=-0.4, scale=0.9)
+    full = kda.prefill_backward(x.q, x.k, x.v, x.log_alpha, x.beta, x.gate, do, **kw)
+    lib = kda.load_library()
+    import ctypes
+    from linear_attention_sequence_chunked_amd import _lib as klib
+    p = klib.params(klib.KDA_DTYPE_BF16 if dtype == "bf16" else klib.KDA_DTYPE_F32, 3, 128, 128,
+                    -0.4, 0.9)
+    cu = x.cu_seqlens_host
+    need = lib.kda_prefill_backward_workspace(ctypes.byref(p), (ctypes.c_int32 * len(cu))(*cu),
+                                              len(lengths))
+    one = max(lib.kda_prefill_backward_workspace(ctypes.byref(p), (ctypes.c_int32 * 2)(0, L), 1)
+              for L in lengths)
+    assert one < need
+    for size in (one, (need + one) // 2):
+        part = kda.prefill_backward(x.q, x.k, x.v, x.log_alpha, x.beta, x.gate, do,
+                                    max_workspace_bytes=size, **kw)
+        torch.cuda.synchronize()
+        for key in full:
+            assert torch.equal(full[key], part[key]), f"{key} differs with a {size}-byte workspace"
+    log(f"  groups equal to the single launch (workspace {one} and {(need + one) // 2} of {need} bytes)")
