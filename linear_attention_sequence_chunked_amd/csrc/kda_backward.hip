@@ -357,18 +357,21 @@ __global__ __launch_bounds__(64 * (NCB + 1 + ND)) void walk_kernel(const WalkArg
             const int Cp = rows_of(chunk_of(it));
             if (lane < kC) s_beta[lane] = lane < Cp ? to_f32(xb) : 0.f;
             fetch(xb, it + PF);
-            // A' = strict_lower(Kt Kb^T) and P = lower_incl_diag(Qt Kb^T)
-            f32x4 accA = zero4(), accP = zero4();
+            // A' = strict_lower(Kt Kb^T) and P = lower_incl_diag(Qt Kb^T), each summed in two
+            // independent accumulators (alternate channel-block pairs) so that consecutive
+            // MFMAs do not wait on each other's results
+            f32x4 accA2[2] = {zero4(), zero4()}, accP2[2] = {zero4(), zero4()};
 #pragma unroll
             for (int kb = 0; kb < KB; kb += 2) {
-                const int f0 = fr + 16 * kb, f1 = f0 + 16;
+                const int f0 = fr + 16 * kb, f1 = f0 + 16, u = (kb >> 1) & 1;
                 const Split4 kb0 = lds_split(&o.kb[0][f0], &o.kb[1][f0]);
                 const Split4 kb1 = lds_split(&o.kb[0][f1], &o.kb[1][f1]);
-                accA = mma3x2(lds_split(&o.kt[0][f0], &o.kt[1][f0]), lds_split(&o.kt[0][f1], &o.kt[1][f1]),
-                              kb0, kb1, accA);
-                accP = mma3x2(lds_split(&o.qt[0][f0], &o.qt[1][f0]), lds_split(&o.qt[0][f1], &o.qt[1][f1]),
-                              kb0, kb1, accP);
+                accA2[u] = mma3x2(lds_split(&o.kt[0][f0], &o.kt[1][f0]), lds_split(&o.kt[0][f1], &o.kt[1][f1]),
+                                  kb0, kb1, accA2[u]);
+                accP2[u] = mma3x2(lds_split(&o.qt[0][f0], &o.qt[1][f0]), lds_split(&o.qt[0][f1], &o.qt[1][f1]),
+                                  kb0, kb1, accP2[u]);
             }
+            const f32x4 accA = accA2[0] + accA2[1], accP = accP2[0] + accP2[1];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 4 * g + i;
@@ -580,18 +583,21 @@ __global__ __launch_bounds__(64 * (NCB + 1 + ND)) void walk_kernel(const WalkArg
                           col * kC + 4 * g;
         auto put = [&](float* p, f32x4 x) { *reinterpret_cast<f32x4*>(p) = x; };
         if (!rev) {  // S' = Diag(gamma) S;  R = V - Kt S';  U = T R;  Y = Qt S' + P U;  S <- S' + Kb^T U
-            f32x4 KtS = zero4(), QtS = zero4();
+            // two independent accumulators each (alternate key-block pairs): the sums' MFMAs
+            // then do not wait on each other's results
+            f32x4 KtS2[2] = {zero4(), zero4()}, QtS2[2] = {zero4(), zero4()};
 #pragma unroll
             for (int b = 0; b < KB; b += 2) {
-                const int f0 = fr + 16 * b, f1 = f0 + 16;
+                const int f0 = fr + 16 * b, f1 = f0 + 16, u = (b >> 1) & 1;
                 X[b] *= ld4(&o.gamma[16 * b + 4 * g]);
                 X[b + 1] *= ld4(&o.gamma[16 * b + 16 + 4 * g]);
                 const Split4 x0 = split4(X[b]), x1 = split4(X[b + 1]);
-                KtS = mma3x2(lds_split(&o.kt[0][f0], &o.kt[1][f0]), lds_split(&o.kt[0][f1], &o.kt[1][f1]),
-                             x0, x1, KtS);
-                QtS = mma3x2(lds_split(&o.qt[0][f0], &o.qt[1][f0]), lds_split(&o.qt[0][f1], &o.qt[1][f1]),
-                             x0, x1, QtS);
+                KtS2[u] = mma3x2(lds_split(&o.kt[0][f0], &o.kt[1][f0]), lds_split(&o.kt[0][f1], &o.kt[1][f1]),
+                                 x0, x1, KtS2[u]);
+                QtS2[u] = mma3x2(lds_split(&o.qt[0][f0], &o.qt[1][f0]), lds_split(&o.qt[0][f1], &o.qt[1][f1]),
+                                 x0, x1, QtS2[u]);
             }
+            const f32x4 KtS = KtS2[0] + KtS2[1], QtS = QtS2[0] + QtS2[1];
             const f32x4 Rv = in4 - KtS;
             const Split4 Us = split4(mma3(lds_split(&o.sq1[0][fq], &o.sq1[1][fq]), split4(Rv), zero4()));
             put(ax, Rv);
@@ -601,13 +607,15 @@ __global__ __launch_bounds__(64 * (NCB + 1 + ND)) void walk_kernel(const WalkArg
                 X[b] = mma3(lds_split_tr(&o.kb[0][ft + 16 * b], &o.kb[1][ft + 16 * b]), Us, X[b]);
         } else {  // dU = P^T dY + Kb dS_C;  dR = T^T dU;  dS = Diag(gamma) (dS_C + Qt^T dY - Kt^T dR)
             const Split4 Ys = split4(in4);
-            f32x4 dU = mma3(lds_split(&o.sq1[0][fq], &o.sq1[1][fq]), Ys, zero4());
+            // two independent accumulators (as forwards)
+            f32x4 dU2[2] = {mma3(lds_split(&o.sq1[0][fq], &o.sq1[1][fq]), Ys, zero4()), zero4()};
 #pragma unroll
             for (int b = 0; b < KB; b += 2) {
-                const int f0 = fr + 16 * b, f1 = f0 + 16;
-                dU = mma3x2(lds_split(&o.kb[0][f0], &o.kb[1][f0]), lds_split(&o.kb[0][f1], &o.kb[1][f1]),
-                            split4(X[b]), split4(X[b + 1]), dU);
+                const int f0 = fr + 16 * b, f1 = f0 + 16, u = 1 - ((b >> 1) & 1);
+                dU2[u] = mma3x2(lds_split(&o.kb[0][f0], &o.kb[1][f0]), lds_split(&o.kb[0][f1], &o.kb[1][f1]),
+                                split4(X[b]), split4(X[b + 1]), dU2[u]);
             }
+            const f32x4 dU = dU2[0] + dU2[1];
             const f32x4 dR = mma3(lds_split(&o.sq2[0][fq], &o.sq2[1][fq]), split4(dU), zero4());
             put(ax, dU);  // dR = T^T dU is formed again by the gradient kernel
             const Split4 nRs = split4(-dR);
