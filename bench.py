@@ -105,15 +105,23 @@ def prefill_algorithmic(lengths, H, dk, dv, es, has_s0, chunk=16):
 
 
 def cpu_model() -> str:
+    """/proc/cpuinfo's model name (what lscpu prints as "Model name"), with the family, model
+    and stepping numbers, which identify the part where a virtual machine shortens the name."""
+    fields = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if ":" in line:
+                    k, v = line.split(":", 1)
+                    fields.setdefault(k.strip(), v.strip())
     except OSError:
         pass
-    import platform
-    return platform.processor() or "unknown"
+    name = fields.get("model name")
+    if not name:
+        import platform
+        return platform.processor() or "unknown"
+    ids = [f"{k} {fields[k]}" for k in ("cpu family", "model", "stepping") if k in fields]
+    return f"{name} ({', '.join(ids)})" if ids else name
 
 
 def varlen_sample(lengths, H, per_class: int):
