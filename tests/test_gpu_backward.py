@@ -160,3 +160,49 @@ def test_backward_workspace_groups(dtype):
         for key in full:
             assert torch.equal(full[key], part[key]), f"{key} differs with a {size}-byte workspace"
     log(f"  groups equal to the single launch (workspace {one} and {(need + one) // 2} of {need} bytes)")
+
+
+def test_backward_writes_every_element_and_is_deterministic():
+    """Through the C ABI with NaN-poisoned outputs inside guard bands: every gradient element is
+    written (no NaN left), nothing outside the outputs is (guards intact), and two runs agree
+    bit for bit (no atomics)."""
+    import ctypes
+    from linear_attention_sequence_chunked_amd import _lib as klib
+    lengths, H, d = (100, 33, 64, 17, 0, 48), 3, 128
+    log("backward guards / NaN poison / determinism")
+    x = ki.make_prefill_inputs(lengths, H, d, d, "bf16", 0.3, seed=79, device="cuda")
+    g = torch.Generator().manual_seed(79)
+    do = torch.randn(x.v.shape, generator=g).to(torch.bfloat16).cuda()
+    T, N = x.total_tokens, len(lengths)
+    lib = kda.load_library()
+    p = klib.params(klib.KDA_DTYPE_BF16, H, d, d)
+    cu = x.cu_seqlens_host
+    cu_h = (ctypes.c_int32 * len(cu))(*cu)
+    need = lib.kda_prefill_backward_workspace(ctypes.byref(p), cu_h, N)
+    guard = 4096
+    sizes = dict(dq=T * H * d, dk=T * H * d, dv=T * H * d, dla=T * H * d, dbeta=T * H,
+                 dgate=T * H * d, ds0=N * H * d * d)
+    runs = []
+    for _ in range(2):
+        bufs = {k: torch.full((n + 2 * guard,), float("nan"), dtype=torch.float32, device="cuda")
+                for k, n in sizes.items()}
+        for b in bufs.values():
+            b[:guard] = -7.5
+            b[-guard:] = -7.5
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        ptr = lambda k: bufs[k][guard:].data_ptr()
+        st = lib.kda_prefill_backward(
+            ctypes.byref(p), x.q.data_ptr(), x.k.data_ptr(), x.v.data_ptr(),
+            x.log_alpha.data_ptr(), x.beta.data_ptr(), x.gate.data_ptr(), x.cu_seqlens.data_ptr(),
+            cu_h, N, x.initial_state.data_ptr(), do.data_ptr(), None, ptr("dq"), ptr("dk"),
+            ptr("dv"), ptr("dla"), ptr("dbeta"), ptr("dgate"), ptr("ds0"), ws.data_ptr(), need,
+            torch.cuda.current_stream().cuda_stream)
+        assert st == 0, lib.kda_last_error().decode()
+        torch.cuda.synchronize()
+        for k, b in bufs.items():
+            body = b[guard:guard + sizes[k]]
+            assert torch.isfinite(body).all(), f"{k}: elements left unwritten"
+            assert torch.all(b[:guard] == -7.5) and torch.all(b[-guard:] == -7.5), f"{k}: guard"
+        runs.append({k: b[guard:guard + sizes[k]].clone() for k, b in bufs.items()})
+    for k in sizes:
+        assert torch.equal(runs[0][k], runs[1][k]), f"{k} differs between runs"
