@@ -267,10 +267,11 @@ __device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
 __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-// c + a b, both split (ah bh + al bh + ah bl): two 32-deep MFMAs
+// c + a b, both split (ah bl + al bh, then ah bh): two 32-deep MFMAs on the one A operand
+// (ah, al), so that only the B side needs a second arrangement -- shared where B is
 __device__ __forceinline__ f32x4 mma3(const Split4& a, const Split4& b, f32x4 c) {
-    c = mfma32(cat8(a.h, a.h), cat8(b.l, bf16x4{}), c);
-    return mfma32(cat8(a.h, a.l), cat8(b.h, b.h), c);
+    c = mfma32(cat8(a.h, a.l), cat8(b.l, b.h), c);
+    return mfma32(cat8(a.h, a.l), cat8(b.h, bf16x4{}), c);
 }
 // c + a0 b0 + a1 b1, all split: three 32-deep MFMAs
 __device__ __forceinline__ f32x4 mma3x2(const Split4& a0, const Split4& a1, const Split4& b0,
@@ -642,7 +643,7 @@ __global__ __launch_bounds__(64 * (NCB + 1 + ND)) void walk_kernel(const WalkArg
 }
 
 // ---------------------------------------------------------------------------------------------
-// 2. Per-chunk gradients, one workgroup per (pair of chunks, head).
+// 2. Per-chunk gradients, one (pair of chunks, head) at a time per workgroup.
 //
 // The walks store the state entering each even chunk 2j and the gradient leaving each odd
 // chunk 2j + 1 (leaving chunk 2j when that is the sequence's last); the workgroup of pair j
@@ -653,6 +654,15 @@ __global__ __launch_bounds__(64 * (NCB + 1 + ND)) void walk_kernel(const WalkArg
 // which halves the state traffic of both launches.  Waves 0-3 take chunk 2j and waves 4-7
 // chunk 2j + 1 in the per-chunk phases; in the sums over value columns wave w takes channel
 // block w of both chunks and forms the re-formed blocks as it goes.
+//
+// The workgroup (one per compute unit: ~154 KB of LDS) is persistent: it takes the items
+// (pair slot, head) blockIdx.x, blockIdx.x + gridDim.x, ... and issues the global loads of
+// its next item once the sums over value columns of the current one are done, so that they
+// land while the current item's last phases run.  The memory counter counts loads and stores
+// in issue order, and a wait is only as tight as the compiler can prove: every global
+// access is issued unconditionally (loads re-read rows in range, stores are raw buffer
+// stores whose out-of-range lanes -- rows past the end, halves without a chunk -- are
+// dropped), so that each wait covers exactly the loads it needs.
 template <typename T>
 struct GradArgs {
     const T *q, *k, *v, *la, *beta, *gate, *dout;
@@ -662,11 +672,12 @@ struct GradArgs {
     const float* aux;     // per chunk slot (cu[n] - cu[0])/16 + n + c, [dv][16]: R, Y, dU, aux_stride floats apart
     int64_t aux_stride;
     float *dq, *dk, *dv, *dla, *dbeta, *dgate;
-    int H, N;
+    int H, N, items;  // items = pair slots x heads
     float floor_, scale;
 };
 
 constexpr int kGW = 2 * kNW;  // waves per gradient workgroup: kNW per chunk of the pair
+constexpr int kCuW = 4;       // sequence bounds held in registers for batches of < 64 kCuW
 
 // A-fragment of the transpose of the 16x16 block at column c0 of a row-major tile X with
 // row stride `stride`: element i of lane (r, g) = X[4g + i][c0 + r]
@@ -674,6 +685,29 @@ __device__ __forceinline__ f32x4 ld4_colv(const float* X, int stride, int c0, in
     return f32x4{X[(4 * g) * stride + c0 + r], X[(4 * g + 1) * stride + c0 + r],
                  X[(4 * g + 2) * stride + c0 + r], X[(4 * g + 3) * stride + c0 + r]};
 }
+
+// Raw buffer over [p, p + bytes): stores at offsets past the end are dropped by the range
+// check (no memory access), which masks rows without a branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(float* p, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)bytes, 0x00020000);
+}
+constexpr uint32_t kDropped = 0x80000000u;  // an offset past every output range
+__device__ __forceinline__ void bstore1(__amdgpu_buffer_rsrc_t rs, uint32_t off, float x) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rs, off, 0, 0);
+}
+__device__ __forceinline__ void bstore8(__amdgpu_buffer_rsrc_t rs, uint32_t off, const float (&x)[8]) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 a = {__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])};
+    const u32x4 b = {__float_as_uint(x[4]), __float_as_uint(x[5]), __float_as_uint(x[6]), __float_as_uint(x[7])};
+    __builtin_amdgcn_raw_buffer_store_b128(a, rs, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(b, rs, off + 16, 0, 0);
+}
+
+// One item: the pair slot, its head, and where the pair sits in its sequence
+struct GradItem {
+    int slot, h, n, jp, nch;
+    int64_t tbeg, tend;
+};
 
 template <typename T, int DK, int DV>
 __global__ __launch_bounds__(64 * kGW, 1) void grad_kernel(const GradArgs<T> a) {
@@ -694,34 +728,13 @@ __global__ __launch_bounds__(64 * kGW, 1) void grad_kernel(const GradArgs<T> a) 
     __shared__ __attribute__((aligned(16))) float s_gamma[2][DK], s_dgam[2][DK];
     __shared__ float s_beta[2][kC], s_dbT[2][kC], s_dbA[2][kC];
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int r = lane & 15, g = lane >> 4;
-    // z: the pair's chunk this half of the workgroup takes; wq, ht: wave and thread in the half
-    const int z = wave / kNW, wq = wave % kNW, ht = tid % (64 * kNW);
+    // (the wave index read from lane 0 is known wave-uniform: the output ranges built from it
+    // are scalar registers)
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // z: the pair's chunk this half of the workgroup takes; wq: the wave in the half
+    const int z = wave / kNW, wq = wave % kNW;
     const int H = a.H;
-    const int slot = blockIdx.x / H, h = blockIdx.x % H;
-    // sequence n owns pair slots [(cu[n] - cu[0])/32 + n, (cu[n+1] - cu[0])/32 + n + 1): the
-    // largest n with (cu[n] - cu[0])/32 + n <= slot
-    const int64_t cu0 = a.cu[0];
-    int lo = 0, hi = a.N - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if ((a.cu[mid] - cu0) / (2 * kC) + mid <= slot) lo = mid;
-        else hi = mid - 1;
-    }
-    const int n = lo;
-    const int64_t tbeg = a.cu[n], tend = a.cu[n + 1];
-    const int jp = slot - (int)((tbeg - cu0) / (2 * kC)) - n;
-    const int nch = (int)((tend - tbeg + kC - 1) / kC);
-    if (2 * jp >= nch) return;  // a slot past the sequence's last pair
-    const bool has_b = 2 * jp + 1 < nch;
-    const bool live = z == 0 || has_b;  // this half has a chunk
-    const int c = 2 * jp + z;
-    const int64_t t0 = tbeg + (int64_t)kC * c;
-    const int Cp = live ? (int)min<int64_t>(kC, tend - t0) : 0;
     const int64_t rowq = (int64_t)H * DK, rowv = (int64_t)H * DV, SS = (int64_t)DK * DV;
-    const float* const Sa = a.states + ((int64_t)slot * H + h) * SS;
-    const float* const Dst = a.dsc + ((int64_t)slot * H + h) * SS;
     // U, dY, dR of the value phases as split bf16 tiles [16][VSB] (hi, lo) in s_big
     constexpr int VSB = DV + 8;
     auto vtile = [&](int y, int t, int part) {
@@ -729,20 +742,59 @@ __global__ __launch_bounds__(64 * kGW, 1) void grad_kernel(const GradArgs<T> a) 
     };
     static_assert(6 * 16 * VSB * 2 <= 4 * kC * WS * 4, "split value tiles fit in s_big");
 
-    // The stored S (entering chunk 2j) and dS of channel block `wave`, read along rows
-    // (B-fragments of S^T over each value block), for the sums over value columns
-    const int cb = min(wave, KB - 1);
-    f32x4 S2[VB], D2[VB];
-    auto loadB = [&]() {
+    // Sequence n owns pair slots [(cu[n] - cu[0])/32 + n, (cu[n+1] - cu[0])/32 + n + 1): an
+    // item's sequence is the largest n with (cu[n] - cu[0])/32 + n <= slot.  For batches of
+    // fewer than 64 kCuW sequences, lane l of word j holds cu[64 j + l] - cu[0] and that
+    // sequence's first slot, and the search is a ballot; larger batches search cu in memory.
+    const int64_t cu0 = a.cu[0];
+    const bool cu_regs = a.N < 64 * kCuW;
+    int cur[kCuW], key[kCuW];
 #pragma unroll
-        for (int vb = 0; vb < VB; ++vb) {
+    for (int j = 0; j < kCuW; ++j) {
+        const int m = 64 * j + (tid & 63);
+        cur[j] = (int)(a.cu[min(m, a.N)] - cu0);
+        key[j] = m <= a.N ? cur[j] / (2 * kC) + m : 0x7fffffff;
+    }
+    auto cu_at = [&](int m) -> int64_t {  // cu[m] - cu[0], m <= N (wave-uniform)
+        int x = __builtin_amdgcn_readlane(cur[0], m & 63);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {  // stored transposed: [dv][dk]
-                const int64_t off = (int64_t)(16 * vb + 4 * g + i) * DK + 16 * cb + r;
-                S2[vb][i] = Sa[off];
-                D2[vb][i] = Dst[off];
-            }
+        for (int j = 1; j < kCuW; ++j) {
+            const int y = __builtin_amdgcn_readlane(cur[j], m & 63);
+            x = (m >> 6) == j ? y : x;
         }
+        return x;
+    };
+    // fills `it` for item w; false for a slot past its sequence's last pair
+    auto locate = [&](int w, GradItem& it) -> bool {
+        it.slot = w / H;
+        it.h = w - it.slot * H;
+        int n;
+        if (cu_regs) {
+            int cnt = 0;
+#pragma unroll
+            for (int j = 0; j < kCuW; ++j) cnt += __popcll(__ballot(key[j] <= it.slot));
+            n = cnt - 1;
+            it.tbeg = cu0 + cu_at(n);
+            it.tend = cu0 + cu_at(n + 1);
+        } else {
+            int lo = 0, hi = a.N - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if ((a.cu[mid] - cu0) / (2 * kC) + mid <= it.slot) lo = mid;
+                else hi = mid - 1;
+            }
+            n = lo;
+            it.tbeg = a.cu[n];
+            it.tend = a.cu[n + 1];
+        }
+        it.n = n;
+        it.jp = it.slot - (int)((it.tbeg - cu0) / (2 * kC)) - n;
+        it.nch = (int)((it.tend - it.tbeg + kC - 1) / kC);
+        return 2 * it.jp < it.nch;
+    };
+    auto next_item = [&](int w, GradItem& it) {
+        while (w < a.items && !locate(w, it)) w += gridDim.x;
+        return w;
     };
 
     // Per-channel decay of this half's chunk, row layout: wave wq < NPC takes lane (pr, pg) =
@@ -750,347 +802,412 @@ __global__ __launch_bounds__(64 * kGW, 1) void grad_kernel(const GradArgs<T> a) 
     // pieces; the cumulative sum over rows runs across the 16 lanes of a row.  The wave keeps
     // G of its piece for the last phase.
     constexpr int CW = DK / 4, NPC = CW / 8, NWD = (int)sizeof(T) / 2;
-    const int pr = lane & 15, pg = lane >> 4;
-    const int ch0 = pg * CW + 8 * wq;
-    const bool rin = pr < Cp;
-    // Every wave issues its loads unconditionally (a half without a chunk, and waves past
-    // NPC, re-read rows and channels of chunk 2j that they then ignore), in the order the
-    // phases wait for them, so that each wait on the in-order memory counter leaves the later
-    // loads in flight: the decay inputs, beta and the value blocks here, S and dS during the
-    // value phase.
-    const int64_t tld = live ? t0 : tbeg + (int64_t)kC * 2 * jp;
-    const int Cld = live ? Cp : (int)min<int64_t>(kC, tend - tld);
+    constexpr int NA = VB / kNW;  // value blocks per wave of a half
+    // Per-thread indices, formed again in every pass of the item loop from a copy of the
+    // thread index the compiler cannot see through: hoisted out of the loop, the many
+    // addresses derived from them would stay live across it and spill.
+    //   lane = (r, g) in MFMA fragments; (pr, pg) = (row, channel group) in the decay layout;
+    //   ht = thread in the half
+#define GRAD_THREAD_INDICES(tv)                                                  \
+    const int lane = (tv) & 63, r = lane & 15, g = lane >> 4, pr = r, pg = g;     \
+    const int ht = (tv) % (64 * kNW), ch0 = pg * CW + 8 * min(wq, NPC - 1);        \
+    (void)lane; (void)r; (void)g; (void)pr; (void)pg; (void)ht; (void)ch0
+
+    // The global operands of an item, loaded one item ahead: the decay inputs and beta (rows
+    // of chunk 2j in a half without a chunk, which it then ignores), then per value block of
+    // this half's chunk (rows 4g + i, column 16 vb + r) the walks' R, Y (forwards) and dU
+    // (backwards), dO and the gate.  Rows past the end of the sequence re-read its last row
+    // and are masked.  Issued in the order the phases wait for them.
     uint4 wq4[NWD], wk[NWD], wl[NWD];
-    {
-        const int64_t off = (tld + min(pr, Cld - 1)) * rowq + (int64_t)h * DK + pg * CW +
-                            8 * min(wq, NPC - 1);
+    T bt;
+    f32x4 Rv[NA], Yv[NA], dUv[NA];
+    T rdo[NA][4], rgt[NA][4];
+    auto issue = [&](const GradItem& it, int tv) {
+        GRAD_THREAD_INDICES(tv);
+        const bool hb = 2 * it.jp + 1 < it.nch;
+        const int64_t tld = it.tbeg + (int64_t)kC * (2 * it.jp + (z == 0 || hb ? z : 0));
+        const int Cld = (int)min<int64_t>(kC, it.tend - tld);
+        const int64_t off = (tld + min(pr, Cld - 1)) * rowq + (int64_t)it.h * DK + ch0;
 #pragma unroll
         for (int w = 0; w < NWD; ++w) {
             wq4[w] = *reinterpret_cast<const uint4*>(a.q + off + 4 * w);
             wk[w] = *reinterpret_cast<const uint4*>(a.k + off + 4 * w);
             wl[w] = *reinterpret_cast<const uint4*>(a.la + off + 4 * w);
         }
-    }
-    const T bt = a.beta[(tld + min(ht & 15, Cld - 1)) * H + h];
-    // Global operands of one value block of this half's chunk, rows 4g + i, column 16 vb + r:
-    // the walks' R, Y (forwards) and dU (backwards), dO and the gate -- loaded ahead of their
-    // use.  Rows past the end of the sequence re-read its last row and are masked.
-    constexpr int NA = VB / kNW;  // value blocks per wave of a half
-    const float* const ax = a.aux + (((tbeg - cu0) / kC + n + (tld - tbeg) / kC) * H + h) * kC * DV;
-    f32x4 Rv[NA], Yv[NA], dUv[NA];
-    T rdo[NA][4], rgt[NA][4];
-#pragma unroll
-    for (int ia = 0; ia < NA; ++ia) {
-        const int col = 16 * (wq + kNW * ia) + r;
-        const int64_t o = (int64_t)col * kC + 4 * g;  // stored transposed: [dv][16]
-        Rv[ia] = ld4(ax + o);
-        Yv[ia] = ld4(ax + a.aux_stride + o);
-        dUv[ia] = ld4(ax + 2 * a.aux_stride + o);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t off = (tld + min(4 * g + i, Cld - 1)) * rowv + (int64_t)h * DV + col;
-            rdo[ia][i] = a.dout[off];
-            rgt[ia][i] = a.gate[off];
-        }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-
-    float Gp[8];
-    uint32_t livep = 0;
-    if (live && wq < NPC) {
-        float xq[8], xk[8];
-        unpack8<T>(wq4, xq);
-        unpack8<T>(wk, xk);
-        unpack8<T>(wl, Gp);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            if (rin && Gp[i] > a.floor_) livep |= 1u << i;
-            Gp[i] = rin ? fmaxf(Gp[i], a.floor_) : 0.f;
-        }
-        row_scan8(Gp);
-        float qh[8], kh[8], kc[8], gm[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float e = __expf(Gp[i]), ei = __expf(-Gp[i]);
-            const float qv = rin ? xq[i] : 0.f, kv = rin ? xk[i] : 0.f;
-            gm[i] = __expf(row_last(Gp[i]));
-            qh[i] = a.scale * qv * e;
-            kh[i] = kv * e;
-            kc[i] = kv * ei;
-        }
-        store8(&s_Qh[z][pr * RS + ch0], qh);
-        store8(&s_Kh[z][pr * RS + ch0], kh);
-        store8(&s_Kc[z][pr * RS + ch0], kc);
-        if (pr == 15) store8(&s_gamma[z][ch0], gm);
-    }
-    if (live && ht < kC) s_beta[z][ht] = ht < Cp ? to_f32(bt) : 0.f;
-    lds_barrier();
-    chunk_gram<DK, RS>(s_Kh[z], s_Kc[z], s_beta[z], s_A[z], s_X[z], s_T[z], live && wq == 0, lane);
-
-    // ---- A: value blocks of this half's chunk (wave wq takes blocks wq, wq + 4, ...)
-    if (live) {
-        const f32x4 Tr = ld4(&s_T[z][r * kTS + 4 * g]), Tc = ld4_col(s_T[z], r, g);  // T, T^T
-        bf16 *const Uh = vtile(z, 0, 0), *const Ul = vtile(z, 0, 1);
-        bf16 *const dYh = vtile(z, 1, 0), *const dYl = vtile(z, 1, 1);
-        bf16 *const dRh = vtile(z, 2, 0), *const dRl = vtile(z, 2, 1);
-        auto put = [](bf16* hi, bf16* lo, int idx, float x) {
-            const bf16 xh = (bf16)x;
-            hi[idx] = xh;
-            lo[idx] = (bf16)(x - (float)xh);
-        };
-        float* const sR = s_wv[z][wq][0];
-        float* const sdU = s_wv[z][wq][1];
-        f32x4 dTw = zero4(), dPw = zero4();
+        bt = a.beta[(tld + min(ht & 15, Cld - 1)) * H + it.h];
+        __builtin_amdgcn_sched_barrier(0);
+        const float* const ax =
+            a.aux + (((it.tbeg - cu0) / kC + it.n + (tld - it.tbeg) / kC) * H + it.h) * kC * DV;
 #pragma unroll
         for (int ia = 0; ia < NA; ++ia) {
-            const int vb = wq + kNW * ia;
-            const int col = 16 * vb + r;
-            f32x4 dO, gt;
+            const int col = 16 * (wq + kNW * ia) + r;
+            const int64_t o = (int64_t)col * kC + 4 * g;  // stored transposed: [dv][16]
+            Rv[ia] = ld4(ax + o);
+            Yv[ia] = ld4(ax + a.aux_stride + o);
+            dUv[ia] = ld4(ax + 2 * a.aux_stride + o);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const bool in = 4 * g + i < Cp;
-                dO[i] = in ? to_f32(rdo[ia][i]) : 0.f;
-                gt[i] = in ? to_f32(rgt[ia][i]) : 0.f;
+                const int64_t off2 = (tld + min(4 * g + i, Cld - 1)) * rowv + (int64_t)it.h * DV + col;
+                rdo[ia][i] = a.dout[off2];
+                rgt[ia][i] = a.gate[off2];
             }
-            const f32x4 Rt = Rv[ia], Y = Yv[ia], dU = dUv[ia];
-            if (ia + 1 == NA) loadB();  // in flight during the rest of this phase
             __builtin_amdgcn_sched_barrier(0);
-            const f32x4 U = M::run(Tr, Rt, zero4());
-            const f32x4 dR = M::run(Tc, dU, zero4());  // T^T dU
-            const f32x4 dY = dO * gt;
+        }
+    };
+
+    GradItem it;
+    int w = next_item(blockIdx.x, it);
+    if (w >= a.items) return;
+    issue(it, tid);
+
+    for (;;) {
+        int tv = tid;
+        asm volatile("" : "+v"(tv));
+        GRAD_THREAD_INDICES(tv);
+        const int h = it.h, n = it.n, jp = it.jp, nch = it.nch;
+        const int64_t tbeg = it.tbeg, tend = it.tend;
+        const bool has_b = 2 * jp + 1 < nch;
+        const bool live = z == 0 || has_b;  // this half has a chunk
+        const int c = 2 * jp + z;
+        const int64_t t0 = tbeg + (int64_t)kC * c;
+        const int Cp = live ? (int)min<int64_t>(kC, tend - t0) : 0;
+        const float* const Sa = a.states + ((int64_t)it.slot * H + h) * SS;
+        const float* const Dst = a.dsc + ((int64_t)it.slot * H + h) * SS;
+        (void)n;
+
+        // The stored S (entering chunk 2j) and dS of channel block `wave`, read along rows
+        // (B-fragments of S^T over each value block), for the sums over value columns
+        const int cb = min(wave, KB - 1);
+        f32x4 S2[VB], D2[VB];
+        auto loadB = [&]() {
+#pragma unroll
+            for (int vb = 0; vb < VB; ++vb) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {  // stored transposed: [dv][dk]
+                    const int64_t off = (int64_t)(16 * vb + 4 * g + i) * DK + 16 * cb + r;
+                    S2[vb][i] = Sa[off];
+                    D2[vb][i] = Dst[off];
+                }
+            }
+        };
+
+        const bool rin = pr < Cp;
+        float Gp[8] = {};
+        uint32_t livep = 0;
+        if (live && wq < NPC) {
+            float xq[8], xk[8];
+            unpack8<T>(wq4, xq);
+            unpack8<T>(wk, xk);
+            unpack8<T>(wl, Gp);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if (rin && Gp[i] > a.floor_) livep |= 1u << i;
+                Gp[i] = rin ? fmaxf(Gp[i], a.floor_) : 0.f;
+            }
+            row_scan8(Gp);
+            float qh[8], kh[8], kc[8], gm[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float e = __expf(Gp[i]), ei = __expf(-Gp[i]);
+                const float qv = rin ? xq[i] : 0.f, kv = rin ? xk[i] : 0.f;
+                gm[i] = __expf(row_last(Gp[i]));
+                qh[i] = a.scale * qv * e;
+                kh[i] = kv * e;
+                kc[i] = kv * ei;
+            }
+            store8(&s_Qh[z][pr * RS + ch0], qh);
+            store8(&s_Kh[z][pr * RS + ch0], kh);
+            store8(&s_Kc[z][pr * RS + ch0], kc);
+            if (pr == 15) store8(&s_gamma[z][ch0], gm);
+        }
+        if (live && ht < kC) s_beta[z][ht] = ht < Cp ? to_f32(bt) : 0.f;
+        lds_barrier();
+        // the Gram product and solve of chunk z by wave z of its half (waves 0 and 5: two SIMDs)
+        chunk_gram<DK, RS>(s_Kh[z], s_Kc[z], s_beta[z], s_A[z], s_X[z], s_T[z], live && wq == z, lane);
+
+        // ---- A: value blocks of this half's chunk (wave wq takes blocks wq, wq + 4, ...).  A
+        // half without a chunk runs it too, on stale tiles: its stores all fall outside the
+        // (empty) output range and its LDS tiles are not read.
+        {
+            const f32x4 Tr = ld4(&s_T[z][r * kTS + 4 * g]), Tc = ld4_col(s_T[z], r, g);  // T, T^T
+            bf16 *const Uh = vtile(z, 0, 0), *const Ul = vtile(z, 0, 1);
+            bf16 *const dYh = vtile(z, 1, 0), *const dYl = vtile(z, 1, 1);
+            bf16 *const dRh = vtile(z, 2, 0), *const dRl = vtile(z, 2, 1);
+            auto put = [](bf16* hi, bf16* lo, int idx, float x) {
+                const bf16 xh = (bf16)x;
+                hi[idx] = xh;
+                lo[idx] = (bf16)(x - (float)xh);
+            };
+            const auto rg = out_rsrc(a.dgate + t0 * rowv, (int64_t)Cp * rowv * 4);
+            const auto rv = out_rsrc(a.dv + t0 * rowv, (int64_t)Cp * rowv * 4);
+            float* const sR = s_wv[z][wq][0];
+            float* const sdU = s_wv[z][wq][1];
+            f32x4 dTw = zero4(), dPw = zero4();
+#pragma unroll
+            for (int ia = 0; ia < NA; ++ia) {
+                const int vb = wq + kNW * ia;
+                const int col = 16 * vb + r;
+                f32x4 dO, gt;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bool in = 4 * g + i < Cp;
+                    dO[i] = in ? to_f32(rdo[ia][i]) : 0.f;
+                    gt[i] = in ? to_f32(rgt[ia][i]) : 0.f;
+                }
+                const f32x4 Rt = Rv[ia], Y = Yv[ia], dU = dUv[ia];
+                if (ia + 1 == NA) loadB();  // in flight during the rest of this phase
+                __builtin_amdgcn_sched_barrier(0);
+                const f32x4 U = M::run(Tr, Rt, zero4());
+                const f32x4 dR = M::run(Tc, dU, zero4());  // T^T dU
+                const f32x4 dY = dO * gt;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 4 * g + i;
+                    const uint32_t off = (uint32_t)((row * rowv + (int64_t)h * DV + col) * 4);
+                    bstore1(rg, off, dO[i] * Y[i]);
+                    bstore1(rv, off, dR[i]);
+                    put(Uh, Ul, row * VSB + col, U[i]);
+                    put(dYh, dYl, row * VSB + col, dY[i]);
+                    put(dRh, dRl, row * VSB + col, dR[i]);
+                    sR[row * kTS + r] = Rt[i];
+                    sdU[row * kTS + r] = dU[i];
+                }
+                wave_lds_sync();
+                // dT += dU R^T and dP += dY U^T over this block's 16 columns
+                dTw = M::run(ld4(&sdU[r * kTS + 4 * g]), ld4(&sR[r * kTS + 4 * g]), dTw);
+                const int fo = r * VSB + 16 * vb + 4 * g;
+                dPw = mma3(lds_split(&dYh[fo], &dYl[fo]), lds_split(&Uh[fo], &Ul[fo]), dPw);
+                wave_lds_sync();
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int row = 4 * g + i;
-                if (row < Cp) {
-                    const int64_t off = (t0 + row) * rowv + (int64_t)h * DV + col;
-                    a.dgate[off] = dO[i] * Y[i];
-                    a.dv[off] = dR[i];
-                }
-                put(Uh, Ul, row * VSB + col, U[i]);
-                put(dYh, dYl, row * VSB + col, dY[i]);
-                put(dRh, dRl, row * VSB + col, dR[i]);
-                sR[row * kTS + r] = Rt[i];
-                sdU[row * kTS + r] = dU[i];
+                sR[(4 * g + i) * kTS + r] = dTw[i];
+                sdU[(4 * g + i) * kTS + r] = dPw[i];
             }
-            wave_lds_sync();
-            // dT += dU R^T and dP += dY U^T over this block's 16 columns
-            dTw = M::run(ld4(&sdU[r * kTS + 4 * g]), ld4(&sR[r * kTS + 4 * g]), dTw);
-            const int fo = r * VSB + 16 * vb + 4 * g;
-            dPw = mma3(lds_split(&dYh[fo], &dYl[fo]), lds_split(&Uh[fo], &Ul[fo]), dPw);
-            wave_lds_sync();
         }
+        lds_barrier();
+        if (live) {  // dT, dP: sums of the wave parts (one element per thread of the half)
+            const int i = ht >> 4, j = ht & 15;
+            float t = 0.f, p = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            sR[(4 * g + i) * kTS + r] = dTw[i];
-            sdU[(4 * g + i) * kTS + r] = dPw[i];
+            for (int w2 = 0; w2 < kNW; ++w2) {
+                t += s_wv[z][w2][0][i * kTS + j];
+                p += s_wv[z][w2][1][i * kTS + j];
+            }
+            s_dT[z][i * kTS + j] = t;
+            s_dP[z][i * kTS + j] = j <= i ? p : 0.f;
         }
-    } else {
-        loadB();
-    }
-    lds_barrier();
-    if (live) {  // dT, dP: sums of the wave parts (one element per thread of the half)
-        const int i = ht >> 4, j = ht & 15;
-        float t = 0.f, p = 0.f;
-#pragma unroll
-        for (int w = 0; w < kNW; ++w) {
-            t += s_wv[z][w][0][i * kTS + j];
-            p += s_wv[z][w][1][i * kTS + j];
-        }
-        s_dT[z][i * kTS + j] = t;
-        s_dP[z][i * kTS + j] = j <= i ? p : 0.f;
-    }
 
-    // ---- B: the sums over value columns, channel block `wave`, both chunks.  Chunk 2j uses
-    // the stored S and the re-formed dS leaving it; chunk 2j + 1 the re-formed S entering it
-    // and the stored dS.  Products are split-bf16 (as in the walks), two value blocks per
-    // 32-deep MFMA; the re-formed blocks are fp32 accumulators seeded with the decayed
-    // stored ones, and the sums for dgamma take the fp32 values.
-    f32x4 aQ[2], aK[2], aB[2];
+        // ---- B: the sums over value columns, channel block `wave`, both chunks.  Chunk 2j uses
+        // the stored S and the re-formed dS leaving it; chunk 2j + 1 the re-formed S entering it
+        // and the stored dS.  Products are split-bf16 (as in the walks), two value blocks per
+        // 32-deep MFMA; the re-formed blocks are fp32 accumulators seeded with the decayed
+        // stored ones, and the sums for dgamma take the fp32 values.
+        f32x4 aQ[2], aK[2], aB[2];
 #pragma unroll
-    for (int y = 0; y < 2; ++y) aQ[y] = aK[y] = aB[y] = zero4();
-    if (wave < KB) {
-        const int kc0 = 16 * cb;
-        const float gA = s_gamma[0][kc0 + r], gB = has_b ? s_gamma[1][kc0 + r] : 0.f;
-        f32x4 KbA, QhB, nKhB;  // B-fragments over the chunk's rows: X[4g + i][kc0 + r]
+        for (int y = 0; y < 2; ++y) aQ[y] = aK[y] = aB[y] = zero4();
+        if (wave < KB) {
+            const int kc0 = 16 * cb;
+            const float gA = s_gamma[0][kc0 + r], gB = has_b ? s_gamma[1][kc0 + r] : 0.f;
+            f32x4 KbA, QhB, nKhB;  // B-fragments over the chunk's rows: X[4g + i][kc0 + r]
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int idx = (4 * g + i) * RS + kc0 + r;
-            KbA[i] = s_Kc[0][idx] * gA;  // Kb = Kc Diag(gamma)
-            QhB[i] = s_Qh[1][idx];
-            nKhB[i] = -s_Kh[1][idx];
-        }
-        const Split4 KbAs = split4(KbA), QhBs = split4(QhB), nKhBs = split4(nKhB);
-        // transposed reads of the value tiles (A-fragments of their transposes, see lds_tr)
-        const int ftv = (4 * g + (r >> 2)) * VSB + 4 * (r & 3);
-        float dgA = 0.f, dgB = 0.f;
+            for (int i = 0; i < 4; ++i) {
+                const int idx = (4 * g + i) * RS + kc0 + r;
+                KbA[i] = s_Kc[0][idx] * gA;  // Kb = Kc Diag(gamma)
+                QhB[i] = s_Qh[1][idx];
+                nKhB[i] = -s_Kh[1][idx];
+            }
+            const Split4 KbAs = split4(KbA), QhBs = split4(QhB), nKhBs = split4(nKhB);
+            // transposed reads of the value tiles (A-fragments of their transposes, see lds_tr)
+            const int ftv = (4 * g + (r >> 2)) * VSB + 4 * (r & 3);
+            float dgA = 0.f, dgB = 0.f;
 #pragma unroll
-        for (int vb = 0; vb < VB; vb += 2) {
-            const int vo0 = 16 * vb, vo1 = vo0 + 16;
-            const int fo0 = r * VSB + vo0 + 4 * g, fo1 = fo0 + 16;  // row fragments
-            f32x4 Da[2] = {D2[vb], D2[vb + 1]};  // dS leaving chunk 2j
-            f32x4 Sb[2];                         // S entering chunk 2j + 1
-            if (has_b) {
+            for (int vb = 0; vb < VB; vb += 2) {
+                const int vo0 = 16 * vb, vo1 = vo0 + 16;
+                const int fo0 = r * VSB + vo0 + 4 * g, fo1 = fo0 + 16;  // row fragments
+                f32x4 Da[2] = {D2[vb], D2[vb + 1]};  // dS leaving chunk 2j
+                f32x4 Sb[2];                         // S entering chunk 2j + 1
+                if (has_b) {
 #pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const int vo = vo0 + 16 * u;
-                    Sb[u] = mma3(lds_split_tr(vtile(0, 0, 0) + ftv + vo, vtile(0, 0, 1) + ftv + vo), KbAs,
-                                 S2[vb + u] * gA);
-                    Da[u] = mma3x2(lds_split_tr(vtile(1, 1, 0) + ftv + vo, vtile(1, 1, 1) + ftv + vo),
-                                   lds_split_tr(vtile(1, 2, 0) + ftv + vo, vtile(1, 2, 1) + ftv + vo),
-                                   QhBs, nKhBs, D2[vb + u] * gB);
+                    for (int u = 0; u < 2; ++u) {
+                        const int vo = vo0 + 16 * u;
+                        Sb[u] = mma3(lds_split_tr(vtile(0, 0, 0) + ftv + vo, vtile(0, 0, 1) + ftv + vo), KbAs,
+                                     S2[vb + u] * gA);
+                        Da[u] = mma3x2(lds_split_tr(vtile(1, 1, 0) + ftv + vo, vtile(1, 1, 1) + ftv + vo),
+                                       lds_split_tr(vtile(1, 2, 0) + ftv + vo, vtile(1, 2, 1) + ftv + vo),
+                                       QhBs, nKhBs, D2[vb + u] * gB);
+                    }
+                    const Split4 Sb0 = split4(Sb[0]), Sb1 = split4(Sb[1]);
+                    aQ[1] = mma3x2(lds_split(vtile(1, 1, 0) + fo0, vtile(1, 1, 1) + fo0),
+                                   lds_split(vtile(1, 1, 0) + fo1, vtile(1, 1, 1) + fo1), Sb0, Sb1, aQ[1]);
+                    aK[1] = mma3x2(lds_split(vtile(1, 2, 0) + fo0, vtile(1, 2, 1) + fo0),
+                                   lds_split(vtile(1, 2, 0) + fo1, vtile(1, 2, 1) + fo1), Sb0, Sb1, aK[1]);
+                    aB[1] = mma3x2(lds_split(vtile(1, 0, 0) + fo0, vtile(1, 0, 1) + fo0),
+                                   lds_split(vtile(1, 0, 0) + fo1, vtile(1, 0, 1) + fo1),
+                                   split4(D2[vb]), split4(D2[vb + 1]), aB[1]);
+#pragma unroll
+                    for (int u = 0; u < 2; ++u)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) dgB += D2[vb + u][i] * Sb[u][i];
                 }
-                const Split4 Sb0 = split4(Sb[0]), Sb1 = split4(Sb[1]);
-                aQ[1] = mma3x2(lds_split(vtile(1, 1, 0) + fo0, vtile(1, 1, 1) + fo0),
-                               lds_split(vtile(1, 1, 0) + fo1, vtile(1, 1, 1) + fo1), Sb0, Sb1, aQ[1]);
-                aK[1] = mma3x2(lds_split(vtile(1, 2, 0) + fo0, vtile(1, 2, 1) + fo0),
-                               lds_split(vtile(1, 2, 0) + fo1, vtile(1, 2, 1) + fo1), Sb0, Sb1, aK[1]);
-                aB[1] = mma3x2(lds_split(vtile(1, 0, 0) + fo0, vtile(1, 0, 1) + fo0),
-                               lds_split(vtile(1, 0, 0) + fo1, vtile(1, 0, 1) + fo1),
-                               split4(D2[vb]), split4(D2[vb + 1]), aB[1]);
+                const Split4 Sa0 = split4(S2[vb]), Sa1 = split4(S2[vb + 1]);
+                aQ[0] = mma3x2(lds_split(vtile(0, 1, 0) + fo0, vtile(0, 1, 1) + fo0),
+                               lds_split(vtile(0, 1, 0) + fo1, vtile(0, 1, 1) + fo1), Sa0, Sa1, aQ[0]);
+                aK[0] = mma3x2(lds_split(vtile(0, 2, 0) + fo0, vtile(0, 2, 1) + fo0),
+                               lds_split(vtile(0, 2, 0) + fo1, vtile(0, 2, 1) + fo1), Sa0, Sa1, aK[0]);
+                aB[0] = mma3x2(lds_split(vtile(0, 0, 0) + fo0, vtile(0, 0, 1) + fo0),
+                               lds_split(vtile(0, 0, 0) + fo1, vtile(0, 0, 1) + fo1),
+                               split4(Da[0]), split4(Da[1]), aB[0]);
 #pragma unroll
                 for (int u = 0; u < 2; ++u)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) dgB += D2[vb + u][i] * Sb[u][i];
+                    for (int i = 0; i < 4; ++i) dgA += Da[u][i] * S2[vb + u][i];
             }
-            const Split4 Sa0 = split4(S2[vb]), Sa1 = split4(S2[vb + 1]);
-            aQ[0] = mma3x2(lds_split(vtile(0, 1, 0) + fo0, vtile(0, 1, 1) + fo0),
-                           lds_split(vtile(0, 1, 0) + fo1, vtile(0, 1, 1) + fo1), Sa0, Sa1, aQ[0]);
-            aK[0] = mma3x2(lds_split(vtile(0, 2, 0) + fo0, vtile(0, 2, 1) + fo0),
-                           lds_split(vtile(0, 2, 0) + fo1, vtile(0, 2, 1) + fo1), Sa0, Sa1, aK[0]);
-            aB[0] = mma3x2(lds_split(vtile(0, 0, 0) + fo0, vtile(0, 0, 1) + fo0),
-                           lds_split(vtile(0, 0, 0) + fo1, vtile(0, 0, 1) + fo1),
-                           split4(Da[0]), split4(Da[1]), aB[0]);
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) dgA += Da[u][i] * S2[vb + u][i];
-        }
-        dgA += __shfl_xor(dgA, 16);
-        dgA += __shfl_xor(dgA, 32);
-        dgB += __shfl_xor(dgB, 16);
-        dgB += __shfl_xor(dgB, 32);
-        if (g == 0) {
-            s_dgam[0][kc0 + r] = dgA;
-            s_dgam[1][kc0 + r] = dgB;
-        }
-    }
-    lds_barrier();
-
-    // ---- C: the 16x16 algebra of this half's chunk (one element per thread: row i, column j)
-    float* const s_M = &s_wv[z][0][0][0];   // X^T dT Diag(beta), once the wave parts are summed
-    float* const s_dA = &s_wv[z][1][0][0];  // Diag(beta) dA
-    if (live) {
-        const int i = ht >> 4, j = ht & 15;
-        float m = 0.f;  // (X^T dT)[i][j] beta_j = (X^T dX)[i][j]
-#pragma unroll
-        for (int kk = 0; kk < kC; ++kk) m += s_X[z][kk * kTS + i] * s_dT[z][kk * kTS + j];
-        s_M[i * kTS + j] = m * s_beta[z][j];
-        if (ht < kC) {  // column sums of X * dT
-            float s = 0.f;
-#pragma unroll
-            for (int kk = 0; kk < kC; ++kk) s += s_X[z][kk * kTS + ht] * s_dT[z][kk * kTS + ht];
-            s_dbT[z][ht] = s;
-        }
-    }
-    lds_barrier();
-    if (live) {
-        const int i = ht >> 4, j = ht & 15;
-        float d = 0.f;  // dA[i][j] = -(M X^T)[i][j] on the strict lower triangle
-#pragma unroll
-        for (int kk = 0; kk < kC; ++kk) d -= s_M[i * kTS + kk] * s_X[z][j * kTS + kk];
-        d = j < i ? d : 0.f;
-        s_dA[i * kTS + j] = s_beta[z][i] * d;
-        float e = d * s_A[z][i * kTS + j];
-        e += __shfl_xor(e, 8);
-        e += __shfl_xor(e, 4);
-        e += __shfl_xor(e, 2);
-        e += __shfl_xor(e, 1);
-        if (j == 0) s_dbA[z][i] = e;
-    }
-    lds_barrier();
-
-    // ---- D: the chunk-local terms, then the four operand gradients into LDS, channel block
-    // `wave` of both chunks (the value-phase tiles are dead: every wave has passed two
-    // barriers since reading them)
-    if (wave < KB) {
-        const int kc0 = 16 * cb;
-#pragma unroll
-        for (int y = 0; y < 2; ++y) {
-            if (y == 1 && !has_b) break;
-            const float* const sdA_y = &s_wv[y][1][0][0];  // Diag(beta) dA of chunk y
-            const f32x4 dPr = ld4(&s_dP[y][r * kTS + 4 * g]), dPc = ld4_col(s_dP[y], r, g);
-            const f32x4 dAr = ld4(&sdA_y[r * kTS + 4 * g]), dAc = ld4_col(sdA_y, r, g);
-            f32x4 KcB, QhB, KhB;  // B-fragments: X[4g + i][kc0 + r]
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int idx = (4 * g + i) * RS + kc0 + r;
-                KcB[i] = s_Kc[y][idx];
-                QhB[i] = s_Qh[y][idx];
-                KhB[i] = s_Kh[y][idx];
-            }
-            const f32x4 dQh = M::run(dPr, KcB, aQ[y]);
-            const f32x4 dKh = M::run(dAr, KcB, -aK[y]);
-            const f32x4 dKc = M::run(dAc, KhB, M::run(dPc, QhB, zero4()));
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int idx = (4 * g + i) * RS + kc0 + r;
-                s_big[y][idx] = dQh[i];
-                s_big[y][kC * WS + idx] = dKh[i];
-                s_big[y][2 * kC * WS + idx] = dKc[i];
-                s_big[y][3 * kC * WS + idx] = aB[y][i];
+            dgA += __shfl_xor(dgA, 16);
+            dgA += __shfl_xor(dgA, 32);
+            dgB += __shfl_xor(dgB, 16);
+            dgB += __shfl_xor(dgB, 32);
+            if (g == 0) {
+                s_dgam[0][kc0 + r] = dgA;
+                s_dgam[1][kc0 + r] = dgB;
             }
         }
-    }
-    lds_barrier();
 
-    // ---- E: dq, dk, and dlambda of this half's chunk by the reverse cumulative sum of dG over
-    // the rows, in the decay's row layout (the 16 lanes of a row hold the chunk's rows of 8
-    // channels)
-    if (live && wq < NPC) {
-        const int idx = pr * RS + ch0;
-        float qh[8], kh[8], kc[8], dqh[8], dkh[8], dkc[8], dkb[8], gm[8], dgm[8];
-        load8(&s_Qh[z][idx], qh);
-        load8(&s_Kh[z][idx], kh);
-        load8(&s_Kc[z][idx], kc);
-        load8(&s_big[z][idx], dqh);
-        load8(&s_big[z][kC * WS + idx], dkh);
-        load8(&s_big[z][2 * kC * WS + idx], dkc);
-        load8(&s_big[z][3 * kC * WS + idx], dkb);
-        load8(&s_gamma[z][ch0], gm);
-        load8(&s_dgam[z][ch0], dgm);
-        float dq8[8], dk8[8], dl8[8], kbs[8];
+        // The next item's loads (the current item's again after its last, so that every
+        // pass issues the same accesses), in flight during the phases below
+        GradItem nx = it;
+        const int wn = next_item(w + gridDim.x, nx);
+        const bool more = wn < a.items;
+        issue(more ? nx : it, tv);
+        lds_barrier();
+
+        // ---- C: the 16x16 algebra of this half's chunk (one element per thread: row i, column j)
+        float* const s_M = &s_wv[z][0][0][0];   // X^T dT Diag(beta), once the wave parts are summed
+        float* const s_dA = &s_wv[z][1][0][0];  // Diag(beta) dA
+        if (live) {
+            const int i = ht >> 4, j = ht & 15;
+            float m = 0.f;  // (X^T dT)[i][j] beta_j = (X^T dX)[i][j]
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            kbs[i] = kc[i] * gm[i] * dkb[i];  // Kb dKb
-            dl8[i] = qh[i] * dqh[i] + kh[i] * dkh[i] - kc[i] * dkc[i] - kbs[i];  // dG
-            const float e = __expf(Gp[i]), ei = __expf(-Gp[i]);
-            dq8[i] = a.scale * e * dqh[i];
-            dk8[i] = e * dkh[i] + ei * dkc[i] + gm[i] * ei * dkb[i];
-        }
-        // G_C is the last row's G (padding rows add no decay): row 15 also takes the gradient
-        // reaching G_C, the sum over rows of Kb dKb plus gamma dgamma
-        row_scan8(kbs);
-        float inc[8];
+            for (int kk = 0; kk < kC; ++kk) m += s_X[z][kk * kTS + i] * s_dT[z][kk * kTS + j];
+            s_M[i * kTS + j] = m * s_beta[z][j];
+            if (ht < kC) {  // column sums of X * dT
+                float s = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float tot_kb = row_last(kbs[i]);
-            if (pr == 15) dl8[i] += tot_kb + gm[i] * dgm[i];
-            inc[i] = dl8[i];
+                for (int kk = 0; kk < kC; ++kk) s += s_X[z][kk * kTS + ht] * s_dT[z][kk * kTS + ht];
+                s_dbT[z][ht] = s;
+            }
         }
-        row_scan8(inc);  // inclusive sums over rows <= pr
+        lds_barrier();
+        if (live) {
+            const int i = ht >> 4, j = ht & 15;
+            float d = 0.f;  // dA[i][j] = -(M X^T)[i][j] on the strict lower triangle
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float rev = row_last(inc[i]) - inc[i] + dl8[i];  // sum over rows >= pr
-            dl8[i] = (livep >> i) & 1u ? rev : 0.f;
+            for (int kk = 0; kk < kC; ++kk) d -= s_M[i * kTS + kk] * s_X[z][j * kTS + kk];
+            d = j < i ? d : 0.f;
+            s_dA[i * kTS + j] = s_beta[z][i] * d;
+            float e = d * s_A[z][i * kTS + j];
+            e += __shfl_xor(e, 8);
+            e += __shfl_xor(e, 4);
+            e += __shfl_xor(e, 2);
+            e += __shfl_xor(e, 1);
+            if (j == 0) s_dbA[z][i] = e;
         }
-        if (rin) {
-            const int64_t off = (t0 + pr) * rowq + (int64_t)h * DK + ch0;
-            store8(a.dq + off, dq8);
-            store8(a.dk + off, dk8);
-            store8(a.dla + off, dl8);
+        lds_barrier();
+
+        // ---- D: the chunk-local terms, then the four operand gradients into LDS, channel block
+        // `wave` of both chunks (the value-phase tiles are dead: every wave has passed two
+        // barriers since reading them)
+        if (wave < KB) {
+            const int kc0 = 16 * cb;
+#pragma unroll
+            for (int y = 0; y < 2; ++y) {
+                if (y == 1 && !has_b) break;
+                const float* const sdA_y = &s_wv[y][1][0][0];  // Diag(beta) dA of chunk y
+                const f32x4 dPr = ld4(&s_dP[y][r * kTS + 4 * g]), dPc = ld4_col(s_dP[y], r, g);
+                const f32x4 dAr = ld4(&sdA_y[r * kTS + 4 * g]), dAc = ld4_col(sdA_y, r, g);
+                f32x4 KcB, QhB, KhB;  // B-fragments: X[4g + i][kc0 + r]
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int idx = (4 * g + i) * RS + kc0 + r;
+                    KcB[i] = s_Kc[y][idx];
+                    QhB[i] = s_Qh[y][idx];
+                    KhB[i] = s_Kh[y][idx];
+                }
+                const f32x4 dQh = M::run(dPr, KcB, aQ[y]);
+                const f32x4 dKh = M::run(dAr, KcB, -aK[y]);
+                const f32x4 dKc = M::run(dAc, KhB, M::run(dPc, QhB, zero4()));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int idx = (4 * g + i) * RS + kc0 + r;
+                    s_big[y][idx] = dQh[i];
+                    s_big[y][kC * WS + idx] = dKh[i];
+                    s_big[y][2 * kC * WS + idx] = dKc[i];
+                    s_big[y][3 * kC * WS + idx] = aB[y][i];
+                }
+            }
         }
+        lds_barrier();
+
+        // ---- E: dq, dk, and dlambda of this half's chunk by the reverse cumulative sum of dG over
+        // the rows, in the decay's row layout (the 16 lanes of a row hold the chunk's rows of 8
+        // channels)
+        {
+            const bool act = live && wq < NPC;
+            float dq8[8] = {}, dk8[8] = {}, dl8[8] = {};
+            if (act) {
+                const int idx = pr * RS + ch0;
+                float qh[8], kh[8], kc[8], dqh[8], dkh[8], dkc[8], dkb[8], gm[8], dgm[8];
+                load8(&s_Qh[z][idx], qh);
+                load8(&s_Kh[z][idx], kh);
+                load8(&s_Kc[z][idx], kc);
+                load8(&s_big[z][idx], dqh);
+                load8(&s_big[z][kC * WS + idx], dkh);
+                load8(&s_big[z][2 * kC * WS + idx], dkc);
+                load8(&s_big[z][3 * kC * WS + idx], dkb);
+                load8(&s_gamma[z][ch0], gm);
+                load8(&s_dgam[z][ch0], dgm);
+                float kbs[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    kbs[i] = kc[i] * gm[i] * dkb[i];  // Kb dKb
+                    dl8[i] = qh[i] * dqh[i] + kh[i] * dkh[i] - kc[i] * dkc[i] - kbs[i];  // dG
+                    const float e = __expf(Gp[i]), ei = __expf(-Gp[i]);
+                    dq8[i] = a.scale * e * dqh[i];
+                    dk8[i] = e * dkh[i] + ei * dkc[i] + gm[i] * ei * dkb[i];
+                }
+                // G_C is the last row's G (padding rows add no decay): row 15 also takes the
+                // gradient reaching G_C, the sum over rows of Kb dKb plus gamma dgamma
+                row_scan8(kbs);
+                float inc[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float tot_kb = row_last(kbs[i]);
+                    if (pr == 15) dl8[i] += tot_kb + gm[i] * dgm[i];
+                    inc[i] = dl8[i];
+                }
+                row_scan8(inc);  // inclusive sums over rows <= pr
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float rev = row_last(inc[i]) - inc[i] + dl8[i];  // sum over rows >= pr
+                    dl8[i] = (livep >> i) & 1u ? rev : 0.f;
+                }
+            }
+            // rows past Cp (all rows of a half without a chunk) fall outside the ranges
+            const int64_t qbytes = (int64_t)Cp * rowq * 4;
+            const uint32_t off = act ? (uint32_t)((pr * rowq + (int64_t)h * DK + ch0) * 4) : kDropped;
+            bstore8(out_rsrc(a.dq + t0 * rowq, qbytes), off, dq8);
+            bstore8(out_rsrc(a.dk + t0 * rowq, qbytes), off, dk8);
+            bstore8(out_rsrc(a.dla + t0 * rowq, qbytes), off, dl8);
+            const int hb = ht & (kC - 1);
+            bstore1(out_rsrc(a.dbeta + t0 * H, (int64_t)Cp * H * 4),
+                    ht < kC ? (uint32_t)((ht * H + h) * 4) : kDropped, s_dbT[z][hb] + s_dbA[z][hb]);
+        }
+        if (!more) break;
+        w = wn;
+        it = nx;
+        lds_barrier();  // the next item's tiles overwrite what this one's last phase read
     }
-    if (live && ht < Cp) a.dbeta[(t0 + ht) * H + h] = s_dbT[z][ht] + s_dbA[z][ht];
+#undef GRAD_THREAD_INDICES
 }
 
 template <typename T, int DK, int DV, int NCB, int ND>
@@ -1128,8 +1245,15 @@ hipError_t launch_typed(const BackwardArgs& p, hipStream_t st) {
     a.dq = p.dq; a.dk = p.dk_; a.dv = p.dv_; a.dla = p.dlog_alpha; a.dbeta = p.dbeta;
     a.dgate = p.dgate; a.H = p.H; a.N = p.num_seqs; a.floor_ = p.floor_; a.scale = p.scale;
     const int64_t slots = p.T_total / (2 * kC) + p.num_seqs;  // pair slots (T_total: the batch's tokens)
-    hipLaunchKernelGGL((grad_kernel<T, DK, DV>), dim3((unsigned)(slots * p.H)), dim3(64 * kGW), 0,
-                       st, a);
+    if (slots * p.H > 0x7fffffff) return hipErrorInvalidValue;
+    a.items = (int)(slots * p.H);
+    // one persistent workgroup per compute unit (the LDS allows no second)
+    int dev = 0, cus = 0;
+    e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const int grid = (int)std::min<int64_t>(a.items, std::max(cus, 1));
+    hipLaunchKernelGGL((grad_kernel<T, DK, DV>), dim3((unsigned)grid), dim3(64 * kGW), 0, st, a);
     return hipGetLastError();
 }
 

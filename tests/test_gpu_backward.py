@@ -114,6 +114,36 @@ def test_backward_bench_workload_sampled():
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_many_items_per_workgroup(dtype):
+    """More (pair of chunks, head) items than compute units (538 at H=8): each persistent
+    gradient workgroup takes several in turn, loading the next one's operands while it
+    finishes the current one.  Every (sequence, head) against the oracle."""
+    lengths = (700, 513, 250, 31, 0, 480)
+    log(f"backward many items per workgroup dtype={dtype} lengths={lengths} H=8")
+    x = ki.make_prefill_inputs(lengths, 8, 128, 128, dtype, 0.3, seed=81, device="cuda",
+                               log_alpha_min=-0.6)
+    g = torch.Generator().manual_seed(81)
+    do = torch.randn(x.v.shape, generator=g).to(x.v.dtype).cuda()
+    dSf = (torch.randn(x.initial_state.shape, generator=g) * 0.1).cuda()
+    run_case(x, do, dSf, floor=-0.4, scale=0.9)
+
+
+@pytest.mark.parametrize("n_seq", [100, 300])
+def test_backward_many_sequences(n_seq):
+    """Batches of 100 and 300 sequences of 0..40 tokens: the gradient kernel finds an item's
+    sequence among bounds held in registers (fewer than 256 sequences) or by a search of
+    cu_seqlens in memory (more)."""
+    rng = np.random.default_rng(n_seq)
+    lengths = tuple(int(v) for v in rng.integers(0, 41, n_seq))
+    log(f"backward {n_seq} sequences, {sum(lengths)} tokens")
+    x = ki.make_prefill_inputs(lengths, 1, 64, 64, "bf16", 0.3, seed=n_seq, device="cuda")
+    g = torch.Generator().manual_seed(n_seq)
+    do = torch.randn(x.v.shape, generator=g).to(x.v.dtype).cuda()
+    dSf = (torch.randn(x.initial_state.shape, generator=g) * 0.1).cuda()
+    run_case(x, do, dSf, floor=-0.3, scale=1.0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_backward_strongest_decay_floor(dtype):
     """Floor -5 with log-decays drawn down to -5: decay-folded operands span ~e^80 within a
     chunk (finite in fp32 and in bf16 hi/lo pairs)."""
