@@ -232,8 +232,9 @@ int32_t kda_prefill_segment_plan(const kda_params* params, const int32_t* cu_seq
  *   workspace       : device memory, 256-byte aligned, overlapping no other argument, of
  *                     workspace_bytes; receives, per pair of 16-token chunks and head, the
  *                     state entering the first and the gradient of the state leaving the
- *                     second (fp32, dk x dv each), and three 16 x dv fp32 blocks per chunk and
- *                     head passed from the walks to the gradients.  With
+ *                     second (fp32, dk x dv each), and three 16 x dv fp32 blocks and two
+ *                     16 x 16 ones per chunk and head passed from the walks to the
+ *                     gradients.  With
  *                     kda_prefill_backward_workspace(...) bytes the batch runs at once; with
  *                     less, the call runs groups of consecutive sequences one after another
  *                     on the stream, each as large as the workspace allows, and fails
@@ -241,8 +242,8 @@ int32_t kda_prefill_segment_plan(const kda_params* params, const int32_t* cu_seq
  *                     (kda_prefill_backward_workspace over that sequence alone).
  * The gradients are computed in fp32 with the 16-token chunk algebra of the forward: one
  * launch walks every sequence forwards (the states) and backwards (the state gradient) side
- * by side, a second forms the input gradients of each pair of chunks from those, all pairs
- * in parallel.
+ * by side, a second forms the input gradients of each pair of chunks from those (one
+ * persistent workgroup per compute unit taking the pairs in turn).
  */
 kda_status kda_prefill_backward(const kda_params* params, const void* q, const void* k,
                                 const void* v, const void* log_alpha, const void* beta,

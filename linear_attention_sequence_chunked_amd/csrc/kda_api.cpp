@@ -622,14 +622,15 @@ namespace {
 // Workspace of the backward over sequences [n0, n1): the state entering chunk 2j of sequence
 // n at pair slot (cu[n] - cu[n0])/32 + (n - n0) + j (at most (cu[n1] - cu[n0])/32 + n1 - n0
 // slots), then the gradient leaving chunk 2j + 1 (2j if it is the last) at the same slot, then
-// three [16][dv] arrays per chunk slot (cu[n] - cu[n0])/16 + (n - n0) + c (R, Y, dU).
+// three [16][dv] arrays per chunk slot (cu[n] - cu[n0])/16 + (n - n0) + c (R, Y, dU), then
+// per chunk slot the chunk's A'^T and X^T ([16][16] each).
 void bwd_group_size(const kda_params* params, const int32_t* cu, int32_t n0, int32_t n1,
                     uint64_t& bytes, uint64_t& grad_off, uint64_t& aux_stride) {
     const uint64_t H = params->num_heads, ss = (uint64_t)params->dk * params->dv;
     const uint64_t T = (uint64_t)(cu[n1] - cu[n0]), N = (uint64_t)(n1 - n0);
     grad_off = (T / 32 + N) * H * ss;
     aux_stride = (T / 16 + N) * H * 16 * (uint64_t)params->dv;
-    bytes = 4 * (2 * grad_off + 3 * aux_stride);
+    bytes = 4 * (2 * grad_off + 3 * aux_stride + (T / 16 + N) * H * 2 * 16 * 16);
 }
 
 kda_status bwd_size(const kda_params* params, const int32_t* cu, int32_t N, uint64_t& bytes,

@@ -122,44 +122,26 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// A' = strict_lower(Kh Kc^T) of the chunk (by the one wave with `active` set), then X and T
-// by forward substitution.  Every thread of the workgroup calls it (two barriers).
-template <int DK, int RS>
-__device__ __forceinline__ void chunk_gram(const float* s_Kh, const float* s_Kc,
-                                           const float* s_beta, float* s_A, float* s_X,
-                                           float* s_T, bool active, int lane) {
-    const int r = lane & 15, g = lane >> 4;
-    if (active) {
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int kb = 0; kb < DK / 16; ++kb)
-            acc = M::run(ld4(&s_Kh[r * RS + 16 * kb + 4 * g]), ld4(&s_Kc[r * RS + 16 * kb + 4 * g]), acc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = 4 * g + i;  // acc[i] = (Kh Kc^T)[row][r]
-            s_A[row * kTS + r] = r < row ? acc[i] : 0.f;
-        }
-    }
-    lds_barrier();
-    if (active && lane < 16) {  // column `lane` of X = (I + Diag(beta) A')^-1
-        const int col = lane;
-        float x[kC];
-#pragma unroll
-        for (int i = 0; i < kC; ++i) {
-            float d = 0.f;
-#pragma unroll
-            for (int j = 0; j < i; ++j) d += s_A[i * kTS + j] * x[j];
-            x[i] = (i == col ? 1.f : 0.f) - s_beta[i] * d;
-        }
-        const float bc = s_beta[col];
-#pragma unroll
-        for (int i = 0; i < kC; ++i) {
-            s_X[i * kTS + col] = x[i];
-            s_T[i * kTS + col] = x[i] * bc;
-        }
-    }
-    lds_barrier();
+// Raw buffer over [p, p + bytes): stores at offsets past the end are dropped by the range
+// check (no memory access), which masks rows without a branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(float* p, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)bytes, 0x00020000);
 }
+constexpr uint32_t kDropped = 0x80000000u;  // an offset past every output range
+__device__ __forceinline__ void bstore1(__amdgpu_buffer_rsrc_t rs, uint32_t off, float x) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rs, off, 0, 0);
+}
+__device__ __forceinline__ void bstore4(__amdgpu_buffer_rsrc_t rs, uint32_t off, f32x4 x) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rs, off, 0, 0);
+}
+__device__ __forceinline__ void bstore8(__amdgpu_buffer_rsrc_t rs, uint32_t off, const float (&x)[8]) {
+    bstore4(rs, off, f32x4{x[0], x[1], x[2], x[3]});
+    bstore4(rs, off + 16, f32x4{x[4], x[5], x[6], x[7]});
+}
+// Per chunk slot of the workspace, after the three [16][dv] arrays: A'^T then X^T, [16][16]
+// fp32 each, written by the forward walk for the gradient kernel
+constexpr int kGramFloats = 2 * kC * kC;
 
 // ---------------------------------------------------------------------------------------------
 // 1. The two sequential walks.  Blocks [0, half) run forwards, [half, 2 half) backwards.
@@ -349,6 +331,11 @@ __global__ __launch_bounds__(64 * (NCB + 1 + ND)) void walk_kernel(const WalkArg
 
     if (wave == NCB) {
         // ---------------- producer: Gram products and T, one step ahead of the consumers
+        // (the forward walk of the first value slice also stores A' and X of every chunk, for
+        // the gradient kernel: chunk slot (cu[n] - cu[0])/16 + n + c)
+        const bool keep = !rev && slice == 0;
+        float* const gram_out = a.aux + 3 * a.aux_stride + ((tbeg - a.cu[0]) / kC + n) * H * kGramFloats +
+                                (int64_t)h * kGramFloats;
         T rb[PF];
         auto fetch = [&](T& x, int it) {  // every lane loads (lanes 16.. repeat rows 0..15)
             x = a.beta[row_at(chunk_of(it), lane & 15) * H + h];
@@ -373,10 +360,12 @@ __global__ __launch_bounds__(64 * (NCB + 1 + ND)) void walk_kernel(const WalkArg
                                   kb0, kb1, accP2[u]);
             }
             const f32x4 accA = accA2[0] + accA2[1], accP = accP2[0] + accP2[1];
+            f32x4 am;  // lane (r, g) holds A'[4g + i][r]
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 4 * g + i;
-                s_A[row * kTS + r] = r < row ? accA[i] : 0.f;
+                am[i] = r < row ? accA[i] : 0.f;
+                s_A[row * kTS + r] = am[i];
             }
             {  // lane (r, g) holds P[4g + i][r]
                 f32x4 pm;
@@ -395,8 +384,8 @@ __global__ __launch_bounds__(64 * (NCB + 1 + ND)) void walk_kernel(const WalkArg
                 }
             }
             wave_lds_sync();
+            float xs[kC] = {};
             if (lane < 16) {  // column `lane` of X = (I + Diag(beta) A')^-1, then T = X Diag(beta)
-                float xs[kC];
 #pragma unroll
                 for (int i = 0; i < kC; ++i) {
                     float d = 0.f;
@@ -425,6 +414,17 @@ __global__ __launch_bounds__(64 * (NCB + 1 + ND)) void walk_kernel(const WalkArg
                         o.sq1[1][i * TSB + lane] = (bf16)(t[i] - (float)hi);
                     }
                 }
+            }
+            {  // A'^T (row r: lane (r, g) holds columns 4g..4g+3) and X^T (row `lane` < 16);
+               // issued by every producer, past the last chunk and where not kept into an
+               // empty range, so the producer's loads keep exact waits
+                const auto rs = out_rsrc(gram_out + (int64_t)chunk_of(it) * H * kGramFloats,
+                                         keep && it < nch ? kGramFloats * 4 : 0);
+                bstore4(rs, (uint32_t)(r * kC + 4 * g) * 4, am);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    bstore4(rs, lane < 16 ? (uint32_t)(kC * kC + lane * kC + 4 * j) * 4 : kDropped,
+                            f32x4{xs[4 * j], xs[4 * j + 1], xs[4 * j + 2], xs[4 * j + 3]});
             }
             wave_lds_sync();  // s_A and s_beta are rewritten by the next step
         };
@@ -686,23 +686,6 @@ __device__ __forceinline__ f32x4 ld4_colv(const float* X, int stride, int c0, in
                  X[(4 * g + 2) * stride + c0 + r], X[(4 * g + 3) * stride + c0 + r]};
 }
 
-// Raw buffer over [p, p + bytes): stores at offsets past the end are dropped by the range
-// check (no memory access), which masks rows without a branch.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(float* p, int64_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)bytes, 0x00020000);
-}
-constexpr uint32_t kDropped = 0x80000000u;  // an offset past every output range
-__device__ __forceinline__ void bstore1(__amdgpu_buffer_rsrc_t rs, uint32_t off, float x) {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rs, off, 0, 0);
-}
-__device__ __forceinline__ void bstore8(__amdgpu_buffer_rsrc_t rs, uint32_t off, const float (&x)[8]) {
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4 a = {__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])};
-    const u32x4 b = {__float_as_uint(x[4]), __float_as_uint(x[5]), __float_as_uint(x[6]), __float_as_uint(x[7])};
-    __builtin_amdgcn_raw_buffer_store_b128(a, rs, off, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b128(b, rs, off + 16, 0, 0);
-}
-
 // One item: the pair slot, its head, and where the pair sits in its sequence
 struct GradItem {
     int slot, h, n, jp, nch;
@@ -724,9 +707,9 @@ __global__ __launch_bounds__(64 * kGW, 1) void grad_kernel(const GradArgs<T> a) 
     // per wave: R and dU of the current value block, then the wave's parts of dT and dP
     __shared__ __attribute__((aligned(16))) float s_wv[2][kNW][2][16 * kTS];
     __shared__ __attribute__((aligned(16))) float s_A[2][16 * kTS], s_X[2][16 * kTS],
-        s_T[2][16 * kTS], s_dT[2][16 * kTS], s_dP[2][16 * kTS];
+        s_dT[2][16 * kTS], s_dP[2][16 * kTS];
     __shared__ __attribute__((aligned(16))) float s_gamma[2][DK], s_dgam[2][DK];
-    __shared__ float s_beta[2][kC], s_dbT[2][kC], s_dbA[2][kC];
+    __shared__ __attribute__((aligned(16))) float s_beta[2][kC], s_dbT[2][kC], s_dbA[2][kC];
 
     // (the wave index read from lane 0 is known wave-uniform: the output ranges built from it
     // are scalar registers)
@@ -820,6 +803,7 @@ __global__ __launch_bounds__(64 * kGW, 1) void grad_kernel(const GradArgs<T> a) 
     // and are masked.  Issued in the order the phases wait for them.
     uint4 wq4[NWD], wk[NWD], wl[NWD];
     T bt;
+    f32x4 xa4;  // four floats of the chunk's A'^T | X^T (threads 0..127 of the half; the rest repeat)
     f32x4 Rv[NA], Yv[NA], dUv[NA];
     T rdo[NA][4], rgt[NA][4];
     auto issue = [&](const GradItem& it, int tv) {
@@ -835,9 +819,10 @@ __global__ __launch_bounds__(64 * kGW, 1) void grad_kernel(const GradArgs<T> a) 
             wl[w] = *reinterpret_cast<const uint4*>(a.la + off + 4 * w);
         }
         bt = a.beta[(tld + min(ht & 15, Cld - 1)) * H + it.h];
+        const int64_t cslot = ((it.tbeg - cu0) / kC + it.n + (tld - it.tbeg) / kC) * H + it.h;
+        xa4 = ld4(a.aux + 3 * a.aux_stride + cslot * kGramFloats + 4 * (ht & 127));
         __builtin_amdgcn_sched_barrier(0);
-        const float* const ax =
-            a.aux + (((it.tbeg - cu0) / kC + it.n + (tld - it.tbeg) / kC) * H + it.h) * kC * DV;
+        const float* const ax = a.aux + cslot * kC * DV;
 #pragma unroll
         for (int ia = 0; ia < NA; ++ia) {
             const int col = 16 * (wq + kNW * ia) + r;
@@ -921,15 +906,21 @@ __global__ __launch_bounds__(64 * kGW, 1) void grad_kernel(const GradArgs<T> a) 
             if (pr == 15) store8(&s_gamma[z][ch0], gm);
         }
         if (live && ht < kC) s_beta[z][ht] = ht < Cp ? to_f32(bt) : 0.f;
+        if (live && ht < 128) {  // A' and X of the chunk, as the forward walk formed them
+            const int m = (ht & 63) >> 2, c0 = 4 * (ht & 3);  // row m of the transpose, columns c0..
+            float* const dst = ht < 64 ? s_A[z] : s_X[z];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[(c0 + e) * kTS + m] = xa4[e];
+        }
         lds_barrier();
-        // the Gram product and solve of chunk z by wave z of its half (waves 0 and 5: two SIMDs)
-        chunk_gram<DK, RS>(s_Kh[z], s_Kc[z], s_beta[z], s_A[z], s_X[z], s_T[z], live && wq == z, lane);
 
         // ---- A: value blocks of this half's chunk (wave wq takes blocks wq, wq + 4, ...).  A
         // half without a chunk runs it too, on stale tiles: its stores all fall outside the
         // (empty) output range and its LDS tiles are not read.
         {
-            const f32x4 Tr = ld4(&s_T[z][r * kTS + 4 * g]), Tc = ld4_col(s_T[z], r, g);  // T, T^T
+            // T = X Diag(beta) and T^T, A-fragments: T[r][4g + i] and T[4g + i][r]
+            const f32x4 Tr = ld4(&s_X[z][r * kTS + 4 * g]) * ld4(&s_beta[z][4 * g]);
+            const f32x4 Tc = ld4_col(s_X[z], r, g) * s_beta[z][r];
             bf16 *const Uh = vtile(z, 0, 0), *const Ul = vtile(z, 0, 1);
             bf16 *const dYh = vtile(z, 1, 0), *const dYl = vtile(z, 1, 1);
             bf16 *const dRh = vtile(z, 2, 0), *const dRl = vtile(z, 2, 1);

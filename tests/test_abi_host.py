@@ -274,12 +274,13 @@ def test_backward_workspace_size():
     slot cu[n]/32 + n + j (at most 100 // 32 + 3 = 6 slots per head; the sequences of 3, 0
     and 4 chunks take slots {0, 1} and {3, 4}), then the gradient leaving each odd chunk (or
     the last) at the same slots, then three [16][dv] vectors per chunk slot cu[n]/16 + n + c
-    (100 // 16 + 3 = 9) and head."""
+    (100 // 16 + 3 = 9) and head, then the chunk's A'^T and X^T ([16][16] each) per chunk
+    slot and head."""
     lib = _lib.load()
     p = _lib.params(_lib.KDA_DTYPE_BF16, 2, 64, 64)
     ss = 64 * 64 * 4
     assert lib.kda_prefill_backward_workspace(ctypes.byref(p), cu(0, 40, 40, 100), 3) == \
-        2 * 6 * 2 * ss + 3 * 9 * 2 * 16 * 64 * 4
+        2 * 6 * 2 * ss + 3 * 9 * 2 * 16 * 64 * 4 + 9 * 2 * 2 * 16 * 16 * 4
     assert lib.kda_prefill_backward_workspace(ctypes.byref(p), cu(0, 40, 30), 2) == -1
 
 
