@@ -511,8 +511,9 @@ def main() -> int:
             "tokens_per_s": bx.total_tokens / (bms * 1e-3), "forward_ms": fms,
             "vs_forward": bms / fms,
             "note": "chunk form, fp32 state and sums: forward and reverse chunk walks in one "
-                    "launch storing every other state and gradient, then all pairs of chunks "
-                    "in parallel (split-bf16 and fp32 MFMA); medians of launches each after "
+                    "launch storing every other state and gradient, then the pairs of chunks "
+                    "on persistent workgroups (split-bf16 and fp32 MFMA); medians of launches "
+                    "each after "
                     "the same cache flush as the forward's",
         }
         del bws, dout, bx, fout

@@ -29,10 +29,11 @@
 //   1. walk_kernel walks every (sequence, head, value slice) twice, as two halves of one
 //      grid that run side by side: forwards from the initial state, storing the state
 //      entering every even chunk, and backwards from dS_final, storing the gradient leaving
-//      every odd chunk and the last (dS in MFMA accumulators, as the forward keeps S);
-//   2. grad_kernel takes one (pair of chunks, head) per workgroup -- all pairs in parallel --
-//      re-forms the pair's other state and gradient from the chunk-local terms, and forms
-//      every input gradient of both chunks.
+//      every odd chunk and the last (dS in MFMA accumulators, as the forward keeps S); the
+//      forward walk also stores each chunk's A' and X;
+//   2. grad_kernel, one persistent workgroup per compute unit, takes the (pair of chunks,
+//      head) items in turn, re-forms each pair's other state and gradient from the
+//      chunk-local terms, and forms every input gradient of both chunks.
 // Whatever the input dtype, the state, its gradient and every sum are fp32: the products
 // over key channels or value columns are split-bf16 (three bf16 MFMAs per product, relative
 // error ~2^-17), the 16x16 chunk-local ones fp32 MFMAs (v_mfma_f32_16x16x4_f32).
