@@ -707,8 +707,7 @@ __global__ __launch_bounds__(64 * kGW, 1) void grad_kernel(const GradArgs<T> a) 
     __shared__ __attribute__((aligned(16))) float s_big[2][4 * kC * WS];
     // per wave: R and dU of the current value block, then the wave's parts of dT and dP
     __shared__ __attribute__((aligned(16))) float s_wv[2][kNW][2][16 * kTS];
-    __shared__ __attribute__((aligned(16))) float s_A[2][16 * kTS], s_X[2][16 * kTS],
-        s_dT[2][16 * kTS], s_dP[2][16 * kTS];
+    __shared__ __attribute__((aligned(16))) float s_A[2][16 * kTS], s_X[2][16 * kTS], s_dP[2][16 * kTS];
     __shared__ __attribute__((aligned(16))) float s_gamma[2][DK], s_dgam[2][DK];
     __shared__ __attribute__((aligned(16))) float s_beta[2][kC], s_dbT[2][kC], s_dbA[2][kC];
 
@@ -978,16 +977,53 @@ __global__ __launch_bounds__(64 * kGW, 1) void grad_kernel(const GradArgs<T> a) 
             }
         }
         lds_barrier();
-        if (live) {  // dT, dP: sums of the wave parts (one element per thread of the half)
-            const int i = ht >> 4, j = ht & 15;
-            float t = 0.f, p = 0.f;
+
+        // ---- C: the 16x16 algebra of chunk z, by wave z of its half (waves 0 and 5: two
+        // SIMDs) before its share of the sums over value columns, which the other waves start
+        // at once.  Fragments are in accumulator layout, element i of lane (r, g) = [4g + i][r]:
+        //   dT, dP = sums of the four wave parts (dP lower triangle incl. the diagonal);
+        //   M^T = dT^T X (its accumulator layout is the A-fragment of M = X^T dT), times beta
+        //   along M's columns gives M Diag(beta) = X^T dX;
+        //   dA = -strict_lower(M Diag(beta) X^T);  Diag(beta) dA for the operand products;
+        //   dbeta += colsum(X * dT) + rowsum(dA * A').
+        if (live && wq == z) {
+            f32x4 dT = zero4(), dP = zero4();
 #pragma unroll
             for (int w2 = 0; w2 < kNW; ++w2) {
-                t += s_wv[z][w2][0][i * kTS + j];
-                p += s_wv[z][w2][1][i * kTS + j];
+                dT += ld4_col(s_wv[z][w2][0], r, g);
+                dP += ld4_col(s_wv[z][w2][1], r, g);
             }
-            s_dT[z][i * kTS + j] = t;
-            s_dP[z][i * kTS + j] = j <= i ? p : 0.f;
+            const f32x4 Xc = ld4_col(s_X[z], r, g);                 // X[4g + i][r]
+            const f32x4 Xr = ld4(&s_X[z][r * kTS + 4 * g]);         // X[r][4g + i]
+            const f32x4 Ac = ld4_col(s_A[z], r, g);                 // A'[4g + i][r]
+            const f32x4 b4 = ld4(&s_beta[z][4 * g]);                // beta[4g + i]
+            const f32x4 Mb = M::run(dT, Xc, zero4()) * b4;          // (M Diag(beta))[r][4g + i]
+            const f32x4 nA = M::run(Mb, Xr, zero4());               // -dA[4g + i][r] (unmasked)
+            float* const sdA = &s_wv[z][1][0][0];  // Diag(beta) dA (after the parts are read)
+            float bT = 0.f;
+            f32x4 e;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 4 * g + i;
+                const float dA = r < row ? -nA[i] : 0.f;
+                s_dP[z][row * kTS + r] = r <= row ? dP[i] : 0.f;
+                sdA[row * kTS + r] = b4[i] * dA;
+                e[i] = dA * Ac[i];
+                bT += Xc[i] * dT[i];
+            }
+            // row sums of dA * A' over the 16 lanes of a row group; column sums of X * dT
+            // over the four row groups
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                e[i] += __shfl_xor(e[i], 8);
+                e[i] += __shfl_xor(e[i], 4);
+                e[i] += __shfl_xor(e[i], 2);
+                e[i] += __shfl_xor(e[i], 1);
+            }
+            bT += __shfl_xor(bT, 16);
+            bT += __shfl_xor(bT, 32);
+            if (r == 0) *reinterpret_cast<f32x4*>(&s_dbA[z][4 * g]) = e;
+            if (g == 0) s_dbT[z][r] = bT;
         }
 
         // ---- B: the sums over value columns, channel block `wave`, both chunks.  Chunk 2j uses
@@ -1073,42 +1109,9 @@ __global__ __launch_bounds__(64 * kGW, 1) void grad_kernel(const GradArgs<T> a) 
         issue(more ? nx : it, tv);
         lds_barrier();
 
-        // ---- C: the 16x16 algebra of this half's chunk (one element per thread: row i, column j)
-        float* const s_M = &s_wv[z][0][0][0];   // X^T dT Diag(beta), once the wave parts are summed
-        float* const s_dA = &s_wv[z][1][0][0];  // Diag(beta) dA
-        if (live) {
-            const int i = ht >> 4, j = ht & 15;
-            float m = 0.f;  // (X^T dT)[i][j] beta_j = (X^T dX)[i][j]
-#pragma unroll
-            for (int kk = 0; kk < kC; ++kk) m += s_X[z][kk * kTS + i] * s_dT[z][kk * kTS + j];
-            s_M[i * kTS + j] = m * s_beta[z][j];
-            if (ht < kC) {  // column sums of X * dT
-                float s = 0.f;
-#pragma unroll
-                for (int kk = 0; kk < kC; ++kk) s += s_X[z][kk * kTS + ht] * s_dT[z][kk * kTS + ht];
-                s_dbT[z][ht] = s;
-            }
-        }
-        lds_barrier();
-        if (live) {
-            const int i = ht >> 4, j = ht & 15;
-            float d = 0.f;  // dA[i][j] = -(M X^T)[i][j] on the strict lower triangle
-#pragma unroll
-            for (int kk = 0; kk < kC; ++kk) d -= s_M[i * kTS + kk] * s_X[z][j * kTS + kk];
-            d = j < i ? d : 0.f;
-            s_dA[i * kTS + j] = s_beta[z][i] * d;
-            float e = d * s_A[z][i * kTS + j];
-            e += __shfl_xor(e, 8);
-            e += __shfl_xor(e, 4);
-            e += __shfl_xor(e, 2);
-            e += __shfl_xor(e, 1);
-            if (j == 0) s_dbA[z][i] = e;
-        }
-        lds_barrier();
-
         // ---- D: the chunk-local terms, then the four operand gradients into LDS, channel block
-        // `wave` of both chunks (the value-phase tiles are dead: every wave has passed two
-        // barriers since reading them)
+        // `wave` of both chunks (over the value tiles: every wave's reads of them completed
+        // before the barrier)
         if (wave < KB) {
             const int kc0 = 16 * cb;
 #pragma unroll
