@@ -513,14 +513,14 @@ __global__ __launch_bounds__(64 * (NCB + 1 + ND)) void walk_kernel(const WalkArg
 #pragma unroll
                 for (int i = 0; i < 8; ++i) G[i] = in ? fmaxf(G[i], a.floor_) : 0.f;
                 row_scan8(G);
-                float qt[8], kt[8], kb[8], gm[8];
+                float qt[8], kt[8], kb[8], gc = 0.f;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const float GC = row_last(G[i]);  // G of the chunk's last row
                     const float d = G[i] - GC;        // >= 0
                     const float e = __expf(d), ei = __expf(-d);
                     const float qv = in ? xq[i] : 0.f, kv = in ? xk[i] : 0.f;
-                    gm[i] = __expf(GC);
+                    gc = (pr & 7) == i ? GC : gc;  // lane pr: the total of channel ch0 + (pr & 7)
                     qt[i] = a.scale * qv * e;
                     kt[i] = kv * e;
                     kb[i] = kv * ei;
@@ -529,7 +529,9 @@ __global__ __launch_bounds__(64 * (NCB + 1 + ND)) void walk_kernel(const WalkArg
                 store_split8(&o.kt[0][off], &o.kt[1][off], kt);
                 store_split8(&o.kb[0][off], &o.kb[1][off], kb);
                 store_split8(&o.qt[0][off], &o.qt[1][off], qt);
-                if (pr == 15) store8(&o.gamma[ch0], gm);
+                // gamma = e^G_C: one exponential per lane, lanes pr < 8 store one channel each
+                const float ge = __expf(gc);
+                if (pr < 8) o.gamma[ch0 + pr] = ge;
             }
         };
         // steps 0 .. nch + 1, one barrier each (the last two write buffers nobody reads).  The
@@ -877,10 +879,10 @@ __global__ __launch_bounds__(64 * kGW, 1) void grad_kernel(const GradArgs<T> a) 
         };
 
         const bool rin = pr < Cp;
-        float Gp[8] = {};
+        float eG[8] = {}, eGi[8] = {};  // e^G and e^-G of the wave's piece, kept for the last phase
         uint32_t livep = 0;
         if (live && wq < NPC) {
-            float xq[8], xk[8];
+            float xq[8], xk[8], Gp[8];
             unpack8<T>(wq4, xq);
             unpack8<T>(wk, xk);
             unpack8<T>(wl, Gp);
@@ -893,12 +895,13 @@ __global__ __launch_bounds__(64 * kGW, 1) void grad_kernel(const GradArgs<T> a) 
             float qh[8], kh[8], kc[8], gm[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const float e = __expf(Gp[i]), ei = __expf(-Gp[i]);
+                eG[i] = __expf(Gp[i]);
+                eGi[i] = __expf(-Gp[i]);
                 const float qv = rin ? xq[i] : 0.f, kv = rin ? xk[i] : 0.f;
-                gm[i] = __expf(row_last(Gp[i]));
-                qh[i] = a.scale * qv * e;
-                kh[i] = kv * e;
-                kc[i] = kv * ei;
+                gm[i] = row_last(eG[i]);  // gamma = e^G_C, G of the last row
+                qh[i] = a.scale * qv * eG[i];
+                kh[i] = kv * eG[i];
+                kc[i] = kv * eGi[i];
             }
             store8(&s_Qh[z][pr * RS + ch0], qh);
             store8(&s_Kh[z][pr * RS + ch0], kh);
@@ -1166,7 +1169,7 @@ __global__ __launch_bounds__(64 * kGW, 1) void grad_kernel(const GradArgs<T> a) 
                 for (int i = 0; i < 8; ++i) {
                     kbs[i] = kc[i] * gm[i] * dkb[i];  // Kb dKb
                     dl8[i] = qh[i] * dqh[i] + kh[i] * dkh[i] - kc[i] * dkc[i] - kbs[i];  // dG
-                    const float e = __expf(Gp[i]), ei = __expf(-Gp[i]);
+                    const float e = eG[i], ei = eGi[i];
                     dq8[i] = a.scale * e * dqh[i];
                     dk8[i] = e * dkh[i] + ei * dkc[i] + gm[i] * ei * dkb[i];
                 }
