@@ -39,6 +39,8 @@
 // error ~2^-17), the 16x16 chunk-local ones fp32 MFMAs (v_mfma_f32_16x16x4_f32).
 #include <math.h>
 
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -114,6 +116,11 @@ __device__ __forceinline__ void row_scan8(float (&x)[8]) {
     for (int j = 0; j < 8; ++j) x[j] += dpp<0x118>(x[j]);
 }
 __device__ __forceinline__ float row_last(float x) { return dpp<0x15F>(x); }  // lane 15 of the row
+// e^x as the fast exponential computes it, 2^(x log2 e) on v_exp_f32; e^x and e^-x from one
+// product t = x log2 e (the negated product is exact, so both equal the exponential of x
+// and of -x)
+constexpr float kLog2e = 1.44269504088896341f;
+__device__ __forceinline__ float exp2_(float t) { return __builtin_amdgcn_exp2f(t); }
 
 // Workgroup barrier that orders LDS only: __syncthreads() would also wait for every
 // outstanding global access, including loads issued a chunk ahead and the state stores.
@@ -486,10 +493,12 @@ __global__ __launch_bounds__(64 * (NCB + 1 + ND)) void walk_kernel(const WalkArg
                     x[p].l[w] = *reinterpret_cast<const uint4*>(a.la + off + 8 * p + 4 * w);
                 }
         };
-        auto decay = [&](const Piece (&x)[PPW], const VPiece& y, int s) {
+        // FULL: a chunk of 16 rows (every chunk but a sequence's last), with no row to mask
+        auto decay_body = [&](auto FULL, const Piece (&x)[PPW], const VPiece& y, int s) {
+            constexpr bool kFull = decltype(FULL)::value;
             B& o = s_buf[s % 3];
             const int Cp = rows_of(chunk_of(s));
-            const bool in = pr < Cp;
+            const bool in = kFull || pr < Cp;
             {  // the consumers' input, zero on rows past the end of the sequence
                 float xv[8];
                 unpack8<T>(y.v, xv);
@@ -501,7 +510,7 @@ __global__ __launch_bounds__(64 * (NCB + 1 + ND)) void walk_kernel(const WalkArg
                 }
                 float* const dst = &o.vin[vc * kTS + vr];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) dst[i * kTS] = vr < Cp ? xv[i] : 0.f;
+                for (int i = 0; i < 8; ++i) dst[i * kTS] = kFull || vr < Cp ? xv[i] : 0.f;
             }
 #pragma unroll
             for (int p = 0; p < PPW; ++p) {
@@ -517,8 +526,8 @@ __global__ __launch_bounds__(64 * (NCB + 1 + ND)) void walk_kernel(const WalkArg
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const float GC = row_last(G[i]);  // G of the chunk's last row
-                    const float d = G[i] - GC;        // >= 0
-                    const float e = __expf(d), ei = __expf(-d);
+                    const float t = (G[i] - GC) * kLog2e;  // >= 0, in base-2 units
+                    const float e = exp2_(t), ei = exp2_(-t);
                     const float qv = in ? xq[i] : 0.f, kv = in ? xk[i] : 0.f;
                     gc = (pr & 7) == i ? GC : gc;  // lane pr: the total of channel ch0 + (pr & 7)
                     qt[i] = a.scale * qv * e;
@@ -533,6 +542,10 @@ __global__ __launch_bounds__(64 * (NCB + 1 + ND)) void walk_kernel(const WalkArg
                 const float ge = __expf(gc);
                 if (pr < 8) o.gamma[ch0 + pr] = ge;
             }
+        };
+        auto decay = [&](const Piece (&x)[PPW], const VPiece& y, int s) {
+            if (rows_of(chunk_of(s)) == kC) decay_body(std::true_type{}, x, y, s);
+            else decay_body(std::false_type{}, x, y, s);
         };
         // steps 0 .. nch + 1, one barrier each (the last two write buffers nobody reads).  The
         // loads and the LDS writes run unconditionally, so that the memory-counter waits
@@ -895,8 +908,9 @@ __global__ __launch_bounds__(64 * kGW, 1) void grad_kernel(const GradArgs<T> a) 
             float qh[8], kh[8], kc[8], gm[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                eG[i] = __expf(Gp[i]);
-                eGi[i] = __expf(-Gp[i]);
+                const float t = Gp[i] * kLog2e;
+                eG[i] = exp2_(t);
+                eGi[i] = exp2_(-t);
                 const float qv = rin ? xq[i] : 0.f, kv = rin ? xk[i] : 0.f;
                 gm[i] = row_last(eG[i]);  // gamma = e^G_C, G of the last row
                 qh[i] = a.scale * qv * eG[i];
