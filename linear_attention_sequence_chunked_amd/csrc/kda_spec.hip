@@ -153,6 +153,7 @@ __global__ __launch_bounds__(kSpecThreads) void spec_kernel(const SArgs<T> a) {
                 for (int c = 0; c < 4; ++c) o[c] = from_f32<T>(s_g[j][4 * cg + c] * (b[c] + kq * u[c]));
             }
         }
+        if (VERIFY && j + 1 == steps) break;  // verify: the state after the last draft is not needed
 #pragma unroll
         for (int i = 0; i < RPT; ++i) s[i] += s_k[j][rg + ROWG * i] * u;
     }
