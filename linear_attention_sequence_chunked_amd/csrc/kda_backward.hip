@@ -67,15 +67,17 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 }
 
-// eight consecutive channels (16 bytes of bf16 or 32 of fp32) to floats
+// eight consecutive channels (16 bytes of bf16 or 32 of fp32) to floats.  bf16 values are
+// widened as conversions, not as bit moves, so that the compiler knows them to be canonical
+// floats: a max() on them then needs no quieting instruction first.
 template <typename T>
 __device__ __forceinline__ void unpack8(const uint4 (&w)[sizeof(T) / 2], float (&x)[8]) {
     if constexpr (sizeof(T) == 2) {
         const uint32_t u[4] = {w[0].x, w[0].y, w[0].z, w[0].w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            x[2 * i] = __uint_as_float(u[i] << 16);
-            x[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+            x[2 * i] = (float)__builtin_bit_cast(bf16, (uint16_t)(u[i] & 0xffffu));
+            x[2 * i + 1] = (float)__builtin_bit_cast(bf16, (uint16_t)(u[i] >> 16));
         }
     } else {
 #pragma unroll
