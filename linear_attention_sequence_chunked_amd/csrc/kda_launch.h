@@ -106,6 +106,9 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 bool prefill_bf16_supports(int dk, int dv, int nv, bool checkpoints);
 bool prefill_bf16_dual_supports(int dk, int dv);
+// whether the bf16-input prefill takes single fp16 operands (rather than bf16 hi/lo pairs)
+// at this log-decay floor (kda_plan.cpp)
+bool prefill_bf16_half(float log_alpha_floor);
 
 // value-slice width the prefill would pick for this problem (exposed for tests)
 int prefill_pick_nv(int dv, int64_t num_pairs, int64_t longest_chunks, int cu_count);

@@ -2,9 +2,24 @@
 // and fused passes the bf16 kernel implements, the slice width a launch uses, and when
 // the segmented schedule pays.  No device code: the C ABI's validation and planning can be
 // built and checked on a machine without a GPU.
+#include <cstdlib>
+
 #include "kda_launch.h"
 
 namespace kda {
+
+bool prefill_bf16_half(float log_alpha_floor) {
+    // Single fp16 operands (11 significant bits) meet the outputs' and states' tolerance
+    // without the bf16 hi/lo pairs, at a third of the matrix-core work of the state step.
+    // Their range is the limit: the decay-folded tiles Qt, Kt = (q, k) e^{G - G_C} reach
+    // e^{16 |floor|} times the inputs, so fp16 (largest finite value 65504) is taken only
+    // while that factor stays at or below e^8 ~ 2981, where unit-norm q and k (entries at
+    // most 1 in size) and entries up to ~20 stay finite.  KDA_PREFILL_HALF=0 forces the
+    // hi/lo form.
+    const char* env = std::getenv("KDA_PREFILL_HALF");
+    if (env && std::atoi(env) == 0) return false;
+    return log_alpha_floor >= -0.5f;
+}
 
 // value-slice widths the bf16 path implements for (dk, dv); the fused state-and-transition
 // workgroup of the segmented prefill needs dk == dv

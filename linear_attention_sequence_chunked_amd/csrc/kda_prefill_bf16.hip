@@ -64,6 +64,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -82,6 +84,27 @@ __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
 __device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
     return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
+// fp16 forms (v_mfma_f32_16x16x{16,32}_f16: the same issue cost and fragment layout as
+// the bf16 ones)
+__device__ __forceinline__ f32x4 mfma16h(f16x4 a, f16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma32h(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f16x8 cat8h(f16x4 a, f16x4 b) {
+    return f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+__device__ __forceinline__ f16x4 zero_h4() { return __builtin_bit_cast(f16x4, u32x2{0u, 0u}); }
+// round to fp16 pairwise (v_cvt_pk_f16_f32, round to nearest even)
+__device__ __forceinline__ f16x4 to_h4(f32x4 x) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    const f16x2 lo = __builtin_convertvector(f32x2{x[0], x[1]}, f16x2);
+    const f16x2 hi = __builtin_convertvector(f32x2{x[2], x[3]}, f16x2);
+    return __builtin_bit_cast(f16x4, u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)});
+}
+__device__ __forceinline__ f16x8 to_h8(f32x4 a, f32x4 b) { return cat8h(to_h4(a), to_h4(b)); }
 __device__ __forceinline__ bf16x4 zero_bf4() { return __builtin_bit_cast(bf16x4, u32x2{0u, 0u}); }
 // round to bf16 pairwise: the four-wide conversion of MFMA results is split by the
 // compiler into single conversions plus permutes; two-wide ones map to v_cvt_pk_bf16_f32
@@ -123,9 +146,12 @@ __device__ __forceinline__ void split4(f32x4 x, bf16x4& hi, bf16x4& lo) {
                   __builtin_amdgcn_fdot2_f32_bf16(h23, m1, x[3], false)};
     lo = to_bf4(d);
 }
-// C(L R) in bf16 from fp32 operands given as the A-fragment of L (== C(L^T)) and C(R)
+// C(L R) in bf16 (or fp16) from fp32 operands given as the A-fragment of L (== C(L^T))
+// and C(R)
+template <bool H16>
 __device__ __forceinline__ f32x4 prod(f32x4 aL, f32x4 cR) {
-    return mfma16(to_bf4(aL), to_bf4(cR), zero4());
+    if constexpr (H16) return mfma16h(to_h4(aL), to_h4(cR), zero4());
+    else return mfma16(to_bf4(aL), to_bf4(cR), zero4());
 }
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
@@ -168,6 +194,7 @@ __device__ __forceinline__ bf16x4 lds_tr(const unsigned char* p) {
     return __builtin_bit_cast(
         bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(const_cast<unsigned char*>(p))));
 }
+__device__ __forceinline__ f16x4 lds_trh(const unsigned char* p) { return __builtin_bit_cast(f16x4, lds_tr(p)); }
 template <typename T>
 __device__ __forceinline__ T lds_ld(const unsigned char* p) { return *reinterpret_cast<const T*>(p); }
 template <typename T>
@@ -286,7 +313,11 @@ struct BArgs {
 // state of the value columns from the given initial state, those of the second half the
 // columns of the identity with zero values, i.e. the chunk transitions' product; one pass
 // of key-side work serves both.
-template <int DK, int DV, int NCB, bool CK, bool OUT, bool DUAL>
+// H16: every product takes single fp16 operands (11-bit significands) in place of the bf16
+// hi/lo pairs, and the state's residual S' - hi is not formed.  The decay-folded tiles reach
+// e^{16 |floor|} times the inputs, so the host takes this form only while that stays well
+// inside the fp16 range (see prefill_bf16_half).
+template <int DK, int DV, int NCB, bool CK, bool OUT, bool DUAL, bool H16>
 __global__ __launch_bounds__((Cfg<DK, NCB, DUAL>::THREADS)) void prefill_bf16_kernel(const BArgs a) {
     typedef Cfg<DK, NCB, DUAL> C;
     static_assert(!DUAL || (!OUT && !CK && DK == DV), "the dual workgroup has no outputs");
@@ -456,7 +487,7 @@ __global__ __launch_bounds__((Cfg<DK, NCB, DUAL>::THREADS)) void prefill_bf16_ke
         // conflict-free row pattern, where two 8-byte halves 16 bytes apart conflict.
         const int jp = 2 * (g & 1) + (g >> 1);
         const int rowq = r * C::RSQ + 64 * w + 16 * jp, rowk = r * C::RSK + 64 * w + 16 * jp;
-        auto piece = [](bf16x4 a, bf16x4 b) {  // [quad 2g | quad 2g+1] -> the lane's piece
+        auto piece = [](auto a, auto b) {  // [quad 2g | quad 2g+1] -> the lane's piece
             const u32x2 x = __builtin_bit_cast(u32x2, a), y = __builtin_bit_cast(u32x2, b);
             const auto s0 = __builtin_amdgcn_permlane32_swap(x[0], y[0], false, false);
             const auto s1 = __builtin_amdgcn_permlane32_swap(x[1], y[1], false, false);
@@ -486,6 +517,7 @@ __global__ __launch_bounds__((Cfg<DK, NCB, DUAL>::THREADS)) void prefill_bf16_ke
 #pragma unroll
                 for (int j = 0; j < 8; ++j) GC[j] = row_last(G[j]);  // chunk totals
                 bf16x4 qh[2], ql[2], kbh[2], kbl[2], kt[2];
+                f16x4 qx[2], kbx[2], ktx[2];  // H16: single fp16 tiles
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
                     f32x4 F, Fi;
@@ -495,17 +527,29 @@ __global__ __launch_bounds__((Cfg<DK, NCB, DUAL>::THREADS)) void prefill_bf16_ke
                         F[i] = __builtin_amdgcn_exp2f(d);
                         Fi[i] = __builtin_amdgcn_exp2f(-d);
                     }
-                    if constexpr (OUT) split4(q4[hh] * F, qh[hh], ql[hh]);
-                    split4(k4[hh] * Fi, kbh[hh], kbl[hh]);
-                    kt[hh] = to_bf4(k4[hh] * F);
+                    if constexpr (H16) {
+                        if constexpr (OUT) qx[hh] = to_h4(q4[hh] * F);
+                        kbx[hh] = to_h4(k4[hh] * Fi);
+                        ktx[hh] = to_h4(k4[hh] * F);
+                    } else {
+                        if constexpr (OUT) split4(q4[hh] * F, qh[hh], ql[hh]);
+                        split4(k4[hh] * Fi, kbh[hh], kbl[hh]);
+                        kt[hh] = to_bf4(k4[hh] * F);
+                    }
                 }
-                if constexpr (OUT) {
-                    lds_st(L + C::L_QH + rowq, piece(qh[0], qh[1]));
-                    lds_st(L + C::L_QL + rowq, piece(ql[0], ql[1]));
+                if constexpr (H16) {
+                    if constexpr (OUT) lds_st(L + C::L_QH + rowq, piece(qx[0], qx[1]));
+                    lds_st(L + C::L_KBH + rowk, piece(kbx[0], kbx[1]));
+                    lds_st(kslot(c) + rowk, piece(ktx[0], ktx[1]));
+                } else {
+                    if constexpr (OUT) {
+                        lds_st(L + C::L_QH + rowq, piece(qh[0], qh[1]));
+                        lds_st(L + C::L_QL + rowq, piece(ql[0], ql[1]));
+                    }
+                    lds_st(L + C::L_KBH + rowk, piece(kbh[0], kbh[1]));
+                    lds_st(L + C::L_KBL + rowk, piece(kbl[0], kbl[1]));
+                    lds_st(kslot(c) + rowk, piece(kt[0], kt[1]));
                 }
-                lds_st(L + C::L_KBH + rowk, piece(kbh[0], kbh[1]));
-                lds_st(L + C::L_KBL + rowk, piece(kbl[0], kbl[1]));
-                lds_st(kslot(c) + rowk, piece(kt[0], kt[1]));
                 const float x01 = gb0 ? GC[1] : GC[0], x23 = gb0 ? GC[3] : GC[2];
                 const float x45 = gb0 ? GC[5] : GC[4], x67 = gb0 ? GC[7] : GC[6];
                 const float y0 = gb1 ? x23 : x01, y1 = gb1 ? x67 : x45;
@@ -542,10 +586,17 @@ __global__ __launch_bounds__((Cfg<DK, NCB, DUAL>::THREADS)) void prefill_bf16_ke
 #pragma unroll
                 for (int p = 0; p < KP; ++p) {
                     const int off = r * C::RSK + 2 * (32 * p + 8 * g);
-                    const bf16x8 kt = lds_ld<bf16x8>(Kt + off);
-                    const bf16x8 kb = lds_ld<bf16x8>(Kb + off);
-                    ac = mfma32(kt, kb, ac);    // C(Kt Kb^T)
-                    atc = mfma32(kb, kt, atc);  // C(Kb Kt^T)
+                    if constexpr (H16) {
+                        const f16x8 kt = lds_ld<f16x8>(Kt + off);
+                        const f16x8 kb = lds_ld<f16x8>(Kb + off);
+                        ac = mfma32h(kt, kb, ac);
+                        atc = mfma32h(kb, kt, atc);
+                    } else {
+                        const bf16x8 kt = lds_ld<bf16x8>(Kt + off);
+                        const bf16x8 kb = lds_ld<bf16x8>(Kb + off);
+                        ac = mfma32(kt, kb, ac);    // C(Kt Kb^T)
+                        atc = mfma32(kb, kt, atc);  // C(Kb Kt^T)
+                    }
                 }
                 const float* beta = reinterpret_cast<const float*>(bslot(c));
                 const float br = beta[r];
@@ -558,19 +609,20 @@ __global__ __launch_bounds__((Cfg<DK, NCB, DUAL>::THREADS)) void prefill_bf16_ke
                     cAT[i] = row < r ? br * atc[i] : 0.f;
                 }
                 // A-fragment(X) == C(X^T): powers of A and of A^T in both layouts
-                const f32x4 cA2 = prod(cAT, cA);      // C(A A)
-                const f32x4 cAT2 = prod(cA, cAT);     // C(A^T A^T)
-                const f32x4 cA4 = prod(cAT2, cA2);
-                const f32x4 cAT4 = prod(cA2, cAT2);
-                const f32x4 cAT8 = prod(cA4, cAT4);
+                const f32x4 cA2 = prod<H16>(cAT, cA);      // C(A A)
+                const f32x4 cAT2 = prod<H16>(cA, cAT);     // C(A^T A^T)
+                const f32x4 cA4 = prod<H16>(cAT2, cA2);
+                const f32x4 cAT4 = prod<H16>(cA2, cAT2);
+                const f32x4 cAT8 = prod<H16>(cA4, cAT4);
                 f32x4 y = cAT8;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) y[i] += (4 * g + i) == r ? 1.f : 0.f;  // I + (A^T)^8
-                y += prod(cA4, y);   // (I + (A^T)^4) y
-                y += prod(cA2, y);   // (I + (A^T)^2) y
-                y -= prod(cA, y);    // (I - A^T) y   ->  X^T = ((I + A)^-1)^T
+                y += prod<H16>(cA4, y);   // (I + (A^T)^4) y
+                y += prod<H16>(cA2, y);   // (I + (A^T)^2) y
+                y -= prod<H16>(cA, y);    // (I - A^T) y   ->  X^T = ((I + A)^-1)^T
                 // C(T^T), rows scaled by beta, as the lower half of a 32-deep operand
-                lds_st(gslot(c) + C::G_TT + lane * 16, cat8(to_bf4(y * bi), zero_bf4()));
+                if constexpr (H16) lds_st(gslot(c) + C::G_TT + lane * 16, cat8h(to_h4(y * bi), zero_h4()));
+                else lds_st(gslot(c) + C::G_TT + lane * 16, cat8(to_bf4(y * bi), zero_bf4()));
             }
             lds_barrier();
         }
@@ -583,6 +635,14 @@ __global__ __launch_bounds__((Cfg<DK, NCB, DUAL>::THREADS)) void prefill_bf16_ke
                 if (OUT && c >= 0 && c < nch) {
                     const unsigned char* L = lslot(c);
                     f32x4 acc = zero4();
+                    if constexpr (H16) {
+#pragma unroll
+                        for (int p = 0; p < KP; ++p) {
+                            const int offk = r * C::RSK + 2 * (32 * p + 8 * g);
+                            const int offq = r * C::RSQ + 2 * (32 * p + 8 * g);
+                            acc = mfma32h(lds_ld<f16x8>(L + C::L_KBH + offk), lds_ld<f16x8>(L + C::L_QH + offq), acc);
+                        }
+                    } else {
 #pragma unroll
                     for (int p = 0; p < KP; ++p) {
                         const int offk = r * C::RSK + 2 * (32 * p + 8 * g);
@@ -595,12 +655,17 @@ __global__ __launch_bounds__((Cfg<DK, NCB, DUAL>::THREADS)) void prefill_bf16_ke
                         acc = mfma32(kbh, ql, acc);
                         acc = mfma32(kbl, qh, acc);
                     }
+                    }
                     // acc[i] = P[r][4g+i]; keep the causal part (key position <= query position)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) acc[i] = (4 * g + i) <= r ? acc[i] : 0.f;
-                    bf16x4 ph_, pl_;
-                    split4(acc, ph_, pl_);
-                    lds_st(gslot(c) + C::G_P + lane * 16, cat8(ph_, pl_));
+                    if constexpr (H16) {  // P in the lower half of a 32-deep operand
+                        lds_st(gslot(c) + C::G_P + lane * 16, cat8h(to_h4(acc), zero_h4()));
+                    } else {
+                        bf16x4 ph_, pl_;
+                        split4(acc, ph_, pl_);
+                        lds_st(gslot(c) + C::G_P + lane * 16, cat8(ph_, pl_));
+                    }
                 }
             }
             {
@@ -619,8 +684,14 @@ __global__ __launch_bounds__((Cfg<DK, NCB, DUAL>::THREADS)) void prefill_bf16_ke
                     for (int nb = 0; nb < KB; ++nb) ktt[nb] = lds_tr(Kt + tr_blk(nb));
 #pragma unroll
                     for (int nb = 0; nb < KB; ++nb) {
-                        const f32x4 w = mfma16(ktt[nb], ntt, zero4());  // -Wt[r][16nb + 4g + i]
-                        lds_st(W + C::W_WT + (nb >> 1) * 1024 + lane * 16 + (nb & 1) * 8, to_bf4(w));
+                        unsigned char* dst = W + C::W_WT + (nb >> 1) * 1024 + lane * 16 + (nb & 1) * 8;
+                        if constexpr (H16) {  // (the sign flip above is the same bit in fp16)
+                            const f32x4 w = mfma16h(__builtin_bit_cast(f16x4, ktt[nb]), __builtin_bit_cast(f16x4, ntt), zero4());
+                            lds_st(dst, to_h4(w));
+                        } else {
+                            const f32x4 w = mfma16(ktt[nb], ntt, zero4());  // -Wt[r][16nb + 4g + i]
+                            lds_st(dst, to_bf4(w));
+                        }
                     }
                 }
             }
@@ -685,19 +756,22 @@ __global__ __launch_bounds__((Cfg<DK, NCB, DUAL>::THREADS)) void prefill_bf16_ke
                 // (the scheduling barriers keep each step's reads ahead of the previous
                 // step's products), so LDS latency overlaps the matrix core instead of
                 // stalling it once per step.
-                struct Ops { bf16x8 wt, qh, ql; };
+                // (with H16 the operands are fp16 and Qt has no lo half)
+                typedef std::conditional_t<H16, f16x8, bf16x8> E8;
+                struct Ops { E8 wt, qh, ql; };
                 auto ldp = [&](int p) {
                     Ops o;
-                    o.wt = lds_ld<bf16x8>(W + C::W_WT + p * 1024 + lane * 16);
+                    o.wt = lds_ld<E8>(W + C::W_WT + p * 1024 + lane * 16);
                     if constexpr (OUT) {
                         const int off = r * C::RSQ + 2 * (32 * p + 8 * g);
-                        o.qh = lds_ld<bf16x8>(L + C::L_QH + off);
-                        o.ql = lds_ld<bf16x8>(L + C::L_QL + off);
+                        o.qh = lds_ld<E8>(L + C::L_QH + off);
+                        if constexpr (!H16) o.ql = lds_ld<E8>(L + C::L_QL + off);
                     }
                     return o;
                 };
-                auto ldk = [&](int b) {  // Kb^T fragments of row block b, hi | lo
-                    return cat8(lds_tr(L + C::L_KBH + tr_k + tr_blk(b)), lds_tr(L + C::L_KBL + tr_k + tr_blk(b)));
+                auto ldk = [&](int b) {  // Kb^T fragments of row block b, hi | lo (fp16 | 0)
+                    if constexpr (H16) return cat8h(lds_trh(L + C::L_KBH + tr_k + tr_blk(b)), zero_h4());
+                    else return cat8(lds_tr(L + C::L_KBH + tr_k + tr_blk(b)), lds_tr(L + C::L_KBL + tr_k + tr_blk(b)));
                 };
                 // the next chunk's gamma (its decay tiles were written three iterations ago;
                 // past the last chunk the decay waves store gamma = 1)
@@ -705,7 +779,7 @@ __global__ __launch_bounds__((Cfg<DK, NCB, DUAL>::THREADS)) void prefill_bf16_ke
                 auto ldg = [&](int b) { return *reinterpret_cast<const f32x4*>(gn + 16 * b + 4 * g); };
                 // Ut = T V: T^T is stored with a zero upper half (one 32-deep step; each
                 // accumulator is fed by one instruction shape only)
-                const bf16x8 tt0 = lds_ld<bf16x8>(Gs + C::G_TT + lane * 16);
+                const E8 tt0 = lds_ld<E8>(Gs + C::G_TT + lane * 16);
                 bf16x4 vt[CPW];
 #pragma unroll
                 for (int cb = 0; cb < CPW; ++cb)  // columns of the identity have zero values
@@ -715,7 +789,10 @@ __global__ __launch_bounds__((Cfg<DK, NCB, DUAL>::THREADS)) void prefill_bf16_ke
                 f32x4 U[CPW], O[CPW];
 #pragma unroll
                 for (int cb = 0; cb < CPW; ++cb) {
-                    U[cb] = mfma32(tt0, cat8(vt[cb], zero_bf4()), zero4());
+                    if constexpr (H16)  // V rounded to fp16 (exact within the fp16 range)
+                        U[cb] = mfma32h(tt0, cat8h(to_h4(to_f4(vt[cb])), zero_h4()), zero4());
+                    else
+                        U[cb] = mfma32(tt0, cat8(vt[cb], zero_bf4()), zero4());
                     O[cb] = zero4();
                 }
                 unroll<0, KP>([&](auto PI) {  // channel blocks 2p, 2p+1 stacked
@@ -724,36 +801,53 @@ __global__ __launch_bounds__((Cfg<DK, NCB, DUAL>::THREADS)) void prefill_bf16_ke
                     Ops& nxt = (p & 1) ? o0 : o1;
                     if constexpr (p + 1 < KP) nxt = ldp(p + 1);
                     __builtin_amdgcn_sched_barrier(0);
+                    if constexpr (H16) {
 #pragma unroll
-                    for (int cb = 0; cb < CPW; ++cb) {  // S holds S' = Diag(gamma) S already
-                        const bf16x8 sh = to_bf8(S[cb][2 * p], S[cb][2 * p + 1]);
-                        U[cb] = mfma32(cur.wt, sh, U[cb]);  // U = Ut - Wt S'
-                        if constexpr (OUT) {
-                            const bf16x8 sl = to_bf8(mfma32(nid_lo, sh, S[cb][2 * p]),       // S' - hi
-                                                     mfma32(nid_hi, sh, S[cb][2 * p + 1]));
-                            O[cb] = mfma32(cur.qh, sh, O[cb]);  // O = Qt S': qh sh + ql sh + qh sl
-                            O[cb] = mfma32(cur.ql, sh, O[cb]);
-                            O[cb] = mfma32(cur.qh, sl, O[cb]);
+                        for (int cb = 0; cb < CPW; ++cb) {  // one fp16 copy of S'
+                            const f16x8 sx = to_h8(S[cb][2 * p], S[cb][2 * p + 1]);
+                            U[cb] = mfma32h(cur.wt, sx, U[cb]);
+                            if constexpr (OUT) O[cb] = mfma32h(cur.qh, sx, O[cb]);
+                        }
+                    } else {
+#pragma unroll
+                        for (int cb = 0; cb < CPW; ++cb) {  // S holds S' = Diag(gamma) S already
+                            const bf16x8 sh = to_bf8(S[cb][2 * p], S[cb][2 * p + 1]);
+                            U[cb] = mfma32(cur.wt, sh, U[cb]);  // U = Ut - Wt S'
+                            if constexpr (OUT) {
+                                const bf16x8 sl = to_bf8(mfma32(nid_lo, sh, S[cb][2 * p]),       // S' - hi
+                                                         mfma32(nid_hi, sh, S[cb][2 * p + 1]));
+                                O[cb] = mfma32(cur.qh, sh, O[cb]);  // O = Qt S': qh sh + ql sh + qh sl
+                                O[cb] = mfma32(cur.ql, sh, O[cb]);
+                                O[cb] = mfma32(cur.qh, sl, O[cb]);
+                            }
                         }
                     }
                 });
-                const bf16x8 pp = OUT ? lds_ld<bf16x8>(Gs + C::G_P + lane * 16) : tt0;  // P hi | P lo
-                bf16x8 k0 = ldk(0), k1;
+                const E8 pp = OUT ? lds_ld<E8>(Gs + C::G_P + lane * 16) : tt0;  // P hi | P lo (fp16 | 0)
+                E8 k0 = ldk(0), k1;
                 f32x4 gm0 = ldg(0), gm1;
                 __builtin_amdgcn_sched_barrier(0);
-                bf16x8 uu[CPW];
+                E8 uu[CPW];
                 bf16x4 ul[CPW];
 #pragma unroll
                 for (int cb = 0; cb < CPW; ++cb) {
-                    bf16x4 uh;
-                    split4(U[cb], uh, ul[cb]);
-                    uu[cb] = cat8(uh, uh);
+                    if constexpr (H16) {
+                        uu[cb] = cat8h(to_h4(U[cb]), zero_h4());
+                    } else {
+                        bf16x4 uh;
+                        split4(U[cb], uh, ul[cb]);
+                        uu[cb] = cat8(uh, uh);
+                    }
                 }
                 if constexpr (OUT) {
 #pragma unroll
                     for (int cb = 0; cb < CPW; ++cb) {
-                        O[cb] = mfma32(pp, uu[cb], O[cb]);                      // + P U: ph uh + pl uh
-                        O[cb] = mfma32(pp, cat8(ul[cb], zero_bf4()), O[cb]);   //        + ph ul
+                        if constexpr (H16) {
+                            O[cb] = mfma32h(pp, uu[cb], O[cb]);                    // + P U
+                        } else {
+                            O[cb] = mfma32(pp, uu[cb], O[cb]);                      // + P U: ph uh + pl uh
+                            O[cb] = mfma32(pp, cat8(ul[cb], zero_bf4()), O[cb]);   //        + ph ul
+                        }
                     }
                 }
                 // S <- S' + Kb^T U, row block by row block: kh uh + kl uh, then kh ul.  Then
@@ -762,15 +856,19 @@ __global__ __launch_bounds__((Cfg<DK, NCB, DUAL>::THREADS)) void prefill_bf16_ke
                 // the snapshot instead.
                 unroll<0, KB>([&](auto BI) {
                     constexpr int b = decltype(BI)::value;
-                    bf16x8& kc = (b & 1) ? k1 : k0;
-                    bf16x8& kn = (b & 1) ? k0 : k1;
+                    E8& kc = (b & 1) ? k1 : k0;
+                    E8& kn = (b & 1) ? k0 : k1;
                     f32x4& gp = (b & 1) ? gm0 : gm1;  // gamma of block b - 1
                     if constexpr (b + 1 < KB) kn = ldk(b + 1);
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int cb = 0; cb < CPW; ++cb) {
-                        S[cb][b] = mfma32(kc, uu[cb], S[cb][b]);
-                        S[cb][b] = mfma32(kc, cat8(ul[cb], zero_bf4()), S[cb][b]);
+                        if constexpr (H16) {
+                            S[cb][b] = mfma32h(kc, uu[cb], S[cb][b]);
+                        } else {
+                            S[cb][b] = mfma32(kc, uu[cb], S[cb][b]);
+                            S[cb][b] = mfma32(kc, cat8(ul[cb], zero_bf4()), S[cb][b]);
+                        }
                     }
                     if constexpr (!CK && b > 0) {
 #pragma unroll
@@ -835,7 +933,7 @@ __global__ __launch_bounds__((Cfg<DK, NCB, DUAL>::THREADS)) void prefill_bf16_ke
     }
 }
 
-template <int DK, int DV, int NCB, bool CK, bool OUT, bool DUAL = false>
+template <int DK, int DV, int NCB, bool CK, bool OUT, bool DUAL, bool H16>
 hipError_t launch_bf16(const PrefillArgs& p, hipStream_t st) {
     typedef Cfg<DK, NCB, DUAL> C;
     static_assert(C::LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -853,22 +951,27 @@ hipError_t launch_bf16(const PrefillArgs& p, hipStream_t st) {
     if (a.num_groups == 0) return hipSuccess;
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)prefill_bf16_kernel<DK, DV, NCB, CK, OUT, DUAL>,
+        hipError_t e = hipFuncSetAttribute((const void*)prefill_bf16_kernel<DK, DV, NCB, CK, OUT, DUAL, H16>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL((prefill_bf16_kernel<DK, DV, NCB, CK, OUT, DUAL>), dim3((unsigned)blocks), dim3(C::THREADS),
+    hipLaunchKernelGGL((prefill_bf16_kernel<DK, DV, NCB, CK, OUT, DUAL, H16>), dim3((unsigned)blocks), dim3(C::THREADS),
                        C::LDS_BYTES, st, a);
     return hipGetLastError();
 }
 
-template <int DK, int DV, int NCB>
-hipError_t launch_ck(const PrefillArgs& p, hipStream_t st) {
+template <int DK, int DV, int NCB, bool H16>
+hipError_t launch_ck_h(const PrefillArgs& p, hipStream_t st) {
     // snapshots come with outputs only (the variant without outputs serves the segmented
     // prefill's state and transition passes)
-    if (p.checkpoints) return launch_bf16<DK, DV, NCB, true, true>(p, st);
-    return p.out ? launch_bf16<DK, DV, NCB, false, true>(p, st) : launch_bf16<DK, DV, NCB, false, false>(p, st);
+    if (p.checkpoints) return launch_bf16<DK, DV, NCB, true, true, false, H16>(p, st);
+    return p.out ? launch_bf16<DK, DV, NCB, false, true, false, H16>(p, st)
+                 : launch_bf16<DK, DV, NCB, false, false, false, H16>(p, st);
+}
+template <int DK, int DV, int NCB>
+hipError_t launch_ck(const PrefillArgs& p, hipStream_t st) {
+    return prefill_bf16_half(p.floor_) ? launch_ck_h<DK, DV, NCB, true>(p, st) : launch_ck_h<DK, DV, NCB, false>(p, st);
 }
 
 }  // namespace
@@ -876,8 +979,13 @@ hipError_t launch_ck(const PrefillArgs& p, hipStream_t st) {
 // value-slice widths this path supports for (dk, dv)
 hipError_t launch_prefill_bf16(const PrefillArgs& p, hipStream_t st) {
     if (p.dual) {  // state and transition passes of the segmented prefill, fused
-        if (p.dk == 128 && p.dv == 128) return launch_bf16<128, 128, 16, false, false, true>(p, st);
-        if (p.dk == 64 && p.dv == 64) return launch_bf16<64, 64, 8, false, false, true>(p, st);
+        const bool h = prefill_bf16_half(p.floor_);
+        if (p.dk == 128 && p.dv == 128)
+            return h ? launch_bf16<128, 128, 16, false, false, true, true>(p, st)
+                     : launch_bf16<128, 128, 16, false, false, true, false>(p, st);
+        if (p.dk == 64 && p.dv == 64)
+            return h ? launch_bf16<64, 64, 8, false, false, true, true>(p, st)
+                     : launch_bf16<64, 64, 8, false, false, true, false>(p, st);
         return hipErrorInvalidValue;
     }
 #define KDA_NV_CASES(DK, DV)                                          \

@@ -194,3 +194,34 @@ def test_strongest_decay_floor(dtype):
     x = ki.make_prefill_inputs((40, 64, 17), 2, 128, 128, dtype, 0.3, seed=55, device="cuda",
                                log_alpha_min=-5.0)
     check_full(x, dtype, log_alpha_floor=-5.0)
+
+
+@pytest.mark.parametrize("half", ["1", "0"])
+def test_both_precision_forms(half, monkeypatch):
+    """At floors >= -0.5 the bf16-input prefill takes single fp16 operands; KDA_PREFILL_HALF=0
+    forces the bf16 hi/lo pairs instead.  Both forms against the oracle on varlen input with
+    ragged chunks and clamped decays, at the full and a quarter slice width."""
+    log(f"prefill precision form half={half}")
+    monkeypatch.setenv("KDA_PREFILL_HALF", half)
+    x = ki.make_prefill_inputs((300, 0, 17, 1024, 48), 4, 128, 128, "bf16", 0.05, seed=91,
+                               device="cuda", log_alpha_min=-1.0)
+    for nv in ("128", "32"):
+        monkeypatch.setenv("KDA_PREFILL_NV", nv)
+        check_full(x, "bf16", log_alpha_floor=-0.4)
+
+
+def test_half_form_at_its_range_edge():
+    """The fp16 form's range: with every log-decay clamped at the floor -0.5, the decay-folded
+    query rows reach e^{7.5} ~ 1808 times q; q is a one-hot of size 20 per token (entries up
+    to 20, ~36,000 after folding, inside fp16's 65504), k unit-norm."""
+    log("prefill fp16 range edge: |q| = 20 one-hot, all decays at the floor -0.5")
+    x = ki.make_prefill_inputs((160, 37), 2, 128, 128, "bf16", 0.05, seed=92, device="cuda")
+    T, H, d = x.total_tokens, 2, 128
+    idx = torch.arange(T * H, device="cuda") % d
+    q = torch.zeros(T * H, d, device="cuda")
+    q[torch.arange(T * H, device="cuda"), idx] = 20.0
+    la = torch.full_like(x.log_alpha, -3.0)
+    xe = ki.KdaInputs(q.view(T, H, d).to(torch.bfloat16), x.k, x.v, la, x.beta, x.gate,
+                      x.cu_seqlens, x.cu_seqlens_host, x.initial_state)
+    o, S = check_full(xe, "bf16", log_alpha_floor=-0.5)
+    assert torch.isfinite(o.float()).all()
