@@ -224,9 +224,11 @@ def prefill_record(w, x, times_ms, wall, segment_len=0):
         rec["roofline"]["traffic_source"] = os.path.relpath(traffic_file(w.name), ROOT)
     mc = stored_summary(mfma_file(w.name), w.name, src)
     if mc is not None:  # rocprofv3 MFMA counters of the same kernel, this launch's time
-        ex = mc["executed_bf16_flops_per_launch"]
+        ex = mc["executed_mfma_flops_per_launch"]
         rec["mfma"]["rocprof"] = {
-            "executed_bf16_flops_per_launch": ex,
+            "executed_mfma_flops_per_launch": ex,
+            "executed_bf16_flops_per_launch": mc["executed_bf16_flops_per_launch"],
+            "executed_f16_flops_per_launch": mc["executed_f16_flops_per_launch"],
             "executed_TFLOPs": ex / (ms * 1e-3) / 1e12,
             "executed_frac": ex / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
             "mfma_busy_frac": mc["mfma_busy_frac"],
@@ -622,8 +624,9 @@ def summarize(args) -> int:
     WRITE_SIZE runs of `bench.py --steps S` and of `bench.py --copy-calibration`): HBM
     bytes per launch of the last S launches, each counter scaled by the factor that makes it
     read exactly 1 GiB for the plain 1 GiB copy.
-    mfma: --pmc-dirs DIR (SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES
-    GRBM_GUI_ACTIVE): executed bf16 MFMA flops and the MFMA busy fraction.
+    mfma: --pmc-dirs DIR (SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F16
+    SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE): executed bf16 and fp16 MFMA flops and the
+    MFMA busy fraction.
     trace: --pmc-dirs DIR (--kernel-trace --stats): per-kernel call counts and durations."""
     import numpy as np
     import kda_inputs as ki
@@ -668,22 +671,26 @@ def summarize(args) -> int:
     elif args.summarize == "mfma":
         c, dur, names = (_read_steps if args.per_step else _read_counters)(args.pmc_dirs, args.kernel)
         mops = float(np.mean(c["SQ_INSTS_VALU_MFMA_MOPS_BF16"][-steps:]))
+        mops16 = float(np.mean(c["SQ_INSTS_VALU_MFMA_MOPS_F16"][-steps:]))
         busy = float(np.mean(c["SQ_VALU_MFMA_BUSY_CYCLES"][-steps:]))
         act = float(np.mean(c["GRBM_GUI_ACTIVE"][-steps:]))
         us = float(np.mean(dur[-steps:]))
-        ex = mops * 512
+        ex = (mops + mops16) * 512
         res.update({"kernel": names[-1], "dispatches": steps,
                     "SQ_INSTS_VALU_MFMA_MOPS_BF16_per_launch": mops,
+                    "SQ_INSTS_VALU_MFMA_MOPS_F16_per_launch": mops16,
                     "SQ_VALU_MFMA_BUSY_CYCLES_per_launch": busy,
                     "GRBM_GUI_ACTIVE_per_launch": act,
                     "kernel_duration_us_under_counters": us,
-                    "executed_bf16_flops_per_launch": ex,
+                    "executed_bf16_flops_per_launch": mops * 512,
+                    "executed_f16_flops_per_launch": mops16 * 512,
+                    "executed_mfma_flops_per_launch": ex,
                     "mfma_busy_frac": busy / (act * 1024 / 8) if act else None})
         if w is not None:
             _, alg_f = prefill_algorithmic(w.lengths, w.H, w.dk, w.dv, 2, w.s0_std > 0)
             res["algorithmic_flops_per_launch"] = alg_f
             res["executed_over_algorithmic"] = ex / alg_f
-        res["note"] = ("executed flops = MOPS x 512 (the counter's unit); mfma_busy_frac = MFMA "
+        res["note"] = ("executed flops = (bf16 + fp16 MOPS) x 512 (the counters' unit); mfma_busy_frac = MFMA "
                        "busy cycles summed over the 1024 SIMDs / (GPU-active cycles per XCD x "
                        "1024), the MfmaUtil of rocprofv3 (GRBM_GUI_ACTIVE sums the 8 XCDs).")
     else:  # trace

@@ -89,6 +89,16 @@ typedef struct {
  *
  * A zero-length sequence writes no output rows and copies its initial state (or
  * zeros) to final_state.  T_total == 0 is allowed and only writes final_state.
+ *
+ * Precision of bf16 inputs: the state and every sum are fp32.  With log_alpha_floor >= -0.5
+ * the chunk products take single fp16 operands (11 significant bits); below it they take
+ * bf16 hi/lo pairs (~16 bits, the range of fp32).  The fp16 form needs the decay-folded
+ * rows q e^{G - G_C} and k e^{G - G_C} (at most e^{15 |floor|} <= 1808 times q and k) and
+ * v, the states and the outputs to stay inside fp16's range (65504): q and k entries up to
+ * ~30 in size (unit-norm q and k have entries of at most 1), v, state and output entries up
+ * to ~1e4.  Setting the environment variable KDA_PREFILL_HALF=0 selects the hi/lo form at
+ * every floor.  This covers every entry point that runs the bf16 prefill (plain,
+ * checkpointed, segmented, allocation-free).
  */
 kda_status kda_chunk_prefill(const kda_params* params, const void* q, const void* k,
                              const void* v, const void* log_alpha, const void* beta,

@@ -17,14 +17,18 @@
 // current chunk runs (same digest, section "基础设施": intra-chunk work overlapped with
 // inter-chunk state propagation).
 //
-// Precision.  Products whose bf16 rounding would cost accuracy carry a second bf16 half
-// (x = hi + lo, ~16 significant bits): P and the Qt/Kb it is built from, the chunk's
-// writes U, Kb in the state update, and both Qt and S' in the readout Qt S' (the
-// readout of the state is where a single bf16 copy costs the most: outputs are small
-// differences of larger terms).  The fp32 state is kept in MFMA accumulators; its bf16
-// hi copy alone feeds the Wt S' product.  The powers
-// of A in the inverse are plain bf16 products (A is strictly lower triangular with
-// entries below one in size, and T only enters through bf16 operands anyway).
+// Precision.  The state and every sum are fp32 (MFMA accumulators); a single bf16 copy of
+// the operands (8 significant bits) would miss the outputs' tolerance, so the operands come
+// in one of two forms (template flag H16, chosen on the host from the log-decay floor):
+//  * half form: every product takes single fp16 operands (11 significant bits), the Gram
+//    products, P and the powers of A included.  The decay-folded tiles Qt, Kt reach
+//    e^{15 |floor|} times q and k, which bounds the floors this form serves.
+//  * split form: products whose bf16 rounding would cost accuracy carry a second bf16 half
+//    (x = hi + lo, ~16 significant bits, the range of fp32): P and the Qt/Kb it is built
+//    from, the chunk's writes U, Kb in the state update, and both Qt and S' in the readout
+//    Qt S'.  S''s bf16 hi copy alone feeds the Wt S' product; the powers of A in the
+//    inverse are plain bf16 products (A is strictly lower triangular with entries below
+//    one in size, and T only enters through bf16 operands anyway).
 //
 // Workgroup = one (sequence, head, slice of NV = 16*NCB value columns).  Waves:
 //   chain  (NCB/CPW): CPW 16-column blocks of S each -- two in the full-width workgroup
@@ -268,7 +272,8 @@ struct Cfg {
     static constexpr int VGI = 2 * VGI_T;
     static constexpr int VG_PER_WAVE = (VGI + NDW - 1) / NDW;
     // long ring (4 slots, chunk c written at iteration c-3, read up to iteration c):
-    // Qt hi/lo, Kb hi/lo rows, gamma, value and gate rows
+    // Qt hi/lo, Kb hi/lo rows (the half form uses the hi slots for its fp16 tiles), gamma,
+    // value and gate rows
     static constexpr int L_QH = 0, L_QL = ROWQ, L_KBH = 2 * ROWQ, L_KBL = 2 * ROWQ + ROWK,
                          L_GAM = 2 * ROWQ + 2 * ROWK, L_V = L_GAM + DK * 4, L_G = L_V + VT,
                          L_SIZE = L_G + VT;
@@ -630,7 +635,7 @@ __global__ __launch_bounds__((Cfg<DK, NCB, DUAL>::THREADS)) void prefill_bf16_ke
         // ================================================================ P / Wt wave
         for (int it = -3; it < it_end; ++it) {
             {
-                // P of chunk it + 2, as A-fragments hi/lo: C(P^T) = C(Kb Qt^T)
+                // P of chunk it + 2, as A-fragments (hi/lo, or fp16 | 0): C(P^T) = C(Kb Qt^T)
                 const int c = it + 2;
                 if (OUT && c >= 0 && c < nch) {
                     const unsigned char* L = lslot(c);
@@ -644,17 +649,17 @@ __global__ __launch_bounds__((Cfg<DK, NCB, DUAL>::THREADS)) void prefill_bf16_ke
                         }
                     } else {
 #pragma unroll
-                    for (int p = 0; p < KP; ++p) {
-                        const int offk = r * C::RSK + 2 * (32 * p + 8 * g);
-                        const int offq = r * C::RSQ + 2 * (32 * p + 8 * g);
-                        const bf16x8 kbh = lds_ld<bf16x8>(L + C::L_KBH + offk);
-                        const bf16x8 kbl = lds_ld<bf16x8>(L + C::L_KBL + offk);
-                        const bf16x8 qh = lds_ld<bf16x8>(L + C::L_QH + offq);
-                        const bf16x8 ql = lds_ld<bf16x8>(L + C::L_QL + offq);
-                        acc = mfma32(kbh, qh, acc);
-                        acc = mfma32(kbh, ql, acc);
-                        acc = mfma32(kbl, qh, acc);
-                    }
+                        for (int p = 0; p < KP; ++p) {
+                            const int offk = r * C::RSK + 2 * (32 * p + 8 * g);
+                            const int offq = r * C::RSQ + 2 * (32 * p + 8 * g);
+                            const bf16x8 kbh = lds_ld<bf16x8>(L + C::L_KBH + offk);
+                            const bf16x8 kbl = lds_ld<bf16x8>(L + C::L_KBL + offk);
+                            const bf16x8 qh = lds_ld<bf16x8>(L + C::L_QH + offq);
+                            const bf16x8 ql = lds_ld<bf16x8>(L + C::L_QL + offq);
+                            acc = mfma32(kbh, qh, acc);
+                            acc = mfma32(kbh, ql, acc);
+                            acc = mfma32(kbl, qh, acc);
+                        }
                     }
                     // acc[i] = P[r][4g+i]; keep the causal part (key position <= query position)
 #pragma unroll
