@@ -39,7 +39,7 @@ CSRC = os.path.join(ROOT, "linear_attention_sequence_chunked_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 BUILD_SCRIPT = os.path.join(ROOT, "linear_attention_sequence_chunked_amd", "build.py")
 # sources whose change invalidates a stored counter summary of the prefill / decode kernels
-PREFILL_SOURCES = ("kda_prefill_bf16.hip", "kda_prefill.hip", "kda_plan.cpp", "kda_device.h",
+PREFILL_SOURCES = ("kda_prefill_bf16.hip", "kda_mfma.h", "kda_prefill.hip", "kda_plan.cpp", "kda_device.h",
                    "kda_launch.h", "kda_api.cpp")
 DECODE_SOURCES = ("kda_decode.hip", "kda_device.h", "kda_launch.h", "kda_api.cpp")
 COPY_BYTES = 1 << 30  # calibration copy: 1 GiB read + 1 GiB written

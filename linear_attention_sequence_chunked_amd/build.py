@@ -18,7 +18,7 @@ OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkda.so")
 SOURCES = ["kda_api.cpp", "kda_plan.cpp", "kda_decode.hip", "kda_prefill.hip", "kda_prefill_bf16.hip",
            "kda_spec.hip", "kda_segment.hip", "kda_backward.hip", "kda_scratch.hip"]
-HEADERS = ["kda_device.h", "kda_launch.h"]
+HEADERS = ["kda_device.h", "kda_launch.h", "kda_mfma.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

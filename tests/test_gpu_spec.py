@@ -4,8 +4,13 @@ no per-draft state stored).
 
 Verify outputs are checked against the oracle's token loop over the K drafts from the
 stored state; commit is checked for every accepted length 0..K (and clamped values)
-against the oracle's state after that many drafts.  Both are also compared bit for bit
-with the same number of kda_decode_step calls, which compute each step in the same order."""
+against the oracle's state after that many drafts.  Commit is also compared bit for bit
+with the same number of kda_decode_step calls, which compute each step in the same order,
+and so is verify where it runs step by step (fp32 drafts, floors below -0.5, or
+KDA_PREFILL_HALF=0); bf16 drafts at floors >= -0.5 are verified in chunk form on the
+matrix core, which sums in another order."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -85,7 +90,9 @@ def verify_and_commit_case(dtype, dk, dv, K, floor, log_alpha_min):
     assert torch.equal(state[N - 1], x.initial_state[N - 1]), "accepted < 0 changed the state"
     do, dS = decode_steps(x, N, K, a, floor, scale)
     torch.cuda.synchronize()
-    assert torch.equal(o, do), "verify differs from consecutive decode steps"
+    chunk_form = dtype == "bf16" and floor >= -0.5 and os.environ.get("KDA_PREFILL_HALF") != "0"
+    if not chunk_form:
+        assert torch.equal(o, do), "verify differs from consecutive decode steps"
     assert torch.equal(state, dS), "commit differs from consecutive decode steps"
 
 
@@ -104,6 +111,15 @@ def test_log_decay_below_floor(dtype, floor, K):
     """Draft log-decays drawn down to -2 with the floor at -0.3 / -0.5."""
     log(f"spec below-floor decays dtype={dtype} floor={floor} K={K}")
     verify_and_commit_case(dtype, 128, 128, K, floor=floor, log_alpha_min=-2.0)
+
+
+@pytest.mark.parametrize("K", [1, 4, 16])
+def test_step_by_step_verify_when_forced(K, monkeypatch):
+    """KDA_PREFILL_HALF=0 keeps bf16 verify on the step-by-step kernel: oracle parity and
+    bit-for-bit agreement with consecutive decode steps."""
+    log(f"spec bf16 step-by-step verify K={K}")
+    monkeypatch.setenv("KDA_PREFILL_HALF", "0")
+    verify_and_commit_case("bf16", 128, 128, K, floor=-0.3, log_alpha_min=-2.0)
 
 
 def test_decode_workload_with_four_drafts():
