@@ -301,7 +301,11 @@ kda_status kda_decode_step(const kda_params* params, const void* q, const void* 
  * kda_spec_verify -- out[n*K + j] = the output kda_decode_step would give for draft j
  * after drafts 0 .. j-1 had been decoded (equivalently, kda_chunk_prefill of the K drafts
  * from `state`).  The state is only read.  out : [num_seqs * K, H, dv], params->dtype;
- * must not overlap any other argument.
+ * must not overlap any other argument.  bf16 drafts at log_alpha_floor >= -0.5 are
+ * verified in chunk form on the matrix core with fp16 operands (the same choice and range
+ * as kda_chunk_prefill's; KDA_PREFILL_HALF=0 turns it off): outputs then agree with the
+ * decode steps to rounding.  Otherwise the drafts are stepped one by one and the outputs
+ * equal those of kda_decode_step bit for bit.
  */
 kda_status kda_spec_verify(const kda_params* params, const void* q, const void* k,
                            const void* v, const void* log_alpha, const void* beta,
