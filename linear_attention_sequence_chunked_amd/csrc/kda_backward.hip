@@ -43,6 +43,7 @@
 
 #include "kda_device.h"
 #include "kda_launch.h"
+#include "kda_mfma.h"
 
 namespace kda {
 namespace {
@@ -101,36 +102,12 @@ __device__ __forceinline__ void store8(float* p, const float (&x)[8]) {
     *reinterpret_cast<f32x4*>(p) = f32x4{x[0], x[1], x[2], x[3]};
     *reinterpret_cast<f32x4*>(p + 4) = f32x4{x[4], x[5], x[6], x[7]};
 }
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
-                                                                 CTRL, 0xF, 0xF, true));
-}
-// eight independent inclusive prefix sums over the 16 lanes of each DPP row
-__device__ __forceinline__ void row_scan8(float (&x)[8]) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] += dpp<0x111>(x[j]);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] += dpp<0x112>(x[j]);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] += dpp<0x114>(x[j]);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] += dpp<0x118>(x[j]);
-}
-__device__ __forceinline__ float row_last(float x) { return dpp<0x15F>(x); }  // lane 15 of the row
+// (dpp, row_scan8, row_last, kLog2e and lds_barrier -- the LDS-only workgroup barrier that
+// leaves loads issued a chunk ahead and the state stores in flight -- come from kda_mfma.h)
 // e^x as the fast exponential computes it, 2^(x log2 e) on v_exp_f32; e^x and e^-x from one
 // product t = x log2 e (the negated product is exact, so both equal the exponential of x
 // and of -x)
-constexpr float kLog2e = 1.44269504088896341f;
 __device__ __forceinline__ float exp2_(float t) { return __builtin_amdgcn_exp2f(t); }
-
-// Workgroup barrier that orders LDS only: __syncthreads() would also wait for every
-// outstanding global access, including loads issued a chunk ahead and the state stores.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 // Raw buffer over [p, p + bytes): stores at offsets past the end are dropped by the range
 // check (no memory access), which masks rows without a branch.
@@ -223,7 +200,6 @@ struct Split4 {
 // packed four-vector, which made the compiler feed the first pair to every use).
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ bf16x4 pack4(bf16x2 a, bf16x2 b) {
     return __builtin_bit_cast(bf16x4, u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)});
 }
@@ -248,17 +224,10 @@ __device__ __forceinline__ bf16x4 lds_tr(const bf16* p) {
     return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(const_cast<bf16*>(p))));
 }
 __device__ __forceinline__ Split4 lds_split_tr(const bf16* hi, const bf16* lo) { return Split4{lds_tr(hi), lds_tr(lo)}; }
-// The products use the 32-deep v_mfma_f32_16x16x32_bf16, which issues at the cost of the
-// 16-deep form; a 32-deep step pairs element j of the A operand with element j of the B
-// operand on each lane, so two 16-deep operands stack into one.  Every accumulator is fed
-// by this one instruction shape only.
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
-    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
-__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
+// The products use the 32-deep v_mfma_f32_16x16x32_bf16 (mfma32 and cat8 of kda_mfma.h),
+// which issues at the cost of the 16-deep form; a 32-deep step pairs element j of the A
+// operand with element j of the B operand on each lane, so two 16-deep operands stack into
+// one.  Every accumulator is fed by this one instruction shape only.
 // c + a b, both split (ah bl + al bh, then ah bh): two 32-deep MFMAs on the one A operand
 // (ah, al), so that only the B side needs a second arrangement -- shared where B is
 __device__ __forceinline__ f32x4 mma3(const Split4& a, const Split4& b, f32x4 c) {
