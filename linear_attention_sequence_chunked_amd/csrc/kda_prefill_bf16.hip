@@ -609,8 +609,10 @@ __global__ __launch_bounds__((Cfg<DK, NCB, DUAL>::THREADS)) void prefill_bf16_ke
                     }
                     return o;
                 };
-                auto ldk = [&](int b) {  // Kb^T fragments of row block b, hi | lo (fp16 | 0)
-                    if constexpr (H16) return cat8h(lds_trh(L + C::L_KBH + tr_k + tr_blk(b)), zero_h4());
+                // Kb^T fragments of row block b: hi | lo, or one fp16 fragment (a 16-deep step)
+                typedef std::conditional_t<H16, f16x4, bf16x8> EK;
+                auto ldk = [&](int b) -> EK {
+                    if constexpr (H16) return lds_trh(L + C::L_KBH + tr_k + tr_blk(b));
                     else return cat8(lds_tr(L + C::L_KBH + tr_k + tr_blk(b)), lds_tr(L + C::L_KBL + tr_k + tr_blk(b)));
                 };
                 // the next chunk's gamma (its decay tiles were written three iterations ago;
@@ -664,15 +666,17 @@ __global__ __launch_bounds__((Cfg<DK, NCB, DUAL>::THREADS)) void prefill_bf16_ke
                     }
                 });
                 const E8 pp = OUT ? lds_ld<E8>(Gs + C::G_P + lane * 16) : tt0;  // P hi | P lo (fp16 | 0)
-                E8 k0 = ldk(0), k1;
+                EK k0 = ldk(0), k1;
                 f32x4 gm0 = ldg(0), gm1;
                 __builtin_amdgcn_sched_barrier(0);
                 E8 uu[CPW];
                 bf16x4 ul[CPW];
+                f16x4 ux[CPW];  // H16: U in fp16 for the 16-deep update
 #pragma unroll
                 for (int cb = 0; cb < CPW; ++cb) {
                     if constexpr (H16) {
-                        uu[cb] = cat8h(to_h4(U[cb]), zero_h4());
+                        ux[cb] = to_h4(U[cb]);
+                        uu[cb] = cat8h(ux[cb], zero_h4());
                     } else {
                         bf16x4 uh;
                         split4(U[cb], uh, ul[cb]);
@@ -696,15 +700,15 @@ __global__ __launch_bounds__((Cfg<DK, NCB, DUAL>::THREADS)) void prefill_bf16_ke
                 // the snapshot instead.
                 unroll<0, KB>([&](auto BI) {
                     constexpr int b = decltype(BI)::value;
-                    E8& kc = (b & 1) ? k1 : k0;
-                    E8& kn = (b & 1) ? k0 : k1;
+                    EK& kc = (b & 1) ? k1 : k0;
+                    EK& kn = (b & 1) ? k0 : k1;
                     f32x4& gp = (b & 1) ? gm0 : gm1;  // gamma of block b - 1
                     if constexpr (b + 1 < KB) kn = ldk(b + 1);
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int cb = 0; cb < CPW; ++cb) {
-                        if constexpr (H16) {
-                            S[cb][b] = mfma32h(kc, uu[cb], S[cb][b]);
+                        if constexpr (H16) {  // the one instruction shape feeding S in this form
+                            S[cb][b] = mfma16h(kc, ux[cb], S[cb][b]);
                         } else {
                             S[cb][b] = mfma32(kc, uu[cb], S[cb][b]);
                             S[cb][b] = mfma32(kc, cat8(ul[cb], zero_bf4()), S[cb][b]);
