@@ -147,3 +147,25 @@ def test_decode_workload_with_four_drafts():
                                   sa(x.gate), [0, a[n]], host(x.initial_state[n:n + 1, h:h + 1]))
             assert_close(f"S n={n} h={h} a={a[n]}", host(state[n, h:h + 1]), rS[0],
                          torch.bfloat16)
+
+
+def test_chunk_form_verify_at_its_range_edge():
+    """Verify in chunk form with every draft decay at the floor -0.5 and q entries of 20
+    (one-hot rows): the operands that meet the state are bounded by q and k, and k e^{-G}
+    stays below e^8 times k; outputs against the oracle."""
+    N, K, H, d = 6, 16, 2, 128
+    log("spec chunk-form verify at the fp16 range edge")
+    x = drafts(N, K, H, d, d, "bf16", seed=31, log_alpha_min=-3.0)
+    T = N * K
+    q = torch.zeros(T * H, d, device="cuda")
+    q[torch.arange(T * H, device="cuda"), torch.arange(T * H, device="cuda") % d] = 20.0
+    xe = ki.KdaInputs(q.view(T, H, d).to(torch.bfloat16), x.k, x.v,
+                      torch.full_like(x.log_alpha, -3.0), x.beta, x.gate, x.cu_seqlens,
+                      x.cu_seqlens_host, x.initial_state)
+    state = xe.initial_state.clone()
+    o = kda.spec_verify(xe.q, xe.k, xe.v, xe.log_alpha, xe.beta, xe.gate, state,
+                        log_alpha_floor=-0.5)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all()
+    ro, _ = oracle_after(xe, K, [0] * N, -0.5, 1.0)
+    assert_close("o (verify, range edge)", host(o), ro, torch.bfloat16)
