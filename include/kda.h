@@ -96,7 +96,8 @@ typedef struct {
  * rows q e^{G - G_C} and k e^{G - G_C} (at most e^{15 |floor|} <= 1808 times q and k) and
  * v, the states and the outputs to stay inside fp16's range (65504): q and k entries up to
  * ~30 in size (unit-norm q and k have entries of at most 1), v, state and output entries up
- * to ~1e4.  Setting the environment variable KDA_PREFILL_HALF=0 selects the hi/lo form at
+ * to ~1e4; inputs beyond that overflow to non-finite outputs rather than to finite wrong
+ * ones.  Setting the environment variable KDA_PREFILL_HALF=0 selects the hi/lo form at
  * every floor.  This covers every entry point that runs the bf16 prefill (plain,
  * checkpointed, segmented, allocation-free).
  */
