@@ -26,10 +26,25 @@ pytestmark = pytest.mark.gpu
 TOL = 32 * 2.0 ** -16
 
 
-def check(name, got, want):
+def check(name, got, want, zero_scale=0.0):
+    """max|err| <= TOL * RMS(want).  Where the oracle's tensor is identically zero (a
+    one-token sequence without S0 and dS_final has no decay gradient: the decay multiplies
+    a zero state), the relative form divides by zero; the bar is then TOL * zero_scale in
+    absolute terms, zero_scale being the size of the products that cancel to form it
+    (exactly zero when none is given).  Empty tensors (no tokens) pass only if both are."""
     got, want = np.asarray(got, np.float64), np.asarray(want, np.float64)
+    assert got.shape == want.shape, f"{name}: shape {got.shape} != {want.shape}"
+    if want.size == 0:
+        log(f"  {name}: empty")
+        return
     assert np.all(np.isfinite(got)), f"{name}: non-finite values"
     rms = float(np.sqrt(np.mean(want * want)))
+    if rms == 0.0:
+        err = float(np.max(np.abs(got)))
+        log(f"  {name}: the oracle's tensor is zero; max|got| = {err:.2e} "
+            f"(bar {TOL * zero_scale:.2e})")
+        assert err <= TOL * zero_scale, f"{name}: {err:.3e} > {TOL * zero_scale:.3e}"
+        return
     err = float(np.max(np.abs(got - want))) / max(rms, 1e-30)
     log(f"  {name}: max|err|/RMS = {err:.2e} (tol {TOL:.2e}, margin {TOL / max(err, 1e-30):.1f}x)")
     assert err <= TOL, f"{name}: {err:.3e} > {TOL}"
@@ -61,8 +76,16 @@ def run_case(x, do, dSf, floor, scale, pairs=None):
             got[key].append(host(g[gk][a:e, h]).reshape(-1))
         want["dS0"].append(r["dS0"].reshape(-1))
         got["dS0"].append(host(g["d_initial_state"][n, h]).reshape(-1))
+    # the decay gradient sums products of q with dq and of k with dk (the terms of the
+    # decay-folded operands' gradients), which cancel exactly where it vanishes
+    rms = lambda a: float(np.sqrt(np.mean(a * a))) if a.size else 0.0
+    qk = [(host(x.q[cu[n]:cu[n + 1], h]).reshape(-1), host(x.k[cu[n]:cu[n + 1], h]).reshape(-1))
+          for n, h in pairs]
+    qdq = np.concatenate([q * d for (q, _), d in zip(qk, want["dq"])])
+    kdk = np.concatenate([k * d for (_, k), d in zip(qk, want["dk"])])
     for key in want:
-        check(key, np.concatenate(got[key]), np.concatenate(want[key]))
+        check(key, np.concatenate(got[key]), np.concatenate(want[key]),
+              zero_scale=rms(qdq) + rms(kdk) if key == "dlog_alpha" else 0.0)
     return g
 
 

@@ -45,3 +45,20 @@ def test_random_backward(seed):
     if c["dsf"]:
         dSf = (torch.randn((N, c["H"], c["dk"], c["dv"]), generator=g) * 0.1).cuda()
     bw.run_case(x, do, dSf, floor=c["floor"], scale=c["scale"])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("lengths,s0,dsf", [((1,), False, False), ((1, 1), False, False),
+                                            ((0,), True, False), ((0,), False, True),
+                                            ((0, 1), False, True)])
+def test_backward_degenerate_batches(dtype, lengths, s0, dsf):
+    """Batches whose oracle gradients vanish or are empty: one-token sequences without S0 and
+    dS_final (no decay gradient: the decay multiplies a zero state), and empty sequences (no
+    token gradients; dS0 is dS_final passed through, or zero)."""
+    log(f"backward degenerate dtype={dtype} lengths={lengths} s0={s0} dsf={dsf}")
+    x = ki.make_prefill_inputs(lengths, 2, 64, 64, dtype, 0.3 if s0 else 0.0, seed=41,
+                               device="cuda", log_alpha_min=-0.5)
+    g = torch.Generator().manual_seed(41)
+    do = (torch.randn(x.v.shape, generator=g) * 0.5).to(x.v.dtype).cuda()
+    dSf = (torch.randn((len(lengths), 2, 64, 64), generator=g) * 0.1).cuda() if dsf else None
+    bw.run_case(x, do, dSf, floor=-0.5, scale=0.9)
